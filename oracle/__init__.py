@@ -1,0 +1,188 @@
+"""CPU oracle for the batched symmetric tridiagonal eigensolver.
+
+TEST INFRASTRUCTURE ONLY. Only the tests, ``__graft_entry__.smoke()`` and
+the benchmark's CPU-baseline leg may import this package. The GPU library
+and its Python binding never import, link or call it, and it shares no code
+with them.
+
+The solver itself is plain C (``steqr_oracle_impl.h``), an implicit shifted
+QR/QL iteration written step by step from the BatchLAS steqr algorithm page
+(deflation, scaling, shift, Givens bulge chase, split bookkeeping,
+eigenvector accumulation, sort). It runs in the item's precision with IEEE
+semantics and no FMA contraction. This module builds it with gcc, loads it
+with ctypes and splits batches across threads (ctypes releases the GIL while
+the C code runs).
+"""
+from __future__ import annotations
+
+import concurrent.futures as _cf
+import ctypes as _ct
+import os as _os
+import subprocess as _sp
+from typing import Optional, Tuple
+
+import numpy as _np
+
+HERE = _os.path.dirname(_os.path.abspath(__file__))
+SOURCE = _os.path.join(HERE, "steqr_oracle.c")
+IMPL = _os.path.join(HERE, "steqr_oracle_impl.h")
+LIBNAME = "liboracle_steqr.so"
+CFLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared"]
+
+_libs = {}
+
+
+def build(out_dir: str = HERE, source_dir: str = HERE, extra_flags=()) -> str:
+    """Compile the oracle library with gcc and return its path."""
+    out = _os.path.join(out_dir, LIBNAME)
+    tmp = out + ".tmp%d" % _os.getpid()
+    cmd = ["gcc", *CFLAGS, *extra_flags, "-o", tmp,
+           _os.path.join(source_dir, "steqr_oracle.c"), "-lm"]
+    _sp.run(cmd, check=True)
+    _os.replace(tmp, out)
+    return out
+
+
+def _stale(path: str) -> bool:
+    if not _os.path.exists(path):
+        return True
+    t = _os.path.getmtime(path)
+    return any(_os.path.getmtime(s) > t for s in (SOURCE, IMPL))
+
+
+def lib(path: Optional[str] = None) -> _ct.CDLL:
+    """Load (building first if absent or older than its sources)."""
+    if path is None:
+        path = _os.path.join(HERE, LIBNAME)
+        if _stale(path):
+            build()
+    if path not in _libs:
+        L = _ct.CDLL(path)
+        for sfx, ct in (("f32", _ct.c_float), ("f64", _ct.c_double)):
+            P = _ct.POINTER(ct)
+            f = getattr(L, "oracle_steqr_batched_" + sfx)
+            f.restype = _ct.c_int
+            f.argtypes = [_ct.c_void_p] * 6 + [_ct.c_int, _ct.c_long, _ct.c_int, _ct.c_int]
+            f = getattr(L, "oracle_lartg_" + sfx)
+            f.restype = None
+            f.argtypes = [ct, ct, P, P, P]
+            f = getattr(L, "oracle_shift_" + sfx)
+            f.restype = ct
+            f.argtypes = [ct, ct, ct]
+            f = getattr(L, "oracle_sym2x2_" + sfx)
+            f.restype = None
+            f.argtypes = [ct, ct, ct, P, P, P, P]
+            f = getattr(L, "oracle_sweep_" + sfx)
+            f.restype = _ct.c_long
+            f.argtypes = [_ct.c_void_p, _ct.c_void_p, _ct.c_void_p, _ct.c_int,
+                          _ct.c_int, _ct.c_int, ct]
+            f = getattr(L, "oracle_constants_" + sfx)
+            f.restype = None
+            f.argtypes = [_ct.c_void_p]
+        _libs[path] = L
+    return _libs[path]
+
+
+def _sfx(dtype) -> str:
+    dt = _np.dtype(dtype)
+    if dt == _np.float32:
+        return "f32"
+    if dt == _np.float64:
+        return "f64"
+    raise TypeError("oracle supports float32 and float64, got %s" % dt)
+
+
+def _ptr(a: Optional[_np.ndarray]):
+    return None if a is None else a.ctypes.data
+
+
+def steqr(d: _np.ndarray, e: _np.ndarray, jobz: bool = True,
+          max_sweeps_per_n: int = 30, sort: bool = True, threads: int = 1,
+          libpath: Optional[str] = None
+          ) -> Tuple[_np.ndarray, Optional[_np.ndarray], _np.ndarray, _np.ndarray]:
+    """Solve a batch. d: (batch, n), e: (batch, n-1), same float dtype.
+
+    Returns (lam (batch, n), Q (batch, n, n) or None, info (batch,) int32,
+    stats (batch, 3) int64 = [implicit sweeps, sweep rotations, 2x2 solves]).
+    """
+    d = _np.ascontiguousarray(d)
+    e = _np.ascontiguousarray(e)
+    if d.ndim != 2 or e.ndim != 2 or e.shape[0] != d.shape[0] or \
+            e.shape[1] != max(d.shape[1] - 1, 0) or e.dtype != d.dtype:
+        raise ValueError("bad band shapes %s %s" % (d.shape, e.shape))
+    batch, n = d.shape
+    sfx = _sfx(d.dtype)
+    lam = _np.empty_like(d)
+    Q = _np.empty((batch, n, n), dtype=d.dtype) if jobz else None
+    info = _np.zeros(batch, dtype=_np.int32)
+    stats = _np.zeros((batch, 3), dtype=_np.int64)
+    if batch == 0 or n == 0:
+        return lam, Q, info, stats
+    fn = getattr(lib(libpath), "oracle_steqr_batched_" + sfx)
+    it = d.itemsize
+
+    def run(lo: int, hi: int) -> int:
+        cnt = hi - lo
+        return fn(d.ctypes.data + lo * n * it,
+                  e.ctypes.data + lo * max(n - 1, 0) * it,
+                  lam.ctypes.data + lo * n * it,
+                  None if Q is None else Q.ctypes.data + lo * n * n * it,
+                  info.ctypes.data + lo * 4,
+                  stats.ctypes.data + lo * 3 * 8,
+                  n, cnt, int(max_sweeps_per_n), int(bool(sort)))
+
+    threads = max(1, min(int(threads), batch))
+    if threads == 1:
+        rc = run(0, batch)
+        if rc != 0:
+            raise ValueError("oracle rejected n=%d" % n)
+    else:
+        cuts = [batch * k // threads for k in range(threads + 1)]
+        with _cf.ThreadPoolExecutor(threads) as ex:
+            rcs = list(ex.map(lambda k: run(cuts[k], cuts[k + 1]), range(threads)))
+        if any(rcs):
+            raise ValueError("oracle rejected n=%d" % n)
+    return lam, Q, info, stats
+
+
+def lartg(f: float, g: float, dtype=_np.float64, libpath=None):
+    """(c, s, r) with G(c,s)^T (f, g) = (r, 0), G = [[c,-s],[s,c]]."""
+    sfx = _sfx(dtype)
+    ct = _ct.c_float if sfx == "f32" else _ct.c_double
+    c, s, r = ct(), ct(), ct()
+    getattr(lib(libpath), "oracle_lartg_" + sfx)(f, g, _ct.byref(c), _ct.byref(s), _ct.byref(r))
+    return c.value, s.value, r.value
+
+
+def shift(d1: float, d2: float, e1: float, dtype=_np.float64, libpath=None) -> float:
+    """Eigenvalue of [[d2, e1], [e1, d1]] nearest d1 (LAPACK-form shift)."""
+    return getattr(lib(libpath), "oracle_shift_" + _sfx(dtype))(d1, d2, e1)
+
+
+def sym2x2(a: float, b: float, c: float, dtype=_np.float64, libpath=None):
+    """(rt1, rt2, cs, sn): J^T [[a,b],[b,c]] J = diag(rt1, rt2), J = [[cs,sn],[-sn,cs]]."""
+    sfx = _sfx(dtype)
+    ct = _ct.c_float if sfx == "f32" else _ct.c_double
+    o = [ct() for _ in range(4)]
+    getattr(lib(libpath), "oracle_sym2x2_" + sfx)(a, b, c, *[_ct.byref(x) for x in o])
+    return tuple(x.value for x in o)
+
+
+def sweep(d: _np.ndarray, e: _np.ndarray, Q: Optional[_np.ndarray], s: int, m: int,
+          mu: float, libpath=None) -> int:
+    """One implicit QR sweep on [s, m] in place (d: (n,), e: (n-1,), Q: (n,n))."""
+    n = d.shape[0]
+    assert d.flags.c_contiguous and e.flags.c_contiguous
+    assert 0 <= s < m < n
+    if Q is not None:
+        assert Q.flags.c_contiguous and Q.shape == (n, n) and Q.dtype == d.dtype
+    return getattr(lib(libpath), "oracle_sweep_" + _sfx(d.dtype))(
+        d.ctypes.data, e.ctypes.data, _ptr(Q), n, s, m, mu)
+
+
+def constants(dtype) -> dict:
+    """eps, safmin, ssfmax, ssfmin, eps^2 as the oracle computes them."""
+    sfx = _sfx(dtype)
+    out = _np.zeros(5, dtype=_np.float32 if sfx == "f32" else _np.float64)
+    getattr(lib(), "oracle_constants_" + sfx)(out.ctypes.data)
+    return dict(zip(("eps", "safmin", "ssfmax", "ssfmin", "eps2"), out.tolist()))

@@ -1,0 +1,272 @@
+"""Core pins of the CPU oracle against mathematics independent of it.
+
+Each pin returns a list of failure strings (empty = pinned). They are run
+by tests/test_oracle_pins.py on the real oracle, and on deliberately broken
+copies of the oracle source (tests/test_oracle_mutants.py) to show that a
+plausible mistake anywhere in the oracle fails at least one of them.
+
+What each pin checks, and why it is independent of the oracle's own code:
+  lartg      the defining relations of the Givens rotation on the pages
+             (G^T (f,g) = (r,0), c^2 + s^2 = 1) and its stated special case
+             g = 0 -> (1, 0, f), plus overflow-free behaviour at 1e+-30 in f32;
+  shift      the LAPACK-form shift equals the closed-form 2x2 eigenvalue
+             nearest the endpoint (quadratic formula, long double);
+  sym2x2     the analytic 2x2 solve against the same closed form and the
+             diagonalisation J^T B J = diag;
+  sweep      one implicit sweep against an explicit shifted QR step
+             T - mu I = QR, T' = RQ + mu I (numpy QR in float64): by the
+             implicit-Q theorem the two agree up to the signs of e; and the
+             accumulated rotations reproduce T' = Q^T T Q;
+  solve      whole solves against Sturm-count bisection in long double, the
+             residual and orthogonality bounds, the trace and Frobenius
+             invariants, the Kac-Sylvester-Clement matrix (integer spectrum),
+             and the scaling identity lambda(1e18 T) = 1e18 lambda(T).
+"""
+from __future__ import annotations
+
+import math
+from typing import List, Optional
+
+import numpy as np
+
+import validate as V
+import workloads as W
+
+
+def _fail(out: List[str], cond: bool, msg: str) -> None:
+    if not cond:
+        out.append(msg)
+
+
+def pin_lartg(oracle, libpath: Optional[str] = None) -> List[str]:
+    out: List[str] = []
+    rng = np.random.default_rng(7)
+    for dt in (np.float32, np.float64):
+        eps = V.eps_of(dt)
+        pairs = list(zip(rng.standard_normal(200), rng.standard_normal(200)))
+        pairs += [(3.0, 4.0), (-3.0, 4.0), (3.0, -4.0), (-3.0, -4.0), (1e-3, 5.0),
+                  (7.0, 1e-6)]
+        if dt == np.float32:
+            pairs += [(1e30, 3e30), (-2e30, 1e30), (1e-30, -3e-30), (4e-30, 1e-30),
+                      (1e30, 1e-30)]
+        else:
+            pairs += [(1e300, 3e300), (1e-300, -2e-300)]
+        for f, g in pairs:
+            f = float(dt(f))
+            g = float(dt(g))
+            c, s, r = oracle.lartg(f, g, dt, libpath)
+            if not all(map(math.isfinite, (c, s, r))):
+                out.append("lartg non-finite for (%g,%g)" % (f, g))
+                continue
+            scale = max(abs(f), abs(g))
+            fl, gl, cl, sl, rl = (np.longdouble(v) for v in (f, g, c, s, r))
+            _fail(out, abs(cl * fl + sl * gl - rl) <= 4 * eps * scale,
+                  "lartg c f + s g != r at (%g,%g)" % (f, g))
+            _fail(out, abs(-sl * fl + cl * gl) <= 4 * eps * scale,
+                  "lartg -s f + c g != 0 at (%g,%g)" % (f, g))
+            _fail(out, abs(cl * cl + sl * sl - 1) <= 4 * eps,
+                  "lartg c^2+s^2 != 1 at (%g,%g)" % (f, g))
+            _fail(out, c >= 0 and (r == 0 or math.copysign(1, r) == math.copysign(1, f)),
+                  "lartg sign convention (c >= 0, sign r = sign f) at (%g,%g)" % (f, g))
+        for f in (2.5, -1.0, 0.0):
+            c, s, r = oracle.lartg(f, 0.0, dt, libpath)
+            _fail(out, (c, s, r) == (1.0, 0.0, f), "lartg(f, 0) != (1, 0, f)")
+        c, s, r = oracle.lartg(0.0, -2.0, dt, libpath)
+        _fail(out, (c, s, r) == (0.0, -1.0, 2.0), "lartg(0, g) != (0, sign g, |g|)")
+    return out
+
+
+def _closest_eig(d1, d2, e1):
+    """Eigenvalue of [[d2, e1], [e1, d1]] nearest d1, by the quadratic formula
+    of the algorithm page's shift section, in long double."""
+    a, c, b = np.longdouble(d2), np.longdouble(d1), np.longdouble(e1)
+    mid = (a + c) / 2
+    rad = np.sqrt(((a - c) / 2) ** 2 + b * b)
+    lp, lm = mid + rad, mid - rad
+    return lp if abs(lp - c) < abs(lm - c) else lm
+
+
+def pin_shift(oracle, libpath: Optional[str] = None) -> List[str]:
+    out: List[str] = []
+    rng = np.random.default_rng(11)
+    for dt in (np.float32, np.float64):
+        eps = V.eps_of(dt)
+        trip = [tuple(map(float, rng.standard_normal(3))) for _ in range(300)]
+        trip += [(0.0, 2.0, 1.0), (2.0, 0.0, 1.0), (1.0, 1.0, 1e-3), (5.0, -5.0, 1e-2)]
+        for d1, d2, e1 in trip:
+            d1, d2, e1 = (float(dt(v)) for v in (d1, d2, e1))
+            if e1 == 0:
+                continue
+            mu = oracle.shift(d1, d2, e1, dt, libpath)
+            ref = _closest_eig(d1, d2, e1)
+            scale = abs(d1) + abs(d2) + abs(e1)
+            _fail(out, abs(np.longdouble(mu) - ref) <= 8 * eps * scale,
+                  "shift(%g,%g,%g)=%r, closed form %r" % (d1, d2, e1, mu, float(ref)))
+    return out
+
+
+def pin_sym2x2(oracle, libpath: Optional[str] = None) -> List[str]:
+    out: List[str] = []
+    rng = np.random.default_rng(13)
+    for dt in (np.float32, np.float64):
+        eps = V.eps_of(dt)
+        trip = [tuple(map(float, rng.standard_normal(3))) for _ in range(300)]
+        trip += [(1.0, 1.0, 1.0), (2.0, 0.0, 2.0), (0.0, 1e-20, 1.0), (3.0, 4.0, -3.0)]
+        for a, b, c in trip:
+            a, b, c = (float(dt(v)) for v in (a, b, c))
+            rt1, rt2, cs, sn = oracle.sym2x2(a, b, c, dt, libpath)
+            A, B, C = (np.longdouble(v) for v in (a, b, c))
+            mid = (A + C) / 2
+            rad = np.sqrt(((A - C) / 2) ** 2 + B * B)
+            got = sorted([np.longdouble(rt1), np.longdouble(rt2)])
+            scale = abs(a) + abs(b) + abs(c)
+            _fail(out, abs(got[0] - (mid - rad)) <= 8 * eps * scale and
+                  abs(got[1] - (mid + rad)) <= 8 * eps * scale,
+                  "sym2x2 eigenvalues (%g,%g,%g)" % (a, b, c))
+            J = np.array([[cs, sn], [-sn, cs]], dtype=np.longdouble)
+            Bm = np.array([[A, B], [B, C]], dtype=np.longdouble)
+            D = J.T @ Bm @ J
+            _fail(out, abs(D[0, 1]) <= 8 * eps * scale and
+                  abs(D[0, 0] - np.longdouble(rt1)) <= 8 * eps * scale and
+                  abs(D[1, 1] - np.longdouble(rt2)) <= 8 * eps * scale,
+                  "sym2x2 rotation does not diagonalise (%g,%g,%g)" % (a, b, c))
+            _fail(out, abs(np.longdouble(cs) ** 2 + np.longdouble(sn) ** 2 - 1) <= 4 * eps,
+                  "sym2x2 rotation not orthogonal")
+    return out
+
+
+def pin_sweep(oracle, libpath: Optional[str] = None) -> List[str]:
+    """One implicit sweep against an explicit shifted QR step."""
+    out: List[str] = []
+    rng = np.random.default_rng(17)
+    n = 10
+    for trial in range(20):
+        d = rng.standard_normal(n)
+        e = rng.standard_normal(n - 1)
+        s, m = (0, n - 1) if trial % 2 == 0 else (2, 7)
+        mu = float(rng.standard_normal())
+        d1, e1 = d.copy(), e.copy()
+        Qs = np.eye(n)
+        rots = oracle.sweep(d1, e1, Qs, s, m, mu, libpath)
+        _fail(out, rots == m - s, "sweep rotation count %d != %d" % (rots, m - s))
+        T = W.dense_from_bands(d[None], e[None])[0]
+        # explicit step on the unreduced sub-block [s, m]
+        blk = T[s:m + 1, s:m + 1]
+        Qe, Re = np.linalg.qr(blk - mu * np.eye(m - s + 1))
+        T1 = Re @ Qe + mu * np.eye(m - s + 1)
+        dref = np.diag(T1)
+        eref = np.diag(T1, 1)
+        scale = np.abs(blk).sum(axis=0).max()
+        tol = 1e-12 * scale
+        _fail(out, np.abs(d1[s:m + 1] - dref).max() <= tol,
+              "sweep diagonal differs from explicit QR step (trial %d)" % trial)
+        _fail(out, np.abs(np.abs(e1[s:m]) - np.abs(eref)).max() <= tol,
+              "sweep off-diagonal differs from explicit QR step (trial %d)" % trial)
+        # untouched parts stay untouched
+        _fail(out, np.array_equal(d1[:s], d[:s]) and np.array_equal(d1[m + 1:], d[m + 1:]),
+              "sweep touched d outside [s, m]")
+        # accumulated rotations reproduce the new tridiagonal
+        T1full = Qs.T @ T @ Qs
+        T1b = W.dense_from_bands(d1[None], e1[None])[0]
+        if s > 0:
+            # couplings to the rest of the matrix are outside the sweep; keep them
+            T1b[s - 1, s] = T1full[s - 1, s]
+            T1b[s, s - 1] = T1full[s, s - 1]
+        if m < n - 1:
+            T1b[m, m + 1] = T1full[m, m + 1]
+            T1b[m + 1, m] = T1full[m + 1, m]
+        _fail(out, np.abs(T1full[s:m + 1, s:m + 1] - T1b[s:m + 1, s:m + 1]).max() <= tol,
+              "accumulated Q does not reproduce the swept block (trial %d)" % trial)
+        # invariants: trace and Frobenius norm of the block
+        _fail(out, abs(d1[s:m + 1].sum() - d[s:m + 1].sum()) <= tol,
+              "sweep trace not preserved")
+        fro0 = (d[s:m + 1] ** 2).sum() + 2 * (e[s:m] ** 2).sum()
+        fro1 = (d1[s:m + 1] ** 2).sum() + 2 * (e1[s:m] ** 2).sum()
+        _fail(out, abs(fro1 - fro0) <= 1e-12 * fro0, "sweep Frobenius norm not preserved")
+    # a sweep with an exact eigenvalue of the trailing 2x2 as shift on a
+    # 2x2 block deflates it
+    d = np.array([1.0, 3.0])
+    e = np.array([0.5])
+    mu = float(_closest_eig(3.0, 1.0, 0.5))
+    oracle.sweep(d, e, None, 0, 1, mu, libpath)
+    _fail(out, abs(e[0]) <= 1e-14, "exact shift does not deflate a 2x2 (e=%g)" % e[0])
+    _fail(out, abs(d[1] - mu) <= 1e-14, "exact shift: d_m != mu")
+    return out
+
+
+def clement(n: int):
+    """Symmetric Kac-Sylvester-Clement matrix: zero diagonal, e_k =
+    sqrt(k (n-k)); its eigenvalues are -(n-1), -(n-3), ..., n-1."""
+    d = np.zeros((1, n))
+    k = np.arange(1, n)
+    e = np.sqrt(k * (n - k)).reshape(1, -1).astype(np.float64)
+    lam = np.arange(-(n - 1), n, 2, dtype=np.float64)
+    return d, e, lam
+
+
+def pin_solve(oracle, libpath: Optional[str] = None, quick: bool = False) -> List[str]:
+    out: List[str] = []
+    sizes = (3, 8, 13) if quick else (1, 2, 3, 5, 8, 13, 16)
+    for dt in (np.float32, np.float64):
+        for n in sizes:
+            d, e = W.random_batch(n, 16 if quick else 48, dt, salt=5)
+            lam, Q, info, _ = oracle.steqr(d, e, True, libpath=libpath)
+            _fail(out, not info.any(), "solve info != 0 (%s n=%d)" % (dt.__name__, n))
+            tol = V.tol_of(dt, n)
+            ref = V.sturm_eigvals(d, e)
+            err = V.sorted_err(lam, ref.astype(np.float64), d, e)
+            _fail(out, err.max() <= tol, "solve vs Sturm %s n=%d: %g > %g"
+                  % (dt.__name__, n, err.max(), tol))
+            _fail(out, np.all(np.diff(lam, axis=1) >= 0), "solve output not ascending")
+            res = V.band_residual(d, e, lam, Q)
+            _fail(out, res.max() <= tol, "solve residual %s n=%d: %g" % (dt.__name__, n, res.max()))
+            orth = V.orthogonality(Q)
+            _fail(out, orth.max() <= tol, "solve orthogonality %s n=%d: %g"
+                  % (dt.__name__, n, orth.max()))
+            lam64 = lam.astype(np.float64)
+            dd, ee = d.astype(np.float64), e.astype(np.float64)
+            tn = V.tnorm1(d, e)
+            tr = np.abs(lam64.sum(1) - dd.sum(1))
+            _fail(out, np.all(tr <= n * tol * tn), "trace invariant %s n=%d" % (dt.__name__, n))
+            fro = (dd ** 2).sum(1) + 2 * (ee ** 2).sum(1)
+            _fail(out, np.all(np.abs((lam64 ** 2).sum(1) - fro) <= 4 * n * tol * tn * tn),
+                  "Frobenius invariant %s n=%d" % (dt.__name__, n))
+    for n in ((8, 16) if quick else (4, 8, 16, 32, 64)):
+        d, e, ref = clement(n)
+        for dt in (np.float32, np.float64):
+            lam, Q, info, _ = oracle.steqr(d.astype(dt), e.astype(dt), True, libpath=libpath)
+            tol = V.tol_of(dt, n)
+            err = np.abs(lam[0].astype(np.float64) - ref).max() / V.tnorm1(d, e)[0]
+            _fail(out, info[0] == 0 and err <= tol, "Clement n=%d %s: %g" % (n, dt.__name__, err))
+    # scaling identity lambda(f T) = f lambda(T). float32: 1e18 straddles
+    # ssfmax = 2^63/3, 1e19 is above it, 1e-18 below ssfmin = 2^-15;
+    # float64: 1e200 above ssfmax = 2^511/3, 1e-200 below ssfmin = 2^-405.
+    n = 12
+    d, e = W.random_batch(n, 32, np.float64, salt=9)
+    for dt, factors in ((np.float32, (1e18, 1e19, 1e-18)), (np.float64, (1e200, 1e-200))):
+        base_l, _, _, _ = oracle.steqr(d.astype(dt), e.astype(dt), False, libpath=libpath)
+        for f in factors:
+            lam, Q, info, _ = oracle.steqr((d * f).astype(dt), (e * f).astype(dt), True,
+                                           libpath=libpath)
+            err = V.sorted_err(lam.astype(np.float64) / f, base_l, d, e)
+            _fail(out, not info.any() and err.max() <= V.tol_of(dt, n),
+                  "scaling identity %s at %g: %g" % (dt.__name__, f, err.max()))
+            orth = V.orthogonality(Q).max()
+            _fail(out, orth <= V.tol_of(dt, n), "scaled orthogonality %s at %g" % (dt.__name__, f))
+    return out
+
+
+ALL_PINS = (pin_lartg, pin_shift, pin_sym2x2, pin_sweep, pin_solve)
+
+
+def run_all(oracle, libpath: Optional[str] = None, quick: bool = True) -> List[str]:
+    fails: List[str] = []
+    for p in ALL_PINS:
+        try:
+            if p is pin_solve:
+                fails += p(oracle, libpath, quick=quick)
+            else:
+                fails += p(oracle, libpath)
+        except Exception as exc:  # a crash of the oracle is a failed pin too
+            fails.append("%s raised %r" % (p.__name__, exc))
+    return fails

@@ -1,0 +1,70 @@
+"""Anti-vacuity: plausible mistakes planted in a copy of the oracle source
+must each fail at least one pin.
+
+Each mutant is the oracle's C source with one textual change (a dropped
+term, a flipped sign, a wrong index, a transposed operand, a missing step),
+compiled into a temporary directory on the CPU. The real oracle is never
+modified.
+"""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+import oracle
+import oracle_pins as P
+
+MUTANTS = [
+    ("drop_cross_term", "d[i] = cc * a + (REAL)2 * cs * b + ss * dd;",
+     "d[i] = cc * a + ss * dd;"),
+    ("bulge_sign", "bulge = sn * e[i + 1];", "bulge = -sn * e[i + 1];"),
+    ("r_wrong_index", "e[i - 1] = r;", "e[i] = r;"),
+    ("e_update_sign", "e[i] = cs * (dd - a) + (cc - ss) * b;",
+     "e[i] = cs * (dd - a) + (cc + ss) * b;"),
+    ("q_rotation_transposed", "Q[row * n + k] = c * qa + s * qb;",
+     "Q[row * n + k] = c * qa - s * qb;"),
+    ("shift_sign", "return d1 - e1 / (g + R_COPYSIGN(r, g));",
+     "return d1 + e1 / (g + R_COPYSIGN(r, g));"),
+    ("shift_operands_swapped", "REAL g = (d2 - d1) / ((REAL)2 * e1);",
+     "REAL g = (d1 - d2) / ((REAL)2 * e1);"),
+    ("lartg_s_unsigned", "*s = g / rr;", "*s = g / h;"),
+    ("sym2x2_sign", "*rt1 = a - t * b;", "*rt1 = a + t * b;"),
+    ("sym2x2_q_transposed", "SFX(rot_cols)(Q, n, m - 1, cs, -sn);",
+     "SFX(rot_cols)(Q, n, m - 1, cs, sn);"),
+    ("chase_short", "for (int i = s; i < m; ++i) {", "for (int i = s; i < m - 1; ++i) {"),
+    ("bulge_not_moved", "e[i + 1] = c * e[i + 1];", "e[i + 1] = e[i + 1];"),
+    ("scale_inverted", "sigma = ssfmax / anorm;", "sigma = anorm / ssfmax;"),
+    ("unscale_wrong", "REAL undo = (mode == 1) ? anorm / ssfmax : anorm / ssfmin;",
+     "REAL undo = (mode == 1) ? anorm / ssfmax : ssfmin / anorm;"),
+    ("no_sort", "lam[rk] = d[j];", "lam[j] = d[j];"),
+    ("sort_q_not_permuted", "Q[row * n + rank[j]] = qtmp[row * n + j];",
+     "Q[row * n + j] = qtmp[row * n + j];"),
+    ("reverse_e_off_by_one", "for (int i = l, j = hi - 1; i < j; ++i, --j) {",
+     "for (int i = l, j = hi; i < j; ++i, --j) {"),
+    ("deflation_wrong_pair", "if (SFX(negligible)(e[k - 1], d[k - 1], d[k])) {",
+     "if (SFX(negligible)(e[k - 1] * (REAL)1e-3, d[k - 1], d[k])) {"),
+]
+
+
+def _build_mutant(tmp, old, new):
+    src = os.path.join(tmp, "src")
+    os.makedirs(src)
+    for f in ("steqr_oracle.c", "steqr_oracle_impl.h"):
+        shutil.copy(os.path.join(oracle.HERE, f), src)
+    impl = os.path.join(src, "steqr_oracle_impl.h")
+    text = open(impl).read()
+    assert text.count(old) == 1, "mutation anchor not unique/absent: %r" % old
+    open(impl, "w").write(text.replace(old, new))
+    return oracle.build(out_dir=src, source_dir=src)
+
+
+def test_real_oracle_passes_quick_pins(oracle_mod):
+    assert P.run_all(oracle_mod, quick=True) == []
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, name, old, new):
+    path = _build_mutant(str(tmp_path), old, new)
+    fails = P.run_all(oracle, libpath=path, quick=True)
+    assert fails, "mutant %s passed every pin" % name
