@@ -1,0 +1,109 @@
+/*
+ * steqr.h -- C ABI of the MI355X (gfx950) batched symmetric tridiagonal
+ * eigensolver.
+ *
+ * The operation (BatchLAS steqr algorithm page, problem statement at the top
+ * of the page): for each matrix b of a batch, the symmetric tridiagonal
+ *     T_b = tridiag(e_1..e_{n-1}; d_1..d_n; e_1..e_{n-1})
+ * stored only by its diagonal d and off-diagonal e (band storage, same
+ * page), compute the eigenvalues Lambda and, on request, an orthogonal Q
+ * with T_b = Q Lambda Q^T. The method is the implicit shifted QR/QL
+ * iteration of that page: relative deflation, block scaling, a shift from
+ * the end 2x2 block, a Givens bulge chase, analytic 2x2 blocks and a final
+ * ascending sort that permutes Q's columns the same way.
+ *
+ * Memory layout (all arrays packed, no strides):
+ *   d      [batch][n]       element type T, read only
+ *   e      [batch][n-1]     element type T, read only (absent when n == 1)
+ *   lambda [batch][n]       T, written: eigenvalues, ascending per matrix
+ *   Q      [batch][n][n]    T, written: row-major per matrix, Q[b][i][j] is
+ *                           Q_ij, so eigenvector k is column k (the column
+ *                           for lambda[b][k])
+ * T is float when dtype == STEQR_F32 and double when dtype == STEQR_F64.
+ *
+ * Ownership: every pointer is DEVICE memory owned by the caller (for
+ * example torch tensors on the HIP device). The library keeps no pointer,
+ * allocates nothing and holds no state between calls; calls are
+ * thread-safe. Inputs are never modified.
+ *
+ * Asynchrony: the call only enqueues work on `stream` (0 = the null
+ * stream); results are valid once that stream is synchronised.
+ *
+ * Errors: 0 on success. A negative value -k names the first invalid
+ * argument in the order of steqr_batched's parameter list (LAPACK style):
+ *   -1 d == NULL (n > 0, batch > 0)     -2 e == NULL (n > 1, batch > 0)
+ *   -3 lambda == NULL                   -4 Q == NULL with jobz == STEQR_V
+ *   -5 n < 0 or n > STEQR_MAX_N         -6 batch < 0
+ *   -7 jobz not STEQR_N / STEQR_V       -8 dtype not STEQR_F32 / STEQR_F64
+ *   -10 (steqr_batched_ex only) a params field out of range
+ * A positive value is a hipError_t returned by the kernel launch. n == 0 or
+ * batch == 0 returns 0 at once without touching the GPU.
+ */
+#ifndef STEQR_H
+#define STEQR_H
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define STEQR_MAX_N 64
+
+enum { STEQR_N = 0, STEQR_V = 1 };     /* jobz: values only / values+vectors */
+enum { STEQR_F32 = 0, STEQR_F64 = 1 }; /* dtype */
+
+/* Options of steqr_batched_ex. Zero-initialised fields mean "default". */
+typedef struct steqr_params {
+    /* Sweep budget: max_sweeps_per_n * n implicit sweeps per matrix, the
+     * pages' "30 sweeps per eigenvalue" (BatchLAS "STEQR: the CTA
+     * tridiagonal solver" page, setup paragraph). 0 = 30; negative values
+     * mean a budget of zero sweeps (every matrix that needs one fails). */
+    int max_sweeps_per_n;
+    /* 0 = sort eigenpairs ascending (default), 1 = keep converged order. */
+    int no_sort;
+    /* Lanes per problem P (problems per 64-lane wavefront = 64 / P). 0 =
+     * tuned default; otherwise a power of two the build provides for this
+     * (dtype, n, jobz); steqr_query() lists it. */
+    int lanes_per_problem;
+    /* Wavefronts per workgroup (1, 2, 4 or 8); 0 = default. Launch shape
+     * only: the arithmetic and results do not depend on it. */
+    int waves_per_block;
+} steqr_params;
+
+/* Eigenvalues (jobz = STEQR_N) or eigenpairs (jobz = STEQR_V) of a batch of
+ * symmetric tridiagonal matrices, n <= STEQR_MAX_N, in the precision given
+ * by dtype. Layout, ownership and error codes as described above. A matrix
+ * whose sweep budget runs out keeps its current unsorted values; use
+ * steqr_batched_ex to receive the per-matrix status. */
+int steqr_batched(const void *d, const void *e, void *lambda, void *Q,
+                  int n, int batch, int jobz, int dtype, hipStream_t stream);
+
+/* As steqr_batched, plus:
+ *   info    [batch] int, DEVICE memory, may be NULL. info[b] = 0 when matrix
+ *           b converged; k > 0 when its sweep budget ran out, k being the
+ *           number of nonzero off-diagonal entries left (LAPACK steqr
+ *           convention); lambda[b] and Q[b] are then the current unsorted
+ *           values, unscaled.
+ *   params  may be NULL (all defaults). */
+int steqr_batched_ex(const void *d, const void *e, void *lambda, void *Q,
+                     int n, int batch, int jobz, int dtype, hipStream_t stream,
+                     int *info, const steqr_params *params);
+
+/* Describe the launch steqr_batched_ex would make, without launching:
+ * padded order (the compile-time order the kernel runs at, >= n), lanes per
+ * problem P, rows of Q held per lane, wavefronts per workgroup and
+ * workgroups for `batch` matrices. Returns 0 or the same negative codes as
+ * steqr_batched_ex (-5/-7/-8/-10). Any output pointer may be NULL. */
+int steqr_query(int n, int batch, int jobz, int dtype, const steqr_params *params,
+                int *padded_n, int *lanes_per_problem, int *rows_per_lane,
+                int *waves_per_block, int *workgroups);
+
+/* Library version string, e.g. "steqr-mi355x 0.1.0 gfx950". */
+const char *steqr_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* STEQR_H */

@@ -1,0 +1,134 @@
+// C ABI of the batched steqr library: argument checks, launch-shape choice
+// and dispatch to the compiled kernel instantiations. The declarations and
+// the documentation of every entry point are in include/steqr.h.
+#include <hip/hip_runtime.h>
+
+#include "../../include/steqr.h"
+#include "steqr_registry.hpp"
+
+namespace {
+
+using steqr::Entry;
+using steqr::Table;
+
+// Compile-time orders the build provides, smallest first.
+constexpr int kOrders[] = {4, 8, 16, 32};
+
+int padded_order(int n) {
+    for (int N : kOrders)
+        if (n <= N) return N;
+    return -1;
+}
+
+// Default lanes per problem: the spec mapping, one row of Q per lane
+// (P = N) with values and vectors, and the same P for values only.
+int default_lanes(int dtype, int N, int jobz) {
+    (void)dtype;
+    (void)jobz;
+    return N;
+}
+
+const Entry* find_entry(int dtype, int N, int P, int jobz) {
+    Table t;
+    if (dtype == STEQR_F32)
+        t = jobz ? steqr::table_f32_v() : steqr::table_f32_n();
+    else
+        t = jobz ? steqr::table_f64_v() : steqr::table_f64_n();
+    for (int i = 0; i < t.count; ++i) {
+        const Entry& x = t.entries[i];
+        if (x.dtype == dtype && x.N == N && x.P == P && x.jobz == jobz) return &x;
+    }
+    return nullptr;
+}
+
+struct Plan {
+    const Entry* entry;
+    int N, P, R, waves, grid;
+};
+
+int plan_launch(int n, int batch, int jobz, int dtype, const steqr_params* prm, Plan* out) {
+    if (n < 0 || n > STEQR_MAX_N) return -5;
+    if (batch < 0) return -6;
+    if (jobz != STEQR_N && jobz != STEQR_V) return -7;
+    if (dtype != STEQR_F32 && dtype != STEQR_F64) return -8;
+    int waves = 4;
+    int P = 0;
+    if (prm) {
+        if (prm->waves_per_block != 0) {
+            if (prm->waves_per_block != 1 && prm->waves_per_block != 2 && prm->waves_per_block != 4)
+                return -10;
+            waves = prm->waves_per_block;
+        }
+        P = prm->lanes_per_problem;
+        if (P < 0 || P > 64 || (P != 0 && (64 % P) != 0)) return -10;
+        if (prm->no_sort != 0 && prm->no_sort != 1) return -10;
+    }
+    Plan p{};
+    p.waves = waves;
+    if (n == 0) {
+        *out = p;
+        return 0;
+    }
+    const int N = padded_order(n < 2 ? 2 : n);
+    if (N < 0) return -5;  // order not provided by this build
+    if (P == 0) P = default_lanes(dtype, N, jobz);
+    const Entry* ent = find_entry(dtype, N, P, jobz);
+    if (!ent) return -10;
+    const int per_block = waves * (64 / P);
+    p.entry = ent;
+    p.N = N;
+    p.P = P;
+    p.R = jobz ? (N + P - 1) / P : 0;
+    p.grid = batch > 0 ? (int)(((long)batch + per_block - 1) / per_block) : 0;
+    *out = p;
+    return 0;
+}
+
+}  // namespace
+
+extern "C" int steqr_query(int n, int batch, int jobz, int dtype, const steqr_params* params,
+                           int* padded_n, int* lanes_per_problem, int* rows_per_lane,
+                           int* waves_per_block, int* workgroups) {
+    Plan p;
+    const int rc = plan_launch(n, batch, jobz, dtype, params, &p);
+    if (rc != 0) return rc;
+    if (padded_n) *padded_n = p.N;
+    if (lanes_per_problem) *lanes_per_problem = p.P;
+    if (rows_per_lane) *rows_per_lane = p.R;
+    if (waves_per_block) *waves_per_block = p.waves;
+    if (workgroups) *workgroups = p.grid;
+    return 0;
+}
+
+extern "C" int steqr_batched_ex(const void* d, const void* e, void* lambda, void* Q, int n,
+                                int batch, int jobz, int dtype, hipStream_t stream, int* info,
+                                const steqr_params* params) {
+    Plan p;
+    int rc = plan_launch(n, batch, jobz, dtype, params, &p);
+    if (rc != 0) return rc;
+    if (n == 0 || batch == 0) return 0;
+    if (d == nullptr) return -1;
+    if (n > 1 && e == nullptr) return -2;
+    if (lambda == nullptr) return -3;
+    if (jobz == STEQR_V && Q == nullptr) return -4;
+    steqr::KernelArgs a;
+    a.d = d;
+    a.e = e;
+    a.lam = lambda;
+    a.q = Q;
+    a.info = info;
+    a.n = n;
+    a.batch = batch;
+    const int ms = params ? params->max_sweeps_per_n : 0;
+    a.max_sweeps_per_n = ms == 0 ? 30 : (ms < 0 ? 0 : ms);
+    a.do_sort = params ? !params->no_sort : 1;
+    const hipError_t err = p.entry->fn(a, p.grid, p.waves * 64, stream);
+    return err == hipSuccess ? 0 : (int)err;
+}
+
+extern "C" int steqr_batched(const void* d, const void* e, void* lambda, void* Q, int n,
+                             int batch, int jobz, int dtype, hipStream_t stream) {
+    return steqr_batched_ex(d, e, lambda, Q, n, batch, jobz, dtype, stream, nullptr, nullptr);
+}
+
+extern "C" const char* steqr_version(void) { return "steqr-mi355x 0.1.0 gfx950"; }

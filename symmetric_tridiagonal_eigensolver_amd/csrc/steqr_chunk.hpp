@@ -1,0 +1,399 @@
+// Chunked batched steqr kernel for CDNA4 (gfx950, wave64).
+//
+// One problem per chunk of P consecutive lanes; a wavefront holds 64/P
+// problems. Design (MI355X-first, not a port of the pages' CUDA-warp
+// schedulers):
+//
+//  * Replicated band state. Every lane of a chunk holds the whole d[N], e[N]
+//    of its problem in VGPRs and performs the (serial) chase itself, so the
+//    rotation (c, s) is available in every lane without any cross-lane
+//    broadcast. All lanes of a chunk compute identical values.
+//  * Q rows in VGPRs. Lane r of a chunk holds rows r*R .. r*R+R-1 of Q
+//    (R = ceil(N/P)); each rotation is a lane-parallel update of two columns
+//    of those rows [algo, eigenvector accumulation].
+//  * Static positions. N is a compile-time order (n <= N, padded with a
+//    zero problem tail, [cta, "padding rows are zeroed"]); every loop over
+//    positions is fully unrolled, so d[p], e[p], q[i][p] are registers.
+//  * Direction unification [cta, "QL versus QR ... QR runs as QL on the
+//    mirrored block"]: a block that must converge at its top is mirrored
+//    (the whole order-N problem, Q's columns included, by a static register
+//    reversal) so that every chunk always chases top to bottom and always
+//    converges at the bottom of its block.
+//  * Lockstep passes. The wavefront repeats: settle (each chunk opens blocks,
+//    deflates converged eigenvalues with bit operations over a position
+//    mask, and picks its next operation: a sweep on [s, m] or an analytic
+//    2x2 solve at one position), then one chase pass over the static
+//    positions in which every chunk with a sweep applies its rotation at p
+//    when s <= p < m. Lanes whose chunk is idle at p are masked off (EXEC),
+//    and positions where no chunk is active are skipped by the wave.
+//    The 2x2 solve runs inside the pass at its own static position.
+//
+// The per-chunk sequence of operations is the one of the steqr algorithm
+// page: split blocks at exact zeros with a running left boundary [algo,
+// steqr_cta paragraph], scale each block [algo, scaling], converge the end
+// of smaller |d| first [cta, micro-structure list], re-test deflation after
+// every step and locate the last new zero from the converging end [algo],
+// solve 2x2 blocks analytically [algo], shift from the trailing 2x2 block
+// (LAPACK form) [algo, shift section], chase with Givens rotations as
+// similarities [algo], count sweeps against a budget of
+// max_sweeps_per_n * n [cta, setup paragraph], unscale, sort ascending and
+// permute Q's columns [algo].
+#pragma once
+
+#include "steqr_device.hpp"
+
+namespace steqr {
+
+struct KernelArgs {
+    const void* d;
+    const void* e;
+    void* lam;
+    void* q;
+    int* info;
+    int n;
+    int batch;
+    int max_sweeps_per_n;
+    int do_sort;
+};
+
+// Reverse the whole order-N problem in place (positions p <-> N-1-p for d
+// and Q's columns, e_p <-> e_{N-2-p}) when `mir` holds.
+template <typename T, int N, int RQ, bool WITHQ>
+__device__ __forceinline__ void mirror_problem(bool mir, T (&d)[N], T (&e)[N], T (&q)[RQ][N]) {
+    static_for<N / 2>([&](auto I) {
+        constexpr int p = decltype(I)::value;
+        const T a = d[p], b = d[N - 1 - p];
+        d[p] = mir ? b : a;
+        d[N - 1 - p] = mir ? a : b;
+    });
+    static_for<(N - 1) / 2>([&](auto I) {
+        constexpr int p = decltype(I)::value;
+        const T a = e[p], b = e[N - 2 - p];
+        e[p] = mir ? b : a;
+        e[N - 2 - p] = mir ? a : b;
+    });
+    if constexpr (WITHQ) {
+        static_for<RQ>([&](auto II) {
+            constexpr int i = decltype(II)::value;
+            static_for<N / 2>([&](auto I) {
+                constexpr int p = decltype(I)::value;
+                const T a = q[i][p], b = q[i][N - 1 - p];
+                q[i][p] = mir ? b : a;
+                q[i][N - 1 - p] = mir ? a : b;
+            });
+        });
+    }
+}
+
+// Value at a run-time position of a register array (static selects).
+template <typename T, int N>
+__device__ __forceinline__ T pick(const T (&a)[N], int idx) {
+    T v = a[0];
+    static_for<N - 1>([&](auto I) {
+        constexpr int p = decltype(I)::value + 1;
+        v = (idx == p) ? a[p] : v;
+    });
+    return v;
+}
+
+template <typename T, int N, int P, bool WANTQ>
+__global__ void __launch_bounds__(256) steqr_chunk_kernel(KernelArgs args) {
+    static_assert(P >= 1 && P <= 64 && (64 % P) == 0, "P must divide 64");
+    constexpr int CH = 64 / P;                       // problems per wavefront
+    constexpr int R = WANTQ ? (N + P - 1) / P : 0;   // rows of Q per lane
+    constexpr int RQ = R > 0 ? R : 1;
+    using M = PosMask<N>;
+    using F = Fp<T>;
+    enum { ST_OPEN = 0, ST_ITER = 1, ST_DONE = 2 };
+
+    const T* __restrict__ gd = static_cast<const T*>(args.d);
+    const T* __restrict__ ge = static_cast<const T*>(args.e);
+    T* __restrict__ glam = static_cast<T*>(args.lam);
+    T* __restrict__ gq = static_cast<T*>(args.q);
+    const int n = args.n;
+
+    const int lane = threadIdx.x & 63;
+    const int chunk = lane / P;
+    const int r = lane % P;
+    const long prob = ((long)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6)) * CH + chunk;
+    const bool live = prob < (long)args.batch;
+    const long pb = live ? prob : (long)args.batch - 1;  // in-bounds address for dead chunks
+
+    // ---------------------------------------------------------------- load
+    T d[N], e[N];
+    static_for<N>([&](auto I) {
+        constexpr int p = decltype(I)::value;
+        const int pc = p < n ? p : n - 1;
+        const T v = gd[pb * n + pc];
+        d[p] = (live & (p < n)) ? v : T(0);
+        e[p] = T(0);
+    });
+    if (n > 1) {
+        static_for<N - 1>([&](auto I) {
+            constexpr int p = decltype(I)::value;
+            const int pc = p < n - 1 ? p : n - 2;
+            const T v = ge[pb * (n - 1) + pc];
+            e[p] = (live & (p < n - 1)) ? v : T(0);
+        });
+    }
+    T q[RQ][N];
+    static_for<RQ>([&](auto II) {
+        constexpr int i = decltype(II)::value;
+        const int row = r * R + i;
+        static_for<N>([&](auto J) {
+            constexpr int j = decltype(J)::value;
+            q[i][j] = (WANTQ & (row == j)) ? T(1) : T(0);
+        });
+    });
+    // bit p set <=> e_p == 0 (positions >= n-1 are zero padding)
+    M zeromask = 0;
+    static_for<N>([&](auto I) {
+        constexpr int p = decltype(I)::value;
+        zeromask |= (e[p] == T(0)) ? ((M)1 << p) : (M)0;
+    });
+
+    // ---------------------------------------------------------------- state
+    int state = live ? ST_OPEN : ST_DONE;
+    int l1 = 0;           // running left boundary of the next split block (original coords)
+    int bt = 0, bb = 0;   // current block [bt, bb] in current (possibly mirrored) coords
+    int m = 0;            // converging (bottom) end of the active part
+    int s = 0;            // top of the unreduced part [s, m]
+    int jpos = -1;        // position of a pending analytic 2x2 solve
+    int jtot = 0;
+    const int nmaxit = (args.max_sweeps_per_n > 0 ? args.max_sweeps_per_n : 0) * n;
+    bool mir = false, failed = false;
+    int mode = 0;
+    T anorm = T(0);
+    M zeroed = 0;  // negligible e's found inside the current block
+    int info = 0;
+    T mu = T(0);
+
+    // Close the current block: zero the negligible e's found in it, undo the
+    // scaling (d always, e too when the block failed), undo the mirror.
+    auto close_block = [&](bool fail) __attribute__((always_inline)) {
+        static_for<N - 1>([&](auto I) {
+            constexpr int p = decltype(I)::value;
+            e[p] = ((zeroed >> p) & 1) ? T(0) : e[p];
+        });
+        if (mode != 0) {
+            const T un = (mode == 1) ? anorm / F::ssfmax : anorm / F::ssfmin;
+            static_for<N>([&](auto I) {
+                constexpr int p = decltype(I)::value;
+                d[p] = ((p >= bt) & (p <= bb)) ? d[p] * un : d[p];
+                if constexpr (p < N - 1) e[p] = (fail & (p >= bt) & (p < bb)) ? e[p] * un : e[p];
+            });
+        }
+        mirror_problem<T, N, RQ, WANTQ>(mir, d, e, q);
+        mir = false;
+        mode = 0;
+        zeroed = 0;
+    };
+
+    while (state != ST_DONE) {
+        bool sweep = false, jac = false;
+        // ------------------------------------------------------------ settle
+        while (true) {
+            if (state == ST_OPEN) {
+                // next block: skip 1x1 blocks (zero e), stop at the first zero
+                // e at or right of its start [algo, steqr_cta paragraph]
+                const M avail = ~zeromask & ~bits_below<M>(l1) & bits_below<M>(n - 1);
+                if (avail == 0) {
+                    state = ST_DONE;
+                    break;
+                }
+                const int lo = lsb(avail);
+                const int hi = lsb((M)(zeromask & ~bits_below<M>(lo)));
+                l1 = hi + 1;
+                // block norm, NaN-propagating [algo, scaling]
+                T an = T(0);
+                bool hasnan = false;
+                static_for<N>([&](auto I) {
+                    constexpr int p = decltype(I)::value;
+                    const bool ind = (p >= lo) & (p <= hi);
+                    const bool ine = (p >= lo) & (p < hi);
+                    an = ind ? F::max(an, F::abs(d[p])) : an;
+                    an = ine ? F::max(an, F::abs(e[p])) : an;
+                    hasnan = hasnan | (ind & (d[p] != d[p])) | (ine & (e[p] != e[p]));
+                });
+                anorm = hasnan ? F::qnan() : an;
+                if (anorm == T(0)) continue;
+                mode = (anorm > F::ssfmax) ? 1 : ((anorm < F::ssfmin) ? 2 : 0);
+                if (mode != 0) {
+                    const T sg = ((mode == 1) ? F::ssfmax : F::ssfmin) / anorm;
+                    static_for<N>([&](auto I) {
+                        constexpr int p = decltype(I)::value;
+                        d[p] = ((p >= lo) & (p <= hi)) ? d[p] * sg : d[p];
+                        e[p] = ((p >= lo) & (p < hi)) ? e[p] * sg : e[p];
+                    });
+                }
+                // converge the end of smaller magnitude first; a tie or NaN
+                // converges the top end first, i.e. mirror
+                const T dlo = pick(d, lo), dhi = pick(d, hi);
+                mir = !(F::abs(dhi) < F::abs(dlo));
+                mirror_problem<T, N, RQ, WANTQ>(mir, d, e, q);
+                bt = mir ? N - 1 - hi : lo;
+                bb = mir ? N - 1 - lo : hi;
+                m = bb;
+                zeroed = 0;
+                state = ST_ITER;
+            }
+            // ST_ITER: deflation test over the active part [bt, m]
+            M neg = 0;
+            static_for<N - 1>([&](auto I) {
+                constexpr int p = decltype(I)::value;
+                neg |= negligible(e[p], d[p], d[p + 1]) ? ((M)1 << p) : (M)0;
+            });
+            const M rng = bit_range<M>(bt, m - 1);
+            const M nb = neg & rng;
+            const M clr = rng & ~neg;
+            if (clr == 0) {
+                // every remaining eigenvalue of the block has converged
+                zeroed |= nb;
+                close_block(false);
+                state = ST_OPEN;
+                continue;
+            }
+            // the bottom run of negligible e's deflates 1x1 eigenvalues
+            const int t = msb(clr);
+            zeroed |= nb & bit_range<M>(t + 1, m - 1);
+            m = t + 1;
+            // last negligible e above the converging end bounds the
+            // unreduced part [s, m]
+            const M above = nb & bit_range<M>(bt, t - 1);
+            s = above ? msb(above) + 1 : bt;
+            if (above) zeroed |= (M)1 << (s - 1);
+            if (m - s == 1) {
+                jac = true;
+                jpos = s;
+                m = s - 1;
+                break;
+            }
+            if (jtot >= nmaxit) {
+                failed = true;
+                close_block(true);
+                M nz = 0;
+                static_for<N - 1>([&](auto I) {
+                    constexpr int p = decltype(I)::value;
+                    nz |= (e[p] != T(0)) ? ((M)1 << p) : (M)0;
+                });
+                info = popc((M)(nz & bits_below<M>(n - 1)));
+                info = info > 0 ? info : 1;
+                state = ST_DONE;
+                break;
+            }
+            ++jtot;
+            mu = lapack_shift(pick(d, m), pick(d, m - 1), pick(e, m - 1));
+            sweep = true;
+            break;
+        }
+        if (state == ST_DONE) break;
+
+        // ------------------------------------------------------------ chase pass
+        T x = T(0), y = T(0);
+        static_for<N - 1>([&](auto I) {
+            constexpr int p = decltype(I)::value;
+            if (sweep & (p >= s) & (p < m)) {
+                // [algo]: first rotation from (d_s - mu, e_s), later ones
+                // from (e_{p-1}, bulge); apply G^T B G to the 2x2 at (p, p+1)
+                const bool first = (p == s);
+                const T xin = first ? d[p] - mu : x;
+                const T yin = first ? e[p] : y;
+                T c, sn, rr;
+                lartg(xin, yin, c, sn, rr);
+                if constexpr (p > 0) e[p - 1] = first ? e[p - 1] : rr;
+                const T a = d[p], b = e[p], dd = d[p + 1];
+                const T pp = c * a + sn * b;
+                const T qq = c * b + sn * dd;
+                const T an = pp * c + qq * sn;
+                const T bn = qq * c - pp * sn;
+                d[p] = an;
+                e[p] = bn;
+                d[p + 1] = (a + dd) - an;  // trace of the 2x2 is invariant
+                if constexpr (p + 1 < N - 1) {
+                    const T g = e[p + 1];
+                    y = sn * g;  // new bulge
+                    e[p + 1] = (p + 1 < m) ? c * g : g;
+                }
+                x = bn;
+                if constexpr (WANTQ) {
+                    static_for<R>([&](auto II) {
+                        constexpr int i = decltype(II)::value;
+                        const T qa = q[i][p], qb = q[i][p + 1];
+                        q[i][p] = c * qa + sn * qb;
+                        q[i][p + 1] = c * qb - sn * qa;
+                    });
+                }
+            }
+            if (jac & (p == jpos)) {
+                // analytic 2x2 [algo]: symmetric Schur rotation
+                // J = [[cs, sn], [-sn, cs]], J^T B J = diag
+                const T a = d[p], b = e[p], cc = d[p + 1];
+                const T tau = (cc - a) / (T(2) * b);
+                const T den = F::abs(tau) + F::sqrt(F::fma(tau, tau, T(1)));
+                T t = ((tau >= T(0)) ? T(1) : T(-1)) / den;
+                t = (b == T(0)) ? T(0) : t;
+                const T cs = T(1) / F::sqrt(F::fma(t, t, T(1)));
+                const T sj = t * cs;
+                d[p] = a - t * b;
+                d[p + 1] = cc + t * b;
+                e[p] = T(0);
+                if constexpr (WANTQ) {
+                    static_for<R>([&](auto II) {
+                        constexpr int i = decltype(II)::value;
+                        const T qa = q[i][p], qb = q[i][p + 1];
+                        q[i][p] = cs * qa - sj * qb;
+                        q[i][p + 1] = sj * qa + cs * qb;
+                    });
+                }
+            }
+        });
+        // a NaN shift turns [s, m] into NaN, a fixed point of every further
+        // sweep: spend the rest of the budget at once (same final state)
+        if (sweep & (mu != mu)) jtot = nmaxit;
+    }
+
+    // ---------------------------------------------------------------- sort
+    // rank[j] = #{k < n : (d_k, k) precedes (d_j, j)}; ascending, ties by
+    // index, NaN last [algo, sort paragraph]
+    int rank[N];
+    const bool sort_it = (args.do_sort != 0) & !failed;
+    static_for<N>([&](auto J) {
+        constexpr int j = decltype(J)::value;
+        const T dj = d[j];
+        const bool nanj = dj != dj;
+        int rk = 0;
+        static_for<N>([&](auto K) {
+            constexpr int k = decltype(K)::value;
+            if constexpr (k != j) {
+                const T dk = d[k];
+                const bool before = (k < j) ? ((dk <= dj) | nanj) : ((dk < dj) | (nanj & (dk == dk)));
+                rk += ((k < n) & before) ? 1 : 0;
+            }
+        });
+        rank[j] = sort_it ? rk : j;
+    });
+
+    // ---------------------------------------------------------------- store
+    if (live) {
+        static_for<N>([&](auto J) {
+            constexpr int j = decltype(J)::value;
+            if ((j < n) & ((j % P) == r)) glam[prob * n + rank[j]] = d[j];
+        });
+        if constexpr (WANTQ) {
+            const long qb = prob * (long)n * n;
+            static_for<R>([&](auto II) {
+                constexpr int i = decltype(II)::value;
+                const int row = r * R + i;
+                if (row < n) {
+                    static_for<N>([&](auto J) {
+                        constexpr int j = decltype(J)::value;
+                        if (j < n) gq[qb + (long)row * n + rank[j]] = q[i][j];
+                    });
+                }
+            });
+        }
+        if (args.info != nullptr && r == 0) args.info[prob] = info;
+    }
+}
+
+}  // namespace steqr

@@ -1,0 +1,167 @@
+// Device building blocks of the chunked steqr solve for CDNA4 (gfx950).
+//
+// Everything here runs per lane on values the lane holds in registers; no
+// cross-lane operation is involved. Citations name the BatchLAS pages:
+//   [algo]  the steqr algorithm page ("steqr, steqr_wg and steqr_cta solve
+//           batches of symmetric tridiagonal eigenproblems ...");
+//   [cta]   "STEQR: the CTA tridiagonal solver".
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+#include <utility>
+
+namespace steqr {
+
+// Compile-time loop: fn(std::integral_constant<int, i>) for i = 0..COUNT-1.
+// Register arrays indexed by the constant stay registers from the first
+// optimisation pass on (a plain unrolled loop can be folded into a
+// run-time-indexed memory access before it is unrolled).
+template <typename Fn, int... Is>
+__device__ __forceinline__ void static_for_impl(Fn&& fn, std::integer_sequence<int, Is...>) {
+    (fn(std::integral_constant<int, Is>{}), ...);
+}
+template <int COUNT, typename Fn>
+__device__ __forceinline__ void static_for(Fn&& fn) {
+    if constexpr (COUNT > 0) static_for_impl(fn, std::make_integer_sequence<int, COUNT>{});
+}
+
+// Precision-dependent constants and hardware helpers.
+//  eps2    = eps^2 with eps the unit roundoff (2^-24 / 2^-53)  [algo, deflation]
+//  safmin  = smallest normal number                            [algo, deflation]
+//  ssfmax  = sqrt(1/safmin)/3, ssfmin = sqrt(safmin)/eps^2     [algo, scaling]
+//            (LAPACK's definitions; the page names them only)
+template <typename T>
+struct Fp;
+
+template <>
+struct Fp<float> {
+    static constexpr float eps2 = 0x1p-48f;
+    static constexpr float safmin = 0x1p-126f;
+    static constexpr float ssfmax = 0x1p63f / 3.0f;
+    static constexpr float ssfmin = 0x1p-15f;
+    static constexpr int newton_steps = 1;  // v_rsq_f32 is ~1 ulp
+    __device__ static __forceinline__ int frexp_exp(float x) { return __builtin_amdgcn_frexp_expf(x); }
+    __device__ static __forceinline__ float ldexp(float x, int k) { return __builtin_amdgcn_ldexpf(x, k); }
+    __device__ static __forceinline__ float rsq(float x) { return __builtin_amdgcn_rsqf(x); }
+    __device__ static __forceinline__ float qnan() { return __builtin_nanf(""); }
+    __device__ static __forceinline__ float abs(float x) { return __builtin_fabsf(x); }
+    __device__ static __forceinline__ float sqrt(float x) { return __builtin_sqrtf(x); }
+    __device__ static __forceinline__ float fma(float a, float b, float c) { return __builtin_fmaf(a, b, c); }
+    __device__ static __forceinline__ float max(float a, float b) { return __builtin_fmaxf(a, b); }
+    __device__ static __forceinline__ float copysign(float a, float b) { return __builtin_copysignf(a, b); }
+};
+
+template <>
+struct Fp<double> {
+    static constexpr double eps2 = 0x1p-106;
+    static constexpr double safmin = 0x1p-1022;
+    static constexpr double ssfmax = 0x1p511 / 3.0;
+    static constexpr double ssfmin = 0x1p-405;
+    static constexpr int newton_steps = 2;  // v_rsq_f64 is a low-precision seed
+    __device__ static __forceinline__ int frexp_exp(double x) { return __builtin_amdgcn_frexp_exp(x); }
+    __device__ static __forceinline__ double ldexp(double x, int k) { return __builtin_amdgcn_ldexp(x, k); }
+    __device__ static __forceinline__ double rsq(double x) { return __builtin_amdgcn_rsq(x); }
+    __device__ static __forceinline__ double qnan() { return __builtin_nan(""); }
+    __device__ static __forceinline__ double abs(double x) { return __builtin_fabs(x); }
+    __device__ static __forceinline__ double sqrt(double x) { return __builtin_sqrt(x); }
+    __device__ static __forceinline__ double fma(double a, double b, double c) { return __builtin_fma(a, b, c); }
+    __device__ static __forceinline__ double max(double a, double b) { return __builtin_fmax(a, b); }
+    __device__ static __forceinline__ double copysign(double a, double b) { return __builtin_copysign(a, b); }
+};
+
+// ---------------------------------------------------------------- bit masks
+// Position masks over the off-diagonal index p (bit p <-> e_p).
+
+template <int N>
+using PosMask = typename std::conditional<(N > 32), uint64_t, uint32_t>::type;
+
+// bits [0, k), 0 <= k <= width
+template <typename M>
+__device__ __forceinline__ M bits_below(int k) {
+    if constexpr (sizeof(M) == 4) {
+        return (M)((1ull << k) - 1ull);
+    } else {
+        return k >= 64 ? ~(M)0 : (((M)1 << k) - (M)1);
+    }
+}
+
+// bits [lo, hi]; empty when hi < lo (lo >= 0)
+template <typename M>
+__device__ __forceinline__ M bit_range(int lo, int hi) {
+    return hi < lo ? (M)0 : (M)(bits_below<M>(hi + 1) & ~bits_below<M>(lo));
+}
+
+// index of the highest / lowest set bit (x != 0)
+template <typename M>
+__device__ __forceinline__ int msb(M x) {
+    if constexpr (sizeof(M) == 4) return 31 - __clz((int)x);
+    else return 63 - __clzll((long long)x);
+}
+template <typename M>
+__device__ __forceinline__ int lsb(M x) {
+    if constexpr (sizeof(M) == 4) return __ffs((int)x) - 1;
+    else return __ffsll((long long)x) - 1;
+}
+
+template <typename M>
+__device__ __forceinline__ int popc(M x) {
+    if constexpr (sizeof(M) == 4) return __popc((unsigned)x);
+    else return __popcll((unsigned long long)x);
+}
+
+// ---------------------------------------------------------------- arithmetic
+
+// Deflation test [algo, deflation]: e is negligible between d1 and d2 when
+// |e|^2 <= eps^2 |d1| |d2| + safmin. NaN never passes.
+template <typename T>
+__device__ __forceinline__ bool negligible(T e, T d1, T d2) {
+    return e * e <= Fp<T>::eps2 * (Fp<T>::abs(d1) * Fp<T>::abs(d2)) + Fp<T>::safmin;
+}
+
+// Givens rotation [algo, "G(c,s)" paragraph]: G(c,s) = [[c,-s],[s,c]],
+// G^T (f, g)^T = (r, 0)^T, r with the sign of f (so c >= 0).
+// The norm is formed as a hardware reciprocal square root refined by Newton
+// steps [cta, Givens rotation paragraph]; instead of a range guard with a
+// slow path, f and g are first scaled by an exact power of two (frexp /
+// ldexp of the larger magnitude) so that f^2 + g^2 lies in [1/4, 2) and can
+// neither overflow nor underflow. g = 0 gives (1, 0, f) through a final
+// select [cta, Givens rotation paragraph]. NaN inputs give NaN outputs.
+template <typename T>
+__device__ __forceinline__ void lartg(T f, T g, T& c, T& s, T& r) {
+    using F = Fp<T>;
+    const T mx = F::max(F::abs(f), F::abs(g));
+    const int ex = F::frexp_exp(mx);
+    const T fs = F::ldexp(f, -ex);
+    const T gs = F::ldexp(g, -ex);
+    const T t = fs * fs + gs * gs;
+    T y = F::rsq(t);
+#pragma unroll
+    for (int k = 0; k < F::newton_steps; ++k) {
+        // y <- y + y (1 - t y^2) / 2
+        const T h = t * y;
+        const T res = F::fma(-h, y, T(1));
+        y = F::fma(y * res, T(0.5), y);
+    }
+    const T ys = F::copysign(y, f);
+    const bool gz = (g == T(0));
+    c = gz ? T(1) : fs * ys;
+    s = gz ? T(0) : gs * ys;
+    r = gz ? f : F::ldexp(t * ys, ex);
+}
+
+// LAPACK-form shift [algo, shift section]: the eigenvalue of the 2x2 block
+// [[d2, e1], [e1, d1]] nearest the endpoint d1,
+//   g = (d2 - d1)/(2 e1), r = sqrt(g^2 + 1), mu = d1 - e1/(g + copysign(r, g)).
+// If g^2 overflows, r = inf and mu = d1, which is harmless.
+template <typename T>
+__device__ __forceinline__ T lapack_shift(T d1, T d2, T e1) {
+    using F = Fp<T>;
+    const T g = (d2 - d1) / (T(2) * e1);
+    const T r = F::sqrt(F::fma(g, g, T(1)));
+    return d1 - e1 / (g + F::copysign(r, g));
+}
+
+}  // namespace steqr

@@ -1,0 +1,17 @@
+// Kernel instantiations: float32, eigenvalues only.
+#include "steqr_registry.hpp"
+
+namespace steqr {
+
+#define E(N, P) {0, N, P, 0, &launch_chunk<float, N, P, false>}
+static const Entry kEntries[] = {
+    E(4, 4),   E(4, 1),
+    E(8, 8),   E(8, 1),
+    E(16, 16), E(16, 4),  E(16, 1),
+    E(32, 32), E(32, 4),  E(32, 1),
+};
+#undef E
+
+Table table_f32_n() { return {kEntries, (int)(sizeof(kEntries) / sizeof(kEntries[0]))}; }
+
+}  // namespace steqr

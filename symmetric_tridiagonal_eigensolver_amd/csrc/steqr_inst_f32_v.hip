@@ -1,0 +1,17 @@
+// Kernel instantiations: float32, eigenvalues and eigenvectors.
+#include "steqr_registry.hpp"
+
+namespace steqr {
+
+#define E(N, P) {0, N, P, 1, &launch_chunk<float, N, P, true>}
+static const Entry kEntries[] = {
+    E(4, 4),  E(4, 2),   E(4, 1),
+    E(8, 8),  E(8, 4),   E(8, 2),
+    E(16, 16), E(16, 8), E(16, 4),
+    E(32, 32), E(32, 16), E(32, 8),
+};
+#undef E
+
+Table table_f32_v() { return {kEntries, (int)(sizeof(kEntries) / sizeof(kEntries[0]))}; }
+
+}  // namespace steqr

@@ -1,0 +1,38 @@
+// Launch registry: one entry per compiled (dtype, padded order, lanes per
+// problem, jobz) kernel instantiation. The instantiation units
+// (steqr_inst_*.hip) each export a table; steqr_api.hip searches them.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "steqr_chunk.hpp"
+
+namespace steqr {
+
+typedef hipError_t (*LaunchFn)(const KernelArgs& args, int grid, int block, hipStream_t stream);
+
+struct Entry {
+    int dtype;  // 0 = float, 1 = double
+    int N;      // compile-time (padded) order
+    int P;      // lanes per problem
+    int jobz;   // 0 = values, 1 = values and vectors
+    LaunchFn fn;
+};
+
+template <typename T, int N, int P, bool WANTQ>
+hipError_t launch_chunk(const KernelArgs& args, int grid, int block, hipStream_t stream) {
+    hipLaunchKernelGGL((steqr_chunk_kernel<T, N, P, WANTQ>), dim3(grid), dim3(block), 0, stream, args);
+    return hipGetLastError();
+}
+
+struct Table {
+    const Entry* entries;
+    int count;
+};
+
+Table table_f32_v();
+Table table_f32_n();
+Table table_f64_v();
+Table table_f64_n();
+
+}  // namespace steqr

@@ -1,0 +1,87 @@
+"""GPU-vs-oracle parity checks (test infrastructure).
+
+run_gpu() calls the HIP library through its C ABI (via the Python
+binding); check() compares its outputs with the CPU oracle's on the same
+inputs, item by item:
+  * status: the same items fail (info > 0) on both sides, with equal info;
+  * converged items: sorted eigenvalues within 16 n eps ||T||_1, and for
+    jobz=V residual ||TQ - Q Lambda||_1/||T||_1 and ||Q^T Q - I||_1 within
+    16 n eps (eps = 2^-23 / 2^-52);
+  * zero matrices: eigenvalues exactly 0 and Q exactly I;
+  * failed items: NaN at the same unsorted positions.
+Eigenvectors are compared through residual and orthogonality only: their
+signs (and the basis of a repeated eigenvalue) are not unique.
+"""
+from __future__ import annotations
+
+from typing import List, Optional
+
+import numpy as np
+
+import validate as V
+
+
+def run_gpu(d: np.ndarray, e: np.ndarray, jobz: bool, *, sort: bool = True,
+            max_sweeps_per_n: int = 0, lanes: int = 0, waves: int = 0):
+    import torch
+    import symmetric_tridiagonal_eigensolver_amd as st
+    dev = torch.device("cuda:0")
+    td = torch.from_numpy(np.ascontiguousarray(d)).to(dev)
+    te = torch.from_numpy(np.ascontiguousarray(e)).to(dev)
+    lam, Q, info = st.solve(td, te, jobz, info=True, sort=sort,
+                            max_sweeps_per_n=max_sweeps_per_n, lanes_per_problem=lanes,
+                            waves_per_block=waves)
+    torch.cuda.synchronize()
+    return (lam.cpu().numpy(), None if Q is None else Q.cpu().numpy(), info.cpu().numpy())
+
+
+def check(d, e, gpu, ora, jobz: bool, tol_factor: float = 16.0,
+          items: Optional[np.ndarray] = None) -> List[str]:
+    """Compare gpu = (lam, Q, info) with ora = (lam, Q, info) on items
+    (indices into d/e; default all). gpu arrays may hold more items than
+    ora: gpu[items[k]] pairs with ora[k]."""
+    out: List[str] = []
+    lg, Qg, ig = gpu
+    lo, Qo, io = ora[:3]
+    if items is None:
+        items = np.arange(d.shape[0])
+    d, e = d[items], e[items]
+    lg, ig = lg[items], ig[items]
+    if Qg is not None:
+        Qg = Qg[items]
+    n = d.shape[1]
+    tol = V.tol_of(d.dtype, n, tol_factor)
+    fail_g, fail_o = ig > 0, io > 0
+    if not np.array_equal(fail_g, fail_o):
+        bad = np.nonzero(fail_g != fail_o)[0][:8]
+        out.append("status differs at items %s (gpu info %s, oracle %s)"
+                   % (items[bad].tolist(), ig[bad].tolist(), io[bad].tolist()))
+    both_fail = fail_g & fail_o
+    if both_fail.any():
+        if not np.array_equal(ig[both_fail], io[both_fail]):
+            out.append("info counts differ on failed items")
+        if not np.array_equal(np.isnan(lg[both_fail]), np.isnan(lo[both_fail])):
+            out.append("NaN positions differ on failed items")
+    ok = ~fail_g & ~fail_o
+    if ok.any():
+        err = V.sorted_err(lg[ok], lo[ok], d[ok], e[ok])
+        if not (err.max() <= tol):
+            k = int(np.argmax(err))
+            out.append("eigenvalues: max err %.3g > tol %.3g (item %d)"
+                       % (err.max(), tol, int(items[ok][k])))
+        if not np.all(np.diff(lg[ok], axis=1) >= 0):
+            out.append("gpu eigenvalues not ascending")
+        if jobz:
+            res = V.band_residual(d[ok], e[ok], lg[ok], Qg[ok])
+            if not (res.max() <= tol):
+                out.append("residual %.3g > tol %.3g" % (res.max(), tol))
+            orth = V.orthogonality(Qg[ok])
+            if not (orth.max() <= tol):
+                out.append("orthogonality %.3g > tol %.3g" % (orth.max(), tol))
+        zero = ok & (V.tnorm1(d, e) == 0)
+        if zero.any():
+            if not np.all(lg[zero] == 0):
+                out.append("zero matrix: eigenvalues not exactly 0")
+            if jobz and not np.array_equal(Qg[zero], np.broadcast_to(np.eye(n), Qg[zero].shape)):
+                out.append("zero matrix: Q not exactly I")
+    return out

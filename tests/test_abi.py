@@ -1,0 +1,105 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry
+point include/steqr.h declares, plans launches, and rejects bad arguments
+before touching the device (those paths make no HIP call)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "steqr.h")
+LIB = os.path.join(ROOT, "symmetric_tridiagonal_eigensolver_amd", "libsteqr.so")
+
+
+def _ensure_built():
+    if not os.path.exists(LIB):
+        import __graft_entry__ as g
+        g.build()
+
+
+@pytest.fixture(scope="module")
+def st():
+    _ensure_built()
+    import symmetric_tridiagonal_eigensolver_amd as st
+    return st
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(steqr_\w+)\s*\(", text)))
+
+
+def test_header_declares_expected_entry_points():
+    assert _declared() == ["steqr_batched", "steqr_batched_ex", "steqr_query", "steqr_version"]
+
+
+def test_library_exports_every_declared_symbol(st):
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(l.split()[-1] for l in out.splitlines() if " T " in l)
+    for name in _declared():
+        assert name in exported, name
+        assert hasattr(st.lib(), name)
+    assert set(st.EXPORTS) == set(_declared())
+
+
+def test_library_links_no_oracle():
+    out = subprocess.run(["nm", "-D", LIB], capture_output=True, text=True, check=True).stdout
+    assert "oracle" not in out
+
+
+def test_version(st):
+    assert "gfx950" in st.version()
+
+
+@pytest.mark.parametrize("n,jobz,dtype,N,P", [
+    (1, 1, 0, 4, 4), (4, 1, 0, 4, 4), (5, 1, 0, 8, 8), (8, 0, 0, 8, 8), (12, 1, 1, 16, 16),
+    (16, 1, 0, 16, 16), (17, 1, 0, 32, 32), (32, 0, 1, 32, 32)])
+def test_query_default_plan(st, n, jobz, dtype, N, P):
+    q = st.steqr_query(n, 1000, jobz, dtype)
+    assert q["padded_n"] == N and q["lanes_per_problem"] == P
+    assert q["rows_per_lane"] == ((N + P - 1) // P if jobz else 0)
+    per_block = q["waves_per_block"] * (64 // P)
+    assert q["workgroups"] == -(-1000 // per_block)
+
+
+def test_query_explicit_lanes(st):
+    prm = st.make_params(lanes_per_problem=4)
+    q = st.steqr_query(16, 32768, 1, 0, prm)
+    assert q["lanes_per_problem"] == 4 and q["rows_per_lane"] == 4
+    assert q["workgroups"] == 32768 // (4 * 16)
+
+
+@pytest.mark.parametrize("args,rc", [
+    # (d, e, lam, Q, n, batch, jobz, dtype) -> code
+    ((0, 8, 8, 8, 4, 10, 1, 0), -1),
+    ((8, 0, 8, 8, 4, 10, 1, 0), -2),
+    ((8, 0, 8, 8, 1, 10, 1, 0), None),   # n == 1 needs no e: would launch, skipped
+    ((8, 8, 0, 8, 4, 10, 1, 0), -3),
+    ((8, 8, 8, 0, 4, 10, 1, 0), -4),
+    ((8, 8, 8, 8, -1, 10, 1, 0), -5),
+    ((8, 8, 8, 8, 65, 10, 1, 0), -5),
+    ((8, 8, 8, 8, 4, -1, 1, 0), -6),
+    ((8, 8, 8, 8, 4, 10, 2, 0), -7),
+    ((8, 8, 8, 8, 4, 10, 1, 5), -8),
+    ((0, 0, 0, 0, 0, 10, 1, 0), 0),      # n == 0: quick return
+    ((0, 0, 0, 0, 4, 0, 1, 0), 0),       # batch == 0: quick return
+])
+def test_argument_errors(st, args, rc):
+    if rc is None:
+        pytest.skip("valid call: would launch a kernel")
+    d, e, lam, Q, n, batch, jobz, dtype = args
+    got = st.lib().steqr_batched(d or None, e or None, lam or None, Q or None, n, batch,
+                                 jobz, dtype, None)
+    assert got == rc
+
+
+def test_bad_params(st):
+    L = st.lib()
+    for prm in (st.make_params(lanes_per_problem=3), st.make_params(lanes_per_problem=128),
+                st.make_params(waves_per_block=3), st.make_params(lanes_per_problem=2)):
+        got = L.steqr_batched_ex(8, 8, 8, 8, 16, 10, 1, 0, None, None, ctypes.byref(prm))
+        assert got == -10

@@ -1,0 +1,210 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on
+the same seeded inputs. Needs an MI355X; run with -m gpu."""
+import numpy as np
+import pytest
+
+import oracle
+import validate as V
+import workloads as W
+from parity import check, run_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import symmetric_tridiagonal_eigensolver_amd  # noqa: F401  (fails loudly if not built)
+
+
+def _case(w, jobz, batch):
+    if w.n > 32:
+        pytest.skip("order-64 kernel (one problem per wavefront) not built yet")
+    print("case %s jobz=%s batch=%d" % (w.name, jobz, batch), flush=True)
+
+
+SMALL = 1000 + 13  # several workgroups and a ragged tail for every P
+
+
+@pytest.mark.parametrize("wname", list(W.WORKLOADS))
+@pytest.mark.parametrize("jobz", [True, False], ids=["V", "N"])
+def test_workload_small_batch(wname, jobz):
+    w = W.WORKLOADS[wname]
+    _case(w, jobz, SMALL)
+    d, e = W.make_batch(w, SMALL)
+    g = run_gpu(d, e, jobz)
+    o = oracle.steqr(d, e, jobz, threads=8)
+    assert check(d, e, g, o, jobz) == []
+
+
+@pytest.mark.parametrize("wname", list(W.WORKLOADS))
+@pytest.mark.parametrize("jobz", [True, False], ids=["V", "N"])
+def test_workload_full_size(wname, jobz):
+    """Full batch in the default launch configuration (the one the
+    benchmark times); the oracle checks a spread sample plus the tail, and
+    properties that hold at any size are checked on every item."""
+    w = W.WORKLOADS[wname]
+    _case(w, jobz, w.batch)
+    d, e = W.make_batch(w)
+    g = run_gpu(d, e, jobz)
+    nb = w.batch
+    items = np.unique(np.concatenate([np.linspace(0, nb - 1, 384).astype(int),
+                                      np.arange(nb - 40, nb)]))
+    o = oracle.steqr(d[items], e[items], jobz, threads=8)
+    assert check(d, e, g, o, jobz, items=items) == []
+    lam, Q, info = g
+    finite = np.isfinite(d).all(1) & np.isfinite(e).all(1)
+    assert not info[finite].any()
+    assert np.all(info[~finite] > 0)
+    ok = info == 0
+    tol = V.tol_of(d.dtype, w.n)
+    assert np.all(np.diff(lam[ok], axis=1) >= 0)
+    tn = V.tnorm1(d[ok], e[ok])
+    assert np.all(np.abs(lam[ok].astype(np.float64).sum(1)
+                         - d[ok].astype(np.float64).sum(1)) <= w.n * tol * tn)
+    if jobz:
+        assert V.band_residual(d[ok], e[ok], lam[ok], Q[ok]).max() <= tol
+        assert V.orthogonality(Q[ok]).max() <= tol
+
+
+LANE_CASES = [
+    # dtype, n, jobz, lanes
+    (np.float32, 4, True, 4), (np.float32, 4, True, 2), (np.float32, 4, True, 1),
+    (np.float32, 8, True, 8), (np.float32, 8, True, 4), (np.float32, 8, True, 2),
+    (np.float32, 16, True, 16), (np.float32, 16, True, 8), (np.float32, 16, True, 4),
+    (np.float32, 32, True, 32), (np.float32, 32, True, 16), (np.float32, 32, True, 8),
+    (np.float32, 4, False, 1), (np.float32, 8, False, 1), (np.float32, 16, False, 4),
+    (np.float32, 16, False, 1), (np.float32, 32, False, 4), (np.float32, 32, False, 1),
+    (np.float64, 4, True, 2), (np.float64, 8, True, 4), (np.float64, 16, True, 8),
+    (np.float64, 32, True, 16), (np.float64, 4, False, 1), (np.float64, 8, False, 1),
+    (np.float64, 16, False, 1), (np.float64, 32, False, 1),
+]
+
+
+@pytest.mark.parametrize("dt,n,jobz,lanes", LANE_CASES,
+                         ids=lambda v: v.__name__ if isinstance(v, type) else str(v))
+def test_lanes_per_problem_variants(dt, n, jobz, lanes):
+    d, e = W.random_batch(n, 777, dt, salt=21)
+    print("lanes case", dt.__name__, n, jobz, lanes, flush=True)
+    g = run_gpu(d, e, jobz, lanes=lanes)
+    o = oracle.steqr(d, e, jobz, threads=8)
+    assert check(d, e, g, o, jobz) == []
+
+
+@pytest.mark.parametrize("dt", [np.float32, np.float64], ids=["f32", "f64"])
+@pytest.mark.parametrize("jobz", [True, False], ids=["V", "N"])
+def test_every_order_up_to_32(dt, jobz):
+    for n in range(1, 33):
+        d, e = W.random_batch(n, 67, dt, salt=n)
+        print("order", n, flush=True)
+        g = run_gpu(d, e, jobz)
+        o = oracle.steqr(d, e, jobz)
+        assert check(d, e, g, o, jobz) == [], "n=%d" % n
+
+
+@pytest.mark.parametrize("kind", range(5), ids=W.EDGE_NAMES)
+@pytest.mark.parametrize("dt", [np.float32, np.float64], ids=["f32", "f64"])
+@pytest.mark.parametrize("n", [3, 4, 16, 32])
+def test_edge_items(kind, dt, n):
+    d, e = W.edge_batch(kind, n, 130, dt)
+    print("edge", W.EDGE_NAMES[kind], dt.__name__, n, flush=True)
+    for jobz in (True, False):
+        g = run_gpu(d, e, jobz)
+        o = oracle.steqr(d, e, jobz)
+        assert check(d, e, g, o, jobz) == [], (W.EDGE_NAMES[kind], jobz)
+    if kind == W.EDGE_ZERO:
+        assert np.all(g[0] == 0)
+    if kind == W.EDGE_NAN:
+        assert np.all(g[2] > 0)
+
+
+def test_scaled_items_match_unscaled_twins():
+    n = 32
+    d, e = W.edge_batch(W.EDGE_SCALED, n, 64, np.float64)
+    f = np.where(np.arange(64) % 2 == 0, 1e18, 1e-18)
+    for dt in (np.float32, np.float64):
+        lam, _, info = run_gpu(d.astype(dt), e.astype(dt), False)
+        base, _, binfo = run_gpu((d / f[:, None]).astype(dt), (e / f[:, None]).astype(dt), False)
+        assert not info.any() and not binfo.any()
+        err = V.sorted_err(lam.astype(np.float64) / f[:, None], base, d / f[:, None],
+                           e / f[:, None])
+        assert err.max() <= V.tol_of(dt, n)
+
+
+def test_nan_confined_to_block():
+    n = 12
+    d, e = W.random_batch(n, 8, np.float64, salt=3)
+    e[:, 5] = 0.0
+    d[:, 8] = np.nan
+    g = run_gpu(d, e, True)
+    o = oracle.steqr(d, e, True)
+    assert check(d, e, g, o, True) == []
+    assert np.all(g[2] == 5)
+    assert np.all(np.isfinite(g[0][:, :6])) and np.all(np.isnan(g[0][:, 6:]))
+
+
+@pytest.mark.parametrize("dt", [np.float32, np.float64], ids=["f32", "f64"])
+def test_budget_exhaustion(dt):
+    d, e = W.random_batch(16, 100, dt, salt=8)
+    lam, _, info = run_gpu(d, e, False, max_sweeps_per_n=-1)
+    ol, _, oinfo, _ = oracle.steqr(d, e, False, max_sweeps_per_n=0)
+    assert np.array_equal(info, oinfo) and np.all(info > 0)
+    assert np.array_equal(lam, d)
+    lam1, _, info1 = run_gpu(d, e, True, max_sweeps_per_n=1)
+    o1 = oracle.steqr(d, e, True, max_sweeps_per_n=1)
+    assert np.array_equal(info1 > 0, o1[2] > 0)
+
+
+def test_unsorted_output():
+    d, e = W.random_batch(13, 300, np.float32, salt=4)
+    lam, Q, info = run_gpu(d, e, True, sort=False)
+    slam, _, _ = run_gpu(d, e, True)
+    assert not info.any()
+    assert np.array_equal(np.sort(lam, axis=1), slam)
+    assert V.band_residual(d, e, lam, Q).max() <= V.tol_of(np.float32, 13)
+
+
+def test_deterministic_and_launch_shape_independent():
+    d, e = W.make_batch(W.WORKLOADS["c2_f32_n16"], 4096)
+    a = run_gpu(d, e, True)
+    b = run_gpu(d, e, True)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+    for waves in (1, 2, 4):
+        c = run_gpu(d, e, True, waves=waves)
+        for x, y in zip(a, c):
+            assert np.array_equal(x, y)
+
+
+def test_checker_is_not_vacuous():
+    d, e = W.random_batch(16, 200, np.float32, salt=6)
+    g = run_gpu(d, e, True)
+    o = oracle.steqr(d, e, True)
+    assert check(d, e, g, o, True) == []
+    lam, Q, info = g
+    bad = lam.copy()
+    bad[7, 3] += 1e-3 * V.tnorm1(d, e)[7]
+    assert check(d, e, (bad, Q, info), o, True)
+    badq = Q.copy()
+    badq[9, :, [2, 3]] = badq[9, :, [3, 2]]
+    assert check(d, e, (lam, badq, info), o, True)
+    badi = info.copy()
+    badi[0] = 1
+    assert check(d, e, (lam, Q, badi), o, True)
+
+
+def test_non_default_stream():
+    import torch
+    import symmetric_tridiagonal_eigensolver_amd as st
+    d, e = W.random_batch(16, 500, np.float32, salt=1)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        td = torch.from_numpy(d).cuda()
+        te = torch.from_numpy(e).cuda()
+        lam, Q = st.solve(td, te, True)
+    s.synchronize()
+    o = oracle.steqr(d, e, True)
+    g = (lam.cpu().numpy(), Q.cpu().numpy(), np.zeros(500, np.int32))
+    assert check(d, e, g, o, True) == []
