@@ -108,6 +108,12 @@ def main() -> int:
     ap.add_argument("--lanes", type=int, default=0, help="lanes per problem (0 = default)")
     ap.add_argument("--waves", type=int, default=0, help="waves per workgroup (0 = default)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--replicate", action="store_true",
+                    help="lockstep-ideal batch: every chunk of a wavefront holds the same "
+                         "matrix (each item repeated 64/P times); for divergence counters")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="instead of solving, run a plain device-to-device copy of MIB MiB "
+                         "per step (reference kernel for HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -119,9 +125,28 @@ def main() -> int:
     import torch
     import symmetric_tridiagonal_eigensolver_amd as st
 
+    if args.copy_calibration:
+        nbytes = args.copy_calibration << 20
+        a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
+        b = torch.empty_like(a)
+        for _ in range(args.warmup):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / max(args.steps, 1)
+        print(json.dumps({"copy_calibration_bytes_read": nbytes, "bytes_written": nbytes,
+                          "steps": args.steps, "GBs": 2 * nbytes / dt / 1e9}), flush=True)
+        return 0
+
     w = W.WORKLOADS[args.workload]
     jobz = args.jobz == "V"
-    d, e = W.make_batch(w)
+    prm0 = st.make_params(lanes_per_problem=args.lanes, waves_per_block=args.waves)
+    lanes0 = st.steqr_query(w.n, w.batch, int(jobz), 0 if w.dtype == "f32" else 1,
+                            prm0)["lanes_per_problem"]
+    d, e = W.make_batch(w, replicate=(64 // lanes0) if args.replicate else 1)
     dev = torch.device("cuda:0")
     td = torch.from_numpy(d).to(dev)
     te = torch.from_numpy(e).to(dev)
@@ -193,7 +218,10 @@ def main() -> int:
                    "precision": dtype, "lanes_per_problem": plan["lanes_per_problem"],
                    "rows_per_lane": plan["rows_per_lane"], "padded_n": plan["padded_n"],
                    "waves_per_block": plan["waves_per_block"],
-                   "workgroups": plan["workgroups"], "inputs": "d,e iid N(0,1), seed 1234"},
+                   "workgroups": plan["workgroups"],
+                   "inputs": ("replicated per wavefront (lockstep ideal)" if args.replicate
+                              else ("90% iid N(0,1) + 10% edge items" if w.edge_mix
+                                    else "d,e iid N(0,1)")) + ", seed 1234"},
         "roofline": roof,
         "hbm": {"algorithmic_bytes_per_launch": bpm * nb,
                 "achieved_GBs": bpm * nb / sec / 1e9, "peak_GBs": HBM_PEAK_GBS},

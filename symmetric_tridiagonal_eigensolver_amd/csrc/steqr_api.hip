@@ -74,6 +74,9 @@ int plan_launch(int n, int batch, int jobz, int dtype, const steqr_params* prm, 
     if (P == 0) P = default_lanes(dtype, N, jobz);
     const Entry* ent = find_entry(dtype, N, P, jobz);
     if (!ent) return -10;
+    // keep a workgroup's LDS within 64 KiB
+    while (waves > 1 && (long)waves * ent->lds_per_wave > 65536) waves /= 2;
+    p.waves = waves;
     const int per_block = waves * (64 / P);
     p.entry = ent;
     p.N = N;

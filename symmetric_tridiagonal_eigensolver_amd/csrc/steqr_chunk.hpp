@@ -27,6 +27,10 @@
 //    when s <= p < m. Lanes whose chunk is idle at p are masked off (EXEC),
 //    and positions where no chunk is active are skipped by the wave.
 //    The 2x2 solve runs inside the pass at its own static position.
+//  * Run-time positions (the shift inputs at the converging end, the block
+//    ends, the sort keys) are read from a per-chunk copy of the band in LDS,
+//    republished after every change of the band; register arrays are only
+//    ever indexed by compile-time positions.
 //
 // The per-chunk sequence of operations is the one of the steqr algorithm
 // page: split blocks at exact zeros with a running left boundary [algo,
@@ -85,16 +89,18 @@ __device__ __forceinline__ void mirror_problem(bool mir, T (&d)[N], T (&e)[N], T
     }
 }
 
-// Value at a run-time position of a register array (static selects).
-template <typename T, int N>
-__device__ __forceinline__ T pick(const T (&a)[N], int idx) {
-    T v = a[0];
-    static_for<N - 1>([&](auto I) {
-        constexpr int p = decltype(I)::value + 1;
-        v = (idx == p) ? a[p] : v;
-    });
-    return v;
-}
+// LDS per wavefront: one band slot per chunk (d then e, padded to an odd
+// number of elements against bank conflicts) and, for P > 1, one rank row
+// per chunk for the final sort.
+template <typename T, int N, int P>
+struct Smem {
+    static constexpr int CH = 64 / P;
+    static constexpr int SLOT = 2 * N + 1;
+    static constexpr int band_elems = CH * SLOT;
+    static constexpr int rank_ints = (P > 1) ? CH * N : 0;
+    static constexpr size_t bytes_per_wave =
+        ((band_elems * sizeof(T) + 15) / 16) * 16 + (size_t)rank_ints * sizeof(int);
+};
 
 template <typename T, int N, int P, bool WANTQ>
 __global__ void __launch_bounds__(256) steqr_chunk_kernel(KernelArgs args) {
@@ -102,9 +108,13 @@ __global__ void __launch_bounds__(256) steqr_chunk_kernel(KernelArgs args) {
     constexpr int CH = 64 / P;                       // problems per wavefront
     constexpr int R = WANTQ ? (N + P - 1) / P : 0;   // rows of Q per lane
     constexpr int RQ = R > 0 ? R : 1;
+    constexpr int RJ = (N + P - 1) / P;              // sort keys ranked per lane
     using M = PosMask<N>;
     using F = Fp<T>;
+    using S = Smem<T, N, P>;
     enum { ST_OPEN = 0, ST_ITER = 1, ST_DONE = 2 };
+
+    extern __shared__ __align__(16) unsigned char smem_raw[];
 
     const T* __restrict__ gd = static_cast<const T*>(args.d);
     const T* __restrict__ ge = static_cast<const T*>(args.e);
@@ -113,11 +123,18 @@ __global__ void __launch_bounds__(256) steqr_chunk_kernel(KernelArgs args) {
     const int n = args.n;
 
     const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
     const int chunk = lane / P;
     const int r = lane % P;
-    const long prob = ((long)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6)) * CH + chunk;
+    const long prob = ((long)blockIdx.x * (blockDim.x >> 6) + wave) * CH + chunk;
     const bool live = prob < (long)args.batch;
     const long pb = live ? prob : (long)args.batch - 1;  // in-bounds address for dead chunks
+
+    unsigned char* wave_smem = smem_raw + (size_t)wave * S::bytes_per_wave;
+    T* const sd = reinterpret_cast<T*>(wave_smem) + chunk * S::SLOT;  // chunk's d copy
+    T* const se = sd + N;                                              // chunk's e copy
+    int* const srank = reinterpret_cast<int*>(
+                           wave_smem + ((S::band_elems * sizeof(T) + 15) / 16) * 16) + chunk * N;
 
     // ---------------------------------------------------------------- load
     T d[N], e[N];
@@ -148,9 +165,24 @@ __global__ void __launch_bounds__(256) steqr_chunk_kernel(KernelArgs args) {
     // bit p set <=> e_p == 0 (positions >= n-1 are zero padding)
     M zeromask = 0;
     static_for<N>([&](auto I) {
-        constexpr int p = decltype(I)::value;
-        zeromask |= (e[p] == T(0)) ? ((M)1 << p) : (M)0;
+        constexpr int p = N - 1 - decltype(I)::value;
+        zeromask = zeromask + zeromask + ((e[p] == T(0)) ? (M)1 : (M)0);
     });
+
+    // Publish the chunk's band to LDS (one lane per chunk writes; the
+    // wavefront executes its LDS operations in order, so later reads by any
+    // lane of the chunk see it).
+    auto publish = [&]() __attribute__((always_inline)) {
+        if (r == 0) {
+            static_for<N>([&](auto I) {
+                constexpr int p = decltype(I)::value;
+                sd[p] = d[p];
+                se[p] = e[p];
+            });
+        }
+        __builtin_amdgcn_wave_barrier();
+    };
+    publish();
 
     // ---------------------------------------------------------------- state
     int state = live ? ST_OPEN : ST_DONE;
@@ -187,6 +219,7 @@ __global__ void __launch_bounds__(256) steqr_chunk_kernel(KernelArgs args) {
         mir = false;
         mode = 0;
         zeroed = 0;
+        publish();
     };
 
     while (state != ST_DONE) {
@@ -218,8 +251,8 @@ __global__ void __launch_bounds__(256) steqr_chunk_kernel(KernelArgs args) {
                 anorm = hasnan ? F::qnan() : an;
                 if (anorm == T(0)) continue;
                 mode = (anorm > F::ssfmax) ? 1 : ((anorm < F::ssfmin) ? 2 : 0);
+                const T sg = (mode == 0) ? T(1) : ((mode == 1) ? F::ssfmax : F::ssfmin) / anorm;
                 if (mode != 0) {
-                    const T sg = ((mode == 1) ? F::ssfmax : F::ssfmin) / anorm;
                     static_for<N>([&](auto I) {
                         constexpr int p = decltype(I)::value;
                         d[p] = ((p >= lo) & (p <= hi)) ? d[p] * sg : d[p];
@@ -227,21 +260,23 @@ __global__ void __launch_bounds__(256) steqr_chunk_kernel(KernelArgs args) {
                     });
                 }
                 // converge the end of smaller magnitude first; a tie or NaN
-                // converges the top end first, i.e. mirror
-                const T dlo = pick(d, lo), dhi = pick(d, hi);
-                mir = !(F::abs(dhi) < F::abs(dlo));
+                // converges the top end first, i.e. mirror. |sg*x| = sg*|x|
+                // exactly, so this compares the scaled end values.
+                const T dlo = F::abs(sd[lo]) * sg, dhi = F::abs(sd[hi]) * sg;
+                mir = !(dhi < dlo);
                 mirror_problem<T, N, RQ, WANTQ>(mir, d, e, q);
                 bt = mir ? N - 1 - hi : lo;
                 bb = mir ? N - 1 - lo : hi;
                 m = bb;
                 zeroed = 0;
                 state = ST_ITER;
+                publish();
             }
-            // ST_ITER: deflation test over the active part [bt, m]
+            // ST_ITER: deflation test [algo, deflation] at every position
             M neg = 0;
             static_for<N - 1>([&](auto I) {
-                constexpr int p = decltype(I)::value;
-                neg |= negligible(e[p], d[p], d[p + 1]) ? ((M)1 << p) : (M)0;
+                constexpr int p = N - 2 - decltype(I)::value;
+                neg = neg + neg + (negligible(e[p], d[p], d[p + 1]) ? (M)1 : (M)0);
             });
             const M rng = bit_range<M>(bt, m - 1);
             const M nb = neg & rng;
@@ -273,8 +308,8 @@ __global__ void __launch_bounds__(256) steqr_chunk_kernel(KernelArgs args) {
                 close_block(true);
                 M nz = 0;
                 static_for<N - 1>([&](auto I) {
-                    constexpr int p = decltype(I)::value;
-                    nz |= (e[p] != T(0)) ? ((M)1 << p) : (M)0;
+                    constexpr int p = N - 2 - decltype(I)::value;
+                    nz = nz + nz + ((e[p] != T(0)) ? (M)1 : (M)0);
                 });
                 info = popc((M)(nz & bits_below<M>(n - 1)));
                 info = info > 0 ? info : 1;
@@ -282,14 +317,16 @@ __global__ void __launch_bounds__(256) steqr_chunk_kernel(KernelArgs args) {
                 break;
             }
             ++jtot;
-            mu = lapack_shift(pick(d, m), pick(d, m - 1), pick(e, m - 1));
+            mu = lapack_shift(sd[m], sd[m - 1], se[m - 1]);
             sweep = true;
             break;
         }
         if (state == ST_DONE) break;
 
         // ------------------------------------------------------------ chase pass
-        T x = T(0), y = T(0);
+        // Running pair (x, y) and the previous cosine cp: the update
+        // e_{p+1} <- c_p e_{p+1} of step p is applied when step p+1 reads it.
+        T x = T(0), y = T(0), cp = T(1);
         static_for<N - 1>([&](auto I) {
             constexpr int p = decltype(I)::value;
             if (sweep & (p >= s) & (p < m)) {
@@ -301,7 +338,7 @@ __global__ void __launch_bounds__(256) steqr_chunk_kernel(KernelArgs args) {
                 T c, sn, rr;
                 lartg(xin, yin, c, sn, rr);
                 if constexpr (p > 0) e[p - 1] = first ? e[p - 1] : rr;
-                const T a = d[p], b = e[p], dd = d[p + 1];
+                const T a = d[p], b = cp * e[p], dd = d[p + 1];
                 const T pp = c * a + sn * b;
                 const T qq = c * b + sn * dd;
                 const T an = pp * c + qq * sn;
@@ -309,12 +346,9 @@ __global__ void __launch_bounds__(256) steqr_chunk_kernel(KernelArgs args) {
                 d[p] = an;
                 e[p] = bn;
                 d[p + 1] = (a + dd) - an;  // trace of the 2x2 is invariant
-                if constexpr (p + 1 < N - 1) {
-                    const T g = e[p + 1];
-                    y = sn * g;  // new bulge
-                    e[p + 1] = (p + 1 < m) ? c * g : g;
-                }
+                if constexpr (p + 1 < N - 1) y = sn * e[p + 1];  // new bulge
                 x = bn;
+                cp = c;
                 if constexpr (WANTQ) {
                     static_for<R>([&](auto II) {
                         constexpr int i = decltype(II)::value;
@@ -325,17 +359,10 @@ __global__ void __launch_bounds__(256) steqr_chunk_kernel(KernelArgs args) {
                 }
             }
             if (jac & (p == jpos)) {
-                // analytic 2x2 [algo]: symmetric Schur rotation
-                // J = [[cs, sn], [-sn, cs]], J^T B J = diag
-                const T a = d[p], b = e[p], cc = d[p + 1];
-                const T tau = (cc - a) / (T(2) * b);
-                const T den = F::abs(tau) + F::sqrt(F::fma(tau, tau, T(1)));
-                T t = ((tau >= T(0)) ? T(1) : T(-1)) / den;
-                t = (b == T(0)) ? T(0) : t;
-                const T cs = T(1) / F::sqrt(F::fma(t, t, T(1)));
-                const T sj = t * cs;
-                d[p] = a - t * b;
-                d[p + 1] = cc + t * b;
+                T rt1, rt2, cs, sj;
+                sym2x2(d[p], e[p], d[p + 1], rt1, rt2, cs, sj);
+                d[p] = rt1;
+                d[p + 1] = rt2;
                 e[p] = T(0);
                 if constexpr (WANTQ) {
                     static_for<R>([&](auto II) {
@@ -347,38 +374,66 @@ __global__ void __launch_bounds__(256) steqr_chunk_kernel(KernelArgs args) {
                 }
             }
         });
+        publish();
         // a NaN shift turns [s, m] into NaN, a fixed point of every further
         // sweep: spend the rest of the budget at once (same final state)
         if (sweep & (mu != mu)) jtot = nmaxit;
     }
 
     // ---------------------------------------------------------------- sort
-    // rank[j] = #{k < n : (d_k, k) precedes (d_j, j)}; ascending, ties by
-    // index, NaN last [algo, sort paragraph]
-    int rank[N];
+    // rank_j = #{k < n : (d_k, k) precedes (d_j, j)}: ascending, ties by
+    // index, NaN last [algo, sort paragraph]. Lane r of a chunk ranks keys
+    // j = r, r+P, ... and shares the ranks through LDS.
     const bool sort_it = (args.do_sort != 0) & !failed;
-    static_for<N>([&](auto J) {
-        constexpr int j = decltype(J)::value;
-        const T dj = d[j];
+    auto rank_of = [&](T dj, int j) __attribute__((always_inline)) {
         const bool nanj = dj != dj;
         int rk = 0;
         static_for<N>([&](auto K) {
             constexpr int k = decltype(K)::value;
-            if constexpr (k != j) {
-                const T dk = d[k];
-                const bool before = (k < j) ? ((dk <= dj) | nanj) : ((dk < dj) | (nanj & (dk == dk)));
-                rk += ((k < n) & before) ? 1 : 0;
-            }
+            const T dk = d[k];
+            const bool before = (k < j) ? ((dk <= dj) | nanj) : ((dk < dj) | (nanj & (dk == dk)));
+            rk += ((k < n) & (k != j) & before) ? 1 : 0;
         });
-        rank[j] = sort_it ? rk : j;
-    });
+        return sort_it ? rk : j;
+    };
+    int rank[N];
+    T myd[RJ];
+    int myrank[RJ];
+    if constexpr (P == 1) {
+        static_for<N>([&](auto J) {
+            constexpr int j = decltype(J)::value;
+            rank[j] = rank_of(d[j], j);
+        });
+    } else {
+        static_for<RJ>([&](auto K) {
+            constexpr int k = decltype(K)::value;
+            const int j = r + k * P;
+            const int jc = j < N ? j : N - 1;
+            myd[k] = sd[jc];
+            myrank[k] = rank_of(myd[k], j);
+            if (j < N) srank[j] = myrank[k];
+        });
+        __builtin_amdgcn_wave_barrier();
+        static_for<N>([&](auto J) {
+            constexpr int j = decltype(J)::value;
+            rank[j] = srank[j];
+        });
+    }
 
     // ---------------------------------------------------------------- store
     if (live) {
-        static_for<N>([&](auto J) {
-            constexpr int j = decltype(J)::value;
-            if ((j < n) & ((j % P) == r)) glam[prob * n + rank[j]] = d[j];
-        });
+        if constexpr (P == 1) {
+            static_for<N>([&](auto J) {
+                constexpr int j = decltype(J)::value;
+                if (j < n) glam[prob * n + rank[j]] = d[j];
+            });
+        } else {
+            static_for<RJ>([&](auto K) {
+                constexpr int k = decltype(K)::value;
+                const int j = r + k * P;
+                if (j < n) glam[prob * n + myrank[k]] = myd[k];
+            });
+        }
         if constexpr (WANTQ) {
             const long qb = prob * (long)n * n;
             static_for<R>([&](auto II) {

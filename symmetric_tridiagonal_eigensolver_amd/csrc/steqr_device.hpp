@@ -46,6 +46,8 @@ struct Fp<float> {
     __device__ static __forceinline__ int frexp_exp(float x) { return __builtin_amdgcn_frexp_expf(x); }
     __device__ static __forceinline__ float ldexp(float x, int k) { return __builtin_amdgcn_ldexpf(x, k); }
     __device__ static __forceinline__ float rsq(float x) { return __builtin_amdgcn_rsqf(x); }
+    __device__ static __forceinline__ float rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+    __device__ static __forceinline__ float sqrt_fast(float x) { return __builtin_amdgcn_sqrtf(x); }
     __device__ static __forceinline__ float qnan() { return __builtin_nanf(""); }
     __device__ static __forceinline__ float abs(float x) { return __builtin_fabsf(x); }
     __device__ static __forceinline__ float sqrt(float x) { return __builtin_sqrtf(x); }
@@ -64,6 +66,14 @@ struct Fp<double> {
     __device__ static __forceinline__ int frexp_exp(double x) { return __builtin_amdgcn_frexp_exp(x); }
     __device__ static __forceinline__ double ldexp(double x, int k) { return __builtin_amdgcn_ldexp(x, k); }
     __device__ static __forceinline__ double rsq(double x) { return __builtin_amdgcn_rsq(x); }
+    // double reciprocal / square root: hardware seed refined by Newton steps
+    __device__ static __forceinline__ double rcp(double x) {
+        double y = __builtin_amdgcn_rcp(x);
+        y = __builtin_fma(__builtin_fma(-x, y, 1.0), y, y);
+        y = __builtin_fma(__builtin_fma(-x, y, 1.0), y, y);
+        return y;
+    }
+    __device__ static __forceinline__ double sqrt_fast(double x) { return __builtin_sqrt(x); }
     __device__ static __forceinline__ double qnan() { return __builtin_nan(""); }
     __device__ static __forceinline__ double abs(double x) { return __builtin_fabs(x); }
     __device__ static __forceinline__ double sqrt(double x) { return __builtin_sqrt(x); }
@@ -125,14 +135,17 @@ __device__ __forceinline__ bool negligible(T e, T d1, T d2) {
 // G^T (f, g)^T = (r, 0)^T, r with the sign of f (so c >= 0).
 // The norm is formed as a hardware reciprocal square root refined by Newton
 // steps [cta, Givens rotation paragraph]; instead of a range guard with a
-// slow path, f and g are first scaled by an exact power of two (frexp /
-// ldexp of the larger magnitude) so that f^2 + g^2 lies in [1/4, 2) and can
-// neither overflow nor underflow. g = 0 gives (1, 0, f) through a final
-// select [cta, Givens rotation paragraph]. NaN inputs give NaN outputs.
+// slow path, f and g are first scaled by an exact power of two (2^-k with k
+// the exponent of |f| + |g|, which lies within a factor 2 of max(|f|,|g|))
+// so that f^2 + g^2 lies in [1/16, 1] and can neither overflow nor
+// underflow. g = 0 gives (1, 0, f) through a final select [cta, Givens
+// rotation paragraph]. NaN inputs give NaN outputs. |f| + |g| cannot
+// overflow for the block-scaled values the solver passes (|f|, |g| stay
+// within a small multiple of ssfmax).
 template <typename T>
 __device__ __forceinline__ void lartg(T f, T g, T& c, T& s, T& r) {
     using F = Fp<T>;
-    const T mx = F::max(F::abs(f), F::abs(g));
+    const T mx = F::abs(f) + F::abs(g);
     const int ex = F::frexp_exp(mx);
     const T fs = F::ldexp(f, -ex);
     const T gs = F::ldexp(g, -ex);
@@ -155,13 +168,41 @@ __device__ __forceinline__ void lartg(T f, T g, T& c, T& s, T& r) {
 // LAPACK-form shift [algo, shift section]: the eigenvalue of the 2x2 block
 // [[d2, e1], [e1, d1]] nearest the endpoint d1,
 //   g = (d2 - d1)/(2 e1), r = sqrt(g^2 + 1), mu = d1 - e1/(g + copysign(r, g)).
-// If g^2 overflows, r = inf and mu = d1, which is harmless.
+// The shift only steers convergence, so hardware reciprocal and square
+// root (about 1 ulp) replace the correctly rounded forms. If g^2 overflows
+// (or e1 = 0 makes g infinite), r = inf and mu = d1, which is harmless.
 template <typename T>
 __device__ __forceinline__ T lapack_shift(T d1, T d2, T e1) {
     using F = Fp<T>;
-    const T g = (d2 - d1) / (T(2) * e1);
-    const T r = F::sqrt(F::fma(g, g, T(1)));
-    return d1 - e1 / (g + F::copysign(r, g));
+    const T g = (d2 - d1) * F::rcp(T(2) * e1);
+    const T r = F::sqrt_fast(F::fma(g, g, T(1)));
+    return d1 - e1 * F::rcp(g + F::copysign(r, g));
+}
+
+// Analytic 2x2 solve [algo, "A deflated block of size 2" paragraph]: for
+// B = [[a, b], [b, c]] the symmetric Schur rotation J = [[cs, sn], [-sn, cs]]
+// with J^T B J = diag(a - t b, c + t b), tau = (c - a)/(2b),
+// t = sign(tau)/(|tau| + sqrt(1 + tau^2)) (sign(0) = +1), cs = 1/sqrt(1+t^2),
+// sn = t cs (Golub and Van Loan, symmetric Schur decomposition). b = 0
+// gives the identity. Hardware reciprocal / square root as in the shift.
+template <typename T>
+__device__ __forceinline__ void sym2x2(T a, T b, T c, T& rt1, T& rt2, T& cs, T& sn) {
+    using F = Fp<T>;
+    const T tau = (c - a) * F::rcp(T(2) * b);
+    const T den = F::abs(tau) + F::sqrt_fast(F::fma(tau, tau, T(1)));
+    T t = F::copysign(F::rcp(den), tau >= T(0) ? T(1) : T(-1));
+    t = (b == T(0)) ? T(0) : t;
+    T y = F::rsq(F::fma(t, t, T(1)));
+#pragma unroll
+    for (int k = 0; k < F::newton_steps; ++k) {
+        const T w = F::fma(t, t, T(1));
+        const T h = w * y;
+        y = F::fma(y * F::fma(-h, y, T(1)), T(0.5), y);
+    }
+    cs = y;
+    sn = t * y;
+    rt1 = a - t * b;
+    rt2 = c + t * b;
 }
 
 }  // namespace steqr

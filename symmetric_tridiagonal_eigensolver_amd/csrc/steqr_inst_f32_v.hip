@@ -3,11 +3,11 @@
 
 namespace steqr {
 
-#define E(N, P) {0, N, P, 1, &launch_chunk<float, N, P, true>}
+#define E(N, P) STEQR_ENTRY(0, float, N, P, 1)
 static const Entry kEntries[] = {
-    E(4, 4),  E(4, 2),   E(4, 1),
-    E(8, 8),  E(8, 4),   E(8, 2),
-    E(16, 16), E(16, 8), E(16, 4),
+    E(4, 4), E(4, 2), E(4, 1),
+    E(8, 8), E(8, 4), E(8, 2), E(8, 1),
+    E(16, 16), E(16, 8), E(16, 4), E(16, 2),
     E(32, 32), E(32, 16), E(32, 8),
 };
 #undef E

@@ -3,11 +3,11 @@
 
 namespace steqr {
 
-#define E(N, P) {1, N, P, 1, &launch_chunk<double, N, P, true>}
+#define E(N, P) STEQR_ENTRY(1, double, N, P, 1)
 static const Entry kEntries[] = {
-    E(4, 4),   E(4, 2),
-    E(8, 8),   E(8, 4),
-    E(16, 16), E(16, 8),
+    E(4, 4), E(4, 2),
+    E(8, 8), E(8, 4), E(8, 2),
+    E(16, 16), E(16, 8), E(16, 4),
     E(32, 32), E(32, 16),
 };
 #undef E

@@ -12,18 +12,24 @@ namespace steqr {
 typedef hipError_t (*LaunchFn)(const KernelArgs& args, int grid, int block, hipStream_t stream);
 
 struct Entry {
-    int dtype;  // 0 = float, 1 = double
-    int N;      // compile-time (padded) order
-    int P;      // lanes per problem
-    int jobz;   // 0 = values, 1 = values and vectors
+    int dtype;             // 0 = float, 1 = double
+    int N;                 // compile-time (padded) order
+    int P;                 // lanes per problem
+    int jobz;              // 0 = values, 1 = values and vectors
+    int lds_per_wave;      // bytes of LDS each wavefront uses
     LaunchFn fn;
 };
 
 template <typename T, int N, int P, bool WANTQ>
 hipError_t launch_chunk(const KernelArgs& args, int grid, int block, hipStream_t stream) {
-    hipLaunchKernelGGL((steqr_chunk_kernel<T, N, P, WANTQ>), dim3(grid), dim3(block), 0, stream, args);
+    const size_t lds = (size_t)(block / 64) * Smem<T, N, P>::bytes_per_wave;
+    hipLaunchKernelGGL((steqr_chunk_kernel<T, N, P, WANTQ>), dim3(grid), dim3(block), lds, stream,
+                       args);
     return hipGetLastError();
 }
+
+#define STEQR_ENTRY(DT, T, N, P, Q) \
+    { DT, N, P, Q, (int)Smem<T, N, P>::bytes_per_wave, &launch_chunk<T, N, P, (Q) != 0> }
 
 struct Table {
     const Entry* entries;

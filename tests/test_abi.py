@@ -98,8 +98,16 @@ def test_argument_errors(st, args, rc):
 
 
 def test_bad_params(st):
+    # every call here is rejected by argument validation before any launch
+    # (the pointers are not device memory)
     L = st.lib()
     for prm in (st.make_params(lanes_per_problem=3), st.make_params(lanes_per_problem=128),
-                st.make_params(waves_per_block=3), st.make_params(lanes_per_problem=2)):
+                st.make_params(waves_per_block=3), st.make_params(lanes_per_problem=-4)):
         got = L.steqr_batched_ex(8, 8, 8, 8, 16, 10, 1, 0, None, None, ctypes.byref(prm))
         assert got == -10
+
+
+def test_uninstantiated_lanes_rejected_by_query(st):
+    with pytest.raises(st.SteqrError) as ex:
+        st.steqr_query(16, 10, 1, 0, st.make_params(lanes_per_problem=64))
+    assert ex.value.rc == -10

@@ -80,6 +80,10 @@ LANE_CASES = [
     (np.float64, 4, True, 2), (np.float64, 8, True, 4), (np.float64, 16, True, 8),
     (np.float64, 32, True, 16), (np.float64, 4, False, 1), (np.float64, 8, False, 1),
     (np.float64, 16, False, 1), (np.float64, 32, False, 1),
+    (np.float32, 16, True, 2), (np.float32, 8, True, 1), (np.float32, 8, False, 2),
+    (np.float32, 16, False, 2), (np.float32, 32, False, 2), (np.float64, 16, True, 4),
+    (np.float64, 8, True, 2), (np.float64, 4, True, 4), (np.float64, 8, False, 2),
+    (np.float64, 16, False, 2), (np.float64, 32, False, 2), (np.float64, 32, True, 32),
 ]
 
 
