@@ -12,7 +12,7 @@ using steqr::Entry;
 using steqr::Table;
 
 // Compile-time orders the build provides, smallest first.
-constexpr int kOrders[] = {4, 8, 16, 32};
+constexpr int kOrders[] = {4, 8, 16, 32, 64};
 
 int padded_order(int n) {
     for (int N : kOrders)
@@ -25,10 +25,18 @@ int padded_order(int n) {
 int default_lanes(int dtype, int N, int jobz) {
     (void)dtype;
     (void)jobz;
-    return N;
+    return N > 64 ? 64 : N;
 }
 
 const Entry* find_entry(int dtype, int N, int P, int jobz) {
+    if (N == 64) {
+        const Table w = steqr::table_wave();
+        for (int i = 0; i < w.count; ++i) {
+            const Entry& x = w.entries[i];
+            if (x.dtype == dtype && x.N == N && x.P == P && x.jobz == jobz) return &x;
+        }
+        return nullptr;
+    }
     Table t;
     if (dtype == STEQR_F32)
         t = jobz ? steqr::table_f32_v() : steqr::table_f32_n();

@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include "steqr_chunk.hpp"
+#include "steqr_wave.hpp"
 
 namespace steqr {
 
@@ -28,6 +29,18 @@ hipError_t launch_chunk(const KernelArgs& args, int grid, int block, hipStream_t
     return hipGetLastError();
 }
 
+// One problem per wavefront (P = 64).
+template <typename T, int N, bool WANTQ>
+hipError_t launch_wave(const KernelArgs& args, int grid, int block, hipStream_t stream) {
+    const size_t lds = (size_t)(block / 64) * WaveSmem<T, N>::bytes_per_wave;
+    hipLaunchKernelGGL((steqr_wave_kernel<T, N, WANTQ>), dim3(grid), dim3(block), lds, stream,
+                       args);
+    return hipGetLastError();
+}
+
+#define STEQR_WAVE_ENTRY(DT, T, N, Q) \
+    { DT, N, 64, Q, (int)WaveSmem<T, N>::bytes_per_wave, &launch_wave<T, N, (Q) != 0> }
+
 #define STEQR_ENTRY(DT, T, N, P, Q) \
     { DT, N, P, Q, (int)Smem<T, N, P>::bytes_per_wave, &launch_chunk<T, N, P, (Q) != 0> }
 
@@ -40,5 +53,6 @@ Table table_f32_v();
 Table table_f32_n();
 Table table_f64_v();
 Table table_f64_n();
+Table table_wave();
 
 }  // namespace steqr

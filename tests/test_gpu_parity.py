@@ -20,8 +20,6 @@ def _gpu():
 
 
 def _case(w, jobz, batch):
-    if w.n > 32:
-        pytest.skip("order-64 kernel (one problem per wavefront) not built yet")
     print("case %s jobz=%s batch=%d" % (w.name, jobz, batch), flush=True)
 
 
@@ -83,6 +81,8 @@ LANE_CASES = [
     (np.float32, 16, True, 2), (np.float32, 8, True, 1), (np.float32, 8, False, 2),
     (np.float32, 16, False, 2), (np.float32, 32, False, 2), (np.float64, 16, True, 4),
     (np.float64, 8, True, 2), (np.float64, 4, True, 4), (np.float64, 8, False, 2),
+    (np.float32, 64, True, 64), (np.float32, 64, False, 64), (np.float64, 64, False, 64),
+    (np.float64, 64, True, 64), (np.float64, 48, True, 64), (np.float32, 33, True, 64),
     (np.float64, 16, False, 2), (np.float64, 32, False, 2), (np.float64, 32, True, 32),
 ]
 
@@ -99,8 +99,8 @@ def test_lanes_per_problem_variants(dt, n, jobz, lanes):
 
 @pytest.mark.parametrize("dt", [np.float32, np.float64], ids=["f32", "f64"])
 @pytest.mark.parametrize("jobz", [True, False], ids=["V", "N"])
-def test_every_order_up_to_32(dt, jobz):
-    for n in range(1, 33):
+def test_every_order_up_to_64(dt, jobz):
+    for n in range(1, 65):
         d, e = W.random_batch(n, 67, dt, salt=n)
         print("order", n, flush=True)
         g = run_gpu(d, e, jobz)
@@ -110,7 +110,7 @@ def test_every_order_up_to_32(dt, jobz):
 
 @pytest.mark.parametrize("kind", range(5), ids=W.EDGE_NAMES)
 @pytest.mark.parametrize("dt", [np.float32, np.float64], ids=["f32", "f64"])
-@pytest.mark.parametrize("n", [3, 4, 16, 32])
+@pytest.mark.parametrize("n", [3, 4, 16, 32, 40, 64])
 def test_edge_items(kind, dt, n):
     d, e = W.edge_batch(kind, n, 130, dt)
     print("edge", W.EDGE_NAMES[kind], dt.__name__, n, flush=True)
