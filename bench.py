@@ -183,6 +183,33 @@ def main() -> int:
     ms = start.elapsed_time(stop) / args.steps  # mean kernel duration (back-to-back launches)
     sec = ms / 1e3
 
+    # secondary timing at the lanes-per-problem the workload list names
+    named = None
+    if args.lanes == 0 and plan["lanes_per_problem"] != w.lanes and not args.replicate:
+        prm_n = st.make_params(lanes_per_problem=w.lanes, waves_per_block=args.waves)
+        try:
+            st.steqr_query(n, nb, int(jobz), st.dtype_code(td.dtype), prm_n)
+        except st.SteqrError:
+            prm_n = None
+        if prm_n is not None:
+            def step_n():
+                rc = st.steqr_batched_ex(td, te, lam, Q, n, nb, int(jobz),
+                                         st.dtype_code(td.dtype), stream, info, prm_n)
+                if rc != 0:
+                    raise st.SteqrError(rc, "steqr_batched_ex")
+            for _ in range(3):
+                step_n()
+            k = max(10, args.steps // 4)
+            torch.cuda.synchronize()
+            start.record(stream)
+            for _ in range(k):
+                step_n()
+            stop.record(stream)
+            torch.cuda.synchronize()
+            ms_n = start.elapsed_time(stop) / k
+            named = {"lanes_per_problem": w.lanes, "ms_per_step": ms_n,
+                     "value": nb / (ms_n / 1e3), "steps": k}
+
     cpu = None
     flops = None
     if not args.no_cpu:
@@ -194,7 +221,11 @@ def main() -> int:
     roof = None
     if flops is not None:
         ach = flops / sec / 1e12
-        roof = {"bound": "alu", "achieved": ach, "peak": peak, "unit": "TFLOP/s",
+        roof = {"kernel": "steqr_%s_kernel<%s, N=%d, P=%d, %s>"
+                          % ("wave" if plan["lanes_per_problem"] == 64 else "chunk",
+                             "float" if dtype == "f32" else "double", plan["padded_n"],
+                             plan["lanes_per_problem"], "V" if jobz else "N"),
+                "bound": "alu", "achieved": ach, "peak": peak, "unit": "TFLOP/s",
                 "frac": ach / peak,
                 "traffic": traffic_from_profiles(w.name, jobz),
                 "algorithmic_flops_per_launch": flops,
@@ -223,6 +254,7 @@ def main() -> int:
                               else ("90% iid N(0,1) + 10% edge items" if w.edge_mix
                                     else "d,e iid N(0,1)")) + ", seed 1234"},
         "roofline": roof,
+        "at_named_lanes": named,
         "hbm": {"algorithmic_bytes_per_launch": bpm * nb,
                 "achieved_GBs": bpm * nb / sec / 1e9, "peak_GBs": HBM_PEAK_GBS},
         "cpu_baseline": cpu,

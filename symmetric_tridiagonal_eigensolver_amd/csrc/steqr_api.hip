@@ -20,12 +20,24 @@ int padded_order(int n) {
     return -1;
 }
 
-// Default lanes per problem: the spec mapping, one row of Q per lane
-// (P = N) with values and vectors, and the same P for values only.
+// Default lanes per problem P, measured on MI355X at the benchmark batches
+// (32,768-65,536 matrices). With eigenvectors, fewer lanes per problem
+// means more problems per wavefront and less repeated chase arithmetic, at
+// the price of R = N/P rows of Q per lane in VGPRs; the best balance is
+// four to eight rows per lane while the wavefront still fits two waves per
+// SIMD. Values only keep one lane per problem unless the batch would leave
+// SIMDs idle (n = 32 keeps two lanes). Orders 33..64 run one problem per
+// wavefront.
 int default_lanes(int dtype, int N, int jobz) {
-    (void)dtype;
-    (void)jobz;
-    return N > 64 ? 64 : N;
+    if (N >= 64) return 64;
+    if (jobz) {
+        if (N == 4) return 4;
+        if (N == 8) return dtype == STEQR_F32 ? 2 : 4;
+        if (N == 16) return 4;
+        return 16;  // N == 32
+    }
+    if (N == 32 && dtype == STEQR_F32) return 2;
+    return 1;
 }
 
 const Entry* find_entry(int dtype, int N, int P, int jobz) {

@@ -56,9 +56,9 @@ def test_version(st):
 
 
 @pytest.mark.parametrize("n,jobz,dtype,N,P", [
-    (1, 1, 0, 4, 4), (4, 1, 0, 4, 4), (5, 1, 0, 8, 8), (8, 0, 0, 8, 8), (12, 1, 1, 16, 16),
-    (16, 1, 0, 16, 16), (17, 1, 0, 32, 32), (32, 0, 1, 32, 32), (33, 1, 1, 64, 64),
-    (64, 1, 1, 64, 64), (64, 0, 0, 64, 64)])
+    (1, 1, 0, 4, 4), (4, 1, 0, 4, 4), (5, 1, 0, 8, 2), (8, 0, 0, 8, 1), (12, 1, 1, 16, 4),
+    (16, 1, 0, 16, 4), (17, 1, 0, 32, 16), (32, 0, 1, 32, 1), (32, 0, 0, 32, 2),
+    (33, 1, 1, 64, 64), (64, 1, 1, 64, 64), (64, 0, 0, 64, 64)])
 def test_query_default_plan(st, n, jobz, dtype, N, P):
     q = st.steqr_query(n, 1000, jobz, dtype)
     assert q["padded_n"] == N and q["lanes_per_problem"] == P
