@@ -107,6 +107,8 @@ def main() -> int:
     ap.add_argument("--jobz", default="V", choices=["V", "N"])
     ap.add_argument("--lanes", type=int, default=0, help="lanes per problem (0 = default)")
     ap.add_argument("--waves", type=int, default=0, help="waves per workgroup (0 = default)")
+    ap.add_argument("--band", type=int, default=0,
+                    help="band storage: 0 default, 1 registers, 2 LDS")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--replicate", action="store_true",
                     help="lockstep-ideal batch: every chunk of a wavefront holds the same "
@@ -143,7 +145,8 @@ def main() -> int:
 
     w = W.WORKLOADS[args.workload]
     jobz = args.jobz == "V"
-    prm0 = st.make_params(lanes_per_problem=args.lanes, waves_per_block=args.waves)
+    prm0 = st.make_params(lanes_per_problem=args.lanes, waves_per_block=args.waves,
+                          band_storage=args.band)
     lanes0 = st.steqr_query(w.n, w.batch, int(jobz), 0 if w.dtype == "f32" else 1,
                             prm0)["lanes_per_problem"]
     d, e = W.make_batch(w, replicate=(64 // lanes0) if args.replicate else 1)
@@ -154,7 +157,8 @@ def main() -> int:
     lam = torch.empty_like(td)
     Q = torch.empty((nb, n, n), dtype=td.dtype, device=dev) if jobz else None
     info = torch.empty((nb,), dtype=torch.int32, device=dev)
-    prm = st.make_params(lanes_per_problem=args.lanes, waves_per_block=args.waves)
+    prm = st.make_params(lanes_per_problem=args.lanes, waves_per_block=args.waves,
+                         band_storage=args.band)
     plan = st.steqr_query(n, nb, int(jobz), st.dtype_code(td.dtype), prm)
     stream = torch.cuda.current_stream()
 
@@ -186,7 +190,8 @@ def main() -> int:
     # secondary timing at the lanes-per-problem the workload list names
     named = None
     if args.lanes == 0 and plan["lanes_per_problem"] != w.lanes and not args.replicate:
-        prm_n = st.make_params(lanes_per_problem=w.lanes, waves_per_block=args.waves)
+        prm_n = st.make_params(lanes_per_problem=w.lanes, waves_per_block=args.waves,
+                               band_storage=1 if w.n <= 32 else 2)
         try:
             st.steqr_query(n, nb, int(jobz), st.dtype_code(td.dtype), prm_n)
         except st.SteqrError:
@@ -222,7 +227,8 @@ def main() -> int:
     if flops is not None:
         ach = flops / sec / 1e12
         roof = {"kernel": "steqr_%s_kernel<%s, N=%d, P=%d, %s>"
-                          % ("wave" if plan["lanes_per_problem"] == 64 else "chunk",
+                          % ("wave" if plan["lanes_per_problem"] == 64 else
+                             ("chunkl" if plan["band_storage"] == 2 else "chunk"),
                              "float" if dtype == "f32" else "double", plan["padded_n"],
                              plan["lanes_per_problem"], "V" if jobz else "N"),
                 "bound": "alu", "achieved": ach, "peak": peak, "unit": "TFLOP/s",
@@ -248,6 +254,7 @@ def main() -> int:
         "config": {"workload": w.name, "n": n, "batch": nb, "jobz": "V" if jobz else "N",
                    "precision": dtype, "lanes_per_problem": plan["lanes_per_problem"],
                    "rows_per_lane": plan["rows_per_lane"], "padded_n": plan["padded_n"],
+                   "band_storage": "LDS" if plan["band_storage"] == 2 else "registers",
                    "waves_per_block": plan["waves_per_block"],
                    "workgroups": plan["workgroups"],
                    "inputs": ("replicated per wavefront (lockstep ideal)" if args.replicate

@@ -66,9 +66,14 @@ typedef struct steqr_params {
      * tuned default; otherwise a power of two the build provides for this
      * (dtype, n, jobz); steqr_query() lists it. */
     int lanes_per_problem;
-    /* Wavefronts per workgroup (1, 2, 4 or 8); 0 = default. Launch shape
+    /* Wavefronts per workgroup (1, 2 or 4); 0 = default. Launch shape
      * only: the arithmetic and results do not depend on it. */
     int waves_per_block;
+    /* Where a chunked kernel keeps the band d, e during the solve:
+     * 0 = tuned default, 1 = replicated in every lane's registers,
+     * 2 = shared in LDS (frees registers for more rows of Q per lane).
+     * Orders above 32 always use LDS. */
+    int band_storage;
 } steqr_params;
 
 /* Eigenvalues (jobz = STEQR_N) or eigenpairs (jobz = STEQR_V) of a batch of
@@ -92,12 +97,13 @@ int steqr_batched_ex(const void *d, const void *e, void *lambda, void *Q,
 
 /* Describe the launch steqr_batched_ex would make, without launching:
  * padded order (the compile-time order the kernel runs at, >= n), lanes per
- * problem P, rows of Q held per lane, wavefronts per workgroup and
- * workgroups for `batch` matrices. Returns 0 or the same negative codes as
- * steqr_batched_ex (-5/-7/-8/-10). Any output pointer may be NULL. */
+ * problem P, rows of Q held per lane, wavefronts per workgroup, workgroups
+ * for `batch` matrices and band storage (1 registers, 2 LDS). Returns 0 or
+ * the same negative codes as steqr_batched_ex (-5/-7/-8/-10). Any output
+ * pointer may be NULL. */
 int steqr_query(int n, int batch, int jobz, int dtype, const steqr_params *params,
                 int *padded_n, int *lanes_per_problem, int *rows_per_lane,
-                int *waves_per_block, int *workgroups);
+                int *waves_per_block, int *workgroups, int *band_storage);
 
 /* Library version string, e.g. "steqr-mi355x 0.1.0 gfx950". */
 const char *steqr_version(void);

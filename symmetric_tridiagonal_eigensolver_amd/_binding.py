@@ -22,7 +22,8 @@ class steqr_params(ct.Structure):
     _fields_ = [("max_sweeps_per_n", ct.c_int),
                 ("no_sort", ct.c_int),
                 ("lanes_per_problem", ct.c_int),
-                ("waves_per_block", ct.c_int)]
+                ("waves_per_block", ct.c_int),
+                ("band_storage", ct.c_int)]
 
 
 class SteqrError(RuntimeError):
@@ -44,7 +45,7 @@ _lib.steqr_batched_ex.restype = _i
 _lib.steqr_batched_ex.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp,
                                   ct.POINTER(steqr_params)]
 _lib.steqr_query.restype = _i
-_lib.steqr_query.argtypes = [_i, _i, _i, _i, ct.POINTER(steqr_params)] + [ct.POINTER(_i)] * 5
+_lib.steqr_query.argtypes = [_i, _i, _i, _i, ct.POINTER(steqr_params)] + [ct.POINTER(_i)] * 6
 _lib.steqr_version.restype = ct.c_char_p
 _lib.steqr_version.argtypes = []
 
@@ -60,9 +61,9 @@ def version() -> str:
 
 
 def make_params(max_sweeps_per_n: int = 0, sort: bool = True, lanes_per_problem: int = 0,
-                waves_per_block: int = 0) -> steqr_params:
+                waves_per_block: int = 0, band_storage: int = 0) -> steqr_params:
     return steqr_params(int(max_sweeps_per_n), 0 if sort else 1, int(lanes_per_problem),
-                        int(waves_per_block))
+                        int(waves_per_block), int(band_storage))
 
 
 def _ptr(x) -> Optional[int]:
@@ -98,13 +99,14 @@ def steqr_batched_ex(d, e, lam, Q, n: int, batch: int, jobz: int, dtype: int, st
 
 def steqr_query(n: int, batch: int, jobz: int, dtype: int,
                 params: Optional[steqr_params] = None) -> dict:
-    outs = [ct.c_int(0) for _ in range(5)]
+    outs = [ct.c_int(0) for _ in range(6)]
     rc = _lib.steqr_query(int(n), int(batch), int(jobz), int(dtype),
                           ct.byref(params) if params is not None else None,
                           *[ct.byref(o) for o in outs])
     if rc != 0:
         raise SteqrError(rc, "steqr_query")
-    keys = ("padded_n", "lanes_per_problem", "rows_per_lane", "waves_per_block", "workgroups")
+    keys = ("padded_n", "lanes_per_problem", "rows_per_lane", "waves_per_block", "workgroups",
+            "band_storage")
     return dict(zip(keys, (o.value for o in outs)))
 
 
@@ -119,7 +121,7 @@ def dtype_code(tdtype) -> int:
 
 def solve(d, e, jobz: bool = True, *, info: bool = False, sort: bool = True,
           max_sweeps_per_n: int = 0, lanes_per_problem: int = 0, waves_per_block: int = 0,
-          stream=None, out: Optional[Tuple] = None):
+          band_storage: int = 0, stream=None, out: Optional[Tuple] = None):
     """Solve a batch held in device tensors d (batch, n), e (batch, n-1).
 
     Returns (lam, Q or None[, info]) as device tensors; the work is enqueued
@@ -139,7 +141,7 @@ def solve(d, e, jobz: bool = True, *, info: bool = False, sort: bool = True,
         lam = torch.empty_like(d)
         Q = torch.empty((batch, n, n), dtype=d.dtype, device=d.device) if jobz else None
         inf = torch.empty((batch,), dtype=torch.int32, device=d.device) if info else None
-    prm = make_params(max_sweeps_per_n, sort, lanes_per_problem, waves_per_block)
+    prm = make_params(max_sweeps_per_n, sort, lanes_per_problem, waves_per_block, band_storage)
     rc = steqr_batched_ex(d, e, lam, Q, n, batch, STEQR_V if jobz else STEQR_N,
                           dtype_code(d.dtype), stream, inf, prm)
     if rc != 0:

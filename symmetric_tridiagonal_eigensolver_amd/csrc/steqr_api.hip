@@ -28,43 +28,53 @@ int padded_order(int n) {
 // SIMD. Values only keep one lane per problem unless the batch would leave
 // SIMDs idle (n = 32 keeps two lanes). Orders 33..64 run one problem per
 // wavefront.
-int default_lanes(int dtype, int N, int jobz) {
+int default_lanes(int dtype, int N, int jobz, int band) {
     if (N >= 64) return 64;
     if (jobz) {
         if (N == 4) return 4;
         if (N == 8) return dtype == STEQR_F32 ? 2 : 4;
-        if (N == 16) return 4;
-        return 16;  // N == 32
+        if (N == 16) return band == 2 ? 8 : 4;
+        return band == 2 ? 8 : 16;  // N == 32
     }
     if (N == 32 && dtype == STEQR_F32) return 2;
     return 1;
 }
 
-const Entry* find_entry(int dtype, int N, int P, int jobz) {
-    if (N == 64) {
-        const Table w = steqr::table_wave();
-        for (int i = 0; i < w.count; ++i) {
-            const Entry& x = w.entries[i];
-            if (x.dtype == dtype && x.N == N && x.P == P && x.jobz == jobz) return &x;
-        }
-        return nullptr;
+const Entry* search(const Table& t, int dtype, int N, int P, int jobz, int band) {
+    for (int i = 0; i < t.count; ++i) {
+        const Entry& x = t.entries[i];
+        if (x.dtype == dtype && x.N == N && x.P == P && x.jobz == jobz && x.band == band) return &x;
+    }
+    return nullptr;
+}
+
+const Entry* find_entry(int dtype, int N, int P, int jobz, int band) {
+    if (N == 64) return band == 2 ? search(steqr::table_wave(), dtype, N, P, jobz, band) : nullptr;
+    if (band == 2) {
+        const Table t = dtype == STEQR_F32 ? steqr::table_lds_f32() : steqr::table_lds_f64();
+        return search(t, dtype, N, P, jobz, band);
     }
     Table t;
     if (dtype == STEQR_F32)
         t = jobz ? steqr::table_f32_v() : steqr::table_f32_n();
     else
         t = jobz ? steqr::table_f64_v() : steqr::table_f64_n();
-    for (int i = 0; i < t.count; ++i) {
-        const Entry& x = t.entries[i];
-        if (x.dtype == dtype && x.N == N && x.P == P && x.jobz == jobz) return &x;
-    }
-    return nullptr;
+    return search(t, dtype, N, P, jobz, band);
 }
 
 struct Plan {
     const Entry* entry;
-    int N, P, R, waves, grid;
+    int N, P, R, waves, grid, band;
 };
+
+// Default band storage (measured): LDS for orders above 32 (one problem per
+// wavefront) and, with eigenvectors, wherever the registers are better
+// spent on rows of Q: order 32, and order 16 in double precision.
+int default_band(int dtype, int N, int jobz) {
+    if (N >= 64) return 2;
+    if (jobz && (N == 32 || (N == 16 && dtype == STEQR_F64))) return 2;
+    return 1;
+}
 
 int plan_launch(int n, int batch, int jobz, int dtype, const steqr_params* prm, Plan* out) {
     if (n < 0 || n > STEQR_MAX_N) return -5;
@@ -73,7 +83,10 @@ int plan_launch(int n, int batch, int jobz, int dtype, const steqr_params* prm, 
     if (dtype != STEQR_F32 && dtype != STEQR_F64) return -8;
     int waves = 4;
     int P = 0;
+    int band = 0;
     if (prm) {
+        band = prm->band_storage;
+        if (band < 0 || band > 2) return -10;
         if (prm->waves_per_block != 0) {
             if (prm->waves_per_block != 1 && prm->waves_per_block != 2 && prm->waves_per_block != 4)
                 return -10;
@@ -91,8 +104,9 @@ int plan_launch(int n, int batch, int jobz, int dtype, const steqr_params* prm, 
     }
     const int N = padded_order(n < 2 ? 2 : n);
     if (N < 0) return -5;  // order not provided by this build
-    if (P == 0) P = default_lanes(dtype, N, jobz);
-    const Entry* ent = find_entry(dtype, N, P, jobz);
+    if (band == 0 || N >= 64) band = default_band(dtype, N, jobz);
+    if (P == 0) P = default_lanes(dtype, N, jobz, band);
+    const Entry* ent = find_entry(dtype, N, P, jobz, band);
     if (!ent) return -10;
     // keep a workgroup's LDS within 64 KiB
     while (waves > 1 && (long)waves * ent->lds_per_wave > 65536) waves /= 2;
@@ -102,6 +116,7 @@ int plan_launch(int n, int batch, int jobz, int dtype, const steqr_params* prm, 
     p.N = N;
     p.P = P;
     p.R = jobz ? (N + P - 1) / P : 0;
+    p.band = band;
     p.grid = batch > 0 ? (int)(((long)batch + per_block - 1) / per_block) : 0;
     *out = p;
     return 0;
@@ -111,7 +126,7 @@ int plan_launch(int n, int batch, int jobz, int dtype, const steqr_params* prm, 
 
 extern "C" int steqr_query(int n, int batch, int jobz, int dtype, const steqr_params* params,
                            int* padded_n, int* lanes_per_problem, int* rows_per_lane,
-                           int* waves_per_block, int* workgroups) {
+                           int* waves_per_block, int* workgroups, int* band_storage) {
     Plan p;
     const int rc = plan_launch(n, batch, jobz, dtype, params, &p);
     if (rc != 0) return rc;
@@ -120,6 +135,7 @@ extern "C" int steqr_query(int n, int batch, int jobz, int dtype, const steqr_pa
     if (rows_per_lane) *rows_per_lane = p.R;
     if (waves_per_block) *waves_per_block = p.waves;
     if (workgroups) *workgroups = p.grid;
+    if (band_storage) *band_storage = p.band;
     return 0;
 }
 

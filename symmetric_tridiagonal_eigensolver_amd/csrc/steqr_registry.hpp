@@ -7,6 +7,7 @@
 
 #include "steqr_chunk.hpp"
 #include "steqr_wave.hpp"
+#include "steqr_chunkl.hpp"
 
 namespace steqr {
 
@@ -17,6 +18,7 @@ struct Entry {
     int N;                 // compile-time (padded) order
     int P;                 // lanes per problem
     int jobz;              // 0 = values, 1 = values and vectors
+    int band;              // 1 = band replicated in VGPRs, 2 = band in LDS
     int lds_per_wave;      // bytes of LDS each wavefront uses
     LaunchFn fn;
 };
@@ -39,10 +41,22 @@ hipError_t launch_wave(const KernelArgs& args, int grid, int block, hipStream_t 
 }
 
 #define STEQR_WAVE_ENTRY(DT, T, N, Q) \
-    { DT, N, 64, Q, (int)WaveSmem<T, N>::bytes_per_wave, &launch_wave<T, N, (Q) != 0> }
+    { DT, N, 64, Q, 2, (int)WaveSmem<T, N>::bytes_per_wave, &launch_wave<T, N, (Q) != 0> }
+
+// Chunked, band in LDS.
+template <typename T, int N, int P, bool WANTQ>
+hipError_t launch_chunkl(const KernelArgs& args, int grid, int block, hipStream_t stream) {
+    const size_t lds = (size_t)(block / 64) * SmemL<T, N, P>::bytes_per_wave;
+    hipLaunchKernelGGL((steqr_chunkl_kernel<T, N, P, WANTQ>), dim3(grid), dim3(block), lds, stream,
+                       args);
+    return hipGetLastError();
+}
+
+#define STEQR_LENTRY(DT, T, N, P, Q) \
+    { DT, N, P, Q, 2, (int)SmemL<T, N, P>::bytes_per_wave, &launch_chunkl<T, N, P, (Q) != 0> }
 
 #define STEQR_ENTRY(DT, T, N, P, Q) \
-    { DT, N, P, Q, (int)Smem<T, N, P>::bytes_per_wave, &launch_chunk<T, N, P, (Q) != 0> }
+    { DT, N, P, Q, 1, (int)Smem<T, N, P>::bytes_per_wave, &launch_chunk<T, N, P, (Q) != 0> }
 
 struct Table {
     const Entry* entries;
@@ -54,5 +68,7 @@ Table table_f32_n();
 Table table_f64_v();
 Table table_f64_n();
 Table table_wave();
+Table table_lds_f32();
+Table table_lds_f64();
 
 }  // namespace steqr

@@ -56,8 +56,8 @@ def test_version(st):
 
 
 @pytest.mark.parametrize("n,jobz,dtype,N,P", [
-    (1, 1, 0, 4, 4), (4, 1, 0, 4, 4), (5, 1, 0, 8, 2), (8, 0, 0, 8, 1), (12, 1, 1, 16, 4),
-    (16, 1, 0, 16, 4), (17, 1, 0, 32, 16), (32, 0, 1, 32, 1), (32, 0, 0, 32, 2),
+    (1, 1, 0, 4, 4), (4, 1, 0, 4, 4), (5, 1, 0, 8, 2), (8, 0, 0, 8, 1), (12, 1, 1, 16, 8),
+    (16, 1, 0, 16, 4), (17, 1, 0, 32, 8), (32, 1, 1, 32, 8), (32, 0, 1, 32, 1), (32, 0, 0, 32, 2),
     (33, 1, 1, 64, 64), (64, 1, 1, 64, 64), (64, 0, 0, 64, 64)])
 def test_query_default_plan(st, n, jobz, dtype, N, P):
     q = st.steqr_query(n, 1000, jobz, dtype)
@@ -72,6 +72,17 @@ def test_query_explicit_lanes(st):
     q = st.steqr_query(16, 32768, 1, 0, prm)
     assert q["lanes_per_problem"] == 4 and q["rows_per_lane"] == 4
     assert q["workgroups"] == 32768 // (4 * 16)
+
+
+def test_query_band_storage(st):
+    assert st.steqr_query(16, 100, 1, 0)["band_storage"] == 1
+    assert st.steqr_query(16, 100, 1, 1)["band_storage"] == 2
+    assert st.steqr_query(32, 100, 1, 0)["band_storage"] == 2
+    assert st.steqr_query(16, 100, 1, 0, st.make_params(band_storage=2))["band_storage"] == 2
+    # orders above 32 always keep the band in LDS
+    assert st.steqr_query(40, 100, 1, 1, st.make_params(band_storage=1))["band_storage"] == 2
+    with pytest.raises(st.SteqrError):
+        st.steqr_query(16, 100, 1, 0, st.make_params(band_storage=3))
 
 
 @pytest.mark.parametrize("args,rc", [

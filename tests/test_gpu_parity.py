@@ -87,14 +87,36 @@ LANE_CASES = [
 ]
 
 
-@pytest.mark.parametrize("dt,n,jobz,lanes", LANE_CASES,
+LANE_CASES = [c + (1,) for c in LANE_CASES if c[1] <= 32] + [c + (2,) for c in LANE_CASES
+                                                              if c[1] > 32]
+# band in LDS (chunked kernel variant)
+LANE_CASES += [
+    (np.float32, 16, True, 8, 2), (np.float32, 16, True, 4, 2), (np.float32, 16, True, 2, 2),
+    (np.float32, 32, True, 16, 2), (np.float32, 32, True, 8, 2), (np.float32, 32, True, 4, 2),
+    (np.float64, 16, True, 8, 2), (np.float64, 16, True, 4, 2), (np.float64, 32, True, 16, 2),
+    (np.float64, 32, True, 8, 2), (np.float32, 12, True, 4, 2), (np.float64, 27, True, 8, 2),
+]
+
+
+@pytest.mark.parametrize("dt,n,jobz,lanes,band", LANE_CASES,
                          ids=lambda v: v.__name__ if isinstance(v, type) else str(v))
-def test_lanes_per_problem_variants(dt, n, jobz, lanes):
+def test_lanes_per_problem_variants(dt, n, jobz, lanes, band):
     d, e = W.random_batch(n, 777, dt, salt=21)
-    print("lanes case", dt.__name__, n, jobz, lanes, flush=True)
-    g = run_gpu(d, e, jobz, lanes=lanes)
+    print("lanes case", dt.__name__, n, jobz, lanes, band, flush=True)
+    g = run_gpu(d, e, jobz, lanes=lanes, band=band)
     o = oracle.steqr(d, e, jobz, threads=8)
     assert check(d, e, g, o, jobz) == []
+
+
+@pytest.mark.parametrize("dt", [np.float32, np.float64], ids=["f32", "f64"])
+@pytest.mark.parametrize("band", [1, 2], ids=["regs", "lds"])
+def test_band_storage_variants_on_edge_items(dt, band):
+    for kind in range(5):
+        for n in (9, 16, 32):
+            d, e = W.edge_batch(kind, n, 70, dt, salt=3)
+            g = run_gpu(d, e, True, band=band)
+            o = oracle.steqr(d, e, True)
+            assert check(d, e, g, o, True) == [], (W.EDGE_NAMES[kind], n)
 
 
 @pytest.mark.parametrize("dt", [np.float32, np.float64], ids=["f32", "f64"])
