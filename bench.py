@@ -110,6 +110,8 @@ def main() -> int:
     ap.add_argument("--band", type=int, default=0,
                     help="band storage: 0 default, 1 registers, 2 LDS")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-named", action="store_true",
+                    help="skip the secondary timing at the configuration's named lanes")
     ap.add_argument("--replicate", action="store_true",
                     help="lockstep-ideal batch: every chunk of a wavefront holds the same "
                          "matrix (each item repeated 64/P times); for divergence counters")
@@ -189,7 +191,8 @@ def main() -> int:
 
     # secondary timing at the lanes-per-problem the workload list names
     named = None
-    if args.lanes == 0 and plan["lanes_per_problem"] != w.lanes and not args.replicate:
+    if (args.lanes == 0 and plan["lanes_per_problem"] != w.lanes and not args.replicate
+            and not args.no_named):
         prm_n = st.make_params(lanes_per_problem=w.lanes, waves_per_block=args.waves,
                                band_storage=1 if w.n <= 32 else 2)
         try:

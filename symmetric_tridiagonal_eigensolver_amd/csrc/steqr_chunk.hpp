@@ -222,6 +222,7 @@ __global__ void __launch_bounds__(256) steqr_chunk_kernel(KernelArgs args) {
         publish();
     };
 
+    T x = T(0), y = T(0);  // running pair of the chase
     while (state != ST_DONE) {
         bool sweep = false, jac = false;
         // ------------------------------------------------------------ settle
@@ -268,7 +269,9 @@ __global__ void __launch_bounds__(256) steqr_chunk_kernel(KernelArgs args) {
                 bt = mir ? N - 1 - hi : lo;
                 bb = mir ? N - 1 - lo : hi;
                 m = bb;
-                zeroed = 0;
+                // the coupling above the block is zero; the chase may write
+                // it and closing the block restores it
+                zeroed = bt > 0 ? ((M)1 << (bt - 1)) : (M)0;
                 state = ST_ITER;
                 publish();
             }
@@ -278,6 +281,7 @@ __global__ void __launch_bounds__(256) steqr_chunk_kernel(KernelArgs args) {
                 constexpr int p = N - 2 - decltype(I)::value;
                 neg = neg + neg + (negligible(e[p], d[p], d[p + 1]) ? (M)1 : (M)0);
             });
+            neg |= zeroed;  // e's found negligible earlier (the chase may overwrite them)
             const M rng = bit_range<M>(bt, m - 1);
             const M nb = neg & rng;
             const M clr = rng & ~neg;
@@ -318,26 +322,30 @@ __global__ void __launch_bounds__(256) steqr_chunk_kernel(KernelArgs args) {
             }
             ++jtot;
             mu = lapack_shift(sd[m], sd[m - 1], se[m - 1]);
+            // running pair for the first rotation: (d_s - mu, e_s)
+            x = sd[s] - mu;
+            y = se[s];
             sweep = true;
             break;
         }
         if (state == ST_DONE) break;
 
         // ------------------------------------------------------------ chase pass
-        // Running pair (x, y) and the previous cosine cp: the update
-        // e_{p+1} <- c_p e_{p+1} of step p is applied when step p+1 reads it.
-        T x = T(0), y = T(0), cp = T(1);
+        // Running pair (x, y), seeded in the settle, and the previous cosine
+        // cp: the update e_{p+1} <- c_p e_{p+1} of step p is applied when
+        // step p+1 reads it. Step p writes r into e_{p-1}; at the first step
+        // that position is a zero coupling or a negligible e already in
+        // `zeroed`, which the next deflation test keeps and closing the
+        // block restores.
+        T cp = T(1);
         static_for<N - 1>([&](auto I) {
             constexpr int p = decltype(I)::value;
             if (sweep & (p >= s) & (p < m)) {
                 // [algo]: first rotation from (d_s - mu, e_s), later ones
                 // from (e_{p-1}, bulge); apply G^T B G to the 2x2 at (p, p+1)
-                const bool first = (p == s);
-                const T xin = first ? d[p] - mu : x;
-                const T yin = first ? e[p] : y;
                 T c, sn, rr;
-                lartg(xin, yin, c, sn, rr);
-                if constexpr (p > 0) e[p - 1] = first ? e[p - 1] : rr;
+                lartg(x, y, c, sn, rr);
+                if constexpr (p > 0) e[p - 1] = rr;
                 const T a = d[p], b = cp * e[p], dd = d[p + 1];
                 const T pp = c * a + sn * b;
                 const T qq = c * b + sn * dd;
@@ -353,11 +361,16 @@ __global__ void __launch_bounds__(256) steqr_chunk_kernel(KernelArgs args) {
                     static_for<R>([&](auto II) {
                         constexpr int i = decltype(II)::value;
                         const T qa = q[i][p], qb = q[i][p + 1];
-                        q[i][p] = c * qa + sn * qb;
-                        q[i][p + 1] = c * qb - sn * qa;
+                        const T tb = sn * qb, ta = sn * qa;
+                        q[i][p] = F::fma(c, qa, tb);
+                        q[i][p + 1] = F::fma(c, qb, -ta);
                     });
                 }
             }
+        });
+        // analytic 2x2 solves, only when some chunk of the wavefront has one
+        if (__any(jac)) static_for<N - 1>([&](auto I) {
+            constexpr int p = decltype(I)::value;
             if (jac & (p == jpos)) {
                 T rt1, rt2, cs, sj;
                 sym2x2(d[p], e[p], d[p + 1], rt1, rt2, cs, sj);

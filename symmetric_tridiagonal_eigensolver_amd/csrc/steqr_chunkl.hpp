@@ -184,6 +184,7 @@ __global__ void __launch_bounds__(256) steqr_chunkl_kernel(KernelArgs args) {
         zeroed = 0;
     };
 
+    T x = T(0), y = T(0), dcur = T(0);  // running pair and current d_p of the chase
     while (state != ST_DONE) {
         bool sweep = false, jac = false;
         // ------------------------------------------------------------ settle
@@ -230,7 +231,7 @@ __global__ void __launch_bounds__(256) steqr_chunkl_kernel(KernelArgs args) {
                 bt = mir ? N - 1 - hi : lo;
                 bb = mir ? N - 1 - lo : hi;
                 m = bb;
-                zeroed = 0;
+                zeroed = bt > 0 ? ((M)1 << (bt - 1)) : (M)0;  // zero coupling above
                 state = ST_ITER;
             }
             // deflation test [algo, deflation], positions split over the chunk
@@ -244,7 +245,7 @@ __global__ void __launch_bounds__(256) steqr_chunkl_kernel(KernelArgs args) {
                         part |= negligible(se[p], sd[p], sd[p + 1 < N ? p + 1 : N - 1])
                                     ? ((M)1 << p) : (M)0;
                 });
-                neg = chunk_or<P>(part);
+                neg = chunk_or<P>(part) | zeroed;
             }
             const M rng = bit_range<M>(bt, m - 1);
             const M nb = neg & rng;
@@ -283,6 +284,9 @@ __global__ void __launch_bounds__(256) steqr_chunkl_kernel(KernelArgs args) {
             }
             ++jtot;
             mu = lapack_shift(sd[m], sd[m - 1], se[m - 1]);
+            dcur = sd[s];
+            x = dcur - mu;
+            y = se[s];
             sweep = true;
             break;
         }
@@ -293,7 +297,7 @@ __global__ void __launch_bounds__(256) steqr_chunkl_kernel(KernelArgs args) {
         // d_{p+2}, e_{p+2} are read at position p. No step writes a position
         // before the window has read it.
         T d0 = sd[0], e0 = se[0], d1 = sd[1], e1 = se[1];
-        T x = T(0), y = T(0), cp = T(1), dcur = T(0);
+        T cp = T(1);
         static_for<N - 1>([&](auto I) {
             constexpr int p = decltype(I)::value;
             T d2 = T(0), e2 = T(0);
@@ -302,21 +306,19 @@ __global__ void __launch_bounds__(256) steqr_chunkl_kernel(KernelArgs args) {
                 e2 = se[p + 2];
             }
             if (sweep & (p >= s) & (p < m)) {
-                const bool first = (p == s);
-                const T a = first ? d0 : dcur;
-                const T xin = first ? a - mu : x;
-                const T yin = first ? e0 : y;
+                // running pair and d_p seeded in the settle; r goes to
+                // e_{p-1} (at the first step a zero coupling or an e already
+                // in `zeroed`, restored when the block closes)
+                const T a = dcur;
                 T c, sn, rr;
-                lartg(xin, yin, c, sn, rr);
+                lartg(x, y, c, sn, rr);
                 const T b = cp * e0;
                 const T pp = c * a + sn * b;
                 const T qq = c * b + sn * d1;
                 const T an = pp * c + qq * sn;
                 const T bn = qq * c - pp * sn;
                 if (writer) {
-                    if constexpr (p > 0) {
-                        if (!first) se[p - 1] = rr;
-                    }
+                    if constexpr (p > 0) se[p - 1] = rr;
                     sd[p] = an;
                 }
                 dcur = (a + d1) - an;
@@ -327,8 +329,9 @@ __global__ void __launch_bounds__(256) steqr_chunkl_kernel(KernelArgs args) {
                     static_for<R>([&](auto II) {
                         constexpr int i = decltype(II)::value;
                         const T qa = q[i][p], qb = q[i][p + 1];
-                        q[i][p] = c * qa + sn * qb;
-                        q[i][p + 1] = c * qb - sn * qa;
+                        const T tb = sn * qb, ta = sn * qa;
+                        q[i][p] = F::fma(c, qa, tb);
+                        q[i][p + 1] = F::fma(c, qb, -ta);
                     });
                 }
             }

@@ -42,11 +42,13 @@ struct Fp<float> {
     static constexpr float safmin = 0x1p-126f;
     static constexpr float ssfmax = 0x1p63f / 3.0f;
     static constexpr float ssfmin = 0x1p-15f;
-    static constexpr int newton_steps = 1;  // v_rsq_f32 is ~1 ulp
+    static constexpr int newton_steps = 0;  // v_rsq_f32 is accurate to about 1 ulp
     __device__ static __forceinline__ int frexp_exp(float x) { return __builtin_amdgcn_frexp_expf(x); }
     __device__ static __forceinline__ float ldexp(float x, int k) { return __builtin_amdgcn_ldexpf(x, k); }
     __device__ static __forceinline__ float rsq(float x) { return __builtin_amdgcn_rsqf(x); }
     __device__ static __forceinline__ float rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+    // true when x is a positive normal number (v_cmp_class, mask bit 8)
+    __device__ static __forceinline__ bool pos_normal(float x) { return __builtin_amdgcn_classf(x, 0x100); }
     __device__ static __forceinline__ float sqrt_fast(float x) { return __builtin_amdgcn_sqrtf(x); }
     __device__ static __forceinline__ float qnan() { return __builtin_nanf(""); }
     __device__ static __forceinline__ float abs(float x) { return __builtin_fabsf(x); }
@@ -66,6 +68,7 @@ struct Fp<double> {
     __device__ static __forceinline__ int frexp_exp(double x) { return __builtin_amdgcn_frexp_exp(x); }
     __device__ static __forceinline__ double ldexp(double x, int k) { return __builtin_amdgcn_ldexp(x, k); }
     __device__ static __forceinline__ double rsq(double x) { return __builtin_amdgcn_rsq(x); }
+    __device__ static __forceinline__ bool pos_normal(double x) { return __builtin_amdgcn_class(x, 0x100); }
     // double reciprocal / square root: hardware seed refined by Newton steps
     __device__ static __forceinline__ double rcp(double x) {
         double y = __builtin_amdgcn_rcp(x);
@@ -133,17 +136,17 @@ __device__ __forceinline__ bool negligible(T e, T d1, T d2) {
 
 // Givens rotation [algo, "G(c,s)" paragraph]: G(c,s) = [[c,-s],[s,c]],
 // G^T (f, g)^T = (r, 0)^T, r with the sign of f (so c >= 0).
-// The norm is formed as a hardware reciprocal square root refined by Newton
-// steps [cta, Givens rotation paragraph]; instead of a range guard with a
-// slow path, f and g are first scaled by an exact power of two (2^-k with k
-// the exponent of |f| + |g|, which lies within a factor 2 of max(|f|,|g|))
-// so that f^2 + g^2 lies in [1/16, 1] and can neither overflow nor
-// underflow. g = 0 gives (1, 0, f) through a final select [cta, Givens
-// rotation paragraph]. NaN inputs give NaN outputs. |f| + |g| cannot
-// overflow for the block-scaled values the solver passes (|f|, |g| stay
-// within a small multiple of ssfmax).
+//
+// Scaled form (always valid): f and g are first scaled by an exact power of
+// two (2^-k with k the exponent of |f| + |g|, which lies within a factor 2
+// of max(|f|,|g|)) so that f^2 + g^2 lies in [1/16, 1] and can neither
+// overflow nor underflow; the norm is a hardware reciprocal square root
+// refined by Newton steps [cta, Givens rotation paragraph]; g = 0 gives
+// (1, 0, f) through a final select [cta, Givens rotation paragraph]. NaN
+// inputs give NaN outputs. |f| + |g| cannot overflow for the block-scaled
+// values the solver passes (|f|, |g| stay within a small multiple of ssfmax).
 template <typename T>
-__device__ __forceinline__ void lartg(T f, T g, T& c, T& s, T& r) {
+__device__ __forceinline__ void lartg_scaled(T f, T g, T& c, T& s, T& r) {
     using F = Fp<T>;
     const T mx = F::abs(f) + F::abs(g);
     const int ex = F::frexp_exp(mx);
@@ -163,6 +166,29 @@ __device__ __forceinline__ void lartg(T f, T g, T& c, T& s, T& r) {
     c = gz ? T(1) : fs * ys;
     s = gz ? T(0) : gs * ys;
     r = gz ? f : F::ldexp(t * ys, ex);
+}
+
+// Givens rotation, fast form: t = f^2 + g^2 directly; whenever t is not a
+// positive normal number (overflow, underflow, zero or NaN) the lanes
+// concerned take the scaled form above (a branch the wavefront skips when
+// no lane needs it). With t normal the unscaled formulas are exact to a
+// few ulps, g = 0 included (c = |f| / |f|, s = 0, r = f).
+template <typename T>
+__device__ __forceinline__ void lartg(T f, T g, T& c, T& s, T& r) {
+    using F = Fp<T>;
+    const T t = F::fma(f, f, g * g);
+    T y = F::rsq(t);
+#pragma unroll
+    for (int k = 0; k < F::newton_steps; ++k) {
+        const T h = t * y;
+        const T res = F::fma(-h, y, T(1));
+        y = F::fma(y * res, T(0.5), y);
+    }
+    const T ys = F::copysign(y, f);
+    c = f * ys;
+    s = g * ys;
+    r = t * ys;
+    if (!F::pos_normal(t)) lartg_scaled(f, g, c, s, r);
 }
 
 // LAPACK-form shift [algo, shift section]: the eigenvalue of the 2x2 block

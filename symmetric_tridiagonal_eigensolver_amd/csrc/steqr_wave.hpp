@@ -176,13 +176,13 @@ __global__ void __launch_bounds__(256) steqr_wave_kernel(KernelArgs args) {
                 bt = mir ? N - 1 - hi : lo;
                 bb = mir ? N - 1 - lo : hi;
                 m = bb;
-                zeroed = 0;
+                zeroed = bt > 0 ? ((M)1 << (bt - 1)) : (M)0;  // zero coupling above
                 state = ST_ITER;
             }
             // deflation test: lane i tests e_i between d_i and d_{i+1}
             const T di = sd[lane], ei = se[lane];
             const T dn = sd[lane < N - 1 ? lane + 1 : N - 1];
-            const M neg = wave_ballot(negligible(ei, di, dn));
+            const M neg = wave_ballot(negligible(ei, di, dn)) | zeroed;
             const M rng = bit_range<M>(bt, m - 1);
             const M nb = neg & rng;
             const M clr = rng & ~neg;
@@ -226,25 +226,26 @@ __global__ void __launch_bounds__(256) steqr_wave_kernel(KernelArgs args) {
             // update e_p <- c_{p-1} e_p is applied here), (x, y) = running
             // pair. d_{p+1}, e_{p+1} are read one step ahead: no step writes
             // them before step p.
-            T x = T(0), y = T(0), cp = T(1), dcur = T(0), ecur = T(0);
+            // running pair (d_s - mu, e_s) for the first rotation
+            T dcur = sd[s], ecur = se[s];
+            T x = dcur - mu, y = ecur, cp = T(1);
             T dnext = sd[s + 1], enext = se[s + 1];
             static_for<N - 1>([&](auto I) {
                 constexpr int p = decltype(I)::value;
                 if ((p >= s) & (p < m)) {
-                    const bool first = (p == s);
+                    // r goes to e_{p-1}: at the first step a zero coupling or
+                    // an e already in `zeroed`, restored when the block closes
                     const T dp1 = dnext, ep1 = enext;
                     if constexpr (p + 2 < N) {
                         dnext = sd[p + 2];
                         enext = se[p + 2];
                     }
-                    const T a = first ? sd[p] : dcur;
-                    const T ep = first ? se[p] : ecur;
-                    const T xin = first ? a - mu : x;
-                    const T yin = first ? ep : y;
+                    const T a = dcur;
+                    const T ep = ecur;
                     T c, sn, rr;
-                    lartg(xin, yin, c, sn, rr);
+                    lartg(x, y, c, sn, rr);
                     if constexpr (p > 0) {
-                        if (!first && writer) se[p - 1] = rr;
+                        if (writer) se[p - 1] = rr;
                     }
                     const T b = cp * ep;
                     const T pp = c * a + sn * b;
@@ -259,8 +260,9 @@ __global__ void __launch_bounds__(256) steqr_wave_kernel(KernelArgs args) {
                     ecur = ep1;
                     if constexpr (WANTQ) {
                         const T qa = q[p], qb = q[p + 1];
-                        q[p] = c * qa + sn * qb;
-                        q[p + 1] = c * qb - sn * qa;
+                        const T tb = sn * qb, ta = sn * qa;
+                        q[p] = F::fma(c, qa, tb);
+                        q[p + 1] = F::fma(c, qb, -ta);
                     }
                 }
             });

@@ -234,3 +234,20 @@ def test_non_default_stream():
     o = oracle.steqr(d, e, True)
     g = (lam.cpu().numpy(), Q.cpu().numpy(), np.zeros(500, np.int32))
     assert check(d, e, g, o, True) == []
+
+
+def test_accuracy_margins_report():
+    """Report (and bound) error / tolerance on every configuration: the
+    largest eigenvalue, residual and orthogonality error as a fraction of
+    the 16 n eps acceptance bound."""
+    for wname, w in W.WORKLOADS.items():
+        d, e = W.make_batch(w, 2048)
+        g = run_gpu(d, e, True)
+        o = oracle.steqr(d, e, True, threads=8)
+        ok = (g[2] == 0) & (o[2] == 0)
+        tol = V.tol_of(d.dtype, w.n)
+        ev = V.sorted_err(g[0][ok], o[0][ok], d[ok], e[ok]).max() / tol
+        rs = V.band_residual(d[ok], e[ok], g[0][ok], g[1][ok]).max() / tol
+        og = V.orthogonality(g[1][ok]).max() / tol
+        print("margin %-12s eig %.3f  residual %.3f  orth %.3f" % (wname, ev, rs, og), flush=True)
+        assert max(ev, rs, og) <= 1.0
