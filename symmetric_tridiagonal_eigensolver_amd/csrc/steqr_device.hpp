@@ -173,7 +173,7 @@ __device__ __forceinline__ void lartg_scaled(T f, T g, T& c, T& s, T& r) {
 // concerned take the scaled form above (a branch the wavefront skips when
 // no lane needs it). With t normal the unscaled formulas are exact to a
 // few ulps, g = 0 included (c = |f| / |f|, s = 0, r = f).
-template <typename T>
+template <typename T, bool UNIFORM = false>
 __device__ __forceinline__ void lartg(T f, T g, T& c, T& s, T& r) {
     using F = Fp<T>;
     const T t = F::fma(f, f, g * g);
@@ -188,7 +188,12 @@ __device__ __forceinline__ void lartg(T f, T g, T& c, T& s, T& r) {
     c = f * ys;
     s = g * ys;
     r = t * ys;
-    if (!F::pos_normal(t)) lartg_scaled(f, g, c, s, r);
+    if constexpr (UNIFORM) {
+        // every lane holds the same (f, g): one scalar branch
+        if (__builtin_amdgcn_readfirstlane((int)!F::pos_normal(t))) lartg_scaled(f, g, c, s, r);
+    } else {
+        if (!F::pos_normal(t)) lartg_scaled(f, g, c, s, r);
+    }
 }
 
 // LAPACK-form shift [algo, shift section]: the eigenvalue of the 2x2 block

@@ -243,16 +243,14 @@ __global__ void __launch_bounds__(256) steqr_wave_kernel(KernelArgs args) {
                     const T a = dcur;
                     const T ep = ecur;
                     T c, sn, rr;
-                    lartg(x, y, c, sn, rr);
-                    if constexpr (p > 0) {
-                        if (writer) se[p - 1] = rr;
-                    }
+                    lartg<T, true>(x, y, c, sn, rr);
+                    if constexpr (p > 0) se[p - 1] = rr;  // every lane writes the same word
                     const T b = cp * ep;
                     const T pp = c * a + sn * b;
                     const T qq = c * b + sn * dp1;
                     const T an = pp * c + qq * sn;
                     const T bn = qq * c - pp * sn;
-                    if (writer) sd[p] = an;
+                    sd[p] = an;
                     dcur = (a + dp1) - an;
                     x = bn;
                     y = sn * ep1;  // new bulge
@@ -266,12 +264,10 @@ __global__ void __launch_bounds__(256) steqr_wave_kernel(KernelArgs args) {
                     }
                 }
             });
-            if (writer) {
-                sd[m] = dcur;
-                se[m - 1] = x;
-            }
+            sd[m] = dcur;
+            se[m - 1] = x;
             __builtin_amdgcn_wave_barrier();
-            if (mu != mu) jtot = nmaxit;
+            if (uniform_int(mu != mu)) jtot = nmaxit;
         }
         if (jac) {
             static_for<N - 1>([&](auto I) {
