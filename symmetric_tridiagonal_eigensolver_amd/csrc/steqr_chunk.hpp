@@ -90,16 +90,20 @@ __device__ __forceinline__ void mirror_problem(bool mir, T (&d)[N], T (&e)[N], T
 }
 
 // LDS per wavefront: one band slot per chunk (d then e, padded to an odd
-// number of elements against bank conflicts) and, for P > 1, one rank row
-// per chunk for the final sort.
-template <typename T, int N, int P>
+// number of elements against bank conflicts), for P > 1 one rank row per
+// chunk for the final sort, and with eigenvectors a staging area holding the
+// wavefront's Q blocks in their HBM layout, so that the store is one
+// contiguous, fully coalesced copy.
+template <typename T, int N, int P, bool WANTQ = false>
 struct Smem {
     static constexpr int CH = 64 / P;
     static constexpr int SLOT = 2 * N + 1;
     static constexpr int band_elems = CH * SLOT;
     static constexpr int rank_ints = (P > 1) ? CH * N : 0;
-    static constexpr size_t bytes_per_wave =
-        ((band_elems * sizeof(T) + 15) / 16) * 16 + (size_t)rank_ints * sizeof(int);
+    static constexpr size_t band_bytes = ((band_elems * sizeof(T) + 15) / 16) * 16;
+    static constexpr size_t rank_bytes = (((size_t)rank_ints * sizeof(int) + 15) / 16) * 16;
+    static constexpr size_t stage_bytes = WANTQ ? (size_t)CH * N * N * sizeof(T) : 0;
+    static constexpr size_t bytes_per_wave = band_bytes + rank_bytes + stage_bytes;
 };
 
 template <typename T, int N, int P, bool WANTQ>
@@ -111,7 +115,7 @@ __global__ void __launch_bounds__(256) steqr_chunk_kernel(KernelArgs args) {
     constexpr int RJ = (N + P - 1) / P;              // sort keys ranked per lane
     using M = PosMask<N>;
     using F = Fp<T>;
-    using S = Smem<T, N, P>;
+    using S = Smem<T, N, P, WANTQ>;
     enum { ST_OPEN = 0, ST_ITER = 1, ST_DONE = 2 };
 
     extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -133,8 +137,8 @@ __global__ void __launch_bounds__(256) steqr_chunk_kernel(KernelArgs args) {
     unsigned char* wave_smem = smem_raw + (size_t)wave * S::bytes_per_wave;
     T* const sd = reinterpret_cast<T*>(wave_smem) + chunk * S::SLOT;  // chunk's d copy
     T* const se = sd + N;                                              // chunk's e copy
-    int* const srank = reinterpret_cast<int*>(
-                           wave_smem + ((S::band_elems * sizeof(T) + 15) / 16) * 16) + chunk * N;
+    int* const srank = reinterpret_cast<int*>(wave_smem + S::band_bytes) + chunk * N;
+    T* const stage = reinterpret_cast<T*>(wave_smem + S::band_bytes + S::rank_bytes);
 
     // ---------------------------------------------------------------- load
     T d[N], e[N];
@@ -447,20 +451,54 @@ __global__ void __launch_bounds__(256) steqr_chunk_kernel(KernelArgs args) {
                 if (j < n) glam[prob * n + myrank[k]] = myd[k];
             });
         }
-        if constexpr (WANTQ) {
-            const long qb = prob * (long)n * n;
-            static_for<R>([&](auto II) {
-                constexpr int i = decltype(II)::value;
-                const int row = r * R + i;
-                if (row < n) {
-                    static_for<N>([&](auto J) {
-                        constexpr int j = decltype(J)::value;
-                        if (j < n) gq[qb + (long)row * n + rank[j]] = q[i][j];
-                    });
+        if (args.info != nullptr && r == 0) args.info[prob] = info;
+    }
+    if constexpr (WANTQ) {
+        // stage the wavefront's Q blocks (chunk c at c*n*n, row-major with
+        // the sort's column permutation applied), then copy them to HBM as
+        // one contiguous range: the wavefront's problems are consecutive.
+        const int nn = n * n;
+        T* const myq = stage + chunk * nn;
+        static_for<R>([&](auto II) {
+            constexpr int i = decltype(II)::value;
+            const int row = r * R + i;
+            if (row < n) {
+                static_for<N>([&](auto J) {
+                    constexpr int j = decltype(J)::value;
+                    if (j < n) myq[row * n + rank[j]] = q[i][j];
+                });
+            }
+        });
+        __builtin_amdgcn_wave_barrier();
+        const long first = ((long)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6)) * CH;
+        const long left = (long)args.batch - first;
+        const int nprob = left < CH ? (int)left : CH;
+        const int total = nprob * nn;  // elements this wavefront writes
+        T* const dst = gq + first * nn;
+        constexpr int MAXE = CH * N * N;
+        if (((nn & 3) == 0) & ((reinterpret_cast<uintptr_t>(gq) & 15) == 0)) {
+            // 16-byte pieces, consecutive lanes at consecutive addresses
+            constexpr int V = 16 / sizeof(T);
+            static_for<(MAXE + 64 * V - 1) / (64 * V)>([&](auto K) {
+                constexpr int k = decltype(K)::value;
+                const int idx = (k * 64 + lane) * V;
+                if (idx < total) {
+                    if constexpr (sizeof(T) == 4) {
+                        *reinterpret_cast<float4*>(dst + idx) =
+                            *reinterpret_cast<const float4*>(stage + idx);
+                    } else {
+                        *reinterpret_cast<double2*>(dst + idx) =
+                            *reinterpret_cast<const double2*>(stage + idx);
+                    }
                 }
             });
+        } else {
+            static_for<(MAXE + 63) / 64>([&](auto K) {
+                constexpr int k = decltype(K)::value;
+                const int idx = k * 64 + lane;
+                if (idx < total) dst[idx] = stage[idx];
+            });
         }
-        if (args.info != nullptr && r == 0) args.info[prob] = info;
     }
 }
 

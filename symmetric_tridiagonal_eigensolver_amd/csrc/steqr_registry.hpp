@@ -25,7 +25,7 @@ struct Entry {
 
 template <typename T, int N, int P, bool WANTQ>
 hipError_t launch_chunk(const KernelArgs& args, int grid, int block, hipStream_t stream) {
-    const size_t lds = (size_t)(block / 64) * Smem<T, N, P>::bytes_per_wave;
+    const size_t lds = (size_t)(block / 64) * Smem<T, N, P, WANTQ>::bytes_per_wave;
     hipLaunchKernelGGL((steqr_chunk_kernel<T, N, P, WANTQ>), dim3(grid), dim3(block), lds, stream,
                        args);
     return hipGetLastError();
@@ -56,7 +56,7 @@ hipError_t launch_chunkl(const KernelArgs& args, int grid, int block, hipStream_
     { DT, N, P, Q, 2, (int)SmemL<T, N, P>::bytes_per_wave, &launch_chunkl<T, N, P, (Q) != 0> }
 
 #define STEQR_ENTRY(DT, T, N, P, Q) \
-    { DT, N, P, Q, 1, (int)Smem<T, N, P>::bytes_per_wave, &launch_chunk<T, N, P, (Q) != 0> }
+    { DT, N, P, Q, 1, (int)Smem<T, N, P, (Q) != 0>::bytes_per_wave, &launch_chunk<T, N, P, (Q) != 0> }
 
 struct Table {
     const Entry* entries;
