@@ -71,7 +71,10 @@ def test_query_explicit_lanes(st):
     prm = st.make_params(lanes_per_problem=4)
     q = st.steqr_query(16, 32768, 1, 0, prm)
     assert q["lanes_per_problem"] == 4 and q["rows_per_lane"] == 4
-    assert q["workgroups"] == 32768 // (4 * 16)
+    assert 1 <= q["waves_per_block"] <= 4
+    assert q["workgroups"] == 32768 // (q["waves_per_block"] * 16)
+    q1 = st.steqr_query(16, 32768, 1, 0, st.make_params(lanes_per_problem=4, waves_per_block=1))
+    assert q1["waves_per_block"] == 1 and q1["workgroups"] == 32768 // 16
 
 
 def test_query_band_storage(st):
