@@ -342,32 +342,33 @@ __global__ void __launch_bounds__(256) steqr_chunk_kernel(KernelArgs args) {
         // `zeroed`, which the next deflation test keeps and closing the
         // block restores.
         T cp = T(1);
+        // step p runs when s <= p < m: one unsigned compare of p - s with
+        // the step count (0 when this chunk does not sweep)
+        const unsigned steps = sweep ? (unsigned)(m - s) : 0u;
         static_for<N - 1>([&](auto I) {
             constexpr int p = decltype(I)::value;
-            if (sweep & (p >= s) & (p < m)) {
+            if ((unsigned)(p - s) < steps) {
                 // [algo]: first rotation from (d_s - mu, e_s), later ones
                 // from (e_{p-1}, bulge); apply G^T B G to the 2x2 at (p, p+1)
+                const T b = cp * e[p];
                 T c, sn, rr;
                 lartg(x, y, c, sn, rr);
                 if constexpr (p > 0) e[p - 1] = rr;
-                const T a = d[p], b = cp * e[p], dd = d[p + 1];
+                const T a = d[p], dd = d[p + 1];
+                const T tr = a + dd;  // trace of the 2x2 is invariant
                 const T pp = c * a + sn * b;
                 const T qq = c * b + sn * dd;
-                const T an = pp * c + qq * sn;
                 const T bn = qq * c - pp * sn;
-                d[p] = an;
+                F::fma_over(d[p], pp, c, qq * sn);
                 e[p] = bn;
-                d[p + 1] = (a + dd) - an;  // trace of the 2x2 is invariant
+                d[p + 1] = tr - d[p];
                 if constexpr (p + 1 < N - 1) y = sn * e[p + 1];  // new bulge
                 x = bn;
                 cp = c;
                 if constexpr (WANTQ) {
                     static_for<R>([&](auto II) {
                         constexpr int i = decltype(II)::value;
-                        const T qa = q[i][p], qb = q[i][p + 1];
-                        const T tb = sn * qb, ta = sn * qa;
-                        q[i][p] = F::fma(c, qa, tb);
-                        q[i][p + 1] = F::fma(c, qb, -ta);
+                        F::rot(q[i][p], q[i][p + 1], c, sn);
                     });
                 }
             }
@@ -384,9 +385,7 @@ __global__ void __launch_bounds__(256) steqr_chunk_kernel(KernelArgs args) {
                 if constexpr (WANTQ) {
                     static_for<R>([&](auto II) {
                         constexpr int i = decltype(II)::value;
-                        const T qa = q[i][p], qb = q[i][p + 1];
-                        q[i][p] = cs * qa - sj * qb;
-                        q[i][p + 1] = sj * qa + cs * qb;
+                        F::rot(q[i][p], q[i][p + 1], cs, -sj);
                     });
                 }
             }

@@ -298,6 +298,10 @@ __global__ void __launch_bounds__(256) steqr_chunkl_kernel(KernelArgs args) {
         // before the window has read it.
         T d0 = sd[0], e0 = se[0], d1 = sd[1], e1 = se[1];
         T cp = T(1);
+        // step p runs when s <= p < m: one unsigned compare of p - s with
+        // the step count (0 when this chunk does not sweep)
+        const unsigned steps = sweep ? (unsigned)(m - s) : 0u;
+        const int jat = jac ? jpos : -1;  // position of this chunk's 2x2 solve
         static_for<N - 1>([&](auto I) {
             constexpr int p = decltype(I)::value;
             T d2 = T(0), e2 = T(0);
@@ -305,7 +309,7 @@ __global__ void __launch_bounds__(256) steqr_chunkl_kernel(KernelArgs args) {
                 d2 = sd[p + 2];
                 e2 = se[p + 2];
             }
-            if (sweep & (p >= s) & (p < m)) {
+            if ((unsigned)(p - s) < steps) {
                 // running pair and d_p seeded in the settle; r goes to
                 // e_{p-1} (at the first step a zero coupling or an e already
                 // in `zeroed`, restored when the block closes)
@@ -317,10 +321,9 @@ __global__ void __launch_bounds__(256) steqr_chunkl_kernel(KernelArgs args) {
                 const T qq = c * b + sn * d1;
                 const T an = pp * c + qq * sn;
                 const T bn = qq * c - pp * sn;
-                if (writer) {
-                    if constexpr (p > 0) se[p - 1] = rr;
-                    sd[p] = an;
-                }
+                // every lane of the chunk writes the same value to the same word
+                if constexpr (p > 0) se[p - 1] = rr;
+                sd[p] = an;
                 dcur = (a + d1) - an;
                 x = bn;
                 y = sn * e1;
@@ -328,27 +331,20 @@ __global__ void __launch_bounds__(256) steqr_chunkl_kernel(KernelArgs args) {
                 if constexpr (WANTQ) {
                     static_for<R>([&](auto II) {
                         constexpr int i = decltype(II)::value;
-                        const T qa = q[i][p], qb = q[i][p + 1];
-                        const T tb = sn * qb, ta = sn * qa;
-                        q[i][p] = F::fma(c, qa, tb);
-                        q[i][p + 1] = F::fma(c, qb, -ta);
+                        F::rot(q[i][p], q[i][p + 1], c, sn);
                     });
                 }
             }
-            if (jac & (p == jpos)) {
+            if (p == jat) {
                 T rt1, rt2, cs, sj;
                 sym2x2(d0, e0, d1, rt1, rt2, cs, sj);
-                if (writer) {
-                    sd[p] = rt1;
-                    sd[p + 1] = rt2;
-                    se[p] = T(0);
-                }
+                sd[p] = rt1;
+                sd[p + 1] = rt2;
+                se[p] = T(0);
                 if constexpr (WANTQ) {
                     static_for<R>([&](auto II) {
                         constexpr int i = decltype(II)::value;
-                        const T qa = q[i][p], qb = q[i][p + 1];
-                        q[i][p] = cs * qa - sj * qb;
-                        q[i][p + 1] = sj * qa + cs * qb;
+                        F::rot(q[i][p], q[i][p + 1], cs, -sj);
                     });
                 }
             }

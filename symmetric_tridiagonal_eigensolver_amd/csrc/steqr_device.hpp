@@ -49,6 +49,8 @@ struct Fp<float> {
     __device__ static __forceinline__ float rcp(float x) { return __builtin_amdgcn_rcpf(x); }
     // true when x is a positive normal number (v_cmp_class, mask bit 8)
     __device__ static __forceinline__ bool pos_normal(float x) { return __builtin_amdgcn_classf(x, 0x100); }
+    // true when x is anything but a positive normal number (every other class bit)
+    __device__ static __forceinline__ bool not_pos_normal(float x) { return __builtin_amdgcn_classf(x, 0x2ff); }
     __device__ static __forceinline__ float sqrt_fast(float x) { return __builtin_amdgcn_sqrtf(x); }
     __device__ static __forceinline__ float qnan() { return __builtin_nanf(""); }
     __device__ static __forceinline__ float abs(float x) { return __builtin_fabsf(x); }
@@ -56,6 +58,18 @@ struct Fp<float> {
     __device__ static __forceinline__ float fma(float a, float b, float c) { return __builtin_fmaf(a, b, c); }
     __device__ static __forceinline__ float max(float a, float b) { return __builtin_fmaxf(a, b); }
     __device__ static __forceinline__ float copysign(float a, float b) { return __builtin_copysignf(a, b); }
+    // (a, b) <- (fma(c, a, s b), fma(c, b, -s a)) with each result written
+    // over its own input register. Inside a lane-masked region the
+    // compiler's accumulate-into-temporary form needs a copy back per value.
+    __device__ static __forceinline__ void rot(float& a, float& b, float c, float s) {
+        const float sa = s * a, sb = s * b;
+        asm("v_fma_f32 %0, %1, %0, %2" : "+v"(a) : "v"(c), "v"(sb));
+        asm("v_fma_f32 %0, %1, %0, -%2" : "+v"(b) : "v"(c), "v"(sa));
+    }
+    // dst <- fma(a, b, c) in dst's register (old value of dst unused)
+    __device__ static __forceinline__ void fma_over(float& dst, float a, float b, float c) {
+        asm("v_fma_f32 %0, %1, %2, %3" : "+v"(dst) : "v"(a), "v"(b), "v"(c));
+    }
 };
 
 template <>
@@ -69,6 +83,7 @@ struct Fp<double> {
     __device__ static __forceinline__ double ldexp(double x, int k) { return __builtin_amdgcn_ldexp(x, k); }
     __device__ static __forceinline__ double rsq(double x) { return __builtin_amdgcn_rsq(x); }
     __device__ static __forceinline__ bool pos_normal(double x) { return __builtin_amdgcn_class(x, 0x100); }
+    __device__ static __forceinline__ bool not_pos_normal(double x) { return __builtin_amdgcn_class(x, 0x2ff); }
     // double reciprocal / square root: hardware seed refined by Newton steps
     __device__ static __forceinline__ double rcp(double x) {
         double y = __builtin_amdgcn_rcp(x);
@@ -83,6 +98,16 @@ struct Fp<double> {
     __device__ static __forceinline__ double fma(double a, double b, double c) { return __builtin_fma(a, b, c); }
     __device__ static __forceinline__ double max(double a, double b) { return __builtin_fmax(a, b); }
     __device__ static __forceinline__ double copysign(double a, double b) { return __builtin_copysign(a, b); }
+    // (a, b) <- (fma(c, a, s b), fma(c, b, -s a)). v_fma_f64 has no
+    // accumulate-in-place form, so plain code already writes in place.
+    __device__ static __forceinline__ void rot(double& a, double& b, double c, double s) {
+        const double sa = s * a, sb = s * b;
+        a = __builtin_fma(c, a, sb);
+        b = __builtin_fma(c, b, -sa);
+    }
+    __device__ static __forceinline__ void fma_over(double& dst, double a, double b, double c) {
+        dst = __builtin_fma(a, b, c);
+    }
 };
 
 // ---------------------------------------------------------------- bit masks
@@ -170,9 +195,11 @@ __device__ __forceinline__ void lartg_scaled(T f, T g, T& c, T& s, T& r) {
 
 // Givens rotation, fast form: t = f^2 + g^2 directly; whenever t is not a
 // positive normal number (overflow, underflow, zero or NaN) the lanes
-// concerned take the scaled form above (a branch the wavefront skips when
-// no lane needs it). With t normal the unscaled formulas are exact to a
-// few ulps, g = 0 included (c = |f| / |f|, s = 0, r = f).
+// concerned take the scaled form above. The test is one ballot and a
+// scalar branch the wavefront skips when no active lane needs the scaled
+// form (UNIFORM: every lane holds the same (f, g), one lane decides). With
+// t normal the unscaled formulas are exact to a few ulps, g = 0 included
+// (c = |f| / |f|, s = 0, r = f).
 template <typename T, bool UNIFORM = false>
 __device__ __forceinline__ void lartg(T f, T g, T& c, T& s, T& r) {
     using F = Fp<T>;
@@ -192,7 +219,14 @@ __device__ __forceinline__ void lartg(T f, T g, T& c, T& s, T& r) {
         // every lane holds the same (f, g): one scalar branch
         if (__builtin_amdgcn_readfirstlane((int)!F::pos_normal(t))) lartg_scaled(f, g, c, s, r);
     } else {
-        if (!F::pos_normal(t)) lartg_scaled(f, g, c, s, r);
+        const bool slow = F::not_pos_normal(t);
+        if (__builtin_amdgcn_ballot_w64(slow)) {
+            T c2, s2, r2;
+            lartg_scaled(f, g, c2, s2, r2);
+            c = slow ? c2 : c;
+            s = slow ? s2 : s;
+            r = slow ? r2 : r;
+        }
     }
 }
 

@@ -257,10 +257,7 @@ __global__ void __launch_bounds__(256) steqr_wave_kernel(KernelArgs args) {
                     cp = c;
                     ecur = ep1;
                     if constexpr (WANTQ) {
-                        const T qa = q[p], qb = q[p + 1];
-                        const T tb = sn * qb, ta = sn * qa;
-                        q[p] = F::fma(c, qa, tb);
-                        q[p + 1] = F::fma(c, qb, -ta);
+                        F::rot(q[p], q[p + 1], c, sn);
                     }
                 }
             });
@@ -281,9 +278,7 @@ __global__ void __launch_bounds__(256) steqr_wave_kernel(KernelArgs args) {
                         se[p] = T(0);
                     }
                     if constexpr (WANTQ) {
-                        const T qa = q[p], qb = q[p + 1];
-                        q[p] = cs * qa - sj * qb;
-                        q[p + 1] = sj * qa + cs * qb;
+                        F::rot(q[p], q[p + 1], cs, -sj);
                     }
                 }
             });
