@@ -189,20 +189,23 @@ __global__ void __launch_bounds__(256) steqr_chunk_kernel(KernelArgs args) {
     publish();
 
     // ---------------------------------------------------------------- state
+    // ST_OPEN: the chunk's next block is to be opened; ST_ITER: a block is
+    // being reduced; ST_DONE: nothing left to reduce (a converged last block
+    // may still wait for its close, `pending`).
     int state = live ? ST_OPEN : ST_DONE;
     int l1 = 0;           // running left boundary of the next split block (original coords)
     int bt = 0, bb = 0;   // current block [bt, bb] in current (possibly mirrored) coords
     int m = 0;            // converging (bottom) end of the active part
     int s = 0;            // top of the unreduced part [s, m]
-    int jpos = -1;        // position of a pending analytic 2x2 solve
     int jtot = 0;
     const int nmaxit = (args.max_sweeps_per_n > 0 ? args.max_sweeps_per_n : 0) * n;
     bool mir = false, failed = false;
+    bool last = false;     // no block follows the current one
+    bool pending = false;  // converged last block, closed after the loop
     int mode = 0;
     T anorm = T(0);
     M zeroed = 0;  // negligible e's found inside the current block
     int info = 0;
-    T mu = T(0);
 
     // Close the current block: zero the negligible e's found in it, undo the
     // scaling (d always, e too when the block failed), undo the mirror.
@@ -223,116 +226,132 @@ __global__ void __launch_bounds__(256) steqr_chunk_kernel(KernelArgs args) {
         mir = false;
         mode = 0;
         zeroed = 0;
-        publish();
     };
 
-    T x = T(0), y = T(0);  // running pair of the chase
-    while (state != ST_DONE) {
-        bool sweep = false, jac = false;
-        // ------------------------------------------------------------ settle
-        while (true) {
-            if (state == ST_OPEN) {
-                // next block: skip 1x1 blocks (zero e), stop at the first zero
-                // e at or right of its start [algo, steqr_cta paragraph]
-                const M avail = ~zeromask & ~bits_below<M>(l1) & bits_below<M>(n - 1);
-                if (avail == 0) {
-                    state = ST_DONE;
-                    break;
-                }
-                const int lo = lsb(avail);
-                const int hi = lsb((M)(zeromask & ~bits_below<M>(lo)));
-                l1 = hi + 1;
-                // block norm, NaN-propagating [algo, scaling]
-                T an = T(0);
-                bool hasnan = false;
-                static_for<N>([&](auto I) {
-                    constexpr int p = decltype(I)::value;
-                    const bool ind = (p >= lo) & (p <= hi);
-                    const bool ine = (p >= lo) & (p < hi);
-                    an = ind ? F::max(an, F::abs(d[p])) : an;
-                    an = ine ? F::max(an, F::abs(e[p])) : an;
-                    hasnan = hasnan | (ind & (d[p] != d[p])) | (ine & (e[p] != e[p]));
-                });
-                anorm = hasnan ? F::qnan() : an;
-                if (anorm == T(0)) continue;
-                mode = (anorm > F::ssfmax) ? 1 : ((anorm < F::ssfmin) ? 2 : 0);
-                const T sg = (mode == 0) ? T(1) : ((mode == 1) ? F::ssfmax : F::ssfmin) / anorm;
-                if (mode != 0) {
-                    static_for<N>([&](auto I) {
-                        constexpr int p = decltype(I)::value;
-                        d[p] = ((p >= lo) & (p <= hi)) ? d[p] * sg : d[p];
-                        e[p] = ((p >= lo) & (p < hi)) ? e[p] * sg : e[p];
-                    });
-                }
-                // converge the end of smaller magnitude first; a tie or NaN
-                // converges the top end first, i.e. mirror. |sg*x| = sg*|x|
-                // exactly, so this compares the scaled end values.
-                const T dlo = F::abs(sd[lo]) * sg, dhi = F::abs(sd[hi]) * sg;
-                mir = !(dhi < dlo);
-                mirror_problem<T, N, RQ, WANTQ>(mir, d, e, q);
-                bt = mir ? N - 1 - hi : lo;
-                bb = mir ? N - 1 - lo : hi;
-                m = bb;
-                // the coupling above the block is zero; the chase may write
-                // it and closing the block restores it
-                zeroed = bt > 0 ? ((M)1 << (bt - 1)) : (M)0;
-                state = ST_ITER;
-                publish();
-            }
-            // ST_ITER: deflation test [algo, deflation] at every position
-            M neg = 0;
-            static_for<N - 1>([&](auto I) {
-                constexpr int p = N - 2 - decltype(I)::value;
-                neg = neg + neg + (negligible(e[p], d[p], d[p + 1]) ? (M)1 : (M)0);
-            });
-            neg |= zeroed;  // e's found negligible earlier (the chase may overwrite them)
-            const M rng = bit_range<M>(bt, m - 1);
-            const M nb = neg & rng;
-            const M clr = rng & ~neg;
-            if (clr == 0) {
-                // every remaining eigenvalue of the block has converged
-                zeroed |= nb;
-                close_block(false);
-                state = ST_OPEN;
-                continue;
-            }
-            // the bottom run of negligible e's deflates 1x1 eigenvalues
-            const int t = msb(clr);
-            zeroed |= nb & bit_range<M>(t + 1, m - 1);
-            m = t + 1;
-            // last negligible e above the converging end bounds the
-            // unreduced part [s, m]
-            const M above = nb & bit_range<M>(bt, t - 1);
-            s = above ? msb(above) + 1 : bt;
-            if (above) zeroed |= (M)1 << (s - 1);
-            if (m - s == 1) {
-                jac = true;
-                jpos = s;
-                m = s - 1;
-                break;
-            }
-            if (jtot >= nmaxit) {
-                failed = true;
-                close_block(true);
-                M nz = 0;
-                static_for<N - 1>([&](auto I) {
-                    constexpr int p = N - 2 - decltype(I)::value;
-                    nz = nz + nz + ((e[p] != T(0)) ? (M)1 : (M)0);
-                });
-                info = popc((M)(nz & bits_below<M>(n - 1)));
-                info = info > 0 ? info : 1;
+    // Open the next block of every chunk in ST_OPEN: skip 1x1 blocks (zero
+    // e) and stop at the first zero e at or right of the block start [algo,
+    // steqr_cta paragraph]; skip blocks of norm zero; scale [algo, scaling];
+    // pick the converging end and mirror.
+    auto open_blocks = [&]() __attribute__((always_inline)) {
+        while (state == ST_OPEN) {
+            const M avail = ~zeromask & ~bits_below<M>(l1) & bits_below<M>(n - 1);
+            if (avail == 0) {
                 state = ST_DONE;
                 break;
             }
-            ++jtot;
-            mu = lapack_shift(sd[m], sd[m - 1], se[m - 1]);
-            // running pair for the first rotation: (d_s - mu, e_s)
-            x = sd[s] - mu;
-            y = se[s];
-            sweep = true;
-            break;
+            const int lo = lsb(avail);
+            const int hi = lsb((M)(zeromask & ~bits_below<M>(lo)));
+            l1 = hi + 1;
+            last = (avail & ~bits_below<M>(l1)) == 0;
+            // block norm, NaN-propagating [algo, scaling]
+            T an = T(0);
+            bool hasnan = false;
+            static_for<N>([&](auto I) {
+                constexpr int p = decltype(I)::value;
+                const bool ind = (p >= lo) & (p <= hi);
+                const bool ine = (p >= lo) & (p < hi);
+                an = ind ? F::max(an, F::abs(d[p])) : an;
+                an = ine ? F::max(an, F::abs(e[p])) : an;
+                hasnan = hasnan | (ind & (d[p] != d[p])) | (ine & (e[p] != e[p]));
+            });
+            anorm = hasnan ? F::qnan() : an;
+            if (anorm == T(0)) continue;
+            mode = (anorm > F::ssfmax) ? 1 : ((anorm < F::ssfmin) ? 2 : 0);
+            const T sg = (mode == 0) ? T(1) : ((mode == 1) ? F::ssfmax : F::ssfmin) / anorm;
+            if (mode != 0) {
+                static_for<N>([&](auto I) {
+                    constexpr int p = decltype(I)::value;
+                    d[p] = ((p >= lo) & (p <= hi)) ? d[p] * sg : d[p];
+                    e[p] = ((p >= lo) & (p < hi)) ? e[p] * sg : e[p];
+                });
+            }
+            // converge the end of smaller magnitude first; a tie or NaN
+            // converges the top end first, i.e. mirror. |sg*x| = sg*|x|
+            // exactly, so this compares the scaled end values.
+            const T dlo = F::abs(sd[lo]) * sg, dhi = F::abs(sd[hi]) * sg;
+            mir = !(dhi < dlo);
+            mirror_problem<T, N, RQ, WANTQ>(mir, d, e, q);
+            bt = mir ? N - 1 - hi : lo;
+            bb = mir ? N - 1 - lo : hi;
+            m = bb;
+            // the coupling above the block is zero; the chase may write
+            // it and closing the block restores it
+            zeroed = bt > 0 ? ((M)1 << (bt - 1)) : (M)0;
+            state = ST_ITER;
         }
-        if (state == ST_DONE) break;
+    };
+
+    T x = T(0), y = T(0);  // running pair of the chase
+    while (true) {
+        // ------------------------------------------------------------ settle
+        // Opening and closing blocks are rare (once per block); they run
+        // behind wavefront-wide tests. The per-pass part is straight-line.
+        if (__any(state == ST_OPEN)) {
+            open_blocks();
+            publish();
+        }
+        const bool iter = state == ST_ITER;
+        if (!__any(iter)) break;
+        // deflation test [algo, deflation] at every position; e's found
+        // negligible earlier count too (the chase may overwrite them)
+        M neg = 0;
+        static_for<N - 1>([&](auto I) {
+            constexpr int p = N - 2 - decltype(I)::value;
+            neg = neg + neg + (negligible(e[p], d[p], d[p + 1]) ? (M)1 : (M)0);
+        });
+        neg |= zeroed;
+        const M rng = bit_range<M>(bt, m - 1);
+        const M nb = neg & rng;
+        const M clr = rng & ~neg;
+        // every remaining eigenvalue of the block has converged
+        const bool conv = iter & (clr == 0);
+        const bool go = iter & (clr != 0);
+        // the bottom run of negligible e's deflates 1x1 eigenvalues (new
+        // end t); the last negligible e above t bounds the unreduced part
+        // [s, t] [algo]
+        const int t = msb((M)(clr | (M)1));
+        const M above = nb & bit_range<M>(bt, t - 1);
+        const int s2 = above ? msb(above) + 1 : bt;
+        const M znew = (nb & bit_range<M>(t + 1, m - 1)) | (above ? ((M)1 << (above ? s2 - 1 : 0)) : (M)0);
+        zeroed |= conv ? nb : (go ? znew : (M)0);
+        // next operation: an analytic 2x2 solve, a failure (budget spent)
+        // or a sweep on [s, m]
+        const bool jac = go & (t == s2);
+        const bool fail = go & !jac & (jtot >= nmaxit);
+        const bool sweep = go & !jac & !fail;
+        const int jpos = s2;
+        m = jac ? s2 - 1 : (go ? t + 1 : m);
+        s = go ? s2 : s;
+        jtot += sweep ? 1 : 0;
+        // a failed block, or a converged block with another one after it
+        const bool close_now = fail | (conv & !last);
+        if (__any(close_now)) {
+            if (close_now) {
+                close_block(fail);
+                if (fail) {
+                    failed = true;
+                    M nz = 0;
+                    static_for<N - 1>([&](auto I) {
+                        constexpr int p = N - 2 - decltype(I)::value;
+                        nz = nz + nz + ((e[p] != T(0)) ? (M)1 : (M)0);
+                    });
+                    info = popc((M)(nz & bits_below<M>(n - 1)));
+                    info = info > 0 ? info : 1;
+                }
+                state = fail ? ST_DONE : ST_OPEN;
+            }
+            publish();
+        }
+        // a converged last block is closed after the loop
+        pending = pending | (conv & last);
+        state = (conv & last) ? ST_DONE : state;
+        // shift from the trailing 2x2 (LAPACK form) [algo, shift section];
+        // running pair for the first rotation: (d_s - mu, e_s)
+        const int mi = sweep ? m : 1;
+        const int si = sweep ? s : 0;
+        const T mu = lapack_shift(sd[mi], sd[mi - 1], se[mi - 1]);
+        x = sd[si] - mu;
+        y = se[si];
 
         // ------------------------------------------------------------ chase pass
         // Running pair (x, y), seeded in the settle, and the previous cosine
@@ -373,7 +392,8 @@ __global__ void __launch_bounds__(256) steqr_chunk_kernel(KernelArgs args) {
                 }
             }
         });
-        // analytic 2x2 solves, only when some chunk of the wavefront has one
+        // analytic 2x2 solves [algo, "A deflated block of size 2"
+        // paragraph], only when some chunk of the wavefront has one
         if (__any(jac)) static_for<N - 1>([&](auto I) {
             constexpr int p = decltype(I)::value;
             if (jac & (p == jpos)) {
@@ -393,7 +413,12 @@ __global__ void __launch_bounds__(256) steqr_chunk_kernel(KernelArgs args) {
         publish();
         // a NaN shift turns [s, m] into NaN, a fixed point of every further
         // sweep: spend the rest of the budget at once (same final state)
-        if (sweep & (mu != mu)) jtot = nmaxit;
+        jtot = (sweep & (mu != mu)) ? nmaxit : jtot;
+    }
+    // closes of converged last blocks, all at once
+    if (__any(pending)) {
+        if (pending) close_block(false);
+        publish();
     }
 
     // ---------------------------------------------------------------- sort
