@@ -12,10 +12,11 @@
 //    sort keys are split over the P lanes of the chunk (lane r handles
 //    positions r, r+P, ...) and combined with butterfly shuffles;
 //  * the chase reads d_{p+2}, e_{p+2} at position p (a two-deep window), so
-//    the LDS latency overlaps the rotation; one lane per chunk writes back
-//    the final d_p and e_{p-1};
-//  * Q is written through an LDS slice per row index, so each output row is
-//    written contiguously (a full cache line per row) after the column
+//    the LDS latency overlaps the rotation; every lane of the chunk writes
+//    the same final d_p and e_{p-1} to the same word (no lane mask);
+//  * Q is written through an LDS slice per row index: lane r of a chunk
+//    holds rows r, r+P, ..., so each slice is P consecutive rows of every
+//    chunk's Q, copied out in coalesced 16-byte pieces after the column
 //    permutation of the sort.
 // Citations as in steqr_chunk.hpp ([algo] = the steqr algorithm page,
 // [cta] = "STEQR: the CTA tridiagonal solver").
@@ -112,26 +113,33 @@ __global__ void __launch_bounds__(256) steqr_chunkl_kernel(KernelArgs args) {
         });
         zeromask = chunk_or<P>(part);
     }
+    // lane r of a chunk holds rows r, r+P, r+2P, ... of Q, so that the
+    // chunk's lanes hold P consecutive rows in each row slice i
     T q[RQ][N];
     static_for<RQ>([&](auto II) {
         constexpr int i = decltype(II)::value;
-        const int row = r * R + i;
+        const int row = i * P + r;
         static_for<N>([&](auto J) {
             constexpr int j = decltype(J)::value;
             q[i][j] = (WANTQ & (row == j)) ? T(1) : T(0);
         });
     });
 
+    // ST_OPEN: the chunk's next block is to be opened; ST_ITER: a block is
+    // being reduced; ST_DONE: nothing left to reduce (a converged last block
+    // may still wait for its close, `pending`). All lanes of a chunk hold
+    // the same state, so chunk-wide shuffles inside these branches are safe.
     int state = live ? ST_OPEN : ST_DONE;
-    int l1 = 0, bt = 0, bb = 0, m = 0, s = 0, jpos = -1;
+    int l1 = 0, bt = 0, bb = 0, m = 0, s = 0;
     int jtot = 0;
     const int nmaxit = (args.max_sweeps_per_n > 0 ? args.max_sweeps_per_n : 0) * n;
     bool mir = false, failed = false;
+    bool last = false;     // no block follows the current one
+    bool pending = false;  // converged last block, closed after the loop
     int mode = 0;
     T anorm = T(0);
     M zeroed = 0;
     int info = 0;
-    T mu = T(0);
 
     // reverse the band of the chunk (lane-parallel) and Q's columns
     auto mirror_all = [&]() __attribute__((always_inline)) {
@@ -163,6 +171,8 @@ __global__ void __launch_bounds__(256) steqr_chunkl_kernel(KernelArgs args) {
         }
     };
 
+    // Close the current block: zero the negligible e's found in it, undo the
+    // scaling (d always, e too when the block failed), undo the mirror.
     auto close_block = [&](bool fail) __attribute__((always_inline)) {
         const T un = (mode == 1) ? anorm / F::ssfmax : ((mode == 2) ? anorm / F::ssfmin : T(1));
         static_for<K>([&](auto KK) {
@@ -184,113 +194,136 @@ __global__ void __launch_bounds__(256) steqr_chunkl_kernel(KernelArgs args) {
         zeroed = 0;
     };
 
-    T x = T(0), y = T(0), dcur = T(0);  // running pair and current d_p of the chase
-    while (state != ST_DONE) {
-        bool sweep = false, jac = false;
-        // ------------------------------------------------------------ settle
-        while (true) {
-            if (state == ST_OPEN) {
-                const M avail = ~zeromask & ~bits_below<M>(l1) & bits_below<M>(n - 1);
-                if (avail == 0) {
-                    state = ST_DONE;
-                    break;
-                }
-                const int lo = lsb(avail);
-                const int hi = lsb((M)(zeromask & ~bits_below<M>(lo)));
-                l1 = hi + 1;
-                T an = T(0);
-                bool hasnan = false;
-                static_for<K>([&](auto KK) {
-                    constexpr int k = decltype(KK)::value;
-                    const int p = r + k * P;
-                    const bool ind = (p >= lo) & (p <= hi);
-                    const bool ine = (p >= lo) & (p < hi);
-                    const T dv = sd[p], ev = se[p];
-                    an = ind ? F::max(an, F::abs(dv)) : an;
-                    an = ine ? F::max(an, F::abs(ev)) : an;
-                    hasnan = hasnan | (ind & (dv != dv)) | (ine & (ev != ev));
-                });
-                an = chunk_max<P>(an);
-                hasnan = chunk_or<P>(hasnan ? 1u : 0u) != 0;
-                anorm = hasnan ? F::qnan() : an;
-                if (anorm == T(0)) continue;
-                mode = (anorm > F::ssfmax) ? 1 : ((anorm < F::ssfmin) ? 2 : 0);
-                if (mode != 0) {
-                    const T sg = ((mode == 1) ? F::ssfmax : F::ssfmin) / anorm;
-                    static_for<K>([&](auto KK) {
-                        constexpr int k = decltype(KK)::value;
-                        const int p = r + k * P;
-                        const T dv = sd[p], ev = se[p];
-                        sd[p] = ((p >= lo) & (p <= hi)) ? dv * sg : dv;
-                        se[p] = ((p >= lo) & (p < hi)) ? ev * sg : ev;
-                    });
-                    __builtin_amdgcn_wave_barrier();
-                }
-                mir = !(F::abs(sd[hi]) < F::abs(sd[lo]));
-                if (mir) mirror_all();
-                bt = mir ? N - 1 - hi : lo;
-                bb = mir ? N - 1 - lo : hi;
-                m = bb;
-                zeroed = bt > 0 ? ((M)1 << (bt - 1)) : (M)0;  // zero coupling above
-                state = ST_ITER;
-            }
-            // deflation test [algo, deflation], positions split over the chunk
-            M neg;
-            {
-                M part = 0;
-                static_for<K>([&](auto KK) {
-                    constexpr int k = decltype(KK)::value;
-                    const int p = r + k * P;
-                    if (p < N - 1)
-                        part |= negligible(se[p], sd[p], sd[p + 1 < N ? p + 1 : N - 1])
-                                    ? ((M)1 << p) : (M)0;
-                });
-                neg = chunk_or<P>(part) | zeroed;
-            }
-            const M rng = bit_range<M>(bt, m - 1);
-            const M nb = neg & rng;
-            const M clr = rng & ~neg;
-            if (clr == 0) {
-                zeroed |= nb;
-                close_block(false);
-                state = ST_OPEN;
-                continue;
-            }
-            const int t = msb(clr);
-            zeroed |= nb & bit_range<M>(t + 1, m - 1);
-            m = t + 1;
-            const M above = nb & bit_range<M>(bt, t - 1);
-            s = above ? msb(above) + 1 : bt;
-            if (above) zeroed |= (M)1 << (s - 1);
-            if (m - s == 1) {
-                jac = true;
-                jpos = s;
-                m = s - 1;
-                break;
-            }
-            if (jtot >= nmaxit) {
-                failed = true;
-                close_block(true);
-                M part = 0;
-                static_for<K>([&](auto KK) {
-                    constexpr int k = decltype(KK)::value;
-                    const int p = r + k * P;
-                    part |= ((p < n - 1) & (se[p] != T(0))) ? ((M)1 << p) : (M)0;
-                });
-                info = popc(chunk_or<P>(part));
-                info = info > 0 ? info : 1;
+    // Open the next block of every chunk in ST_OPEN: skip 1x1 blocks (zero
+    // e) and stop at the first zero e at or right of the block start [algo,
+    // steqr_cta paragraph]; skip blocks of norm zero; scale [algo, scaling];
+    // pick the converging end and mirror.
+    auto open_blocks = [&]() __attribute__((always_inline)) {
+        while (state == ST_OPEN) {
+            const M avail = ~zeromask & ~bits_below<M>(l1) & bits_below<M>(n - 1);
+            if (avail == 0) {
                 state = ST_DONE;
                 break;
             }
-            ++jtot;
-            mu = lapack_shift(sd[m], sd[m - 1], se[m - 1]);
-            dcur = sd[s];
-            x = dcur - mu;
-            y = se[s];
-            sweep = true;
-            break;
+            const int lo = lsb(avail);
+            const int hi = lsb((M)(zeromask & ~bits_below<M>(lo)));
+            l1 = hi + 1;
+            last = (avail & ~bits_below<M>(l1)) == 0;
+            T an = T(0);
+            bool hasnan = false;
+            static_for<K>([&](auto KK) {
+                constexpr int k = decltype(KK)::value;
+                const int p = r + k * P;
+                const bool ind = (p >= lo) & (p <= hi);
+                const bool ine = (p >= lo) & (p < hi);
+                const T dv = sd[p], ev = se[p];
+                an = ind ? F::max(an, F::abs(dv)) : an;
+                an = ine ? F::max(an, F::abs(ev)) : an;
+                hasnan = hasnan | (ind & (dv != dv)) | (ine & (ev != ev));
+            });
+            an = chunk_max<P>(an);
+            hasnan = chunk_or<P>(hasnan ? 1u : 0u) != 0;
+            anorm = hasnan ? F::qnan() : an;
+            if (anorm == T(0)) continue;
+            mode = (anorm > F::ssfmax) ? 1 : ((anorm < F::ssfmin) ? 2 : 0);
+            if (mode != 0) {
+                const T sg = ((mode == 1) ? F::ssfmax : F::ssfmin) / anorm;
+                static_for<K>([&](auto KK) {
+                    constexpr int k = decltype(KK)::value;
+                    const int p = r + k * P;
+                    const T dv = sd[p], ev = se[p];
+                    sd[p] = ((p >= lo) & (p <= hi)) ? dv * sg : dv;
+                    se[p] = ((p >= lo) & (p < hi)) ? ev * sg : ev;
+                });
+                __builtin_amdgcn_wave_barrier();
+            }
+            // converge the end of smaller magnitude first; a tie or NaN
+            // converges the top end first, i.e. mirror
+            mir = !(F::abs(sd[hi]) < F::abs(sd[lo]));
+            if (mir) mirror_all();
+            bt = mir ? N - 1 - hi : lo;
+            bb = mir ? N - 1 - lo : hi;
+            m = bb;
+            zeroed = bt > 0 ? ((M)1 << (bt - 1)) : (M)0;  // zero coupling above
+            state = ST_ITER;
         }
-        if (state == ST_DONE) break;
+    };
+
+    T x = T(0), y = T(0), dcur = T(0);  // running pair and current d_p of the chase
+    while (true) {
+        // ------------------------------------------------------------ settle
+        // Opening and closing blocks are rare (once per block); they run
+        // behind wavefront-wide tests. The per-pass part is straight-line.
+        if (__any(state == ST_OPEN)) open_blocks();
+        const bool iter = state == ST_ITER;
+        if (!__any(iter)) break;
+        // deflation test [algo, deflation], positions split over the chunk;
+        // e's found negligible earlier count too
+        M neg;
+        {
+            M part = 0;
+            static_for<K>([&](auto KK) {
+                constexpr int k = decltype(KK)::value;
+                const int p = r + k * P;
+                if (p < N - 1)
+                    part |= negligible(se[p], sd[p], sd[p + 1 < N ? p + 1 : N - 1])
+                                ? ((M)1 << p) : (M)0;
+            });
+            neg = chunk_or<P>(part) | zeroed;
+        }
+        const M rng = bit_range<M>(bt, m - 1);
+        const M nb = neg & rng;
+        const M clr = rng & ~neg;
+        // every remaining eigenvalue of the block has converged
+        const bool conv = iter & (clr == 0);
+        const bool go = iter & (clr != 0);
+        // the bottom run of negligible e's deflates 1x1 eigenvalues (new
+        // end t); the last negligible e above t bounds the unreduced part
+        // [s, t] [algo]
+        const int t = msb((M)(clr | (M)1));
+        const M above = nb & bit_range<M>(bt, t - 1);
+        const int s2 = above ? msb(above) + 1 : bt;
+        const M znew = (nb & bit_range<M>(t + 1, m - 1)) | (above ? ((M)1 << (above ? s2 - 1 : 0)) : (M)0);
+        zeroed |= conv ? nb : (go ? znew : (M)0);
+        // next operation: an analytic 2x2 solve, a failure (budget spent)
+        // or a sweep on [s, m]
+        const bool jac = go & (t == s2);
+        const bool fail = go & !jac & (jtot >= nmaxit);
+        const bool sweep = go & !jac & !fail;
+        const int jpos = s2;
+        m = jac ? s2 - 1 : (go ? t + 1 : m);
+        s = go ? s2 : s;
+        jtot += sweep ? 1 : 0;
+        // a failed block, or a converged block with another one after it
+        const bool close_now = fail | (conv & !last);
+        if (__any(close_now)) {
+            if (close_now) {
+                close_block(fail);
+                if (fail) {
+                    failed = true;
+                    M part = 0;
+                    static_for<K>([&](auto KK) {
+                        constexpr int k = decltype(KK)::value;
+                        const int p = r + k * P;
+                        part |= ((p < n - 1) & (se[p] != T(0))) ? ((M)1 << p) : (M)0;
+                    });
+                    info = popc(chunk_or<P>(part));
+                    info = info > 0 ? info : 1;
+                }
+                state = fail ? ST_DONE : ST_OPEN;
+            }
+        }
+        // a converged last block is closed after the loop
+        pending = pending | (conv & last);
+        state = (conv & last) ? ST_DONE : state;
+        // shift from the trailing 2x2 (LAPACK form) [algo, shift section];
+        // running pair for the first rotation: (d_s - mu, e_s)
+        const int mi = sweep ? m : 1;
+        const int si = sweep ? s : 0;
+        const T mu = lapack_shift(sd[mi], sd[mi - 1], se[mi - 1]);
+        dcur = sd[si];
+        x = dcur - mu;
+        y = se[si];
 
         // ------------------------------------------------------------ chase pass
         // window: (d0, e0) = original d_p, e_p; (d1, e1) = d_{p+1}, e_{p+1};
@@ -353,12 +386,18 @@ __global__ void __launch_bounds__(256) steqr_chunkl_kernel(KernelArgs args) {
             d1 = d2;
             e1 = e2;
         });
-        if (sweep & writer) {
+        if (sweep) {
             sd[m] = dcur;
             se[m - 1] = x;
         }
         __builtin_amdgcn_wave_barrier();
-        if (sweep & (mu != mu)) jtot = nmaxit;
+        // a NaN shift turns [s, m] into NaN, a fixed point of every further
+        // sweep: spend the rest of the budget at once (same final state)
+        jtot = (sweep & (mu != mu)) ? nmaxit : jtot;
+    }
+    // closes of converged last blocks, all at once
+    if (__any(pending)) {
+        if (pending) close_block(false);
     }
 
     // ---------------------------------------------------------------- sort
@@ -393,24 +432,51 @@ __global__ void __launch_bounds__(256) steqr_chunkl_kernel(KernelArgs args) {
         if (args.info != nullptr && writer) args.info[prob] = info;
     }
     if constexpr (WANTQ) {
-        // slice i: row r*R + i of every chunk, columns permuted by rank,
-        // staged in LDS then written row by row (a row is contiguous in HBM)
+        // Row slice i: lane (chunk c, r) holds row i*P + r of its problem, so
+        // the chunk's P rows are one contiguous range of its Q in HBM. Each
+        // lane writes its row, columns permuted by rank, to its own LDS row
+        // (stride N+1 against bank conflicts); then the wavefront copies the
+        // slice out in 16-byte pieces, consecutive lanes at consecutive
+        // addresses within each chunk's range.
         T* const myrow = stage + lane * S::STAGE_STRIDE;
-        const long qbase = prob * (long)n * n;
+        const long first = ((long)blockIdx.x * (blockDim.x >> 6) + wave) * CH;
+        const bool vec = ((n & 3) == 0) & ((reinterpret_cast<uintptr_t>(gq) & 15) == 0);
         static_for<R>([&](auto II) {
             constexpr int i = decltype(II)::value;
-            const int row = r * R + i;
             static_for<N>([&](auto J) {
                 constexpr int j = decltype(J)::value;
                 if (j < n) myrow[srank[j]] = q[i][j];
             });
             __builtin_amdgcn_wave_barrier();
-            if (live & (row < n)) {
-                T* dst = gq + qbase + (long)row * n;
-                static_for<N>([&](auto J) {
-                    constexpr int j = decltype(J)::value;
-                    if (j < n) dst[j] = myrow[j];
+            if (vec) {
+                constexpr int V = 16 / sizeof(T);
+                constexpr int PR = N / V;  // pieces per staged row
+                static_for<PR>([&](auto KK) {
+                    constexpr int k = decltype(KK)::value;
+                    const int idx = k * 64 + lane;
+                    const int L = idx / PR, c4 = idx % PR;  // source lane (row), piece
+                    const int c = L / P, rr = L % P;
+                    const long pr = first + c;
+                    const int row = i * P + rr;
+                    if ((pr < (long)args.batch) & (row < n) & (c4 * V < n)) {
+                        const T* src = stage + L * S::STAGE_STRIDE + c4 * V;
+                        T* dst = gq + (pr * n + row) * (long)n + c4 * V;
+                        if constexpr (sizeof(T) == 4) {
+                            *reinterpret_cast<float4*>(dst) = make_float4(src[0], src[1], src[2], src[3]);
+                        } else {
+                            *reinterpret_cast<double2*>(dst) = make_double2(src[0], src[1]);
+                        }
+                    }
                 });
+            } else {
+                const int row = i * P + r;
+                if (live & (row < n)) {
+                    T* dst = gq + (prob * (long)n + row) * n;
+                    static_for<N>([&](auto J) {
+                        constexpr int j = decltype(J)::value;
+                        if (j < n) dst[j] = myrow[j];
+                    });
+                }
             }
             __builtin_amdgcn_wave_barrier();
         });
