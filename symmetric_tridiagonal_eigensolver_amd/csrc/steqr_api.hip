@@ -33,7 +33,7 @@ int default_lanes(int dtype, int N, int jobz, int band) {
     if (jobz) {
         if (N == 4) return 4;
         if (N == 8) return dtype == STEQR_F32 ? 2 : 4;
-        if (N == 16) return band == 2 ? 8 : 4;
+        if (N == 16) return 4;
         return band == 2 ? 8 : 16;  // N == 32
     }
     if (N == 32 && dtype == STEQR_F32) return 2;
