@@ -347,11 +347,24 @@ __global__ void __launch_bounds__(256) steqr_chunk_kernel(KernelArgs args) {
         state = (conv & last) ? ST_DONE : state;
         // shift from the trailing 2x2 (LAPACK form) [algo, shift section];
         // running pair for the first rotation: (d_s - mu, e_s)
-        const int mi = sweep ? m : 1;
+        const int mi = sweep ? m : (jac ? jpos + 1 : 1);
         const int si = sweep ? s : 0;
-        const T mu = lapack_shift(sd[mi], sd[mi - 1], se[mi - 1]);
+        const T dm = sd[mi], dm1 = sd[mi - 1], em1 = se[mi - 1];
+        const T mu = lapack_shift(dm, dm1, em1);
         x = sd[si] - mu;
         y = se[si];
+        // A 2x2 block at (jpos, jpos+1) [algo, "A deflated block of size 2"
+        // paragraph]: its closed-form Schur rotation becomes the running
+        // pair of a one-step chase at jpos (lartg returns that rotation), so
+        // it is applied by the same similarity and Q update as the sweeps.
+        // The leftover e_jpos (rounding size) joins `zeroed`.
+        if (__any(jac)) {
+            T rt1, rt2, cs, sj;
+            sym2x2(dm1, em1, dm, rt1, rt2, cs, sj);
+            x = jac ? cs : x;
+            y = jac ? -sj : y;
+            zeroed |= jac ? ((M)1 << jpos) : (M)0;
+        }
 
         // ------------------------------------------------------------ chase pass
         // Running pair (x, y), seeded in the settle, and the previous cosine
@@ -363,7 +376,7 @@ __global__ void __launch_bounds__(256) steqr_chunk_kernel(KernelArgs args) {
         T cp = T(1);
         // step p runs when s <= p < m: one unsigned compare of p - s with
         // the step count (0 when this chunk does not sweep)
-        const unsigned steps = sweep ? (unsigned)(m - s) : 0u;
+        const unsigned steps = sweep ? (unsigned)(m - s) : (jac ? 1u : 0u);
         static_for<N - 1>([&](auto I) {
             constexpr int p = decltype(I)::value;
             if ((unsigned)(p - s) < steps) {
@@ -388,24 +401,6 @@ __global__ void __launch_bounds__(256) steqr_chunk_kernel(KernelArgs args) {
                     static_for<R>([&](auto II) {
                         constexpr int i = decltype(II)::value;
                         F::rot(q[i][p], q[i][p + 1], c, sn);
-                    });
-                }
-            }
-        });
-        // analytic 2x2 solves [algo, "A deflated block of size 2"
-        // paragraph], only when some chunk of the wavefront has one
-        if (__any(jac)) static_for<N - 1>([&](auto I) {
-            constexpr int p = decltype(I)::value;
-            if (jac & (p == jpos)) {
-                T rt1, rt2, cs, sj;
-                sym2x2(d[p], e[p], d[p + 1], rt1, rt2, cs, sj);
-                d[p] = rt1;
-                d[p + 1] = rt2;
-                e[p] = T(0);
-                if constexpr (WANTQ) {
-                    static_for<R>([&](auto II) {
-                        constexpr int i = decltype(II)::value;
-                        F::rot(q[i][p], q[i][p + 1], cs, -sj);
                     });
                 }
             }

@@ -318,12 +318,25 @@ __global__ void __launch_bounds__(256) steqr_chunkl_kernel(KernelArgs args) {
         state = (conv & last) ? ST_DONE : state;
         // shift from the trailing 2x2 (LAPACK form) [algo, shift section];
         // running pair for the first rotation: (d_s - mu, e_s)
-        const int mi = sweep ? m : 1;
-        const int si = sweep ? s : 0;
-        const T mu = lapack_shift(sd[mi], sd[mi - 1], se[mi - 1]);
+        const int mi = sweep ? m : (jac ? jpos + 1 : 1);
+        const int si = sweep ? s : (jac ? jpos : 0);
+        const T dm = sd[mi], dm1 = sd[mi - 1], em1 = se[mi - 1];
+        const T mu = lapack_shift(dm, dm1, em1);
         dcur = sd[si];
         x = dcur - mu;
         y = se[si];
+        // A 2x2 block at (jpos, jpos+1) [algo, "A deflated block of size 2"
+        // paragraph]: its closed-form Schur rotation becomes the running
+        // pair of a one-step chase at jpos (lartg returns that rotation), so
+        // it is applied by the same similarity and Q update as the sweeps.
+        // The leftover e_jpos (rounding size) joins `zeroed`.
+        if (__any(jac)) {
+            T rt1, rt2, cs, sj;
+            sym2x2(dm1, em1, dm, rt1, rt2, cs, sj);
+            x = jac ? cs : x;
+            y = jac ? -sj : y;
+            zeroed |= jac ? ((M)1 << jpos) : (M)0;
+        }
 
         // ------------------------------------------------------------ chase pass
         // window: (d0, e0) = original d_p, e_p; (d1, e1) = d_{p+1}, e_{p+1};
@@ -333,8 +346,7 @@ __global__ void __launch_bounds__(256) steqr_chunkl_kernel(KernelArgs args) {
         T cp = T(1);
         // step p runs when s <= p < m: one unsigned compare of p - s with
         // the step count (0 when this chunk does not sweep)
-        const unsigned steps = sweep ? (unsigned)(m - s) : 0u;
-        const int jat = jac ? jpos : -1;  // position of this chunk's 2x2 solve
+        const unsigned steps = sweep ? (unsigned)(m - s) : (jac ? 1u : 0u);
         static_for<N - 1>([&](auto I) {
             constexpr int p = decltype(I)::value;
             T d2 = T(0), e2 = T(0);
@@ -368,27 +380,16 @@ __global__ void __launch_bounds__(256) steqr_chunkl_kernel(KernelArgs args) {
                     });
                 }
             }
-            if (p == jat) {
-                T rt1, rt2, cs, sj;
-                sym2x2(d0, e0, d1, rt1, rt2, cs, sj);
-                sd[p] = rt1;
-                sd[p + 1] = rt2;
-                se[p] = T(0);
-                if constexpr (WANTQ) {
-                    static_for<R>([&](auto II) {
-                        constexpr int i = decltype(II)::value;
-                        F::rot(q[i][p], q[i][p + 1], cs, -sj);
-                    });
-                }
-            }
             d0 = d1;
             e0 = e1;
             d1 = d2;
             e1 = e2;
         });
-        if (sweep) {
-            sd[m] = dcur;
-            se[m - 1] = x;
+        if (steps != 0u) {
+            // the last step's d_{p+1} and e_p
+            const int me = s + (int)steps;
+            sd[me] = dcur;
+            se[me - 1] = x;
         }
         __builtin_amdgcn_wave_barrier();
         // a NaN shift turns [s, m] into NaN, a fixed point of every further
