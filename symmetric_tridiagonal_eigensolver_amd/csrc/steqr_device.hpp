@@ -160,7 +160,11 @@ __device__ __forceinline__ bool negligible(T e, T d1, T d2) {
 }
 
 // Givens rotation [algo, "G(c,s)" paragraph]: G(c,s) = [[c,-s],[s,c]],
-// G^T (f, g)^T = (r, 0)^T, r with the sign of f (so c >= 0).
+// G^T (f, g)^T = (r, 0)^T with r = sqrt(f^2 + g^2) >= 0 (c takes the sign
+// of f). The pages' convention (r with the sign of f, c >= 0) differs by the
+// rotation -G, which gives the same similarity and flips the signs of two
+// Q columns and of an off-diagonal entry only; the plain one saves the sign
+// transfer at every step.
 //
 // Scaled form (always valid): f and g are first scaled by an exact power of
 // two (2^-k with k the exponent of |f| + |g|, which lies within a factor 2
@@ -186,11 +190,10 @@ __device__ __forceinline__ void lartg_scaled(T f, T g, T& c, T& s, T& r) {
         const T res = F::fma(-h, y, T(1));
         y = F::fma(y * res, T(0.5), y);
     }
-    const T ys = F::copysign(y, f);
     const bool gz = (g == T(0));
-    c = gz ? T(1) : fs * ys;
-    s = gz ? T(0) : gs * ys;
-    r = gz ? f : F::ldexp(t * ys, ex);
+    c = gz ? T(1) : fs * y;
+    s = gz ? T(0) : gs * y;
+    r = gz ? f : F::ldexp(t * y, ex);
 }
 
 // Givens rotation, fast form: t = f^2 + g^2 directly; whenever t is not a
@@ -199,7 +202,8 @@ __device__ __forceinline__ void lartg_scaled(T f, T g, T& c, T& s, T& r) {
 // scalar branch the wavefront skips when no active lane needs the scaled
 // form (UNIFORM: every lane holds the same (f, g), one lane decides). With
 // t normal the unscaled formulas are exact to a few ulps, g = 0 included
-// (c = |f| / |f|, s = 0, r = f).
+// (c = f / |f| = +-1, s = 0, r = |f|: a valid rotation, like the scaled
+// form's (1, 0, f)).
 template <typename T, bool UNIFORM = false>
 __device__ __forceinline__ void lartg(T f, T g, T& c, T& s, T& r) {
     using F = Fp<T>;
@@ -211,10 +215,9 @@ __device__ __forceinline__ void lartg(T f, T g, T& c, T& s, T& r) {
         const T res = F::fma(-h, y, T(1));
         y = F::fma(y * res, T(0.5), y);
     }
-    const T ys = F::copysign(y, f);
-    c = f * ys;
-    s = g * ys;
-    r = t * ys;
+    c = f * y;
+    s = g * y;
+    r = t * y;
     if constexpr (UNIFORM) {
         // every lane holds the same (f, g): one scalar branch
         if (__builtin_amdgcn_readfirstlane((int)!F::pos_normal(t))) lartg_scaled(f, g, c, s, r);
