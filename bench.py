@@ -53,28 +53,37 @@ def bytes_per_matrix(n: int, itemsize: int, jobz: bool) -> int:
     return ((2 * n - 1) + n + (n * n if jobz else 0)) * itemsize
 
 
-def kernel_source_hash() -> str:
+# Sources each kernel family is compiled from (its hash guards committed
+# counter records against kernel changes).
+KERNEL_SOURCES = {
+    "chunk": ["steqr_device.hpp", "steqr_chunk.hpp"],
+    "chunkl": ["steqr_device.hpp", "steqr_chunk.hpp", "steqr_chunkl.hpp"],
+    "wave": ["steqr_device.hpp", "steqr_chunk.hpp", "steqr_wave.hpp"],
+}
+
+
+def kernel_source_hash(family: str = "chunk") -> str:
     h = hashlib.sha256()
     cs = os.path.join(ROOT, "symmetric_tridiagonal_eigensolver_amd", "csrc")
-    for f in sorted(os.listdir(cs)):
-        if f.endswith((".hip", ".hpp")):
-            h.update(open(os.path.join(cs, f), "rb").read())
+    for f in KERNEL_SOURCES[family]:
+        h.update(open(os.path.join(cs, f), "rb").read())
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(wname: str, jobz: bool):
-    """HBM bytes per launch from the committed counter summary, or None when
-    absent or taken on other kernel sources."""
-    p = os.path.join(ROOT, "profiles", "traffic_%s_%s.json" % (wname, "V" if jobz else "N"))
+def counters_from_profiles(wname: str, jobz: bool, family: str):
+    """Per-launch counter record (HBM bytes, executed VALU instructions and
+    FLOPs, replicated-batch instructions) committed under profiles/, or None
+    when absent or taken on other kernel sources."""
+    p = os.path.join(ROOT, "profiles", "counters_%s_%s.json" % (wname, "V" if jobz else "N"))
     if not os.path.exists(p):
         return None
     try:
         t = json.load(open(p))
     except Exception:
         return None
-    if t.get("kernel_source_hash") != kernel_source_hash():
+    if t.get("kernel_source_hash") != kernel_source_hash(family):
         return None
-    return t.get("hbm_bytes_per_launch")
+    return t
 
 
 def cpu_baseline(d: np.ndarray, e: np.ndarray, jobz: bool, wname: str):
@@ -227,18 +236,27 @@ def main() -> int:
     dtype = w.dtype
     peak = PEAK_TFLOPS[dtype]
     roof = None
+    family = ("wave" if plan["lanes_per_problem"] == 64 else
+              ("chunkl" if plan["band_storage"] == 2 else "chunk"))
     if flops is not None:
         ach = flops / sec / 1e12
+        ctr = None if args.replicate else counters_from_profiles(w.name, jobz, family)
         roof = {"kernel": "steqr_%s_kernel<%s, N=%d, P=%d, %s>"
-                          % ("wave" if plan["lanes_per_problem"] == 64 else
-                             ("chunkl" if plan["band_storage"] == 2 else "chunk"),
-                             "float" if dtype == "f32" else "double", plan["padded_n"],
+                          % (family, "float" if dtype == "f32" else "double", plan["padded_n"],
                              plan["lanes_per_problem"], "V" if jobz else "N"),
                 "bound": "alu", "achieved": ach, "peak": peak, "unit": "TFLOP/s",
                 "frac": ach / peak,
-                "traffic": traffic_from_profiles(w.name, jobz),
+                "traffic": None if ctr is None else ctr.get("hbm_bytes_per_launch"),
                 "algorithmic_flops_per_launch": flops,
                 "algorithmic_flops_per_matrix": flops / nb}
+        if ctr is not None and ctr.get("executed_flops_per_launch"):
+            # executed VALU FLOPs (64 lanes x FP counter) at this run's time
+            ex = ctr["executed_flops_per_launch"] / sec / 1e12
+            roof["executed"] = {"tflops": ex, "frac": ex / peak,
+                                "flops_per_launch": ctr["executed_flops_per_launch"],
+                                "source": "rocprofv3 SQ_INSTS_VALU_FLOPS_FP%s" % dtype[1:]}
+        if ctr is not None and ctr.get("valu_insts_replicated"):
+            roof["divergence"] = ctr["valu_insts_per_launch"] / ctr["valu_insts_replicated"]
     bpm = bytes_per_matrix(n, d.itemsize, jobz)
     out = {
         "metric": "matrices/sec (us/matrix) float n=16 jobz=V; % FP32 VALU peak",
