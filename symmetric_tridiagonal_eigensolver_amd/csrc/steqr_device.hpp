@@ -27,6 +27,16 @@ template <int COUNT, typename Fn>
 __device__ __forceinline__ void static_for(Fn&& fn) {
     if constexpr (COUNT > 0) static_for_impl(fn, std::make_integer_sequence<int, COUNT>{});
 }
+// As static_for, but stops after the first index whose body returns false
+// (meant for wave-uniform conditions: the stop is one scalar branch).
+template <typename Fn, int... Is>
+__device__ __forceinline__ void static_for_while_impl(Fn&& fn, std::integer_sequence<int, Is...>) {
+    (void)(fn(std::integral_constant<int, Is>{}) && ...);
+}
+template <int COUNT, typename Fn>
+__device__ __forceinline__ void static_for_while(Fn&& fn) {
+    if constexpr (COUNT > 0) static_for_while_impl(fn, std::make_integer_sequence<int, COUNT>{});
+}
 
 // Precision-dependent constants and hardware helpers.
 //  eps2    = eps^2 with eps the unit roundoff (2^-24 / 2^-53)  [algo, deflation]
@@ -219,8 +229,8 @@ __device__ __forceinline__ void lartg(T f, T g, T& c, T& s, T& r) {
     s = g * y;
     r = t * y;
     if constexpr (UNIFORM) {
-        // every lane holds the same (f, g): one scalar branch
-        if (__builtin_amdgcn_readfirstlane((int)!F::pos_normal(t))) lartg_scaled(f, g, c, s, r);
+        // every lane holds the same (f, g): the ballot is all or nothing
+        if (__builtin_amdgcn_ballot_w64(F::not_pos_normal(t))) lartg_scaled(f, g, c, s, r);
     } else {
         const bool slow = F::not_pos_normal(t);
         if (__builtin_amdgcn_ballot_w64(slow)) {

@@ -230,9 +230,10 @@ __global__ void __launch_bounds__(256) steqr_wave_kernel(KernelArgs args) {
             T dcur = sd[s], ecur = se[s];
             T x = dcur - mu, y = ecur, cp = T(1);
             T dnext = sd[s + 1], enext = se[s + 1];
-            static_for<N - 1>([&](auto I) {
+            // positions s .. m-1; the walk stops after m-1 (uniform branch)
+            static_for_while<N - 1>([&](auto I) {
                 constexpr int p = decltype(I)::value;
-                if ((p >= s) & (p < m)) {
+                if (p >= s) {
                     // r goes to e_{p-1}: at the first step a zero coupling or
                     // an e already in `zeroed`, restored when the block closes
                     const T dp1 = dnext, ep1 = enext;
@@ -260,6 +261,7 @@ __global__ void __launch_bounds__(256) steqr_wave_kernel(KernelArgs args) {
                         F::rot(q[p], q[p + 1], c, sn);
                     }
                 }
+                return p + 1 < m;
             });
             sd[m] = dcur;
             se[m - 1] = x;
