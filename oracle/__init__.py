@@ -62,7 +62,8 @@ def lib(path: Optional[str] = None) -> _ct.CDLL:
             P = _ct.POINTER(ct)
             f = getattr(L, "oracle_steqr_batched_" + sfx)
             f.restype = _ct.c_int
-            f.argtypes = [_ct.c_void_p] * 6 + [_ct.c_int, _ct.c_long, _ct.c_int, _ct.c_int]
+            f.argtypes = [_ct.c_void_p] * 6 + [_ct.c_int, _ct.c_long, _ct.c_int, _ct.c_int,
+                                               _ct.c_int]
             f = getattr(L, "oracle_lartg_" + sfx)
             f.restype = None
             f.argtypes = [ct, ct, P, P, P]
@@ -72,10 +73,11 @@ def lib(path: Optional[str] = None) -> _ct.CDLL:
             f = getattr(L, "oracle_sym2x2_" + sfx)
             f.restype = None
             f.argtypes = [ct, ct, ct, P, P, P, P]
-            f = getattr(L, "oracle_sweep_" + sfx)
-            f.restype = _ct.c_long
-            f.argtypes = [_ct.c_void_p, _ct.c_void_p, _ct.c_void_p, _ct.c_int,
-                          _ct.c_int, _ct.c_int, ct]
+            for name in ("oracle_sweep_", "oracle_sweep_pg_"):
+                f = getattr(L, name + sfx)
+                f.restype = _ct.c_long
+                f.argtypes = [_ct.c_void_p, _ct.c_void_p, _ct.c_void_p, _ct.c_int,
+                              _ct.c_int, _ct.c_int, ct]
             f = getattr(L, "oracle_constants_" + sfx)
             f.restype = None
             f.argtypes = [_ct.c_void_p]
@@ -98,9 +100,10 @@ def _ptr(a: Optional[_np.ndarray]):
 
 def steqr(d: _np.ndarray, e: _np.ndarray, jobz: bool = True,
           max_sweeps_per_n: int = 30, sort: bool = True, threads: int = 1,
-          libpath: Optional[str] = None
+          libpath: Optional[str] = None, scheme: int = 0
           ) -> Tuple[_np.ndarray, Optional[_np.ndarray], _np.ndarray, _np.ndarray]:
     """Solve a batch. d: (batch, n), e: (batch, n-1), same float dtype.
+    scheme: 0 = EXP sweeps (local similarities), 1 = PG (Parlett-Gray) sweeps.
 
     Returns (lam (batch, n), Q (batch, n, n) or None, info (batch,) int32,
     stats (batch, 3) int64 = [implicit sweeps, sweep rotations, 2x2 solves]).
@@ -129,7 +132,7 @@ def steqr(d: _np.ndarray, e: _np.ndarray, jobz: bool = True,
                   None if Q is None else Q.ctypes.data + lo * n * n * it,
                   info.ctypes.data + lo * 4,
                   stats.ctypes.data + lo * 3 * 8,
-                  n, cnt, int(max_sweeps_per_n), int(bool(sort)))
+                  n, cnt, int(max_sweeps_per_n), int(bool(sort)), int(scheme))
 
     threads = max(1, min(int(threads), batch))
     if threads == 1:
@@ -169,14 +172,16 @@ def sym2x2(a: float, b: float, c: float, dtype=_np.float64, libpath=None):
 
 
 def sweep(d: _np.ndarray, e: _np.ndarray, Q: Optional[_np.ndarray], s: int, m: int,
-          mu: float, libpath=None) -> int:
-    """One implicit QR sweep on [s, m] in place (d: (n,), e: (n-1,), Q: (n,n))."""
+          mu: float, libpath=None, scheme: int = 0) -> int:
+    """One implicit QR sweep on [s, m] in place (d: (n,), e: (n-1,), Q: (n,n)),
+    EXP form (scheme 0) or PG form (scheme 1)."""
     n = d.shape[0]
     assert d.flags.c_contiguous and e.flags.c_contiguous
     assert 0 <= s < m < n
     if Q is not None:
         assert Q.flags.c_contiguous and Q.shape == (n, n) and Q.dtype == d.dtype
-    return getattr(lib(libpath), "oracle_sweep_" + _sfx(d.dtype))(
+    name = "oracle_sweep_pg_" if scheme else "oracle_sweep_"
+    return getattr(lib(libpath), name + _sfx(d.dtype))(
         d.ctypes.data, e.ctypes.data, _ptr(Q), n, s, m, mu)
 
 

@@ -163,6 +163,45 @@ long SFX(oracle_sweep)(REAL *d, REAL *e, REAL *Q, int n, int s, int m, REAL mu)
     return rots;
 }
 
+/* One implicit QR sweep on [s, m] in the Parlett-Gray (PG) form of the
+ * algorithm page ("the two CTA update schemes"): the scalars (g, p, c, s)
+ * are carried along the sweep instead of writing each local similarity.
+ * Step i (QR form, as the page writes it):
+ *   f_i = s_{i-1} e_i,  (c_i, s_i, r_i) = lartg(g_{i-1}, f_i),
+ *   g*_i = d_i - p_{i-1},  r*_i = (d_{i+1} - g*_i) s_i + 2 c_i c_{i-1} e_i,
+ *   p_i = s_i r*_i,  d_i <- g*_i + p_i,  g_i = c_i r*_i - c_{i-1} e_i,
+ * with e_{i-1} <- r_i for i > s. The page leaves the start and the end
+ * implicit; read plainly: g_{s-1} = d_s - mu (the shifted corner that the
+ * first rotation annihilates), s_{s-1} = c_{s-1} = 1, p_{s-1} = 0, and
+ * after the last step d_m <- d_m - p_{m-1}, e_{m-1} <- g_{m-1}. Q receives
+ * the same rotations as in the EXP form. Returns the number of rotations. */
+long SFX(oracle_sweep_pg)(REAL *d, REAL *e, REAL *Q, int n, int s, int m, REAL mu)
+{
+    REAL g = d[s] - mu;
+    REAL p = (REAL)0, cprev = (REAL)1, sprev = (REAL)1;
+    long rots = 0;
+    for (int k = s; k < m; ++k) {
+        REAL f = sprev * e[k];
+        REAL c, sn, r;
+        SFX(oracle_lartg)(g, f, &c, &sn, &r);
+        if (k > s)
+            e[k - 1] = r;
+        REAL gs = d[k] - p;
+        REAL rs = (d[k + 1] - gs) * sn + (REAL)2 * c * cprev * e[k];
+        p = sn * rs;
+        d[k] = gs + p;
+        g = c * rs - cprev * e[k];
+        if (Q)
+            SFX(rot_cols)(Q, n, k, c, sn);
+        cprev = c;
+        sprev = sn;
+        ++rots;
+    }
+    d[m] = d[m] - p;
+    e[m - 1] = g;
+    return rots;
+}
+
 /* Reverse the block [l, hi] in place: d~_k = d_{l+hi-k}, e~_k = e_{l+hi-1-k}
  * and reverse Q's columns l..hi (algorithm page: "QL runs the same formulas
  * on reversed local indices"). Applying it twice restores the block. */
@@ -200,7 +239,7 @@ static void SFX(reverse_block)(REAL *d, REAL *e, REAL *Q, int n, int l, int hi)
  *        take mu from the trailing 2x2 and sweep [s, m].
  * Returns 1 when the block converged, 0 when the budget ran out. */
 static int SFX(qr_block)(REAL *d, REAL *e, REAL *Q, int n, int l, int hi,
-                         int *jtot, int nmaxit, long long *stats)
+                         int *jtot, int nmaxit, int scheme, long long *stats)
 {
     int m = hi;
     while (m > l) {
@@ -233,7 +272,8 @@ static int SFX(qr_block)(REAL *d, REAL *e, REAL *Q, int n, int l, int hi,
             return 0;
         *jtot += 1;
         REAL mu = SFX(oracle_shift)(d[m], d[m - 1], e[m - 1]);
-        long rots = SFX(oracle_sweep)(d, e, Q, n, s, m, mu);
+        long rots = scheme ? SFX(oracle_sweep_pg)(d, e, Q, n, s, m, mu)
+                           : SFX(oracle_sweep)(d, e, Q, n, s, m, mu);
         if (stats) {
             stats[0] += 1;
             stats[1] += rots;
@@ -276,7 +316,7 @@ static int SFX(before)(REAL a, int ia, REAL b, int ib)
  * list), run as a QR procedure on the possibly reversed block, then
  * unscaled. */
 int SFX(oracle_solve_one)(int n, REAL *d, REAL *e, REAL *Q, REAL *lam,
-                          int max_sweeps_per_n, int sort, long long *stats)
+                          int max_sweeps_per_n, int sort, int scheme, long long *stats)
 {
     const REAL ssfmax = SFX(c_ssfmax)();
     const REAL ssfmin = SFX(c_ssfmin)();
@@ -336,7 +376,7 @@ int SFX(oracle_solve_one)(int n, REAL *d, REAL *e, REAL *Q, REAL *lam,
         int rev = !(R_FABS(d[hi]) < R_FABS(d[l]));
         if (rev)
             SFX(reverse_block)(d, e, Q, n, l, hi);
-        int ok = SFX(qr_block)(d, e, Q, n, l, hi, &jtot, nmaxit, stats);
+        int ok = SFX(qr_block)(d, e, Q, n, l, hi, &jtot, nmaxit, scheme, stats);
         if (rev)
             SFX(reverse_block)(d, e, Q, n, l, hi);
         if (mode) {
@@ -386,10 +426,11 @@ int SFX(oracle_solve_one)(int n, REAL *d, REAL *e, REAL *Q, REAL *lam,
 /* Batched entry: d [batch][n], e [batch][n-1] (read only), lam [batch][n],
  * Q [batch][n][n] row-major or NULL, info [batch] or NULL, stats
  * [batch][3] or NULL (implicit sweeps, sweep rotations, analytic 2x2
- * solves per item). Returns 0, or -1 if n is out of range. */
+ * solves per item); scheme 0 = EXP sweeps, 1 = PG sweeps. Returns 0, or -1
+ * if n is out of range. */
 int SFX(oracle_steqr_batched)(const REAL *d, const REAL *e, REAL *lam,
                               REAL *Q, int *info, long long *stats, int n,
-                              long batch, int max_sweeps_per_n, int sort)
+                              long batch, int max_sweeps_per_n, int sort, int scheme)
 {
     if (n < 0 || n > 256)
         return -1;
@@ -406,7 +447,7 @@ int SFX(oracle_steqr_batched)(const REAL *d, const REAL *e, REAL *lam,
         if (st)
             st[0] = st[1] = st[2] = 0;
         int inf = SFX(oracle_solve_one)(n, dw, ew, Q ? Q + b * (long)n * n : 0,
-                                        lam + b * n, max_sweeps_per_n, sort, st);
+                                        lam + b * n, max_sweeps_per_n, sort, scheme, st);
         if (info)
             info[b] = inf;
     }

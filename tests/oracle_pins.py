@@ -135,8 +135,9 @@ def pin_sym2x2(oracle, libpath: Optional[str] = None) -> List[str]:
     return out
 
 
-def pin_sweep(oracle, libpath: Optional[str] = None) -> List[str]:
-    """One implicit sweep against an explicit shifted QR step."""
+def pin_sweep(oracle, libpath: Optional[str] = None, scheme: int = 0) -> List[str]:
+    """One implicit sweep (EXP form, scheme 0, or PG form, scheme 1) against
+    an explicit shifted QR step."""
     out: List[str] = []
     rng = np.random.default_rng(17)
     n = 10
@@ -147,7 +148,7 @@ def pin_sweep(oracle, libpath: Optional[str] = None) -> List[str]:
         mu = float(rng.standard_normal())
         d1, e1 = d.copy(), e.copy()
         Qs = np.eye(n)
-        rots = oracle.sweep(d1, e1, Qs, s, m, mu, libpath)
+        rots = oracle.sweep(d1, e1, Qs, s, m, mu, libpath, scheme=scheme)
         _fail(out, rots == m - s, "sweep rotation count %d != %d" % (rots, m - s))
         T = W.dense_from_bands(d[None], e[None])[0]
         # explicit step on the unreduced sub-block [s, m]
@@ -188,7 +189,7 @@ def pin_sweep(oracle, libpath: Optional[str] = None) -> List[str]:
     d = np.array([1.0, 3.0])
     e = np.array([0.5])
     mu = float(_closest_eig(3.0, 1.0, 0.5))
-    oracle.sweep(d, e, None, 0, 1, mu, libpath)
+    oracle.sweep(d, e, None, 0, 1, mu, libpath, scheme=scheme)
     _fail(out, abs(e[0]) <= 1e-14, "exact shift does not deflate a 2x2 (e=%g)" % e[0])
     _fail(out, abs(d[1] - mu) <= 1e-14, "exact shift: d_m != mu")
     return out
@@ -204,13 +205,14 @@ def clement(n: int):
     return d, e, lam
 
 
-def pin_solve(oracle, libpath: Optional[str] = None, quick: bool = False) -> List[str]:
+def pin_solve(oracle, libpath: Optional[str] = None, quick: bool = False,
+              scheme: int = 0) -> List[str]:
     out: List[str] = []
     sizes = (3, 8, 13) if quick else (1, 2, 3, 5, 8, 13, 16)
     for dt in (np.float32, np.float64):
         for n in sizes:
             d, e = W.random_batch(n, 16 if quick else 48, dt, salt=5)
-            lam, Q, info, _ = oracle.steqr(d, e, True, libpath=libpath)
+            lam, Q, info, _ = oracle.steqr(d, e, True, libpath=libpath, scheme=scheme)
             _fail(out, not info.any(), "solve info != 0 (%s n=%d)" % (dt.__name__, n))
             tol = V.tol_of(dt, n)
             ref = V.sturm_eigvals(d, e)
@@ -234,7 +236,7 @@ def pin_solve(oracle, libpath: Optional[str] = None, quick: bool = False) -> Lis
     for n in ((8, 16) if quick else (4, 8, 16, 32, 64)):
         d, e, ref = clement(n)
         for dt in (np.float32, np.float64):
-            lam, Q, info, _ = oracle.steqr(d.astype(dt), e.astype(dt), True, libpath=libpath)
+            lam, Q, info, _ = oracle.steqr(d.astype(dt), e.astype(dt), True, libpath=libpath, scheme=scheme)
             tol = V.tol_of(dt, n)
             err = np.abs(lam[0].astype(np.float64) - ref).max() / V.tnorm1(d, e)[0]
             _fail(out, info[0] == 0 and err <= tol, "Clement n=%d %s: %g" % (n, dt.__name__, err))
@@ -244,10 +246,10 @@ def pin_solve(oracle, libpath: Optional[str] = None, quick: bool = False) -> Lis
     n = 12
     d, e = W.random_batch(n, 32, np.float64, salt=9)
     for dt, factors in ((np.float32, (1e18, 1e19, 1e-18)), (np.float64, (1e200, 1e-200))):
-        base_l, _, _, _ = oracle.steqr(d.astype(dt), e.astype(dt), False, libpath=libpath)
+        base_l, _, _, _ = oracle.steqr(d.astype(dt), e.astype(dt), False, libpath=libpath, scheme=scheme)
         for f in factors:
             lam, Q, info, _ = oracle.steqr((d * f).astype(dt), (e * f).astype(dt), True,
-                                           libpath=libpath)
+                                           libpath=libpath, scheme=scheme)
             err = V.sorted_err(lam.astype(np.float64) / f, base_l, d, e)
             _fail(out, not info.any() and err.max() <= V.tol_of(dt, n),
                   "scaling identity %s at %g: %g" % (dt.__name__, f, err.max()))
@@ -260,13 +262,18 @@ ALL_PINS = (pin_lartg, pin_shift, pin_sym2x2, pin_sweep, pin_solve)
 
 
 def run_all(oracle, libpath: Optional[str] = None, quick: bool = True) -> List[str]:
+    """Every pin; the sweep and whole-solve pins for both update schemes."""
     fails: List[str] = []
     for p in ALL_PINS:
-        try:
-            if p is pin_solve:
-                fails += p(oracle, libpath, quick=quick)
-            else:
-                fails += p(oracle, libpath)
-        except Exception as exc:  # a crash of the oracle is a failed pin too
-            fails.append("%s raised %r" % (p.__name__, exc))
+        for scheme in ((0, 1) if p in (pin_sweep, pin_solve) else (0,)):
+            try:
+                if p is pin_solve:
+                    fails += [f + " [scheme %d]" % scheme
+                              for f in p(oracle, libpath, quick=quick, scheme=scheme)]
+                elif p is pin_sweep:
+                    fails += [f + " [scheme %d]" % scheme for f in p(oracle, libpath, scheme=scheme)]
+                else:
+                    fails += p(oracle, libpath)
+            except Exception as exc:  # a crash of the oracle is a failed pin too
+                fails.append("%s raised %r" % (p.__name__, exc))
     return fails

@@ -44,6 +44,14 @@ MUTANTS = [
      "for (int i = l, j = hi; i < j; ++i, --j) {"),
     ("deflation_wrong_pair", "if (SFX(negligible)(e[k - 1], d[k - 1], d[k])) {",
      "if (SFX(negligible)(e[k - 1] * (REAL)1e-3, d[k - 1], d[k])) {"),
+    # the PG form of the sweep
+    ("pg_drop_factor2", "REAL rs = (d[k + 1] - gs) * sn + (REAL)2 * c * cprev * e[k];",
+     "REAL rs = (d[k + 1] - gs) * sn + c * cprev * e[k];"),
+    ("pg_g_sign", "g = c * rs - cprev * e[k];", "g = c * rs + cprev * e[k];"),
+    ("pg_no_end_fixup", "d[m] = d[m] - p;", "d[m] = d[m];"),
+    ("pg_p_not_carried", "REAL gs = d[k] - p;", "REAL gs = d[k];"),
+    ("pg_f_unscaled", "REAL f = sprev * e[k];", "REAL f = e[k];"),
+    ("pg_q_skipped", "SFX(rot_cols)(Q, n, k, c, sn);", "(void)0;"),
 ]
 
 

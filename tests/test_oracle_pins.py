@@ -42,8 +42,32 @@ def test_building_block_pins(oracle_mod, pin):
     assert pin(oracle_mod) == []
 
 
-def test_solve_pins_full(oracle_mod):
-    assert P.pin_solve(oracle_mod, quick=False) == []
+def test_pg_sweep_pins(oracle_mod):
+    """The PG form of the sweep against the same explicit shifted QR step."""
+    assert P.pin_sweep(oracle_mod, scheme=1) == []
+
+
+@pytest.mark.parametrize("scheme", [0, 1], ids=["exp", "pg"])
+def test_solve_pins_full(oracle_mod, scheme):
+    assert P.pin_solve(oracle_mod, quick=False, scheme=scheme) == []
+
+
+@pytest.mark.parametrize("wname", ["c2_f32_n16", "c3_f64_n12", "c4_f64_n32"])
+def test_pg_and_exp_agree(oracle_mod, wname):
+    """The two update schemes are equivalent forms of one implicit step: on
+    the same inputs their eigenvalues agree within the tolerance and their
+    sweep counts agree (up to rounding-decided deflations)."""
+    w = W.WORKLOADS[wname]
+    d, e = W.make_batch(w, 128)
+    ok = np.isfinite(d).all(1) & np.isfinite(e).all(1)
+    l0, _, i0, s0 = oracle_mod.steqr(d, e, False)
+    l1, Q1, i1, s1 = oracle_mod.steqr(d, e, True, scheme=1)
+    assert np.array_equal(i0 > 0, i1 > 0)
+    tol = V.tol_of(d.dtype, w.n)
+    assert V.sorted_err(l1[ok], l0[ok].astype(np.float64), d[ok], e[ok]).max() <= tol
+    assert V.band_residual(d[ok], e[ok], l1[ok], Q1[ok]).max() <= tol
+    assert V.orthogonality(Q1[ok]).max() <= tol
+    assert abs(int(s1[ok, 0].sum()) - int(s0[ok, 0].sum())) <= 0.02 * s0[ok, 0].sum()
 
 
 # ---------------------------------------------------------------- golden fixtures
@@ -93,14 +117,15 @@ def test_golden_closed_forms(oracle_mod, row, dt):
 
 # ---------------------------------------------------------------- Toeplitz closed form
 
+@pytest.mark.parametrize("scheme", [0, 1], ids=["exp", "pg"])
 @pytest.mark.parametrize("n", [1, 2, 3, 4, 7, 8, 12, 16, 31, 32, 64])
 @pytest.mark.parametrize("dt", [np.float32, np.float64], ids=["f32", "f64"])
-def test_toeplitz_closed_form(oracle_mod, n, dt):
+def test_toeplitz_closed_form(oracle_mod, n, dt, scheme):
     """tridiag(b; a; b): lambda_k = a + 2b cos(k pi/(n+1)) and eigenvectors
     sqrt(2/(n+1)) sin(j k pi/(n+1)) up to sign."""
     for a, b in ((2.0, -1.0), (0.3, 1.7), (-5.0, 0.25)):
         d, e = W.toeplitz_batch(n, a, b, 1, dt)
-        lam, Q, info, _ = oracle_mod.steqr(d, e, True)
+        lam, Q, info, _ = oracle_mod.steqr(d, e, True, scheme=scheme)
         assert info[0] == 0
         k = np.arange(1, n + 1)
         ref = np.sort(a + 2 * b * np.cos(k * np.pi / (n + 1)))
@@ -251,14 +276,15 @@ def test_scaled_items_against_twins(oracle_mod, dt):
     assert V.orthogonality(Q).max() <= V.tol_of(dt, n)
 
 
+@pytest.mark.parametrize("scheme", [0, 1], ids=["exp", "pg"])
 @pytest.mark.parametrize("dt", [np.float32, np.float64], ids=["f32", "f64"])
 @pytest.mark.parametrize("n", [3, 16, 32])
-def test_nan_items_fail_with_budget(oracle_mod, dt, n):
+def test_nan_items_fail_with_budget(oracle_mod, dt, n, scheme):
     """A NaN never passes the deflation test, so the block holding it burns
     the whole 30n sweep budget: info > 0, the solve terminates, and the NaN
     spreads over that block only."""
     d, e = W.edge_batch(W.EDGE_NAN, n, 12, dt)
-    lam, Q, info, st = oracle_mod.steqr(d, e, True)
+    lam, Q, info, st = oracle_mod.steqr(d, e, True, scheme=scheme)
     assert np.all(info > 0)
     assert np.all(st[:, 0] == 30 * n)
     # one block (random e has no zeros): every eigenvalue slot is NaN,
@@ -267,12 +293,13 @@ def test_nan_items_fail_with_budget(oracle_mod, dt, n):
     assert np.all(info == n - 1)
 
 
-def test_nan_confined_to_its_block(oracle_mod):
+@pytest.mark.parametrize("scheme", [0, 1], ids=["exp", "pg"])
+def test_nan_confined_to_its_block(oracle_mod, scheme):
     n = 12
     d, e = W.random_batch(n, 4, np.float64, salt=3)
     e[:, 5] = 0.0  # blocks [0,5] and [6,11]
     d[:, 8] = np.nan  # NaN in the second block
-    lam, _, info, _ = oracle_mod.steqr(d, e, False)
+    lam, _, info, _ = oracle_mod.steqr(d, e, False, scheme=scheme)
     assert np.all(info == 5)  # e_6..e_10 of the NaN block stay nonzero
     assert np.all(np.isfinite(lam[:, :6])) and np.all(np.isnan(lam[:, 6:]))
     # the first block converged to its own eigenvalues (unsorted output)
@@ -282,7 +309,7 @@ def test_nan_confined_to_its_block(oracle_mod):
     d2, e2 = W.random_batch(n, 4, np.float64, salt=4)
     e2[:, 5] = 0.0
     d2[:, 2] = np.nan
-    lam2, _, info2, _ = oracle_mod.steqr(d2, e2, False)
+    lam2, _, info2, _ = oracle_mod.steqr(d2, e2, False, scheme=scheme)
     assert np.all(info2 == 5 + 5)
     assert np.all(np.isnan(lam2[:, :6]))
     assert np.array_equal(lam2[:, 6:], d2[:, 6:])
