@@ -86,7 +86,7 @@ def counters_from_profiles(wname: str, jobz: bool, family: str):
     return t
 
 
-def cpu_baseline(d: np.ndarray, e: np.ndarray, jobz: bool, wname: str):
+def cpu_baseline(d: np.ndarray, e: np.ndarray, jobz: bool, wname: str, scheme: int = 0):
     """The CPU oracle (as is) on the host cores over the same workload."""
     import oracle
     cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
@@ -95,7 +95,7 @@ def cpu_baseline(d: np.ndarray, e: np.ndarray, jobz: bool, wname: str):
     stats = None
     for _ in range(3):
         t = time.perf_counter()
-        _, _, _, stats = oracle.steqr(d, e, jobz, threads=cores)
+        _, _, _, stats = oracle.steqr(d, e, jobz, threads=cores, scheme=scheme)
         times.append(time.perf_counter() - t)
     tmed = statistics.median(times)
     nb = d.shape[0]
@@ -118,6 +118,8 @@ def main() -> int:
     ap.add_argument("--waves", type=int, default=0, help="waves per workgroup (0 = default)")
     ap.add_argument("--band", type=int, default=0,
                     help="band storage: 0 default, 1 registers, 2 LDS")
+    ap.add_argument("--scheme", default="exp", choices=["exp", "pg"],
+                    help="form of the chase step: EXP (default) or PG (Parlett-Gray)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-named", action="store_true",
                     help="skip the secondary timing at the configuration's named lanes")
@@ -156,8 +158,9 @@ def main() -> int:
 
     w = W.WORKLOADS[args.workload]
     jobz = args.jobz == "V"
+    scheme = 1 if args.scheme == "pg" else 0
     prm0 = st.make_params(lanes_per_problem=args.lanes, waves_per_block=args.waves,
-                          band_storage=args.band)
+                          band_storage=args.band, update_scheme=scheme)
     lanes0 = st.steqr_query(w.n, w.batch, int(jobz), 0 if w.dtype == "f32" else 1,
                             prm0)["lanes_per_problem"]
     d, e = W.make_batch(w, replicate=(64 // lanes0) if args.replicate else 1)
@@ -169,7 +172,7 @@ def main() -> int:
     Q = torch.empty((nb, n, n), dtype=td.dtype, device=dev) if jobz else None
     info = torch.empty((nb,), dtype=torch.int32, device=dev)
     prm = st.make_params(lanes_per_problem=args.lanes, waves_per_block=args.waves,
-                         band_storage=args.band)
+                         band_storage=args.band, update_scheme=scheme)
     plan = st.steqr_query(n, nb, int(jobz), st.dtype_code(td.dtype), prm)
     stream = torch.cuda.current_stream()
 
@@ -203,7 +206,7 @@ def main() -> int:
     if (args.lanes == 0 and plan["lanes_per_problem"] != w.lanes and not args.replicate
             and not args.no_named):
         prm_n = st.make_params(lanes_per_problem=w.lanes, waves_per_block=args.waves,
-                               band_storage=1 if w.n <= 32 else 2)
+                               band_storage=1 if w.n <= 32 else 2, update_scheme=scheme)
         try:
             st.steqr_query(n, nb, int(jobz), st.dtype_code(td.dtype), prm_n)
         except st.SteqrError:
@@ -230,7 +233,7 @@ def main() -> int:
     cpu = None
     flops = None
     if not args.no_cpu:
-        cpu, stats = cpu_baseline(d, e, jobz, w.name)
+        cpu, stats = cpu_baseline(d, e, jobz, w.name, scheme)
         fin = np.isfinite(d).all(1) & np.isfinite(e).all(1)
         flops = float(flops_per_matrix(stats[fin], n, jobz).sum())
     dtype = w.dtype
@@ -240,7 +243,7 @@ def main() -> int:
               ("chunkl" if plan["band_storage"] == 2 else "chunk"))
     if flops is not None:
         ach = flops / sec / 1e12
-        ctr = None if args.replicate else counters_from_profiles(w.name, jobz, family)
+        ctr = None if (args.replicate or scheme) else counters_from_profiles(w.name, jobz, family)
         roof = {"kernel": "steqr_%s_kernel<%s, N=%d, P=%d, %s>"
                           % (family, "float" if dtype == "f32" else "double", plan["padded_n"],
                              plan["lanes_per_problem"], "V" if jobz else "N"),
@@ -277,6 +280,7 @@ def main() -> int:
                    "rows_per_lane": plan["rows_per_lane"], "padded_n": plan["padded_n"],
                    "band_storage": "LDS" if plan["band_storage"] == 2 else "registers",
                    "waves_per_block": plan["waves_per_block"],
+                   "update_scheme": args.scheme.upper(),
                    "workgroups": plan["workgroups"],
                    "inputs": ("replicated per wavefront (lockstep ideal)" if args.replicate
                               else ("90% iid N(0,1) + 10% edge items" if w.edge_mix

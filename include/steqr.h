@@ -52,6 +52,7 @@ extern "C" {
 
 enum { STEQR_N = 0, STEQR_V = 1 };     /* jobz: values only / values+vectors */
 enum { STEQR_F32 = 0, STEQR_F64 = 1 }; /* dtype */
+enum { STEQR_EXP = 0, STEQR_PG = 1 };  /* update_scheme */
 
 /* Options of steqr_batched_ex. Zero-initialised fields mean "default". */
 typedef struct steqr_params {
@@ -74,6 +75,12 @@ typedef struct steqr_params {
      * 2 = shared in LDS (frees registers for more rows of Q per lane).
      * Orders above 32 always use LDS. */
     int band_storage;
+    /* Form of the implicit step (BatchLAS steqr algorithm page, "the two CTA
+     * update schemes"): STEQR_EXP (0, default) writes each local similarity
+     * G^T T G; STEQR_PG (1) is the Parlett-Gray form, which carries the
+     * scalars (g, p, c, s) along the sweep. Both are the same implicit
+     * step; results differ by rounding only. */
+    int update_scheme;
 } steqr_params;
 
 /* Eigenvalues (jobz = STEQR_N) or eigenpairs (jobz = STEQR_V) of a batch of

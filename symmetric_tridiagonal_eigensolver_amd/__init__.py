@@ -4,10 +4,11 @@ The solver is the HIP library libsteqr.so (C ABI in include/steqr.h);
 this package is its Python binding. Importing it requires the library to
 be built (``python -m symmetric_tridiagonal_eigensolver_amd.build``).
 """
-from ._binding import (STEQR_F32, STEQR_F64, STEQR_MAX_N, STEQR_N, STEQR_V, EXPORTS,
+from ._binding import (STEQR_EXP, STEQR_F32, STEQR_F64, STEQR_MAX_N, STEQR_N, STEQR_PG,
+                       STEQR_V, EXPORTS,
                        LIB_PATH, SteqrError, dtype_code, lib, make_params, solve,
                        steqr_batched, steqr_batched_ex, steqr_params, steqr_query, version)
 
-__all__ = ["STEQR_F32", "STEQR_F64", "STEQR_MAX_N", "STEQR_N", "STEQR_V", "EXPORTS",
+__all__ = ["STEQR_EXP", "STEQR_PG", "STEQR_F32", "STEQR_F64", "STEQR_MAX_N", "STEQR_N", "STEQR_V", "EXPORTS",
            "LIB_PATH", "SteqrError", "dtype_code", "lib", "make_params", "solve",
            "steqr_batched", "steqr_batched_ex", "steqr_params", "steqr_query", "version"]

@@ -48,17 +48,28 @@ const Entry* search(const Table& t, int dtype, int N, int P, int jobz, int band)
     return nullptr;
 }
 
-const Entry* find_entry(int dtype, int N, int P, int jobz, int band) {
-    if (N == 64) return band == 2 ? search(steqr::table_wave(), dtype, N, P, jobz, band) : nullptr;
-    if (band == 2) {
-        const Table t = dtype == STEQR_F32 ? steqr::table_lds_f32() : steqr::table_lds_f64();
-        return search(t, dtype, N, P, jobz, band);
+const Entry* find_entry(int dtype, int N, int P, int jobz, int band, int pg) {
+    if (N == 64) {
+        if (band != 2) return nullptr;
+        return search(pg ? steqr::table_wave_pg() : steqr::table_wave(), dtype, N, P, jobz, band);
     }
     Table t;
-    if (dtype == STEQR_F32)
-        t = jobz ? steqr::table_f32_v() : steqr::table_f32_n();
-    else
-        t = jobz ? steqr::table_f64_v() : steqr::table_f64_n();
+    if (band == 2) {
+        if (dtype == STEQR_F32)
+            t = pg ? steqr::table_lds_f32_pg() : steqr::table_lds_f32();
+        else
+            t = pg ? steqr::table_lds_f64_pg() : steqr::table_lds_f64();
+    } else if (dtype == STEQR_F32) {
+        if (jobz)
+            t = pg ? steqr::table_f32_v_pg() : steqr::table_f32_v();
+        else
+            t = pg ? steqr::table_f32_n_pg() : steqr::table_f32_n();
+    } else {
+        if (jobz)
+            t = pg ? steqr::table_f64_v_pg() : steqr::table_f64_v();
+        else
+            t = pg ? steqr::table_f64_n_pg() : steqr::table_f64_n();
+    }
     return search(t, dtype, N, P, jobz, band);
 }
 
@@ -84,7 +95,10 @@ int plan_launch(int n, int batch, int jobz, int dtype, const steqr_params* prm, 
     int waves = 4;
     int P = 0;
     int band = 0;
+    int pg = 0;
     if (prm) {
+        if (prm->update_scheme != STEQR_EXP && prm->update_scheme != STEQR_PG) return -10;
+        pg = prm->update_scheme == STEQR_PG;
         band = prm->band_storage;
         if (band < 0 || band > 2) return -10;
         if (prm->waves_per_block != 0) {
@@ -106,7 +120,7 @@ int plan_launch(int n, int batch, int jobz, int dtype, const steqr_params* prm, 
     if (N < 0) return -5;  // order not provided by this build
     if (band == 0 || N >= 64) band = default_band(dtype, N, jobz);
     if (P == 0) P = default_lanes(dtype, N, jobz, band);
-    const Entry* ent = find_entry(dtype, N, P, jobz, band);
+    const Entry* ent = find_entry(dtype, N, P, jobz, band, pg);
     if (!ent) return -10;
     // keep a workgroup's LDS within 64 KiB
     while (waves > 1 && (long)waves * ent->lds_per_wave > 65536) waves /= 2;

@@ -26,7 +26,10 @@
 //    positions in which every chunk with a sweep applies its rotation at p
 //    when s <= p < m. Lanes whose chunk is idle at p are masked off (EXEC),
 //    and positions where no chunk is active are skipped by the wave.
-//    The 2x2 solve runs inside the pass at its own static position.
+//    A 2x2 block is a one-step chase at its position, seeded with its
+//    closed-form rotation. The step is written in the EXP form (local
+//    similarity) or, with the PG template flag, in the Parlett-Gray form
+//    [algo, the two CTA update schemes].
 //  * Run-time positions (the shift inputs at the converging end, the block
 //    ends, the sort keys) are read from a per-chunk copy of the band in LDS,
 //    republished after every change of the band; register arrays are only
@@ -106,7 +109,7 @@ struct Smem {
     static constexpr size_t bytes_per_wave = band_bytes + rank_bytes + stage_bytes;
 };
 
-template <typename T, int N, int P, bool WANTQ>
+template <typename T, int N, int P, bool WANTQ, bool PG>
 __global__ void __launch_bounds__(256) steqr_chunk_kernel(KernelArgs args) {
     static_assert(P >= 1 && P <= 64 && (64 % P) == 0, "P must divide 64");
     constexpr int CH = 64 / P;                       // problems per wavefront
@@ -351,17 +354,20 @@ __global__ void __launch_bounds__(256) steqr_chunk_kernel(KernelArgs args) {
         const int si = sweep ? s : 0;
         const T dm = sd[mi], dm1 = sd[mi - 1], em1 = se[mi - 1];
         const T mu = lapack_shift(dm, dm1, em1);
+        // EXP carries the pair (x, y) the next rotation annihilates; PG
+        // carries g in x and the previous sine in y (f = y e_p)
         x = sd[si] - mu;
-        y = se[si];
+        y = PG ? T(1) : se[si];
         // A 2x2 block at (jpos, jpos+1) [algo, "A deflated block of size 2"
         // paragraph]: its closed-form Schur rotation becomes the running
-        // pair of a one-step chase at jpos (lartg returns that rotation), so
-        // it is applied by the same similarity and Q update as the sweeps.
-        // The leftover e_jpos (rounding size) joins `zeroed`.
+        // pair of a one-step chase at jpos (lartg returns that rotation, for
+        // PG from (cs e, -sj e), the same rotation up to sign), so it is
+        // applied by the same similarity and Q update as the sweeps. The
+        // leftover e_jpos (rounding size) joins `zeroed`.
         if (__any(jac)) {
             T rt1, rt2, cs, sj;
             sym2x2(dm1, em1, dm, rt1, rt2, cs, sj);
-            x = jac ? cs : x;
+            x = jac ? (PG ? cs * em1 : cs) : x;
             y = jac ? -sj : y;
             zeroed |= jac ? ((M)1 << jpos) : (M)0;
         }
@@ -380,23 +386,47 @@ __global__ void __launch_bounds__(256) steqr_chunk_kernel(KernelArgs args) {
         static_for<N - 1>([&](auto I) {
             constexpr int p = decltype(I)::value;
             if ((unsigned)(p - s) < steps) {
-                // [algo]: first rotation from (d_s - mu, e_s), later ones
-                // from (e_{p-1}, bulge); apply G^T B G to the 2x2 at (p, p+1)
-                const T b = cp * e[p];
                 T c, sn, rr;
-                lartg(x, y, c, sn, rr);
-                if constexpr (p > 0) e[p - 1] = rr;
-                const T a = d[p], dd = d[p + 1];
-                const T tr = a + dd;  // trace of the 2x2 is invariant
-                const T pp = c * a + sn * b;
-                const T qq = c * b + sn * dd;
-                const T bn = qq * c - pp * sn;
-                F::fma_over(d[p], pp, c, qq * sn);
-                e[p] = bn;
-                d[p + 1] = tr - d[p];
-                if constexpr (p + 1 < N - 1) y = sn * e[p + 1];  // new bulge
-                x = bn;
-                cp = c;
+                if constexpr (PG) {
+                    // PG step [algo, the two CTA update schemes]: f = s' e_p,
+                    // (c, s, r) = lartg(g, f), r* = (d_{p+1} - g*) s + 2 c c' e_p,
+                    // d_p = g* + s r*, g = c r* - c' e_p (c', s' of the previous
+                    // step). g* = d_p - s' r*' is folded into d_p by the
+                    // previous step (d_{p+1} -= s r* below), which also leaves
+                    // the sweep's final d_m -= p in place; e_p = g is the
+                    // final e_{m-1} = g, and the next step overwrites it with r.
+                    const T f = y * e[p];
+                    const T b = cp * e[p];
+                    lartg(x, f, c, sn, rr);
+                    if constexpr (p > 0) e[p - 1] = rr;
+                    const T gs = d[p];
+                    const T rs = F::fma(d[p + 1] - gs, sn, (c + c) * b);
+                    const T pk = sn * rs;
+                    d[p] = gs + pk;
+                    d[p + 1] = d[p + 1] - pk;
+                    x = F::fma(c, rs, -b);
+                    e[p] = x;
+                    y = sn;
+                    cp = c;
+                } else {
+                    // EXP step [algo]: first rotation from (d_s - mu, e_s),
+                    // later ones from (e_{p-1}, bulge); apply G^T B G to the
+                    // 2x2 at (p, p+1)
+                    const T b = cp * e[p];
+                    lartg(x, y, c, sn, rr);
+                    if constexpr (p > 0) e[p - 1] = rr;
+                    const T a = d[p], dd = d[p + 1];
+                    const T tr = a + dd;  // trace of the 2x2 is invariant
+                    const T pp = c * a + sn * b;
+                    const T qq = c * b + sn * dd;
+                    const T bn = qq * c - pp * sn;
+                    F::fma_over(d[p], pp, c, qq * sn);
+                    e[p] = bn;
+                    d[p + 1] = tr - d[p];
+                    if constexpr (p + 1 < N - 1) y = sn * e[p + 1];  // new bulge
+                    x = bn;
+                    cp = c;
+                }
                 if constexpr (WANTQ) {
                     static_for<R>([&](auto II) {
                         constexpr int i = decltype(II)::value;

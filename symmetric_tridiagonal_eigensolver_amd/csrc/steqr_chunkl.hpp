@@ -52,7 +52,7 @@ __device__ __forceinline__ T chunk_max(T v) {
     return v;
 }
 
-template <typename T, int N, int P, bool WANTQ>
+template <typename T, int N, int P, bool WANTQ, bool PG>
 __global__ void __launch_bounds__(256) steqr_chunkl_kernel(KernelArgs args) {
     static_assert(P >= 2 && P <= N && (N % P) == 0 && (64 % P) == 0, "2 <= P <= N, P | N");
     static_assert(N <= 32, "position masks are 32 bits");
@@ -322,18 +322,21 @@ __global__ void __launch_bounds__(256) steqr_chunkl_kernel(KernelArgs args) {
         const int si = sweep ? s : (jac ? jpos : 0);
         const T dm = sd[mi], dm1 = sd[mi - 1], em1 = se[mi - 1];
         const T mu = lapack_shift(dm, dm1, em1);
+        // EXP carries the pair (x, y) the next rotation annihilates; PG
+        // carries g in x and the previous sine in y (f = y e_p)
         dcur = sd[si];
         x = dcur - mu;
-        y = se[si];
+        y = PG ? T(1) : se[si];
         // A 2x2 block at (jpos, jpos+1) [algo, "A deflated block of size 2"
         // paragraph]: its closed-form Schur rotation becomes the running
-        // pair of a one-step chase at jpos (lartg returns that rotation), so
-        // it is applied by the same similarity and Q update as the sweeps.
-        // The leftover e_jpos (rounding size) joins `zeroed`.
+        // pair of a one-step chase at jpos (lartg returns that rotation, for
+        // PG from (cs e, -sj e), the same rotation up to sign), so it is
+        // applied by the same similarity and Q update as the sweeps. The
+        // leftover e_jpos (rounding size) joins `zeroed`.
         if (__any(jac)) {
             T rt1, rt2, cs, sj;
             sym2x2(dm1, em1, dm, rt1, rt2, cs, sj);
-            x = jac ? cs : x;
+            x = jac ? (PG ? cs * em1 : cs) : x;
             y = jac ? -sj : y;
             zeroed |= jac ? ((M)1 << jpos) : (M)0;
         }
@@ -357,22 +360,41 @@ __global__ void __launch_bounds__(256) steqr_chunkl_kernel(KernelArgs args) {
             if ((unsigned)(p - s) < steps) {
                 // running pair and d_p seeded in the settle; r goes to
                 // e_{p-1} (at the first step a zero coupling or an e already
-                // in `zeroed`, restored when the block closes)
-                const T a = dcur;
+                // in `zeroed`, restored when the block closes). Every lane of
+                // the chunk writes the same value to the same word.
                 T c, sn, rr;
-                lartg(x, y, c, sn, rr);
-                const T b = cp * e0;
-                const T pp = c * a + sn * b;
-                const T qq = c * b + sn * d1;
-                const T an = pp * c + qq * sn;
-                const T bn = qq * c - pp * sn;
-                // every lane of the chunk writes the same value to the same word
-                if constexpr (p > 0) se[p - 1] = rr;
-                sd[p] = an;
-                dcur = (a + d1) - an;
-                x = bn;
-                y = sn * e1;
-                cp = c;
+                if constexpr (PG) {
+                    // PG step [algo, the two CTA update schemes]; dcur holds
+                    // g* = d_p - s' r*' (folded in by the previous step), and
+                    // after the last step d_m - p and g are what the sweep's
+                    // end writes back
+                    const T f = y * e0;
+                    const T b = cp * e0;
+                    lartg(x, f, c, sn, rr);
+                    const T gs = dcur;
+                    const T rs = F::fma(d1 - gs, sn, (c + c) * b);
+                    const T pk = sn * rs;
+                    if constexpr (p > 0) se[p - 1] = rr;
+                    sd[p] = gs + pk;
+                    dcur = d1 - pk;
+                    x = F::fma(c, rs, -b);
+                    y = sn;
+                    cp = c;
+                } else {
+                    const T a = dcur;
+                    lartg(x, y, c, sn, rr);
+                    const T b = cp * e0;
+                    const T pp = c * a + sn * b;
+                    const T qq = c * b + sn * d1;
+                    const T an = pp * c + qq * sn;
+                    const T bn = qq * c - pp * sn;
+                    if constexpr (p > 0) se[p - 1] = rr;
+                    sd[p] = an;
+                    dcur = (a + d1) - an;
+                    x = bn;
+                    y = sn * e1;
+                    cp = c;
+                }
                 if constexpr (WANTQ) {
                     static_for<R>([&](auto II) {
                         constexpr int i = decltype(II)::value;

@@ -12,6 +12,6 @@ static const Entry kEntries[] = {
 };
 #undef E
 
-Table table_f32_v() { return {kEntries, (int)(sizeof(kEntries) / sizeof(kEntries[0]))}; }
+Table STEQR_TABLE(table_f32_v)() { return {kEntries, (int)(sizeof(kEntries) / sizeof(kEntries[0]))}; }
 
 }  // namespace steqr

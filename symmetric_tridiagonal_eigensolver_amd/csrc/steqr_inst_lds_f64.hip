@@ -10,6 +10,6 @@ static const Entry kEntries[] = {
 };
 #undef E
 
-Table table_lds_f64() { return {kEntries, (int)(sizeof(kEntries) / sizeof(kEntries[0]))}; }
+Table STEQR_TABLE(table_lds_f64)() { return {kEntries, (int)(sizeof(kEntries) / sizeof(kEntries[0]))}; }
 
 }  // namespace steqr

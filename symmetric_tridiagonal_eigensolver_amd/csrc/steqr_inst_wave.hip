@@ -8,6 +8,6 @@ static const Entry kEntries[] = {
     STEQR_WAVE_ENTRY(1, double, 64, 1), STEQR_WAVE_ENTRY(1, double, 64, 0),
 };
 
-Table table_wave() { return {kEntries, (int)(sizeof(kEntries) / sizeof(kEntries[0]))}; }
+Table STEQR_TABLE(table_wave)() { return {kEntries, (int)(sizeof(kEntries) / sizeof(kEntries[0]))}; }
 
 }  // namespace steqr

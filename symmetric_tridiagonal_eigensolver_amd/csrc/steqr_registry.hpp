@@ -13,6 +13,13 @@ namespace steqr {
 
 typedef hipError_t (*LaunchFn)(const KernelArgs& args, int grid, int block, hipStream_t stream);
 
+// Each instantiation unit is compiled twice: once for the EXP form of the
+// chase step (STEQR_INST_PG 0) and once for the PG form (STEQR_INST_PG 1,
+// the *_pg.hip units), giving one table per unit and scheme.
+#ifndef STEQR_INST_PG
+#define STEQR_INST_PG 0
+#endif
+
 struct Entry {
     int dtype;             // 0 = float, 1 = double
     int N;                 // compile-time (padded) order
@@ -23,40 +30,43 @@ struct Entry {
     LaunchFn fn;
 };
 
-template <typename T, int N, int P, bool WANTQ>
+template <typename T, int N, int P, bool WANTQ, bool PG>
 hipError_t launch_chunk(const KernelArgs& args, int grid, int block, hipStream_t stream) {
     const size_t lds = (size_t)(block / 64) * Smem<T, N, P, WANTQ>::bytes_per_wave;
-    hipLaunchKernelGGL((steqr_chunk_kernel<T, N, P, WANTQ>), dim3(grid), dim3(block), lds, stream,
-                       args);
+    hipLaunchKernelGGL((steqr_chunk_kernel<T, N, P, WANTQ, PG>), dim3(grid), dim3(block), lds,
+                       stream, args);
     return hipGetLastError();
 }
 
 // One problem per wavefront (P = 64).
-template <typename T, int N, bool WANTQ>
+template <typename T, int N, bool WANTQ, bool PG>
 hipError_t launch_wave(const KernelArgs& args, int grid, int block, hipStream_t stream) {
     const size_t lds = (size_t)(block / 64) * WaveSmem<T, N>::bytes_per_wave;
-    hipLaunchKernelGGL((steqr_wave_kernel<T, N, WANTQ>), dim3(grid), dim3(block), lds, stream,
-                       args);
+    hipLaunchKernelGGL((steqr_wave_kernel<T, N, WANTQ, PG>), dim3(grid), dim3(block), lds,
+                       stream, args);
     return hipGetLastError();
 }
 
 #define STEQR_WAVE_ENTRY(DT, T, N, Q) \
-    { DT, N, 64, Q, 2, (int)WaveSmem<T, N>::bytes_per_wave, &launch_wave<T, N, (Q) != 0> }
+    { DT, N, 64, Q, 2, (int)WaveSmem<T, N>::bytes_per_wave, \
+      &launch_wave<T, N, (Q) != 0, STEQR_INST_PG != 0> }
 
 // Chunked, band in LDS.
-template <typename T, int N, int P, bool WANTQ>
+template <typename T, int N, int P, bool WANTQ, bool PG>
 hipError_t launch_chunkl(const KernelArgs& args, int grid, int block, hipStream_t stream) {
     const size_t lds = (size_t)(block / 64) * SmemL<T, N, P>::bytes_per_wave;
-    hipLaunchKernelGGL((steqr_chunkl_kernel<T, N, P, WANTQ>), dim3(grid), dim3(block), lds, stream,
-                       args);
+    hipLaunchKernelGGL((steqr_chunkl_kernel<T, N, P, WANTQ, PG>), dim3(grid), dim3(block), lds,
+                       stream, args);
     return hipGetLastError();
 }
 
 #define STEQR_LENTRY(DT, T, N, P, Q) \
-    { DT, N, P, Q, 2, (int)SmemL<T, N, P>::bytes_per_wave, &launch_chunkl<T, N, P, (Q) != 0> }
+    { DT, N, P, Q, 2, (int)SmemL<T, N, P>::bytes_per_wave, \
+      &launch_chunkl<T, N, P, (Q) != 0, STEQR_INST_PG != 0> }
 
 #define STEQR_ENTRY(DT, T, N, P, Q) \
-    { DT, N, P, Q, 1, (int)Smem<T, N, P, (Q) != 0>::bytes_per_wave, &launch_chunk<T, N, P, (Q) != 0> }
+    { DT, N, P, Q, 1, (int)Smem<T, N, P, (Q) != 0>::bytes_per_wave, \
+      &launch_chunk<T, N, P, (Q) != 0, STEQR_INST_PG != 0> }
 
 struct Table {
     const Entry* entries;
@@ -70,5 +80,19 @@ Table table_f64_n();
 Table table_wave();
 Table table_lds_f32();
 Table table_lds_f64();
+Table table_f32_v_pg();
+Table table_f32_n_pg();
+Table table_f64_v_pg();
+Table table_f64_n_pg();
+Table table_wave_pg();
+Table table_lds_f32_pg();
+Table table_lds_f64_pg();
+
+// table name for the scheme this unit is compiled for
+#if STEQR_INST_PG
+#define STEQR_TABLE(name) name##_pg
+#else
+#define STEQR_TABLE(name) name
+#endif
 
 }  // namespace steqr

@@ -44,7 +44,7 @@ __device__ __forceinline__ T shfl_xor(T v, int mask) {
     }
 }
 
-template <typename T, int N, bool WANTQ>
+template <typename T, int N, bool WANTQ, bool PG>
 __global__ void __launch_bounds__(256) steqr_wave_kernel(KernelArgs args) {
     static_assert(N == 64, "one problem per wavefront needs N == 64");
     using F = Fp<T>;
@@ -226,9 +226,10 @@ __global__ void __launch_bounds__(256) steqr_wave_kernel(KernelArgs args) {
             // update e_p <- c_{p-1} e_p is applied here), (x, y) = running
             // pair. d_{p+1}, e_{p+1} are read one step ahead: no step writes
             // them before step p.
-            // running pair (d_s - mu, e_s) for the first rotation
+            // running pair (d_s - mu, e_s) for the first rotation (PG: g
+            // in x, the previous sine in y)
             T dcur = sd[s], ecur = se[s];
-            T x = dcur - mu, y = ecur, cp = T(1);
+            T x = dcur - mu, y = PG ? T(1) : ecur, cp = T(1);
             T dnext = sd[s + 1], enext = se[s + 1];
             // positions s .. m-1; the walk stops after m-1 (uniform branch)
             static_for_while<N - 1>([&](auto I) {
@@ -241,20 +242,36 @@ __global__ void __launch_bounds__(256) steqr_wave_kernel(KernelArgs args) {
                         dnext = sd[p + 2];
                         enext = se[p + 2];
                     }
-                    const T a = dcur;
                     const T ep = ecur;
                     T c, sn, rr;
-                    lartg<T, true>(x, y, c, sn, rr);
-                    if constexpr (p > 0) se[p - 1] = rr;  // every lane writes the same word
-                    const T b = cp * ep;
-                    const T pp = c * a + sn * b;
-                    const T qq = c * b + sn * dp1;
-                    const T an = pp * c + qq * sn;
-                    const T bn = qq * c - pp * sn;
-                    sd[p] = an;
-                    dcur = (a + dp1) - an;
-                    x = bn;
-                    y = sn * ep1;  // new bulge
+                    if constexpr (PG) {
+                        // PG step [algo, the two CTA update schemes]; dcur
+                        // holds g* (see steqr_chunk.hpp)
+                        const T f = y * ep;
+                        const T b = cp * ep;
+                        lartg<T, true>(x, f, c, sn, rr);
+                        if constexpr (p > 0) se[p - 1] = rr;  // every lane writes the same word
+                        const T gs = dcur;
+                        const T rs = F::fma(dp1 - gs, sn, (c + c) * b);
+                        const T pk = sn * rs;
+                        sd[p] = gs + pk;
+                        dcur = dp1 - pk;
+                        x = F::fma(c, rs, -b);
+                        y = sn;
+                    } else {
+                        const T a = dcur;
+                        lartg<T, true>(x, y, c, sn, rr);
+                        if constexpr (p > 0) se[p - 1] = rr;  // every lane writes the same word
+                        const T b = cp * ep;
+                        const T pp = c * a + sn * b;
+                        const T qq = c * b + sn * dp1;
+                        const T an = pp * c + qq * sn;
+                        const T bn = qq * c - pp * sn;
+                        sd[p] = an;
+                        dcur = (a + dp1) - an;
+                        x = bn;
+                        y = sn * ep1;  // new bulge
+                    }
                     cp = c;
                     ecur = ep1;
                     if constexpr (WANTQ) {

@@ -117,9 +117,31 @@ def test_bad_params(st):
     # (the pointers are not device memory)
     L = st.lib()
     for prm in (st.make_params(lanes_per_problem=3), st.make_params(lanes_per_problem=128),
-                st.make_params(waves_per_block=3), st.make_params(lanes_per_problem=-4)):
+                st.make_params(waves_per_block=3), st.make_params(lanes_per_problem=-4),
+                st.make_params(update_scheme=2), st.make_params(update_scheme=-1)):
         got = L.steqr_batched_ex(8, 8, 8, 8, 16, 10, 1, 0, None, None, ctypes.byref(prm))
         assert got == -10
+
+
+@pytest.mark.parametrize("n,jobz,dtype", [(4, 1, 0), (16, 1, 0), (16, 0, 0), (12, 1, 1),
+                                          (32, 1, 0), (32, 0, 1), (64, 1, 1), (50, 0, 0)])
+def test_pg_scheme_has_the_same_plans(st, n, jobz, dtype):
+    """Every launch plan exists in both forms of the chase step."""
+    for lanes in (0, 1, 2, 4, 8, 16, 32, 64):
+        for band in (0, 1, 2):
+            try:
+                a = st.steqr_query(n, 1000, jobz, dtype,
+                                   st.make_params(lanes_per_problem=lanes, band_storage=band))
+            except st.SteqrError:
+                with pytest.raises(st.SteqrError):
+                    st.steqr_query(n, 1000, jobz, dtype,
+                                   st.make_params(lanes_per_problem=lanes, band_storage=band,
+                                                  update_scheme=st.STEQR_PG))
+                continue
+            b = st.steqr_query(n, 1000, jobz, dtype,
+                               st.make_params(lanes_per_problem=lanes, band_storage=band,
+                                              update_scheme=st.STEQR_PG))
+            assert a == b
 
 
 def test_uninstantiated_lanes_rejected_by_query(st):
