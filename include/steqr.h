@@ -72,8 +72,12 @@ typedef struct steqr_params {
     int waves_per_block;
     /* Where a chunked kernel keeps the band d, e during the solve:
      * 0 = tuned default, 1 = replicated in every lane's registers,
-     * 2 = shared in LDS (frees registers for more rows of Q per lane).
-     * Orders above 32 always use LDS. */
+     * 2 = shared in LDS (frees registers for more rows of Q per lane),
+     * 3 = (orders 33..64 with eigenvectors) shared in LDS by one producer
+     *     wavefront per workgroup that runs the chase for several problems
+     *     and logs its rotations, applied to Q by one consumer wavefront per
+     *     problem; lanes_per_problem then counts producer lanes.
+     * Orders above 32 always use LDS (1 means the default there). */
     int band_storage;
     /* Form of the implicit step (BatchLAS steqr algorithm page, "the two CTA
      * update schemes"): STEQR_EXP (0, default) writes each local similarity
@@ -105,7 +109,8 @@ int steqr_batched_ex(const void *d, const void *e, void *lambda, void *Q,
 /* Describe the launch steqr_batched_ex would make, without launching:
  * padded order (the compile-time order the kernel runs at, >= n), lanes per
  * problem P, rows of Q held per lane, wavefronts per workgroup, workgroups
- * for `batch` matrices and band storage (1 registers, 2 LDS). Returns 0 or
+ * for `batch` matrices and band storage (1 registers, 2 LDS, 3 LDS with
+ * producer and consumer wavefronts). Returns 0 or
  * the same negative codes as steqr_batched_ex (-5/-7/-8/-10). Any output
  * pointer may be NULL. */
 int steqr_query(int n, int batch, int jobz, int dtype, const steqr_params *params,

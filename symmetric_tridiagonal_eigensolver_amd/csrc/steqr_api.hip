@@ -29,6 +29,7 @@ int padded_order(int n) {
 // SIMDs idle (n = 32 keeps two lanes). Orders 33..64 run one problem per
 // wavefront.
 int default_lanes(int dtype, int N, int jobz, int band) {
+    if (band == 3) return 8;  // producer lanes per problem
     if (N >= 64) return 64;
     if (jobz) {
         if (N == 4) return 4;
@@ -50,6 +51,7 @@ const Entry* search(const Table& t, int dtype, int N, int P, int jobz, int band)
 
 const Entry* find_entry(int dtype, int N, int P, int jobz, int band, int pg) {
     if (N == 64) {
+        if (band == 3) return search(pg ? steqr::table_pc_pg() : steqr::table_pc(), dtype, N, P, jobz, band);
         if (band != 2) return nullptr;
         return search(pg ? steqr::table_wave_pg() : steqr::table_wave(), dtype, N, P, jobz, band);
     }
@@ -82,7 +84,7 @@ struct Plan {
 // wavefront) and, with eigenvectors, wherever the registers are better
 // spent on rows of Q: order 32, and order 16 in double precision.
 int default_band(int dtype, int N, int jobz) {
-    if (N >= 64) return 2;
+    if (N >= 64) return jobz ? 3 : 2;
     if (jobz && (N == 32 || (N == 16 && dtype == STEQR_F64))) return 2;
     return 1;
 }
@@ -100,7 +102,7 @@ int plan_launch(int n, int batch, int jobz, int dtype, const steqr_params* prm, 
         if (prm->update_scheme != STEQR_EXP && prm->update_scheme != STEQR_PG) return -10;
         pg = prm->update_scheme == STEQR_PG;
         band = prm->band_storage;
-        if (band < 0 || band > 2) return -10;
+        if (band < 0 || band > 3) return -10;
         if (prm->waves_per_block != 0) {
             if (prm->waves_per_block != 1 && prm->waves_per_block != 2 && prm->waves_per_block != 4)
                 return -10;
@@ -118,18 +120,27 @@ int plan_launch(int n, int batch, int jobz, int dtype, const steqr_params* prm, 
     }
     const int N = padded_order(n < 2 ? 2 : n);
     if (N < 0) return -5;  // order not provided by this build
-    if (band == 0 || N >= 64) band = default_band(dtype, N, jobz);
+    if (band == 0 || (N >= 64 && band == 1)) band = default_band(dtype, N, jobz);
     if (P == 0) P = default_lanes(dtype, N, jobz, band);
     const Entry* ent = find_entry(dtype, N, P, jobz, band, pg);
     if (!ent) return -10;
-    // keep a workgroup's LDS within 64 KiB
-    while (waves > 1 && (long)waves * ent->lds_per_wave > 65536) waves /= 2;
+    int per_block;
+    if (band == 3) {
+        // W consumer wavefronts (one problem each, one row of Q per lane)
+        // and one producer wavefront per workgroup
+        waves = ent->pc_w + 1;
+        per_block = ent->pc_w;
+        p.R = 1;
+    } else {
+        // keep a workgroup's LDS within 64 KiB
+        while (waves > 1 && (long)waves * ent->lds_per_wave > 65536) waves /= 2;
+        per_block = waves * (64 / P);
+        p.R = jobz ? (N + P - 1) / P : 0;
+    }
     p.waves = waves;
-    const int per_block = waves * (64 / P);
     p.entry = ent;
     p.N = N;
     p.P = P;
-    p.R = jobz ? (N + P - 1) / P : 0;
     p.band = band;
     p.grid = batch > 0 ? (int)(((long)batch + per_block - 1) / per_block) : 0;
     *out = p;

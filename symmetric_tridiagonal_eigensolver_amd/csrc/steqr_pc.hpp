@@ -1,0 +1,470 @@
+// Producer-consumer steqr kernel for orders 33..64 with eigenvectors
+// (gfx950, wave64).
+//
+// At these orders one problem's Q fills a wavefront's registers (lane i
+// holds row i: 64 values), so a one-problem-per-wavefront kernel runs the
+// serial band chase on all 64 lanes for the benefit of one problem, and
+// the chase, not the Q update, sets its time. Here a workgroup splits the
+// two parts of the step [algo, Givens/similarity paragraphs and eigenvector
+// accumulation]:
+//  * one producer wavefront holds the bands of W problems in LDS, one chunk
+//    of P lanes per problem, and runs the whole per-problem algorithm of
+//    steqr_chunkl.hpp (settle, shift, chase, 2x2 blocks as one-step chases)
+//    without Q. Each chase step writes its rotation (c, s) to a rotation
+//    log in LDS; each pass writes, per problem, the part of Q it touches
+//    (first position, step count) and whether the problem was mirrored
+//    (block direction) before the pass;
+//  * W consumer wavefronts each hold one problem's Q (lane = row) and apply
+//    the logged rotations of the previous pass while the producer computes
+//    the next one (two log slots, one workgroup barrier per pass).
+// The consumers' column updates are the same as the other kernels' and
+// their order of application is the producer's, so the results equal the
+// chunked kernels' up to the same rounding. The bands, the sort keys and
+// all control decisions stay with the producer; the consumers only read
+// the log, the ranks of the final sort and the final mirror flag.
+// Citations as in steqr_chunk.hpp.
+#pragma once
+
+#include "steqr_chunkl.hpp"
+
+namespace steqr {
+
+template <typename T, int N, int W, int P>
+struct SmemPC {
+    static constexpr int CH = 64 / P;                     // producer chunks (>= W)
+    static constexpr int SLOT = 2 * N + 1;                // d[N], e[N], pad
+    static constexpr size_t band_bytes = ((CH * SLOT * sizeof(T) + 15) / 16) * 16;
+    // rotation log: [slot 0/1][problem][position] -> (c, s)
+    static constexpr size_t rot_bytes = (size_t)2 * W * (N - 1) * 2 * sizeof(T);
+    // per slot: control word, then per problem (flip, first position, steps)
+    static constexpr int HDR = 1 + 3 * W;
+    static constexpr size_t hdr_bytes = ((2 * HDR * sizeof(int) + 15) / 16) * 16;
+    static constexpr size_t rank_bytes = ((CH * N * sizeof(int) + 15) / 16) * 16;
+    static constexpr size_t fin_bytes = ((W * sizeof(int) + 15) / 16) * 16;
+    static constexpr size_t bytes = band_bytes + rot_bytes + hdr_bytes + rank_bytes + fin_bytes;
+};
+
+// OR over the P lanes of a chunk for 64-bit masks
+template <int P>
+__device__ __forceinline__ uint64_t chunk_or64(uint64_t v) {
+    const unsigned lo = chunk_or<P>((unsigned)v), hi = chunk_or<P>((unsigned)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
+template <typename T, int N, int W, int P, bool PG>
+__global__ void __launch_bounds__((W + 1) * 64) steqr_pc_kernel(KernelArgs args) {
+    static_assert(N == 64, "the producer-consumer kernel is for order 64");
+    static_assert(P >= 2 && (64 % P) == 0 && (N % P) == 0 && 64 / P >= W, "P lanes per chunk");
+    constexpr int CH = 64 / P;
+    constexpr int K = N / P;  // positions per producer lane
+    using M = uint64_t;
+    using F = Fp<T>;
+    using S = SmemPC<T, N, W, P>;
+    enum { ST_OPEN = 0, ST_ITER = 1, ST_DONE = 2 };
+    enum { CTRL_PASS = 1, CTRL_END = 2 };
+
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    T* const band = reinterpret_cast<T*>(smem_raw);
+    T* const rot = reinterpret_cast<T*>(smem_raw + S::band_bytes);
+    int* const hdr = reinterpret_cast<int*>(smem_raw + S::band_bytes + S::rot_bytes);
+    int* const ranks =
+        reinterpret_cast<int*>(smem_raw + S::band_bytes + S::rot_bytes + S::hdr_bytes);
+    int* const fin = reinterpret_cast<int*>(smem_raw + S::band_bytes + S::rot_bytes +
+                                            S::hdr_bytes + S::rank_bytes);
+
+    const T* __restrict__ gd = static_cast<const T*>(args.d);
+    const T* __restrict__ ge = static_cast<const T*>(args.e);
+    T* __restrict__ glam = static_cast<T*>(args.lam);
+    T* __restrict__ gq = static_cast<T*>(args.q);
+    const int n = args.n;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const long first = (long)blockIdx.x * W;  // the workgroup's first problem
+
+    if (wave < W) {
+        // ============================================================ consumer
+        const long prob = first + wave;
+        const bool live = prob < (long)args.batch;
+        T q[N];
+        static_for<N>([&](auto J) {
+            constexpr int j = decltype(J)::value;
+            q[j] = (lane == j) ? T(1) : T(0);
+        });
+        // The producer mirrors a problem (positions p <-> N-1-p, Q's columns
+        // included) while a block that converges at its top is reduced.
+        // Instead of reversing its registers, the consumer tracks the
+        // orientation and applies a rotation at mirrored position p to the
+        // columns (N-1-p, N-2-p), which is the same update.
+        int orient = 0;
+        int slot = 0;
+        while (true) {
+            __syncthreads();
+            const int* h = hdr + slot * S::HDR;
+            if (h[0] == CTRL_END) break;
+            orient ^= h[1 + 3 * wave];
+            const int s = h[2 + 3 * wave];
+            const int steps = h[3 + 3 * wave];
+            if (steps > 0) {
+                const T* lg = rot + (size_t)(slot * W + wave) * (N - 1) * 2;
+                const int me = s + steps;
+                if (orient == 0) {
+                    static_for_while<N - 1>([&](auto I) {
+                        constexpr int p = decltype(I)::value;
+                        if (p >= s) F::rot(q[p], q[p + 1], lg[2 * p], lg[2 * p + 1]);
+                        return p + 1 < me;
+                    });
+                } else {
+                    static_for_while<N - 1>([&](auto I) {
+                        constexpr int p = decltype(I)::value;
+                        if (p >= s) F::rot(q[N - 1 - p], q[N - 2 - p], lg[2 * p], lg[2 * p + 1]);
+                        return p + 1 < me;
+                    });
+                }
+            }
+            slot ^= 1;
+        }
+        __syncthreads();
+        // every block is closed, hence un-mirrored, by now (orient ^ fin is
+        // 0); a remaining reversal would be folded into the column index
+        const bool rev = (orient ^ fin[wave]) != 0;
+        if (live & (lane < n)) {
+            const int* rk = ranks + wave * N;
+            T* qrow = gq + prob * (long)n * n + (long)lane * n;
+            static_for<N>([&](auto J) {
+                constexpr int j = decltype(J)::value;
+                const int jj = rev ? N - 1 - j : j;
+                if (jj < n) qrow[rk[jj]] = q[j];
+            });
+        }
+        return;
+    }
+
+    // ================================================================ producer
+    const int chunk = lane / P;
+    const int r = lane % P;
+    const long prob = first + chunk;
+    const bool live = (chunk < W) & (prob < (long)args.batch);
+    const long pb = live ? prob : (long)args.batch - 1;
+    T* const sd = band + chunk * S::SLOT;
+    T* const se = sd + N;
+    int* const srank = ranks + chunk * N;
+
+    static_for<K>([&](auto KK) {
+        constexpr int k = decltype(KK)::value;
+        const int p = r + k * P;
+        const int pc = p < n ? p : n - 1;
+        const T v = gd[pb * n + pc];
+        sd[p] = (live & (p < n)) ? v : T(0);
+        T w = T(0);
+        if (n > 1) {
+            const int ec = p < n - 1 ? p : n - 2;
+            w = ge[pb * (n - 1) + ec];
+        }
+        se[p] = (live & (p < n - 1)) ? w : T(0);
+    });
+    __builtin_amdgcn_wave_barrier();
+    M zeromask;
+    {
+        M part = 0;
+        static_for<K>([&](auto KK) {
+            constexpr int k = decltype(KK)::value;
+            const int p = r + k * P;
+            part |= (se[p] == T(0)) ? ((M)1 << p) : (M)0;
+        });
+        zeromask = chunk_or64<P>(part);
+    }
+
+    int state = live ? ST_OPEN : ST_DONE;
+    int l1 = 0, bt = 0, bb = 0, m = 0, s = 0;
+    int jtot = 0;
+    const int nmaxit = (args.max_sweeps_per_n > 0 ? args.max_sweeps_per_n : 0) * n;
+    bool mir = false, failed = false, last = false, pending = false;
+    int flip = 0;  // mirrors of Q not yet handed to the consumer (parity)
+    int mode = 0;
+    T anorm = T(0);
+    M zeroed = 0;
+    int info = 0;
+
+    // reverse the chunk's band (lane-parallel); Q's columns are the
+    // consumer's: count the reversal
+    auto mirror_all = [&]() __attribute__((always_inline)) {
+        T dv[K], ev[K];
+        static_for<K>([&](auto KK) {
+            constexpr int k = decltype(KK)::value;
+            const int p = r + k * P;
+            dv[k] = sd[N - 1 - p];
+            ev[k] = se[p < N - 1 ? N - 2 - p : N - 1];
+        });
+        __builtin_amdgcn_wave_barrier();
+        static_for<K>([&](auto KK) {
+            constexpr int k = decltype(KK)::value;
+            const int p = r + k * P;
+            sd[p] = dv[k];
+            se[p] = ev[k];
+        });
+        __builtin_amdgcn_wave_barrier();
+        flip ^= 1;
+    };
+
+    // zero the negligible e's found in the block, undo the scaling (d
+    // always, e too when the block failed), undo the mirror
+    auto close_block = [&](bool fail) __attribute__((always_inline)) {
+        const T un = (mode == 1) ? anorm / F::ssfmax : ((mode == 2) ? anorm / F::ssfmin : T(1));
+        static_for<K>([&](auto KK) {
+            constexpr int k = decltype(KK)::value;
+            const int p = r + k * P;
+            T ev = se[p], dv = sd[p];
+            ev = ((zeroed >> p) & 1) ? T(0) : ev;
+            if (mode != 0) {
+                dv = ((p >= bt) & (p <= bb)) ? dv * un : dv;
+                ev = (fail & (p >= bt) & (p < bb)) ? ev * un : ev;
+            }
+            sd[p] = dv;
+            se[p] = ev;
+        });
+        __builtin_amdgcn_wave_barrier();
+        if (mir) mirror_all();
+        mir = false;
+        mode = 0;
+        zeroed = 0;
+    };
+
+    // open the next block [algo, steqr_cta paragraph; scaling], as in
+    // steqr_chunkl.hpp
+    auto open_blocks = [&]() __attribute__((always_inline)) {
+        while (state == ST_OPEN) {
+            const M avail = ~zeromask & ~bits_below<M>(l1) & bits_below<M>(n - 1);
+            if (avail == 0) {
+                state = ST_DONE;
+                break;
+            }
+            const int lo = lsb(avail);
+            const int hi = lsb((M)(zeromask & ~bits_below<M>(lo)));
+            l1 = hi + 1;
+            last = (avail & ~bits_below<M>(l1)) == 0;
+            T an = T(0);
+            bool hasnan = false;
+            static_for<K>([&](auto KK) {
+                constexpr int k = decltype(KK)::value;
+                const int p = r + k * P;
+                const bool ind = (p >= lo) & (p <= hi);
+                const bool ine = (p >= lo) & (p < hi);
+                const T dv = sd[p], ev = se[p];
+                an = ind ? F::max(an, F::abs(dv)) : an;
+                an = ine ? F::max(an, F::abs(ev)) : an;
+                hasnan = hasnan | (ind & (dv != dv)) | (ine & (ev != ev));
+            });
+            an = chunk_max<P>(an);
+            hasnan = chunk_or<P>(hasnan ? 1u : 0u) != 0;
+            anorm = hasnan ? F::qnan() : an;
+            if (anorm == T(0)) continue;
+            mode = (anorm > F::ssfmax) ? 1 : ((anorm < F::ssfmin) ? 2 : 0);
+            if (mode != 0) {
+                const T sg = ((mode == 1) ? F::ssfmax : F::ssfmin) / anorm;
+                static_for<K>([&](auto KK) {
+                    constexpr int k = decltype(KK)::value;
+                    const int p = r + k * P;
+                    const T dv = sd[p], ev = se[p];
+                    sd[p] = ((p >= lo) & (p <= hi)) ? dv * sg : dv;
+                    se[p] = ((p >= lo) & (p < hi)) ? ev * sg : ev;
+                });
+                __builtin_amdgcn_wave_barrier();
+            }
+            mir = !(F::abs(sd[hi]) < F::abs(sd[lo]));
+            if (mir) mirror_all();
+            bt = mir ? N - 1 - hi : lo;
+            bb = mir ? N - 1 - lo : hi;
+            m = bb;
+            zeroed = bt > 0 ? ((M)1 << (bt - 1)) : (M)0;
+            state = ST_ITER;
+        }
+    };
+
+    int slot = 0;
+    T x = T(0), y = T(0), dcur = T(0);
+    while (true) {
+        // ------------------------------------------------------------ settle
+        if (__any(state == ST_OPEN)) open_blocks();
+        const bool iter = state == ST_ITER;
+        if (!__any(iter)) break;
+        M neg;
+        {
+            M part = 0;
+            static_for<K>([&](auto KK) {
+                constexpr int k = decltype(KK)::value;
+                const int p = r + k * P;
+                if (p < N - 1)
+                    part |= negligible(se[p], sd[p], sd[p + 1 < N ? p + 1 : N - 1])
+                                ? ((M)1 << p) : (M)0;
+            });
+            neg = chunk_or64<P>(part) | zeroed;
+        }
+        const M rng = bit_range<M>(bt, m - 1);
+        const M nb = neg & rng;
+        const M clr = rng & ~neg;
+        const bool conv = iter & (clr == 0);
+        const bool go = iter & (clr != 0);
+        const int t = msb((M)(clr | (M)1));
+        const M above = nb & bit_range<M>(bt, t - 1);
+        const int s2 = above ? msb(above) + 1 : bt;
+        const M znew = (nb & bit_range<M>(t + 1, m - 1)) | (above ? ((M)1 << (above ? s2 - 1 : 0)) : (M)0);
+        zeroed |= conv ? nb : (go ? znew : (M)0);
+        const bool jac = go & (t == s2);
+        const bool fail = go & !jac & (jtot >= nmaxit);
+        const bool sweep = go & !jac & !fail;
+        const int jpos = s2;
+        m = jac ? s2 - 1 : (go ? t + 1 : m);
+        s = go ? s2 : s;
+        jtot += sweep ? 1 : 0;
+        const bool close_now = fail | (conv & !last);
+        if (__any(close_now)) {
+            if (close_now) {
+                close_block(fail);
+                if (fail) {
+                    failed = true;
+                    M part = 0;
+                    static_for<K>([&](auto KK) {
+                        constexpr int k = decltype(KK)::value;
+                        const int p = r + k * P;
+                        part |= ((p < n - 1) & (se[p] != T(0))) ? ((M)1 << p) : (M)0;
+                    });
+                    info = popc(chunk_or64<P>(part));
+                    info = info > 0 ? info : 1;
+                }
+                state = fail ? ST_DONE : ST_OPEN;
+            }
+        }
+        pending = pending | (conv & last);
+        state = (conv & last) ? ST_DONE : state;
+        // shift [algo, shift section] and the first running pair; a 2x2
+        // block is a one-step chase seeded with its closed-form rotation
+        const int mi = sweep ? m : (jac ? jpos + 1 : 1);
+        const int si = sweep ? s : (jac ? jpos : 0);
+        const T dm = sd[mi], dm1 = sd[mi - 1], em1 = se[mi - 1];
+        const T mu = lapack_shift(dm, dm1, em1);
+        dcur = sd[si];
+        x = dcur - mu;
+        y = PG ? T(1) : se[si];
+        if (__any(jac)) {
+            T rt1, rt2, cs, sj;
+            sym2x2(dm1, em1, dm, rt1, rt2, cs, sj);
+            x = jac ? (PG ? cs * em1 : cs) : x;
+            y = jac ? -sj : y;
+            zeroed |= jac ? ((M)1 << jpos) : (M)0;
+        }
+        const unsigned steps = sweep ? (unsigned)(m - s) : (jac ? 1u : 0u);
+        // hand the pass to the consumers: mirror parity, first position,
+        // step count (all lanes of a chunk write the same words)
+        int* h = hdr + slot * S::HDR;
+        if (chunk < W) {
+            h[1 + 3 * chunk] = flip;
+            h[2 + 3 * chunk] = s;
+            h[3 + 3 * chunk] = (int)steps;
+        }
+        if (lane == 0) h[0] = CTRL_PASS;
+        flip = 0;
+
+        // ------------------------------------------------------------ chase
+        T* const lg = rot + (size_t)(slot * W + (chunk < W ? chunk : 0)) * (N - 1) * 2;
+        const bool logs = chunk < W;
+        T d0 = sd[0], e0 = se[0], d1 = sd[1], e1 = se[1];
+        T cp = T(1);
+        static_for<N - 1>([&](auto I) {
+            constexpr int p = decltype(I)::value;
+            T d2 = T(0), e2 = T(0);
+            if constexpr (p + 2 < N) {
+                d2 = sd[p + 2];
+                e2 = se[p + 2];
+            }
+            if ((unsigned)(p - s) < steps) {
+                T c, sn, rr;
+                if constexpr (PG) {
+                    // PG step [algo, the two CTA update schemes], as in
+                    // steqr_chunkl.hpp
+                    const T f = y * e0;
+                    const T b = cp * e0;
+                    lartg(x, f, c, sn, rr);
+                    const T gs = dcur;
+                    const T rs = F::fma(d1 - gs, sn, (c + c) * b);
+                    const T pk = sn * rs;
+                    if constexpr (p > 0) se[p - 1] = rr;
+                    sd[p] = gs + pk;
+                    dcur = d1 - pk;
+                    x = F::fma(c, rs, -b);
+                    y = sn;
+                    cp = c;
+                } else {
+                    const T a = dcur;
+                    lartg(x, y, c, sn, rr);
+                    const T b = cp * e0;
+                    const T pp = c * a + sn * b;
+                    const T qq = c * b + sn * d1;
+                    const T an = pp * c + qq * sn;
+                    const T bn = qq * c - pp * sn;
+                    if constexpr (p > 0) se[p - 1] = rr;
+                    sd[p] = an;
+                    dcur = (a + d1) - an;
+                    x = bn;
+                    y = sn * e1;
+                    cp = c;
+                }
+                if (logs) {
+                    lg[2 * p] = c;
+                    lg[2 * p + 1] = sn;
+                }
+            }
+            d0 = d1;
+            e0 = e1;
+            d1 = d2;
+            e1 = e2;
+        });
+        if (steps != 0u) {
+            const int me = s + (int)steps;
+            sd[me] = dcur;
+            se[me - 1] = x;
+        }
+        __builtin_amdgcn_wave_barrier();
+        jtot = (sweep & (mu != mu)) ? nmaxit : jtot;
+        __syncthreads();  // the log of this pass is complete
+        slot ^= 1;
+    }
+    // no pass left: tell the consumers (their last pass was the previous slot)
+    if (lane == 0) hdr[slot * S::HDR] = CTRL_END;
+    __syncthreads();
+
+    // closes of converged last blocks, the final mirror parity and the sort
+    if (__any(pending)) {
+        if (pending) close_block(false);
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (chunk < W) fin[chunk] = flip;
+    const bool sort_it = (args.do_sort != 0) & !failed;
+    T myd[K];
+    int myrank[K];
+    static_for<K>([&](auto KK) {
+        constexpr int kk = decltype(KK)::value;
+        const int j = r + kk * P;
+        const T dj = sd[j];
+        const bool nanj = dj != dj;
+        int rk = 0;
+        for (int k = 0; k < n; ++k) {
+            const T dk = sd[k];
+            const bool before = (k < j) ? ((dk <= dj) | nanj) : ((dk < dj) | (nanj & (dk == dk)));
+            rk += ((k != j) & before) ? 1 : 0;
+        }
+        myd[kk] = dj;
+        myrank[kk] = sort_it ? rk : j;
+        srank[j] = myrank[kk];
+    });
+    if (live) {
+        static_for<K>([&](auto KK) {
+            constexpr int kk = decltype(KK)::value;
+            const int j = r + kk * P;
+            if (j < n) glam[prob * n + myrank[kk]] = myd[kk];
+        });
+        if (args.info != nullptr && r == 0) args.info[prob] = info;
+    }
+    __syncthreads();  // ranks and final parity are visible to the consumers
+}
+
+}  // namespace steqr

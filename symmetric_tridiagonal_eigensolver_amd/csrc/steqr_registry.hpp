@@ -8,6 +8,7 @@
 #include "steqr_chunk.hpp"
 #include "steqr_wave.hpp"
 #include "steqr_chunkl.hpp"
+#include "steqr_pc.hpp"
 
 namespace steqr {
 
@@ -25,9 +26,11 @@ struct Entry {
     int N;                 // compile-time (padded) order
     int P;                 // lanes per problem
     int jobz;              // 0 = values, 1 = values and vectors
-    int band;              // 1 = band replicated in VGPRs, 2 = band in LDS
-    int lds_per_wave;      // bytes of LDS each wavefront uses
+    int band;              // 1 = band replicated in VGPRs, 2 = band in LDS,
+                           // 3 = band in LDS, producer and consumer wavefronts
+    int lds_per_wave;      // bytes of LDS each wavefront uses (band 3: each workgroup)
     LaunchFn fn;
+    int pc_w = 0;          // band 3: problems (consumer wavefronts) per workgroup
 };
 
 template <typename T, int N, int P, bool WANTQ, bool PG>
@@ -64,6 +67,20 @@ hipError_t launch_chunkl(const KernelArgs& args, int grid, int block, hipStream_
     { DT, N, P, Q, 2, (int)SmemL<T, N, P>::bytes_per_wave, \
       &launch_chunkl<T, N, P, (Q) != 0, STEQR_INST_PG != 0> }
 
+// Producer-consumer, order 64 with eigenvectors: W problems per workgroup
+// of W + 1 wavefronts; the grid and block are given by the caller.
+template <typename T, int N, int W, int P, bool PG>
+hipError_t launch_pc(const KernelArgs& args, int grid, int block, hipStream_t stream) {
+    constexpr size_t lds = SmemPC<T, N, W, P>::bytes;
+    hipLaunchKernelGGL((steqr_pc_kernel<T, N, W, P, PG>), dim3(grid), dim3(block), lds, stream,
+                       args);
+    return hipGetLastError();
+}
+
+#define STEQR_PC_ENTRY(DT, T, N, W, P) \
+    { DT, N, P, 1, 3, (int)SmemPC<T, N, W, P>::bytes, \
+      &launch_pc<T, N, W, P, STEQR_INST_PG != 0>, W }
+
 #define STEQR_ENTRY(DT, T, N, P, Q) \
     { DT, N, P, Q, 1, (int)Smem<T, N, P, (Q) != 0>::bytes_per_wave, \
       &launch_chunk<T, N, P, (Q) != 0, STEQR_INST_PG != 0> }
@@ -80,6 +97,7 @@ Table table_f64_n();
 Table table_wave();
 Table table_lds_f32();
 Table table_lds_f64();
+Table table_pc();
 Table table_f32_v_pg();
 Table table_f32_n_pg();
 Table table_f64_v_pg();
@@ -87,6 +105,7 @@ Table table_f64_n_pg();
 Table table_wave_pg();
 Table table_lds_f32_pg();
 Table table_lds_f64_pg();
+Table table_pc_pg();
 
 // table name for the scheme this unit is compiled for
 #if STEQR_INST_PG

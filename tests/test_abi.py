@@ -58,13 +58,35 @@ def test_version(st):
 @pytest.mark.parametrize("n,jobz,dtype,N,P", [
     (1, 1, 0, 4, 4), (4, 1, 0, 4, 4), (5, 1, 0, 8, 2), (8, 0, 0, 8, 1), (12, 1, 1, 16, 4),
     (16, 1, 0, 16, 4), (17, 1, 0, 32, 8), (32, 1, 1, 32, 8), (32, 0, 1, 32, 1), (32, 0, 0, 32, 2),
-    (33, 1, 1, 64, 64), (64, 1, 1, 64, 64), (64, 0, 0, 64, 64)])
+    (33, 1, 1, 64, 8), (64, 1, 1, 64, 8), (64, 1, 0, 64, 8), (64, 0, 0, 64, 64)])
 def test_query_default_plan(st, n, jobz, dtype, N, P):
     q = st.steqr_query(n, 1000, jobz, dtype)
     assert q["padded_n"] == N and q["lanes_per_problem"] == P
-    assert q["rows_per_lane"] == ((N + P - 1) // P if jobz else 0)
-    per_block = q["waves_per_block"] * (64 // P)
+    if q["band_storage"] == 3:
+        # producer and consumer wavefronts: one problem per consumer
+        assert n > 32 and jobz and q["rows_per_lane"] == 1
+        per_block = q["waves_per_block"] - 1
+    else:
+        assert q["rows_per_lane"] == ((N + P - 1) // P if jobz else 0)
+        per_block = q["waves_per_block"] * (64 // P)
     assert q["workgroups"] == -(-1000 // per_block)
+
+
+def test_query_producer_consumer_plans(st):
+    """Orders 33..64 with eigenvectors default to producer and consumer
+    wavefronts; band storage 2 still selects one problem per wavefront, and
+    band 3 is rejected where no such kernel exists."""
+    for dtype, w in ((0, 7), (1, 5)):
+        q = st.steqr_query(50, 700, 1, dtype)
+        assert q["band_storage"] == 3 and q["waves_per_block"] == w + 1
+        assert q["workgroups"] == -(-700 // w)
+        q2 = st.steqr_query(50, 700, 1, dtype, st.make_params(band_storage=2))
+        assert q2["band_storage"] == 2 and q2["lanes_per_problem"] == 64
+        q3 = st.steqr_query(50, 700, 1, dtype, st.make_params(band_storage=1))
+        assert q3["band_storage"] == 3
+    for n, jobz in ((50, 0), (16, 1), (32, 1)):
+        with pytest.raises(st.SteqrError):
+            st.steqr_query(n, 100, jobz, 1, st.make_params(band_storage=3))
 
 
 def test_query_explicit_lanes(st):
@@ -82,10 +104,12 @@ def test_query_band_storage(st):
     assert st.steqr_query(16, 100, 1, 1)["band_storage"] == 2
     assert st.steqr_query(32, 100, 1, 0)["band_storage"] == 2
     assert st.steqr_query(16, 100, 1, 0, st.make_params(band_storage=2))["band_storage"] == 2
-    # orders above 32 always keep the band in LDS
-    assert st.steqr_query(40, 100, 1, 1, st.make_params(band_storage=1))["band_storage"] == 2
+    # orders above 32 always keep the band in LDS (with eigenvectors: the
+    # producer and consumer wavefronts)
+    assert st.steqr_query(40, 100, 1, 1, st.make_params(band_storage=1))["band_storage"] == 3
+    assert st.steqr_query(40, 100, 0, 1, st.make_params(band_storage=1))["band_storage"] == 2
     with pytest.raises(st.SteqrError):
-        st.steqr_query(16, 100, 1, 0, st.make_params(band_storage=3))
+        st.steqr_query(16, 100, 1, 0, st.make_params(band_storage=4))
 
 
 @pytest.mark.parametrize("args,rc", [

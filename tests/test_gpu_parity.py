@@ -96,6 +96,11 @@ LANE_CASES += [
     (np.float64, 16, True, 8, 2), (np.float64, 16, True, 4, 2), (np.float64, 32, True, 16, 2),
     (np.float64, 32, True, 8, 2), (np.float32, 12, True, 4, 2), (np.float64, 27, True, 8, 2),
 ]
+# producer and consumer wavefronts (orders 33..64 with eigenvectors)
+LANE_CASES += [
+    (np.float32, 64, True, 8, 3), (np.float64, 64, True, 8, 3), (np.float64, 33, True, 8, 3),
+    (np.float32, 48, True, 8, 3), (np.float64, 57, True, 8, 3),
+]
 
 
 @pytest.mark.parametrize("dt,n,jobz,lanes,band", LANE_CASES,
