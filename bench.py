@@ -59,6 +59,7 @@ KERNEL_SOURCES = {
     "chunk": ["steqr_device.hpp", "steqr_chunk.hpp"],
     "chunkl": ["steqr_device.hpp", "steqr_chunk.hpp", "steqr_chunkl.hpp"],
     "wave": ["steqr_device.hpp", "steqr_chunk.hpp", "steqr_wave.hpp"],
+    "pc": ["steqr_device.hpp", "steqr_chunk.hpp", "steqr_chunkl.hpp", "steqr_pc.hpp"],
 }
 
 
@@ -239,8 +240,9 @@ def main() -> int:
     dtype = w.dtype
     peak = PEAK_TFLOPS[dtype]
     roof = None
-    family = ("wave" if plan["lanes_per_problem"] == 64 else
-              ("chunkl" if plan["band_storage"] == 2 else "chunk"))
+    family = ("pc" if plan["band_storage"] == 3 else
+              ("wave" if plan["lanes_per_problem"] == 64 else
+               ("chunkl" if plan["band_storage"] == 2 else "chunk")))
     if flops is not None:
         ach = flops / sec / 1e12
         ctr = None if (args.replicate or scheme) else counters_from_profiles(w.name, jobz, family)
@@ -278,7 +280,8 @@ def main() -> int:
         "config": {"workload": w.name, "n": n, "batch": nb, "jobz": "V" if jobz else "N",
                    "precision": dtype, "lanes_per_problem": plan["lanes_per_problem"],
                    "rows_per_lane": plan["rows_per_lane"], "padded_n": plan["padded_n"],
-                   "band_storage": "LDS" if plan["band_storage"] == 2 else "registers",
+                   "band_storage": {1: "registers", 2: "LDS",
+                                    3: "LDS, producer and consumer wavefronts"}[plan["band_storage"]],
                    "waves_per_block": plan["waves_per_block"],
                    "update_scheme": args.scheme.upper(),
                    "workgroups": plan["workgroups"],

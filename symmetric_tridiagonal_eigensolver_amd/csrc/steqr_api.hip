@@ -29,7 +29,7 @@ int padded_order(int n) {
 // SIMDs idle (n = 32 keeps two lanes). Orders 33..64 run one problem per
 // wavefront.
 int default_lanes(int dtype, int N, int jobz, int band) {
-    if (band == 3) return 8;  // producer lanes per problem
+    if (band == 3) return dtype == STEQR_F32 ? 16 : 4;  // producer lanes per problem
     if (N >= 64) return 64;
     if (jobz) {
         if (N == 4) return 4;

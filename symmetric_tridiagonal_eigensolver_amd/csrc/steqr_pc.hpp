@@ -34,8 +34,9 @@ struct SmemPC {
     static constexpr int CH = 64 / P;                     // producer chunks (>= W)
     static constexpr int SLOT = 2 * N + 1;                // d[N], e[N], pad
     static constexpr size_t band_bytes = ((CH * SLOT * sizeof(T) + 15) / 16) * 16;
-    // rotation log: [slot 0/1][problem][position] -> (c, s)
-    static constexpr size_t rot_bytes = (size_t)2 * W * (N - 1) * 2 * sizeof(T);
+    // rotation log: [slot 0/1][problem][position] -> (c, s); row W of each
+    // slot is a sink for the producer's unused chunks
+    static constexpr size_t rot_bytes = (size_t)2 * (W + 1) * (N - 1) * 2 * sizeof(T);
     // per slot: control word, then per problem (flip, first position, steps)
     static constexpr int HDR = 1 + 3 * W;
     static constexpr size_t hdr_bytes = ((2 * HDR * sizeof(int) + 15) / 16) * 16;
@@ -105,7 +106,7 @@ __global__ void __launch_bounds__((W + 1) * 64) steqr_pc_kernel(KernelArgs args)
             const int s = h[2 + 3 * wave];
             const int steps = h[3 + 3 * wave];
             if (steps > 0) {
-                const T* lg = rot + (size_t)(slot * W + wave) * (N - 1) * 2;
+                const T* lg = rot + (size_t)(slot * (W + 1) + wave) * (N - 1) * 2;
                 const int me = s + steps;
                 if (orient == 0) {
                     static_for_while<N - 1>([&](auto I) {
@@ -365,8 +366,7 @@ __global__ void __launch_bounds__((W + 1) * 64) steqr_pc_kernel(KernelArgs args)
         flip = 0;
 
         // ------------------------------------------------------------ chase
-        T* const lg = rot + (size_t)(slot * W + (chunk < W ? chunk : 0)) * (N - 1) * 2;
-        const bool logs = chunk < W;
+        T* const lg = rot + (size_t)(slot * (W + 1) + (chunk < W ? chunk : W)) * (N - 1) * 2;
         T d0 = sd[0], e0 = se[0], d1 = sd[1], e1 = se[1];
         T cp = T(1);
         static_for<N - 1>([&](auto I) {
@@ -408,10 +408,8 @@ __global__ void __launch_bounds__((W + 1) * 64) steqr_pc_kernel(KernelArgs args)
                     y = sn * e1;
                     cp = c;
                 }
-                if (logs) {
-                    lg[2 * p] = c;
-                    lg[2 * p + 1] = sn;
-                }
+                lg[2 * p] = c;
+                lg[2 * p + 1] = sn;
             }
             d0 = d1;
             e0 = e1;

@@ -58,7 +58,7 @@ def test_version(st):
 @pytest.mark.parametrize("n,jobz,dtype,N,P", [
     (1, 1, 0, 4, 4), (4, 1, 0, 4, 4), (5, 1, 0, 8, 2), (8, 0, 0, 8, 1), (12, 1, 1, 16, 4),
     (16, 1, 0, 16, 4), (17, 1, 0, 32, 8), (32, 1, 1, 32, 8), (32, 0, 1, 32, 1), (32, 0, 0, 32, 2),
-    (33, 1, 1, 64, 8), (64, 1, 1, 64, 8), (64, 1, 0, 64, 8), (64, 0, 0, 64, 64)])
+    (33, 1, 1, 64, 4), (64, 1, 1, 64, 4), (64, 1, 0, 64, 16), (64, 0, 0, 64, 64)])
 def test_query_default_plan(st, n, jobz, dtype, N, P):
     q = st.steqr_query(n, 1000, jobz, dtype)
     assert q["padded_n"] == N and q["lanes_per_problem"] == P
@@ -76,7 +76,7 @@ def test_query_producer_consumer_plans(st):
     """Orders 33..64 with eigenvectors default to producer and consumer
     wavefronts; band storage 2 still selects one problem per wavefront, and
     band 3 is rejected where no such kernel exists."""
-    for dtype, w in ((0, 7), (1, 5)):
+    for dtype, w in ((0, 3), (1, 11)):
         q = st.steqr_query(50, 700, 1, dtype)
         assert q["band_storage"] == 3 and q["waves_per_block"] == w + 1
         assert q["workgroups"] == -(-700 // w)

@@ -98,8 +98,8 @@ LANE_CASES += [
 ]
 # producer and consumer wavefronts (orders 33..64 with eigenvectors)
 LANE_CASES += [
-    (np.float32, 64, True, 8, 3), (np.float64, 64, True, 8, 3), (np.float64, 33, True, 8, 3),
-    (np.float32, 48, True, 8, 3), (np.float64, 57, True, 8, 3),
+    (np.float32, 64, True, 16, 3), (np.float32, 64, True, 8, 3), (np.float64, 64, True, 4, 3),
+    (np.float64, 33, True, 16, 3), (np.float32, 48, True, 16, 3), (np.float64, 57, True, 4, 3),
 ]
 
 
