@@ -50,8 +50,8 @@ const Entry* search(const Table& t, int dtype, int N, int P, int jobz, int band)
 }
 
 const Entry* find_entry(int dtype, int N, int P, int jobz, int band, int pg) {
+    if (band == 3) return search(pg ? steqr::table_pc_pg() : steqr::table_pc(), dtype, N, P, jobz, band);
     if (N == 64) {
-        if (band == 3) return search(pg ? steqr::table_pc_pg() : steqr::table_pc(), dtype, N, P, jobz, band);
         if (band != 2) return nullptr;
         return search(pg ? steqr::table_wave_pg() : steqr::table_wave(), dtype, N, P, jobz, band);
     }
@@ -126,10 +126,10 @@ int plan_launch(int n, int batch, int jobz, int dtype, const steqr_params* prm, 
     if (!ent) return -10;
     int per_block;
     if (band == 3) {
-        // W consumer wavefronts (one problem each, one row of Q per lane)
-        // and one producer wavefront per workgroup
-        waves = ent->pc_w + 1;
-        per_block = ent->pc_w;
+        // consumer wavefronts (one row of Q per lane) and one producer
+        // wavefront per workgroup
+        waves = ent->pc_waves;
+        per_block = ent->pc_np;
         p.R = 1;
     } else {
         // keep a workgroup's LDS within 64 KiB

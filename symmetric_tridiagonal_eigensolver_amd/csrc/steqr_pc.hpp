@@ -1,20 +1,21 @@
 // Producer-consumer steqr kernel for orders 33..64 with eigenvectors
 // (gfx950, wave64).
 //
-// At these orders one problem's Q fills a wavefront's registers (lane i
-// holds row i: 64 values), so a one-problem-per-wavefront kernel runs the
-// serial band chase on all 64 lanes for the benefit of one problem, and
-// the chase, not the Q update, sets its time. Here a workgroup splits the
-// two parts of the step [algo, Givens/similarity paragraphs and eigenvector
+// At these orders a problem's Q fills much of a wavefront's registers (at
+// order 64 lane i holds row i: 64 values), so a kernel that keeps both the
+// band chase and the rows of Q in one wavefront either runs the serial
+// chase on many lanes for few problems or runs out of registers; the
+// chase, not the Q update, sets its time. Here a workgroup splits the two
+// parts of the step [algo, Givens/similarity paragraphs and eigenvector
 // accumulation]:
-//  * one producer wavefront holds the bands of W problems in LDS, one chunk
+//  * one producer wavefront holds the bands of NP problems in LDS, one chunk
 //    of P lanes per problem, and runs the whole per-problem algorithm of
 //    steqr_chunkl.hpp (settle, shift, chase, 2x2 blocks as one-step chases)
 //    without Q. Each chase step writes its rotation (c, s) to a rotation
 //    log in LDS; each pass writes, per problem, the part of Q it touches
 //    (first position, step count) and whether the problem was mirrored
 //    (block direction) before the pass;
-//  * W consumer wavefronts each hold one problem's Q (lane = row) and apply
+//  * W consumer wavefronts each hold the Q of 64/N problems (lane = row) and apply
 //    the logged rotations of the previous pass while the producer computes
 //    the next one (two log slots, one workgroup barrier per pass).
 // The consumers' column updates are the same as the other kernels' and
@@ -29,19 +30,23 @@
 
 namespace steqr {
 
+// W consumer wavefronts, each holding CQ = 64/N problems (lane = row of
+// one of them), so NP = W * CQ problems per workgroup.
 template <typename T, int N, int W, int P>
 struct SmemPC {
-    static constexpr int CH = 64 / P;                     // producer chunks (>= W)
+    static constexpr int CQ = 64 / N;                     // problems per consumer
+    static constexpr int NP = W * CQ;                     // problems per workgroup
+    static constexpr int CH = 64 / P;                     // producer chunks (>= NP)
     static constexpr int SLOT = 2 * N + 1;                // d[N], e[N], pad
     static constexpr size_t band_bytes = ((CH * SLOT * sizeof(T) + 15) / 16) * 16;
-    // rotation log: [slot 0/1][problem][position] -> (c, s); row W of each
+    // rotation log: [slot 0/1][problem][position] -> (c, s); row NP of each
     // slot is a sink for the producer's unused chunks
-    static constexpr size_t rot_bytes = (size_t)2 * (W + 1) * (N - 1) * 2 * sizeof(T);
+    static constexpr size_t rot_bytes = (size_t)2 * (NP + 1) * (N - 1) * 2 * sizeof(T);
     // per slot: control word, then per problem (flip, first position, steps)
-    static constexpr int HDR = 1 + 3 * W;
+    static constexpr int HDR = 1 + 3 * NP;
     static constexpr size_t hdr_bytes = ((2 * HDR * sizeof(int) + 15) / 16) * 16;
     static constexpr size_t rank_bytes = ((CH * N * sizeof(int) + 15) / 16) * 16;
-    static constexpr size_t fin_bytes = ((W * sizeof(int) + 15) / 16) * 16;
+    static constexpr size_t fin_bytes = ((NP * sizeof(int) + 15) / 16) * 16;
     static constexpr size_t bytes = band_bytes + rot_bytes + hdr_bytes + rank_bytes + fin_bytes;
 };
 
@@ -54,13 +59,17 @@ __device__ __forceinline__ uint64_t chunk_or64(uint64_t v) {
 
 template <typename T, int N, int W, int P, bool PG>
 __global__ void __launch_bounds__((W + 1) * 64) steqr_pc_kernel(KernelArgs args) {
-    static_assert(N == 64, "the producer-consumer kernel is for order 64");
-    static_assert(P >= 2 && (64 % P) == 0 && (N % P) == 0 && 64 / P >= W, "P lanes per chunk");
+    using S = SmemPC<T, N, W, P>;
+    constexpr int CQ = S::CQ;
+    constexpr int NP = S::NP;
+    // At order 32 (two problems per consumer) this split measured slower
+    // than the LDS-band chunked kernel, so only order 64 is built.
+    static_assert(N == 64 && CQ == 1, "the producer-consumer kernel is for order 64");
+    static_assert(P >= 2 && (64 % P) == 0 && (N % P) == 0 && 64 / P >= NP, "P lanes per chunk");
     constexpr int CH = 64 / P;
     constexpr int K = N / P;  // positions per producer lane
-    using M = uint64_t;
+    using M = PosMask<N>;
     using F = Fp<T>;
-    using S = SmemPC<T, N, W, P>;
     enum { ST_OPEN = 0, ST_ITER = 1, ST_DONE = 2 };
     enum { CTRL_PASS = 1, CTRL_END = 2 };
 
@@ -80,16 +89,19 @@ __global__ void __launch_bounds__((W + 1) * 64) steqr_pc_kernel(KernelArgs args)
     const int n = args.n;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const long first = (long)blockIdx.x * W;  // the workgroup's first problem
+    const long first = (long)blockIdx.x * NP;  // the workgroup's first problem
 
     if (wave < W) {
         // ============================================================ consumer
-        const long prob = first + wave;
+        // lane = row `row` of problem `pi`
+        const int pi = wave * CQ + lane / N;
+        const int row = lane % N;
+        const long prob = first + pi;
         const bool live = prob < (long)args.batch;
         T q[N];
         static_for<N>([&](auto J) {
             constexpr int j = decltype(J)::value;
-            q[j] = (lane == j) ? T(1) : T(0);
+            q[j] = (row == j) ? T(1) : T(0);
         });
         // The producer mirrors a problem (positions p <-> N-1-p, Q's columns
         // included) while a block that converges at its top is reduced.
@@ -102,11 +114,11 @@ __global__ void __launch_bounds__((W + 1) * 64) steqr_pc_kernel(KernelArgs args)
             __syncthreads();
             const int* h = hdr + slot * S::HDR;
             if (h[0] == CTRL_END) break;
-            orient ^= h[1 + 3 * wave];
-            const int s = h[2 + 3 * wave];
-            const int steps = h[3 + 3 * wave];
+            orient ^= h[1 + 3 * pi];
+            const int s = h[2 + 3 * pi];
+            const int steps = h[3 + 3 * pi];
+            const T* lg = rot + (size_t)(slot * (NP + 1) + pi) * (N - 1) * 2;
             if (steps > 0) {
-                const T* lg = rot + (size_t)(slot * (W + 1) + wave) * (N - 1) * 2;
                 const int me = s + steps;
                 if (orient == 0) {
                     static_for_while<N - 1>([&](auto I) {
@@ -127,10 +139,10 @@ __global__ void __launch_bounds__((W + 1) * 64) steqr_pc_kernel(KernelArgs args)
         __syncthreads();
         // every block is closed, hence un-mirrored, by now (orient ^ fin is
         // 0); a remaining reversal would be folded into the column index
-        const bool rev = (orient ^ fin[wave]) != 0;
-        if (live & (lane < n)) {
-            const int* rk = ranks + wave * N;
-            T* qrow = gq + prob * (long)n * n + (long)lane * n;
+        const bool rev = (orient ^ fin[pi]) != 0;
+        if (live & (row < n)) {
+            const int* rk = ranks + pi * N;
+            T* qrow = gq + prob * (long)n * n + (long)row * n;
             static_for<N>([&](auto J) {
                 constexpr int j = decltype(J)::value;
                 const int jj = rev ? N - 1 - j : j;
@@ -144,7 +156,7 @@ __global__ void __launch_bounds__((W + 1) * 64) steqr_pc_kernel(KernelArgs args)
     const int chunk = lane / P;
     const int r = lane % P;
     const long prob = first + chunk;
-    const bool live = (chunk < W) & (prob < (long)args.batch);
+    const bool live = (chunk < NP) & (prob < (long)args.batch);
     const long pb = live ? prob : (long)args.batch - 1;
     T* const sd = band + chunk * S::SLOT;
     T* const se = sd + N;
@@ -357,7 +369,7 @@ __global__ void __launch_bounds__((W + 1) * 64) steqr_pc_kernel(KernelArgs args)
         // hand the pass to the consumers: mirror parity, first position,
         // step count (all lanes of a chunk write the same words)
         int* h = hdr + slot * S::HDR;
-        if (chunk < W) {
+        if (chunk < NP) {
             h[1 + 3 * chunk] = flip;
             h[2 + 3 * chunk] = s;
             h[3 + 3 * chunk] = (int)steps;
@@ -366,7 +378,7 @@ __global__ void __launch_bounds__((W + 1) * 64) steqr_pc_kernel(KernelArgs args)
         flip = 0;
 
         // ------------------------------------------------------------ chase
-        T* const lg = rot + (size_t)(slot * (W + 1) + (chunk < W ? chunk : W)) * (N - 1) * 2;
+        T* const lg = rot + (size_t)(slot * (NP + 1) + (chunk < NP ? chunk : NP)) * (N - 1) * 2;
         T d0 = sd[0], e0 = se[0], d1 = sd[1], e1 = se[1];
         T cp = T(1);
         static_for<N - 1>([&](auto I) {
@@ -435,7 +447,7 @@ __global__ void __launch_bounds__((W + 1) * 64) steqr_pc_kernel(KernelArgs args)
         if (pending) close_block(false);
     }
     __builtin_amdgcn_wave_barrier();
-    if (chunk < W) fin[chunk] = flip;
+    if (chunk < NP) fin[chunk] = flip;
     const bool sort_it = (args.do_sort != 0) & !failed;
     T myd[K];
     int myrank[K];

@@ -30,7 +30,8 @@ struct Entry {
                            // 3 = band in LDS, producer and consumer wavefronts
     int lds_per_wave;      // bytes of LDS each wavefront uses (band 3: each workgroup)
     LaunchFn fn;
-    int pc_w = 0;          // band 3: problems (consumer wavefronts) per workgroup
+    int pc_np = 0;         // band 3: problems per workgroup
+    int pc_waves = 0;      // band 3: wavefronts per workgroup (consumers + producer)
 };
 
 template <typename T, int N, int P, bool WANTQ, bool PG>
@@ -67,8 +68,9 @@ hipError_t launch_chunkl(const KernelArgs& args, int grid, int block, hipStream_
     { DT, N, P, Q, 2, (int)SmemL<T, N, P>::bytes_per_wave, \
       &launch_chunkl<T, N, P, (Q) != 0, STEQR_INST_PG != 0> }
 
-// Producer-consumer, order 64 with eigenvectors: W problems per workgroup
-// of W + 1 wavefronts; the grid and block are given by the caller.
+// Producer-consumer with eigenvectors: W consumer wavefronts (64/N problems
+// each) and one producer per workgroup; the grid and block are given by
+// the caller.
 template <typename T, int N, int W, int P, bool PG>
 hipError_t launch_pc(const KernelArgs& args, int grid, int block, hipStream_t stream) {
     constexpr size_t lds = SmemPC<T, N, W, P>::bytes;
@@ -79,7 +81,7 @@ hipError_t launch_pc(const KernelArgs& args, int grid, int block, hipStream_t st
 
 #define STEQR_PC_ENTRY(DT, T, N, W, P) \
     { DT, N, P, 1, 3, (int)SmemPC<T, N, W, P>::bytes, \
-      &launch_pc<T, N, W, P, STEQR_INST_PG != 0>, W }
+      &launch_pc<T, N, W, P, STEQR_INST_PG != 0>, SmemPC<T, N, W, P>::NP, (W) + 1 }
 
 #define STEQR_ENTRY(DT, T, N, P, Q) \
     { DT, N, P, Q, 1, (int)Smem<T, N, P, (Q) != 0>::bytes_per_wave, \
