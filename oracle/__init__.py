@@ -63,13 +63,14 @@ def lib(path: Optional[str] = None) -> _ct.CDLL:
             f = getattr(L, "oracle_steqr_batched_" + sfx)
             f.restype = _ct.c_int
             f.argtypes = [_ct.c_void_p] * 6 + [_ct.c_int, _ct.c_long, _ct.c_int, _ct.c_int,
-                                               _ct.c_int]
+                                               _ct.c_int, _ct.c_int]
             f = getattr(L, "oracle_lartg_" + sfx)
             f.restype = None
             f.argtypes = [ct, ct, P, P, P]
-            f = getattr(L, "oracle_shift_" + sfx)
-            f.restype = ct
-            f.argtypes = [ct, ct, ct]
+            for name in ("oracle_shift_", "oracle_shift_closed_"):
+                f = getattr(L, name + sfx)
+                f.restype = ct
+                f.argtypes = [ct, ct, ct]
             f = getattr(L, "oracle_sym2x2_" + sfx)
             f.restype = None
             f.argtypes = [ct, ct, ct, P, P, P, P]
@@ -100,10 +101,11 @@ def _ptr(a: Optional[_np.ndarray]):
 
 def steqr(d: _np.ndarray, e: _np.ndarray, jobz: bool = True,
           max_sweeps_per_n: int = 30, sort: bool = True, threads: int = 1,
-          libpath: Optional[str] = None, scheme: int = 0
+          libpath: Optional[str] = None, scheme: int = 0, shift: int = 0
           ) -> Tuple[_np.ndarray, Optional[_np.ndarray], _np.ndarray, _np.ndarray]:
     """Solve a batch. d: (batch, n), e: (batch, n-1), same float dtype.
     scheme: 0 = EXP sweeps (local similarities), 1 = PG (Parlett-Gray) sweeps.
+    shift: 0 = LAPACK-form shift, 1 = closed-form lambda+- shift.
 
     Returns (lam (batch, n), Q (batch, n, n) or None, info (batch,) int32,
     stats (batch, 3) int64 = [implicit sweeps, sweep rotations, 2x2 solves]).
@@ -132,7 +134,7 @@ def steqr(d: _np.ndarray, e: _np.ndarray, jobz: bool = True,
                   None if Q is None else Q.ctypes.data + lo * n * n * it,
                   info.ctypes.data + lo * 4,
                   stats.ctypes.data + lo * 3 * 8,
-                  n, cnt, int(max_sweeps_per_n), int(bool(sort)), int(scheme))
+                  n, cnt, int(max_sweeps_per_n), int(bool(sort)), int(scheme), int(shift))
 
     threads = max(1, min(int(threads), batch))
     if threads == 1:
@@ -157,9 +159,12 @@ def lartg(f: float, g: float, dtype=_np.float64, libpath=None):
     return c.value, s.value, r.value
 
 
-def shift(d1: float, d2: float, e1: float, dtype=_np.float64, libpath=None) -> float:
-    """Eigenvalue of [[d2, e1], [e1, d1]] nearest d1 (LAPACK-form shift)."""
-    return getattr(lib(libpath), "oracle_shift_" + _sfx(dtype))(d1, d2, e1)
+def shift(d1: float, d2: float, e1: float, dtype=_np.float64, libpath=None,
+          closed: bool = False) -> float:
+    """Eigenvalue of [[d2, e1], [e1, d1]] nearest d1 (LAPACK-form shift, or
+    the closed form lambda+- with closed=True)."""
+    name = "oracle_shift_closed_" if closed else "oracle_shift_"
+    return getattr(lib(libpath), name + _sfx(dtype))(d1, d2, e1)
 
 
 def sym2x2(a: float, b: float, c: float, dtype=_np.float64, libpath=None):

@@ -71,6 +71,21 @@ REAL SFX(oracle_shift)(REAL d1, REAL d2, REAL e1)
     return d1 - e1 / (g + R_COPYSIGN(r, g));
 }
 
+/* Shift in the closed form of the algorithm page's shift paragraph: for the
+ * trailing block B = [[a, b], [b, c]] (a = d2, b = e1, c = d1 the entry at
+ * the converging end), lambda+- = (a+c)/2 +- sqrt(((a-c)/2)^2 + b^2) and mu
+ * is lambda+ when |lambda+ - c| < |lambda- - c|, else lambda-. The square
+ * root of the sum is taken with hypot (equal in exact arithmetic, and it
+ * cannot overflow). */
+REAL SFX(oracle_shift_closed)(REAL d1, REAL d2, REAL e1)
+{
+    REAL a = d2, b = e1, c = d1;
+    REAL h = (a + c) / (REAL)2;
+    REAL r = R_HYPOT((a - c) / (REAL)2, b);
+    REAL lp = h + r, lm = h - r;
+    return (R_FABS(lp - c) < R_FABS(lm - c)) ? lp : lm;
+}
+
 /* Analytic solve of a deflated 2x2 block [[a, b], [b, c]] (algorithm page,
  * "A deflated block of size 2 is solved analytically" paragraph): returns
  * its eigenvalues rt1 (replacing a) and rt2 (replacing c) and a rotation
@@ -239,7 +254,7 @@ static void SFX(reverse_block)(REAL *d, REAL *e, REAL *Q, int n, int l, int hi)
  *        take mu from the trailing 2x2 and sweep [s, m].
  * Returns 1 when the block converged, 0 when the budget ran out. */
 static int SFX(qr_block)(REAL *d, REAL *e, REAL *Q, int n, int l, int hi,
-                         int *jtot, int nmaxit, int scheme, long long *stats)
+                         int *jtot, int nmaxit, int scheme, int shift, long long *stats)
 {
     int m = hi;
     while (m > l) {
@@ -271,7 +286,8 @@ static int SFX(qr_block)(REAL *d, REAL *e, REAL *Q, int n, int l, int hi,
         if (*jtot >= nmaxit)
             return 0;
         *jtot += 1;
-        REAL mu = SFX(oracle_shift)(d[m], d[m - 1], e[m - 1]);
+        REAL mu = shift ? SFX(oracle_shift_closed)(d[m], d[m - 1], e[m - 1])
+                        : SFX(oracle_shift)(d[m], d[m - 1], e[m - 1]);
         long rots = scheme ? SFX(oracle_sweep_pg)(d, e, Q, n, s, m, mu)
                            : SFX(oracle_sweep)(d, e, Q, n, s, m, mu);
         if (stats) {
@@ -316,7 +332,8 @@ static int SFX(before)(REAL a, int ia, REAL b, int ib)
  * list), run as a QR procedure on the possibly reversed block, then
  * unscaled. */
 int SFX(oracle_solve_one)(int n, REAL *d, REAL *e, REAL *Q, REAL *lam,
-                          int max_sweeps_per_n, int sort, int scheme, long long *stats)
+                          int max_sweeps_per_n, int sort, int scheme, int shift,
+                          long long *stats)
 {
     const REAL ssfmax = SFX(c_ssfmax)();
     const REAL ssfmin = SFX(c_ssfmin)();
@@ -376,7 +393,7 @@ int SFX(oracle_solve_one)(int n, REAL *d, REAL *e, REAL *Q, REAL *lam,
         int rev = !(R_FABS(d[hi]) < R_FABS(d[l]));
         if (rev)
             SFX(reverse_block)(d, e, Q, n, l, hi);
-        int ok = SFX(qr_block)(d, e, Q, n, l, hi, &jtot, nmaxit, scheme, stats);
+        int ok = SFX(qr_block)(d, e, Q, n, l, hi, &jtot, nmaxit, scheme, shift, stats);
         if (rev)
             SFX(reverse_block)(d, e, Q, n, l, hi);
         if (mode) {
@@ -426,11 +443,13 @@ int SFX(oracle_solve_one)(int n, REAL *d, REAL *e, REAL *Q, REAL *lam,
 /* Batched entry: d [batch][n], e [batch][n-1] (read only), lam [batch][n],
  * Q [batch][n][n] row-major or NULL, info [batch] or NULL, stats
  * [batch][3] or NULL (implicit sweeps, sweep rotations, analytic 2x2
- * solves per item); scheme 0 = EXP sweeps, 1 = PG sweeps. Returns 0, or -1
- * if n is out of range. */
+ * solves per item); scheme 0 = EXP sweeps, 1 = PG sweeps; shift 0 = the
+ * LAPACK form, 1 = the closed form lambda+-. Returns 0, or -1 if n is out
+ * of range. */
 int SFX(oracle_steqr_batched)(const REAL *d, const REAL *e, REAL *lam,
                               REAL *Q, int *info, long long *stats, int n,
-                              long batch, int max_sweeps_per_n, int sort, int scheme)
+                              long batch, int max_sweeps_per_n, int sort, int scheme,
+                              int shift)
 {
     if (n < 0 || n > 256)
         return -1;
@@ -447,7 +466,7 @@ int SFX(oracle_steqr_batched)(const REAL *d, const REAL *e, REAL *lam,
         if (st)
             st[0] = st[1] = st[2] = 0;
         int inf = SFX(oracle_solve_one)(n, dw, ew, Q ? Q + b * (long)n * n : 0,
-                                        lam + b * n, max_sweeps_per_n, sort, scheme, st);
+                                        lam + b * n, max_sweeps_per_n, sort, scheme, shift, st);
         if (info)
             info[b] = inf;
     }

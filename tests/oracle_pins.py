@@ -97,11 +97,20 @@ def pin_shift(oracle, libpath: Optional[str] = None) -> List[str]:
             d1, d2, e1 = (float(dt(v)) for v in (d1, d2, e1))
             if e1 == 0:
                 continue
-            mu = oracle.shift(d1, d2, e1, dt, libpath)
             ref = _closest_eig(d1, d2, e1)
             scale = abs(d1) + abs(d2) + abs(e1)
-            _fail(out, abs(np.longdouble(mu) - ref) <= 8 * eps * scale,
-                  "shift(%g,%g,%g)=%r, closed form %r" % (d1, d2, e1, mu, float(ref)))
+            # when both eigenvalues are (nearly) equally close to d1 either
+            # one is the nearest up to rounding
+            a, c, b = np.longdouble(d2), np.longdouble(d1), np.longdouble(e1)
+            rad = np.sqrt(((a - c) / 2) ** 2 + b * b)
+            lp, lm = (a + c) / 2 + rad, (a + c) / 2 - rad
+            tie = abs(abs(lp - c) - abs(lm - c)) <= 8 * eps * scale
+            for closed in (False, True):
+                mu = np.longdouble(oracle.shift(d1, d2, e1, dt, libpath, closed=closed))
+                ok = abs(mu - ref) <= 8 * eps * scale or \
+                    (tie and min(abs(mu - lp), abs(mu - lm)) <= 8 * eps * scale)
+                _fail(out, ok, "shift(%g,%g,%g, closed=%s)=%r, closed form %r"
+                      % (d1, d2, e1, closed, float(mu), float(ref)))
     return out
 
 
@@ -206,13 +215,13 @@ def clement(n: int):
 
 
 def pin_solve(oracle, libpath: Optional[str] = None, quick: bool = False,
-              scheme: int = 0) -> List[str]:
+              scheme: int = 0, shift: int = 0) -> List[str]:
     out: List[str] = []
     sizes = (3, 8, 13) if quick else (1, 2, 3, 5, 8, 13, 16)
     for dt in (np.float32, np.float64):
         for n in sizes:
             d, e = W.random_batch(n, 16 if quick else 48, dt, salt=5)
-            lam, Q, info, _ = oracle.steqr(d, e, True, libpath=libpath, scheme=scheme)
+            lam, Q, info, _ = oracle.steqr(d, e, True, libpath=libpath, scheme=scheme, shift=shift)
             _fail(out, not info.any(), "solve info != 0 (%s n=%d)" % (dt.__name__, n))
             tol = V.tol_of(dt, n)
             ref = V.sturm_eigvals(d, e)
@@ -236,7 +245,7 @@ def pin_solve(oracle, libpath: Optional[str] = None, quick: bool = False,
     for n in ((8, 16) if quick else (4, 8, 16, 32, 64)):
         d, e, ref = clement(n)
         for dt in (np.float32, np.float64):
-            lam, Q, info, _ = oracle.steqr(d.astype(dt), e.astype(dt), True, libpath=libpath, scheme=scheme)
+            lam, Q, info, _ = oracle.steqr(d.astype(dt), e.astype(dt), True, libpath=libpath, scheme=scheme, shift=shift)
             tol = V.tol_of(dt, n)
             err = np.abs(lam[0].astype(np.float64) - ref).max() / V.tnorm1(d, e)[0]
             _fail(out, info[0] == 0 and err <= tol, "Clement n=%d %s: %g" % (n, dt.__name__, err))
@@ -246,10 +255,10 @@ def pin_solve(oracle, libpath: Optional[str] = None, quick: bool = False,
     n = 12
     d, e = W.random_batch(n, 32, np.float64, salt=9)
     for dt, factors in ((np.float32, (1e18, 1e19, 1e-18)), (np.float64, (1e200, 1e-200))):
-        base_l, _, _, _ = oracle.steqr(d.astype(dt), e.astype(dt), False, libpath=libpath, scheme=scheme)
+        base_l, _, _, _ = oracle.steqr(d.astype(dt), e.astype(dt), False, libpath=libpath, scheme=scheme, shift=shift)
         for f in factors:
             lam, Q, info, _ = oracle.steqr((d * f).astype(dt), (e * f).astype(dt), True,
-                                           libpath=libpath, scheme=scheme)
+                                           libpath=libpath, scheme=scheme, shift=shift)
             err = V.sorted_err(lam.astype(np.float64) / f, base_l, d, e)
             _fail(out, not info.any() and err.max() <= V.tol_of(dt, n),
                   "scaling identity %s at %g: %g" % (dt.__name__, f, err.max()))
@@ -268,8 +277,10 @@ def run_all(oracle, libpath: Optional[str] = None, quick: bool = True) -> List[s
         for scheme in ((0, 1) if p in (pin_sweep, pin_solve) else (0,)):
             try:
                 if p is pin_solve:
-                    fails += [f + " [scheme %d]" % scheme
-                              for f in p(oracle, libpath, quick=quick, scheme=scheme)]
+                    for shift in (0, 1):
+                        fails += [f + " [scheme %d, shift %d]" % (scheme, shift)
+                                  for f in p(oracle, libpath, quick=quick, scheme=scheme,
+                                             shift=shift)]
                 elif p is pin_sweep:
                     fails += [f + " [scheme %d]" % scheme for f in p(oracle, libpath, scheme=scheme)]
                 else:

@@ -52,6 +52,11 @@ MUTANTS = [
     ("pg_p_not_carried", "REAL gs = d[k] - p;", "REAL gs = d[k];"),
     ("pg_f_unscaled", "REAL f = sprev * e[k];", "REAL f = e[k];"),
     ("pg_q_skipped", "SFX(rot_cols)(Q, n, k, c, sn);", "(void)0;"),
+    # the closed-form shift
+    ("closed_shift_farther", "return (R_FABS(lp - c) < R_FABS(lm - c)) ? lp : lm;",
+     "return (R_FABS(lp - c) < R_FABS(lm - c)) ? lm : lp;"),
+    ("closed_shift_radius", "REAL r = R_HYPOT((a - c) / (REAL)2, b);",
+     "REAL r = R_HYPOT((a - c), b);"),
 ]
 
 

@@ -47,9 +47,28 @@ def test_pg_sweep_pins(oracle_mod):
     assert P.pin_sweep(oracle_mod, scheme=1) == []
 
 
+@pytest.mark.parametrize("shift", [0, 1], ids=["lapack_shift", "closed_shift"])
 @pytest.mark.parametrize("scheme", [0, 1], ids=["exp", "pg"])
-def test_solve_pins_full(oracle_mod, scheme):
-    assert P.pin_solve(oracle_mod, quick=False, scheme=scheme) == []
+def test_solve_pins_full(oracle_mod, scheme, shift):
+    assert P.pin_solve(oracle_mod, quick=False, scheme=scheme, shift=shift) == []
+
+
+@pytest.mark.parametrize("wname", ["c2_f32_n16", "c4_f64_n32", "c5_f64_n64"])
+def test_closed_and_lapack_shift_agree(oracle_mod, wname):
+    """The two forms of the shift give the same eigenvalue of the trailing
+    2x2 up to rounding, hence the same eigenvalues to the tolerance and
+    nearly the same sweep counts."""
+    w = W.WORKLOADS[wname]
+    d, e = W.make_batch(w, 96)
+    ok = np.isfinite(d).all(1) & np.isfinite(e).all(1)
+    l0, _, i0, s0 = oracle_mod.steqr(d, e, False)
+    l1, Q1, i1, s1 = oracle_mod.steqr(d, e, True, shift=1)
+    assert np.array_equal(i0 > 0, i1 > 0)
+    tol = V.tol_of(d.dtype, w.n)
+    assert V.sorted_err(l1[ok], l0[ok].astype(np.float64), d[ok], e[ok]).max() <= tol
+    assert V.band_residual(d[ok], e[ok], l1[ok], Q1[ok]).max() <= tol
+    assert V.orthogonality(Q1[ok]).max() <= tol
+    assert abs(int(s1[ok, 0].sum()) - int(s0[ok, 0].sum())) <= 0.02 * s0[ok, 0].sum()
 
 
 @pytest.mark.parametrize("wname", ["c2_f32_n16", "c3_f64_n12", "c4_f64_n32"])
