@@ -53,6 +53,7 @@ extern "C" {
 enum { STEQR_N = 0, STEQR_V = 1 };     /* jobz: values only / values+vectors */
 enum { STEQR_F32 = 0, STEQR_F64 = 1 }; /* dtype */
 enum { STEQR_EXP = 0, STEQR_PG = 1 };  /* update_scheme */
+enum { STEQR_SHIFT_LAPACK = 0, STEQR_SHIFT_CLOSED = 1 };  /* shift */
 
 /* Options of steqr_batched_ex. Zero-initialised fields mean "default". */
 typedef struct steqr_params {
@@ -85,6 +86,12 @@ typedef struct steqr_params {
      * scalars (g, p, c, s) along the sweep. Both are the same implicit
      * step; results differ by rounding only. */
     int update_scheme;
+    /* Shift of each implicit step from the trailing 2x2 block (BatchLAS
+     * steqr algorithm page, shift section): STEQR_SHIFT_LAPACK (0, default)
+     * mu = d1 - e1/(g + copysign(sqrt(g^2+1), g)), g = (d2-d1)/(2 e1);
+     * STEQR_SHIFT_CLOSED (1) the closed form lambda+- of the block, the one
+     * nearer d1. The same eigenvalue of the block up to rounding. */
+    int shift;
 } steqr_params;
 
 /* Eigenvalues (jobz = STEQR_N) or eigenpairs (jobz = STEQR_V) of a batch of

@@ -5,10 +5,10 @@ this package is its Python binding. Importing it requires the library to
 be built (``python -m symmetric_tridiagonal_eigensolver_amd.build``).
 """
 from ._binding import (STEQR_EXP, STEQR_F32, STEQR_F64, STEQR_MAX_N, STEQR_N, STEQR_PG,
-                       STEQR_V, EXPORTS,
+                       STEQR_SHIFT_CLOSED, STEQR_SHIFT_LAPACK, STEQR_V, EXPORTS,
                        LIB_PATH, SteqrError, dtype_code, lib, make_params, solve,
                        steqr_batched, steqr_batched_ex, steqr_params, steqr_query, version)
 
-__all__ = ["STEQR_EXP", "STEQR_PG", "STEQR_F32", "STEQR_F64", "STEQR_MAX_N", "STEQR_N", "STEQR_V", "EXPORTS",
+__all__ = ["STEQR_EXP", "STEQR_PG", "STEQR_SHIFT_LAPACK", "STEQR_SHIFT_CLOSED", "STEQR_F32", "STEQR_F64", "STEQR_MAX_N", "STEQR_N", "STEQR_V", "EXPORTS",
            "LIB_PATH", "SteqrError", "dtype_code", "lib", "make_params", "solve",
            "steqr_batched", "steqr_batched_ex", "steqr_params", "steqr_query", "version"]

@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(PKG, "libsteqr.so")
 STEQR_N, STEQR_V = 0, 1
 STEQR_F32, STEQR_F64 = 0, 1
 STEQR_EXP, STEQR_PG = 0, 1
+STEQR_SHIFT_LAPACK, STEQR_SHIFT_CLOSED = 0, 1
 STEQR_MAX_N = 64
 
 
@@ -25,7 +26,8 @@ class steqr_params(ct.Structure):
                 ("lanes_per_problem", ct.c_int),
                 ("waves_per_block", ct.c_int),
                 ("band_storage", ct.c_int),
-                ("update_scheme", ct.c_int)]
+                ("update_scheme", ct.c_int),
+                ("shift", ct.c_int)]
 
 
 class SteqrError(RuntimeError):
@@ -64,9 +66,10 @@ def version() -> str:
 
 def make_params(max_sweeps_per_n: int = 0, sort: bool = True, lanes_per_problem: int = 0,
                 waves_per_block: int = 0, band_storage: int = 0,
-                update_scheme: int = 0) -> steqr_params:
+                update_scheme: int = 0, shift: int = 0) -> steqr_params:
     return steqr_params(int(max_sweeps_per_n), 0 if sort else 1, int(lanes_per_problem),
-                        int(waves_per_block), int(band_storage), int(update_scheme))
+                        int(waves_per_block), int(band_storage), int(update_scheme),
+                        int(shift))
 
 
 def _ptr(x) -> Optional[int]:
@@ -124,7 +127,7 @@ def dtype_code(tdtype) -> int:
 
 def solve(d, e, jobz: bool = True, *, info: bool = False, sort: bool = True,
           max_sweeps_per_n: int = 0, lanes_per_problem: int = 0, waves_per_block: int = 0,
-          band_storage: int = 0, update_scheme: int = 0, stream=None,
+          band_storage: int = 0, update_scheme: int = 0, shift: int = 0, stream=None,
           out: Optional[Tuple] = None):
     """Solve a batch held in device tensors d (batch, n), e (batch, n-1).
 
@@ -146,7 +149,7 @@ def solve(d, e, jobz: bool = True, *, info: bool = False, sort: bool = True,
         Q = torch.empty((batch, n, n), dtype=d.dtype, device=d.device) if jobz else None
         inf = torch.empty((batch,), dtype=torch.int32, device=d.device) if info else None
     prm = make_params(max_sweeps_per_n, sort, lanes_per_problem, waves_per_block, band_storage,
-                      update_scheme)
+                      update_scheme, shift)
     rc = steqr_batched_ex(d, e, lam, Q, n, batch, STEQR_V if jobz else STEQR_N,
                           dtype_code(d.dtype), stream, inf, prm)
     if rc != 0:

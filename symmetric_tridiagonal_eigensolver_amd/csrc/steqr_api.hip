@@ -35,7 +35,8 @@ int default_lanes(int dtype, int N, int jobz, int band) {
         if (N == 4) return 4;
         if (N == 8) return dtype == STEQR_F32 ? 2 : 4;
         if (N == 16) return 4;
-        return band == 2 ? 8 : 16;  // N == 32
+        if (band == 2) return dtype == STEQR_F32 ? 8 : 16;  // N == 32
+        return 16;
     }
     if (N == 32 && dtype == STEQR_F32) return 2;
     return 1;
@@ -100,6 +101,7 @@ int plan_launch(int n, int batch, int jobz, int dtype, const steqr_params* prm, 
     int pg = 0;
     if (prm) {
         if (prm->update_scheme != STEQR_EXP && prm->update_scheme != STEQR_PG) return -10;
+        if (prm->shift != STEQR_SHIFT_LAPACK && prm->shift != STEQR_SHIFT_CLOSED) return -10;
         pg = prm->update_scheme == STEQR_PG;
         band = prm->band_storage;
         if (band < 0 || band > 3) return -10;
@@ -186,6 +188,7 @@ extern "C" int steqr_batched_ex(const void* d, const void* e, void* lambda, void
     const int ms = params ? params->max_sweeps_per_n : 0;
     a.max_sweeps_per_n = ms == 0 ? 30 : (ms < 0 ? 0 : ms);
     a.do_sort = params ? !params->no_sort : 1;
+    a.shift_kind = params ? params->shift : 0;
     const hipError_t err = p.entry->fn(a, p.grid, p.waves * 64, stream);
     return err == hipSuccess ? 0 : (int)err;
 }

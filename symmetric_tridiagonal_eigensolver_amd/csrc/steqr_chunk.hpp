@@ -61,6 +61,7 @@ struct KernelArgs {
     int batch;
     int max_sweeps_per_n;
     int do_sort;
+    int shift_kind;  // 0 = LAPACK-form shift, 1 = closed form lambda+-
 };
 
 // Reverse the whole order-N problem in place (positions p <-> N-1-p for d
@@ -353,7 +354,7 @@ __global__ void __launch_bounds__(256) steqr_chunk_kernel(KernelArgs args) {
         const int mi = sweep ? m : (jac ? jpos + 1 : 1);
         const int si = sweep ? s : 0;
         const T dm = sd[mi], dm1 = sd[mi - 1], em1 = se[mi - 1];
-        const T mu = lapack_shift(dm, dm1, em1);
+        const T mu = sweep_shift(args.shift_kind != 0, dm, dm1, em1);
         // EXP carries the pair (x, y) the next rotation annihilates; PG
         // carries g in x and the previous sine in y (f = y e_p)
         x = sd[si] - mu;

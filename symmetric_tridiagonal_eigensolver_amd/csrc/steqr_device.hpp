@@ -253,6 +253,27 @@ __device__ __forceinline__ T lapack_shift(T d1, T d2, T e1) {
     return d1 - e1 * F::rcp(g + F::copysign(r, g));
 }
 
+// Closed-form shift [algo, shift section]: for the trailing block
+// B = [[a, b], [b, c]] (a = d2, b = e1, c = d1 at the converging end),
+// lambda+- = (a+c)/2 +- sqrt(((a-c)/2)^2 + b^2); the one nearer c. The block
+// is scaled, so the squares cannot overflow.
+template <typename T>
+__device__ __forceinline__ T closed_shift(T d1, T d2, T e1) {
+    using F = Fp<T>;
+    const T h = (d2 + d1) * T(0.5), hd = (d2 - d1) * T(0.5);
+    const T r = F::sqrt_fast(F::fma(hd, hd, e1 * e1));
+    const T lp = h + r, lm = h - r;
+    return (F::abs(lp - d1) < F::abs(lm - d1)) ? lp : lm;
+}
+
+// The shift of one sweep: the LAPACK form, or the closed form when
+// `closed` (a kernel argument, uniform).
+template <typename T>
+__device__ __forceinline__ T sweep_shift(bool closed, T d1, T d2, T e1) {
+    if (closed) return closed_shift(d1, d2, e1);
+    return lapack_shift(d1, d2, e1);
+}
+
 // Analytic 2x2 solve [algo, "A deflated block of size 2" paragraph]: for
 // B = [[a, b], [b, c]] the symmetric Schur rotation J = [[cs, sn], [-sn, cs]]
 // with J^T B J = diag(a - t b, c + t b), tau = (c - a)/(2b),

@@ -6,7 +6,10 @@ namespace steqr {
 #define E(N, P) STEQR_LENTRY(1, double, N, P, 1)
 static const Entry kEntries[] = {
     E(16, 8), E(16, 4),
-    E(32, 16), E(32, 8),
+    // (32, 8) needs 256 rows-of-Q registers per lane plus the chase state:
+    // register spills, and it produced wrong eigenvectors in one build;
+    // not provided
+    E(32, 16),
 };
 #undef E
 

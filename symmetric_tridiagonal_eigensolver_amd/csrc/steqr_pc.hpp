@@ -354,7 +354,7 @@ __global__ void __launch_bounds__((W + 1) * 64) steqr_pc_kernel(KernelArgs args)
         const int mi = sweep ? m : (jac ? jpos + 1 : 1);
         const int si = sweep ? s : (jac ? jpos : 0);
         const T dm = sd[mi], dm1 = sd[mi - 1], em1 = se[mi - 1];
-        const T mu = lapack_shift(dm, dm1, em1);
+        const T mu = sweep_shift(args.shift_kind != 0, dm, dm1, em1);
         dcur = sd[si];
         x = dcur - mu;
         y = PG ? T(1) : se[si];

@@ -214,7 +214,7 @@ __global__ void __launch_bounds__(256) steqr_wave_kernel(KernelArgs args) {
                 break;
             }
             ++jtot;
-            mu = lapack_shift(sd[m], sd[m - 1], se[m - 1]);
+            mu = sweep_shift(args.shift_kind != 0, sd[m], sd[m - 1], se[m - 1]);
             sweep = true;
             break;
         }

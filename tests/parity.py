@@ -23,7 +23,7 @@ import validate as V
 
 def run_gpu(d: np.ndarray, e: np.ndarray, jobz: bool, *, sort: bool = True,
             max_sweeps_per_n: int = 0, lanes: int = 0, waves: int = 0, band: int = 0,
-            scheme: int = 0):
+            scheme: int = 0, shift: int = 0):
     import torch
     import symmetric_tridiagonal_eigensolver_amd as st
     dev = torch.device("cuda:0")
@@ -31,7 +31,8 @@ def run_gpu(d: np.ndarray, e: np.ndarray, jobz: bool, *, sort: bool = True,
     te = torch.from_numpy(np.ascontiguousarray(e)).to(dev)
     lam, Q, info = st.solve(td, te, jobz, info=True, sort=sort,
                             max_sweeps_per_n=max_sweeps_per_n, lanes_per_problem=lanes,
-                            waves_per_block=waves, band_storage=band, update_scheme=scheme)
+                            waves_per_block=waves, band_storage=band, update_scheme=scheme,
+                            shift=shift)
     torch.cuda.synchronize()
     return (lam.cpu().numpy(), None if Q is None else Q.cpu().numpy(), info.cpu().numpy())
 

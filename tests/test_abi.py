@@ -57,7 +57,7 @@ def test_version(st):
 
 @pytest.mark.parametrize("n,jobz,dtype,N,P", [
     (1, 1, 0, 4, 4), (4, 1, 0, 4, 4), (5, 1, 0, 8, 2), (8, 0, 0, 8, 1), (12, 1, 1, 16, 4),
-    (16, 1, 0, 16, 4), (17, 1, 0, 32, 8), (32, 1, 1, 32, 8), (32, 0, 1, 32, 1), (32, 0, 0, 32, 2),
+    (16, 1, 0, 16, 4), (17, 1, 0, 32, 8), (32, 1, 1, 32, 16), (32, 0, 1, 32, 1), (32, 0, 0, 32, 2),
     (33, 1, 1, 64, 4), (64, 1, 1, 64, 4), (64, 1, 0, 64, 16), (64, 0, 0, 64, 64)])
 def test_query_default_plan(st, n, jobz, dtype, N, P):
     q = st.steqr_query(n, 1000, jobz, dtype)
@@ -142,7 +142,8 @@ def test_bad_params(st):
     L = st.lib()
     for prm in (st.make_params(lanes_per_problem=3), st.make_params(lanes_per_problem=128),
                 st.make_params(waves_per_block=3), st.make_params(lanes_per_problem=-4),
-                st.make_params(update_scheme=2), st.make_params(update_scheme=-1)):
+                st.make_params(update_scheme=2), st.make_params(update_scheme=-1),
+                st.make_params(shift=2), st.make_params(shift=-1)):
         got = L.steqr_batched_ex(8, 8, 8, 8, 16, 10, 1, 0, None, None, ctypes.byref(prm))
         assert got == -10
 

@@ -92,9 +92,9 @@ LANE_CASES = [c + (1,) for c in LANE_CASES if c[1] <= 32] + [c + (2,) for c in L
 # band in LDS (chunked kernel variant)
 LANE_CASES += [
     (np.float32, 16, True, 8, 2), (np.float32, 16, True, 4, 2), (np.float32, 16, True, 2, 2),
-    (np.float32, 32, True, 16, 2), (np.float32, 32, True, 8, 2), (np.float32, 32, True, 4, 2),
+    (np.float32, 32, True, 16, 2), (np.float32, 32, True, 8, 2),
     (np.float64, 16, True, 8, 2), (np.float64, 16, True, 4, 2), (np.float64, 32, True, 16, 2),
-    (np.float64, 32, True, 8, 2), (np.float32, 12, True, 4, 2), (np.float64, 27, True, 8, 2),
+    (np.float32, 12, True, 4, 2), (np.float64, 27, True, 16, 2),
 ]
 # producer and consumer wavefronts (orders 33..64 with eigenvectors)
 LANE_CASES += [
