@@ -63,7 +63,7 @@ def lib(path: Optional[str] = None) -> _ct.CDLL:
             f = getattr(L, "oracle_steqr_batched_" + sfx)
             f.restype = _ct.c_int
             f.argtypes = [_ct.c_void_p] * 6 + [_ct.c_int, _ct.c_long, _ct.c_int, _ct.c_int,
-                                               _ct.c_int, _ct.c_int]
+                                               _ct.c_int, _ct.c_int, _ct.c_int]
             f = getattr(L, "oracle_lartg_" + sfx)
             f.restype = None
             f.argtypes = [ct, ct, P, P, P]
@@ -101,11 +101,15 @@ def _ptr(a: Optional[_np.ndarray]):
 
 def steqr(d: _np.ndarray, e: _np.ndarray, jobz: bool = True,
           max_sweeps_per_n: int = 30, sort: bool = True, threads: int = 1,
-          libpath: Optional[str] = None, scheme: int = 0, shift: int = 0
+          libpath: Optional[str] = None, scheme: int = 0, shift: int = 0,
+          Z: Optional[_np.ndarray] = None
           ) -> Tuple[_np.ndarray, Optional[_np.ndarray], _np.ndarray, _np.ndarray]:
     """Solve a batch. d: (batch, n), e: (batch, n-1), same float dtype.
     scheme: 0 = EXP sweeps (local similarities), 1 = PG (Parlett-Gray) sweeps.
     shift: 0 = LAPACK-form shift, 1 = closed-form lambda+- shift.
+    Z: None (Q starts as the identity) or a (batch, n, n) row-major basis of
+    the same dtype (back-transformation: Q = Z times the rotations; needs
+    jobz). Z itself is not modified.
 
     Returns (lam (batch, n), Q (batch, n, n) or None, info (batch,) int32,
     stats (batch, 3) int64 = [implicit sweeps, sweep rotations, 2x2 solves]).
@@ -119,6 +123,12 @@ def steqr(d: _np.ndarray, e: _np.ndarray, jobz: bool = True,
     sfx = _sfx(d.dtype)
     lam = _np.empty_like(d)
     Q = _np.empty((batch, n, n), dtype=d.dtype) if jobz else None
+    if Z is not None:
+        if not jobz:
+            raise ValueError("back-transformation needs eigenvectors (jobz)")
+        if Z.shape != (batch, n, n) or Z.dtype != d.dtype:
+            raise ValueError("bad basis shape %s / dtype %s" % (Z.shape, Z.dtype))
+        Q[...] = Z
     info = _np.zeros(batch, dtype=_np.int32)
     stats = _np.zeros((batch, 3), dtype=_np.int64)
     if batch == 0 or n == 0:
@@ -134,7 +144,8 @@ def steqr(d: _np.ndarray, e: _np.ndarray, jobz: bool = True,
                   None if Q is None else Q.ctypes.data + lo * n * n * it,
                   info.ctypes.data + lo * 4,
                   stats.ctypes.data + lo * 3 * 8,
-                  n, cnt, int(max_sweeps_per_n), int(bool(sort)), int(scheme), int(shift))
+                  n, cnt, int(max_sweeps_per_n), int(bool(sort)), int(scheme), int(shift),
+                  int(Z is not None))
 
     threads = max(1, min(int(threads), batch))
     if threads == 1:

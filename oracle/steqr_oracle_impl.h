@@ -333,12 +333,16 @@ static int SFX(before)(REAL a, int ia, REAL b, int ib)
  * unscaled. */
 int SFX(oracle_solve_one)(int n, REAL *d, REAL *e, REAL *Q, REAL *lam,
                           int max_sweeps_per_n, int sort, int scheme, int shift,
-                          long long *stats)
+                          int back_transform, long long *stats)
 {
     const REAL ssfmax = SFX(c_ssfmax)();
     const REAL ssfmin = SFX(c_ssfmin)();
     int info = 0;
-    if (Q) {
+    /* Eigenvector accumulation (algorithm page, eigenvector paragraph):
+     * without back-transformation Q starts as the identity; with it, Q
+     * holds the caller's basis on entry and every rotation right-multiplies
+     * it, so the result is that basis times the product of the rotations. */
+    if (Q && !back_transform) {
         for (int i = 0; i < n * n; ++i)
             Q[i] = (REAL)0;
         for (int i = 0; i < n; ++i)
@@ -444,12 +448,13 @@ int SFX(oracle_solve_one)(int n, REAL *d, REAL *e, REAL *Q, REAL *lam,
  * Q [batch][n][n] row-major or NULL, info [batch] or NULL, stats
  * [batch][3] or NULL (implicit sweeps, sweep rotations, analytic 2x2
  * solves per item); scheme 0 = EXP sweeps, 1 = PG sweeps; shift 0 = the
- * LAPACK form, 1 = the closed form lambda+-. Returns 0, or -1 if n is out
- * of range. */
+ * LAPACK form, 1 = the closed form lambda+-; back_transform 0 = Q is
+ * output only (starts as I), 1 = Q holds a basis Z on entry and receives
+ * Z times the rotations. Returns 0, or -1 if n is out of range. */
 int SFX(oracle_steqr_batched)(const REAL *d, const REAL *e, REAL *lam,
                               REAL *Q, int *info, long long *stats, int n,
                               long batch, int max_sweeps_per_n, int sort, int scheme,
-                              int shift)
+                              int shift, int back_transform)
 {
     if (n < 0 || n > 256)
         return -1;
@@ -466,7 +471,8 @@ int SFX(oracle_steqr_batched)(const REAL *d, const REAL *e, REAL *lam,
         if (st)
             st[0] = st[1] = st[2] = 0;
         int inf = SFX(oracle_solve_one)(n, dw, ew, Q ? Q + b * (long)n * n : 0,
-                                        lam + b * n, max_sweeps_per_n, sort, scheme, shift, st);
+                                        lam + b * n, max_sweeps_per_n, sort, scheme, shift,
+                                        back_transform, st);
         if (info)
             info[b] = inf;
     }

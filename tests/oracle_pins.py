@@ -20,7 +20,13 @@ What each pin checks, and why it is independent of the oracle's own code:
   solve      whole solves against Sturm-count bisection in long double, the
              residual and orthogonality bounds, the trace and Frobenius
              invariants, the Kac-Sylvester-Clement matrix (integer spectrum),
-             and the scaling identity lambda(1e18 T) = 1e18 lambda(T).
+             and the scaling identity lambda(1e18 T) = 1e18 lambda(T);
+  back-transform  with a basis Z on entry the result is Z times the
+             rotations: Z = I reproduces the plain solve bit for bit; for an
+             orthogonal Z the columns are eigenvectors of the dense
+             A = Z T Z^T (numpy matmul in float64); for a general Z the
+             result matches the matmul Z Q; a solve that performs no
+             rotation returns Z unchanged.
 """
 from __future__ import annotations
 
@@ -267,16 +273,67 @@ def pin_solve(oracle, libpath: Optional[str] = None, quick: bool = False,
     return out
 
 
-ALL_PINS = (pin_lartg, pin_shift, pin_sym2x2, pin_sweep, pin_solve)
+def pin_back_transform(oracle, libpath: Optional[str] = None, quick: bool = False,
+                       scheme: int = 0, shift: int = 0) -> List[str]:
+    """Eigenvector accumulation with a basis on entry (algorithm page,
+    eigenvector paragraph: the rotations right-multiply the caller's basis
+    instead of the identity)."""
+    out: List[str] = []
+    kw = dict(libpath=libpath, scheme=scheme, shift=shift)
+    for dt in (np.float32, np.float64):
+        for n in ((1, 5, 16) if quick else (1, 2, 3, 7, 16, 33)):
+            batch = 12
+            d, e = W.random_batch(n, batch, dt, salt=21)
+            l0, Q0, i0, _ = oracle.steqr(d, e, True, **kw)
+            ident = np.ascontiguousarray(np.broadcast_to(np.eye(n, dtype=dt), (batch, n, n)))
+            l1, Q1, i1, _ = oracle.steqr(d, e, True, Z=ident, **kw)
+            _fail(out, np.array_equal(l1, l0) and np.array_equal(Q1, Q0)
+                  and np.array_equal(i1, i0), "Z = I differs from Q <- I (%s n=%d)"
+                  % (dt.__name__, n))
+            tol = V.tol_of(dt, n)
+            Z = W.random_basis(n, batch, dt, salt=3)
+            Zin = Z.copy()
+            l2, Q2, i2, _ = oracle.steqr(d, e, True, Z=Z, **kw)
+            _fail(out, np.array_equal(Z, Zin), "the basis was modified")
+            _fail(out, np.array_equal(l2, l0) and np.array_equal(i2, i0),
+                  "eigenvalues depend on the basis (%s n=%d)" % (dt.__name__, n))
+            Z64 = Z.astype(np.float64)
+            A = np.matmul(np.matmul(Z64, W.dense_from_bands(d.astype(np.float64),
+                                                            e.astype(np.float64))),
+                          np.swapaxes(Z64, 1, 2))
+            res = V.dense_residual(A, l2, Q2)
+            _fail(out, res.max() <= tol, "dense residual with orthogonal Z %s n=%d: %g"
+                  % (dt.__name__, n, res.max()))
+            _fail(out, V.orthogonality(Q2).max() <= tol,
+                  "orthogonality with orthogonal Z %s n=%d" % (dt.__name__, n))
+            G = W.random_basis(n, batch, dt, salt=4, orthogonal=False)
+            _, Q3, _, _ = oracle.steqr(d, e, True, Z=G, **kw)
+            ref = np.matmul(G.astype(np.float64), Q0.astype(np.float64))
+            rowerr = np.sqrt(((Q3.astype(np.float64) - ref) ** 2).sum(-1))
+            rown = np.sqrt((G.astype(np.float64) ** 2).sum(-1))
+            _fail(out, np.all(rowerr <= tol * rown), "general Z: not Z times the rotations "
+                  "(%s n=%d): %g" % (dt.__name__, n, (rowerr / rown).max()))
+        # a zero sweep budget on unreduced blocks of order >= 3 stops before
+        # the first rotation: Q must be the basis itself
+        n = 6
+        d, e = W.random_batch(n, 4, dt, salt=22)
+        G = W.random_basis(n, 4, dt, salt=5, orthogonal=False)
+        _, Q4, i4, _ = oracle.steqr(d, e, True, max_sweeps_per_n=0, Z=G, **kw)
+        _fail(out, np.all(i4 > 0) and np.array_equal(Q4, G),
+              "failed solve with no rotation changed the basis (%s)" % dt.__name__)
+    return out
+
+
+ALL_PINS = (pin_lartg, pin_shift, pin_sym2x2, pin_sweep, pin_solve, pin_back_transform)
 
 
 def run_all(oracle, libpath: Optional[str] = None, quick: bool = True) -> List[str]:
     """Every pin; the sweep and whole-solve pins for both update schemes."""
     fails: List[str] = []
     for p in ALL_PINS:
-        for scheme in ((0, 1) if p in (pin_sweep, pin_solve) else (0,)):
+        for scheme in ((0, 1) if p in (pin_sweep, pin_solve, pin_back_transform) else (0,)):
             try:
-                if p is pin_solve:
+                if p in (pin_solve, pin_back_transform):
                     for shift in (0, 1):
                         fails += [f + " [scheme %d, shift %d]" % (scheme, shift)
                                   for f in p(oracle, libpath, quick=quick, scheme=scheme,

@@ -57,6 +57,8 @@ MUTANTS = [
      "return (R_FABS(lp - c) < R_FABS(lm - c)) ? lm : lp;"),
     ("closed_shift_radius", "REAL r = R_HYPOT((a - c) / (REAL)2, b);",
      "REAL r = R_HYPOT((a - c), b);"),
+    # back-transformation: the basis on entry ignored (Q reset to I)
+    ("basis_ignored", "if (Q && !back_transform) {", "if (Q) {"),
 ]
 
 

@@ -53,6 +53,12 @@ def test_solve_pins_full(oracle_mod, scheme, shift):
     assert P.pin_solve(oracle_mod, quick=False, scheme=scheme, shift=shift) == []
 
 
+@pytest.mark.parametrize("shift", [0, 1], ids=["lapack_shift", "closed_shift"])
+@pytest.mark.parametrize("scheme", [0, 1], ids=["exp", "pg"])
+def test_back_transform_pins(oracle_mod, scheme, shift):
+    assert P.pin_back_transform(oracle_mod, quick=False, scheme=scheme, shift=shift) == []
+
+
 @pytest.mark.parametrize("wname", ["c2_f32_n16", "c4_f64_n32", "c5_f64_n64"])
 def test_closed_and_lapack_shift_agree(oracle_mod, wname):
     """The two forms of the shift give the same eigenvalue of the trailing

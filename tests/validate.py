@@ -54,6 +54,18 @@ def band_residual(d, e, lam, Q) -> np.ndarray:
     return np.where(tn > 0, rn / np.where(tn > 0, tn, 1.0), rn)
 
 
+def dense_residual(A, lam, Q) -> np.ndarray:
+    """||A Q - Q diag(lam)||_1 / ||A||_1 per item for dense (batch, n, n) A,
+    in float64. Items with ||A|| = 0 return the absolute value."""
+    A = np.asarray(A, dtype=np.float64)
+    lam = np.asarray(lam, dtype=np.float64)
+    Q = np.asarray(Q, dtype=np.float64)
+    R = np.matmul(A, Q) - Q * lam[:, None, :]
+    rn = np.abs(R).sum(axis=1).max(axis=1)
+    an = np.abs(A).sum(axis=1).max(axis=1)
+    return np.where(an > 0, rn / np.where(an > 0, an, 1.0), rn)
+
+
 def orthogonality(Q) -> np.ndarray:
     """||Q^T Q - I||_1 per item, in float64."""
     Q = np.asarray(Q, dtype=np.float64)

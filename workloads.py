@@ -160,6 +160,18 @@ def random_batch(n: int, batch: int, dtype=np.float64, salt: int = 0,
             np.ascontiguousarray(e.astype(dtype)))
 
 
+def random_basis(n: int, batch: int, dtype=np.float64, salt: int = 0,
+                 orthogonal: bool = True) -> np.ndarray:
+    """Seeded (batch, n, n) row-major basis for back-transformation tests:
+    the orthogonal factor of a Gaussian matrix (numpy QR in float64, then
+    rounded to dtype), or with orthogonal=False the Gaussian matrix itself."""
+    g = rng_for(7, n, salt)
+    a = g.standard_normal((batch, n, n))
+    if orthogonal and n > 0:
+        a = np.linalg.qr(a)[0]
+    return np.ascontiguousarray(a.astype(dtype))
+
+
 def edge_batch(kind: int, n: int, batch: int, dtype=np.float64,
                salt: int = 0) -> Tuple[np.ndarray, np.ndarray]:
     """A batch made only of edge items of one kind (for the edge-case tests).
