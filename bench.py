@@ -47,10 +47,11 @@ def flops_per_matrix(stats: np.ndarray, n: int, jobz: bool) -> np.ndarray:
     return R * (40.0 + q) + S * 10.0 + J * (25.0 + q)
 
 
-def bytes_per_matrix(n: int, itemsize: int, jobz: bool) -> int:
+def bytes_per_matrix(n: int, itemsize: int, jobz: bool, back_transform: bool = False) -> int:
     """Algorithmic HBM bytes: read d (n) and e (n-1), write lambda (n) and
-    Q (n^2) for jobz=V."""
-    return ((2 * n - 1) + n + (n * n if jobz else 0)) * itemsize
+    Q (n^2) for jobz=V; with back-transformation Q is also read (n^2)."""
+    q = (n * n if jobz else 0) * (2 if back_transform else 1)
+    return ((2 * n - 1) + n + q) * itemsize
 
 
 # Sources each kernel family is compiled from (its hash guards committed
@@ -87,7 +88,8 @@ def counters_from_profiles(wname: str, jobz: bool, family: str):
     return t
 
 
-def cpu_baseline(d: np.ndarray, e: np.ndarray, jobz: bool, wname: str, scheme: int = 0):
+def cpu_baseline(d: np.ndarray, e: np.ndarray, jobz: bool, wname: str, scheme: int = 0,
+                 Z: np.ndarray = None):
     """The CPU oracle (as is) on the host cores over the same workload."""
     import oracle
     cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
@@ -96,7 +98,7 @@ def cpu_baseline(d: np.ndarray, e: np.ndarray, jobz: bool, wname: str, scheme: i
     stats = None
     for _ in range(3):
         t = time.perf_counter()
-        _, _, _, stats = oracle.steqr(d, e, jobz, threads=cores, scheme=scheme)
+        _, _, _, stats = oracle.steqr(d, e, jobz, threads=cores, scheme=scheme, Z=Z)
         times.append(time.perf_counter() - t)
     tmed = statistics.median(times)
     nb = d.shape[0]
@@ -121,6 +123,9 @@ def main() -> int:
                     help="band storage: 0 default, 1 registers, 2 LDS")
     ap.add_argument("--scheme", default="exp", choices=["exp", "pg"],
                     help="form of the chase step: EXP (default) or PG (Parlett-Gray)")
+    ap.add_argument("--back-transform", action="store_true",
+                    help="Q holds a basis on entry (seeded random orthogonal) that the "
+                         "rotations right-multiply in place; needs --jobz V")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-named", action="store_true",
                     help="skip the secondary timing at the configuration's named lanes")
@@ -159,6 +164,10 @@ def main() -> int:
 
     w = W.WORKLOADS[args.workload]
     jobz = args.jobz == "V"
+    bt = bool(args.back_transform)
+    if bt and not jobz:
+        print("bench.py: --back-transform needs --jobz V", file=sys.stderr)
+        return 2
     scheme = 1 if args.scheme == "pg" else 0
     prm0 = st.make_params(lanes_per_problem=args.lanes, waves_per_block=args.waves,
                           band_storage=args.band, update_scheme=scheme)
@@ -171,9 +180,15 @@ def main() -> int:
     nb, n = d.shape
     lam = torch.empty_like(td)
     Q = torch.empty((nb, n, n), dtype=td.dtype, device=dev) if jobz else None
+    Z = None
+    if bt:
+        # each step overwrites Q in place with Q times the rotations: the
+        # basis stays orthogonal and its values do not change the work
+        Z = W.random_basis(n, nb, d.dtype, salt=11)
+        Q.copy_(torch.from_numpy(Z))
     info = torch.empty((nb,), dtype=torch.int32, device=dev)
     prm = st.make_params(lanes_per_problem=args.lanes, waves_per_block=args.waves,
-                         band_storage=args.band, update_scheme=scheme)
+                         band_storage=args.band, update_scheme=scheme, back_transform=bt)
     plan = st.steqr_query(n, nb, int(jobz), st.dtype_code(td.dtype), prm)
     stream = torch.cuda.current_stream()
 
@@ -207,7 +222,8 @@ def main() -> int:
     if (args.lanes == 0 and plan["lanes_per_problem"] != w.lanes and not args.replicate
             and not args.no_named):
         prm_n = st.make_params(lanes_per_problem=w.lanes, waves_per_block=args.waves,
-                               band_storage=1 if w.n <= 32 else 2, update_scheme=scheme)
+                               band_storage=1 if w.n <= 32 else 2, update_scheme=scheme,
+                               back_transform=bt)
         try:
             st.steqr_query(n, nb, int(jobz), st.dtype_code(td.dtype), prm_n)
         except st.SteqrError:
@@ -234,7 +250,7 @@ def main() -> int:
     cpu = None
     flops = None
     if not args.no_cpu:
-        cpu, stats = cpu_baseline(d, e, jobz, w.name, scheme)
+        cpu, stats = cpu_baseline(d, e, jobz, w.name, scheme, Z)
         fin = np.isfinite(d).all(1) & np.isfinite(e).all(1)
         flops = float(flops_per_matrix(stats[fin], n, jobz).sum())
     dtype = w.dtype
@@ -245,7 +261,8 @@ def main() -> int:
                ("chunkl" if plan["band_storage"] == 2 else "chunk")))
     if flops is not None:
         ach = flops / sec / 1e12
-        ctr = None if (args.replicate or scheme) else counters_from_profiles(w.name, jobz, family)
+        ctr = (None if (args.replicate or scheme or bt)
+               else counters_from_profiles(w.name, jobz, family))
         roof = {"kernel": "steqr_%s_kernel<%s, N=%d, P=%d, %s>"
                           % (family, "float" if dtype == "f32" else "double", plan["padded_n"],
                              plan["lanes_per_problem"], "V" if jobz else "N"),
@@ -262,7 +279,7 @@ def main() -> int:
                                 "source": "rocprofv3 SQ_INSTS_VALU_FLOPS_FP%s" % dtype[1:]}
         if ctr is not None and ctr.get("valu_insts_replicated"):
             roof["divergence"] = ctr["valu_insts_per_launch"] / ctr["valu_insts_replicated"]
-    bpm = bytes_per_matrix(n, d.itemsize, jobz)
+    bpm = bytes_per_matrix(n, d.itemsize, jobz, bt)
     out = {
         "metric": "matrices/sec (us/matrix) float n=16 jobz=V; % FP32 VALU peak",
         "value": nb / sec,
@@ -284,6 +301,7 @@ def main() -> int:
                                     3: "LDS, producer and consumer wavefronts"}[plan["band_storage"]],
                    "waves_per_block": plan["waves_per_block"],
                    "update_scheme": args.scheme.upper(),
+                   "back_transform": bt,
                    "workgroups": plan["workgroups"],
                    "inputs": ("replicated per wavefront (lockstep ideal)" if args.replicate
                               else ("90% iid N(0,1) + 10% edge items" if w.edge_mix

@@ -24,7 +24,9 @@
  * Ownership: every pointer is DEVICE memory owned by the caller (for
  * example torch tensors on the HIP device). The library keeps no pointer,
  * allocates nothing and holds no state between calls; calls are
- * thread-safe. Inputs are never modified.
+ * thread-safe. d and e are never modified; Q is written only, except with
+ * back-transformation (steqr_params.back_transform), where it is read on
+ * entry and overwritten in place.
  *
  * Asynchrony: the call only enqueues work on `stream` (0 = the null
  * stream); results are valid once that stream is synchronised.
@@ -92,6 +94,15 @@ typedef struct steqr_params {
      * STEQR_SHIFT_CLOSED (1) the closed form lambda+- of the block, the one
      * nearer d1. The same eigenvalue of the block up to rounding. */
     int shift;
+    /* Eigenvector accumulation (BatchLAS steqr algorithm page, eigenvector
+     * paragraph): 0 (default) Q is output only and the rotations accumulate
+     * onto the identity; 1 = back-transformation: Q holds a basis Z
+     * [batch][n][n] (row-major, as Q) on entry, the rotations right-multiply
+     * it, and Q receives Z G_1 G_2 ... G_p with the sort's column
+     * permutation. With Z the orthogonal factor of a reduction A = Z T Z^T,
+     * the result is the eigenvectors of A. Needs jobz == STEQR_V (-10
+     * otherwise). */
+    int back_transform;
 } steqr_params;
 
 /* Eigenvalues (jobz = STEQR_N) or eigenpairs (jobz = STEQR_V) of a batch of

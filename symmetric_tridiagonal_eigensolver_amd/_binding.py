@@ -27,7 +27,8 @@ class steqr_params(ct.Structure):
                 ("waves_per_block", ct.c_int),
                 ("band_storage", ct.c_int),
                 ("update_scheme", ct.c_int),
-                ("shift", ct.c_int)]
+                ("shift", ct.c_int),
+                ("back_transform", ct.c_int)]
 
 
 class SteqrError(RuntimeError):
@@ -66,10 +67,11 @@ def version() -> str:
 
 def make_params(max_sweeps_per_n: int = 0, sort: bool = True, lanes_per_problem: int = 0,
                 waves_per_block: int = 0, band_storage: int = 0,
-                update_scheme: int = 0, shift: int = 0) -> steqr_params:
+                update_scheme: int = 0, shift: int = 0,
+                back_transform: bool = False) -> steqr_params:
     return steqr_params(int(max_sweeps_per_n), 0 if sort else 1, int(lanes_per_problem),
                         int(waves_per_block), int(band_storage), int(update_scheme),
-                        int(shift))
+                        int(shift), int(bool(back_transform)))
 
 
 def _ptr(x) -> Optional[int]:
@@ -128,9 +130,11 @@ def dtype_code(tdtype) -> int:
 def solve(d, e, jobz: bool = True, *, info: bool = False, sort: bool = True,
           max_sweeps_per_n: int = 0, lanes_per_problem: int = 0, waves_per_block: int = 0,
           band_storage: int = 0, update_scheme: int = 0, shift: int = 0, stream=None,
-          out: Optional[Tuple] = None):
+          out: Optional[Tuple] = None, Z=None):
     """Solve a batch held in device tensors d (batch, n), e (batch, n-1).
 
+    Z: optional (batch, n, n) device basis for back-transformation; it is
+    overwritten in place with Z times the rotations and returned as Q.
     Returns (lam, Q or None[, info]) as device tensors; the work is enqueued
     on `stream` (default: torch's current stream) and not synchronised.
     """
@@ -148,8 +152,15 @@ def solve(d, e, jobz: bool = True, *, info: bool = False, sort: bool = True,
         lam = torch.empty_like(d)
         Q = torch.empty((batch, n, n), dtype=d.dtype, device=d.device) if jobz else None
         inf = torch.empty((batch,), dtype=torch.int32, device=d.device) if info else None
+    if Z is not None:
+        if not jobz:
+            raise ValueError("back-transformation needs jobz")
+        if Z.shape != (batch, n, n) or Z.dtype != d.dtype or Z.device != d.device \
+                or not Z.is_contiguous():
+            raise ValueError("Z must be a contiguous (batch, n, n) device tensor of d's dtype")
+        Q = Z
     prm = make_params(max_sweeps_per_n, sort, lanes_per_problem, waves_per_block, band_storage,
-                      update_scheme, shift)
+                      update_scheme, shift, Z is not None)
     rc = steqr_batched_ex(d, e, lam, Q, n, batch, STEQR_V if jobz else STEQR_N,
                           dtype_code(d.dtype), stream, inf, prm)
     if rc != 0:

@@ -113,6 +113,8 @@ int plan_launch(int n, int batch, int jobz, int dtype, const steqr_params* prm, 
         P = prm->lanes_per_problem;
         if (P < 0 || P > 64 || (P != 0 && (64 % P) != 0)) return -10;
         if (prm->no_sort != 0 && prm->no_sort != 1) return -10;
+        if (prm->back_transform != 0 && prm->back_transform != 1) return -10;
+        if (prm->back_transform == 1 && jobz != STEQR_V) return -10;
     }
     Plan p{};
     p.waves = waves;
@@ -189,6 +191,7 @@ extern "C" int steqr_batched_ex(const void* d, const void* e, void* lambda, void
     a.max_sweeps_per_n = ms == 0 ? 30 : (ms < 0 ? 0 : ms);
     a.do_sort = params ? !params->no_sort : 1;
     a.shift_kind = params ? params->shift : 0;
+    a.back_transform = params ? params->back_transform : 0;
     const hipError_t err = p.entry->fn(a, p.grid, p.waves * 64, stream);
     return err == hipSuccess ? 0 : (int)err;
 }

@@ -62,6 +62,7 @@ struct KernelArgs {
     int max_sweeps_per_n;
     int do_sort;
     int shift_kind;  // 0 = LAPACK-form shift, 1 = closed form lambda+-
+    int back_transform;  // 1: q holds a basis on entry, right-multiplied
 };
 
 // Reverse the whole order-N problem in place (positions p <-> N-1-p for d
@@ -89,6 +90,35 @@ __device__ __forceinline__ void mirror_problem(bool mir, T (&d)[N], T (&e)[N], T
                 q[i][p] = mir ? b : a;
                 q[i][N - 1 - p] = mir ? a : b;
             });
+        });
+    }
+}
+
+// Copy `total` (<= MAXE) consecutive elements from src to dst with the 64
+// lanes of a wavefront, consecutive lanes at consecutive addresses; `vec`
+// (both ends 16-byte aligned, total a multiple of the piece) moves 16-byte
+// pieces. Used between HBM and the LDS staging area of Q.
+template <typename T, int MAXE>
+__device__ __forceinline__ void copy_block(T* __restrict__ dst, const T* __restrict__ src,
+                                           int total, int lane, bool vec) {
+    if (vec) {
+        constexpr int V = 16 / sizeof(T);
+        static_for<(MAXE + 64 * V - 1) / (64 * V)>([&](auto K) {
+            constexpr int k = decltype(K)::value;
+            const int idx = (k * 64 + lane) * V;
+            if (idx < total) {
+                if constexpr (sizeof(T) == 4) {
+                    *reinterpret_cast<float4*>(dst + idx) = *reinterpret_cast<const float4*>(src + idx);
+                } else {
+                    *reinterpret_cast<double2*>(dst + idx) = *reinterpret_cast<const double2*>(src + idx);
+                }
+            }
+        });
+    } else {
+        static_for<(MAXE + 63) / 64>([&](auto K) {
+            constexpr int k = decltype(K)::value;
+            const int idx = k * 64 + lane;
+            if (idx < total) dst[idx] = src[idx];
         });
     }
 }
@@ -161,15 +191,32 @@ __global__ void __launch_bounds__(256) steqr_chunk_kernel(KernelArgs args) {
             e[p] = (live & (p < n - 1)) ? v : T(0);
         });
     }
+    // The wavefront's problems are consecutive, and so are their Q blocks
+    // in HBM: [first, first + nprob) holds the live ones.
+    const long first = ((long)blockIdx.x * (blockDim.x >> 6) + wave) * CH;
+    const int nprob = (long)args.batch - first < CH ? (int)((long)args.batch - first) : CH;
+    const int nn = n * n;
+    const bool qvec = ((nn & 3) == 0) & ((reinterpret_cast<uintptr_t>(gq) & 15) == 0);
     T q[RQ][N];
-    static_for<RQ>([&](auto II) {
-        constexpr int i = decltype(II)::value;
-        const int row = r * R + i;
-        static_for<N>([&](auto J) {
-            constexpr int j = decltype(J)::value;
-            q[i][j] = (WANTQ & (row == j)) ? T(1) : T(0);
+    if (WANTQ && args.back_transform) {
+        // back-transformation [algo, eigenvector accumulation]: the lane's
+        // rows of the caller's basis, loaded straight into registers (the
+        // loads overlap the first settle)
+        const bool vec = (n == N) & ((reinterpret_cast<uintptr_t>(gq) & 15) == 0);
+        static_for<RQ>([&](auto II) {
+            constexpr int i = decltype(II)::value;
+            load_basis_row<T, N>(gq + pb * nn, n, r * R + i, live, true, vec, q[i]);
         });
-    });
+    } else {
+        static_for<RQ>([&](auto II) {
+            constexpr int i = decltype(II)::value;
+            const int row = r * R + i;
+            static_for<N>([&](auto J) {
+                constexpr int j = decltype(J)::value;
+                q[i][j] = (WANTQ & (row == j)) ? T(1) : T(0);
+            });
+        });
+    }
     // bit p set <=> e_p == 0 (positions >= n-1 are zero padding)
     M zeromask = 0;
     static_for<N>([&](auto I) {
@@ -507,7 +554,6 @@ __global__ void __launch_bounds__(256) steqr_chunk_kernel(KernelArgs args) {
         // stage the wavefront's Q blocks (chunk c at c*n*n, row-major with
         // the sort's column permutation applied), then copy them to HBM as
         // one contiguous range: the wavefront's problems are consecutive.
-        const int nn = n * n;
         T* const myq = stage + chunk * nn;
         static_for<R>([&](auto II) {
             constexpr int i = decltype(II)::value;
@@ -520,35 +566,7 @@ __global__ void __launch_bounds__(256) steqr_chunk_kernel(KernelArgs args) {
             }
         });
         __builtin_amdgcn_wave_barrier();
-        const long first = ((long)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6)) * CH;
-        const long left = (long)args.batch - first;
-        const int nprob = left < CH ? (int)left : CH;
-        const int total = nprob * nn;  // elements this wavefront writes
-        T* const dst = gq + first * nn;
-        constexpr int MAXE = CH * N * N;
-        if (((nn & 3) == 0) & ((reinterpret_cast<uintptr_t>(gq) & 15) == 0)) {
-            // 16-byte pieces, consecutive lanes at consecutive addresses
-            constexpr int V = 16 / sizeof(T);
-            static_for<(MAXE + 64 * V - 1) / (64 * V)>([&](auto K) {
-                constexpr int k = decltype(K)::value;
-                const int idx = (k * 64 + lane) * V;
-                if (idx < total) {
-                    if constexpr (sizeof(T) == 4) {
-                        *reinterpret_cast<float4*>(dst + idx) =
-                            *reinterpret_cast<const float4*>(stage + idx);
-                    } else {
-                        *reinterpret_cast<double2*>(dst + idx) =
-                            *reinterpret_cast<const double2*>(stage + idx);
-                    }
-                }
-            });
-        } else {
-            static_for<(MAXE + 63) / 64>([&](auto K) {
-                constexpr int k = decltype(K)::value;
-                const int idx = k * 64 + lane;
-                if (idx < total) dst[idx] = stage[idx];
-            });
-        }
+        copy_block<T, CH * N * N>(gq + first * nn, stage, nprob * nn, lane, qvec);
     }
 }
 

@@ -116,14 +116,24 @@ __global__ void __launch_bounds__(256) steqr_chunkl_kernel(KernelArgs args) {
     // lane r of a chunk holds rows r, r+P, r+2P, ... of Q, so that the
     // chunk's lanes hold P consecutive rows in each row slice i
     T q[RQ][N];
-    static_for<RQ>([&](auto II) {
-        constexpr int i = decltype(II)::value;
-        const int row = i * P + r;
-        static_for<N>([&](auto J) {
-            constexpr int j = decltype(J)::value;
-            q[i][j] = (WANTQ & (row == j)) ? T(1) : T(0);
+    if (WANTQ && args.back_transform) {
+        // back-transformation [algo, eigenvector accumulation]: the rows of
+        // the caller's basis instead of the identity
+        const bool vec = (n == N) & ((reinterpret_cast<uintptr_t>(gq) & 15) == 0);
+        static_for<RQ>([&](auto II) {
+            constexpr int i = decltype(II)::value;
+            load_basis_row<T, N>(gq + pb * n * n, n, i * P + r, live, true, vec, q[i]);
         });
-    });
+    } else {
+        static_for<RQ>([&](auto II) {
+            constexpr int i = decltype(II)::value;
+            const int row = i * P + r;
+            static_for<N>([&](auto J) {
+                constexpr int j = decltype(J)::value;
+                q[i][j] = (WANTQ & (row == j)) ? T(1) : T(0);
+            });
+        });
+    }
 
     // ST_OPEN: the chunk's next block is to be opened; ST_ITER: a block is
     // being reduced; ST_DONE: nothing left to reduce (a converged last block

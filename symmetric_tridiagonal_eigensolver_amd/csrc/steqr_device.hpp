@@ -294,4 +294,48 @@ __device__ __forceinline__ void sym2x2(T a, T b, T c, T& rt1, T& rt2, T& cs, T& 
     rt2 = c + t * b;
 }
 
+// Initial row `row` of Q [algo, eigenvector accumulation]: the identity row
+// without back-transformation; with it, row `row` of the caller's basis Z
+// (qb = the problem's n x n row-major block, in bounds). Rows and columns
+// at or beyond n are padding and always start as the identity, as do rows
+// of dead problems (ok = false). With n == N and a 16-byte aligned block
+// (`vec`) the row is read as whole 16-byte pieces.
+template <typename T, int N>
+__device__ __forceinline__ void load_basis_row(const T* __restrict__ qb, int n, int row, bool ok,
+                                               bool bt, bool vec, T (&q)[N]) {
+    const bool in = bt & ok & (row < n);
+    if (!in) {
+        static_for<N>([&](auto J) {
+            constexpr int j = decltype(J)::value;
+            q[j] = (row == j) ? T(1) : T(0);
+        });
+        return;
+    }
+    const T* src = qb + (long)row * n;
+    if (vec) {
+        constexpr int V = 16 / sizeof(T);
+        static_for<N / V>([&](auto K) {
+            constexpr int k = decltype(K)::value;
+            if constexpr (sizeof(T) == 4) {
+                const float4 v = *reinterpret_cast<const float4*>(src + k * 4);
+                q[k * 4 + 0] = v.x;
+                q[k * 4 + 1] = v.y;
+                q[k * 4 + 2] = v.z;
+                q[k * 4 + 3] = v.w;
+            } else {
+                const double2 v = *reinterpret_cast<const double2*>(src + k * 2);
+                q[k * 2 + 0] = v.x;
+                q[k * 2 + 1] = v.y;
+            }
+        });
+    } else {
+        static_for<N>([&](auto J) {
+            constexpr int j = decltype(J)::value;
+            const int jc = j < n ? j : n - 1;
+            const T v = src[jc];
+            q[j] = (j < n) ? v : T(0);
+        });
+    }
+}
+
 }  // namespace steqr

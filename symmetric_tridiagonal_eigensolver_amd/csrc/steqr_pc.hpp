@@ -98,11 +98,14 @@ __global__ void __launch_bounds__((W + 1) * 64) steqr_pc_kernel(KernelArgs args)
         const int row = lane % N;
         const long prob = first + pi;
         const bool live = prob < (long)args.batch;
+        // the identity, or with back-transformation [algo, eigenvector
+        // accumulation] row `row` of the caller's basis
         T q[N];
-        static_for<N>([&](auto J) {
-            constexpr int j = decltype(J)::value;
-            q[j] = (row == j) ? T(1) : T(0);
-        });
+        {
+            const bool vec = (n == N) & ((reinterpret_cast<uintptr_t>(gq) & 15) == 0);
+            const long pc = live ? prob : (long)args.batch - 1;
+            load_basis_row<T, N>(gq + pc * n * n, n, row, live, args.back_transform != 0, vec, q);
+        }
         // The producer mirrors a problem (positions p <-> N-1-p, Q's columns
         // included) while a block that converges at its top is reduced.
         // Instead of reversing its registers, the consumer tracks the

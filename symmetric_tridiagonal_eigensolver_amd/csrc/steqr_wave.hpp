@@ -83,11 +83,19 @@ __global__ void __launch_bounds__(256) steqr_wave_kernel(KernelArgs args) {
     __builtin_amdgcn_wave_barrier();
     const M zeromask = wave_ballot(se[lane] == T(0));
 
+    // lane = row of Q; the identity, or with back-transformation [algo,
+    // eigenvector accumulation] the caller's basis
     T q[N];
-    static_for<N>([&](auto J) {
-        constexpr int j = decltype(J)::value;
-        q[j] = (WANTQ & (lane == j)) ? T(1) : T(0);
-    });
+    if (WANTQ && args.back_transform) {
+        const bool vec = (n == N) & ((reinterpret_cast<uintptr_t>(args.q) & 15) == 0);
+        load_basis_row<T, N>(static_cast<const T*>(args.q) + prob * n * n, n, lane, true, true,
+                             vec, q);
+    } else {
+        static_for<N>([&](auto J) {
+            constexpr int j = decltype(J)::value;
+            q[j] = (WANTQ & (lane == j)) ? T(1) : T(0);
+        });
+    }
 
     enum { ST_OPEN = 0, ST_ITER = 1, ST_DONE = 2 };
     int state = ST_OPEN;

@@ -8,7 +8,9 @@ inputs, item by item:
     jobz=V residual ||TQ - Q Lambda||_1/||T||_1 and ||Q^T Q - I||_1 within
     16 n eps (eps = 2^-23 / 2^-52);
   * zero matrices: eigenvalues exactly 0 and Q exactly I;
-  * failed items: NaN at the same unsorted positions.
+  * failed items: NaN at the same unsorted positions;
+  * converged items with a NaN eigenvalue (orders 1 and 2): NaN on both
+    sides.
 Eigenvectors are compared through residual and orthogonality only: their
 signs (and the basis of a repeated eigenvalue) are not unique.
 """
@@ -23,18 +25,49 @@ import validate as V
 
 def run_gpu(d: np.ndarray, e: np.ndarray, jobz: bool, *, sort: bool = True,
             max_sweeps_per_n: int = 0, lanes: int = 0, waves: int = 0, band: int = 0,
-            scheme: int = 0, shift: int = 0):
+            scheme: int = 0, shift: int = 0, Z: Optional[np.ndarray] = None):
+    """Z: optional basis for back-transformation (copied to the device and
+    overwritten there; the numpy array is untouched)."""
     import torch
     import symmetric_tridiagonal_eigensolver_amd as st
     dev = torch.device("cuda:0")
     td = torch.from_numpy(np.ascontiguousarray(d)).to(dev)
     te = torch.from_numpy(np.ascontiguousarray(e)).to(dev)
+    tz = None if Z is None else torch.from_numpy(np.ascontiguousarray(Z)).to(dev)
     lam, Q, info = st.solve(td, te, jobz, info=True, sort=sort,
                             max_sweeps_per_n=max_sweeps_per_n, lanes_per_problem=lanes,
                             waves_per_block=waves, band_storage=band, update_scheme=scheme,
-                            shift=shift)
+                            shift=shift, Z=tz)
     torch.cuda.synchronize()
     return (lam.cpu().numpy(), None if Q is None else Q.cpu().numpy(), info.cpu().numpy())
+
+
+def check_basis(d, e, Z, gpu, ora, tol_factor: float = 16.0) -> List[str]:
+    """Back-transformation with an orthogonal basis Z: status and
+    eigenvalues as in check(); the columns of the GPU's Q are orthonormal
+    eigenvectors of the dense A = Z T Z^T (residual and orthogonality within
+    16 n eps); items with T = 0 return Z exactly."""
+    out = check(d, e, gpu, ora, False, tol_factor)
+    lg, Qg, ig = gpu
+    n = d.shape[1]
+    tol = V.tol_of(d.dtype, n, tol_factor)
+    ok = (ig == 0) & (ora[2] == 0) & ~np.isnan(lg).any(axis=1)
+    if ok.any():
+        Z64 = Z[ok].astype(np.float64)
+        import workloads as W
+        A = np.matmul(np.matmul(Z64, W.dense_from_bands(d[ok].astype(np.float64),
+                                                        e[ok].astype(np.float64))),
+                      np.swapaxes(Z64, 1, 2))
+        res = V.dense_residual(A, lg[ok], Qg[ok])
+        if not (res.max() <= tol):
+            out.append("dense residual %.3g > tol %.3g" % (res.max(), tol))
+        orth = V.orthogonality(Qg[ok])
+        if not (orth.max() <= tol):
+            out.append("orthogonality %.3g > tol %.3g" % (orth.max(), tol))
+        zero = ok & (V.tnorm1(d, e) == 0)
+        if zero.any() and not np.array_equal(Qg[zero], Z[zero]):
+            out.append("zero matrix: Q is not the basis")
+    return out
 
 
 def check(d, e, gpu, ora, jobz: bool, tol_factor: float = 16.0,
@@ -64,7 +97,14 @@ def check(d, e, gpu, ora, jobz: bool, tol_factor: float = 16.0,
             out.append("info counts differ on failed items")
         if not np.array_equal(np.isnan(lg[both_fail]), np.isnan(lo[both_fail])):
             out.append("NaN positions differ on failed items")
-    ok = ~fail_g & ~fail_o
+    # converged items that carry a NaN (orders 1 and 2 reach no iteration
+    # that could fail): NaN on both sides, nothing else to compare
+    nan_g = ~fail_g & np.isnan(lg).any(axis=1)
+    nan_o = ~fail_o & np.isnan(lo).any(axis=1)
+    if not np.array_equal(nan_g, nan_o):
+        out.append("NaN eigenvalues differ on converged items %s"
+                   % items[nan_g != nan_o][:8].tolist())
+    ok = ~fail_g & ~fail_o & ~nan_g & ~nan_o
     if ok.any():
         err = V.sorted_err(lg[ok], lo[ok], d[ok], e[ok])
         if not (err.max() <= tol):

@@ -146,6 +146,16 @@ def test_bad_params(st):
                 st.make_params(shift=2), st.make_params(shift=-1)):
         got = L.steqr_batched_ex(8, 8, 8, 8, 16, 10, 1, 0, None, None, ctypes.byref(prm))
         assert got == -10
+    for bt in (2, -1):
+        prm = st.make_params()
+        prm.back_transform = bt
+        assert L.steqr_batched_ex(8, 8, 8, 8, 16, 10, 1, 0, None, None, ctypes.byref(prm)) == -10
+    # back-transformation needs eigenvectors
+    prm = st.make_params(back_transform=True)
+    assert L.steqr_batched_ex(8, 8, 8, 8, 16, 10, 0, 0, None, None, ctypes.byref(prm)) == -10
+    with pytest.raises(st.SteqrError):
+        st.steqr_query(16, 10, 0, 0, prm)
+    assert st.steqr_query(16, 10, 1, 0, prm) == st.steqr_query(16, 10, 1, 0)
 
 
 @pytest.mark.parametrize("n,jobz,dtype", [(4, 1, 0), (16, 1, 0), (16, 0, 0), (12, 1, 1),
