@@ -8,7 +8,9 @@ with them.
 The solver itself is plain C (``steqr_oracle_impl.h``), an implicit shifted
 QR/QL iteration written step by step from the BatchLAS steqr algorithm page
 (deflation, scaling, shift, Givens bulge chase, split bookkeeping,
-eigenvector accumulation, sort). It runs in the item's precision with IEEE
+eigenvector accumulation, sort), and the dense front end of the fused
+small-n syev (``syev_oracle_impl.h``: Householder reduction to tridiagonal
+form, then that solve with back-transformation). It runs in the item's precision with IEEE
 semantics and no FMA contraction. This module builds it with gcc, loads it
 with ctypes and splits batches across threads (ctypes releases the GIL while
 the C code runs).
@@ -26,6 +28,7 @@ import numpy as _np
 HERE = _os.path.dirname(_os.path.abspath(__file__))
 SOURCE = _os.path.join(HERE, "steqr_oracle.c")
 IMPL = _os.path.join(HERE, "steqr_oracle_impl.h")
+IMPL_SYEV = _os.path.join(HERE, "syev_oracle_impl.h")
 LIBNAME = "liboracle_steqr.so"
 CFLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared"]
 
@@ -47,7 +50,7 @@ def _stale(path: str) -> bool:
     if not _os.path.exists(path):
         return True
     t = _os.path.getmtime(path)
-    return any(_os.path.getmtime(s) > t for s in (SOURCE, IMPL))
+    return any(_os.path.getmtime(s) > t for s in (SOURCE, IMPL, IMPL_SYEV))
 
 
 def lib(path: Optional[str] = None) -> _ct.CDLL:
@@ -82,6 +85,16 @@ def lib(path: Optional[str] = None) -> _ct.CDLL:
             f = getattr(L, "oracle_constants_" + sfx)
             f.restype = None
             f.argtypes = [_ct.c_void_p]
+            f = getattr(L, "oracle_larfg_" + sfx)
+            f.restype = None
+            f.argtypes = [_ct.c_int, ct, _ct.c_void_p, P, P]
+            f = getattr(L, "oracle_sytrd_batched_" + sfx)
+            f.restype = _ct.c_int
+            f.argtypes = [_ct.c_void_p] * 4 + [_ct.c_int, _ct.c_long]
+            f = getattr(L, "oracle_syev_batched_" + sfx)
+            f.restype = _ct.c_int
+            f.argtypes = [_ct.c_void_p] * 4 + [_ct.c_int, _ct.c_long, _ct.c_int, _ct.c_int,
+                                               _ct.c_int, _ct.c_int]
         _libs[path] = L
     return _libs[path]
 
@@ -207,3 +220,70 @@ def constants(dtype) -> dict:
     out = _np.zeros(5, dtype=_np.float32 if sfx == "f32" else _np.float64)
     getattr(lib(), "oracle_constants_" + sfx)(out.ctypes.data)
     return dict(zip(("eps", "safmin", "ssfmax", "ssfmin", "eps2"), out.tolist()))
+
+
+def larfg(alpha: float, x: _np.ndarray, libpath=None):
+    """Householder reflector of (alpha, x): returns (beta, tau, v) with v the
+    trailing part of the reflector vector (its first entry is 1)."""
+    x = _np.array(x, copy=True)
+    assert x.ndim == 1 and x.flags.c_contiguous
+    ct = _ct.c_float if x.dtype == _np.float32 else _ct.c_double
+    beta, tau = ct(), ct()
+    getattr(lib(libpath), "oracle_larfg_" + _sfx(x.dtype))(
+        x.shape[0], alpha, x.ctypes.data, _ct.byref(beta), _ct.byref(tau))
+    return beta.value, tau.value, x
+
+
+def _dense(A: _np.ndarray):
+    A = _np.ascontiguousarray(A)
+    if A.ndim != 3 or A.shape[1] != A.shape[2]:
+        raise ValueError("A must be (batch, n, n), got %s" % (A.shape,))
+    return A, A.shape[0], A.shape[1]
+
+
+def sytrd(A: _np.ndarray, want_q: bool = True, libpath=None):
+    """Householder reduction of each A (lower triangle read) to tridiagonal
+    form: returns (d (batch, n), e (batch, n-1), Q (batch, n, n) or None)
+    with A = Q T Q^T."""
+    A, batch, n = _dense(A)
+    d = _np.empty((batch, n), dtype=A.dtype)
+    e = _np.empty((batch, max(n - 1, 0)), dtype=A.dtype)
+    Q = _np.empty_like(A) if want_q else None
+    if batch and n:
+        rc = getattr(lib(libpath), "oracle_sytrd_batched_" + _sfx(A.dtype))(
+            A.ctypes.data, d.ctypes.data, e.ctypes.data, _ptr(Q), n, batch)
+        if rc != 0:
+            raise ValueError("oracle rejected n=%d" % n)
+    return d, e, Q
+
+
+def syev(A: _np.ndarray, jobz: bool = True, max_sweeps_per_n: int = 30, sort: bool = True,
+         threads: int = 1, libpath: Optional[str] = None, scheme: int = 0, shift: int = 0
+         ) -> Tuple[_np.ndarray, Optional[_np.ndarray], _np.ndarray]:
+    """Dense symmetric eigensolver: (lam (batch, n) ascending, Q (batch, n, n)
+    or None, info (batch,) int32) for each A (lower triangle read)."""
+    A, batch, n = _dense(A)
+    lam = _np.empty((batch, n), dtype=A.dtype)
+    Q = _np.empty_like(A) if jobz else None
+    info = _np.zeros(batch, dtype=_np.int32)
+    if batch == 0 or n == 0:
+        return lam, Q, info
+    fn = getattr(lib(libpath), "oracle_syev_batched_" + _sfx(A.dtype))
+    it = A.itemsize
+
+    def run(lo: int, hi: int) -> int:
+        return fn(A.ctypes.data + lo * n * n * it, lam.ctypes.data + lo * n * it,
+                  None if Q is None else Q.ctypes.data + lo * n * n * it,
+                  info.ctypes.data + lo * 4, n, hi - lo, int(max_sweeps_per_n),
+                  int(bool(sort)), int(scheme), int(shift))
+
+    threads = max(1, min(int(threads), batch))
+    cuts = [batch * k // threads for k in range(threads + 1)]
+    if threads == 1:
+        rcs = [run(0, batch)]
+    else:
+        with _cf.ThreadPoolExecutor(threads) as ex:
+            rcs = list(ex.map(lambda k: run(cuts[k], cuts[k + 1]), range(threads)))
+    if any(rcs):
+        raise ValueError("oracle rejected n=%d" % n)
+    return lam, Q, info

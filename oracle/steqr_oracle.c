@@ -5,8 +5,9 @@
  * CPU-baseline leg load this library; the GPU library never does. Build:
  *   gcc -O2 -ffp-contract=off -fno-fast-math -fPIC -shared \
  *       -o liboracle_steqr.so steqr_oracle.c -lm
- * The algorithm body lives in steqr_oracle_impl.h and is instantiated here
- * for float (REAL = float, every operation in IEEE single precision) and
+ * The algorithm body lives in steqr_oracle_impl.h (the tridiagonal solve)
+ * and syev_oracle_impl.h (the dense front end) and is instantiated here for
+ * float (REAL = float, every operation in IEEE single precision) and
  * double.
  */
 #include <float.h>
@@ -26,6 +27,7 @@
 #define R_HYPOT hypotf
 #define R_COPYSIGN copysignf
 #include "steqr_oracle_impl.h"
+#include "syev_oracle_impl.h"
 #undef REAL
 #undef SFX
 #undef R_EPS
@@ -44,6 +46,7 @@
 #define R_HYPOT hypot
 #define R_COPYSIGN copysign
 #include "steqr_oracle_impl.h"
+#include "syev_oracle_impl.h"
 
 /* Constants as the oracle computes them, for the pins. */
 void oracle_constants_f32(float *out5)

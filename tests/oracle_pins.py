@@ -26,7 +26,19 @@ What each pin checks, and why it is independent of the oracle's own code:
              orthogonal Z the columns are eigenvectors of the dense
              A = Z T Z^T (numpy matmul in float64); for a general Z the
              result matches the matmul Z Q; a solve that performs no
-             rotation returns Z unchanged.
+             rotation returns Z unchanged;
+  larfg      the reflector's defining relations H x = (beta, 0..0), H
+             orthogonal, |beta| = ||x||, sign(beta) = -sign(alpha), in long
+             double, and the stated special case x_1..m = 0 -> H = I;
+  sytrd      A = Q T Q^T and Q^T Q = I by numpy matmul in float64, the
+             spectrum of T (long-double Sturm bisection) against numpy's
+             eigvalsh of A, d_0 = a_00 and |e_0| = ||a_{1:,0}|| exactly as
+             the first step fixes them, a tridiagonal A returned unchanged
+             with Q = I, and the strict upper triangle never read;
+  syev       eigenvalues against numpy's eigvalsh, the dense residual and
+             orthogonality bounds, a tridiagonal A giving the tridiagonal
+             solve bit for bit, and a diagonal A its sorted diagonal with a
+             permutation for Q.
 """
 from __future__ import annotations
 
@@ -324,7 +336,127 @@ def pin_back_transform(oracle, libpath: Optional[str] = None, quick: bool = Fals
     return out
 
 
-ALL_PINS = (pin_lartg, pin_shift, pin_sym2x2, pin_sweep, pin_solve, pin_back_transform)
+def pin_larfg(oracle, libpath: Optional[str] = None) -> List[str]:
+    out: List[str] = []
+    g = np.random.default_rng(31)
+    for dt in (np.float32, np.float64):
+        eps = V.eps_of(dt)
+        for m in (1, 2, 5, 15):
+            for trial in range(6):
+                x = g.standard_normal(m + 1).astype(dt)
+                if trial == 1:
+                    x[0] = -abs(x[0])
+                if trial == 2:
+                    x *= dt(1e15) if dt == np.float32 else 1e150   # no overflow
+                if trial == 3:
+                    x[0] = 0
+                beta, tau, v = oracle.larfg(x[0], x[1:], libpath=libpath)
+                X = x.astype(np.longdouble)
+                u = np.concatenate([[1], v.astype(np.longdouble)])
+                Hx = X - np.longdouble(tau) * u * (u @ X)
+                xn = np.sqrt((X ** 2).sum())
+                _fail(out, np.abs(Hx[1:]).max() <= 8 * m * eps * xn and
+                      abs(Hx[0] - np.longdouble(beta)) <= 8 * m * eps * xn,
+                      "larfg H x != (beta, 0) (%s m=%d trial %d)" % (dt.__name__, m, trial))
+                _fail(out, abs(abs(np.longdouble(beta)) - xn) <= 4 * eps * xn,
+                      "larfg |beta| != ||x|| (%s m=%d)" % (dt.__name__, m))
+                # H orthogonal <=> tau^2 ||u||^2 = 2 tau
+                t = np.longdouble(tau)
+                _fail(out, abs(t * t * (u @ u) - 2 * t) <= 16 * m * eps,
+                      "larfg H not orthogonal (%s m=%d)" % (dt.__name__, m))
+                _fail(out, (beta < 0) == (x[0] >= 0) or np.abs(x[1:]).max() == 0,
+                      "larfg sign of beta (%s m=%d)" % (dt.__name__, m))
+        for alpha in (2.5, -2.5, 0.0):
+            beta, tau, v = oracle.larfg(alpha, np.zeros(3, dtype=dt), libpath=libpath)
+            _fail(out, tau == 0 and beta == alpha and np.all(v == 0),
+                  "larfg x = 0 is not H = I (%s)" % dt.__name__)
+    return out
+
+
+def _sym_from_lower(A) -> np.ndarray:
+    L = np.tril(np.asarray(A, dtype=np.float64))
+    return L + np.swapaxes(np.tril(L, -1), 1, 2)
+
+
+def pin_sytrd(oracle, libpath: Optional[str] = None) -> List[str]:
+    out: List[str] = []
+    for dt in (np.float32, np.float64):
+        for n in (1, 2, 3, 4, 7, 16, 32):
+            A = W.random_symmetric(n, 10, dt, salt=51)
+            d, e, Q = oracle.sytrd(A, libpath=libpath)
+            tol = V.tol_of(dt, n)
+            As = _sym_from_lower(A)
+            an = np.abs(As).sum(1).max(1)
+            T = W.dense_from_bands(d.astype(np.float64), e.astype(np.float64))
+            Q64 = Q.astype(np.float64)
+            rec = np.abs(Q64 @ T @ np.swapaxes(Q64, 1, 2) - As).sum(1).max(1)
+            _fail(out, np.all(rec <= tol * an), "sytrd A != Q T Q^T (%s n=%d): %g"
+                  % (dt.__name__, n, (rec / an).max()))
+            _fail(out, V.orthogonality(Q).max() <= tol, "sytrd Q not orthogonal (%s n=%d)"
+                  % (dt.__name__, n))
+            ref = np.linalg.eigvalsh(As)
+            lam = V.sturm_eigvals(d, e).astype(np.float64)
+            _fail(out, np.all(np.abs(lam - ref).max(1) <= tol * an),
+                  "sytrd spectrum of T != eigvalsh(A) (%s n=%d)" % (dt.__name__, n))
+            _fail(out, np.array_equal(d[:, 0], A[:, 0, 0]), "sytrd d_0 != a_00")
+            if n > 1:
+                cn = np.sqrt((As[:, 1:, 0] ** 2).sum(1))
+                _fail(out, np.all(np.abs(np.abs(e[:, 0]) - cn) <= 4 * n * V.eps_of(dt) * cn),
+                      "sytrd |e_0| != ||a_{1:,0}|| (%s n=%d)" % (dt.__name__, n))
+            # the strict upper triangle is never read
+            P = A.copy()
+            iu = np.triu_indices(n, 1)
+            P[:, iu[0], iu[1]] = dt(7.5)
+            d2, e2, Q2 = oracle.sytrd(P, libpath=libpath)
+            _fail(out, np.array_equal(d2, d) and np.array_equal(e2, e) and
+                  np.array_equal(Q2, Q), "sytrd read the upper triangle (%s n=%d)"
+                  % (dt.__name__, n))
+            # a tridiagonal matrix is already reduced: T = A, Q = I exactly
+            td, te = W.random_batch(n, 4, dt, salt=52)
+            Tm = W.dense_from_bands(td, te)
+            d3, e3, Q3 = oracle.sytrd(Tm, libpath=libpath)
+            _fail(out, np.array_equal(d3, td) and np.array_equal(e3, te) and
+                  np.array_equal(Q3, np.broadcast_to(np.eye(n, dtype=dt), Q3.shape)),
+                  "sytrd changed a tridiagonal matrix (%s n=%d)" % (dt.__name__, n))
+    return out
+
+
+def pin_syev(oracle, libpath: Optional[str] = None, quick: bool = False) -> List[str]:
+    out: List[str] = []
+    for dt in (np.float32, np.float64):
+        for n in ((3, 16) if quick else (1, 2, 3, 5, 8, 13, 16, 32)):
+            A = W.random_symmetric(n, 16, dt, salt=53)
+            lam, Q, info = oracle.syev(A, libpath=libpath)
+            tol = V.tol_of(dt, n)
+            As = _sym_from_lower(A)
+            an = np.abs(As).sum(1).max(1)
+            _fail(out, not info.any(), "syev info != 0 (%s n=%d)" % (dt.__name__, n))
+            ref = np.linalg.eigvalsh(As)
+            _fail(out, np.all(np.abs(lam.astype(np.float64) - ref).max(1) <= tol * an),
+                  "syev eigenvalues vs eigvalsh (%s n=%d)" % (dt.__name__, n))
+            _fail(out, V.dense_residual(As, lam, Q).max() <= tol,
+                  "syev residual (%s n=%d)" % (dt.__name__, n))
+            _fail(out, V.orthogonality(Q).max() <= tol, "syev orthogonality (%s n=%d)"
+                  % (dt.__name__, n))
+            td, te = W.random_batch(n, 6, dt, salt=54)
+            l1, Q1, i1 = oracle.syev(W.dense_from_bands(td, te), libpath=libpath)
+            l2, Q2, i2, _ = oracle.steqr(td, te, True, libpath=libpath)
+            _fail(out, np.array_equal(l1, l2) and np.array_equal(Q1, Q2) and
+                  np.array_equal(i1, i2), "syev of a tridiagonal A != steqr (%s n=%d)"
+                  % (dt.__name__, n))
+            dg = W.random_batch(n, 3, dt, salt=55)[0]
+            Dm = np.zeros((3, n, n), dtype=dt)
+            Dm[:, np.arange(n), np.arange(n)] = dg
+            l3, Q3, _ = oracle.syev(Dm, libpath=libpath)
+            _fail(out, np.array_equal(l3, np.sort(dg, axis=1)) and
+                  np.all(np.abs(Q3).sum(1) == 1) and np.all(np.abs(Q3).sum(2) == 1) and
+                  np.all(np.isin(Q3, (0, 1))), "syev of a diagonal A (%s n=%d)"
+                  % (dt.__name__, n))
+    return out
+
+
+ALL_PINS = (pin_lartg, pin_shift, pin_sym2x2, pin_sweep, pin_solve, pin_back_transform,
+            pin_larfg, pin_sytrd, pin_syev)
 
 
 def run_all(oracle, libpath: Optional[str] = None, quick: bool = True) -> List[str]:

@@ -59,17 +59,37 @@ MUTANTS = [
      "REAL r = R_HYPOT((a - c), b);"),
     # back-transformation: the basis on entry ignored (Q reset to I)
     ("basis_ignored", "if (Q && !back_transform) {", "if (Q) {"),
+    # the dense front end (Householder reduction)
+    ("larfg_beta_sign", "REAL b = -R_COPYSIGN(R_HYPOT(alpha, xnorm), alpha);",
+     "REAL b = R_COPYSIGN(R_HYPOT(alpha, xnorm), alpha);"),
+    ("larfg_tau_inverted", "*tau = (b - alpha) / b;", "*tau = (b - alpha) / alpha;"),
+    ("larfg_v_scale", "REAL scal = (REAL)1 / (alpha - b);", "REAL scal = (REAL)1 / (alpha + b);"),
+    ("sytrd_no_w_correction", "p[i] = p[i] - half * v[i]; /* p now holds w */",
+     "p[i] = p[i]; /* p now holds w */"),
+    ("sytrd_rank1_only", "W[i * n + j] = W[i * n + j] - v[i] * p[j] - p[i] * v[j];",
+     "W[i * n + j] = W[i * n + j] - v[i] * p[j];"),
+    ("sytrd_q_left_applied", "t = t + Q[r * n + j] * v[j];", "t = t + Q[j * n + r] * v[j];"),
+    ("sytrd_reads_upper", "W[i * n + j] = A[i * n + j];\n            W[j * n + i] = A[i * n + j];",
+     "W[i * n + j] = A[j * n + i];\n            W[j * n + i] = A[j * n + i];"),
+    ("sytrd_e_is_alpha", "e[k] = beta;", "e[k] = W[(k + 1) * n + k];"),
+    ("syev_no_back_transform", "scheme, shift, 1, 0);", "scheme, shift, 0, 0);"),
 ]
 
 
 def _build_mutant(tmp, old, new):
     src = os.path.join(tmp, "src")
     os.makedirs(src)
-    for f in ("steqr_oracle.c", "steqr_oracle_impl.h"):
+    for f in ("steqr_oracle.c", "steqr_oracle_impl.h", "syev_oracle_impl.h"):
         shutil.copy(os.path.join(oracle.HERE, f), src)
-    impl = os.path.join(src, "steqr_oracle_impl.h")
-    text = open(impl).read()
-    assert text.count(old) == 1, "mutation anchor not unique/absent: %r" % old
+    hits = []
+    for f in ("steqr_oracle_impl.h", "syev_oracle_impl.h"):
+        impl = os.path.join(src, f)
+        text = open(impl).read()
+        if old in text:
+            hits.append((impl, text))
+    assert len(hits) == 1 and hits[0][1].count(old) == 1, \
+        "mutation anchor not unique/absent: %r" % old
+    impl, text = hits[0]
     open(impl, "w").write(text.replace(old, new))
     return oracle.build(out_dir=src, source_dir=src)
 

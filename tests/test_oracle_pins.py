@@ -59,6 +59,12 @@ def test_back_transform_pins(oracle_mod, scheme, shift):
     assert P.pin_back_transform(oracle_mod, quick=False, scheme=scheme, shift=shift) == []
 
 
+@pytest.mark.parametrize("pin", [P.pin_larfg, P.pin_sytrd, P.pin_syev],
+                         ids=lambda p: p.__name__)
+def test_dense_front_end_pins(oracle_mod, pin):
+    assert pin(oracle_mod) == []
+
+
 @pytest.mark.parametrize("wname", ["c2_f32_n16", "c4_f64_n32", "c5_f64_n64"])
 def test_closed_and_lapack_shift_agree(oracle_mod, wname):
     """The two forms of the shift give the same eigenvalue of the trailing

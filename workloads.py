@@ -172,6 +172,16 @@ def random_basis(n: int, batch: int, dtype=np.float64, salt: int = 0,
     return np.ascontiguousarray(a.astype(dtype))
 
 
+def random_symmetric(n: int, batch: int, dtype=np.float64, salt: int = 0,
+                     cfg: int = 8) -> np.ndarray:
+    """Seeded dense symmetric (batch, n, n) row-major matrices: the lower
+    triangle (diagonal included) iid N(0,1), mirrored into the upper one."""
+    g = rng_for(cfg, n, salt)
+    a = np.tril(g.standard_normal((batch, n, n)))
+    a = a + np.swapaxes(np.tril(a, -1), 1, 2)
+    return np.ascontiguousarray(a.astype(dtype))
+
+
 def edge_batch(kind: int, n: int, batch: int, dtype=np.float64,
                salt: int = 0) -> Tuple[np.ndarray, np.ndarray]:
     """A batch made only of edge items of one kind (for the edge-case tests).
