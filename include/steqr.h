@@ -135,6 +135,46 @@ int steqr_query(int n, int batch, int jobz, int dtype, const steqr_params *param
                 int *padded_n, int *lanes_per_problem, int *rows_per_lane,
                 int *waves_per_block, int *workgroups, int *band_storage);
 
+/* ------------------------------------------------------------------------
+ * Fused small-n dense symmetric eigensolver (BatchLAS syev routing and
+ * tuning page, CTA-family paragraph: one problem resident from the load of
+ * A to the store, reduction to tridiagonal form, the steqr solve above and
+ * the back-transformation in one kernel; steqr algorithm page, eigenvector
+ * paragraph, for the back-transformation). For each symmetric A_b it
+ * computes the eigenvalues and, on request, orthonormal eigenvectors:
+ * A_b = Q Lambda Q^T. The reduction is the Householder tridiagonalization
+ * A = Z T Z^T (reflectors in the LAPACK larfg convention); T is then
+ * solved exactly as by steqr_batched_ex with Z as the basis of the
+ * back-transformation.
+ *
+ * Layout: A [batch][n][n] row-major, read only; only the lower triangle
+ * (A[b][i][j], j <= i) is read, the strict upper triangle is ignored.
+ * lambda [batch][n] ascending; Q [batch][n][n] row-major, eigenvector k in
+ * column k (as for steqr_batched). Ownership, asynchrony and the meaning
+ * of info as for steqr_batched_ex.
+ *
+ * Errors (0 on success; -k names the k-th argument):
+ *   -1 A == NULL          -2 lambda == NULL      -3 Q == NULL with STEQR_V
+ *   -4 n < 0 or n > SYEV_MAX_N                   -5 batch < 0
+ *   -6 jobz invalid       -7 dtype invalid
+ *   -10 (_ex) params: update_scheme other than STEQR_EXP, back_transform
+ *       set, band_storage other than 0/1, or a lanes_per_problem /
+ *       waves_per_block the build does not provide (syev_query lists them)
+ * A positive value is a hipError_t from the launch; n == 0 or batch == 0
+ * returns 0 without touching the GPU. */
+#define SYEV_MAX_N 32
+
+int syev_batched(const void *A, void *lambda, void *Q, int n, int batch, int jobz, int dtype,
+                 hipStream_t stream);
+
+int syev_batched_ex(const void *A, void *lambda, void *Q, int n, int batch, int jobz,
+                    int dtype, hipStream_t stream, int *info, const steqr_params *params);
+
+/* The launch syev_batched_ex would make (outputs as for steqr_query). */
+int syev_query(int n, int batch, int jobz, int dtype, const steqr_params *params,
+               int *padded_n, int *lanes_per_problem, int *rows_per_lane,
+               int *waves_per_block, int *workgroups);
+
 /* Library version string, e.g. "steqr-mi355x 0.1.0 gfx950". */
 const char *steqr_version(void);
 

@@ -18,6 +18,7 @@ STEQR_F32, STEQR_F64 = 0, 1
 STEQR_EXP, STEQR_PG = 0, 1
 STEQR_SHIFT_LAPACK, STEQR_SHIFT_CLOSED = 0, 1
 STEQR_MAX_N = 64
+SYEV_MAX_N = 32
 
 
 class steqr_params(ct.Structure):
@@ -53,8 +54,16 @@ _lib.steqr_query.restype = _i
 _lib.steqr_query.argtypes = [_i, _i, _i, _i, ct.POINTER(steqr_params)] + [ct.POINTER(_i)] * 6
 _lib.steqr_version.restype = ct.c_char_p
 _lib.steqr_version.argtypes = []
+_lib.syev_batched.restype = _i
+_lib.syev_batched.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _vp]
+_lib.syev_batched_ex.restype = _i
+_lib.syev_batched_ex.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp,
+                                 ct.POINTER(steqr_params)]
+_lib.syev_query.restype = _i
+_lib.syev_query.argtypes = [_i, _i, _i, _i, ct.POINTER(steqr_params)] + [ct.POINTER(_i)] * 5
 
-EXPORTS = ("steqr_batched", "steqr_batched_ex", "steqr_query", "steqr_version")
+EXPORTS = ("steqr_batched", "steqr_batched_ex", "steqr_query", "steqr_version",
+           "syev_batched", "syev_batched_ex", "syev_query")
 
 
 def lib() -> ct.CDLL:
@@ -165,4 +174,52 @@ def solve(d, e, jobz: bool = True, *, info: bool = False, sort: bool = True,
                           dtype_code(d.dtype), stream, inf, prm)
     if rc != 0:
         raise SteqrError(rc, "steqr_batched_ex")
+    return (lam, Q, inf) if info else (lam, Q)
+
+
+def syev_batched(A, lam, Q, n: int, batch: int, jobz: int, dtype: int, stream=None) -> int:
+    """Thin call of the C entry point; returns its status code."""
+    return _lib.syev_batched(_ptr(A), _ptr(lam), _ptr(Q), int(n), int(batch), int(jobz),
+                             int(dtype), _stream_handle(stream))
+
+
+def syev_batched_ex(A, lam, Q, n: int, batch: int, jobz: int, dtype: int, stream=None,
+                    info=None, params: Optional[steqr_params] = None) -> int:
+    return _lib.syev_batched_ex(_ptr(A), _ptr(lam), _ptr(Q), int(n), int(batch), int(jobz),
+                                int(dtype), _stream_handle(stream), _ptr(info),
+                                ct.byref(params) if params is not None else None)
+
+
+def syev_query(n: int, batch: int, jobz: int, dtype: int,
+               params: Optional[steqr_params] = None) -> dict:
+    outs = [ct.c_int(0) for _ in range(5)]
+    rc = _lib.syev_query(int(n), int(batch), int(jobz), int(dtype),
+                         ct.byref(params) if params is not None else None,
+                         *[ct.byref(o) for o in outs])
+    if rc != 0:
+        raise SteqrError(rc, "syev_query")
+    keys = ("padded_n", "lanes_per_problem", "rows_per_lane", "waves_per_block", "workgroups")
+    return dict(zip(keys, (o.value for o in outs)))
+
+
+def syev(A, jobz: bool = True, *, info: bool = False, sort: bool = True,
+         max_sweeps_per_n: int = 0, lanes_per_problem: int = 0, waves_per_block: int = 0,
+         shift: int = 0, stream=None):
+    """Eigen-decomposition of a batch of dense symmetric matrices A (batch, n, n)
+    held in a device tensor (lower triangle read). Returns (lam, Q or None[, info])
+    as device tensors; the work is enqueued on `stream` and not synchronised."""
+    import torch
+    if A.dim() != 3 or A.shape[1] != A.shape[2]:
+        raise ValueError("A must be (batch, n, n)")
+    if not (A.is_cuda and A.is_contiguous()):
+        raise ValueError("A must be a contiguous device tensor")
+    batch, n = A.shape[0], A.shape[1]
+    lam = torch.empty((batch, n), dtype=A.dtype, device=A.device)
+    Q = torch.empty_like(A) if jobz else None
+    inf = torch.empty((batch,), dtype=torch.int32, device=A.device) if info else None
+    prm = make_params(max_sweeps_per_n, sort, lanes_per_problem, waves_per_block, 0, 0, shift)
+    rc = syev_batched_ex(A, lam, Q, n, batch, STEQR_V if jobz else STEQR_N, dtype_code(A.dtype),
+                         stream, inf, prm)
+    if rc != 0:
+        raise SteqrError(rc, "syev_batched_ex")
     return (lam, Q, inf) if info else (lam, Q)

@@ -179,7 +179,7 @@ extern "C" int steqr_batched_ex(const void* d, const void* e, void* lambda, void
     if (n > 1 && e == nullptr) return -2;
     if (lambda == nullptr) return -3;
     if (jobz == STEQR_V && Q == nullptr) return -4;
-    steqr::KernelArgs a;
+    steqr::KernelArgs a{};
     a.d = d;
     a.e = e;
     a.lam = lambda;
@@ -199,6 +199,111 @@ extern "C" int steqr_batched_ex(const void* d, const void* e, void* lambda, void
 extern "C" int steqr_batched(const void* d, const void* e, void* lambda, void* Q, int n,
                              int batch, int jobz, int dtype, hipStream_t stream) {
     return steqr_batched_ex(d, e, lambda, Q, n, batch, jobz, dtype, stream, nullptr, nullptr);
+}
+
+// ---------------------------------------------------------------- syev
+
+namespace {
+
+// Default lanes per problem of the fused dense kernel: the lanes hold whole
+// rows of A and Q (N/P rows each), so P is chosen to keep A, Q and the
+// replicated band within the register file at two wavefronts per SIMD.
+int syev_default_lanes(int dtype, int N) {
+    if (N == 4) return 4;
+    if (N == 8) return dtype == STEQR_F32 ? 2 : 4;
+    if (N == 16) return dtype == STEQR_F32 ? 4 : 8;
+    return 16;
+}
+
+int syev_plan(int n, int batch, int jobz, int dtype, const steqr_params* prm, Plan* out) {
+    if (n < 0 || n > SYEV_MAX_N) return -4;
+    if (batch < 0) return -5;
+    if (jobz != STEQR_N && jobz != STEQR_V) return -6;
+    if (dtype != STEQR_F32 && dtype != STEQR_F64) return -7;
+    int waves = 4, P = 0;
+    if (prm) {
+        if (prm->update_scheme != STEQR_EXP) return -10;
+        if (prm->shift != STEQR_SHIFT_LAPACK && prm->shift != STEQR_SHIFT_CLOSED) return -10;
+        if (prm->back_transform != 0) return -10;
+        if (prm->band_storage != 0 && prm->band_storage != 1) return -10;
+        if (prm->no_sort != 0 && prm->no_sort != 1) return -10;
+        if (prm->waves_per_block != 0) {
+            if (prm->waves_per_block != 1 && prm->waves_per_block != 2 && prm->waves_per_block != 4)
+                return -10;
+            waves = prm->waves_per_block;
+        }
+        P = prm->lanes_per_problem;
+        if (P < 0 || P > 64 || (P != 0 && (64 % P) != 0)) return -10;
+    }
+    Plan p{};
+    p.waves = waves;
+    if (n == 0) {
+        *out = p;
+        return 0;
+    }
+    const int N = padded_order(n < 2 ? 2 : n);
+    if (P == 0) P = syev_default_lanes(dtype, N);
+    const Table t = dtype == STEQR_F32 ? steqr::table_syev_f32() : steqr::table_syev_f64();
+    const Entry* ent = search(t, dtype, N, P, jobz, 1);
+    if (!ent) return -10;
+    while (waves > 1 && (long)waves * ent->lds_per_wave > 65536) waves /= 2;
+    p.waves = waves;
+    p.entry = ent;
+    p.N = N;
+    p.P = P;
+    p.R = N / P;
+    p.band = 1;
+    const int per_block = waves * (64 / P);
+    p.grid = batch > 0 ? (int)(((long)batch + per_block - 1) / per_block) : 0;
+    *out = p;
+    return 0;
+}
+
+}  // namespace
+
+extern "C" int syev_query(int n, int batch, int jobz, int dtype, const steqr_params* params,
+                          int* padded_n, int* lanes_per_problem, int* rows_per_lane,
+                          int* waves_per_block, int* workgroups) {
+    Plan p;
+    const int rc = syev_plan(n, batch, jobz, dtype, params, &p);
+    if (rc != 0) return rc;
+    if (padded_n) *padded_n = p.N;
+    if (lanes_per_problem) *lanes_per_problem = p.P;
+    if (rows_per_lane) *rows_per_lane = p.R;
+    if (waves_per_block) *waves_per_block = p.waves;
+    if (workgroups) *workgroups = p.grid;
+    return 0;
+}
+
+extern "C" int syev_batched_ex(const void* A, void* lambda, void* Q, int n, int batch, int jobz,
+                               int dtype, hipStream_t stream, int* info,
+                               const steqr_params* params) {
+    Plan p;
+    const int rc = syev_plan(n, batch, jobz, dtype, params, &p);
+    if (rc != 0) return rc;
+    if (n == 0 || batch == 0) return 0;
+    if (A == nullptr) return -1;
+    if (lambda == nullptr) return -2;
+    if (jobz == STEQR_V && Q == nullptr) return -3;
+    steqr::KernelArgs a{};
+    a.a = A;
+    a.lam = lambda;
+    a.q = Q;
+    a.info = info;
+    a.n = n;
+    a.batch = batch;
+    const int ms = params ? params->max_sweeps_per_n : 0;
+    a.max_sweeps_per_n = ms == 0 ? 30 : (ms < 0 ? 0 : ms);
+    a.do_sort = params ? !params->no_sort : 1;
+    a.shift_kind = params ? params->shift : 0;
+    a.back_transform = 0;
+    const hipError_t err = p.entry->fn(a, p.grid, p.waves * 64, stream);
+    return err == hipSuccess ? 0 : (int)err;
+}
+
+extern "C" int syev_batched(const void* A, void* lambda, void* Q, int n, int batch, int jobz,
+                            int dtype, hipStream_t stream) {
+    return syev_batched_ex(A, lambda, Q, n, batch, jobz, dtype, stream, nullptr, nullptr);
 }
 
 extern "C" const char* steqr_version(void) { return "steqr-mi355x 0.1.0 gfx950"; }

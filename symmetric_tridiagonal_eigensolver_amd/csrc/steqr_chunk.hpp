@@ -48,6 +48,7 @@
 #pragma once
 
 #include "steqr_device.hpp"
+#include "syev_reduce.hpp"
 
 namespace steqr {
 
@@ -63,6 +64,7 @@ struct KernelArgs {
     int do_sort;
     int shift_kind;  // 0 = LAPACK-form shift, 1 = closed form lambda+-
     int back_transform;  // 1: q holds a basis on entry, right-multiplied
+    const void* a;       // dense kernels: A [batch][n][n], lower triangle read
 };
 
 // Reverse the whole order-N problem in place (positions p <-> N-1-p for d
@@ -127,8 +129,8 @@ __device__ __forceinline__ void copy_block(T* __restrict__ dst, const T* __restr
 // number of elements against bank conflicts), for P > 1 one rank row per
 // chunk for the final sort, and with eigenvectors a staging area holding the
 // wavefront's Q blocks in their HBM layout, so that the store is one
-// contiguous, fully coalesced copy.
-template <typename T, int N, int P, bool WANTQ = false>
+// contiguous, fully coalesced copy (the dense kernels also stage A there).
+template <typename T, int N, int P, bool WANTQ = false, bool DENSE = false>
 struct Smem {
     static constexpr int CH = 64 / P;
     static constexpr int SLOT = 2 * N + 1;
@@ -136,20 +138,25 @@ struct Smem {
     static constexpr int rank_ints = (P > 1) ? CH * N : 0;
     static constexpr size_t band_bytes = ((band_elems * sizeof(T) + 15) / 16) * 16;
     static constexpr size_t rank_bytes = (((size_t)rank_ints * sizeof(int) + 15) / 16) * 16;
-    static constexpr size_t stage_bytes = WANTQ ? (size_t)CH * N * N * sizeof(T) : 0;
+    static constexpr size_t stage_bytes = (WANTQ || DENSE) ? (size_t)CH * N * N * sizeof(T) : 0;
     static constexpr size_t bytes_per_wave = band_bytes + rank_bytes + stage_bytes;
 };
 
-template <typename T, int N, int P, bool WANTQ, bool PG>
+// DENSE: the fused dense eigensolver. The chunk loads a dense symmetric
+// matrix (args.a), reduces it to tridiagonal form with Q accumulated in the
+// registers that otherwise start as the identity, and continues with the
+// tridiagonal solve below, which then back-transforms that Q.
+template <typename T, int N, int P, bool WANTQ, bool PG, bool DENSE = false>
 __global__ void __launch_bounds__(256) steqr_chunk_kernel(KernelArgs args) {
     static_assert(P >= 1 && P <= 64 && (64 % P) == 0, "P must divide 64");
+    static_assert(!DENSE || (N % P) == 0, "dense: the lanes hold whole rows");
     constexpr int CH = 64 / P;                       // problems per wavefront
     constexpr int R = WANTQ ? (N + P - 1) / P : 0;   // rows of Q per lane
     constexpr int RQ = R > 0 ? R : 1;
     constexpr int RJ = (N + P - 1) / P;              // sort keys ranked per lane
     using M = PosMask<N>;
     using F = Fp<T>;
-    using S = Smem<T, N, P, WANTQ>;
+    using S = Smem<T, N, P, WANTQ, DENSE>;
     enum { ST_OPEN = 0, ST_ITER = 1, ST_DONE = 2 };
 
     extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -176,38 +183,36 @@ __global__ void __launch_bounds__(256) steqr_chunk_kernel(KernelArgs args) {
 
     // ---------------------------------------------------------------- load
     T d[N], e[N];
-    static_for<N>([&](auto I) {
-        constexpr int p = decltype(I)::value;
-        const int pc = p < n ? p : n - 1;
-        const T v = gd[pb * n + pc];
-        d[p] = (live & (p < n)) ? v : T(0);
-        e[p] = T(0);
-    });
-    if (n > 1) {
-        static_for<N - 1>([&](auto I) {
-            constexpr int p = decltype(I)::value;
-            const int pc = p < n - 1 ? p : n - 2;
-            const T v = ge[pb * (n - 1) + pc];
-            e[p] = (live & (p < n - 1)) ? v : T(0);
-        });
-    }
     // The wavefront's problems are consecutive, and so are their Q blocks
-    // in HBM: [first, first + nprob) holds the live ones.
+    // (and dense matrices) in HBM: [first, first + nprob) holds the live ones.
     const long first = ((long)blockIdx.x * (blockDim.x >> 6) + wave) * CH;
     const int nprob = (long)args.batch - first < CH ? (int)((long)args.batch - first) : CH;
     const int nn = n * n;
     const bool qvec = ((nn & 3) == 0) & ((reinterpret_cast<uintptr_t>(gq) & 15) == 0);
     T q[RQ][N];
-    if (WANTQ && args.back_transform) {
-        // back-transformation [algo, eigenvector accumulation]: the lane's
-        // rows of the caller's basis, loaded straight into registers (the
-        // loads overlap the first settle)
-        const bool vec = (n == N) & ((reinterpret_cast<uintptr_t>(gq) & 15) == 0);
-        static_for<RQ>([&](auto II) {
+    if constexpr (DENSE) {
+        // one coalesced copy of the wavefront's matrices into the staging
+        // area, then each lane takes its rows, the strict upper triangle
+        // mirrored from the lower one
+        constexpr int RA = N / P;
+        const T* __restrict__ ga = static_cast<const T*>(args.a);
+        const bool avec = ((nn & 3) == 0) & ((reinterpret_cast<uintptr_t>(ga) & 15) == 0);
+        copy_block<T, CH * N * N>(stage, ga + first * nn, nprob * nn, lane, avec);
+        __builtin_amdgcn_wave_barrier();
+        const T* const st = stage + chunk * nn;
+        T a[RA][N];
+        static_for<RA>([&](auto II) {
             constexpr int i = decltype(II)::value;
-            load_basis_row<T, N>(gq + pb * nn, n, r * R + i, live, true, vec, q[i]);
+            const int row = r * RA + i;
+            const bool in = live & (row < n);
+            static_for<N>([&](auto J) {
+                constexpr int j = decltype(J)::value;
+                const bool use = in & (j < n);
+                const int idx = use ? ((j <= row) ? row * n + j : j * n + row) : 0;
+                const T v = st[idx];
+                a[i][j] = use ? v : T(0);
+            });
         });
-    } else {
         static_for<RQ>([&](auto II) {
             constexpr int i = decltype(II)::value;
             const int row = r * R + i;
@@ -216,6 +221,42 @@ __global__ void __launch_bounds__(256) steqr_chunk_kernel(KernelArgs args) {
                 q[i][j] = (WANTQ & (row == j)) ? T(1) : T(0);
             });
         });
+        householder_chunk<T, N, P, RA, WANTQ, RQ>(a, q, d, e, sd, se, n, r);
+    } else {
+        static_for<N>([&](auto I) {
+            constexpr int p = decltype(I)::value;
+            const int pc = p < n ? p : n - 1;
+            const T v = gd[pb * n + pc];
+            d[p] = (live & (p < n)) ? v : T(0);
+            e[p] = T(0);
+        });
+        if (n > 1) {
+            static_for<N - 1>([&](auto I) {
+                constexpr int p = decltype(I)::value;
+                const int pc = p < n - 1 ? p : n - 2;
+                const T v = ge[pb * (n - 1) + pc];
+                e[p] = (live & (p < n - 1)) ? v : T(0);
+            });
+        }
+        if (WANTQ && args.back_transform) {
+            // back-transformation [algo, eigenvector accumulation]: the lane's
+            // rows of the caller's basis, loaded straight into registers (the
+            // loads overlap the first settle)
+            const bool vec = (n == N) & ((reinterpret_cast<uintptr_t>(gq) & 15) == 0);
+            static_for<RQ>([&](auto II) {
+                constexpr int i = decltype(II)::value;
+                load_basis_row<T, N>(gq + pb * nn, n, r * R + i, live, true, vec, q[i]);
+            });
+        } else {
+            static_for<RQ>([&](auto II) {
+                constexpr int i = decltype(II)::value;
+                const int row = r * R + i;
+                static_for<N>([&](auto J) {
+                    constexpr int j = decltype(J)::value;
+                    q[i][j] = (WANTQ & (row == j)) ? T(1) : T(0);
+                });
+            });
+        }
     }
     // bit p set <=> e_p == 0 (positions >= n-1 are zero padding)
     M zeromask = 0;

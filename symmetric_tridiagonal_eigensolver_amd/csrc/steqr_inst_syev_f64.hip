@@ -1,0 +1,15 @@
+// Kernel instantiations: fused dense eigensolver, float64.
+#include "steqr_registry.hpp"
+
+namespace steqr {
+
+#define E(N, P, Q) STEQR_SYEV_ENTRY(1, double, N, P, Q)
+static const Entry kEntries[] = {
+    E(4, 4, 1), E(8, 4, 1), E(16, 8, 1), E(16, 4, 1), E(32, 16, 1),
+    E(4, 4, 0), E(8, 4, 0), E(16, 8, 0), E(32, 16, 0),
+};
+#undef E
+
+Table table_syev_f64() { return {kEntries, (int)(sizeof(kEntries) / sizeof(kEntries[0]))}; }
+
+}  // namespace steqr

@@ -34,13 +34,19 @@ struct Entry {
     int pc_waves = 0;      // band 3: wavefronts per workgroup (consumers + producer)
 };
 
-template <typename T, int N, int P, bool WANTQ, bool PG>
+template <typename T, int N, int P, bool WANTQ, bool PG, bool DENSE = false>
 hipError_t launch_chunk(const KernelArgs& args, int grid, int block, hipStream_t stream) {
-    const size_t lds = (size_t)(block / 64) * Smem<T, N, P, WANTQ>::bytes_per_wave;
-    hipLaunchKernelGGL((steqr_chunk_kernel<T, N, P, WANTQ, PG>), dim3(grid), dim3(block), lds,
-                       stream, args);
+    const size_t lds = (size_t)(block / 64) * Smem<T, N, P, WANTQ, DENSE>::bytes_per_wave;
+    hipLaunchKernelGGL((steqr_chunk_kernel<T, N, P, WANTQ, PG, DENSE>), dim3(grid), dim3(block),
+                       lds, stream, args);
     return hipGetLastError();
 }
+
+// Fused dense eigensolver (reduction + solve + back-transformation), chunked
+// kernel with the band in registers, EXP form of the step.
+#define STEQR_SYEV_ENTRY(DT, T, N, P, Q) \
+    { DT, N, P, Q, 1, (int)Smem<T, N, P, (Q) != 0, true>::bytes_per_wave, \
+      &launch_chunk<T, N, P, (Q) != 0, false, true> }
 
 // One problem per wavefront (P = 64).
 template <typename T, int N, bool WANTQ, bool PG>
@@ -108,6 +114,8 @@ Table table_wave_pg();
 Table table_lds_f32_pg();
 Table table_lds_f64_pg();
 Table table_pc_pg();
+Table table_syev_f32();
+Table table_syev_f64();
 
 // table name for the scheme this unit is compiled for
 #if STEQR_INST_PG

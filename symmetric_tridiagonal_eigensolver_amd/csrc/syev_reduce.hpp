@@ -1,0 +1,169 @@
+// Dense front end of the fused small-n symmetric eigensolver: Householder
+// reduction of one dense symmetric matrix per chunk of P lanes to
+// tridiagonal form T = Q^T A Q, inside the chunked steqr kernel, so that
+// the problem stays resident from the load of A to the store of lambda
+// and Q (BatchLAS syev routing and tuning page, CTA-family paragraph: the
+// fused kernel runs the reduction, the tridiagonal solve and the
+// back-transformation with one read of A and one write).
+//
+// The pages give no arithmetic for the reduction; this is the textbook
+// Householder tridiagonalization (Golub and Van Loan) with the reflector
+// in the LAPACK larfg convention: for x = (alpha, x_2..x_m) below the
+// diagonal of column k, H = I - tau v v^T, v = (1, v_2..v_m), H x =
+// (beta, 0..0), beta = -sign(alpha) ||x||, tau = (beta - alpha)/beta,
+// v_j = x_j/(alpha - beta); x_2..x_m = 0 gives H = I. The two-sided update
+// of the trailing block is the symmetric rank-2 form p = tau A v,
+// w = p - (tau p^T v / 2) v, A <- A - v w^T - w v^T, and Q = H_0 H_1 ...
+// is accumulated from the identity by right-multiplication.
+//
+// Layout on chip (MI355X-first): lane r of a chunk holds full rows
+// r*RA .. r*RA+RA-1 of A (both triangles) and the same rows of Q in VGPRs.
+// Step k is fully unrolled (k, the column positions and the row slots are
+// compile-time), so every register array is statically indexed. Per step
+// the owner lane of row k publishes it to LDS (by symmetry it is column k),
+// every lane of the chunk forms the reflector redundantly from it (no
+// broadcast of v), each lane forms p for its own rows, a butterfly over the
+// chunk's lanes sums p^T v, and the lanes exchange w through LDS for the
+// rank-2 update. Rows at or beyond n are zero padding (their reflectors are
+// the identity, their d and e zero).
+#pragma once
+
+#include "steqr_device.hpp"
+
+namespace steqr {
+
+// Sum over the P lanes of a chunk (xor butterfly). Every lane receives the
+// same value bit for bit: each level adds the same two operands in every
+// lane of a pair, and floating-point addition is commutative.
+template <int P, typename T>
+__device__ __forceinline__ T chunk_sum(T v) {
+#pragma unroll
+    for (int o = 1; o < P; o <<= 1) v = v + __shfl_xor(v, o, 64);
+    return v;
+}
+
+// Reduce the chunk's matrix (a: the lane's RA rows, row = r*RA + i) to
+// tridiagonal form: d[0..N), e[0..N) receive T's bands (zero beyond n), and
+// with WANTQ q (the same rows of Q, the identity on entry) receives
+// H_0 H_1 ... H_{n-2}. sx and sw are two chunk-private LDS vectors of N
+// elements. a is destroyed.
+template <typename T, int N, int P, int RA, bool WANTQ, int RQ>
+__device__ __forceinline__ void householder_chunk(T (&a)[RA][N], T (&q)[RQ][N], T (&d)[N],
+                                                  T (&e)[N], T* sx, T* sw, int n, int r) {
+    using F = Fp<T>;
+    static_assert(RA * P == N, "the chunk's lanes hold exactly N rows");
+    static_for<N>([&](auto K) {
+        constexpr int k = decltype(K)::value;
+        // publish row k (= column k by symmetry) from its owner lane
+        if (r == k / RA) {
+            static_for<N - k>([&](auto J) {
+                constexpr int j = k + decltype(J)::value;
+                sx[j] = a[k % RA][j];
+            });
+        }
+        __builtin_amdgcn_wave_barrier();
+        d[k] = (k < n) ? sx[k] : T(0);
+        e[k] = T(0);
+        if constexpr (k + 1 < N) {
+            if (k + 1 < n) {  // uniform: n is the same for every problem
+                T x[N];
+                static_for<N - k - 1>([&](auto J) {
+                    constexpr int j = k + 1 + decltype(J)::value;
+                    x[j] = sx[j];
+                });
+                // reflector of (alpha, x_{k+2..}): scaled 2-norm, NaN-propagating
+                const T alpha = x[k + 1];
+                T sc = F::abs(alpha);
+                bool hasnan = alpha != alpha;
+                static_for<N - k - 2>([&](auto J) {
+                    constexpr int j = k + 2 + decltype(J)::value;
+                    sc = F::max(sc, F::abs(x[j]));
+                    hasnan = hasnan | (x[j] != x[j]);
+                });
+                sc = hasnan ? F::qnan() : sc;
+                const T inv = (sc == T(0)) ? T(0) : T(1) / sc;
+                T ss = T(0);
+                static_for<N - k - 2>([&](auto J) {
+                    constexpr int j = k + 2 + decltype(J)::value;
+                    const T y = x[j] * inv;
+                    ss = F::fma(y, y, ss);
+                });
+                T tau = T(0), beta = alpha, scal = T(0);
+                if (!(ss == T(0))) {
+                    const T ya = alpha * inv;
+                    const T nrm = sc * F::sqrt(F::fma(ya, ya, ss));
+                    beta = -F::copysign(nrm, alpha);
+                    tau = (beta - alpha) / beta;
+                    scal = T(1) / (alpha - beta);
+                }
+                e[k] = beta;
+                if (tau != T(0)) {
+                    T v[N];
+                    v[k + 1] = T(1);
+                    static_for<N - k - 2>([&](auto J) {
+                        constexpr int j = k + 2 + decltype(J)::value;
+                        v[j] = x[j] * scal;
+                    });
+                    // p = tau A v on the lane's rows (rows <= k are done: 0)
+                    T p[RA], vr[RA];
+                    T part = T(0);
+                    static_for<RA>([&](auto II) {
+                        constexpr int i = decltype(II)::value;
+                        const int row = r * RA + i;
+                        T s = a[i][k + 1];
+                        static_for<N - k - 2>([&](auto J) {
+                            constexpr int j = k + 2 + decltype(J)::value;
+                            s = F::fma(a[i][j], v[j], s);
+                        });
+                        p[i] = (row > k) ? tau * s : T(0);
+                        const T xr = sx[row];
+                        vr[i] = (row == k + 1) ? T(1) : ((row > k + 1) ? xr * scal : T(0));
+                        part = F::fma(p[i], vr[i], part);
+                    });
+                    const T pv = chunk_sum<P>(part);
+                    const T half = tau * pv * T(0.5);
+                    T w[RA];
+                    static_for<RA>([&](auto II) {
+                        constexpr int i = decltype(II)::value;
+                        w[i] = F::fma(-half, vr[i], p[i]);
+                        sw[r * RA + i] = w[i];
+                    });
+                    __builtin_amdgcn_wave_barrier();
+                    T wv[N];
+                    static_for<N - k - 1>([&](auto J) {
+                        constexpr int j = k + 1 + decltype(J)::value;
+                        wv[j] = sw[j];
+                    });
+                    // A <- A - v w^T - w v^T on the trailing columns
+                    static_for<RA>([&](auto II) {
+                        constexpr int i = decltype(II)::value;
+                        static_for<N - k - 1>([&](auto J) {
+                            constexpr int j = k + 1 + decltype(J)::value;
+                            a[i][j] = F::fma(-w[i], v[j], F::fma(-vr[i], wv[j], a[i][j]));
+                        });
+                    });
+                    // Q <- Q H_k, row by row
+                    if constexpr (WANTQ) {
+                        static_for<RQ>([&](auto II) {
+                            constexpr int i = decltype(II)::value;
+                            T t = q[i][k + 1];
+                            static_for<N - k - 2>([&](auto J) {
+                                constexpr int j = k + 2 + decltype(J)::value;
+                                t = F::fma(q[i][j], v[j], t);
+                            });
+                            t = tau * t;
+                            static_for<N - k - 1>([&](auto J) {
+                                constexpr int j = k + 1 + decltype(J)::value;
+                                q[i][j] = F::fma(-t, v[j], q[i][j]);
+                            });
+                        });
+                    }
+                }
+            }
+        }
+        // the next step's publish overwrites sx: keep this step's reads first
+        __builtin_amdgcn_wave_barrier();
+    });
+}
+
+}  // namespace steqr

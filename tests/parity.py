@@ -127,3 +127,67 @@ def check(d, e, gpu, ora, jobz: bool, tol_factor: float = 16.0,
             if jobz and not np.array_equal(Qg[zero], np.broadcast_to(np.eye(n), Qg[zero].shape)):
                 out.append("zero matrix: Q not exactly I")
     return out
+
+
+def sym_from_lower(A) -> np.ndarray:
+    """The symmetric matrix a dense solver sees: lower triangle of A,
+    mirrored (float64)."""
+    L = np.tril(np.asarray(A, dtype=np.float64))
+    return L + np.swapaxes(np.tril(L, -1), 1, 2)
+
+
+def run_gpu_syev(A: np.ndarray, jobz: bool, *, sort: bool = True, max_sweeps_per_n: int = 0,
+                 lanes: int = 0, waves: int = 0, shift: int = 0):
+    import torch
+    import symmetric_tridiagonal_eigensolver_amd as st
+    tA = torch.from_numpy(np.ascontiguousarray(A)).to(torch.device("cuda:0"))
+    lam, Q, info = st.syev(tA, jobz, info=True, sort=sort, max_sweeps_per_n=max_sweeps_per_n,
+                           lanes_per_problem=lanes, waves_per_block=waves, shift=shift)
+    torch.cuda.synchronize()
+    return (lam.cpu().numpy(), None if Q is None else Q.cpu().numpy(), info.cpu().numpy())
+
+
+def check_dense(A, gpu, ora, jobz: bool, tol_factor: float = 16.0,
+                sort: bool = True) -> List[str]:
+    """Dense solver parity: the same items fail with equal info; converged
+    items have sorted eigenvalues within 16 n eps ||A||_1 of the oracle's,
+    and with eigenvectors the dense residual ||AQ - Q Lambda||_1/||A||_1
+    and ||Q^T Q - I||_1 within 16 n eps; zero matrices give lambda = 0 and
+    Q = I exactly; NaN items NaN on both sides."""
+    out: List[str] = []
+    lg, Qg, ig = gpu
+    lo, Qo, io = ora[:3]
+    n = A.shape[1]
+    tol = V.tol_of(A.dtype, n, tol_factor)
+    As = sym_from_lower(A)
+    an = np.abs(As).sum(axis=1).max(axis=1)
+    if not np.array_equal(ig > 0, io > 0):
+        bad = np.nonzero((ig > 0) != (io > 0))[0][:8]
+        out.append("status differs at items %s" % bad.tolist())
+    nan_g = np.isnan(lg).any(axis=1)
+    nan_o = np.isnan(lo).any(axis=1)
+    if not np.array_equal(nan_g, nan_o):
+        out.append("NaN items differ: %s" % np.nonzero(nan_g != nan_o)[0][:8].tolist())
+    ok = (ig == 0) & (io == 0) & ~nan_g & ~nan_o
+    if ok.any():
+        err = np.abs(np.sort(lg[ok].astype(np.float64), 1) - np.sort(lo[ok].astype(np.float64), 1))
+        rel = err.max(axis=1) / np.where(an[ok] > 0, an[ok], 1.0)
+        if not (rel.max() <= tol):
+            out.append("eigenvalues: max err %.3g > tol %.3g (item %d)"
+                       % (rel.max(), tol, int(np.nonzero(ok)[0][np.argmax(rel)])))
+        if sort and not np.all(np.diff(lg[ok], axis=1) >= 0):
+            out.append("gpu eigenvalues not ascending")
+        if jobz:
+            res = V.dense_residual(As[ok], lg[ok], Qg[ok])
+            if not (res.max() <= tol):
+                out.append("dense residual %.3g > tol %.3g" % (res.max(), tol))
+            orth = V.orthogonality(Qg[ok])
+            if not (orth.max() <= tol):
+                out.append("orthogonality %.3g > tol %.3g" % (orth.max(), tol))
+        zero = ok & (an == 0)
+        if zero.any():
+            if not np.all(lg[zero] == 0):
+                out.append("zero matrix: eigenvalues not exactly 0")
+            if jobz and not np.array_equal(Qg[zero], np.broadcast_to(np.eye(n), Qg[zero].shape)):
+                out.append("zero matrix: Q not exactly I")
+    return out

@@ -29,11 +29,12 @@ def st():
 def _declared():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(steqr_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b((?:steqr|syev)_\w+)\s*\(", text)))
 
 
 def test_header_declares_expected_entry_points():
-    assert _declared() == ["steqr_batched", "steqr_batched_ex", "steqr_query", "steqr_version"]
+    assert _declared() == ["steqr_batched", "steqr_batched_ex", "steqr_query", "steqr_version",
+                           "syev_batched", "syev_batched_ex", "syev_query"]
 
 
 def test_library_exports_every_declared_symbol(st):
@@ -183,3 +184,37 @@ def test_uninstantiated_lanes_rejected_by_query(st):
     with pytest.raises(st.SteqrError) as ex:
         st.steqr_query(16, 10, 1, 0, st.make_params(lanes_per_problem=64))
     assert ex.value.rc == -10
+
+
+# ---------------------------------------------------------------- dense syev
+
+@pytest.mark.parametrize("n,jobz,dtype,N,P,R", [
+    (1, 1, 0, 4, 4, 1), (4, 1, 0, 4, 4, 1), (5, 1, 0, 8, 2, 4), (16, 1, 0, 16, 4, 4),
+    (16, 0, 0, 16, 4, 4), (12, 1, 1, 16, 8, 2), (17, 1, 0, 32, 16, 2), (32, 1, 1, 32, 16, 2),
+    (8, 0, 1, 8, 4, 2)])
+def test_syev_default_plans(st, n, jobz, dtype, N, P, R):
+    q = st.syev_query(n, 32768, jobz, dtype)
+    assert (q["padded_n"], q["lanes_per_problem"], q["rows_per_lane"]) == (N, P, R)
+    per_block = q["waves_per_block"] * 64 // P
+    assert q["workgroups"] == -(-32768 // per_block)
+
+
+def test_syev_argument_errors(st):
+    L = st.lib()
+    # validation happens before any launch (the pointers are not device memory)
+    assert L.syev_batched(8, 8, 8, 33, 10, 1, 0, None) == -4
+    assert L.syev_batched(8, 8, 8, -1, 10, 1, 0, None) == -4
+    assert L.syev_batched(8, 8, 8, 16, -1, 1, 0, None) == -5
+    assert L.syev_batched(8, 8, 8, 16, 10, 2, 0, None) == -6
+    assert L.syev_batched(8, 8, 8, 16, 10, 1, 2, None) == -7
+    assert L.syev_batched(None, 8, 8, 16, 10, 1, 0, None) == -1
+    assert L.syev_batched(8, None, 8, 16, 10, 1, 0, None) == -2
+    assert L.syev_batched(8, 8, None, 16, 10, 1, 0, None) == -3
+    assert L.syev_batched(None, None, None, 0, 10, 1, 0, None) == 0
+    assert L.syev_batched(None, None, None, 16, 0, 1, 0, None) == 0
+    for prm in (st.make_params(update_scheme=st.STEQR_PG), st.make_params(back_transform=True),
+                st.make_params(band_storage=2), st.make_params(lanes_per_problem=64),
+                st.make_params(waves_per_block=3), st.make_params(shift=2)):
+        assert L.syev_batched_ex(8, 8, 8, 16, 10, 1, 0, None, None, ctypes.byref(prm)) == -10
+    # the closed-form shift is accepted
+    assert st.syev_query(16, 10, 1, 0, st.make_params(shift=st.STEQR_SHIFT_CLOSED))["padded_n"] == 16
