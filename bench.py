@@ -115,7 +115,11 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default=W.HEADLINE, choices=list(W.WORKLOADS))
+    ap.add_argument("--op", default="steqr", choices=["steqr", "syev"],
+                    help="steqr: tridiagonal solve (default); syev: the fused dense "
+                         "eigensolver on a DENSE workload (s_*)")
+    ap.add_argument("--workload", default=None,
+                    choices=list(W.WORKLOADS) + list(W.DENSE_WORKLOADS))
     ap.add_argument("--jobz", default="V", choices=["V", "N"])
     ap.add_argument("--lanes", type=int, default=0, help="lanes per problem (0 = default)")
     ap.add_argument("--waves", type=int, default=0, help="waves per workgroup (0 = default)")
@@ -162,7 +166,12 @@ def main() -> int:
                           "steps": args.steps, "GBs": 2 * nbytes / dt / 1e9}), flush=True)
         return 0
 
-    w = W.WORKLOADS[args.workload]
+    if args.op == "syev":
+        return run_syev(args, torch, st)
+    if args.workload in W.DENSE_WORKLOADS:
+        print("bench.py: %s is a dense workload: use --op syev" % args.workload, file=sys.stderr)
+        return 2
+    w = W.WORKLOADS[args.workload or W.HEADLINE]
     jobz = args.jobz == "V"
     bt = bool(args.back_transform)
     if bt and not jobz:
@@ -308,6 +317,120 @@ def main() -> int:
                                     else "d,e iid N(0,1)")) + ", seed 1234"},
         "roofline": roof,
         "at_named_lanes": named,
+        "hbm": {"algorithmic_bytes_per_launch": bpm * nb,
+                "achieved_GBs": bpm * nb / sec / 1e9, "peak_GBs": HBM_PEAK_GBS},
+        "cpu_baseline": cpu,
+        "wall_s_timed_region": wall,
+        "library": st.version(),
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def dense_flops_per_matrix(n: int, jobz: bool) -> float:
+    """Algorithmic flops of the dense front end: the reduction to tridiagonal
+    form (4n^3/3) and, with eigenvectors, the formation of its Q (4n^3/3),
+    the textbook counts (the kernel's full-storage form performs more)."""
+    return (4.0 / 3.0) * n ** 3 * (2 if jobz else 1)
+
+
+def run_syev(args, torch, st) -> int:
+    """One step = one launch of syev_batched_ex over a dense workload."""
+    name = args.workload or "s_f32_n16"
+    if name not in W.DENSE_WORKLOADS:
+        print("bench.py: --op syev needs a dense workload (%s)" % ", ".join(W.DENSE_WORKLOADS),
+              file=sys.stderr)
+        return 2
+    dtype, n, nb = W.DENSE_WORKLOADS[name]
+    jobz = args.jobz == "V"
+    A = W.make_dense(name)
+    dev = torch.device("cuda:0")
+    tA = torch.from_numpy(A).to(dev)
+    lam = torch.empty((nb, n), dtype=tA.dtype, device=dev)
+    Q = torch.empty_like(tA) if jobz else None
+    info = torch.empty((nb,), dtype=torch.int32, device=dev)
+    prm = st.make_params(lanes_per_problem=args.lanes, waves_per_block=args.waves)
+    dcode = st.dtype_code(tA.dtype)
+    plan = st.syev_query(n, nb, int(jobz), dcode, prm)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        rc = st.syev_batched_ex(tA, lam, Q, n, nb, int(jobz), dcode, stream, info, prm)
+        if rc != 0:
+            raise st.SteqrError(rc, "syev_batched_ex")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if int(info.max().item()) != 0:
+        raise RuntimeError("non-convergence on a finite workload")
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = start.elapsed_time(stop) / args.steps
+    sec = ms / 1e3
+
+    cpu = None
+    roof = None
+    if not args.no_cpu:
+        import oracle
+        cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+        oracle.syev(A[:64], jobz)
+        times = []
+        for _ in range(3):
+            t = time.perf_counter()
+            oracle.syev(A, jobz, threads=cores)
+            times.append(time.perf_counter() - t)
+        tmed = statistics.median(times)
+        cpu = {"value": nb / tmed, "unit": "matrices/s", "cores": cores, "kind": "oracle",
+               "us_per_matrix": tmed / nb * 1e6,
+               "sample": "full %s batch (%d matrices), median of 3 runs on %d threads"
+                         % (name, nb, cores)}
+        # algorithmic flops: the dense front end plus the tridiagonal solve of
+        # the reduced matrices (the oracle's rotation counts)
+        d, e, _ = oracle.sytrd(A, want_q=False)
+        _, _, _, stats = oracle.steqr(d, e, jobz, threads=cores)
+        flops = float(flops_per_matrix(stats, n, jobz).sum()) + nb * dense_flops_per_matrix(n, jobz)
+        ach = flops / sec / 1e12
+        peak = PEAK_TFLOPS[dtype]
+        roof = {"kernel": "steqr_chunk_kernel<%s, N=%d, P=%d, %s, dense>"
+                          % ("float" if dtype == "f32" else "double", plan["padded_n"],
+                             plan["lanes_per_problem"], "V" if jobz else "N"),
+                "bound": "alu", "achieved": ach, "peak": peak, "unit": "TFLOP/s",
+                "frac": ach / peak, "traffic": None,
+                "algorithmic_flops_per_launch": flops,
+                "algorithmic_flops_per_matrix": flops / nb}
+    itemsize = A.itemsize
+    bpm = (n * n + n + (n * n if jobz else 0)) * itemsize
+    out = {
+        "metric": "matrices/sec (us/matrix) fused dense syev",
+        "value": nb / sec,
+        "unit": "matrices/s",
+        "us_per_matrix": sec / nb * 1e6,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic",
+        "config": {"workload": name, "op": "syev", "n": n, "batch": nb,
+                   "jobz": "V" if jobz else "N", "precision": dtype,
+                   "lanes_per_problem": plan["lanes_per_problem"],
+                   "rows_per_lane": plan["rows_per_lane"], "padded_n": plan["padded_n"],
+                   "waves_per_block": plan["waves_per_block"],
+                   "workgroups": plan["workgroups"],
+                   "inputs": "dense symmetric, lower triangle iid N(0,1), seed 1234"},
+        "roofline": roof,
         "hbm": {"algorithmic_bytes_per_launch": bpm * nb,
                 "achieved_GBs": bpm * nb / sec / 1e9, "peak_GBs": HBM_PEAK_GBS},
         "cpu_baseline": cpu,

@@ -25,7 +25,10 @@
 // broadcast of v), each lane forms p for its own rows, a butterfly over the
 // chunk's lanes sums p^T v, and the lanes exchange w through LDS for the
 // rank-2 update. Rows at or beyond n are zero padding (their reflectors are
-// the identity, their d and e zero).
+// the identity, their d and e zero). Reciprocals and the square root use
+// the hardware instructions (about 1 ulp; Newton-refined in double), as the
+// tridiagonal solve's shift does: the reduction is accurate to a few ulps
+// of ||A|| either way.
 #pragma once
 
 #include "steqr_device.hpp"
@@ -81,7 +84,7 @@ __device__ __forceinline__ void householder_chunk(T (&a)[RA][N], T (&q)[RQ][N], 
                     hasnan = hasnan | (x[j] != x[j]);
                 });
                 sc = hasnan ? F::qnan() : sc;
-                const T inv = (sc == T(0)) ? T(0) : T(1) / sc;
+                const T inv = (sc == T(0)) ? T(0) : F::rcp(sc);
                 T ss = T(0);
                 static_for<N - k - 2>([&](auto J) {
                     constexpr int j = k + 2 + decltype(J)::value;
@@ -91,10 +94,10 @@ __device__ __forceinline__ void householder_chunk(T (&a)[RA][N], T (&q)[RQ][N], 
                 T tau = T(0), beta = alpha, scal = T(0);
                 if (!(ss == T(0))) {
                     const T ya = alpha * inv;
-                    const T nrm = sc * F::sqrt(F::fma(ya, ya, ss));
+                    const T nrm = sc * F::sqrt_fast(F::fma(ya, ya, ss));
                     beta = -F::copysign(nrm, alpha);
-                    tau = (beta - alpha) / beta;
-                    scal = T(1) / (alpha - beta);
+                    tau = (beta - alpha) * F::rcp(beta);
+                    scal = F::rcp(alpha - beta);
                 }
                 e[k] = beta;
                 if (tau != T(0)) {

@@ -33,6 +33,9 @@ CASES = [
     (np.float64, 21, 16, True),
     (np.float64, 4, 4, False), (np.float64, 8, 4, False), (np.float64, 16, 8, False),
     (np.float64, 32, 16, False),
+    (np.float32, 8, 1, False), (np.float32, 16, 2, False), (np.float32, 14, 2, False),
+    (np.float32, 32, 8, False), (np.float32, 25, 8, False),
+    (np.float64, 8, 2, False), (np.float64, 16, 4, False), (np.float64, 10, 4, False),
 ]
 
 

@@ -65,6 +65,26 @@ WORKLOADS: Dict[str, Workload] = {
 
 HEADLINE = "c2_f32_n16"
 
+# Dense workloads of the fused small-n syev: seeded symmetric matrices with
+# a lower triangle of iid N(0,1) entries (random_symmetric), at the orders
+# and batches the syev tables on the pages use for the small-n kernels.
+DENSE_WORKLOADS: Dict[str, Tuple[str, int, int]] = {
+    # name: (dtype, n, batch)
+    "s_f32_n8": ("f32", 8, 65536),
+    "s_f32_n16": ("f32", 16, 32768),
+    "s_f32_n32": ("f32", 32, 16384),
+    "s_f64_n16": ("f64", 16, 32768),
+    "s_f64_n32": ("f64", 32, 16384),
+}
+
+
+def make_dense(name: str, batch: int | None = None) -> np.ndarray:
+    """Dense (batch, n, n) matrices of a DENSE_WORKLOADS entry; a smaller
+    batch is a prefix of the full one."""
+    dt, n, nb = DENSE_WORKLOADS[name]
+    nb = nb if batch is None else int(batch)
+    return random_symmetric(n, nb, np.float32 if dt == "f32" else np.float64, cfg=9)
+
 
 def rng_for(cfg: int, n: int, salt: int | None = None) -> np.random.Generator:
     """PCG64 generator seeded from (1234, cfg, n[, salt])."""
