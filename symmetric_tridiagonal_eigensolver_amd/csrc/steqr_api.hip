@@ -205,14 +205,16 @@ extern "C" int steqr_batched(const void* d, const void* e, void* lambda, void* Q
 
 namespace {
 
-// Default lanes per problem of the fused dense kernel: the lanes hold whole
-// rows of A and Q (N/P rows each), so P is chosen to keep A, Q and the
-// replicated band within the register file at two wavefronts per SIMD.
-int syev_default_lanes(int dtype, int N) {
+// Default lanes per problem of the fused dense kernel (measured on MI355X):
+// the lanes hold whole rows of A and Q (N/P rows each), so P keeps A, Q and
+// the replicated band within the register file at two wavefronts per SIMD;
+// without Q there is room for twice the rows at orders 16 (double) and 32
+// (float).
+int syev_default_lanes(int dtype, int N, int jobz) {
     if (N == 4) return 4;
     if (N == 8) return dtype == STEQR_F32 ? 2 : 4;
-    if (N == 16) return dtype == STEQR_F32 ? 4 : 8;
-    return 16;
+    if (N == 16) return dtype == STEQR_F32 ? 4 : (jobz ? 8 : 4);
+    return (dtype == STEQR_F32 && !jobz) ? 8 : 16;
 }
 
 int syev_plan(int n, int batch, int jobz, int dtype, const steqr_params* prm, Plan* out) {
@@ -242,7 +244,7 @@ int syev_plan(int n, int batch, int jobz, int dtype, const steqr_params* prm, Pl
         return 0;
     }
     const int N = padded_order(n < 2 ? 2 : n);
-    if (P == 0) P = syev_default_lanes(dtype, N);
+    if (P == 0) P = syev_default_lanes(dtype, N, jobz);
     const Table t = dtype == STEQR_F32 ? steqr::table_syev_f32() : steqr::table_syev_f64();
     const Entry* ent = search(t, dtype, N, P, jobz, 1);
     if (!ent) return -10;
