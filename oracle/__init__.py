@@ -10,7 +10,9 @@ QR/QL iteration written step by step from the BatchLAS steqr algorithm page
 (deflation, scaling, shift, Givens bulge chase, split bookkeeping,
 eigenvector accumulation, sort), and the dense front end of the fused
 small-n syev (``syev_oracle_impl.h``: Householder reduction to tridiagonal
-form, then that solve with back-transformation). It runs in the item's precision with IEEE
+form, then that solve with back-transformation) and the values-only
+bisection (``stebz_oracle_impl.h``: Sturm counts, one eigenvalue index at
+a time). It runs in the item's precision with IEEE
 semantics and no FMA contraction. This module builds it with gcc, loads it
 with ctypes and splits batches across threads (ctypes releases the GIL while
 the C code runs).
@@ -29,6 +31,7 @@ HERE = _os.path.dirname(_os.path.abspath(__file__))
 SOURCE = _os.path.join(HERE, "steqr_oracle.c")
 IMPL = _os.path.join(HERE, "steqr_oracle_impl.h")
 IMPL_SYEV = _os.path.join(HERE, "syev_oracle_impl.h")
+IMPL_STEBZ = _os.path.join(HERE, "stebz_oracle_impl.h")
 LIBNAME = "liboracle_steqr.so"
 CFLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared"]
 
@@ -50,7 +53,7 @@ def _stale(path: str) -> bool:
     if not _os.path.exists(path):
         return True
     t = _os.path.getmtime(path)
-    return any(_os.path.getmtime(s) > t for s in (SOURCE, IMPL, IMPL_SYEV))
+    return any(_os.path.getmtime(s) > t for s in (SOURCE, IMPL, IMPL_SYEV, IMPL_STEBZ))
 
 
 def lib(path: Optional[str] = None) -> _ct.CDLL:
@@ -89,6 +92,12 @@ def lib(path: Optional[str] = None) -> _ct.CDLL:
             f.restype = None
             f.argtypes = [_ct.c_int, ct, _ct.c_void_p, P, P]
             f = getattr(L, "oracle_sytrd_batched_" + sfx)
+            f.restype = _ct.c_int
+            f.argtypes = [_ct.c_void_p] * 4 + [_ct.c_int, _ct.c_long]
+            f = getattr(L, "oracle_sturm_count_" + sfx)
+            f.restype = _ct.c_int
+            f.argtypes = [_ct.c_int, _ct.c_void_p, _ct.c_void_p, ct, ct]
+            f = getattr(L, "oracle_stebz_batched_" + sfx)
             f.restype = _ct.c_int
             f.argtypes = [_ct.c_void_p] * 4 + [_ct.c_int, _ct.c_long]
             f = getattr(L, "oracle_syev_batched_" + sfx)
@@ -287,3 +296,43 @@ def syev(A: _np.ndarray, jobz: bool = True, max_sweeps_per_n: int = 30, sort: bo
     if any(rcs):
         raise ValueError("oracle rejected n=%d" % n)
     return lam, Q, info
+
+
+def sturm_count(d: _np.ndarray, e: _np.ndarray, x: float, pivmin: float, libpath=None) -> int:
+    """Number of eigenvalues of one tridiagonal (d (n,), e (n-1,)) below x."""
+    d = _np.ascontiguousarray(d)
+    e2 = _np.ascontiguousarray(_np.asarray(e, dtype=d.dtype) ** 2)
+    return getattr(lib(libpath), "oracle_sturm_count_" + _sfx(d.dtype))(
+        d.shape[0], d.ctypes.data, e2.ctypes.data, x, pivmin)
+
+
+def stebz(d: _np.ndarray, e: _np.ndarray, threads: int = 1, libpath=None
+          ) -> Tuple[_np.ndarray, _np.ndarray]:
+    """Values-only bisection of a batch: (lam (batch, n) ascending, info
+    (batch,) = indices that ran out of halvings)."""
+    d = _np.ascontiguousarray(d)
+    e = _np.ascontiguousarray(e)
+    batch, n = d.shape
+    if e.shape != (batch, max(n - 1, 0)) or e.dtype != d.dtype:
+        raise ValueError("bad band shapes %s %s" % (d.shape, e.shape))
+    lam = _np.empty_like(d)
+    info = _np.zeros(batch, dtype=_np.int32)
+    if batch == 0 or n == 0:
+        return lam, info
+    fn = getattr(lib(libpath), "oracle_stebz_batched_" + _sfx(d.dtype))
+    it = d.itemsize
+
+    def run(lo: int, hi: int) -> int:
+        return fn(d.ctypes.data + lo * n * it, e.ctypes.data + lo * max(n - 1, 0) * it,
+                  lam.ctypes.data + lo * n * it, info.ctypes.data + lo * 4, n, hi - lo)
+
+    threads = max(1, min(int(threads), batch))
+    cuts = [batch * k // threads for k in range(threads + 1)]
+    if threads == 1:
+        rcs = [run(0, batch)]
+    else:
+        with _cf.ThreadPoolExecutor(threads) as ex:
+            rcs = list(ex.map(lambda k: run(cuts[k], cuts[k + 1]), range(threads)))
+    if any(rcs):
+        raise ValueError("oracle rejected n=%d" % n)
+    return lam, info

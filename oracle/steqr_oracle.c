@@ -6,7 +6,8 @@
  *   gcc -O2 -ffp-contract=off -fno-fast-math -fPIC -shared \
  *       -o liboracle_steqr.so steqr_oracle.c -lm
  * The algorithm body lives in steqr_oracle_impl.h (the tridiagonal solve)
- * and syev_oracle_impl.h (the dense front end) and is instantiated here for
+ * syev_oracle_impl.h (the dense front end) and stebz_oracle_impl.h (values-
+ * only bisection) and is instantiated here for
  * float (REAL = float, every operation in IEEE single precision) and
  * double.
  */
@@ -28,6 +29,7 @@
 #define R_COPYSIGN copysignf
 #include "steqr_oracle_impl.h"
 #include "syev_oracle_impl.h"
+#include "stebz_oracle_impl.h"
 #undef REAL
 #undef SFX
 #undef R_EPS
@@ -47,6 +49,7 @@
 #define R_COPYSIGN copysign
 #include "steqr_oracle_impl.h"
 #include "syev_oracle_impl.h"
+#include "stebz_oracle_impl.h"
 
 /* Constants as the oracle computes them, for the pins. */
 void oracle_constants_f32(float *out5)

@@ -38,7 +38,12 @@ What each pin checks, and why it is independent of the oracle's own code:
   syev       eigenvalues against numpy's eigvalsh, the dense residual and
              orthogonality bounds, a tridiagonal A giving the tridiagonal
              solve bit for bit, and a diagonal A its sorted diagonal with a
-             permutation for Q.
+             permutation for Q;
+  stebz      the Sturm count against numpy's eigvalsh (the number of
+             eigenvalues below x, at points away from them), whole solves
+             against eigvalsh, the Clement and Toeplitz closed forms and the
+             QR solve, ascending output, exact power-of-two scaling
+             lambda(2^j T) = 2^j lambda(T), a diagonal T, T = 0 and NaN.
 """
 from __future__ import annotations
 
@@ -455,8 +460,69 @@ def pin_syev(oracle, libpath: Optional[str] = None, quick: bool = False) -> List
     return out
 
 
+def pin_stebz(oracle, libpath: Optional[str] = None) -> List[str]:
+    out: List[str] = []
+    g = np.random.default_rng(71)
+    for dt in (np.float32, np.float64):
+        # Sturm counts at random points at least 1e-3 ||T|| from every eigenvalue
+        for n in (1, 2, 5, 16, 40):
+            d, e = W.random_batch(n, 6, dt, salt=72)
+            ref = np.linalg.eigvalsh(W.dense_from_bands(d.astype(np.float64), e.astype(np.float64)))
+            for b in range(6):
+                tn = V.tnorm1(d[b:b + 1], e[b:b + 1])[0]
+                pivmin = float(np.finfo(dt).tiny) * max(1.0, float((e[b].astype(np.float64) ** 2).max(initial=0)))
+                for x in g.uniform(-1.2 * tn, 1.2 * tn, 12):
+                    if np.abs(ref[b] - x).min() < 1e-3 * tn:
+                        continue
+                    c = oracle.sturm_count(d[b], e[b], dt(x), pivmin, libpath=libpath)
+                    _fail(out, c == int((ref[b] < dt(x)).sum()), "Sturm count %s n=%d at %g: %d"
+                          % (dt.__name__, n, x, c))
+        for n in (1, 2, 3, 8, 13, 16, 32, 64):
+            d, e = W.random_batch(n, 24, dt, salt=73)
+            lam, info = oracle.stebz(d, e, libpath=libpath)
+            tol = V.tol_of(dt, n)
+            _fail(out, not info.any(), "stebz info (%s n=%d)" % (dt.__name__, n))
+            ref = np.linalg.eigvalsh(W.dense_from_bands(d.astype(np.float64), e.astype(np.float64)))
+            _fail(out, V.sorted_err(lam, ref, d, e).max() <= tol,
+                  "stebz vs eigvalsh (%s n=%d)" % (dt.__name__, n))
+            _fail(out, np.all(np.diff(lam, axis=1) >= 0), "stebz not ascending")
+            lq, _, _, _ = oracle.steqr(d, e, False, libpath=libpath)
+            _fail(out, V.sorted_err(lam, lq.astype(np.float64), d, e).max() <= tol,
+                  "stebz vs the QR solve (%s n=%d)" % (dt.__name__, n))
+            for j in (-40, 7, 60):
+                ls, _ = oracle.stebz(d * dt(2.0 ** j), e * dt(2.0 ** j), libpath=libpath)
+                _fail(out, np.array_equal(ls, lam * dt(2.0 ** j)),
+                      "stebz power-of-two scaling (%s n=%d, 2^%d)" % (dt.__name__, n, j))
+        for n in (4, 16, 33, 64):
+            d, e, ref = clement(n)
+            lam, info = oracle.stebz(d.astype(dt), e.astype(dt), libpath=libpath)
+            err = np.abs(lam[0].astype(np.float64) - ref).max() / V.tnorm1(d, e)[0]
+            _fail(out, info[0] == 0 and err <= V.tol_of(dt, n), "stebz Clement n=%d %s: %g"
+                  % (n, dt.__name__, err))
+            a, b = 0.5, -1.25
+            k = np.arange(1, n + 1)
+            tz = np.sort(a + 2 * b * np.cos(k * np.pi / (n + 1)))
+            lam, _ = oracle.stebz(np.full((1, n), a, dtype=dt), np.full((1, n - 1), b, dtype=dt),
+                                  libpath=libpath)
+            _fail(out, np.abs(lam[0] - tz).max() <= V.tol_of(dt, n) * (abs(a) + 2 * abs(b)),
+                  "stebz Toeplitz n=%d %s" % (n, dt.__name__))
+        dg = W.random_batch(9, 4, dt, salt=74)[0]
+        lam, _ = oracle.stebz(dg, np.zeros((4, 8), dtype=dt), libpath=libpath)
+        _fail(out, np.all(np.abs(lam - np.sort(dg, 1)) <= V.tol_of(dt, 9) *
+                          np.abs(dg).max(1, keepdims=True)), "stebz diagonal T (%s)" % dt.__name__)
+        lam, info = oracle.stebz(np.zeros((2, 7), dtype=dt), np.zeros((2, 6), dtype=dt),
+                                 libpath=libpath)
+        _fail(out, np.all(lam == 0) and not info.any(), "stebz T = 0")
+        d, e = W.random_batch(7, 2, dt, salt=75)
+        d[0, 3] = np.nan
+        e[1, 2] = np.nan
+        lam, info = oracle.stebz(d, e, libpath=libpath)
+        _fail(out, np.all(np.isnan(lam)) and np.all(info == 7), "stebz NaN")
+    return out
+
+
 ALL_PINS = (pin_lartg, pin_shift, pin_sym2x2, pin_sweep, pin_solve, pin_back_transform,
-            pin_larfg, pin_sytrd, pin_syev)
+            pin_larfg, pin_sytrd, pin_syev, pin_stebz)
 
 
 def run_all(oracle, libpath: Optional[str] = None, quick: bool = True) -> List[str]:

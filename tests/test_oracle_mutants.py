@@ -73,16 +73,27 @@ MUTANTS = [
      "W[i * n + j] = A[j * n + i];\n            W[j * n + i] = A[j * n + i];"),
     ("sytrd_e_is_alpha", "e[k] = beta;", "e[k] = W[(k + 1) * n + k];"),
     ("syev_no_back_transform", "scheme, shift, 1, 0);", "scheme, shift, 0, 0);"),
+    # values-only bisection
+    ("sturm_count_sign", "c += q < (REAL)0;", "c += q > (REAL)0;"),
+    ("sturm_drop_coupling", "q = (d[i] - x) - e2[i - 1] / q;", "q = (d[i] - x);"),
+    ("sturm_wrong_e_index", "q = (d[i] - x) - e2[i - 1] / q;", "q = (d[i] - x) - e2[i] / q;"),
+    ("bisect_update_inverted", "if (SFX(oracle_sturm_count)(n, ds, e2, mid, pivmin) <= k)",
+     "if (SFX(oracle_sturm_count)(n, ds, e2, mid, pivmin) > k)"),
+    ("bisect_index_off_by_one", "if (SFX(oracle_sturm_count)(n, ds, e2, mid, pivmin) <= k)",
+     "if (SFX(oracle_sturm_count)(n, ds, e2, mid, pivmin) <= k + 1)"),
+    ("gershgorin_no_radius", "if (ds[i] - rad < gl)", "if (ds[i] < gl)"),
+    ("stebz_not_unscaled", "lam[k] = ((lo + hi) / (REAL)2) * us;", "lam[k] = ((lo + hi) / (REAL)2);"),
 ]
 
 
 def _build_mutant(tmp, old, new):
     src = os.path.join(tmp, "src")
     os.makedirs(src)
-    for f in ("steqr_oracle.c", "steqr_oracle_impl.h", "syev_oracle_impl.h"):
+    for f in ("steqr_oracle.c", "steqr_oracle_impl.h", "syev_oracle_impl.h",
+              "stebz_oracle_impl.h"):
         shutil.copy(os.path.join(oracle.HERE, f), src)
     hits = []
-    for f in ("steqr_oracle_impl.h", "syev_oracle_impl.h"):
+    for f in ("steqr_oracle_impl.h", "syev_oracle_impl.h", "stebz_oracle_impl.h"):
         impl = os.path.join(src, f)
         text = open(impl).read()
         if old in text:

@@ -59,7 +59,7 @@ def test_back_transform_pins(oracle_mod, scheme, shift):
     assert P.pin_back_transform(oracle_mod, quick=False, scheme=scheme, shift=shift) == []
 
 
-@pytest.mark.parametrize("pin", [P.pin_larfg, P.pin_sytrd, P.pin_syev],
+@pytest.mark.parametrize("pin", [P.pin_larfg, P.pin_sytrd, P.pin_syev, P.pin_stebz],
                          ids=lambda p: p.__name__)
 def test_dense_front_end_pins(oracle_mod, pin):
     assert pin(oracle_mod) == []
