@@ -57,10 +57,12 @@ def bytes_per_matrix(n: int, itemsize: int, jobz: bool, back_transform: bool = F
 # Sources each kernel family is compiled from (its hash guards committed
 # counter records against kernel changes).
 KERNEL_SOURCES = {
-    "chunk": ["steqr_device.hpp", "steqr_chunk.hpp"],
-    "chunkl": ["steqr_device.hpp", "steqr_chunk.hpp", "steqr_chunkl.hpp"],
-    "wave": ["steqr_device.hpp", "steqr_chunk.hpp", "steqr_wave.hpp"],
-    "pc": ["steqr_device.hpp", "steqr_chunk.hpp", "steqr_chunkl.hpp", "steqr_pc.hpp"],
+    "chunk": ["steqr_device.hpp", "syev_reduce.hpp", "steqr_chunk.hpp"],
+    "chunkl": ["steqr_device.hpp", "syev_reduce.hpp", "steqr_chunk.hpp", "steqr_chunkl.hpp"],
+    "wave": ["steqr_device.hpp", "syev_reduce.hpp", "steqr_chunk.hpp", "steqr_wave.hpp"],
+    "pc": ["steqr_device.hpp", "syev_reduce.hpp", "steqr_chunk.hpp", "steqr_chunkl.hpp",
+           "steqr_pc.hpp"],
+    "bisect": ["steqr_device.hpp", "syev_reduce.hpp", "steqr_chunk.hpp", "steqr_bisect.hpp"],
 }
 
 
@@ -88,9 +90,17 @@ def counters_from_profiles(wname: str, jobz: bool, family: str):
     return t
 
 
+def bisect_flops_per_matrix(counts: np.ndarray, n: int) -> np.ndarray:
+    """Algorithmic flops of the values-only bisection: 4n per Sturm count
+    (d_i - x, the reciprocal of the pivot and the multiply-add, per
+    position), from the oracle's count of Sturm counts per matrix."""
+    return counts.astype(np.float64) * 4.0 * n
+
+
 def cpu_baseline(d: np.ndarray, e: np.ndarray, jobz: bool, wname: str, scheme: int = 0,
-                 Z: np.ndarray = None):
-    """The CPU oracle (as is) on the host cores over the same workload."""
+                 Z: np.ndarray = None, method: int = 0):
+    """The CPU oracle (as is) on the host cores over the same workload.
+    method 1: the oracle's bisection; stats is then its Sturm counts."""
     import oracle
     cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
     oracle.steqr(d[:64], e[:64], jobz)  # load / warm
@@ -98,7 +108,10 @@ def cpu_baseline(d: np.ndarray, e: np.ndarray, jobz: bool, wname: str, scheme: i
     stats = None
     for _ in range(3):
         t = time.perf_counter()
-        _, _, _, stats = oracle.steqr(d, e, jobz, threads=cores, scheme=scheme, Z=Z)
+        if method == 1:
+            _, _, stats = oracle.stebz(d, e, threads=cores, counts=True)
+        else:
+            _, _, _, stats = oracle.steqr(d, e, jobz, threads=cores, scheme=scheme, Z=Z)
         times.append(time.perf_counter() - t)
     tmed = statistics.median(times)
     nb = d.shape[0]
@@ -127,6 +140,9 @@ def main() -> int:
                     help="band storage: 0 default, 1 registers, 2 LDS")
     ap.add_argument("--scheme", default="exp", choices=["exp", "pg"],
                     help="form of the chase step: EXP (default) or PG (Parlett-Gray)")
+    ap.add_argument("--method", default="qr", choices=["qr", "bisect"],
+                    help="eigenvalue method: QR iteration (default) or values-only "
+                         "bisection (needs --jobz N)")
     ap.add_argument("--back-transform", action="store_true",
                     help="Q holds a basis on entry (seeded random orthogonal) that the "
                          "rotations right-multiply in place; needs --jobz V")
@@ -177,9 +193,13 @@ def main() -> int:
     if bt and not jobz:
         print("bench.py: --back-transform needs --jobz V", file=sys.stderr)
         return 2
+    method = 1 if args.method == "bisect" else 0
+    if method and jobz:
+        print("bench.py: --method bisect needs --jobz N", file=sys.stderr)
+        return 2
     scheme = 1 if args.scheme == "pg" else 0
     prm0 = st.make_params(lanes_per_problem=args.lanes, waves_per_block=args.waves,
-                          band_storage=args.band, update_scheme=scheme)
+                          band_storage=args.band, update_scheme=scheme, method=method)
     lanes0 = st.steqr_query(w.n, w.batch, int(jobz), 0 if w.dtype == "f32" else 1,
                             prm0)["lanes_per_problem"]
     d, e = W.make_batch(w, replicate=(64 // lanes0) if args.replicate else 1)
@@ -197,7 +217,8 @@ def main() -> int:
         Q.copy_(torch.from_numpy(Z))
     info = torch.empty((nb,), dtype=torch.int32, device=dev)
     prm = st.make_params(lanes_per_problem=args.lanes, waves_per_block=args.waves,
-                         band_storage=args.band, update_scheme=scheme, back_transform=bt)
+                         band_storage=args.band, update_scheme=scheme, back_transform=bt,
+                         method=method)
     plan = st.steqr_query(n, nb, int(jobz), st.dtype_code(td.dtype), prm)
     stream = torch.cuda.current_stream()
 
@@ -229,7 +250,7 @@ def main() -> int:
     # secondary timing at the lanes-per-problem the workload list names
     named = None
     if (args.lanes == 0 and plan["lanes_per_problem"] != w.lanes and not args.replicate
-            and not args.no_named):
+            and not args.no_named and not method):
         prm_n = st.make_params(lanes_per_problem=w.lanes, waves_per_block=args.waves,
                                band_storage=1 if w.n <= 32 else 2, update_scheme=scheme,
                                back_transform=bt)
@@ -259,18 +280,21 @@ def main() -> int:
     cpu = None
     flops = None
     if not args.no_cpu:
-        cpu, stats = cpu_baseline(d, e, jobz, w.name, scheme, Z)
+        cpu, stats = cpu_baseline(d, e, jobz, w.name, scheme, Z, method)
         fin = np.isfinite(d).all(1) & np.isfinite(e).all(1)
-        flops = float(flops_per_matrix(stats[fin], n, jobz).sum())
+        if method:
+            flops = float(bisect_flops_per_matrix(stats[fin], n).sum())
+        else:
+            flops = float(flops_per_matrix(stats[fin], n, jobz).sum())
     dtype = w.dtype
     peak = PEAK_TFLOPS[dtype]
     roof = None
-    family = ("pc" if plan["band_storage"] == 3 else
+    family = ("bisect" if method else "pc" if plan["band_storage"] == 3 else
               ("wave" if plan["lanes_per_problem"] == 64 else
                ("chunkl" if plan["band_storage"] == 2 else "chunk")))
     if flops is not None:
         ach = flops / sec / 1e12
-        ctr = (None if (args.replicate or scheme or bt)
+        ctr = (None if (args.replicate or scheme or bt or method)
                else counters_from_profiles(w.name, jobz, family))
         roof = {"kernel": "steqr_%s_kernel<%s, N=%d, P=%d, %s>"
                           % (family, "float" if dtype == "f32" else "double", plan["padded_n"],
@@ -311,6 +335,7 @@ def main() -> int:
                    "waves_per_block": plan["waves_per_block"],
                    "update_scheme": args.scheme.upper(),
                    "back_transform": bt,
+                   "method": args.method.upper(),
                    "workgroups": plan["workgroups"],
                    "inputs": ("replicated per wavefront (lockstep ideal)" if args.replicate
                               else ("90% iid N(0,1) + 10% edge items" if w.edge_mix

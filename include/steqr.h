@@ -56,6 +56,7 @@ enum { STEQR_N = 0, STEQR_V = 1 };     /* jobz: values only / values+vectors */
 enum { STEQR_F32 = 0, STEQR_F64 = 1 }; /* dtype */
 enum { STEQR_EXP = 0, STEQR_PG = 1 };  /* update_scheme */
 enum { STEQR_SHIFT_LAPACK = 0, STEQR_SHIFT_CLOSED = 1 };  /* shift */
+enum { STEQR_METHOD_QR = 0, STEQR_METHOD_BISECT = 1 };    /* method */
 
 /* Options of steqr_batched_ex. Zero-initialised fields mean "default". */
 typedef struct steqr_params {
@@ -103,6 +104,21 @@ typedef struct steqr_params {
      * the result is the eigenvectors of A. Needs jobz == STEQR_V (-10
      * otherwise). */
     int back_transform;
+    /* Eigenvalue method. STEQR_METHOD_QR (0, default): the implicit QR/QL
+     * iteration above. STEQR_METHOD_BISECT (1), values only (jobz ==
+     * STEQR_N): Sturm-count bisection for every index 0..n-1, ascending
+     * (BatchLAS syev routing and tuning page, the values-only stebz
+     * solve): one lane per eigenvalue, each bisecting the Gershgorin
+     * interval until it is within max(ulp ||T||, 2 ulp |lambda|), the
+     * midpoint stops advancing or floor(log2((||T|| + pivmin)/pivmin)) + 2
+     * halvings are spent (the band is first scaled by an exact power of
+     * two to ||T|| in [0.5, 1)). info[b] is then the number of indices
+     * that ran out of halvings (0 for any finite input in practice), n for
+     * a band holding a NaN (all eigenvalues NaN). max_sweeps_per_n and
+     * no_sort do not apply; update_scheme, shift, band_storage,
+     * back_transform must be 0 and lanes_per_problem 0 or the padded order
+     * (-10 otherwise). */
+    int method;
 } steqr_params;
 
 /* Eigenvalues (jobz = STEQR_N) or eigenpairs (jobz = STEQR_V) of a batch of
@@ -128,7 +144,7 @@ int steqr_batched_ex(const void *d, const void *e, void *lambda, void *Q,
  * padded order (the compile-time order the kernel runs at, >= n), lanes per
  * problem P, rows of Q held per lane, wavefronts per workgroup, workgroups
  * for `batch` matrices and band storage (1 registers, 2 LDS, 3 LDS with
- * producer and consumer wavefronts). Returns 0 or
+ * producer and consumer wavefronts; for bisection 1 or 2). Returns 0 or
  * the same negative codes as steqr_batched_ex (-5/-7/-8/-10). Any output
  * pointer may be NULL. */
 int steqr_query(int n, int batch, int jobz, int dtype, const steqr_params *params,

@@ -99,7 +99,7 @@ def lib(path: Optional[str] = None) -> _ct.CDLL:
             f.argtypes = [_ct.c_int, _ct.c_void_p, _ct.c_void_p, ct, ct]
             f = getattr(L, "oracle_stebz_batched_" + sfx)
             f.restype = _ct.c_int
-            f.argtypes = [_ct.c_void_p] * 4 + [_ct.c_int, _ct.c_long]
+            f.argtypes = [_ct.c_void_p] * 5 + [_ct.c_int, _ct.c_long]
             f = getattr(L, "oracle_syev_batched_" + sfx)
             f.restype = _ct.c_int
             f.argtypes = [_ct.c_void_p] * 4 + [_ct.c_int, _ct.c_long, _ct.c_int, _ct.c_int,
@@ -306,10 +306,11 @@ def sturm_count(d: _np.ndarray, e: _np.ndarray, x: float, pivmin: float, libpath
         d.shape[0], d.ctypes.data, e2.ctypes.data, x, pivmin)
 
 
-def stebz(d: _np.ndarray, e: _np.ndarray, threads: int = 1, libpath=None
-          ) -> Tuple[_np.ndarray, _np.ndarray]:
+def stebz(d: _np.ndarray, e: _np.ndarray, threads: int = 1, libpath=None,
+          counts: bool = False):
     """Values-only bisection of a batch: (lam (batch, n) ascending, info
-    (batch,) = indices that ran out of halvings)."""
+    (batch,) = indices that ran out of halvings[, Sturm counts evaluated per
+    item (batch,) int64 when counts])."""
     d = _np.ascontiguousarray(d)
     e = _np.ascontiguousarray(e)
     batch, n = d.shape
@@ -317,14 +318,16 @@ def stebz(d: _np.ndarray, e: _np.ndarray, threads: int = 1, libpath=None
         raise ValueError("bad band shapes %s %s" % (d.shape, e.shape))
     lam = _np.empty_like(d)
     info = _np.zeros(batch, dtype=_np.int32)
+    cnt = _np.zeros(batch, dtype=_np.int64)
     if batch == 0 or n == 0:
-        return lam, info
+        return (lam, info, cnt) if counts else (lam, info)
     fn = getattr(lib(libpath), "oracle_stebz_batched_" + _sfx(d.dtype))
     it = d.itemsize
 
     def run(lo: int, hi: int) -> int:
         return fn(d.ctypes.data + lo * n * it, e.ctypes.data + lo * max(n - 1, 0) * it,
-                  lam.ctypes.data + lo * n * it, info.ctypes.data + lo * 4, n, hi - lo)
+                  lam.ctypes.data + lo * n * it, info.ctypes.data + lo * 4,
+                  cnt.ctypes.data + lo * 8, n, hi - lo)
 
     threads = max(1, min(int(threads), batch))
     cuts = [batch * k // threads for k in range(threads + 1)]
@@ -335,4 +338,4 @@ def stebz(d: _np.ndarray, e: _np.ndarray, threads: int = 1, libpath=None
             rcs = list(ex.map(lambda k: run(cuts[k], cuts[k + 1]), range(threads)))
     if any(rcs):
         raise ValueError("oracle rejected n=%d" % n)
-    return lam, info
+    return (lam, info, cnt) if counts else (lam, info)

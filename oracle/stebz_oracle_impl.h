@@ -50,9 +50,12 @@ int SFX(oracle_sturm_count)(int n, const REAL *d, const REAL *e2, REAL x, REAL p
 }
 
 /* All eigenvalues of one tridiagonal, ascending, by bisection (above).
- * Returns the number of indices that exhausted the halving budget. */
-int SFX(oracle_stebz_one)(int n, const REAL *d, const REAL *e, REAL *lam)
+ * Returns the number of indices that exhausted the halving budget; *counts
+ * (if non-NULL) receives the number of Sturm counts evaluated. */
+int SFX(oracle_stebz_one)(int n, const REAL *d, const REAL *e, REAL *lam, long long *counts)
 {
+    if (counts)
+        *counts = 0;
     const REAL ulp = (REAL)2 * R_EPS;
     REAL tn = (REAL)0;
     int hasnan = 0;
@@ -110,7 +113,9 @@ int SFX(oracle_stebz_one)(int n, const REAL *d, const REAL *e, REAL *lam)
     gl = gl - widen;
     gu = gu + widen;
     const REAL atol = ulp * tns;
-    const int itmax = (int)floor(log2(((double)tns + (double)pivmin) / (double)pivmin)) + 2;
+    int lg;
+    (void)frexp(((double)tns + (double)pivmin) / (double)pivmin, &lg);
+    const int itmax = (lg - 1) + 2; /* floor(log2(r)) = lg - 1 exactly */
     int info = 0;
     for (int k = 0; k < n; ++k) {
         REAL lo = gl, hi = gu;
@@ -134,6 +139,8 @@ int SFX(oracle_stebz_one)(int n, const REAL *d, const REAL *e, REAL *lam)
             else
                 hi = mid;
             ++it;
+            if (counts)
+                ++*counts;
         }
         lam[k] = ((lo + hi) / (REAL)2) * us;
     }
@@ -143,15 +150,16 @@ int SFX(oracle_stebz_one)(int n, const REAL *d, const REAL *e, REAL *lam)
 }
 
 /* Batched values-only bisection: d [batch][n], e [batch][n-1], lam
- * [batch][n] ascending, info [batch] or NULL. Returns 0, or -1 if n is
- * out of range. */
-int SFX(oracle_stebz_batched)(const REAL *d, const REAL *e, REAL *lam, int *info, int n,
-                              long batch)
+ * [batch][n] ascending, info [batch] or NULL, counts [batch] (Sturm counts
+ * evaluated per item) or NULL. Returns 0, or -1 if n is out of range. */
+int SFX(oracle_stebz_batched)(const REAL *d, const REAL *e, REAL *lam, int *info,
+                              long long *counts, int n, long batch)
 {
     if (n < 0 || n > 256)
         return -1;
     for (long b = 0; b < batch && n > 0; ++b) {
-        int inf = SFX(oracle_stebz_one)(n, d + b * n, e + b * (n - 1), lam + b * n);
+        int inf = SFX(oracle_stebz_one)(n, d + b * n, e + b * (n - 1), lam + b * n,
+                                        counts ? counts + b : 0);
         if (info)
             info[b] = inf;
     }

@@ -17,6 +17,7 @@ STEQR_N, STEQR_V = 0, 1
 STEQR_F32, STEQR_F64 = 0, 1
 STEQR_EXP, STEQR_PG = 0, 1
 STEQR_SHIFT_LAPACK, STEQR_SHIFT_CLOSED = 0, 1
+STEQR_METHOD_QR, STEQR_METHOD_BISECT = 0, 1
 STEQR_MAX_N = 64
 SYEV_MAX_N = 32
 
@@ -29,7 +30,8 @@ class steqr_params(ct.Structure):
                 ("band_storage", ct.c_int),
                 ("update_scheme", ct.c_int),
                 ("shift", ct.c_int),
-                ("back_transform", ct.c_int)]
+                ("back_transform", ct.c_int),
+                ("method", ct.c_int)]
 
 
 class SteqrError(RuntimeError):
@@ -77,10 +79,10 @@ def version() -> str:
 def make_params(max_sweeps_per_n: int = 0, sort: bool = True, lanes_per_problem: int = 0,
                 waves_per_block: int = 0, band_storage: int = 0,
                 update_scheme: int = 0, shift: int = 0,
-                back_transform: bool = False) -> steqr_params:
+                back_transform: bool = False, method: int = 0) -> steqr_params:
     return steqr_params(int(max_sweeps_per_n), 0 if sort else 1, int(lanes_per_problem),
                         int(waves_per_block), int(band_storage), int(update_scheme),
-                        int(shift), int(bool(back_transform)))
+                        int(shift), int(bool(back_transform)), int(method))
 
 
 def _ptr(x) -> Optional[int]:
@@ -139,7 +141,7 @@ def dtype_code(tdtype) -> int:
 def solve(d, e, jobz: bool = True, *, info: bool = False, sort: bool = True,
           max_sweeps_per_n: int = 0, lanes_per_problem: int = 0, waves_per_block: int = 0,
           band_storage: int = 0, update_scheme: int = 0, shift: int = 0, stream=None,
-          out: Optional[Tuple] = None, Z=None):
+          out: Optional[Tuple] = None, Z=None, method: int = 0):
     """Solve a batch held in device tensors d (batch, n), e (batch, n-1).
 
     Z: optional (batch, n, n) device basis for back-transformation; it is
@@ -169,7 +171,7 @@ def solve(d, e, jobz: bool = True, *, info: bool = False, sort: bool = True,
             raise ValueError("Z must be a contiguous (batch, n, n) device tensor of d's dtype")
         Q = Z
     prm = make_params(max_sweeps_per_n, sort, lanes_per_problem, waves_per_block, band_storage,
-                      update_scheme, shift, Z is not None)
+                      update_scheme, shift, Z is not None, method)
     rc = steqr_batched_ex(d, e, lam, Q, n, batch, STEQR_V if jobz else STEQR_N,
                           dtype_code(d.dtype), stream, inf, prm)
     if rc != 0:

@@ -115,6 +115,7 @@ int plan_launch(int n, int batch, int jobz, int dtype, const steqr_params* prm, 
         if (prm->no_sort != 0 && prm->no_sort != 1) return -10;
         if (prm->back_transform != 0 && prm->back_transform != 1) return -10;
         if (prm->back_transform == 1 && jobz != STEQR_V) return -10;
+        if (prm->method != STEQR_METHOD_QR && prm->method != STEQR_METHOD_BISECT) return -10;
     }
     Plan p{};
     p.waves = waves;
@@ -124,6 +125,24 @@ int plan_launch(int n, int batch, int jobz, int dtype, const steqr_params* prm, 
     }
     const int N = padded_order(n < 2 ? 2 : n);
     if (N < 0) return -5;  // order not provided by this build
+    if (prm && prm->method == STEQR_METHOD_BISECT) {
+        // values-only bisection: one lane per eigenvalue
+        if (jobz != STEQR_N || prm->update_scheme != 0 || prm->shift != 0 ||
+            prm->band_storage != 0 || prm->back_transform != 0 || (P != 0 && P != N))
+            return -10;
+        const Entry* ent = search(steqr::table_bisect(), dtype, N, N, STEQR_N,
+                                  (2 * N * (dtype == STEQR_F32 ? 4 : 8) / 4 <= 128) ? 1 : 2);
+        if (!ent) return -10;
+        p.entry = ent;
+        p.N = N;
+        p.P = N;
+        p.R = 0;
+        p.band = ent->band;
+        const int per_block = waves * (64 / N);
+        p.grid = batch > 0 ? (int)(((long)batch + per_block - 1) / per_block) : 0;
+        *out = p;
+        return 0;
+    }
     if (band == 0 || (N >= 64 && band == 1)) band = default_band(dtype, N, jobz);
     if (P == 0) P = default_lanes(dtype, N, jobz, band);
     const Entry* ent = find_entry(dtype, N, P, jobz, band, pg);
@@ -227,6 +246,7 @@ int syev_plan(int n, int batch, int jobz, int dtype, const steqr_params* prm, Pl
         if (prm->update_scheme != STEQR_EXP) return -10;
         if (prm->shift != STEQR_SHIFT_LAPACK && prm->shift != STEQR_SHIFT_CLOSED) return -10;
         if (prm->back_transform != 0) return -10;
+        if (prm->method != STEQR_METHOD_QR) return -10;
         if (prm->band_storage != 0 && prm->band_storage != 1) return -10;
         if (prm->no_sort != 0 && prm->no_sort != 1) return -10;
         if (prm->waves_per_block != 0) {

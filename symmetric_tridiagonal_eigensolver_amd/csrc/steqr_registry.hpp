@@ -9,6 +9,7 @@
 #include "steqr_wave.hpp"
 #include "steqr_chunkl.hpp"
 #include "steqr_pc.hpp"
+#include "steqr_bisect.hpp"
 
 namespace steqr {
 
@@ -93,6 +94,18 @@ hipError_t launch_pc(const KernelArgs& args, int grid, int block, hipStream_t st
     { DT, N, P, Q, 1, (int)Smem<T, N, P, (Q) != 0>::bytes_per_wave, \
       &launch_chunk<T, N, P, (Q) != 0, STEQR_INST_PG != 0> }
 
+// Values-only bisection: one lane per eigenvalue, N lanes per problem.
+template <typename T, int N>
+hipError_t launch_bisect(const KernelArgs& args, int grid, int block, hipStream_t stream) {
+    const size_t lds = (size_t)(block / 64) * SmemB<T, N>::bytes_per_wave;
+    hipLaunchKernelGGL((steqr_bisect_kernel<T, N>), dim3(grid), dim3(block), lds, stream, args);
+    return hipGetLastError();
+}
+
+#define STEQR_BISECT_ENTRY(DT, T, N) \
+    { DT, N, N, 0, (2 * N * (int)sizeof(T) / 4 <= 128) ? 1 : 2, \
+      (int)SmemB<T, N>::bytes_per_wave, &launch_bisect<T, N> }
+
 struct Table {
     const Entry* entries;
     int count;
@@ -116,6 +129,7 @@ Table table_lds_f64_pg();
 Table table_pc_pg();
 Table table_syev_f32();
 Table table_syev_f64();
+Table table_bisect();
 
 // table name for the scheme this unit is compiled for
 #if STEQR_INST_PG

@@ -218,3 +218,31 @@ def test_syev_argument_errors(st):
         assert L.syev_batched_ex(8, 8, 8, 16, 10, 1, 0, None, None, ctypes.byref(prm)) == -10
     # the closed-form shift is accepted
     assert st.syev_query(16, 10, 1, 0, st.make_params(shift=st.STEQR_SHIFT_CLOSED))["padded_n"] == 16
+
+
+# ---------------------------------------------------------------- bisection
+
+@pytest.mark.parametrize("n,dtype,N,band", [(1, 0, 4, 1), (3, 1, 4, 1), (16, 0, 16, 1),
+                                            (17, 1, 32, 1), (64, 0, 64, 1), (40, 1, 64, 2)])
+def test_bisect_plans(st, n, dtype, N, band):
+    q = st.steqr_query(n, 32768, 0, dtype, st.make_params(method=st.STEQR_METHOD_BISECT))
+    assert (q["padded_n"], q["lanes_per_problem"], q["rows_per_lane"], q["band_storage"]) == \
+        (N, N, 0, band)
+    assert q["workgroups"] == -(-32768 // (q["waves_per_block"] * 64 // N))
+
+
+def test_bisect_argument_errors(st):
+    L = st.lib()
+    bad = [st.make_params(method=2), st.make_params(method=-1),
+           st.make_params(method=1, update_scheme=st.STEQR_PG),
+           st.make_params(method=1, shift=1), st.make_params(method=1, band_storage=2),
+           st.make_params(method=1, lanes_per_problem=4)]
+    for prm in bad:
+        assert L.steqr_batched_ex(8, 8, 8, 8, 16, 10, 0, 0, None, None, ctypes.byref(prm)) == -10
+    # values only
+    prm = st.make_params(method=1)
+    assert L.steqr_batched_ex(8, 8, 8, 8, 16, 10, 1, 0, None, None, ctypes.byref(prm)) == -10
+    # the padded order as lanes is accepted
+    assert st.steqr_query(12, 10, 0, 0, st.make_params(method=1, lanes_per_problem=16))["padded_n"] == 16
+    # syev does not take the bisection method
+    assert L.syev_batched_ex(8, 8, 8, 16, 10, 0, 0, None, None, ctypes.byref(prm)) == -10

@@ -1,0 +1,111 @@
+"""GPU parity of the values-only bisection (steqr_params.method =
+STEQR_METHOD_BISECT) against the oracle's bisection on the same seeded
+inputs: status, eigenvalues within 16 n eps ||T||, ascending order; plus
+the exact power-of-two scaling the method has by construction, and
+agreement with the QR solve. Needs an MI355X; run with -m gpu."""
+import numpy as np
+import pytest
+
+import oracle
+import validate as V
+import workloads as W
+from parity import check, run_gpu
+
+pytestmark = pytest.mark.gpu
+
+BISECT = 1
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import symmetric_tridiagonal_eigensolver_amd  # noqa: F401  (fails loudly if not built)
+
+
+def run_bisect(d, e, **kw):
+    import torch
+    import symmetric_tridiagonal_eigensolver_amd as st
+    dev = torch.device("cuda:0")
+    td = torch.from_numpy(np.ascontiguousarray(d)).to(dev)
+    te = torch.from_numpy(np.ascontiguousarray(e)).to(dev)
+    lam, _, info = st.solve(td, te, False, info=True, method=BISECT, **kw)
+    torch.cuda.synchronize()
+    return lam.cpu().numpy(), None, info.cpu().numpy()
+
+
+def oracle_bisect(d, e):
+    lam, info = oracle.stebz(d, e, threads=8)
+    return lam, None, info
+
+
+@pytest.mark.parametrize("wname", list(W.WORKLOADS))
+def test_bisect_workload_small_batch(wname):
+    w = W.WORKLOADS[wname]
+    print("bisect case", wname, flush=True)
+    d, e = W.make_batch(w, 1000 + 13)
+    g = run_bisect(d, e)
+    o = oracle_bisect(d, e)
+    assert check(d, e, g, o, False) == []
+
+
+@pytest.mark.parametrize("wname", ["c2_f32_n16", "c4_f32_n32", "c4_f64_n32", "c5_f64_n64"])
+def test_bisect_full_batch_sampled(wname):
+    """The full batch in the benchmark's launch; the oracle on every 64th item."""
+    w = W.WORKLOADS[wname]
+    print("bisect full", wname, flush=True)
+    d, e = W.make_batch(w)
+    g = run_bisect(d, e)
+    items = np.arange(0, d.shape[0], 64)
+    o = oracle_bisect(d[items], e[items])
+    assert check(d, e, g, o, False, items=items) == []
+
+
+@pytest.mark.parametrize("dt", [np.float32, np.float64], ids=["f32", "f64"])
+def test_bisect_every_order(dt):
+    for n in range(1, 65):
+        print("bisect order", dt.__name__, n, flush=True)
+        d, e = W.random_batch(n, 67, dt, salt=400 + n)
+        g = run_bisect(d, e)
+        o = oracle_bisect(d, e)
+        assert check(d, e, g, o, False) == [], "n=%d" % n
+
+
+@pytest.mark.parametrize("kind", range(5), ids=W.EDGE_NAMES)
+@pytest.mark.parametrize("dt", [np.float32, np.float64], ids=["f32", "f64"])
+@pytest.mark.parametrize("n", [1, 2, 3, 16, 32, 64])
+def test_bisect_edge_items(kind, dt, n):
+    print("bisect edge", W.EDGE_NAMES[kind], dt.__name__, n, flush=True)
+    d, e = W.edge_batch(kind, n, 130, dt)
+    g = run_bisect(d, e)
+    o = oracle_bisect(d, e)
+    assert check(d, e, g, o, False) == [], W.EDGE_NAMES[kind]
+    if kind == W.EDGE_NAN:
+        assert np.all(g[2] == n) and np.all(np.isnan(g[0]))
+
+
+@pytest.mark.parametrize("dt", [np.float32, np.float64], ids=["f32", "f64"])
+@pytest.mark.parametrize("n", [5, 16, 64])
+def test_bisect_power_of_two_scaling_is_exact(dt, n):
+    d, e = W.random_batch(n, 200, dt, salt=76)
+    base = run_bisect(d, e)[0]
+    for j in (-50, 9, 40):
+        f = dt(2.0 ** j)
+        assert np.array_equal(run_bisect(d * f, e * f)[0], base * f), j
+
+
+@pytest.mark.parametrize("dt", [np.float32, np.float64], ids=["f32", "f64"])
+def test_bisect_agrees_with_qr_and_closed_forms(dt):
+    for n in (4, 16, 33, 64):
+        d, e = W.random_batch(n, 500, dt, salt=77)
+        g = run_bisect(d, e)
+        q = run_gpu(d, e, False)
+        assert not g[2].any() and not q[2].any()
+        assert V.sorted_err(g[0], q[0].astype(np.float64), d, e).max() <= V.tol_of(dt, n)
+        # Kac-Sylvester-Clement: eigenvalues -(n-1), -(n-3), ..., n-1
+        k = np.arange(1, n)
+        ce = np.sqrt(k * (n - k)).reshape(1, -1).astype(dt)
+        cl = run_bisect(np.zeros((1, n), dtype=dt), ce)[0][0]
+        ref = np.arange(-(n - 1), n, 2, dtype=np.float64)
+        assert np.abs(cl - ref).max() <= V.tol_of(dt, n) * (2 * ce.max())
