@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define STEQR_MAX_N 64
+#define STEQR_MAX_N 128
 
 enum { STEQR_N = 0, STEQR_V = 1 };     /* jobz: values only / values+vectors */
 enum { STEQR_F32 = 0, STEQR_F64 = 1 }; /* dtype */
@@ -77,11 +77,14 @@ typedef struct steqr_params {
     /* Where a chunked kernel keeps the band d, e during the solve:
      * 0 = tuned default, 1 = replicated in every lane's registers,
      * 2 = shared in LDS (frees registers for more rows of Q per lane),
-     * 3 = (orders 33..64 with eigenvectors) shared in LDS by one producer
+     * 3 = (orders 33..128 with eigenvectors) shared in LDS by one producer
      *     wavefront per workgroup that runs the chase for several problems
-     *     and logs its rotations, applied to Q by one consumer wavefront per
-     *     problem; lanes_per_problem then counts producer lanes.
-     * Orders above 32 always use LDS (1 means the default there). */
+     *     and logs its rotations, applied to Q by consumer wavefronts (one
+     *     per problem up to order 64; four per problem, two lanes per row,
+     *     at orders 65..128); lanes_per_problem then counts producer lanes.
+     * Orders above 32 always use LDS (1 means the default there); orders
+     * 65..128 without eigenvectors run the producer's algorithm alone in
+     * every wavefront (band storage 2). */
     int band_storage;
     /* Form of the implicit step (BatchLAS steqr algorithm page, "the two CTA
      * update schemes"): STEQR_EXP (0, default) writes each local similarity
@@ -117,7 +120,7 @@ typedef struct steqr_params {
      * a band holding a NaN (all eigenvalues NaN). max_sweeps_per_n and
      * no_sort do not apply; update_scheme, shift, band_storage,
      * back_transform must be 0 and lanes_per_problem 0 or the padded order
-     * (-10 otherwise). */
+     * (-10 otherwise). Built for orders up to 64. */
     int method;
 } steqr_params;
 

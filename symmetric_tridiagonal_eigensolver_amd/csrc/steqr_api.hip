@@ -12,7 +12,7 @@ using steqr::Entry;
 using steqr::Table;
 
 // Compile-time orders the build provides, smallest first.
-constexpr int kOrders[] = {4, 8, 16, 32, 64};
+constexpr int kOrders[] = {4, 8, 16, 32, 64, 128};
 
 int padded_order(int n) {
     for (int N : kOrders)
@@ -29,6 +29,7 @@ int padded_order(int n) {
 // SIMDs idle (n = 32 keeps two lanes). Orders 33..64 run one problem per
 // wavefront.
 int default_lanes(int dtype, int N, int jobz, int band) {
+    if (N == 128) return band == 3 ? 16 : 16;  // producer lanes per problem
     if (band == 3) return dtype == STEQR_F32 ? 16 : 4;  // producer lanes per problem
     if (N >= 64) return 64;
     if (jobz) {
@@ -51,6 +52,7 @@ const Entry* search(const Table& t, int dtype, int N, int P, int jobz, int band)
 }
 
 const Entry* find_entry(int dtype, int N, int P, int jobz, int band, int pg) {
+    if (N == 128) return search(pg ? steqr::table_big_pg() : steqr::table_big(), dtype, N, P, jobz, band);
     if (band == 3) return search(pg ? steqr::table_pc_pg() : steqr::table_pc(), dtype, N, P, jobz, band);
     if (N == 64) {
         if (band != 2) return nullptr;

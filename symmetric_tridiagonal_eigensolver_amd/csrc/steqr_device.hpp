@@ -132,16 +132,21 @@ struct Fp<double> {
 // ---------------------------------------------------------------- bit masks
 // Position masks over the off-diagonal index p (bit p <-> e_p).
 
+typedef unsigned __int128 u128;
+
 template <int N>
-using PosMask = typename std::conditional<(N > 32), uint64_t, uint32_t>::type;
+using PosMask = typename std::conditional<
+    (N > 64), u128, typename std::conditional<(N > 32), uint64_t, uint32_t>::type>::type;
 
 // bits [0, k), 0 <= k <= width
 template <typename M>
 __device__ __forceinline__ M bits_below(int k) {
     if constexpr (sizeof(M) == 4) {
         return (M)((1ull << k) - 1ull);
-    } else {
+    } else if constexpr (sizeof(M) == 8) {
         return k >= 64 ? ~(M)0 : (((M)1 << k) - (M)1);
+    } else {
+        return k >= 128 ? ~(M)0 : (((M)1 << k) - (M)1);
     }
 }
 
@@ -154,19 +159,32 @@ __device__ __forceinline__ M bit_range(int lo, int hi) {
 // index of the highest / lowest set bit (x != 0)
 template <typename M>
 __device__ __forceinline__ int msb(M x) {
-    if constexpr (sizeof(M) == 4) return 31 - __clz((int)x);
-    else return 63 - __clzll((long long)x);
+    if constexpr (sizeof(M) == 4) {
+        return 31 - __clz((int)x);
+    } else if constexpr (sizeof(M) == 8) {
+        return 63 - __clzll((long long)x);
+    } else {
+        const uint64_t hi = (uint64_t)(x >> 64), lo = (uint64_t)x;
+        return hi ? 127 - __clzll((long long)hi) : 63 - __clzll((long long)lo);
+    }
 }
 template <typename M>
 __device__ __forceinline__ int lsb(M x) {
-    if constexpr (sizeof(M) == 4) return __ffs((int)x) - 1;
-    else return __ffsll((long long)x) - 1;
+    if constexpr (sizeof(M) == 4) {
+        return __ffs((int)x) - 1;
+    } else if constexpr (sizeof(M) == 8) {
+        return __ffsll((long long)x) - 1;
+    } else {
+        const uint64_t hi = (uint64_t)(x >> 64), lo = (uint64_t)x;
+        return lo ? __ffsll((long long)lo) - 1 : 63 + __ffsll((long long)hi);
+    }
 }
 
 template <typename M>
 __device__ __forceinline__ int popc(M x) {
     if constexpr (sizeof(M) == 4) return __popc((unsigned)x);
-    else return __popcll((unsigned long long)x);
+    else if constexpr (sizeof(M) == 8) return __popcll((unsigned long long)x);
+    else return __popcll((unsigned long long)x) + __popcll((unsigned long long)(x >> 64));
 }
 
 // ---------------------------------------------------------------- arithmetic
@@ -294,27 +312,28 @@ __device__ __forceinline__ void sym2x2(T a, T b, T c, T& rt1, T& rt2, T& cs, T& 
     rt2 = c + t * b;
 }
 
-// Initial row `row` of Q [algo, eigenvector accumulation]: the identity row
-// without back-transformation; with it, row `row` of the caller's basis Z
-// (qb = the problem's n x n row-major block, in bounds). Rows and columns
-// at or beyond n are padding and always start as the identity, as do rows
-// of dead problems (ok = false). With n == N and a 16-byte aligned block
-// (`vec`) the row is read as whole 16-byte pieces.
-template <typename T, int N>
-__device__ __forceinline__ void load_basis_row(const T* __restrict__ qb, int n, int row, bool ok,
-                                               bool bt, bool vec, T (&q)[N]) {
+// Initial columns c0 .. c0+W-1 of row `row` of Q [algo, eigenvector
+// accumulation]: the identity row without back-transformation; with it, the
+// caller's basis Z (qb = the problem's n x n row-major block, in bounds).
+// Rows and columns at or beyond n are padding and always start as the
+// identity, as do rows of dead problems (ok = false). With n equal to the
+// compiled order and a 16-byte aligned block (`vec`) the row is read as
+// whole 16-byte pieces (c0 a multiple of 4).
+template <typename T, int W>
+__device__ __forceinline__ void load_basis_cols(const T* __restrict__ qb, int n, int row, int c0,
+                                                bool ok, bool bt, bool vec, T (&q)[W]) {
     const bool in = bt & ok & (row < n);
     if (!in) {
-        static_for<N>([&](auto J) {
+        static_for<W>([&](auto J) {
             constexpr int j = decltype(J)::value;
-            q[j] = (row == j) ? T(1) : T(0);
+            q[j] = (row == c0 + j) ? T(1) : T(0);
         });
         return;
     }
-    const T* src = qb + (long)row * n;
+    const T* src = qb + (long)row * n + c0;
     if (vec) {
         constexpr int V = 16 / sizeof(T);
-        static_for<N / V>([&](auto K) {
+        static_for<W / V>([&](auto K) {
             constexpr int k = decltype(K)::value;
             if constexpr (sizeof(T) == 4) {
                 const float4 v = *reinterpret_cast<const float4*>(src + k * 4);
@@ -329,13 +348,19 @@ __device__ __forceinline__ void load_basis_row(const T* __restrict__ qb, int n, 
             }
         });
     } else {
-        static_for<N>([&](auto J) {
+        static_for<W>([&](auto J) {
             constexpr int j = decltype(J)::value;
-            const int jc = j < n ? j : n - 1;
-            const T v = src[jc];
-            q[j] = (j < n) ? v : T(0);
+            const int jc = (c0 + j < n) ? j : n - 1 - c0;
+            const T v = src[jc > 0 ? jc : 0];
+            q[j] = (c0 + j < n) ? v : T(0);
         });
     }
+}
+
+template <typename T, int N>
+__device__ __forceinline__ void load_basis_row(const T* __restrict__ qb, int n, int row, bool ok,
+                                               bool bt, bool vec, T (&q)[N]) {
+    load_basis_cols<T, N>(qb, n, row, 0, ok, bt, vec, q);
 }
 
 }  // namespace steqr

@@ -18,6 +18,14 @@
 //  * W consumer wavefronts each hold the Q of 64/N problems (lane = row) and apply
 //    the logged rotations of the previous pass while the producer computes
 //    the next one (two log slots, one workgroup barrier per pass).
+// At order 128 a row of Q is split over two lanes of one wavefront (columns
+// 0..63 and 64..127, lanes l and l^32), so a consumer wavefront holds 32
+// rows and a problem takes four; the unrolled pass applies the rotations in
+// position order, so the lanes of the half a rotation falls in run it while
+// the others are masked, and the one rotation that straddles the halves
+// swaps the two boundary values across the lane pair. Without eigenvectors
+// (WANTQ false) every wavefront is a producer of its own problems and no
+// log is written.
 // The consumers' column updates are the same as the other kernels' and
 // their order of application is the producer's, so the results equal the
 // chunked kernels' up to the same rounding. The bands, the sort keys and
@@ -31,11 +39,14 @@
 namespace steqr {
 
 // W consumer wavefronts, each holding CQ = 64/N problems (lane = row of
-// one of them), so NP = W * CQ problems per workgroup.
+// one of them; at order 128 WPP = 4 wavefronts per problem, two lanes per
+// row), so NP = W * CQ / WPP problems per workgroup.
 template <typename T, int N, int W, int P>
 struct SmemPC {
-    static constexpr int CQ = 64 / N;                     // problems per consumer
-    static constexpr int NP = W * CQ;                     // problems per workgroup
+    static constexpr bool HALF = N > 64;                  // two lanes per row of Q
+    static constexpr int CQ = HALF ? 1 : 64 / N;          // problems per consumer
+    static constexpr int WPP = HALF ? 2 * N / 64 : 1;     // consumers per problem
+    static constexpr int NP = W * CQ / WPP;               // problems per workgroup
     static constexpr int CH = 64 / P;                     // producer chunks (>= NP)
     static constexpr int SLOT = 2 * N + 1;                // d[N], e[N], pad
     static constexpr size_t band_bytes = ((CH * SLOT * sizeof(T) + 15) / 16) * 16;
@@ -50,79 +61,88 @@ struct SmemPC {
     static constexpr size_t bytes = band_bytes + rot_bytes + hdr_bytes + rank_bytes + fin_bytes;
 };
 
-// OR over the P lanes of a chunk for 64-bit masks
-template <int P>
-__device__ __forceinline__ uint64_t chunk_or64(uint64_t v) {
-    const unsigned lo = chunk_or<P>((unsigned)v), hi = chunk_or<P>((unsigned)(v >> 32));
-    return ((uint64_t)hi << 32) | lo;
+// OR over the P lanes of a chunk for 64- and 128-bit masks
+template <int P, typename M>
+__device__ __forceinline__ M chunk_or_mask(M v) {
+    M out = 0;
+    static_for<(int)(sizeof(M) / 4)>([&](auto WW) {
+        constexpr int w = decltype(WW)::value;
+        out |= (M)chunk_or<P>((unsigned)(v >> (32 * w))) << (32 * w);
+    });
+    return out;
 }
 
-template <typename T, int N, int W, int P, bool PG>
-__global__ void __launch_bounds__((W + 1) * 64) steqr_pc_kernel(KernelArgs args) {
+// Values-only form (WANTQ false): the producer's algorithm alone, every
+// wavefront of the workgroup a producer of its own 64/P problems.
+template <typename T, int N, int P>
+struct SmemPV {
+    static constexpr int CH = 64 / P;
+    static constexpr int SLOT = 2 * N + 1;
+    static constexpr size_t band_bytes = ((CH * SLOT * sizeof(T) + 15) / 16) * 16;
+    static constexpr size_t rank_bytes = ((CH * N * sizeof(int) + 15) / 16) * 16;
+    static constexpr size_t bytes_per_wave = band_bytes + rank_bytes;
+};
+
+enum { PC_CTRL_PASS = 1, PC_CTRL_END = 2 };
+
+// Consumer wavefront: hold rows of Q (lane = row, or at order 128 half a
+// row: columns c0 .. c0+QW-1 with the other half in lane ^ 32) and apply the
+// producer's logged rotations pass by pass; at the end store the rows with
+// the sort's column permutation.
+template <typename T, int N, int W, int P>
+__device__ __forceinline__ void consume(const KernelArgs& args, int lane, int wave, long first,
+                                        const T* rot, const int* hdr, const int* ranks,
+                                        const int* fin) {
     using S = SmemPC<T, N, W, P>;
-    constexpr int CQ = S::CQ;
-    constexpr int NP = S::NP;
-    // At order 32 (two problems per consumer) this split measured slower
-    // than the LDS-band chunked kernel, so only order 64 is built.
-    static_assert(N == 64 && CQ == 1, "the producer-consumer kernel is for order 64");
-    static_assert(P >= 2 && (64 % P) == 0 && (N % P) == 0 && 64 / P >= NP, "P lanes per chunk");
-    constexpr int CH = 64 / P;
-    constexpr int K = N / P;  // positions per producer lane
-    using M = PosMask<N>;
     using F = Fp<T>;
-    enum { ST_OPEN = 0, ST_ITER = 1, ST_DONE = 2 };
-    enum { CTRL_PASS = 1, CTRL_END = 2 };
-
-    extern __shared__ __align__(16) unsigned char smem_raw[];
-    T* const band = reinterpret_cast<T*>(smem_raw);
-    T* const rot = reinterpret_cast<T*>(smem_raw + S::band_bytes);
-    int* const hdr = reinterpret_cast<int*>(smem_raw + S::band_bytes + S::rot_bytes);
-    int* const ranks =
-        reinterpret_cast<int*>(smem_raw + S::band_bytes + S::rot_bytes + S::hdr_bytes);
-    int* const fin = reinterpret_cast<int*>(smem_raw + S::band_bytes + S::rot_bytes +
-                                            S::hdr_bytes + S::rank_bytes);
-
-    const T* __restrict__ gd = static_cast<const T*>(args.d);
-    const T* __restrict__ ge = static_cast<const T*>(args.e);
-    T* __restrict__ glam = static_cast<T*>(args.lam);
+    constexpr bool HALF = S::HALF;
+    constexpr int NP = S::NP;
+    constexpr int QW = HALF ? N / 2 : N;  // columns held per lane
     T* __restrict__ gq = static_cast<T*>(args.q);
     const int n = args.n;
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const long first = (long)blockIdx.x * NP;  // the workgroup's first problem
-
-    if (wave < W) {
-        // ============================================================ consumer
-        // lane = row `row` of problem `pi`
-        const int pi = wave * CQ + lane / N;
-        const int row = lane % N;
-        const long prob = first + pi;
-        const bool live = prob < (long)args.batch;
-        // the identity, or with back-transformation [algo, eigenvector
-        // accumulation] row `row` of the caller's basis
-        T q[N];
-        {
-            const bool vec = (n == N) & ((reinterpret_cast<uintptr_t>(gq) & 15) == 0);
-            const long pc = live ? prob : (long)args.batch - 1;
-            load_basis_row<T, N>(gq + pc * n * n, n, row, live, args.back_transform != 0, vec, q);
-        }
-        // The producer mirrors a problem (positions p <-> N-1-p, Q's columns
-        // included) while a block that converges at its top is reduced.
-        // Instead of reversing its registers, the consumer tracks the
-        // orientation and applies a rotation at mirrored position p to the
-        // columns (N-1-p, N-2-p), which is the same update.
-        int orient = 0;
-        int slot = 0;
-        while (true) {
-            __syncthreads();
-            const int* h = hdr + slot * S::HDR;
-            if (h[0] == CTRL_END) break;
-            orient ^= h[1 + 3 * pi];
-            const int s = h[2 + 3 * pi];
-            const int steps = h[3 + 3 * pi];
-            const T* lg = rot + (size_t)(slot * (NP + 1) + pi) * (N - 1) * 2;
-            if (steps > 0) {
-                const int me = s + steps;
+    const int pi = HALF ? wave / S::WPP : wave * S::CQ + lane / N;
+    const int hf = HALF ? (lane >> 5) : 0;
+    const int row = HALF ? (wave % S::WPP) * 32 + (lane & 31) : lane % N;
+    const int c0 = hf * QW;
+    const long prob = first + pi;
+    const bool live = prob < (long)args.batch;
+    // the identity, or with back-transformation [algo, eigenvector
+    // accumulation] the caller's basis
+    T q[QW];
+    {
+        const bool vec = (n == N) & ((reinterpret_cast<uintptr_t>(gq) & 15) == 0);
+        const long pc = live ? prob : (long)args.batch - 1;
+        load_basis_cols<T, QW>(gq + pc * n * n, n, row, c0, live, args.back_transform != 0, vec,
+                               q);
+    }
+    // the rotation straddling the halves (columns QW-1 and QW): the pair of
+    // lanes swaps its boundary values; `lead` is the lane whose value is the
+    // rotation's first operand
+    auto straddle = [&](bool lead, T c, T sn) __attribute__((always_inline)) {
+        const T mine = hf == 0 ? q[QW - 1] : q[0];
+        const T other = __shfl_xor(mine, 32, 64);
+        const T upd = lead ? F::fma(c, mine, sn * other) : F::fma(c, mine, -(sn * other));
+        if (hf == 0) q[QW - 1] = upd;
+        else q[0] = upd;
+    };
+    // The producer mirrors a problem (positions p <-> N-1-p, Q's columns
+    // included) while a block that converges at its top is reduced.
+    // Instead of reversing its registers, the consumer tracks the
+    // orientation and applies a rotation at mirrored position p to the
+    // columns (N-1-p, N-2-p), which is the same update.
+    int orient = 0;
+    int slot = 0;
+    while (true) {
+        __syncthreads();
+        const int* h = hdr + slot * S::HDR;
+        if (h[0] == PC_CTRL_END) break;
+        orient ^= h[1 + 3 * pi];
+        const int s = h[2 + 3 * pi];
+        const int steps = h[3 + 3 * pi];
+        const T* lg = rot + (size_t)(slot * (NP + 1) + pi) * (N - 1) * 2;
+        if (steps > 0) {
+            const int me = s + steps;
+            if constexpr (!HALF) {
                 if (orient == 0) {
                     static_for_while<N - 1>([&](auto I) {
                         constexpr int p = decltype(I)::value;
@@ -136,23 +156,115 @@ __global__ void __launch_bounds__((W + 1) * 64) steqr_pc_kernel(KernelArgs args)
                         return p + 1 < me;
                     });
                 }
+            } else {
+                // positions 0..QW-2 fall in the first half of the columns
+                // (second half when mirrored), QW-1 straddles, the rest fall
+                // in the other half: run the three parts in position order,
+                // each half under one lane mask
+                const int lead = orient;  // the half that holds positions 0..QW-2
+                if (hf == lead) {
+                    if (orient == 0) {
+                        static_for_while<QW - 1>([&](auto I) {
+                            constexpr int p = decltype(I)::value;
+                            if (p >= s) F::rot(q[p], q[p + 1], lg[2 * p], lg[2 * p + 1]);
+                            return p + 1 < me;
+                        });
+                    } else {
+                        static_for_while<QW - 1>([&](auto I) {
+                            constexpr int p = decltype(I)::value;
+                            if (p >= s)
+                                F::rot(q[QW - 1 - p], q[QW - 2 - p], lg[2 * p], lg[2 * p + 1]);
+                            return p + 1 < me;
+                        });
+                    }
+                }
+                if ((s <= QW - 1) & (QW - 1 < me))
+                    straddle(hf == lead, lg[2 * (QW - 1)], lg[2 * (QW - 1) + 1]);
+                if ((hf != lead) & (me > QW)) {
+                    const int s2 = s > QW ? s - QW : 0;
+                    const int me2 = me - QW;
+                    const T* lg2 = lg + 2 * QW;
+                    if (orient == 0) {
+                        static_for_while<QW - 1>([&](auto I) {
+                            constexpr int p = decltype(I)::value;
+                            if (p >= s2) F::rot(q[p], q[p + 1], lg2[2 * p], lg2[2 * p + 1]);
+                            return p + 1 < me2;
+                        });
+                    } else {
+                        static_for_while<QW - 1>([&](auto I) {
+                            constexpr int p = decltype(I)::value;
+                            if (p >= s2)
+                                F::rot(q[QW - 1 - p], q[QW - 2 - p], lg2[2 * p], lg2[2 * p + 1]);
+                            return p + 1 < me2;
+                        });
+                    }
+                }
             }
-            slot ^= 1;
         }
-        __syncthreads();
-        // every block is closed, hence un-mirrored, by now (orient ^ fin is
-        // 0); a remaining reversal would be folded into the column index
-        const bool rev = (orient ^ fin[pi]) != 0;
-        if (live & (row < n)) {
-            const int* rk = ranks + pi * N;
-            T* qrow = gq + prob * (long)n * n + (long)row * n;
-            static_for<N>([&](auto J) {
-                constexpr int j = decltype(J)::value;
-                const int jj = rev ? N - 1 - j : j;
-                if (jj < n) qrow[rk[jj]] = q[j];
-            });
+        slot ^= 1;
+    }
+    __syncthreads();
+    // every block is closed, hence un-mirrored, by now (orient ^ fin is
+    // 0); a remaining reversal would be folded into the column index
+    const bool rev = (orient ^ fin[pi]) != 0;
+    if (live & (row < n)) {
+        const int* rk = ranks + pi * N;
+        T* qrow = gq + prob * (long)n * n + (long)row * n;
+        static_for<QW>([&](auto J) {
+            constexpr int j = decltype(J)::value;
+            const int jg = c0 + j;
+            const int jj = rev ? N - 1 - jg : jg;
+            if (jj < n) qrow[rk[jj]] = q[j];
+        });
+    }
+}
+
+template <typename T, int N, int W, int P, bool PG, bool WANTQ = true>
+__global__ void __launch_bounds__(WANTQ ? (W + 1) * 64 : 256) steqr_pc_kernel(KernelArgs args) {
+    using S = SmemPC<T, N, W, P>;
+    constexpr bool HALF = S::HALF;
+    constexpr int WPP = S::WPP;
+    constexpr int CH = 64 / P;
+    // problems of one producer wavefront
+    constexpr int NP = WANTQ ? S::NP : CH;
+    // At order 32 (two problems per consumer) this split measured slower
+    // than the LDS-band chunked kernel, so orders 64 and 128 are built.
+    static_assert(N == 64 || N == 128, "the producer-consumer kernel is for orders 64 and 128");
+    static_assert(!WANTQ || (W % WPP) == 0, "whole problems per workgroup");
+    static_assert(P >= 2 && (64 % P) == 0 && (N % P) == 0 && 64 / P >= NP, "P lanes per chunk");
+    constexpr int K = N / P;  // positions per producer lane
+    using M = PosMask<N>;
+    using F = Fp<T>;
+    enum { ST_OPEN = 0, ST_ITER = 1, ST_DONE = 2 };
+
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    using SV = SmemPV<T, N, P>;
+    unsigned char* const base = WANTQ ? smem_raw : smem_raw + (size_t)wave * SV::bytes_per_wave;
+    T* const band = reinterpret_cast<T*>(base);
+    T* const rot = reinterpret_cast<T*>(smem_raw + S::band_bytes);
+    int* const hdr = reinterpret_cast<int*>(smem_raw + S::band_bytes + S::rot_bytes);
+    int* const ranks = WANTQ ? reinterpret_cast<int*>(smem_raw + S::band_bytes + S::rot_bytes +
+                                                      S::hdr_bytes)
+                             : reinterpret_cast<int*>(base + SV::band_bytes);
+    int* const fin = reinterpret_cast<int*>(smem_raw + S::band_bytes + S::rot_bytes +
+                                            S::hdr_bytes + S::rank_bytes);
+
+    const T* __restrict__ gd = static_cast<const T*>(args.d);
+    const T* __restrict__ ge = static_cast<const T*>(args.e);
+    T* __restrict__ glam = static_cast<T*>(args.lam);
+    T* __restrict__ gq = static_cast<T*>(args.q);
+    const int n = args.n;
+    // the first problem of the workgroup (with Q) or of this wavefront
+    const long first = WANTQ ? (long)blockIdx.x * NP
+                             : ((long)blockIdx.x * (blockDim.x >> 6) + wave) * CH;
+
+    if constexpr (WANTQ) {
+        if (wave < W) {
+            consume<T, N, W, P>(args, lane, wave, first, rot, hdr, ranks, fin);
+            return;
         }
-        return;
     }
 
     // ================================================================ producer
@@ -187,7 +299,7 @@ __global__ void __launch_bounds__((W + 1) * 64) steqr_pc_kernel(KernelArgs args)
             const int p = r + k * P;
             part |= (se[p] == T(0)) ? ((M)1 << p) : (M)0;
         });
-        zeromask = chunk_or64<P>(part);
+        zeromask = chunk_or_mask<P>(part);
     }
 
     int state = live ? ST_OPEN : ST_DONE;
@@ -313,7 +425,7 @@ __global__ void __launch_bounds__((W + 1) * 64) steqr_pc_kernel(KernelArgs args)
                     part |= negligible(se[p], sd[p], sd[p + 1 < N ? p + 1 : N - 1])
                                 ? ((M)1 << p) : (M)0;
             });
-            neg = chunk_or64<P>(part) | zeroed;
+            neg = chunk_or_mask<P>(part) | zeroed;
         }
         const M rng = bit_range<M>(bt, m - 1);
         const M nb = neg & rng;
@@ -344,7 +456,7 @@ __global__ void __launch_bounds__((W + 1) * 64) steqr_pc_kernel(KernelArgs args)
                         const int p = r + k * P;
                         part |= ((p < n - 1) & (se[p] != T(0))) ? ((M)1 << p) : (M)0;
                     });
-                    info = popc(chunk_or64<P>(part));
+                    info = popc(chunk_or_mask<P>(part));
                     info = info > 0 ? info : 1;
                 }
                 state = fail ? ST_DONE : ST_OPEN;
@@ -371,13 +483,15 @@ __global__ void __launch_bounds__((W + 1) * 64) steqr_pc_kernel(KernelArgs args)
         const unsigned steps = sweep ? (unsigned)(m - s) : (jac ? 1u : 0u);
         // hand the pass to the consumers: mirror parity, first position,
         // step count (all lanes of a chunk write the same words)
-        int* h = hdr + slot * S::HDR;
-        if (chunk < NP) {
-            h[1 + 3 * chunk] = flip;
-            h[2 + 3 * chunk] = s;
-            h[3 + 3 * chunk] = (int)steps;
+        if constexpr (WANTQ) {
+            int* h = hdr + slot * S::HDR;
+            if (chunk < NP) {
+                h[1 + 3 * chunk] = flip;
+                h[2 + 3 * chunk] = s;
+                h[3 + 3 * chunk] = (int)steps;
+            }
+            if (lane == 0) h[0] = PC_CTRL_PASS;
         }
-        if (lane == 0) h[0] = CTRL_PASS;
         flip = 0;
 
         // ------------------------------------------------------------ chase
@@ -423,8 +537,10 @@ __global__ void __launch_bounds__((W + 1) * 64) steqr_pc_kernel(KernelArgs args)
                     y = sn * e1;
                     cp = c;
                 }
-                lg[2 * p] = c;
-                lg[2 * p + 1] = sn;
+                if constexpr (WANTQ) {
+                    lg[2 * p] = c;
+                    lg[2 * p + 1] = sn;
+                }
             }
             d0 = d1;
             e0 = e1;
@@ -438,19 +554,23 @@ __global__ void __launch_bounds__((W + 1) * 64) steqr_pc_kernel(KernelArgs args)
         }
         __builtin_amdgcn_wave_barrier();
         jtot = (sweep & (mu != mu)) ? nmaxit : jtot;
-        __syncthreads();  // the log of this pass is complete
+        if constexpr (WANTQ) __syncthreads();  // the log of this pass is complete
         slot ^= 1;
     }
-    // no pass left: tell the consumers (their last pass was the previous slot)
-    if (lane == 0) hdr[slot * S::HDR] = CTRL_END;
-    __syncthreads();
+    if constexpr (WANTQ) {
+        // no pass left: tell the consumers (their last pass was the previous slot)
+        if (lane == 0) hdr[slot * S::HDR] = PC_CTRL_END;
+        __syncthreads();
+    }
 
     // closes of converged last blocks, the final mirror parity and the sort
     if (__any(pending)) {
         if (pending) close_block(false);
     }
     __builtin_amdgcn_wave_barrier();
-    if (chunk < NP) fin[chunk] = flip;
+    if constexpr (WANTQ) {
+        if (chunk < NP) fin[chunk] = flip;
+    }
     const bool sort_it = (args.do_sort != 0) & !failed;
     T myd[K];
     int myrank[K];
@@ -477,7 +597,7 @@ __global__ void __launch_bounds__((W + 1) * 64) steqr_pc_kernel(KernelArgs args)
         });
         if (args.info != nullptr && r == 0) args.info[prob] = info;
     }
-    __syncthreads();  // ranks and final parity are visible to the consumers
+    if constexpr (WANTQ) __syncthreads();  // ranks and final parity are visible to the consumers
 }
 
 }  // namespace steqr

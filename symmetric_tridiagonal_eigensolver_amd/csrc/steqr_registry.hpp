@@ -86,6 +86,19 @@ hipError_t launch_pc(const KernelArgs& args, int grid, int block, hipStream_t st
     return hipGetLastError();
 }
 
+// Values only at order 128: the producer's algorithm in every wavefront.
+template <typename T, int N, int P, bool PG>
+hipError_t launch_pcv(const KernelArgs& args, int grid, int block, hipStream_t stream) {
+    const size_t lds = (size_t)(block / 64) * SmemPV<T, N, P>::bytes_per_wave;
+    hipLaunchKernelGGL((steqr_pc_kernel<T, N, 0, P, PG, false>), dim3(grid), dim3(block), lds,
+                       stream, args);
+    return hipGetLastError();
+}
+
+#define STEQR_PCV_ENTRY(DT, T, N, P) \
+    { DT, N, P, 0, 2, (int)SmemPV<T, N, P>::bytes_per_wave, \
+      &launch_pcv<T, N, P, STEQR_INST_PG != 0> }
+
 #define STEQR_PC_ENTRY(DT, T, N, W, P) \
     { DT, N, P, 1, 3, (int)SmemPC<T, N, W, P>::bytes, \
       &launch_pc<T, N, W, P, STEQR_INST_PG != 0>, SmemPC<T, N, W, P>::NP, (W) + 1 }
@@ -127,6 +140,8 @@ Table table_wave_pg();
 Table table_lds_f32_pg();
 Table table_lds_f64_pg();
 Table table_pc_pg();
+Table table_big();
+Table table_big_pg();
 Table table_syev_f32();
 Table table_syev_f64();
 Table table_bisect();

@@ -240,7 +240,7 @@ def clement(n: int):
 def pin_solve(oracle, libpath: Optional[str] = None, quick: bool = False,
               scheme: int = 0, shift: int = 0) -> List[str]:
     out: List[str] = []
-    sizes = (3, 8, 13) if quick else (1, 2, 3, 5, 8, 13, 16)
+    sizes = (3, 8, 13) if quick else (1, 2, 3, 5, 8, 13, 16, 100)
     for dt in (np.float32, np.float64):
         for n in sizes:
             d, e = W.random_batch(n, 16 if quick else 48, dt, salt=5)
@@ -265,7 +265,7 @@ def pin_solve(oracle, libpath: Optional[str] = None, quick: bool = False,
             fro = (dd ** 2).sum(1) + 2 * (ee ** 2).sum(1)
             _fail(out, np.all(np.abs((lam64 ** 2).sum(1) - fro) <= 4 * n * tol * tn * tn),
                   "Frobenius invariant %s n=%d" % (dt.__name__, n))
-    for n in ((8, 16) if quick else (4, 8, 16, 32, 64)):
+    for n in ((8, 16) if quick else (4, 8, 16, 32, 64, 128)):
         d, e, ref = clement(n)
         for dt in (np.float32, np.float64):
             lam, Q, info, _ = oracle.steqr(d.astype(dt), e.astype(dt), True, libpath=libpath, scheme=scheme, shift=shift)

@@ -121,7 +121,7 @@ def test_query_band_storage(st):
     ((8, 8, 0, 8, 4, 10, 1, 0), -3),
     ((8, 8, 8, 0, 4, 10, 1, 0), -4),
     ((8, 8, 8, 8, -1, 10, 1, 0), -5),
-    ((8, 8, 8, 8, 65, 10, 1, 0), -5),
+    ((8, 8, 8, 8, 129, 10, 1, 0), -5),
     ((8, 8, 8, 8, 4, -1, 1, 0), -6),
     ((8, 8, 8, 8, 4, 10, 2, 0), -7),
     ((8, 8, 8, 8, 4, 10, 1, 5), -8),
