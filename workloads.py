@@ -61,6 +61,9 @@ WORKLOADS: Dict[str, Workload] = {
     "c4_f32_n32": Workload(4, "c4_f32_n32", "f32", 32, 32768, ("V", "N"), 32, True),
     "c4_f64_n32": Workload(4, "c4_f64_n32", "f64", 32, 32768, ("V", "N"), 32, True),
     "c5_f64_n64": Workload(5, "c5_f64_n64", "f64", 64, 16384, ("V",), 64),
+    # beyond the sub-group width: the work-group path's orders (65..128)
+    "w_f32_n128": Workload(6, "w_f32_n128", "f32", 128, 8192, ("V", "N"), 16),
+    "w_f64_n128": Workload(7, "w_f64_n128", "f64", 128, 8192, ("V", "N"), 16),
 }
 
 HEADLINE = "c2_f32_n16"
