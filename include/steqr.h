@@ -119,8 +119,8 @@ typedef struct steqr_params {
      * that ran out of halvings (0 for any finite input in practice), n for
      * a band holding a NaN (all eigenvalues NaN). max_sweeps_per_n and
      * no_sort do not apply; update_scheme, shift, band_storage,
-     * back_transform must be 0 and lanes_per_problem 0 or the padded order
-     * (-10 otherwise). Built for orders up to 64. */
+     * back_transform must be 0 and lanes_per_problem 0 or the lanes the
+     * kernel uses (the padded order, 64 at order 128; -10 otherwise). */
     int method;
 } steqr_params;
 

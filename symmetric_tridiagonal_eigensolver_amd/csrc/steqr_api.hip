@@ -129,18 +129,19 @@ int plan_launch(int n, int batch, int jobz, int dtype, const steqr_params* prm, 
     if (N < 0) return -5;  // order not provided by this build
     if (prm && prm->method == STEQR_METHOD_BISECT) {
         // values-only bisection: one lane per eigenvalue
+        const int L = N < 64 ? N : 64;  // lanes per problem
         if (jobz != STEQR_N || prm->update_scheme != 0 || prm->shift != 0 ||
-            prm->band_storage != 0 || prm->back_transform != 0 || (P != 0 && P != N))
+            prm->band_storage != 0 || prm->back_transform != 0 || (P != 0 && P != L))
             return -10;
-        const Entry* ent = search(steqr::table_bisect(), dtype, N, N, STEQR_N,
+        const Entry* ent = search(steqr::table_bisect(), dtype, N, L, STEQR_N,
                                   (2 * N * (dtype == STEQR_F32 ? 4 : 8) / 4 <= 128) ? 1 : 2);
         if (!ent) return -10;
         p.entry = ent;
         p.N = N;
-        p.P = N;
+        p.P = L;
         p.R = 0;
         p.band = ent->band;
-        const int per_block = waves * (64 / N);
+        const int per_block = waves * (64 / L);
         p.grid = batch > 0 ? (int)(((long)batch + per_block - 1) / per_block) : 0;
         *out = p;
         return 0;

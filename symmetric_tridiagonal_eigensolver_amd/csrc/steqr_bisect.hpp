@@ -4,7 +4,8 @@
 // exits on the tolerance, the halving budget or a stalled midpoint).
 //
 // Design (MI355X-first). One problem per chunk of N lanes (N = the padded
-// order), one eigenvalue index per lane: lane k of a chunk bisects the k-th
+// order; at order 128 one problem per wavefront with two indices, k and
+// k + 64, per lane), one eigenvalue index per lane: lane k of a chunk bisects the k-th
 // smallest eigenvalue with Sturm counts of its own, so the 64 lanes of a
 // wavefront run 64 independent bisections in lockstep with no exchange at
 // all after the set-up. Every bisection takes about the same number of
@@ -31,7 +32,7 @@ namespace steqr {
 
 template <typename T, int N>
 struct SmemB {
-    static constexpr int CH = 64 / N;
+    static constexpr int CH = N < 64 ? 64 / N : 1;
     static constexpr size_t bytes_per_wave = (size_t)CH * 2 * N * sizeof(T);
 };
 
@@ -57,10 +58,14 @@ __device__ __forceinline__ int chunk_sumi(int v) {
 
 template <typename T, int N>
 __global__ void __launch_bounds__(256) steqr_bisect_kernel(KernelArgs args) {
-    static_assert(N >= 2 && N <= 64 && (64 % N) == 0, "one lane per position");
+    // L lanes per problem, E = N / L positions and eigenvalue indices per
+    // lane (k, k + L, ...): one index per lane up to order 64, two at 128
+    constexpr int L = N < 64 ? N : 64;
+    constexpr int E = N / L;
+    static_assert(N >= 2 && N <= 128 && (64 % L) == 0 && E * L == N, "lanes per position");
     using F = Fp<T>;
     using S = SmemB<T, N>;
-    constexpr int CH = 64 / N;
+    constexpr int CH = 64 / L;
     // band in VGPRs unless it would take more than 128 of them
     constexpr bool REGS = 2 * N * (int)sizeof(T) / 4 <= 128;
     constexpr T ulp = sizeof(T) == 4 ? T(0x1p-23) : T(0x1p-52);
@@ -73,49 +78,65 @@ __global__ void __launch_bounds__(256) steqr_bisect_kernel(KernelArgs args) {
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int chunk = lane / N;
-    const int k = lane % N;  // position / eigenvalue index of this lane
+    const int chunk = lane / L;
+    const int k0 = lane % L;  // first position / eigenvalue index of this lane
     const long prob = ((long)blockIdx.x * (blockDim.x >> 6) + wave) * CH + chunk;
     const bool live = prob < (long)args.batch;
     const long pb = live ? prob : (long)args.batch - 1;
     T* const sdd = reinterpret_cast<T*>(smem_raw + (size_t)wave * S::bytes_per_wave) + chunk * 2 * N;
     T* const se2 = sdd + N;
+    const T inf = T(__builtin_inff());
 
     // ------------------------------------------------------------ set-up
-    const bool hasd = live & (k < n);
-    const bool hase = live & (k < n - 1);
-    T dk = T(0), ek = T(0), ekm = T(0);
-    if (hasd) dk = gd[pb * n + k];
-    if (hase) ek = ge[pb * (n - 1) + k];
-    if (hasd & (k >= 1)) ekm = ge[pb * (n - 1) + k - 1];
-    const T rk = F::abs(ekm) + F::abs(dk) + F::abs(ek);
+    T dk[E], ek[E], ekm[E];
+    bool hasd[E];
+    T rmax = T(0);
+    int nan_here = 0;
+    static_for<E>([&](auto J) {
+        constexpr int j = decltype(J)::value;
+        const int k = k0 + j * L;
+        hasd[j] = live & (k < n);
+        dk[j] = ek[j] = ekm[j] = T(0);
+        if (hasd[j]) dk[j] = gd[pb * n + k];
+        if (live & (k < n - 1)) ek[j] = ge[pb * (n - 1) + k];
+        if (hasd[j] & (k >= 1)) ekm[j] = ge[pb * (n - 1) + k - 1];
+        const T rk = F::abs(ekm[j]) + F::abs(dk[j]) + F::abs(ek[j]);
+        nan_here |= (rk != rk) ? 1 : 0;
+        rmax = F::max(rmax, rk);
+    });
     // NaN anywhere in the band (the butterflies below use fmax, which
     // drops NaNs, so they are counted on their own)
-    const int nnan = chunk_sumi<N>((rk != rk) ? 1 : 0);
-    const T tn = chunk_maxf<N>(rk);
+    const int nnan = chunk_sumi<L>(nan_here);
+    const T tn = chunk_maxf<L>(rmax);
     const bool zero = (nnan == 0) & (tn == T(0));
     const bool bad = nnan != 0;
     // exact power-of-two prescaling: tn * s in [0.5, 1)
     const int ex = (bad | zero) ? 0 : F::frexp_exp(tn);
     const T s = F::ldexp(T(1), -ex);
-    const T ds = dk * s;
-    const T es = ek * s;
-    const T esm = ekm * s;
-    const T e2 = es * es;
-    sdd[k] = ds;
-    se2[k] = e2;
+    T e2loc = T(0), gl_loc = inf, gu_loc = -inf, tn_loc = T(0);
+    static_for<E>([&](auto J) {
+        constexpr int j = decltype(J)::value;
+        const int k = k0 + j * L;
+        const T ds = dk[j] * s;
+        const T es = ek[j] * s;
+        const T esm = ekm[j] * s;
+        const T e2 = es * es;
+        sdd[k] = ds;
+        se2[k] = e2;
+        e2loc = F::max(e2loc, e2);
+        // Gershgorin interval over positions 0..n-1 (padding neutral)
+        const T rad = F::abs(esm) + F::abs(es);
+        gl_loc = hasd[j] ? -F::max(-gl_loc, -(ds - rad)) : gl_loc;
+        gu_loc = hasd[j] ? F::max(gu_loc, ds + rad) : gu_loc;
+        tn_loc = hasd[j] ? F::max(tn_loc, F::abs(ds) + rad) : tn_loc;
+    });
     __builtin_amdgcn_wave_barrier();
-    const T e2max = chunk_maxf<N>(e2);
+    const T e2max = chunk_maxf<L>(e2loc);
     const T pivmin = F::safmin * F::max(T(1), e2max);
-    // Gershgorin interval over positions 0..n-1 (padding lanes neutral)
-    const T rad = F::abs(esm) + F::abs(es);
-    const T inf = T(__builtin_inff());
-    const T gl0 = chunk_minf<N>(hasd ? ds - rad : inf);
-    const T gu0 = chunk_maxf<N>(hasd ? ds + rad : -inf);
-    const T tns = chunk_maxf<N>(hasd ? F::abs(ds) + rad : T(0));
+    const T gl0 = chunk_minf<L>(gl_loc);
+    const T gu0 = chunk_maxf<L>(gu_loc);
+    const T tns = chunk_maxf<L>(tn_loc);
     const T widen = T(2) * T(n) * ulp * tns + T(2) * pivmin;
-    T lo = gl0 - widen;
-    T hi = gu0 + widen;
     const T atol = ulp * tns;
     // floor(log2(r)) = e - 1 for r = f 2^e, f in [0.5, 1): exact
     const int itmax =
@@ -130,61 +151,98 @@ __global__ void __launch_bounds__(256) steqr_bisect_kernel(KernelArgs args) {
         });
     }
 
-    // Sturm count of the scaled band below x
-    auto count = [&](T x) __attribute__((always_inline)) {
-        int c = 0;
-        T q = T(0);
+    // Sturm counts of the scaled band below x[0..E) in one traversal
+    auto count = [&](const T (&x)[E], int (&c)[E]) __attribute__((always_inline)) {
+        T q[E];
+        static_for<E>([&](auto J) { c[decltype(J)::value] = 0; });
         static_for_while<N>([&](auto I) {
             constexpr int i = decltype(I)::value;
             const T di = REGS ? bd[i] : sdd[i];
-            if constexpr (i == 0) {
-                q = di - x;
-            } else {
-                const T ei = REGS ? be2[i - 1] : se2[i - 1];
-                q = F::fma(-ei, F::rcp(q), di - x);
-            }
-            q = (F::abs(q) < pivmin) ? -pivmin : q;
-            c += (q < T(0)) ? 1 : 0;
+            T ei = T(0);
+            if constexpr (i > 0) ei = REGS ? be2[i - 1] : se2[i - 1];
+            static_for<E>([&](auto J) {
+                constexpr int j = decltype(J)::value;
+                if constexpr (i == 0) {
+                    q[j] = di - x[j];
+                } else {
+                    q[j] = F::fma(-ei, F::rcp(q[j]), di - x[j]);
+                }
+                q[j] = (F::abs(q[j]) < pivmin) ? -pivmin : q[j];
+                c[j] += (q[j] < T(0)) ? 1 : 0;
+            });
             return i + 1 < n;  // uniform
         });
-        return c;
     };
 
     // ------------------------------------------------------------ bisection
-    bool done = !hasd | bad | zero;
-    int fail = 0, it = 0;
-    while (__builtin_amdgcn_ballot_w64(!done)) {
-        if (!done) {
-            const T big = F::max(F::abs(lo), F::abs(hi));
-            const T tol = F::max(T(2) * ulp * big, atol);
-            if (hi - lo <= tol) {
-                done = true;
-            } else if (it == itmax) {
-                done = true;
-                fail = 1;
-            } else {
-                const T mid = (lo + hi) * T(0.5);
-                if ((mid == lo) | (mid == hi)) {
-                    done = true;
-                } else {
-                    if (count(mid) <= k)
-                        lo = mid;
-                    else
-                        hi = mid;
-                    ++it;
+    T lo[E], hi[E];
+    bool done[E];
+    int fail = 0, it[E];
+    bool any_open = false;
+    static_for<E>([&](auto J) {
+        constexpr int j = decltype(J)::value;
+        lo[j] = gl0 - widen;
+        hi[j] = gu0 + widen;
+        done[j] = !hasd[j] | bad | zero;
+        it[j] = 0;
+        any_open |= !done[j];
+    });
+    while (__builtin_amdgcn_ballot_w64(any_open)) {
+        if (any_open) {
+            T mid[E];
+            bool step[E];
+            static_for<E>([&](auto J) {
+                constexpr int j = decltype(J)::value;
+                step[j] = false;
+                mid[j] = (lo[j] + hi[j]) * T(0.5);
+                if (!done[j]) {
+                    const T big = F::max(F::abs(lo[j]), F::abs(hi[j]));
+                    const T tol = F::max(T(2) * ulp * big, atol);
+                    if (hi[j] - lo[j] <= tol) {
+                        done[j] = true;
+                    } else if (it[j] == itmax) {
+                        done[j] = true;
+                        fail += 1;
+                    } else if ((mid[j] == lo[j]) | (mid[j] == hi[j])) {
+                        done[j] = true;
+                    } else {
+                        step[j] = true;
+                    }
                 }
+            });
+            bool any_step = false;
+            static_for<E>([&](auto J) { any_step |= step[decltype(J)::value]; });
+            if (any_step) {
+                int c[E];
+                count(mid, c);
+                static_for<E>([&](auto J) {
+                    constexpr int j = decltype(J)::value;
+                    const int k = k0 + j * L;
+                    if (step[j]) {
+                        if (c[j] <= k)
+                            lo[j] = mid[j];
+                        else
+                            hi[j] = mid[j];
+                        ++it[j];
+                    }
+                });
             }
+            any_open = false;
+            static_for<E>([&](auto J) { any_open |= !done[decltype(J)::value]; });
         }
     }
 
     // ------------------------------------------------------------ store
     const T us = F::ldexp(T(1), ex);
-    T lam = ((lo + hi) * T(0.5)) * us;
-    lam = zero ? T(0) : lam;
-    lam = bad ? F::qnan() : lam;
-    if (hasd) glam[prob * n + k] = lam;
-    const int nfail = chunk_sumi<N>(fail);
-    if (live & (k == 0) & (args.info != nullptr)) args.info[prob] = bad ? n : nfail;
+    static_for<E>([&](auto J) {
+        constexpr int j = decltype(J)::value;
+        T lam = ((lo[j] + hi[j]) * T(0.5)) * us;
+        lam = zero ? T(0) : lam;
+        lam = bad ? F::qnan() : lam;
+        if (hasd[j]) glam[prob * n + k0 + j * L] = lam;
+    });
+    const int nfail = chunk_sumi<L>(fail);
+    if (live & (k0 == 0) & (args.info != nullptr)) args.info[prob] = bad ? n : nfail;
 }
 
 }  // namespace steqr

@@ -107,7 +107,8 @@ hipError_t launch_pcv(const KernelArgs& args, int grid, int block, hipStream_t s
     { DT, N, P, Q, 1, (int)Smem<T, N, P, (Q) != 0>::bytes_per_wave, \
       &launch_chunk<T, N, P, (Q) != 0, STEQR_INST_PG != 0> }
 
-// Values-only bisection: one lane per eigenvalue, N lanes per problem.
+// Values-only bisection: one lane per eigenvalue index (two at order 128),
+// min(N, 64) lanes per problem.
 template <typename T, int N>
 hipError_t launch_bisect(const KernelArgs& args, int grid, int block, hipStream_t stream) {
     const size_t lds = (size_t)(block / 64) * SmemB<T, N>::bytes_per_wave;
@@ -116,7 +117,7 @@ hipError_t launch_bisect(const KernelArgs& args, int grid, int block, hipStream_
 }
 
 #define STEQR_BISECT_ENTRY(DT, T, N) \
-    { DT, N, N, 0, (2 * N * (int)sizeof(T) / 4 <= 128) ? 1 : 2, \
+    { DT, N, (N) < 64 ? (N) : 64, 0, (2 * N * (int)sizeof(T) / 4 <= 128) ? 1 : 2, \
       (int)SmemB<T, N>::bytes_per_wave, &launch_bisect<T, N> }
 
 struct Table {

@@ -223,12 +223,14 @@ def test_syev_argument_errors(st):
 # ---------------------------------------------------------------- bisection
 
 @pytest.mark.parametrize("n,dtype,N,band", [(1, 0, 4, 1), (3, 1, 4, 1), (16, 0, 16, 1),
-                                            (17, 1, 32, 1), (64, 0, 64, 1), (40, 1, 64, 2)])
+                                            (17, 1, 32, 1), (64, 0, 64, 1), (40, 1, 64, 2),
+                                            (65, 0, 128, 2), (128, 1, 128, 2)])
 def test_bisect_plans(st, n, dtype, N, band):
     q = st.steqr_query(n, 32768, 0, dtype, st.make_params(method=st.STEQR_METHOD_BISECT))
+    L = min(N, 64)
     assert (q["padded_n"], q["lanes_per_problem"], q["rows_per_lane"], q["band_storage"]) == \
-        (N, N, 0, band)
-    assert q["workgroups"] == -(-32768 // (q["waves_per_block"] * 64 // N))
+        (N, L, 0, band)
+    assert q["workgroups"] == -(-32768 // (q["waves_per_block"] * 64 // L))
 
 
 def test_bisect_argument_errors(st):

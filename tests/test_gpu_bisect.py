@@ -40,8 +40,7 @@ def oracle_bisect(d, e):
     return lam, None, info
 
 
-# the bisection kernel is built for orders up to 64
-BISECT_WORKLOADS = [k for k, w in W.WORKLOADS.items() if w.n <= 64]
+BISECT_WORKLOADS = list(W.WORKLOADS)
 
 
 @pytest.mark.parametrize("wname", BISECT_WORKLOADS)
@@ -54,7 +53,8 @@ def test_bisect_workload_small_batch(wname):
     assert check(d, e, g, o, False) == []
 
 
-@pytest.mark.parametrize("wname", ["c2_f32_n16", "c4_f32_n32", "c4_f64_n32", "c5_f64_n64"])
+@pytest.mark.parametrize("wname", ["c2_f32_n16", "c4_f32_n32", "c4_f64_n32", "c5_f64_n64",
+                                   "w_f32_n128", "w_f64_n128"])
 def test_bisect_full_batch_sampled(wname):
     """The full batch in the benchmark's launch; the oracle on every 64th item."""
     w = W.WORKLOADS[wname]
@@ -68,7 +68,7 @@ def test_bisect_full_batch_sampled(wname):
 
 @pytest.mark.parametrize("dt", [np.float32, np.float64], ids=["f32", "f64"])
 def test_bisect_every_order(dt):
-    for n in range(1, 65):
+    for n in list(range(1, 65)) + [65, 70, 96, 127, 128]:
         print("bisect order", dt.__name__, n, flush=True)
         d, e = W.random_batch(n, 67, dt, salt=400 + n)
         g = run_bisect(d, e)
@@ -78,7 +78,7 @@ def test_bisect_every_order(dt):
 
 @pytest.mark.parametrize("kind", range(5), ids=W.EDGE_NAMES)
 @pytest.mark.parametrize("dt", [np.float32, np.float64], ids=["f32", "f64"])
-@pytest.mark.parametrize("n", [1, 2, 3, 16, 32, 64])
+@pytest.mark.parametrize("n", [1, 2, 3, 16, 32, 64, 100, 128])
 def test_bisect_edge_items(kind, dt, n):
     print("bisect edge", W.EDGE_NAMES[kind], dt.__name__, n, flush=True)
     d, e = W.edge_batch(kind, n, 130, dt)
@@ -90,7 +90,7 @@ def test_bisect_edge_items(kind, dt, n):
 
 
 @pytest.mark.parametrize("dt", [np.float32, np.float64], ids=["f32", "f64"])
-@pytest.mark.parametrize("n", [5, 16, 64])
+@pytest.mark.parametrize("n", [5, 16, 64, 128])
 def test_bisect_power_of_two_scaling_is_exact(dt, n):
     d, e = W.random_batch(n, 200, dt, salt=76)
     base = run_bisect(d, e)[0]
@@ -101,7 +101,7 @@ def test_bisect_power_of_two_scaling_is_exact(dt, n):
 
 @pytest.mark.parametrize("dt", [np.float32, np.float64], ids=["f32", "f64"])
 def test_bisect_agrees_with_qr_and_closed_forms(dt):
-    for n in (4, 16, 33, 64):
+    for n in (4, 16, 33, 64, 128):
         d, e = W.random_batch(n, 500, dt, salt=77)
         g = run_bisect(d, e)
         q = run_gpu(d, e, False)
