@@ -115,11 +115,22 @@ def cpu_baseline(d: np.ndarray, e: np.ndarray, jobz: bool, wname: str, scheme: i
         times.append(time.perf_counter() - t)
     tmed = statistics.median(times)
     nb = d.shape[0]
+    # one-thread figure on a bounded prefix of the batch
+    m1 = min(nb, 2048)
+    t = time.perf_counter()
+    if method == 1:
+        oracle.stebz(d[:m1], e[:m1], threads=1)
+    else:
+        oracle.steqr(d[:m1], e[:m1], jobz, threads=1, scheme=scheme,
+                     Z=None if Z is None else Z[:m1])
+    t1 = time.perf_counter() - t
     return {
         "value": nb / tmed, "unit": "matrices/s", "cores": cores, "kind": "oracle",
         "us_per_matrix": tmed / nb * 1e6,
         "sample": "full %s batch (%d matrices), median of 3 runs on %d threads"
                   % (wname, nb, cores),
+        "one_thread_us_per_matrix": t1 / m1 * 1e6,
+        "one_thread_sample": "first %d matrices, one run on 1 thread" % m1,
     }, stats
 
 
@@ -147,6 +158,8 @@ def main() -> int:
                     help="Q holds a basis on entry (seeded random orthogonal) that the "
                          "rotations right-multiply in place; needs --jobz V")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-saturation", action="store_true",
+                    help="skip the saturation check (the same kernel at twice the batch)")
     ap.add_argument("--no-named", action="store_true",
                     help="skip the secondary timing at the configuration's named lanes")
     ap.add_argument("--replicate", action="store_true",
@@ -247,6 +260,45 @@ def main() -> int:
     ms = start.elapsed_time(stop) / args.steps  # mean kernel duration (back-to-back launches)
     sec = ms / 1e3
 
+    # spread: five short rounds of back-to-back launches
+    rounds = []
+    kr = max(5, args.steps // 10)
+    for _ in range(5):
+        start.record(stream)
+        for _ in range(kr):
+            step()
+        stop.record(stream)
+        torch.cuda.synchronize()
+        rounds.append(start.elapsed_time(stop) / kr)
+    spread = {"rounds": 5, "launches_per_round": kr, "ms_min": min(rounds),
+              "ms_max": max(rounds)}
+
+    # saturation: per-matrix time at twice the batch (the batch repeated)
+    saturation = None
+    if not args.replicate and not bt and not args.no_named and not args.no_saturation:
+        td2 = torch.cat([td, td])
+        te2 = torch.cat([te, te])
+        lam2 = torch.empty_like(td2)
+        Q2 = torch.empty((2 * nb, n, n), dtype=td.dtype, device=dev) if jobz else None
+        info2 = torch.empty((2 * nb,), dtype=torch.int32, device=dev)
+
+        def step2():
+            rc = st.steqr_batched_ex(td2, te2, lam2, Q2, n, 2 * nb, int(jobz),
+                                     st.dtype_code(td.dtype), stream, info2, prm)
+            if rc != 0:
+                raise st.SteqrError(rc, "steqr_batched_ex")
+        step2()
+        torch.cuda.synchronize()
+        start.record(stream)
+        for _ in range(kr):
+            step2()
+        stop.record(stream)
+        torch.cuda.synchronize()
+        ms2 = start.elapsed_time(stop) / kr
+        saturation = {"batch": 2 * nb, "ms_per_step": ms2,
+                      "us_per_matrix_ratio_2x_over_1x": (ms2 / (2 * nb)) / (ms / nb)}
+        del td2, te2, lam2, Q2, info2
+
     # secondary timing at the lanes-per-problem the workload list names
     named = None
     if (args.lanes == 0 and plan["lanes_per_problem"] != w.lanes and not args.replicate
@@ -312,6 +364,14 @@ def main() -> int:
                                 "source": "rocprofv3 SQ_INSTS_VALU_FLOPS_FP%s" % dtype[1:]}
         if ctr is not None and ctr.get("valu_insts_replicated"):
             roof["divergence"] = ctr["valu_insts_per_launch"] / ctr["valu_insts_replicated"]
+        rv = (ctr or {}).get("raw", {}).get("valu")
+        if rv and rv.get("SQ_BUSY_CYCLES") and rv.get("SQ_ACTIVE_INST_VALU"):
+            # VALU busy: 4 cycles per wave64 instruction over every SIMD's
+            # cycles (SQ_BUSY_CYCLES sums 32 shader engines); lane use: active
+            # lanes per VALU instruction
+            roof["valu_busy"] = rv["SQ_INSTS_VALU"] * 4.0 / (1024.0 * rv["SQ_BUSY_CYCLES"] / 32.0)
+            roof["valu_lane_utilisation"] = (rv["SQ_THREAD_CYCLES_VALU"]
+                                             / (64.0 * rv["SQ_ACTIVE_INST_VALU"]))
     bpm = bytes_per_matrix(n, d.itemsize, jobz, bt)
     out = {
         "metric": "matrices/sec (us/matrix) float n=16 jobz=V; % FP32 VALU peak",
@@ -341,6 +401,8 @@ def main() -> int:
                               else ("90% iid N(0,1) + 10% edge items" if w.edge_mix
                                     else "d,e iid N(0,1)")) + ", seed 1234"},
         "roofline": roof,
+        "spread": spread,
+        "saturation": saturation,
         "at_named_lanes": named,
         "hbm": {"algorithmic_bytes_per_launch": bpm * nb,
                 "achieved_GBs": bpm * nb / sec / 1e9, "peak_GBs": HBM_PEAK_GBS},
