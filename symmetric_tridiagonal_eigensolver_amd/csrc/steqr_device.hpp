@@ -38,6 +38,17 @@ __device__ __forceinline__ void static_for_while(Fn&& fn) {
     if constexpr (COUNT > 0) static_for_while_impl(fn, std::make_integer_sequence<int, COUNT>{});
 }
 
+// Largest value over the 64 lanes of the wavefront (every lane active), as
+// a wave-uniform scalar: bounds a static loop with one scalar branch.
+__device__ __forceinline__ int wave_max_uniform(int v) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int w = __shfl_xor(v, o, 64);
+        v = v > w ? v : w;
+    }
+    return __builtin_amdgcn_readfirstlane(v);
+}
+
 // Precision-dependent constants and hardware helpers.
 //  eps2    = eps^2 with eps the unit roundoff (2^-24 / 2^-53)  [algo, deflation]
 //  safmin  = smallest normal number                            [algo, deflation]

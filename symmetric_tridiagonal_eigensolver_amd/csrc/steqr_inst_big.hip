@@ -7,7 +7,10 @@ namespace steqr {
 
 static const Entry kEntries[] = {
     STEQR_PC_ENTRY(0, float, 128, 12, 16),
+    STEQR_PC_ENTRY(0, float, 128, 8, 32),
+    STEQR_PC_ENTRY(0, float, 128, 4, 64),
     STEQR_PC_ENTRY(1, double, 128, 8, 16),
+    STEQR_PC_ENTRY(1, double, 128, 8, 32),
     STEQR_PCV_ENTRY(0, float, 128, 8),
     STEQR_PCV_ENTRY(0, float, 128, 16),
     STEQR_PCV_ENTRY(1, double, 128, 8),

@@ -219,8 +219,17 @@ __device__ __forceinline__ void consume(const KernelArgs& args, int lane, int wa
     }
 }
 
+// Wavefronts per SIMD the register allocation must allow: at order 128 in
+// float two workgroups of W = 8 consumers and a producer (18 wavefronts)
+// share a CU only at five per SIMD.
+template <typename T, int N, int W>
+constexpr int pc_min_waves() {
+    return (N == 128 && sizeof(T) == 4 && W == 8) ? 5 : 1;
+}
+
 template <typename T, int N, int W, int P, bool PG, bool WANTQ = true>
-__global__ void __launch_bounds__(WANTQ ? (W + 1) * 64 : 256) steqr_pc_kernel(KernelArgs args) {
+__global__ void __launch_bounds__((WANTQ ? (W + 1) * 64 : 256), (pc_min_waves<T, N, W>()))
+    steqr_pc_kernel(KernelArgs args) {
     using S = SmemPC<T, N, W, P>;
     constexpr bool HALF = S::HALF;
     constexpr int WPP = S::WPP;
@@ -498,7 +507,10 @@ __global__ void __launch_bounds__(WANTQ ? (W + 1) * 64 : 256) steqr_pc_kernel(Ke
         T* const lg = rot + (size_t)(slot * (NP + 1) + (chunk < NP ? chunk : NP)) * (N - 1) * 2;
         T d0 = sd[0], e0 = se[0], d1 = sd[1], e1 = se[1];
         T cp = T(1);
-        static_for<N - 1>([&](auto I) {
+        // the chase stops after the last position any chunk of the
+        // wavefront steps through (one scalar branch per position)
+        const int me_w = wave_max_uniform(steps != 0u ? s + (int)steps : 0);
+        static_for_while<N - 1>([&](auto I) {
             constexpr int p = decltype(I)::value;
             T d2 = T(0), e2 = T(0);
             if constexpr (p + 2 < N) {
@@ -546,6 +558,7 @@ __global__ void __launch_bounds__(WANTQ ? (W + 1) * 64 : 256) steqr_pc_kernel(Ke
             e0 = e1;
             d1 = d2;
             e1 = e2;
+            return p + 1 < me_w;
         });
         if (steps != 0u) {
             const int me = s + (int)steps;

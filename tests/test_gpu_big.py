@@ -79,3 +79,16 @@ def test_big_unsorted_and_budget(dt):
     g = run_gpu(d, e, False, max_sweeps_per_n=-1)
     o = oracle.steqr(d, e, False, max_sweeps_per_n=0, threads=8)
     assert np.array_equal(g[2], o[2]) and np.all(g[2] > 0) and np.array_equal(g[0], d)
+
+
+@pytest.mark.parametrize("dt,lanes", [(np.float32, 16), (np.float32, 32), (np.float32, 64),
+                                      (np.float64, 16), (np.float64, 32)],
+                         ids=lambda v: v.__name__ if isinstance(v, type) else str(v))
+def test_big_producer_shapes(dt, lanes):
+    """Every built (producer lanes, consumers per workgroup) shape at order 128."""
+    for n in (80, 128):
+        print("big shape", dt.__name__, lanes, n, flush=True)
+        d, e = W.random_batch(n, 150, dt, salt=520 + n)
+        g = run_gpu(d, e, True, lanes=lanes)
+        o = oracle.steqr(d, e, True, threads=8)
+        assert check(d, e, g, o, True) == []
