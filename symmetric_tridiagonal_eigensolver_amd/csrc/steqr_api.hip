@@ -29,7 +29,9 @@ int padded_order(int n) {
 // SIMDs idle (n = 32 keeps two lanes). Orders 33..64 run one problem per
 // wavefront.
 int default_lanes(int dtype, int N, int jobz, int band) {
-    if (N == 128) return band == 3 ? 16 : 16;  // producer lanes per problem
+    // order 128, producer lanes per problem: float with eigenvectors runs
+    // whole rows of Q per lane (5 problems per producer at 8 lanes each)
+    if (N == 128) return (band == 3 && dtype == STEQR_F32) ? 8 : 16;
     if (band == 3) return dtype == STEQR_F32 ? 16 : 4;  // producer lanes per problem
     if (N >= 64) return 64;
     if (jobz) {

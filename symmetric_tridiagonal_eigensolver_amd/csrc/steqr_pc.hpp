@@ -38,14 +38,19 @@
 
 namespace steqr {
 
-// W consumer wavefronts, each holding CQ = 64/N problems (lane = row of
-// one of them; at order 128 WPP = 4 wavefronts per problem, two lanes per
-// row), so NP = W * CQ / WPP problems per workgroup.
-template <typename T, int N, int W, int P>
+// W consumer wavefronts. RS lanes hold one row of Q (RS = 2 at order 128
+// by default: two half rows), so a consumer holds RPW = 64/RS rows: CQ =
+// RPW/N problems when N <= RPW, else WPP = N/RPW consumers per problem;
+// NP = W * CQ / WPP problems per workgroup.
+template <int N>
+constexpr int pc_default_rs() { return N > 64 ? 2 : 1; }
+
+template <typename T, int N, int W, int P, int RS = pc_default_rs<N>()>
 struct SmemPC {
-    static constexpr bool HALF = N > 64;                  // two lanes per row of Q
-    static constexpr int CQ = HALF ? 1 : 64 / N;          // problems per consumer
-    static constexpr int WPP = HALF ? 2 * N / 64 : 1;     // consumers per problem
+    static constexpr bool HALF = RS == 2;                 // two lanes per row of Q
+    static constexpr int RPW = 64 / RS;                   // rows per consumer
+    static constexpr int CQ = N <= RPW ? RPW / N : 1;     // problems per consumer
+    static constexpr int WPP = N <= RPW ? 1 : N / RPW;    // consumers per problem
     static constexpr int NP = W * CQ / WPP;               // problems per workgroup
     static constexpr int CH = 64 / P;                     // producer chunks (>= NP)
     static constexpr int SLOT = 2 * N + 1;                // d[N], e[N], pad
@@ -89,20 +94,21 @@ enum { PC_CTRL_PASS = 1, PC_CTRL_END = 2 };
 // row: columns c0 .. c0+QW-1 with the other half in lane ^ 32) and apply the
 // producer's logged rotations pass by pass; at the end store the rows with
 // the sort's column permutation.
-template <typename T, int N, int W, int P>
+template <typename T, int N, int W, int P, int RS>
 __device__ __forceinline__ void consume(const KernelArgs& args, int lane, int wave, long first,
                                         const T* rot, const int* hdr, const int* ranks,
                                         const int* fin) {
-    using S = SmemPC<T, N, W, P>;
+    using S = SmemPC<T, N, W, P, RS>;
     using F = Fp<T>;
     constexpr bool HALF = S::HALF;
     constexpr int NP = S::NP;
     constexpr int QW = HALF ? N / 2 : N;  // columns held per lane
     T* __restrict__ gq = static_cast<T*>(args.q);
     const int n = args.n;
-    const int pi = HALF ? wave / S::WPP : wave * S::CQ + lane / N;
+    constexpr int RPW = S::RPW;
+    const int pi = (N <= RPW) ? wave * S::CQ + lane / N : wave / S::WPP;
     const int hf = HALF ? (lane >> 5) : 0;
-    const int row = HALF ? (wave % S::WPP) * 32 + (lane & 31) : lane % N;
+    const int row = (N <= RPW) ? lane % N : (wave % S::WPP) * RPW + lane % RPW;
     const int c0 = hf * QW;
     const long prob = first + pi;
     const bool live = prob < (long)args.batch;
@@ -227,11 +233,11 @@ constexpr int pc_min_waves() {
     return (N == 128 && sizeof(T) == 4 && W == 8) ? 5 : 1;
 }
 
-template <typename T, int N, int W, int P, bool PG, bool WANTQ = true>
+template <typename T, int N, int W, int P, bool PG, bool WANTQ = true,
+          int RS = pc_default_rs<N>()>
 __global__ void __launch_bounds__((WANTQ ? (W + 1) * 64 : 256), (pc_min_waves<T, N, W>()))
     steqr_pc_kernel(KernelArgs args) {
-    using S = SmemPC<T, N, W, P>;
-    constexpr bool HALF = S::HALF;
+    using S = SmemPC<T, N, W, P, RS>;
     constexpr int WPP = S::WPP;
     constexpr int CH = 64 / P;
     // problems of one producer wavefront
@@ -271,7 +277,7 @@ __global__ void __launch_bounds__((WANTQ ? (W + 1) * 64 : 256), (pc_min_waves<T,
 
     if constexpr (WANTQ) {
         if (wave < W) {
-            consume<T, N, W, P>(args, lane, wave, first, rot, hdr, ranks, fin);
+            consume<T, N, W, P, RS>(args, lane, wave, first, rot, hdr, ranks, fin);
             return;
         }
     }

@@ -78,11 +78,11 @@ hipError_t launch_chunkl(const KernelArgs& args, int grid, int block, hipStream_
 // Producer-consumer with eigenvectors: W consumer wavefronts (64/N problems
 // each) and one producer per workgroup; the grid and block are given by
 // the caller.
-template <typename T, int N, int W, int P, bool PG>
+template <typename T, int N, int W, int P, bool PG, int RS = pc_default_rs<N>()>
 hipError_t launch_pc(const KernelArgs& args, int grid, int block, hipStream_t stream) {
-    constexpr size_t lds = SmemPC<T, N, W, P>::bytes;
-    hipLaunchKernelGGL((steqr_pc_kernel<T, N, W, P, PG>), dim3(grid), dim3(block), lds, stream,
-                       args);
+    constexpr size_t lds = SmemPC<T, N, W, P, RS>::bytes;
+    hipLaunchKernelGGL((steqr_pc_kernel<T, N, W, P, PG, true, RS>), dim3(grid), dim3(block), lds,
+                       stream, args);
     return hipGetLastError();
 }
 
@@ -102,6 +102,12 @@ hipError_t launch_pcv(const KernelArgs& args, int grid, int block, hipStream_t s
 #define STEQR_PC_ENTRY(DT, T, N, W, P) \
     { DT, N, P, 1, 3, (int)SmemPC<T, N, W, P>::bytes, \
       &launch_pc<T, N, W, P, STEQR_INST_PG != 0>, SmemPC<T, N, W, P>::NP, (W) + 1 }
+
+// The same with RS lanes per row of Q chosen explicitly (order 128 with
+// whole rows per lane: RS = 1).
+#define STEQR_PCR_ENTRY(DT, T, N, W, P, RS) \
+    { DT, N, P, 1, 3, (int)SmemPC<T, N, W, P, RS>::bytes, \
+      &launch_pc<T, N, W, P, STEQR_INST_PG != 0, RS>, SmemPC<T, N, W, P, RS>::NP, (W) + 1 }
 
 #define STEQR_ENTRY(DT, T, N, P, Q) \
     { DT, N, P, Q, 1, (int)Smem<T, N, P, (Q) != 0>::bytes_per_wave, \

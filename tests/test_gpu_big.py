@@ -81,7 +81,8 @@ def test_big_unsorted_and_budget(dt):
     assert np.array_equal(g[2], o[2]) and np.all(g[2] > 0) and np.array_equal(g[0], d)
 
 
-@pytest.mark.parametrize("dt,lanes", [(np.float32, 16), (np.float32, 32), (np.float32, 64),
+@pytest.mark.parametrize("dt,lanes", [(np.float32, 8), (np.float32, 16), (np.float32, 32),
+                                      (np.float32, 64),
                                       (np.float64, 16), (np.float64, 32)],
                          ids=lambda v: v.__name__ if isinstance(v, type) else str(v))
 def test_big_producer_shapes(dt, lanes):
