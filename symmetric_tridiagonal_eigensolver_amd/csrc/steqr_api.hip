@@ -26,8 +26,9 @@ int padded_order(int n) {
 // the price of R = N/P rows of Q per lane in VGPRs; the best balance is
 // four to eight rows per lane while the wavefront still fits two waves per
 // SIMD. Values only keep one lane per problem unless the batch would leave
-// SIMDs idle (n = 32 keeps two lanes). Orders 33..64 run one problem per
-// wavefront.
+// SIMDs idle (n = 32 keeps two lanes). Orders 33..64 without eigenvectors
+// run one problem per wavefront; with eigenvectors, and at orders 65..128,
+// P counts the producer lanes of the producer-consumer kernel.
 int default_lanes(int dtype, int N, int jobz, int band) {
     // order 128, producer lanes per problem: float with eigenvectors runs
     // whole rows of Q per lane (5 problems per producer at 8 lanes each)

@@ -1,4 +1,5 @@
-// Producer-consumer steqr kernel for orders 33..64 with eigenvectors
+// Producer-consumer steqr kernel for orders 33..128 with eigenvectors (and
+// values only at 65..128)
 // (gfx950, wave64).
 //
 // At these orders a problem's Q fills much of a wavefront's registers (at

@@ -75,9 +75,9 @@ hipError_t launch_chunkl(const KernelArgs& args, int grid, int block, hipStream_
     { DT, N, P, Q, 2, (int)SmemL<T, N, P>::bytes_per_wave, \
       &launch_chunkl<T, N, P, (Q) != 0, STEQR_INST_PG != 0> }
 
-// Producer-consumer with eigenvectors: W consumer wavefronts (64/N problems
-// each) and one producer per workgroup; the grid and block are given by
-// the caller.
+// Producer-consumer with eigenvectors: W consumer wavefronts (RS lanes per
+// row of Q) and one producer per workgroup; the grid and block are given
+// by the caller.
 template <typename T, int N, int W, int P, bool PG, int RS = pc_default_rs<N>()>
 hipError_t launch_pc(const KernelArgs& args, int grid, int block, hipStream_t stream) {
     constexpr size_t lds = SmemPC<T, N, W, P, RS>::bytes;
