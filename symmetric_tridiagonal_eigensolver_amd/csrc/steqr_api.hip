@@ -26,14 +26,18 @@ int padded_order(int n) {
 // the price of R = N/P rows of Q per lane in VGPRs; the best balance is
 // four to eight rows per lane while the wavefront still fits two waves per
 // SIMD. Values only keep one lane per problem unless the batch would leave
-// SIMDs idle (n = 32 keeps two lanes). Orders 33..64 without eigenvectors
-// run one problem per wavefront; with eigenvectors, and at orders 65..128,
-// P counts the producer lanes of the producer-consumer kernel.
+// SIMDs idle (n = 32 keeps two lanes). At orders 33..128 P counts the
+// producer lanes of the producer-consumer kernel (with or without its
+// consumers); P = 64 selects one problem per wavefront at orders 33..64.
 int default_lanes(int dtype, int N, int jobz, int band) {
     // order 128, producer lanes per problem: float with eigenvectors runs
     // whole rows of Q per lane (5 problems per producer at 8 lanes each)
     if (N == 128) return (band == 3 && dtype == STEQR_F32) ? 8 : 16;
     if (band == 3) return dtype == STEQR_F32 ? 16 : 4;  // producer lanes per problem
+    // order 64 without eigenvectors: the producer's algorithm, 8 problems
+    // per wavefront (measured 2.9x (float) and 4x (double) faster than one
+    // problem per wavefront)
+    if (N == 64 && !jobz) return 8;
     if (N >= 64) return 64;
     if (jobz) {
         if (N == 4) return 4;

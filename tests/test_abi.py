@@ -59,14 +59,18 @@ def test_version(st):
 @pytest.mark.parametrize("n,jobz,dtype,N,P", [
     (1, 1, 0, 4, 4), (4, 1, 0, 4, 4), (5, 1, 0, 8, 2), (8, 0, 0, 8, 1), (12, 1, 1, 16, 4),
     (16, 1, 0, 16, 4), (17, 1, 0, 32, 8), (32, 1, 1, 32, 16), (32, 0, 1, 32, 1), (32, 0, 0, 32, 2),
-    (33, 1, 1, 64, 4), (64, 1, 1, 64, 4), (64, 1, 0, 64, 16), (64, 0, 0, 64, 64)])
+    (33, 1, 1, 64, 4), (64, 1, 1, 64, 4), (64, 1, 0, 64, 16), (64, 0, 0, 64, 8),
+    (40, 0, 1, 64, 8), (100, 1, 0, 128, 8), (100, 1, 1, 128, 16), (128, 0, 0, 128, 16)])
 def test_query_default_plan(st, n, jobz, dtype, N, P):
     q = st.steqr_query(n, 1000, jobz, dtype)
     assert q["padded_n"] == N and q["lanes_per_problem"] == P
     if q["band_storage"] == 3:
         # producer and consumer wavefronts: one problem per consumer
         assert n > 32 and jobz and q["rows_per_lane"] == 1
-        per_block = q["waves_per_block"] - 1
+        # consumers per problem: 1 up to order 64; at 128 two (float, whole
+        # rows) or four (double, half rows)
+        cpp = 1 if N <= 64 else (2 if dtype == 0 else 4)
+        per_block = (q["waves_per_block"] - 1) // cpp
     else:
         assert q["rows_per_lane"] == ((N + P - 1) // P if jobz else 0)
         per_block = q["waves_per_block"] * (64 // P)

@@ -93,3 +93,16 @@ def test_big_producer_shapes(dt, lanes):
         g = run_gpu(d, e, True, lanes=lanes)
         o = oracle.steqr(d, e, True, threads=8)
         assert check(d, e, g, o, True) == []
+
+
+@pytest.mark.parametrize("dt,lanes", [(np.float32, 8), (np.float32, 16), (np.float64, 8),
+                                      (np.float64, 16)],
+                         ids=lambda v: v.__name__ if isinstance(v, type) else str(v))
+def test_big_values_shapes(dt, lanes):
+    """Every built producer shape of the values-only kernel at order 128."""
+    for n in (70, 128):
+        print("big values shape", dt.__name__, lanes, n, flush=True)
+        d, e = W.random_batch(n, 150, dt, salt=530 + n)
+        g = run_gpu(d, e, False, lanes=lanes)
+        o = oracle.steqr(d, e, False, threads=8)
+        assert check(d, e, g, o, False) == []

@@ -96,6 +96,13 @@ LANE_CASES += [
     (np.float64, 16, True, 8, 2), (np.float64, 16, True, 4, 2), (np.float64, 32, True, 16, 2),
     (np.float32, 12, True, 4, 2), (np.float64, 27, True, 16, 2),
 ]
+# the producer's algorithm alone, several problems per wavefront (orders
+# 33..64 without eigenvectors)
+LANE_CASES += [
+    (np.float32, 64, False, 4, 2), (np.float32, 64, False, 8, 2), (np.float32, 64, False, 16, 2),
+    (np.float64, 64, False, 4, 2), (np.float64, 64, False, 8, 2), (np.float64, 64, False, 16, 2),
+    (np.float32, 41, False, 8, 2), (np.float64, 59, False, 8, 2),
+]
 # producer and consumer wavefronts (orders 33..64 with eigenvectors)
 LANE_CASES += [
     (np.float32, 64, True, 16, 3), (np.float32, 64, True, 8, 3), (np.float64, 64, True, 4, 3),
