@@ -90,9 +90,10 @@ struct Plan {
     int N, P, R, waves, grid, band;
 };
 
-// Default band storage (measured): LDS for orders above 32 (one problem per
-// wavefront) and, with eigenvectors, wherever the registers are better
-// spent on rows of Q: order 32, and order 16 in double precision.
+// Default band storage (measured): above order 32 the producer-consumer
+// kernel with eigenvectors (3) and its producer alone without them (2, band
+// in LDS); with eigenvectors LDS wherever the registers are better spent on
+// rows of Q: order 32, and order 16 in double precision.
 int default_band(int dtype, int N, int jobz) {
     if (N >= 64) return jobz ? 3 : 2;
     if (jobz && (N == 32 || (N == 16 && dtype == STEQR_F64))) return 2;
