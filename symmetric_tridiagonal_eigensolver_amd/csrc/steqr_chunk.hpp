@@ -462,12 +462,14 @@ __global__ void __launch_bounds__(256) steqr_chunk_kernel(KernelArgs args) {
         }
 
         // ------------------------------------------------------------ chase pass
-        // Running pair (x, y), seeded in the settle, and the previous cosine
-        // cp: the update e_{p+1} <- c_p e_{p+1} of step p is applied when
-        // step p+1 reads it. Step p writes r into e_{p-1}; at the first step
-        // that position is a zero coupling or a negligible e already in
-        // `zeroed`, which the next deflation test keeps and closing the
-        // block restores.
+        // Running pair (x, y), seeded in the settle. The update
+        // e_{p+1} <- c_p e_{p+1} of step p is applied by step p itself in the
+        // EXP form (the last step of a sweep scales the negligible or zero e
+        // below the block, which stays negligible) and by step p+1 through
+        // the previous cosine cp in the PG form. Step p writes r into
+        // e_{p-1}; at the first step that position is a zero coupling or a
+        // negligible e already in `zeroed`, which the next deflation test
+        // keeps and closing the block restores.
         T cp = T(1);
         // step p runs when s <= p < m: one unsigned compare of p - s with
         // the step count (0 when this chunk does not sweep)
