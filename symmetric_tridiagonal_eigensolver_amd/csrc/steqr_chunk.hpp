@@ -158,6 +158,10 @@ __global__ void __launch_bounds__(256) steqr_chunk_kernel(KernelArgs args) {
     using F = Fp<T>;
     using S = Smem<T, N, P, WANTQ, DENSE>;
     enum { ST_OPEN = 0, ST_ITER = 1, ST_DONE = 2 };
+    // split the deflation scan over the chunk's lanes from 4 lanes per
+    // problem (DPP lane moves up to 16 lanes; 32-bit position masks); at 2
+    // lanes the LDS reads cost more than the halved scan saves (measured)
+    constexpr bool SPLIT_SCAN = P >= 4 && P <= 16 && N <= 32 && P <= N;
 
     extern __shared__ __align__(16) unsigned char smem_raw[];
 
@@ -385,12 +389,28 @@ __global__ void __launch_bounds__(256) steqr_chunk_kernel(KernelArgs args) {
         const bool iter = state == ST_ITER;
         if (!__any(iter)) break;
         // deflation test [algo, deflation] at every position; e's found
-        // negligible earlier count too (the chase may overwrite them)
+        // negligible earlier count too (the chase may overwrite them). With
+        // several lanes per problem, lane r tests positions r*K .. r*K+K-1
+        // of the chunk's band copy in LDS (current: it is republished after
+        // every change) and the lanes OR their partial masks; the same
+        // values and the same test as the register scan, so the same mask.
         M neg = 0;
-        static_for<N - 1>([&](auto I) {
-            constexpr int p = N - 2 - decltype(I)::value;
-            neg = neg + neg + (negligible(e[p], d[p], d[p + 1]) ? (M)1 : (M)0);
-        });
+        if constexpr (SPLIT_SCAN) {
+            constexpr int K = (N - 1 + P - 1) / P;  // P*K <= N: reads stay in the slot
+            const int p0 = r * K;
+            unsigned loc = 0;
+            static_for<K>([&](auto KK) {
+                constexpr int k = decltype(KK)::value;
+                const int p = p0 + k;
+                loc |= negligible(se[p], sd[p], sd[p + 1]) ? (1u << k) : 0u;
+            });
+            neg = (M)chunk_or_dpp<P>(loc << p0) & bits_below<M>(N - 1);
+        } else {
+            static_for<N - 1>([&](auto I) {
+                constexpr int p = N - 2 - decltype(I)::value;
+                neg = neg + neg + (negligible(e[p], d[p], d[p + 1]) ? (M)1 : (M)0);
+            });
+        }
         neg |= zeroed;
         const M rng = bit_range<M>(bt, m - 1);
         const M nb = neg & rng;

@@ -37,13 +37,12 @@ struct SmemL {
     static constexpr size_t bytes_per_wave = band_bytes + rank_bytes + stage_bytes;
 };
 
-// OR / max over the P lanes of a chunk (butterfly; every lane of the chunk
-// must be active, which holds because a chunk's lanes share control flow).
+// OR / max over the P lanes of a chunk (every lane of the chunk must be
+// active, which holds because a chunk's lanes share control flow). The OR
+// takes DPP lane moves, whose partners never leave the chunk.
 template <int P>
 __device__ __forceinline__ unsigned chunk_or(unsigned v) {
-#pragma unroll
-    for (int o = 1; o < P; o <<= 1) v |= (unsigned)__shfl_xor((int)v, o, 64);
-    return v;
+    return chunk_or_dpp<P>(v);
 }
 template <int P, typename T>
 __device__ __forceinline__ T chunk_max(T v) {

@@ -140,6 +140,24 @@ struct Fp<double> {
     }
 };
 
+// OR over the P consecutive lanes of a chunk (P a power of two, every lane
+// of the wavefront active). Up to 16 lanes the partners come from DPP lane
+// moves within a row of 16: swap neighbours, swap pairs (quad permutes),
+// then mirror 8 and mirror 16 (after the quad steps each quad holds its OR,
+// so a mirror pairs every lane with the other half). Beyond 16 lanes a
+// ds_bpermute shuffle finishes.
+template <int P>
+__device__ __forceinline__ unsigned chunk_or_dpp(unsigned v) {
+    static_assert(P >= 1 && P <= 64 && (P & (P - 1)) == 0, "P a power of two");
+    if constexpr (P >= 2) v |= (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);
+    if constexpr (P >= 4) v |= (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);
+    if constexpr (P >= 8) v |= (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false);
+    if constexpr (P >= 16) v |= (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false);
+    if constexpr (P >= 32) v |= (unsigned)__shfl_xor((int)v, 16, 64);
+    if constexpr (P >= 64) v |= (unsigned)__shfl_xor((int)v, 32, 64);
+    return v;
+}
+
 // ---------------------------------------------------------------- bit masks
 // Position masks over the off-diagonal index p (bit p <-> e_p).
 

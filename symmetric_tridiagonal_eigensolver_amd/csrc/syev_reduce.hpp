@@ -35,13 +35,33 @@
 
 namespace steqr {
 
-// Sum over the P lanes of a chunk (xor butterfly). Every lane receives the
-// same value bit for bit: each level adds the same two operands in every
-// lane of a pair, and floating-point addition is commutative.
+// Sum over the P lanes of a chunk (butterfly). Every lane receives the same
+// value bit for bit: each level adds the same two operands in both lanes of
+// a pair, and floating-point addition is commutative. Up to 16 lanes the
+// partner comes from a DPP lane move (swap neighbours, swap pairs, mirror 8,
+// mirror 16; after each level the lanes of a group hold equal values, so a
+// mirror pairs every lane with the other half), beyond that from a shuffle.
+template <int CTRL, typename T>
+__device__ __forceinline__ T dpp_partner(T v) {
+    if constexpr (sizeof(T) == 4) {
+        return __builtin_bit_cast(
+            T, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+    } else {
+        const unsigned long long u = __builtin_bit_cast(unsigned long long, v);
+        const int lo = __builtin_amdgcn_update_dpp(0, (int)(unsigned)u, CTRL, 0xF, 0xF, false);
+        const int hi = __builtin_amdgcn_update_dpp(0, (int)(unsigned)(u >> 32), CTRL, 0xF, 0xF, false);
+        return __builtin_bit_cast(T, ((unsigned long long)(unsigned)hi << 32) | (unsigned)lo);
+    }
+}
 template <int P, typename T>
 __device__ __forceinline__ T chunk_sum(T v) {
-#pragma unroll
-    for (int o = 1; o < P; o <<= 1) v = v + __shfl_xor(v, o, 64);
+    static_assert(P >= 1 && P <= 64 && (P & (P - 1)) == 0, "P a power of two");
+    if constexpr (P >= 2) v = v + dpp_partner<0xB1>(v);
+    if constexpr (P >= 4) v = v + dpp_partner<0x4E>(v);
+    if constexpr (P >= 8) v = v + dpp_partner<0x141>(v);
+    if constexpr (P >= 16) v = v + dpp_partner<0x140>(v);
+    if constexpr (P >= 32) v = v + __shfl_xor(v, 16, 64);
+    if constexpr (P >= 64) v = v + __shfl_xor(v, 32, 64);
     return v;
 }
 
