@@ -293,6 +293,10 @@ __global__ void __launch_bounds__((WANTQ ? (W + 1) * 64 : 256), (pc_min_waves<T,
     }
 
     // ================================================================ producer
+    // The producer's serial chase sets the workgroup's pace and shares its
+    // SIMD with consumer wavefronts, which have slack: let the SIMD's
+    // instruction arbiter prefer the producer.
+    if constexpr (WANTQ) __builtin_amdgcn_s_setprio(3);
     const int chunk = lane / P;
     const int r = lane % P;
     const long prob = first + chunk;
