@@ -528,7 +528,8 @@ __global__ void __launch_bounds__((WANTQ ? (W + 1) * 64 : 256), (pc_min_waves<T,
         T d0 = sd[0], e0 = se[0], d1 = sd[1], e1 = se[1];
         T cp = T(1);
         // the chase stops after the last position any chunk of the
-        // wavefront steps through (one scalar branch per position)
+        // wavefront steps through, tested after every second position (one
+        // scalar branch per two positions; an extra position steps no chunk)
         const int me_w = wave_max_uniform(steps != 0u ? s + (int)steps : 0);
         static_for_while<N - 1>([&](auto I) {
             constexpr int p = decltype(I)::value;
@@ -555,9 +556,11 @@ __global__ void __launch_bounds__((WANTQ ? (W + 1) * 64 : 256), (pc_min_waves<T,
                     y = sn;
                     cp = c;
                 } else {
+                    // e0 already carries the factor c of the previous step
+                    // (applied to the window below, so no cosine is carried)
                     const T a = dcur;
                     lartg(x, y, c, sn, rr);
-                    const T b = cp * e0;
+                    const T b = e0;
                     const T pp = c * a + sn * b;
                     const T qq = c * b + sn * d1;
                     const T an = pp * c + qq * sn;
@@ -567,7 +570,7 @@ __global__ void __launch_bounds__((WANTQ ? (W + 1) * 64 : 256), (pc_min_waves<T,
                     dcur = (a + d1) - an;
                     x = bn;
                     y = sn * e1;
-                    cp = c;
+                    e1 = c * e1;
                 }
                 if constexpr (WANTQ) {
                     lg[2 * p] = c;
@@ -578,7 +581,7 @@ __global__ void __launch_bounds__((WANTQ ? (W + 1) * 64 : 256), (pc_min_waves<T,
             e0 = e1;
             d1 = d2;
             e1 = e2;
-            return p + 1 < me_w;
+            return (p & 1) == 0 || p + 1 < me_w;
         });
         if (steps != 0u) {
             const int me = s + (int)steps;
