@@ -39,14 +39,23 @@ __device__ __forceinline__ void static_for_while(Fn&& fn) {
 }
 
 // Largest value over the 64 lanes of the wavefront (every lane active), as
-// a wave-uniform scalar: bounds a static loop with one scalar branch.
+// a wave-uniform scalar: bounds a static loop with one scalar branch. DPP
+// lane moves within each row of 16 lanes (swap neighbours, swap pairs,
+// mirror 8, mirror 16) leave every lane with its row's maximum; the four
+// row maxima are read into scalar registers.
 __device__ __forceinline__ int wave_max_uniform(int v) {
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int w = __shfl_xor(v, o, 64);
-        v = v > w ? v : w;
-    }
-    return __builtin_amdgcn_readfirstlane(v);
+    int w = __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);
+    v = v > w ? v : w;
+    w = __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);
+    v = v > w ? v : w;
+    w = __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);
+    v = v > w ? v : w;
+    w = __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false);
+    v = v > w ? v : w;
+    const int r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
+    const int r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
+    const int a = r0 > r1 ? r0 : r1, b = r2 > r3 ? r2 : r3;
+    return a > b ? a : b;
 }
 
 // Precision-dependent constants and hardware helpers.

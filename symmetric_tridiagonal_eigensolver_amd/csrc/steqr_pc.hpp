@@ -67,22 +67,14 @@ struct SmemPC {
     static constexpr size_t bytes = band_bytes + rot_bytes + hdr_bytes + rank_bytes + fin_bytes;
 };
 
-// OR over the P lanes of a chunk for 64- and 128-bit masks: DPP lane moves
-// at order 128; at order 64 the ds_bpermute butterfly, which measured
-// slightly faster there
+// OR over the P lanes of a chunk for 64- and 128-bit masks (DPP lane moves
+// on each 32-bit word)
 template <int P, typename M>
 __device__ __forceinline__ M chunk_or_mask(M v) {
     M out = 0;
     static_for<(int)(sizeof(M) / 4)>([&](auto WW) {
         constexpr int w = decltype(WW)::value;
-        unsigned x = (unsigned)(v >> (32 * w));
-        if constexpr (sizeof(M) > 8) {
-            x = chunk_or<P>(x);
-        } else {
-#pragma unroll
-            for (int o = 1; o < P; o <<= 1) x |= (unsigned)__shfl_xor((int)x, o, 64);
-        }
-        out |= (M)x << (32 * w);
+        out |= (M)chunk_or<P>((unsigned)(v >> (32 * w))) << (32 * w);
     });
     return out;
 }
