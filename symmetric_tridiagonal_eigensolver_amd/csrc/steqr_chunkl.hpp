@@ -44,6 +44,60 @@ template <int P>
 __device__ __forceinline__ unsigned chunk_or(unsigned v) {
     return chunk_or_dpp<P>(v);
 }
+// OR over the P lanes of a chunk for 32-, 64- and 128-bit masks (DPP lane
+// moves on each 32-bit word)
+template <int P, typename M>
+__device__ __forceinline__ M chunk_or_mask(M v) {
+    M out = 0;
+    static_for<(int)(sizeof(M) / 4)>([&](auto WW) {
+        constexpr int w = decltype(WW)::value;
+        out |= (M)chunk_or<P>((unsigned)(v >> (32 * w))) << (32 * w);
+    });
+    return out;
+}
+
+// Deflation test [algo, deflation] of every position of a chunk's band copy
+// in LDS (sd = d, se = e; the slot holds at least 2N values, so sd[N] reads
+// se[0]), split over the chunk's P lanes with no branch; the partial masks
+// are OR-ed and bit N-1 (no such off-diagonal) is cleared. With 8 to 32
+// lanes, lane r tests positions r, r+P, r+2P, ... (consecutive lanes read
+// consecutive words: no bank conflicts); its bits are gathered per 32-bit
+// word of the mask at lane 0's places and shifted by r at the end (kP mod 32
+// + r < 32 as P divides 32). With 2 or 4 lanes (at most 4-way bank
+// conflicts) and with 64, lane r tests the consecutive positions r*K ..
+// r*K+K-1, which take about half as many LDS reads (measured faster at 4
+// lanes, slower at 16).
+template <typename T, int N, int P, typename M>
+__device__ __forceinline__ M scan_negligible(const T* sd, const T* se, int r) {
+    constexpr int K = N / P;
+    constexpr int WORDS = (int)(sizeof(M) / 4);
+    static_assert(K * P == N && K <= 32 && sizeof(M) * 8 >= N, "P lanes per chunk");
+    if constexpr (P <= 4 || P > 32) {
+        unsigned loc = 0;
+        static_for<K>([&](auto KK) {
+            constexpr int k = decltype(KK)::value;
+            const int p = r * K + k;
+            loc |= negligible(se[p], sd[p], sd[p + 1]) ? (1u << k) : 0u;
+        });
+        return chunk_or_mask<P>((M)((M)loc << (r * K))) & bits_below<M>(N - 1);
+    } else {
+        unsigned word[WORDS];
+        static_for<WORDS>([&](auto WW) { word[decltype(WW)::value] = 0u; });
+        static_for<K>([&](auto KK) {
+            constexpr int k = decltype(KK)::value;
+            constexpr int bit = k * P;  // lane 0's position
+            const int p = r + bit;
+            word[bit / 32] |= negligible(se[p], sd[p], sd[p + 1]) ? (1u << (bit % 32)) : 0u;
+        });
+        M part = 0;
+        static_for<WORDS>([&](auto WW) {
+            constexpr int w = decltype(WW)::value;
+            part |= (M)(word[w] << r) << (32 * w);
+        });
+        return chunk_or_mask<P>(part) & bits_below<M>(N - 1);
+    }
+}
+
 template <int P, typename T>
 __device__ __forceinline__ T chunk_max(T v) {
 #pragma unroll
@@ -268,18 +322,7 @@ __global__ void __launch_bounds__(256) steqr_chunkl_kernel(KernelArgs args) {
         if (!__any(iter)) break;
         // deflation test [algo, deflation], positions split over the chunk;
         // e's found negligible earlier count too
-        M neg;
-        {
-            M part = 0;
-            static_for<K>([&](auto KK) {
-                constexpr int k = decltype(KK)::value;
-                const int p = r + k * P;
-                if (p < N - 1)
-                    part |= negligible(se[p], sd[p], sd[p + 1 < N ? p + 1 : N - 1])
-                                ? ((M)1 << p) : (M)0;
-            });
-            neg = chunk_or<P>(part) | zeroed;
-        }
+        const M neg = scan_negligible<T, N, P, M>(sd, se, r) | zeroed;
         const M rng = bit_range<M>(bt, m - 1);
         const M nb = neg & rng;
         const M clr = rng & ~neg;

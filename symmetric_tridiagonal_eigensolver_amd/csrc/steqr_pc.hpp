@@ -67,18 +67,6 @@ struct SmemPC {
     static constexpr size_t bytes = band_bytes + rot_bytes + hdr_bytes + rank_bytes + fin_bytes;
 };
 
-// OR over the P lanes of a chunk for 64- and 128-bit masks (DPP lane moves
-// on each 32-bit word)
-template <int P, typename M>
-__device__ __forceinline__ M chunk_or_mask(M v) {
-    M out = 0;
-    static_for<(int)(sizeof(M) / 4)>([&](auto WW) {
-        constexpr int w = decltype(WW)::value;
-        out |= (M)chunk_or<P>((unsigned)(v >> (32 * w))) << (32 * w);
-    });
-    return out;
-}
-
 // Values-only form (WANTQ false): the producer's algorithm alone, every
 // wavefront of the workgroup a producer of its own 64/P problems.
 template <typename T, int N, int P>
@@ -436,18 +424,7 @@ __global__ void __launch_bounds__((WANTQ ? (W + 1) * 64 : 256), (pc_min_waves<T,
         if (__any(state == ST_OPEN)) open_blocks();
         const bool iter = state == ST_ITER;
         if (!__any(iter)) break;
-        M neg;
-        {
-            M part = 0;
-            static_for<K>([&](auto KK) {
-                constexpr int k = decltype(KK)::value;
-                const int p = r + k * P;
-                if (p < N - 1)
-                    part |= negligible(se[p], sd[p], sd[p + 1 < N ? p + 1 : N - 1])
-                                ? ((M)1 << p) : (M)0;
-            });
-            neg = chunk_or_mask<P>(part) | zeroed;
-        }
+        const M neg = scan_negligible<T, N, P, M>(sd, se, r) | zeroed;
         const M rng = bit_range<M>(bt, m - 1);
         const M nb = neg & rng;
         const M clr = rng & ~neg;
