@@ -25,10 +25,11 @@ int padded_order(int n) {
 // means more problems per wavefront and less repeated chase arithmetic, at
 // the price of R = N/P rows of Q per lane in VGPRs; the best balance is
 // four to eight rows per lane while the wavefront still fits two waves per
-// SIMD. Values only keep one lane per problem unless the batch would leave
-// SIMDs idle (n = 32 keeps two lanes). At orders 33..128 P counts the
-// producer lanes of the producer-consumer kernel (with or without its
-// consumers); P = 64 selects one problem per wavefront at orders 33..64.
+// SIMD. Values only keep one lane per problem in double and at orders up to
+// 8, two at order 16 and four at order 32 in float (measured). At orders
+// 33..128 P counts the producer lanes of the producer-consumer kernel (with
+// or without its consumers); P = 64 selects one problem per wavefront at
+// orders 33..64.
 int default_lanes(int dtype, int N, int jobz, int band) {
     // order 128, producer lanes per problem: float with eigenvectors runs
     // whole rows of Q per lane (5 problems per producer at 8 lanes each)
@@ -46,7 +47,10 @@ int default_lanes(int dtype, int N, int jobz, int band) {
         if (band == 2) return dtype == STEQR_F32 ? 8 : 16;  // N == 32
         return 16;
     }
-    if (N == 32 && dtype == STEQR_F32) return 2;
+    // values only in float: the split deflation scan pays at 4 lanes for
+    // order 32 (-3% against 2) and 2 lanes beat 1 at order 16 (-2%)
+    if (N == 32 && dtype == STEQR_F32) return 4;
+    if (N == 16 && dtype == STEQR_F32) return 2;
     return 1;
 }
 
