@@ -137,15 +137,18 @@ struct Fp<double> {
     __device__ static __forceinline__ double fma(double a, double b, double c) { return __builtin_fma(a, b, c); }
     __device__ static __forceinline__ double max(double a, double b) { return __builtin_fmax(a, b); }
     __device__ static __forceinline__ double copysign(double a, double b) { return __builtin_copysign(a, b); }
-    // (a, b) <- (fma(c, a, s b), fma(c, b, -s a)). v_fma_f64 has no
-    // accumulate-in-place form, so plain code already writes in place.
+    // (a, b) <- (fma(c, a, s b), fma(c, b, -s a)) with each result written
+    // over its own input register, as for float: inside a lane-masked region
+    // the compiler's form (accumulate into a temporary) costs a 64-bit copy
+    // back per value.
     __device__ static __forceinline__ void rot(double& a, double& b, double c, double s) {
         const double sa = s * a, sb = s * b;
-        a = __builtin_fma(c, a, sb);
-        b = __builtin_fma(c, b, -sa);
+        asm("v_fma_f64 %0, %1, %0, %2" : "+v"(a) : "v"(c), "v"(sb));
+        asm("v_fma_f64 %0, %1, %0, -%2" : "+v"(b) : "v"(c), "v"(sa));
     }
+    // dst <- fma(a, b, c) in dst's register (old value of dst unused)
     __device__ static __forceinline__ void fma_over(double& dst, double a, double b, double c) {
-        dst = __builtin_fma(a, b, c);
+        asm("v_fma_f64 %0, %1, %2, %3" : "+v"(dst) : "v"(a), "v"(b), "v"(c));
     }
 };
 
