@@ -433,9 +433,11 @@ __global__ void __launch_bounds__(256) steqr_chunkl_kernel(KernelArgs args) {
                     y = sn;
                     cp = c;
                 } else {
+                    // e0 already carries the factor c of the previous step
+                    // (applied to the window below, so no cosine is carried)
                     const T a = dcur;
                     lartg(x, y, c, sn, rr);
-                    const T b = cp * e0;
+                    const T b = e0;
                     const T pp = c * a + sn * b;
                     const T qq = c * b + sn * d1;
                     const T an = pp * c + qq * sn;
@@ -445,7 +447,7 @@ __global__ void __launch_bounds__(256) steqr_chunkl_kernel(KernelArgs args) {
                     dcur = (a + d1) - an;
                     x = bn;
                     y = sn * e1;
-                    cp = c;
+                    e1 = c * e1;
                 }
                 if constexpr (WANTQ) {
                     static_for<R>([&](auto II) {
