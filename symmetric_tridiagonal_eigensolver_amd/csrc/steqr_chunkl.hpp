@@ -10,7 +10,9 @@
 // settle-phase work:
 //  * the deflation scan, the block norm, the scaling, the mirror and the
 //    sort keys are split over the P lanes of the chunk (lane r handles
-//    positions r, r+P, ...) and combined with butterfly shuffles;
+//    positions r, r+P, ..., or at 2 and 4 lanes a run of consecutive
+//    positions for the scan) and combined with DPP lane moves (the ORs) or
+//    butterfly shuffles (the block norm's maximum, once per block);
 //  * the chase reads d_{p+2}, e_{p+2} at position p (a two-deep window), so
 //    the LDS latency overlaps the rotation; every lane of the chunk writes
 //    the same final d_p and e_{p-1} to the same word (no lane mask);
