@@ -491,6 +491,12 @@ __global__ void __launch_bounds__(256) steqr_chunk_kernel(KernelArgs args) {
         // negligible e already in `zeroed`, which the next deflation test
         // keeps and closing the block restores.
         T cp = T(1);
+        // The chase runs at a raised issue priority and the settle at the
+        // default one: with two wavefronts per SIMD the SIMD's arbiter then
+        // prefers the chase's dense VALU stream over the other wavefront's
+        // settle (measured: 2% faster than no priority change; raising the
+        // settle's priority instead gains 1.4%).
+        __builtin_amdgcn_s_setprio(1);
         // step p runs when s <= p < m: one unsigned compare of p - s with
         // the step count (0 when this chunk does not sweep)
         const unsigned steps = sweep ? (unsigned)(m - s) : (jac ? 1u : 0u);
@@ -550,6 +556,7 @@ __global__ void __launch_bounds__(256) steqr_chunk_kernel(KernelArgs args) {
                 }
             }
         });
+        __builtin_amdgcn_s_setprio(0);
         publish();
         // a NaN shift turns [s, m] into NaN, a fixed point of every further
         // sweep: spend the rest of the budget at once (same final state)
