@@ -401,6 +401,9 @@ __global__ void __launch_bounds__(256) steqr_chunkl_kernel(KernelArgs args) {
         // before the window has read it.
         T d0 = sd[0], e0 = se[0], d1 = sd[1], e1 = se[1];
         T cp = T(1);
+        // chase at a raised issue priority, settle at the default one (as in
+        // steqr_chunk.hpp)
+        __builtin_amdgcn_s_setprio(1);
         // step p runs when s <= p < m: one unsigned compare of p - s with
         // the step count (0 when this chunk does not sweep)
         const unsigned steps = sweep ? (unsigned)(m - s) : (jac ? 1u : 0u);
@@ -469,6 +472,7 @@ __global__ void __launch_bounds__(256) steqr_chunkl_kernel(KernelArgs args) {
             sd[me] = dcur;
             se[me - 1] = x;
         }
+        __builtin_amdgcn_s_setprio(0);
         __builtin_amdgcn_wave_barrier();
         // a NaN shift turns [s, m] into NaN, a fixed point of every further
         // sweep: spend the rest of the budget at once (same final state)

@@ -496,6 +496,9 @@ __global__ void __launch_bounds__((WANTQ ? (W + 1) * 64 : 256), (pc_min_waves<T,
         T* const lg = rot + (size_t)(slot * (NP + 1) + (chunk < NP ? chunk : NP)) * (N - 1) * 2;
         T d0 = sd[0], e0 = se[0], d1 = sd[1], e1 = se[1];
         T cp = T(1);
+        // values only: every wavefront a producer; chase at a raised issue
+        // priority, settle at the default one (as in steqr_chunk.hpp)
+        if constexpr (!WANTQ) __builtin_amdgcn_s_setprio(1);
         // the chase stops after the last position any chunk of the
         // wavefront steps through, tested after every second position (one
         // scalar branch per two positions; an extra position steps no chunk)
@@ -557,6 +560,7 @@ __global__ void __launch_bounds__((WANTQ ? (W + 1) * 64 : 256), (pc_min_waves<T,
             sd[me] = dcur;
             se[me - 1] = x;
         }
+        if constexpr (!WANTQ) __builtin_amdgcn_s_setprio(0);
         __builtin_amdgcn_wave_barrier();
         jtot = (sweep & (mu != mu)) ? nmaxit : jtot;
         if constexpr (WANTQ) __syncthreads();  // the log of this pass is complete
