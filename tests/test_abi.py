@@ -104,6 +104,18 @@ def test_query_explicit_lanes(st):
     assert q1["waves_per_block"] == 1 and q1["workgroups"] == 32768 // 16
 
 
+@pytest.mark.parametrize("batch,waves", [(32768, 4), (4096, 1), (8192, 2), (1000, 1), (16384, 4)])
+def test_query_small_batch_spreads_workgroups(st, batch, waves):
+    # order 4 with eigenvectors: 16 problems per wavefront; the default packs
+    # 4 wavefronts per workgroup unless that leaves fewer than 256 workgroups
+    q = st.steqr_query(4, batch, 1, 0)
+    assert q["waves_per_block"] == waves
+    assert q["workgroups"] == -(-batch // (waves * 16))
+    # an explicit choice is kept
+    q4 = st.steqr_query(4, batch, 1, 0, st.make_params(waves_per_block=4))
+    assert q4["waves_per_block"] == 4
+
+
 def test_query_band_storage(st):
     assert st.steqr_query(16, 100, 1, 0)["band_storage"] == 1
     assert st.steqr_query(16, 100, 1, 1)["band_storage"] == 2
