@@ -71,8 +71,9 @@ typedef struct steqr_params {
      * tuned default; otherwise a power of two the build provides for this
      * (dtype, n, jobz); steqr_query() lists it. */
     int lanes_per_problem;
-    /* Wavefronts per workgroup (1, 2 or 4); 0 = default. Launch shape
-     * only: the arithmetic and results do not depend on it. */
+    /* Wavefronts per workgroup (1, 2 or 4); 0 = default (4, fewer when a
+     * small batch would otherwise leave fewer than 256 workgroups). Launch
+     * shape only: the arithmetic and results do not depend on it. */
     int waves_per_block;
     /* Where a chunked kernel keeps the band d, e during the solve:
      * 0 = tuned default, 1 = replicated in every lane's registers,
