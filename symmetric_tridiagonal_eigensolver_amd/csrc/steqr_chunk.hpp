@@ -573,15 +573,33 @@ __global__ void __launch_bounds__(256) steqr_chunk_kernel(KernelArgs args) {
     // index, NaN last [algo, sort paragraph]. Lane r of a chunk ranks keys
     // j = r, r+P, ... and shares the ranks through LDS.
     const bool sort_it = (args.do_sort != 0) & !failed;
+    // with no NaN among the wavefront's keys (a wave-uniform test) the
+    // comparison drops its NaN terms: (d_k, k) precedes (d_j, j) iff
+    // d_k < d_j, or d_k = d_j and k < j (k = j then never counts)
+    bool nan_here = false;
+    static_for<N>([&](auto K) {
+        constexpr int k = decltype(K)::value;
+        nan_here = nan_here | ((k < n) & (d[k] != d[k]));
+    });
+    const bool nonan = !__any(nan_here);
     auto rank_of = [&](T dj, int j) __attribute__((always_inline)) {
-        const bool nanj = dj != dj;
         int rk = 0;
-        static_for<N>([&](auto K) {
-            constexpr int k = decltype(K)::value;
-            const T dk = d[k];
-            const bool before = (k < j) ? ((dk <= dj) | nanj) : ((dk < dj) | (nanj & (dk == dk)));
-            rk += ((k < n) & (k != j) & before) ? 1 : 0;
-        });
+        if (nonan) {
+            static_for<N>([&](auto K) {
+                constexpr int k = decltype(K)::value;
+                const T dk = d[k];
+                rk += ((k < n) & ((dk < dj) | ((dk == dj) & (k < j)))) ? 1 : 0;
+            });
+        } else {
+            const bool nanj = dj != dj;
+            static_for<N>([&](auto K) {
+                constexpr int k = decltype(K)::value;
+                const T dk = d[k];
+                const bool before =
+                    (k < j) ? ((dk <= dj) | nanj) : ((dk < dj) | (nanj & (dk == dk)));
+                rk += ((k < n) & (k != j) & before) ? 1 : 0;
+            });
+        }
         return sort_it ? rk : j;
     };
     int rank[N];

@@ -486,18 +486,36 @@ __global__ void __launch_bounds__(256) steqr_chunkl_kernel(KernelArgs args) {
     // ---------------------------------------------------------------- sort
     __builtin_amdgcn_wave_barrier();
     const bool sort_it = (args.do_sort != 0) & !failed;
+    // with no NaN among the wavefront's keys (a wave-uniform test) the
+    // comparison drops its NaN terms, as in steqr_chunk.hpp
+    bool nan_here = false;
+    static_for<K>([&](auto KK) {
+        constexpr int kk = decltype(KK)::value;
+        const int j = r + kk * P;
+        const T dj = sd[j];
+        nan_here = nan_here | ((j < n) & (dj != dj));
+    });
+    const bool nonan = !__any(nan_here);
     T myd[K];
     int myrank[K];
     static_for<K>([&](auto KK) {
         constexpr int kk = decltype(KK)::value;
         const int j = r + kk * P;
         const T dj = sd[j];
-        const bool nanj = dj != dj;
         int rk = 0;
-        for (int k = 0; k < n; ++k) {
-            const T dk = sd[k];
-            const bool before = (k < j) ? ((dk <= dj) | nanj) : ((dk < dj) | (nanj & (dk == dk)));
-            rk += ((k != j) & before) ? 1 : 0;
+        if (nonan) {
+            for (int k = 0; k < n; ++k) {
+                const T dk = sd[k];
+                rk += ((dk < dj) | ((dk == dj) & (k < j))) ? 1 : 0;
+            }
+        } else {
+            const bool nanj = dj != dj;
+            for (int k = 0; k < n; ++k) {
+                const T dk = sd[k];
+                const bool before =
+                    (k < j) ? ((dk <= dj) | nanj) : ((dk < dj) | (nanj & (dk == dk)));
+                rk += ((k != j) & before) ? 1 : 0;
+            }
         }
         myd[kk] = dj;
         myrank[kk] = sort_it ? rk : j;
