@@ -647,16 +647,32 @@ __global__ void __launch_bounds__(256) steqr_chunk_kernel(KernelArgs args) {
         // the sort's column permutation applied), then copy them to HBM as
         // one contiguous range: the wavefront's problems are consecutive.
         T* const myq = stage + chunk * nn;
-        static_for<R>([&](auto II) {
-            constexpr int i = decltype(II)::value;
-            const int row = r * R + i;
-            if (row < n) {
-                static_for<N>([&](auto J) {
-                    constexpr int j = decltype(J)::value;
-                    if (j < n) myq[row * n + rank[j]] = q[i][j];
+        if (n == N) {
+            // full order (uniform): the lane's rows r*R .. r*R+R-1 lie N
+            // elements apart, so one address per column serves all of them
+            // through the instruction's constant offset
+            static_assert(!WANTQ || R * P == N, "the chunk's lanes hold exactly N rows");
+            T* const base = myq + r * R * N;
+            static_for<N>([&](auto J) {
+                constexpr int j = decltype(J)::value;
+                T* const col = base + rank[j];
+                static_for<R>([&](auto II) {
+                    constexpr int i = decltype(II)::value;
+                    col[i * N] = q[i][j];
                 });
-            }
-        });
+            });
+        } else {
+            static_for<R>([&](auto II) {
+                constexpr int i = decltype(II)::value;
+                const int row = r * R + i;
+                if (row < n) {
+                    static_for<N>([&](auto J) {
+                        constexpr int j = decltype(J)::value;
+                        if (j < n) myq[row * n + rank[j]] = q[i][j];
+                    });
+                }
+            });
+        }
         __builtin_amdgcn_wave_barrier();
         copy_block<T, CH * N * N>(gq + first * nn, stage, nprob * nn, lane, qvec);
     }
