@@ -32,8 +32,9 @@
 //    [algo, the two CTA update schemes].
 //  * Run-time positions (the shift inputs at the converging end, the block
 //    ends, the sort keys) are read from a per-chunk copy of the band in LDS,
-//    republished after every change of the band; register arrays are only
-//    ever indexed by compile-time positions.
+//    kept current after every change of the band (written by the chase's
+//    steps with eigenvectors, republished after the pass without); register
+//    arrays are only ever indexed by compile-time positions.
 //
 // The per-chunk sequence of operations is the one of the steqr algorithm
 // page: split blocks at exact zeros with a running left boundary [algo,
@@ -548,6 +549,19 @@ __global__ void __launch_bounds__(256) steqr_chunk_kernel(KernelArgs args) {
                         e[p + 1] = c * e[p + 1];
                     }
                 }
+                // With eigenvectors the band copy in LDS follows the chase
+                // (every lane of the chunk writes the same words): this
+                // step's final d_p and e_{p-1}, and d_{p+1}, e_p, final after
+                // the sweep's last step. The factor c the EXP step applies to
+                // e_{p+1} at the last step is not copied: that e is zero or
+                // already in `zeroed`. Without eigenvectors the shorter step
+                // measured faster with one publish after the pass.
+                if constexpr (WANTQ) {
+                    if constexpr (p > 0) se[p - 1] = e[p - 1];
+                    sd[p] = d[p];
+                    sd[p + 1] = d[p + 1];
+                    se[p] = e[p];
+                }
                 if constexpr (WANTQ) {
                     static_for<R>([&](auto II) {
                         constexpr int i = decltype(II)::value;
@@ -557,7 +571,8 @@ __global__ void __launch_bounds__(256) steqr_chunk_kernel(KernelArgs args) {
             }
         });
         __builtin_amdgcn_s_setprio(0);
-        publish();
+        if constexpr (WANTQ) __builtin_amdgcn_wave_barrier();
+        else publish();
         // a NaN shift turns [s, m] into NaN, a fixed point of every further
         // sweep: spend the rest of the budget at once (same final state)
         jtot = (sweep & (mu != mu)) ? nmaxit : jtot;
