@@ -206,8 +206,8 @@ def test_uninstantiated_lanes_rejected_by_query(st):
 
 @pytest.mark.parametrize("n,jobz,dtype,N,P,R", [
     (1, 1, 0, 4, 4, 1), (4, 1, 0, 4, 4, 1), (5, 1, 0, 8, 2, 4), (16, 1, 0, 16, 4, 4),
-    (16, 0, 0, 16, 4, 4), (12, 1, 1, 16, 8, 2), (17, 1, 0, 32, 16, 2), (32, 1, 1, 32, 16, 2),
-    (8, 0, 1, 8, 4, 2), (32, 0, 0, 32, 8, 4), (16, 0, 1, 16, 4, 4), (16, 1, 1, 16, 8, 2)])
+    (16, 0, 0, 16, 4, 4), (12, 1, 1, 16, 4, 4), (17, 1, 0, 32, 16, 2), (32, 1, 1, 32, 16, 2),
+    (8, 0, 1, 8, 4, 2), (32, 0, 0, 32, 8, 4), (16, 0, 1, 16, 4, 4), (16, 1, 1, 16, 4, 4)])
 def test_syev_default_plans(st, n, jobz, dtype, N, P, R):
     q = st.syev_query(n, 32768, jobz, dtype)
     assert (q["padded_n"], q["lanes_per_problem"], q["rows_per_lane"]) == (N, P, R)
