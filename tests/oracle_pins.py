@@ -290,6 +290,96 @@ def pin_solve(oracle, libpath: Optional[str] = None, quick: bool = False,
     return out
 
 
+def _graded(n: int, batch: int, dt, small_end_top: bool):
+    """Graded items of the workload recipe (d_i = 10^(-i/2), coupling
+    z_i sqrt(d_i d_{i+1})): the small end is the bottom; reversed, the top."""
+    d, e = W.edge_batch(W.EDGE_NAMES.index("graded"), n, batch, np.float64)
+    if small_end_top:
+        d, e = d[:, ::-1].copy(), e[:, ::-1].copy()
+    return d.astype(dt), e.astype(dt)
+
+
+def pin_direction(oracle, libpath: Optional[str] = None, quick: bool = False,
+                  scheme: int = 0, shift: int = 0) -> List[str]:
+    """The choice of the converging end ("STEQR: the CTA tridiagonal solver",
+    micro-structure list, QL versus QR; the steqr algorithm page, QR/QL
+    paragraph): a graded block must converge its small end first. The CTA
+    page reports that the opposite rule needed about twice the steps and
+    lost relative accuracy on graded input. Pinned on graded items with the
+    small end at the bottom and, reversed, at the top (a rule that always or
+    never reverses fails one of the two):
+      * implicit sweeps per eigenvalue, averaged over the batch, at most 1.5
+        (the right rule takes 1.0-1.3 at orders 8-32; the opposite one 1.6-2.4);
+      * every eigenvalue within a relative error of 2^-10 (float) or 2^-30
+        (double) of its long-double Sturm value (the right rule stays below
+        5e-4 / 4e-13; the opposite one loses every digit of the small
+        eigenvalues at order 32);
+      * the normwise residual and orthogonality bounds still hold.
+    """
+    out: List[str] = []
+    for dt, rel_tol in ((np.float32, 2.0 ** -10), (np.float64, 2.0 ** -30)):
+        for n in ((16, 32) if quick else (8, 16, 32)):
+            for top in (False, True):
+                d, e = _graded(n, 16 if quick else 64, dt, top)
+                lam, Q, info, st = oracle.steqr(d, e, True, libpath=libpath,
+                                                scheme=scheme, shift=shift)
+                tag = "%s n=%d small end %s" % (dt.__name__, n, "top" if top else "bottom")
+                _fail(out, not info.any(), "graded solve info != 0 (%s)" % tag)
+                per_eig = st[:, 0].mean() / n
+                _fail(out, per_eig <= 1.5, "graded sweeps per eigenvalue %.2f > 1.5 (%s)"
+                      % (per_eig, tag))
+                ref = np.sort(V.sturm_eigvals(d, e).astype(np.float64), axis=1)
+                got = np.sort(lam.astype(np.float64), axis=1)
+                rel = np.abs(got - ref) / np.abs(ref)
+                _fail(out, rel.max() <= rel_tol, "graded relative error %.3g > %.3g (%s)"
+                      % (rel.max(), rel_tol, tag))
+                tol = V.tol_of(dt, n)
+                _fail(out, V.band_residual(d, e, lam, Q).max() <= tol
+                      and V.orthogonality(Q).max() <= tol, "graded residual (%s)" % tag)
+    return out
+
+
+def pin_block2(oracle, libpath: Optional[str] = None, quick: bool = False,
+               scheme: int = 0, shift: int = 0) -> List[str]:
+    """A block of order 2 is solved in closed form (steqr algorithm page,
+    2x2 block paragraph), not by implicit sweeps: order-2 items and items
+    split into 2x2 blocks by exact zeros take no sweep at all (so they also
+    converge with a sweep budget of zero), count one analytic solve per
+    block, and return the closed-form eigenvalues (a+c)/2 +- sqrt(((a-c)/2)^2
+    + b^2) of each block (long double) within 8 eps ||T||, with eigenvectors
+    meeting the residual and orthogonality bounds."""
+    out: List[str] = []
+    for dt in (np.float32, np.float64):
+        eps = V.eps_of(dt)
+        for n, zeros in ((2, ()), (8, (1, 3, 5)), (12, (1, 3, 5, 7, 9))):
+            d, e = W.random_batch(n, 24, dt, salt=31)
+            for z in zeros:
+                e[:, z] = 0
+            blocks = n // 2
+            tn = V.tnorm1(d, e)
+            A = d[:, 0::2].astype(np.longdouble)
+            C = d[:, 1::2].astype(np.longdouble)
+            B = np.concatenate([e, np.zeros((e.shape[0], 1), dt)], 1)[:, 0::2].astype(np.longdouble)
+            mid, rad = (A + C) / 2, np.sqrt(((A - C) / 2) ** 2 + B * B)
+            ref = np.sort(np.concatenate([mid - rad, mid + rad], 1).astype(np.float64), axis=1)
+            for budget in (30, 0):
+                lam, Q, info, st = oracle.steqr(d, e, True, max_sweeps_per_n=budget,
+                                                libpath=libpath, scheme=scheme, shift=shift)
+                tag = "%s n=%d budget %d" % (dt.__name__, n, budget)
+                _fail(out, not info.any(), "2x2 blocks did not converge (%s)" % tag)
+                _fail(out, np.all(st[:, 0] == 0) and np.all(st[:, 1] == 0),
+                      "2x2 blocks took implicit sweeps (%s)" % tag)
+                _fail(out, np.all(st[:, 2] == blocks), "2x2 blocks: %s analytic solves, "
+                      "expected %d (%s)" % (np.unique(st[:, 2]), blocks, tag))
+                err = np.abs(np.sort(lam.astype(np.float64), axis=1) - ref).max(1) / tn
+                _fail(out, err.max() <= 8 * eps, "2x2 blocks against the closed form: %g (%s)"
+                      % (err.max(), tag))
+                tol = V.tol_of(dt, n)
+                _fail(out, V.band_residual(d, e, lam, Q).max() <= tol
+                      and V.orthogonality(Q).max() <= tol, "2x2 blocks residual (%s)" % tag)
+    return out
+
+
 def pin_back_transform(oracle, libpath: Optional[str] = None, quick: bool = False,
                        scheme: int = 0, shift: int = 0) -> List[str]:
     """Eigenvector accumulation with a basis on entry (algorithm page,
@@ -521,7 +611,8 @@ def pin_stebz(oracle, libpath: Optional[str] = None) -> List[str]:
     return out
 
 
-ALL_PINS = (pin_lartg, pin_shift, pin_sym2x2, pin_sweep, pin_solve, pin_back_transform,
+ALL_PINS = (pin_lartg, pin_shift, pin_sym2x2, pin_sweep, pin_solve, pin_direction,
+            pin_block2, pin_back_transform,
             pin_larfg, pin_sytrd, pin_syev, pin_stebz)
 
 
@@ -529,9 +620,10 @@ def run_all(oracle, libpath: Optional[str] = None, quick: bool = True) -> List[s
     """Every pin; the sweep and whole-solve pins for both update schemes."""
     fails: List[str] = []
     for p in ALL_PINS:
-        for scheme in ((0, 1) if p in (pin_sweep, pin_solve, pin_back_transform) else (0,)):
+        multi = p in (pin_sweep, pin_solve, pin_direction, pin_block2, pin_back_transform)
+        for scheme in ((0, 1) if multi else (0,)):
             try:
-                if p in (pin_solve, pin_back_transform):
+                if p in (pin_solve, pin_direction, pin_block2, pin_back_transform):
                     for shift in (0, 1):
                         fails += [f + " [scheme %d, shift %d]" % (scheme, shift)
                                   for f in p(oracle, libpath, quick=quick, scheme=scheme,

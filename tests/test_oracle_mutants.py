@@ -42,6 +42,13 @@ MUTANTS = [
      "Q[row * n + j] = qtmp[row * n + j];"),
     ("reverse_e_off_by_one", "for (int i = l, j = hi - 1; i < j; ++i, --j) {",
      "for (int i = l, j = hi; i < j; ++i, --j) {"),
+    # the choice of the converging end (CTA page, QL versus QR) and the
+    # closed-form solve of 2x2 blocks (algorithm page, 2x2 block paragraph)
+    ("direction_inverted", "int rev = !(R_FABS(d[hi]) < R_FABS(d[l]));",
+     "int rev = (R_FABS(d[hi]) < R_FABS(d[l]));"),
+    ("direction_never_reversed", "int rev = !(R_FABS(d[hi]) < R_FABS(d[l]));", "int rev = 0;"),
+    ("direction_always_reversed", "int rev = !(R_FABS(d[hi]) < R_FABS(d[l]));", "int rev = 1;"),
+    ("no_analytic_2x2", "if (s == m - 1) {", "if (0) {"),
     ("deflation_wrong_pair", "if (SFX(negligible)(e[k - 1], d[k - 1], d[k])) {",
      "if (SFX(negligible)(e[k - 1] * (REAL)1e-3, d[k - 1], d[k])) {"),
     # the PG form of the sweep
