@@ -32,14 +32,18 @@
  * stream); results are valid once that stream is synchronised.
  *
  * Errors: 0 on success. A negative value -k names the first invalid
- * argument in the order of steqr_batched's parameter list (LAPACK style):
+ * argument in the order of steqr_batched's parameter list (LAPACK style;
+ * the array pointers are checked first, then n, batch, jobz, dtype and
+ * finally the params of steqr_batched_ex):
  *   -1 d == NULL (n > 0, batch > 0)     -2 e == NULL (n > 1, batch > 0)
  *   -3 lambda == NULL                   -4 Q == NULL with jobz == STEQR_V
  *   -5 n < 0 or n > STEQR_MAX_N         -6 batch < 0
  *   -7 jobz not STEQR_N / STEQR_V       -8 dtype not STEQR_F32 / STEQR_F64
  *   -10 (steqr_batched_ex only) a params field out of range
- * A positive value is a hipError_t returned by the kernel launch. n == 0 or
- * batch == 0 returns 0 at once without touching the GPU.
+ * A positive value is a hipError_t returned by the kernel launch (an error
+ * pending from an earlier HIP call is cleared before the launch, so the
+ * value is this launch's). n == 0 or batch == 0 returns 0 at once without
+ * touching the GPU.
  */
 #ifndef STEQR_H
 #define STEQR_H
@@ -175,7 +179,8 @@ int steqr_query(int n, int batch, int jobz, int dtype, const steqr_params *param
  *
  * Errors (0 on success; -k names the k-th argument):
  *   -1 A == NULL          -2 lambda == NULL      -3 Q == NULL with STEQR_V
- *   -4 n < 0 or n > SYEV_MAX_N                   -5 batch < 0
+ *   -4 n < 0 or n > SYEV_MAX_N (SYEV_MAX_N_F64_V for double with
+ *      eigenvectors)                             -5 batch < 0
  *   -6 jobz invalid       -7 dtype invalid
  *   -10 (_ex) params: update_scheme other than STEQR_EXP, back_transform
  *       set, band_storage other than 0/1, or a lanes_per_problem /
@@ -183,6 +188,9 @@ int steqr_query(int n, int batch, int jobz, int dtype, const steqr_params *param
  * A positive value is a hipError_t from the launch; n == 0 or batch == 0
  * returns 0 without touching the GPU. */
 #define SYEV_MAX_N 32
+/* Double precision with eigenvectors: rows of A and Q and the band of an
+ * order-32 problem do not fit 256 registers per lane. */
+#define SYEV_MAX_N_F64_V 16
 
 int syev_batched(const void *A, void *lambda, void *Q, int n, int batch, int jobz, int dtype,
                  hipStream_t stream);

@@ -20,6 +20,7 @@ STEQR_SHIFT_LAPACK, STEQR_SHIFT_CLOSED = 0, 1
 STEQR_METHOD_QR, STEQR_METHOD_BISECT = 0, 1
 STEQR_MAX_N = 128
 SYEV_MAX_N = 32
+SYEV_MAX_N_F64_V = 16
 
 
 class steqr_params(ct.Structure):

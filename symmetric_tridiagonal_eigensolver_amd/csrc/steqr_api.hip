@@ -47,9 +47,11 @@ int default_lanes(int dtype, int N, int jobz, int band) {
     if (jobz) {
         if (N == 4) return 4;
         if (N == 8) return dtype == STEQR_F32 ? 2 : 4;
-        if (N == 16) return 4;
+        // double with the band in registers at 4 lanes needs more than
+        // 256 registers per lane and is not built: 8 lanes there
+        if (N == 16) return (dtype == STEQR_F64 && band == 1) ? 8 : 4;
         if (band == 2) return dtype == STEQR_F32 ? 8 : 16;  // N == 32
-        return 16;
+        return 16;  // double, band in registers: not built (-10)
     }
     // values only in float: the split deflation scan pays at 4 lanes for
     // order 32 (-3% against 2) and 2 lanes beat 1 at order 16 (-2%)
@@ -216,14 +218,17 @@ extern "C" int steqr_query(int n, int batch, int jobz, int dtype, const steqr_pa
 extern "C" int steqr_batched_ex(const void* d, const void* e, void* lambda, void* Q, int n,
                                 int batch, int jobz, int dtype, hipStream_t stream, int* info,
                                 const steqr_params* params) {
+    // arguments in the order of the parameter list: a NULL array is an
+    // error only where the call has work to do (n > 0 and batch > 0)
+    const bool work = n > 0 && batch > 0;
+    if (work && d == nullptr) return -1;
+    if (work && n > 1 && e == nullptr) return -2;
+    if (work && lambda == nullptr) return -3;
+    if (work && jobz == STEQR_V && Q == nullptr) return -4;
     Plan p;
-    int rc = plan_launch(n, batch, jobz, dtype, params, &p);
+    const int rc = plan_launch(n, batch, jobz, dtype, params, &p);
     if (rc != 0) return rc;
     if (n == 0 || batch == 0) return 0;
-    if (d == nullptr) return -1;
-    if (n > 1 && e == nullptr) return -2;
-    if (lambda == nullptr) return -3;
-    if (jobz == STEQR_V && Q == nullptr) return -4;
     steqr::KernelArgs a{};
     a.d = d;
     a.e = e;
@@ -237,6 +242,8 @@ extern "C" int steqr_batched_ex(const void* d, const void* e, void* lambda, void
     a.do_sort = params ? !params->no_sort : 1;
     a.shift_kind = params ? params->shift : 0;
     a.back_transform = params ? params->back_transform : 0;
+    // an error left by an earlier, unrelated HIP call is not this launch's
+    (void)hipGetLastError();
     const hipError_t err = p.entry->fn(a, p.grid, p.waves * 64, stream);
     return err == hipSuccess ? 0 : (int)err;
 }
@@ -258,12 +265,16 @@ namespace {
 int syev_default_lanes(int dtype, int N, int jobz) {
     if (N == 4) return 4;
     if (N == 8) return dtype == STEQR_F32 ? 2 : 4;
-    if (N == 16) return 4;  // double with vectors: 271 against 351 us at 8 lanes
-    return (dtype == STEQR_F32 && !jobz) ? 8 : 16;
+    // double with vectors at 4 lanes (271 against 351 us at 8) needs more
+    // than 256 registers per lane and is not built
+    if (N == 16) return (dtype == STEQR_F64 && jobz) ? 8 : 4;
+    if (dtype == STEQR_F64) return 32;  // values only (no order-32 double with vectors)
+    return jobz ? 16 : 8;
 }
 
 int syev_plan(int n, int batch, int jobz, int dtype, const steqr_params* prm, Plan* out) {
     if (n < 0 || n > SYEV_MAX_N) return -4;
+    if (dtype == STEQR_F64 && jobz == STEQR_V && n > SYEV_MAX_N_F64_V) return -4;
     if (batch < 0) return -5;
     if (jobz != STEQR_N && jobz != STEQR_V) return -6;
     if (dtype != STEQR_F32 && dtype != STEQR_F64) return -7;
@@ -326,13 +337,14 @@ extern "C" int syev_query(int n, int batch, int jobz, int dtype, const steqr_par
 extern "C" int syev_batched_ex(const void* A, void* lambda, void* Q, int n, int batch, int jobz,
                                int dtype, hipStream_t stream, int* info,
                                const steqr_params* params) {
+    const bool work = n > 0 && batch > 0;
+    if (work && A == nullptr) return -1;
+    if (work && lambda == nullptr) return -2;
+    if (work && jobz == STEQR_V && Q == nullptr) return -3;
     Plan p;
     const int rc = syev_plan(n, batch, jobz, dtype, params, &p);
     if (rc != 0) return rc;
     if (n == 0 || batch == 0) return 0;
-    if (A == nullptr) return -1;
-    if (lambda == nullptr) return -2;
-    if (jobz == STEQR_V && Q == nullptr) return -3;
     steqr::KernelArgs a{};
     a.a = A;
     a.lam = lambda;
@@ -345,6 +357,7 @@ extern "C" int syev_batched_ex(const void* A, void* lambda, void* Q, int n, int 
     a.do_sort = params ? !params->no_sort : 1;
     a.shift_kind = params ? params->shift : 0;
     a.back_transform = 0;
+    (void)hipGetLastError();  // clear an earlier call's error
     const hipError_t err = p.entry->fn(a, p.grid, p.waves * 64, stream);
     return err == hipSuccess ? 0 : (int)err;
 }

@@ -8,7 +8,6 @@ namespace steqr {
 static const Entry kEntries[] = {
     STEQR_PC_ENTRY(0, float, 128, 12, 16),
     STEQR_PC_ENTRY(0, float, 128, 8, 32),
-    STEQR_PC_ENTRY(0, float, 128, 4, 64),
     // whole rows of Q per lane: two consumers per problem, five problems
     STEQR_PCR_ENTRY(0, float, 128, 10, 8, 1),
     STEQR_PC_ENTRY(1, double, 128, 8, 16),

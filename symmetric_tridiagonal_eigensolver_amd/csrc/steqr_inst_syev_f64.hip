@@ -5,8 +5,11 @@ namespace steqr {
 
 #define E(N, P, Q) STEQR_SYEV_ENTRY(1, double, N, P, Q)
 static const Entry kEntries[] = {
-    E(4, 4, 1), E(8, 4, 1), E(16, 8, 1), E(16, 4, 1), E(32, 16, 1),
-    E(4, 4, 0), E(8, 4, 0), E(8, 2, 0), E(16, 8, 0), E(16, 4, 0), E(32, 16, 0),
+    // with eigenvectors, (16, 4) and every order-32 shape need more than
+    // 256 registers per lane (rows of A and Q plus the band): double with
+    // eigenvectors stops at order 16
+    E(4, 4, 1), E(8, 4, 1), E(16, 8, 1),
+    E(4, 4, 0), E(8, 4, 0), E(8, 2, 0), E(16, 8, 0), E(16, 4, 0), E(32, 32, 0),
 };
 #undef E
 

@@ -324,20 +324,21 @@ __global__ void __launch_bounds__((WANTQ ? (W + 1) * 64 : 256), (pc_min_waves<T,
 
     // reverse the chunk's band (lane-parallel); Q's columns are the
     // consumer's: count the reversal
+    // Each lane swaps whole pairs (p, N-1-p) of d and (p, N-2-p) of e for
+    // its positions p = r + kP in the first half, so no value crosses lanes
+    // and at most two pairs are held in registers at a time.
     auto mirror_all = [&]() __attribute__((always_inline)) {
-        T dv[K], ev[K];
-        static_for<K>([&](auto KK) {
+        static_for<K / 2>([&](auto KK) {
             constexpr int k = decltype(KK)::value;
-            const int p = r + k * P;
-            dv[k] = sd[N - 1 - p];
-            ev[k] = se[p < N - 1 ? N - 2 - p : N - 1];
-        });
-        __builtin_amdgcn_wave_barrier();
-        static_for<K>([&](auto KK) {
-            constexpr int k = decltype(KK)::value;
-            const int p = r + k * P;
-            sd[p] = dv[k];
-            se[p] = ev[k];
+            const int p = r + k * P;  // p < N/2
+            const T da = sd[p], db = sd[N - 1 - p];
+            sd[p] = db;
+            sd[N - 1 - p] = da;
+            if (p < N / 2 - 1) {
+                const T ea = se[p], eb = se[N - 2 - p];
+                se[p] = eb;
+                se[N - 2 - p] = ea;
+            }
         });
         __builtin_amdgcn_wave_barrier();
         flip ^= 1;
@@ -456,6 +457,9 @@ __global__ void __launch_bounds__((WANTQ ? (W + 1) * 64 : 256), (pc_min_waves<T,
                     });
                     info = popc(chunk_or_mask<P>(part));
                     info = info > 0 ? info : 1;
+                    // the status is final: store it now rather than keep
+                    // it in a register through the remaining passes
+                    if (live & (args.info != nullptr) & (r == 0)) args.info[prob] = info;
                 }
                 state = fail ? ST_DONE : ST_OPEN;
             }
@@ -631,12 +635,15 @@ __global__ void __launch_bounds__((WANTQ ? (W + 1) * 64 : 256), (pc_min_waves<T,
         srank[j] = myrank[kk];
     });
     if (live) {
+        // addressed from the wavefront's first problem (scalar) and the
+        // chunk index, so no 64-bit problem index stays live through the loop
+        T* const glw = glam + first * n;
         static_for<K>([&](auto KK) {
             constexpr int kk = decltype(KK)::value;
             const int j = r + kk * P;
-            if (j < n) glam[prob * n + myrank[kk]] = myd[kk];
+            if (j < n) glw[chunk * n + myrank[kk]] = myd[kk];
         });
-        if (args.info != nullptr && r == 0) args.info[prob] = info;
+        if (args.info != nullptr && r == 0 && !failed) (args.info + first)[chunk] = 0;
     }
     if constexpr (WANTQ) __syncthreads();  // ranks and final parity are visible to the consumers
 }

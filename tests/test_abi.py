@@ -6,6 +6,7 @@ import os
 import re
 import subprocess
 
+import numpy as np
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -85,8 +86,14 @@ def test_query_producer_consumer_plans(st):
         q = st.steqr_query(50, 700, 1, dtype)
         assert q["band_storage"] == 3 and q["waves_per_block"] == w + 1
         assert q["workgroups"] == -(-700 // w)
-        q2 = st.steqr_query(50, 700, 1, dtype, st.make_params(band_storage=2))
-        assert q2["band_storage"] == 2 and q2["lanes_per_problem"] == 64
+        if dtype == 0:
+            q2 = st.steqr_query(50, 700, 1, dtype, st.make_params(band_storage=2))
+            assert q2["band_storage"] == 2 and q2["lanes_per_problem"] == 64
+        else:
+            # one problem per wavefront in double with eigenvectors needs
+            # more than 256 registers per lane: not built
+            with pytest.raises(st.SteqrError):
+                st.steqr_query(50, 700, 1, dtype, st.make_params(band_storage=2))
         q3 = st.steqr_query(50, 700, 1, dtype, st.make_params(band_storage=1))
         assert q3["band_storage"] == 3
     for n, jobz in ((50, 0), (16, 1), (32, 1)):
@@ -141,6 +148,11 @@ def test_query_band_storage(st):
     ((8, 8, 8, 8, 4, -1, 1, 0), -6),
     ((8, 8, 8, 8, 4, 10, 2, 0), -7),
     ((8, 8, 8, 8, 4, 10, 1, 5), -8),
+    # the first invalid argument in parameter order wins
+    ((0, 8, 8, 8, 4, 10, 2, 0), -1),     # NULL d before a bad jobz
+    ((8, 8, 0, 8, 4, 10, 1, 7), -3),     # NULL lambda before a bad dtype
+    ((8, 8, 8, 0, 200, 10, 1, 0), -4),   # NULL Q before an unsupported n
+    ((0, 8, 8, 8, -1, 10, 1, 0), -5),    # no work (n < 0): NULL d is not an error
     ((0, 0, 0, 0, 0, 10, 1, 0), 0),      # n == 0: quick return
     ((0, 0, 0, 0, 4, 0, 1, 0), 0),       # batch == 0: quick return
 ])
@@ -167,6 +179,10 @@ def test_bad_params(st):
         prm = st.make_params()
         prm.back_transform = bt
         assert L.steqr_batched_ex(8, 8, 8, 8, 16, 10, 1, 0, None, None, ctypes.byref(prm)) == -10
+    # a NULL array is reported before a bad params field
+    prm = st.make_params(lanes_per_problem=3)
+    assert L.steqr_batched_ex(8, 8, None, 8, 16, 10, 1, 0, None, None, ctypes.byref(prm)) == -3
+    assert L.steqr_batched_ex(None, 8, 8, 8, 16, 10, 1, 0, None, None, ctypes.byref(prm)) == -1
     # back-transformation needs eigenvectors
     prm = st.make_params(back_transform=True)
     assert L.steqr_batched_ex(8, 8, 8, 8, 16, 10, 0, 0, None, None, ctypes.byref(prm)) == -10
@@ -206,8 +222,8 @@ def test_uninstantiated_lanes_rejected_by_query(st):
 
 @pytest.mark.parametrize("n,jobz,dtype,N,P,R", [
     (1, 1, 0, 4, 4, 1), (4, 1, 0, 4, 4, 1), (5, 1, 0, 8, 2, 4), (16, 1, 0, 16, 4, 4),
-    (16, 0, 0, 16, 4, 4), (12, 1, 1, 16, 4, 4), (17, 1, 0, 32, 16, 2), (32, 1, 1, 32, 16, 2),
-    (8, 0, 1, 8, 4, 2), (32, 0, 0, 32, 8, 4), (16, 0, 1, 16, 4, 4), (16, 1, 1, 16, 4, 4)])
+    (16, 0, 0, 16, 4, 4), (12, 1, 1, 16, 8, 2), (17, 1, 0, 32, 16, 2), (32, 0, 1, 32, 32, 1),
+    (8, 0, 1, 8, 4, 2), (32, 0, 0, 32, 8, 4), (16, 0, 1, 16, 4, 4), (16, 1, 1, 16, 8, 2)])
 def test_syev_default_plans(st, n, jobz, dtype, N, P, R):
     q = st.syev_query(n, 32768, jobz, dtype)
     assert (q["padded_n"], q["lanes_per_problem"], q["rows_per_lane"]) == (N, P, R)
@@ -219,6 +235,7 @@ def test_syev_argument_errors(st):
     L = st.lib()
     # validation happens before any launch (the pointers are not device memory)
     assert L.syev_batched(8, 8, 8, 33, 10, 1, 0, None) == -4
+    assert L.syev_batched(8, 8, 8, 17, 10, 1, 1, None) == -4   # double with vectors: n <= 16
     assert L.syev_batched(8, 8, 8, -1, 10, 1, 0, None) == -4
     assert L.syev_batched(8, 8, 8, 16, -1, 1, 0, None) == -5
     assert L.syev_batched(8, 8, 8, 16, 10, 2, 0, None) == -6
@@ -226,6 +243,8 @@ def test_syev_argument_errors(st):
     assert L.syev_batched(None, 8, 8, 16, 10, 1, 0, None) == -1
     assert L.syev_batched(8, None, 8, 16, 10, 1, 0, None) == -2
     assert L.syev_batched(8, 8, None, 16, 10, 1, 0, None) == -3
+    assert L.syev_batched(None, 8, 8, 16, 10, 2, 0, None) == -1   # NULL A before a bad jobz
+    assert L.syev_batched(8, None, 8, 40, 10, 1, 0, None) == -2   # NULL lambda before n
     assert L.syev_batched(None, None, None, 0, 10, 1, 0, None) == 0
     assert L.syev_batched(None, None, None, 16, 0, 1, 0, None) == 0
     for prm in (st.make_params(update_scheme=st.STEQR_PG), st.make_params(back_transform=True),
@@ -264,3 +283,46 @@ def test_bisect_argument_errors(st):
     assert st.steqr_query(12, 10, 0, 0, st.make_params(method=1, lanes_per_problem=16))["padded_n"] == 16
     # syev does not take the bisection method
     assert L.syev_batched_ex(8, 8, 8, 16, 10, 0, 0, None, None, ctypes.byref(prm)) == -10
+
+
+def _case_lists():
+    """The (dtype, n, jobz, lanes, band, scheme) launches the GPU tests make."""
+    import test_gpu_back_transform as BT
+    import test_gpu_big as BIG
+    import test_gpu_parity as GP
+    import test_gpu_pg as PGT
+    out = []
+    for c in GP.LANE_CASES:
+        if hasattr(c, "values"):  # a skipped pytest.param: not launched
+            continue
+        dt, n, jobz, lanes, band = c
+        out.append((dt, n, jobz, lanes, band, 0))
+    for dt, n, jobz, lanes, band in PGT.PG_LANES:
+        out.append((dt, n, jobz, lanes, band, 1))
+    for dt, n, lanes, band in BT.KERNEL_CASES:
+        out += [(dt, n, True, lanes, band, 0), (dt, n, True, lanes, band, 1)]
+    for mark in BIG.test_big_producer_shapes.pytestmark:
+        if mark.name == "parametrize":
+            out += [(dt, n, True, lanes, 0, 0) for dt, lanes in mark.args[1] for n in (80, 128)]
+    for dt in (np.float32, np.float64):
+        for band in (1, 2):
+            for n in ((9, 16) if (dt == np.float64 and band == 1) else (9, 16, 32)):
+                out.append((dt, n, True, 0, band, 0))
+    return out
+
+
+def test_gpu_test_cases_have_built_kernels(st):
+    """Every launch shape the GPU tests request has a built kernel (no
+    GPU needed: steqr_query plans without launching)."""
+    for dt, n, jobz, lanes, band, scheme in _case_lists():
+        code = st.STEQR_F32 if dt == np.float32 else st.STEQR_F64
+        st.steqr_query(n, 777, int(jobz), code,
+                       st.make_params(lanes_per_problem=lanes, band_storage=band,
+                                      update_scheme=scheme))
+
+
+def test_syev_test_cases_have_built_kernels(st):
+    import test_gpu_syev as SY
+    for dt, n, lanes, jobz in SY.CASES:
+        code = st.STEQR_F32 if dt == np.float32 else st.STEQR_F64
+        st.syev_query(n, 777, int(jobz), code, st.make_params(lanes_per_problem=lanes))

@@ -30,10 +30,10 @@ def _gpu():
 KERNEL_CASES = [
     (np.float32, 4, 4, 1), (np.float32, 8, 2, 1), (np.float32, 16, 4, 1), (np.float32, 13, 4, 1),
     (np.float32, 16, 16, 1), (np.float32, 32, 16, 1), (np.float32, 3, 1, 1),
-    (np.float64, 8, 4, 1), (np.float64, 16, 8, 1), (np.float64, 32, 16, 1),
+    (np.float64, 8, 4, 1), (np.float64, 16, 8, 1), (np.float64, 16, 16, 1),
     (np.float32, 16, 4, 2), (np.float32, 32, 8, 2), (np.float32, 27, 8, 2),
     (np.float64, 16, 4, 2), (np.float64, 32, 16, 2), (np.float64, 12, 4, 2),
-    (np.float32, 64, 64, 2), (np.float64, 64, 64, 2), (np.float64, 45, 64, 2),
+    (np.float32, 64, 64, 2), (np.float32, 45, 64, 2),
     (np.float32, 64, 16, 3), (np.float64, 64, 4, 3), (np.float64, 33, 16, 3),
     (np.float32, 50, 16, 3),
 ]

@@ -82,7 +82,6 @@ def test_big_unsorted_and_budget(dt):
 
 
 @pytest.mark.parametrize("dt,lanes", [(np.float32, 8), (np.float32, 16), (np.float32, 32),
-                                      (np.float32, 64),
                                       (np.float64, 16), (np.float64, 32)],
                          ids=lambda v: v.__name__ if isinstance(v, type) else str(v))
 def test_big_producer_shapes(dt, lanes):

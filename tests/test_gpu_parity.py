@@ -72,18 +72,18 @@ LANE_CASES = [
     (np.float32, 4, True, 4), (np.float32, 4, True, 2), (np.float32, 4, True, 1),
     (np.float32, 8, True, 8), (np.float32, 8, True, 4), (np.float32, 8, True, 2),
     (np.float32, 16, True, 16), (np.float32, 16, True, 8), (np.float32, 16, True, 4),
-    (np.float32, 32, True, 32), (np.float32, 32, True, 16), (np.float32, 32, True, 8),
+    (np.float32, 32, True, 32), (np.float32, 32, True, 16),
     (np.float32, 4, False, 1), (np.float32, 8, False, 1), (np.float32, 16, False, 4),
     (np.float32, 16, False, 1), (np.float32, 32, False, 4), (np.float32, 32, False, 1),
     (np.float64, 4, True, 2), (np.float64, 8, True, 4), (np.float64, 16, True, 8),
-    (np.float64, 32, True, 16), (np.float64, 4, False, 1), (np.float64, 8, False, 1),
+    (np.float64, 4, False, 1), (np.float64, 8, False, 1),
     (np.float64, 16, False, 1), (np.float64, 32, False, 1),
     (np.float32, 16, True, 2), (np.float32, 8, True, 1), (np.float32, 8, False, 2),
-    (np.float32, 16, False, 2), (np.float32, 32, False, 2), (np.float64, 16, True, 4),
+    (np.float32, 16, False, 2), (np.float32, 32, False, 2),
     (np.float64, 8, True, 2), (np.float64, 4, True, 4), (np.float64, 8, False, 2),
     (np.float32, 64, True, 64), (np.float32, 64, False, 64), (np.float64, 64, False, 64),
-    (np.float64, 64, True, 64), (np.float64, 48, True, 64), (np.float32, 33, True, 64),
-    (np.float64, 16, False, 2), (np.float64, 32, False, 2), (np.float64, 32, True, 32),
+    (np.float32, 33, True, 64),
+    (np.float64, 16, False, 2), (np.float64, 32, False, 2),
 ]
 
 
@@ -110,6 +110,22 @@ LANE_CASES += [
 ]
 
 
+# Variants that need more than 256 registers per lane are not built (the
+# build rejects them): the LDS-band kernel in double at order 32 with 8 lanes
+# per problem returned wrong eigenvectors on the GPU in one build, with
+# correct eigenvalues, and its cause was not found; the register-band
+# kernels at these lanes and the one-problem-per-wavefront kernel in double
+# with eigenvectors share the register budget. Kept as skipped cases.
+OVER_BUDGET = [
+    (np.float64, 32, True, 8, 2), (np.float32, 32, True, 4, 2),
+    (np.float32, 32, True, 8, 1), (np.float64, 16, True, 4, 1), (np.float64, 32, True, 16, 1),
+    (np.float64, 32, True, 32, 1), (np.float64, 64, True, 64, 2), (np.float64, 48, True, 64, 2),
+]
+LANE_CASES += [pytest.param(*c, marks=pytest.mark.skip(
+    reason="needs more than 256 registers per lane: not built (wrong eigenvectors in one "
+           "build of double order 32 at 8 lanes, cause not found)")) for c in OVER_BUDGET]
+
+
 @pytest.mark.parametrize("dt,n,jobz,lanes,band", LANE_CASES,
                          ids=lambda v: v.__name__ if isinstance(v, type) else str(v))
 def test_lanes_per_problem_variants(dt, n, jobz, lanes, band):
@@ -123,8 +139,10 @@ def test_lanes_per_problem_variants(dt, n, jobz, lanes, band):
 @pytest.mark.parametrize("dt", [np.float32, np.float64], ids=["f32", "f64"])
 @pytest.mark.parametrize("band", [1, 2], ids=["regs", "lds"])
 def test_band_storage_variants_on_edge_items(dt, band):
+    # double with eigenvectors keeps the band in registers up to order 16
+    orders = (9, 16) if (dt == np.float64 and band == 1) else (9, 16, 32)
     for kind in range(5):
-        for n in (9, 16, 32):
+        for n in orders:
             d, e = W.edge_batch(kind, n, 70, dt, salt=3)
             g = run_gpu(d, e, True, band=band)
             o = oracle.steqr(d, e, True)
@@ -263,3 +281,59 @@ def test_accuracy_margins_report():
         og = V.orthogonality(g[1][ok]).max() / tol
         print("margin %-12s eig %.3f  residual %.3f  orth %.3f" % (wname, ev, rs, og), flush=True)
         assert max(ev, rs, og) <= 1.0
+
+
+@pytest.mark.parametrize("wname,jobz", [("c2_f32_n16", True), ("c4_f64_n32", False),
+                                        ("c3_f64_n12", True)])
+def test_plain_entry_point(wname, jobz):
+    """The 9-argument steqr_batched (no status, no params) on a full
+    workload batch: the same launch as steqr_batched_ex with defaults, so
+    its outputs are bit-identical to that call's; a sample checked against
+    the oracle."""
+    import torch
+    import symmetric_tridiagonal_eigensolver_amd as st
+    w = W.WORKLOADS[wname]
+    _case(w, jobz, w.batch)
+    d, e = W.make_batch(w)
+    dev = torch.device("cuda:0")
+    td, te = torch.from_numpy(d).to(dev), torch.from_numpy(e).to(dev)
+    lam = torch.empty_like(td)
+    Q = torch.empty((w.batch, w.n, w.n), dtype=td.dtype, device=dev) if jobz else None
+    rc = st.steqr_batched(td, te, lam, Q, w.n, w.batch, st.STEQR_V if jobz else st.STEQR_N,
+                          st.dtype_code(td.dtype))
+    assert rc == 0
+    torch.cuda.synchronize()
+    g = (lam.cpu().numpy(), None if Q is None else Q.cpu().numpy())
+    ref = run_gpu(d, e, jobz)
+    assert np.array_equal(g[0], ref[0], equal_nan=True)
+    if jobz:
+        assert np.array_equal(g[1], ref[1], equal_nan=True)
+    items = np.unique(np.concatenate([np.linspace(0, w.batch - 1, 256).astype(int),
+                                      np.arange(w.batch - 16, w.batch)]))
+    o = oracle.steqr(d[items], e[items], jobz, threads=8)
+    assert check(d, e, (g[0], g[1], ref[2]), o, jobz, items=items) == []
+
+
+@pytest.mark.parametrize("dt", [np.float32, np.float64], ids=["f32", "f64"])
+@pytest.mark.parametrize("n", [16, 32])
+@pytest.mark.parametrize("top", [False, True], ids=["small_end_bottom", "small_end_top"])
+def test_graded_keeps_relative_accuracy(dt, n, top):
+    """Graded items converge their small end first ("STEQR: the CTA
+    tridiagonal solver", QL versus QR), which keeps the small eigenvalues
+    accurate relative to their size in both orientations: within 2^-6
+    (float) or 2^-30 (double) of long-double Sturm values, where the
+    opposite rule loses all digits in float at these orders (1.4 at order
+    16) and 2.8e-9 or more in double (oracle measurements). Float keeps no
+    fixed number of digits on graded input (the pages call the method
+    normwise accurate), hence the loose float bound; the usual parity with
+    the oracle is checked too."""
+    d, e = W.edge_batch(W.EDGE_NAMES.index("graded"), n, 333, np.float64)
+    if top:
+        d, e = d[:, ::-1].copy(), e[:, ::-1].copy()
+    d, e = d.astype(dt), e.astype(dt)
+    g = run_gpu(d, e, True)
+    o = oracle.steqr(d, e, True, threads=8)
+    assert check(d, e, g, o, True) == []
+    ref = np.sort(V.sturm_eigvals(d[:64], e[:64]).astype(np.float64), axis=1)
+    rel = np.abs(np.sort(g[0][:64].astype(np.float64), axis=1) - ref) / np.abs(ref)
+    assert rel.max() <= (2.0 ** -6 if dt == np.float32 else 2.0 ** -30)

@@ -62,7 +62,7 @@ PG_LANES = [
     (np.float32, 32, True, 32, 1), (np.float32, 32, False, 2, 1), (np.float32, 16, False, 1, 1),
     (np.float64, 12, True, 4, 2), (np.float64, 16, True, 8, 1), (np.float64, 32, True, 16, 2),
     (np.float64, 32, False, 1, 1), (np.float64, 8, True, 4, 1),
-    (np.float32, 64, True, 64, 2), (np.float64, 48, True, 64, 2), (np.float64, 64, False, 64, 2),
+    (np.float32, 64, True, 64, 2), (np.float64, 64, False, 64, 2),
     (np.float64, 64, True, 4, 3), (np.float32, 40, True, 16, 3), (np.float64, 50, True, 16, 3),
 ]
 

@@ -21,6 +21,12 @@ def _gpu():
     import symmetric_tridiagonal_eigensolver_amd  # noqa: F401  (fails loudly if not built)
 
 
+def _vectors_ok(dt, n: int) -> bool:
+    """Double precision with eigenvectors is built up to order 16."""
+    import symmetric_tridiagonal_eigensolver_amd as st
+    return dt != np.float64 or n <= st.SYEV_MAX_N_F64_V
+
+
 # every instantiated (dtype, compiled order, lanes) at full and ragged orders
 CASES = [
     (np.float32, 4, 4, True), (np.float32, 3, 4, True), (np.float32, 8, 2, True),
@@ -29,10 +35,9 @@ CASES = [
     (np.float32, 4, 4, False), (np.float32, 8, 2, False), (np.float32, 16, 4, False),
     (np.float32, 11, 4, False), (np.float32, 32, 16, False),
     (np.float64, 4, 4, True), (np.float64, 8, 4, True), (np.float64, 16, 8, True),
-    (np.float64, 16, 4, True), (np.float64, 12, 8, True), (np.float64, 32, 16, True),
-    (np.float64, 21, 16, True),
+    (np.float64, 12, 8, True),
     (np.float64, 4, 4, False), (np.float64, 8, 4, False), (np.float64, 16, 8, False),
-    (np.float64, 32, 16, False),
+    (np.float64, 32, 32, False), (np.float64, 21, 32, False),
     (np.float32, 8, 1, False), (np.float32, 16, 2, False), (np.float32, 14, 2, False),
     (np.float32, 32, 8, False), (np.float32, 25, 8, False),
     (np.float64, 8, 2, False), (np.float64, 16, 4, False), (np.float64, 10, 4, False),
@@ -54,7 +59,7 @@ def test_syev_every_order(dt):
     for n in range(1, 33):
         print("syev order", dt.__name__, n, flush=True)
         A = W.random_symmetric(n, 67, dt, salt=300 + n)
-        for jobz in (True, False):
+        for jobz in ((True, False) if _vectors_ok(dt, n) else (False,)):
             g = run_gpu_syev(A, jobz)
             o = oracle.syev(A, jobz)
             assert check_dense(A, g, o, jobz) == [], (n, jobz)
@@ -66,6 +71,8 @@ def test_syev_special_matrices(dt, n):
     """Zero, diagonal, tridiagonal, scaled (1e+-18 / 1e+-150) and NaN items in
     one batch; the upper triangle is never read."""
     print("syev special", dt.__name__, n, flush=True)
+    if not _vectors_ok(dt, n):
+        pytest.skip("double with eigenvectors is built up to order 16")
     A = W.random_symmetric(n, 60, dt, salt=62)
     A[0:5] = 0
     idx = np.arange(n)
@@ -110,7 +117,16 @@ def test_syev_zero_budget_and_no_sort():
                                   (np.float64, 32)])
 def test_syev_workload_batches(dt, n, shift):
     print("syev workload", dt.__name__, n, shift, flush=True)
+    jobz = _vectors_ok(dt, n)
     A = W.random_symmetric(n, 4099, dt, salt=66)
-    g = run_gpu_syev(A, True, shift=shift)
-    o = oracle.syev(A, True, threads=8, shift=shift)
-    assert check_dense(A, g, o, True) == []
+    g = run_gpu_syev(A, jobz, shift=shift)
+    o = oracle.syev(A, jobz, threads=8, shift=shift)
+    assert check_dense(A, g, o, jobz) == []
+
+
+def test_syev_double_vectors_limit():
+    """Double precision with eigenvectors above order 16 is rejected (-4)
+    before any launch; values only run up to order 32."""
+    import symmetric_tridiagonal_eigensolver_amd as st
+    assert st.lib().syev_batched(8, 8, 8, 17, 10, st.STEQR_V, st.STEQR_F64, None) == -4
+    assert st.syev_query(32, 10, st.STEQR_N, st.STEQR_F64)["lanes_per_problem"] == 32
