@@ -529,21 +529,19 @@ __global__ void __launch_bounds__(256) steqr_chunk_kernel(KernelArgs args) {
                 } else {
                     // EXP step [algo]: first rotation from (d_s - mu, e_s),
                     // later ones from (e_{p-1}, bulge); apply G^T B G to the
-                    // 2x2 at (p, p+1). e_p already carries the previous
-                    // step's factor c (applied eagerly below), and the new
-                    // running x is written over the old one in place, so the
-                    // lanes this step masks off keep theirs without a copy.
+                    // 2x2 at (p, p+1) (exp_step_w). e_p already carries the
+                    // previous step's factor c (applied eagerly below); the
+                    // new d_p, d_{p+1} and running x are written over the old
+                    // values in place, so the lanes this step masks off keep
+                    // theirs without a copy.
                     const T b = e[p];
                     lartg(x, y, c, sn, rr);
                     if constexpr (p > 0) e[p - 1] = rr;
-                    const T a = d[p], dd = d[p + 1];
-                    const T tr = a + dd;  // trace of the 2x2 is invariant
-                    const T pp = c * a + sn * b;
-                    const T qq = c * b + sn * dd;
-                    F::fma_over(x, qq, c, -(pp * sn));
-                    F::fma_over(d[p], pp, c, qq * sn);
+                    const T w = exp_step_w(c, sn, d[p], b, d[p + 1]);
+                    F::fma_acc(d[p], sn, w);
+                    F::fma_acc_neg(d[p + 1], sn, w);
+                    F::fma_over_neg(x, c, w, b);
                     e[p] = x;
-                    d[p + 1] = tr - d[p];
                     if constexpr (p + 1 < N - 1) {
                         y = sn * e[p + 1];     // new bulge
                         e[p + 1] = c * e[p + 1];

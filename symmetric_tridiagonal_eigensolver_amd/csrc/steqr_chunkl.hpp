@@ -443,14 +443,11 @@ __global__ void __launch_bounds__(256) steqr_chunkl_kernel(KernelArgs args) {
                     const T a = dcur;
                     lartg(x, y, c, sn, rr);
                     const T b = e0;
-                    const T pp = c * a + sn * b;
-                    const T qq = c * b + sn * d1;
-                    const T an = pp * c + qq * sn;
-                    const T bn = qq * c - pp * sn;
+                    const T w = exp_step_w(c, sn, a, b, d1);
                     if constexpr (p > 0) se[p - 1] = rr;
-                    sd[p] = an;
-                    dcur = (a + d1) - an;
-                    x = bn;
+                    sd[p] = F::fma(sn, w, a);
+                    dcur = F::fma(-sn, w, d1);
+                    x = F::fma(c, w, -b);
                     y = sn * e1;
                     e1 = c * e1;
                 }

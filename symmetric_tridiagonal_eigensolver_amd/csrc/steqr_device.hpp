@@ -101,6 +101,17 @@ struct Fp<float> {
     __device__ static __forceinline__ void fma_over(float& dst, float a, float b, float c) {
         asm("v_fma_f32 %0, %1, %2, %3" : "+v"(dst) : "v"(a), "v"(b), "v"(c));
     }
+    // dst <- fma(a, b, -c) in dst's register (old value of dst unused)
+    __device__ static __forceinline__ void fma_over_neg(float& dst, float a, float b, float c) {
+        asm("v_fma_f32 %0, %1, %2, -%3" : "+v"(dst) : "v"(a), "v"(b), "v"(c));
+    }
+    // dst <- dst + a b and dst <- dst - a b, in dst's register
+    __device__ static __forceinline__ void fma_acc(float& dst, float a, float b) {
+        asm("v_fma_f32 %0, %1, %2, %0" : "+v"(dst) : "v"(a), "v"(b));
+    }
+    __device__ static __forceinline__ void fma_acc_neg(float& dst, float a, float b) {
+        asm("v_fma_f32 %0, -%1, %2, %0" : "+v"(dst) : "v"(a), "v"(b));
+    }
 };
 
 template <>
@@ -149,6 +160,15 @@ struct Fp<double> {
     // dst <- fma(a, b, c) in dst's register (old value of dst unused)
     __device__ static __forceinline__ void fma_over(double& dst, double a, double b, double c) {
         asm("v_fma_f64 %0, %1, %2, %3" : "+v"(dst) : "v"(a), "v"(b), "v"(c));
+    }
+    __device__ static __forceinline__ void fma_over_neg(double& dst, double a, double b, double c) {
+        asm("v_fma_f64 %0, %1, %2, -%3" : "+v"(dst) : "v"(a), "v"(b), "v"(c));
+    }
+    __device__ static __forceinline__ void fma_acc(double& dst, double a, double b) {
+        asm("v_fma_f64 %0, %1, %2, %0" : "+v"(dst) : "v"(a), "v"(b));
+    }
+    __device__ static __forceinline__ void fma_acc_neg(double& dst, double a, double b) {
+        asm("v_fma_f64 %0, -%1, %2, %0" : "+v"(dst) : "v"(a), "v"(b));
     }
 };
 
@@ -310,6 +330,18 @@ __device__ __forceinline__ T lapack_shift(T d1, T d2, T e1) {
     const T g = (d2 - d1) * F::rcp(T(2) * e1);
     const T r = F::sqrt_fast(F::fma(g, g, T(1)));
     return d1 - e1 * F::rcp(g + F::copysign(r, g));
+}
+
+// EXP step of the chase [algo, similarity paragraph]: the congruence G^T B G
+// of the 2x2 block B = [[a, b], [b, dd]] by the rotation (c, s), written with
+// c^2 + s^2 = 1 (which the rotation satisfies to rounding):
+//   w = s (dd - a) + 2 c b,  a' = a + s w,  dd' = dd - s w,  b' = c w - b,
+// the same values as c^2 a + 2cs b + s^2 dd, s^2 a - 2cs b + c^2 dd and
+// cs (dd - a) + (c^2 - s^2) b with three multiplications fewer.
+template <typename T>
+__device__ __forceinline__ T exp_step_w(T c, T s, T a, T b, T dd) {
+    const T cb = c * b;
+    return Fp<T>::fma(s, dd - a, cb) + cb;
 }
 
 // Closed-form shift [algo, shift section]: for the trailing block

@@ -271,13 +271,10 @@ __global__ void __launch_bounds__(256) steqr_wave_kernel(KernelArgs args) {
                         lartg<T, true>(x, y, c, sn, rr);
                         if constexpr (p > 0) se[p - 1] = rr;  // every lane writes the same word
                         const T b = cp * ep;
-                        const T pp = c * a + sn * b;
-                        const T qq = c * b + sn * dp1;
-                        const T an = pp * c + qq * sn;
-                        const T bn = qq * c - pp * sn;
-                        sd[p] = an;
-                        dcur = (a + dp1) - an;
-                        x = bn;
+                        const T w = exp_step_w(c, sn, a, b, dp1);
+                        sd[p] = F::fma(sn, w, a);
+                        dcur = F::fma(-sn, w, dp1);
+                        x = F::fma(c, w, -b);
                         y = sn * ep1;  // new bulge
                     }
                     cp = c;
