@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define STEQR_MAX_N 128
+#define STEQR_MAX_N 256
 
 enum { STEQR_N = 0, STEQR_V = 1 };     /* jobz: values only / values+vectors */
 enum { STEQR_F32 = 0, STEQR_F64 = 1 }; /* dtype */

@@ -12,7 +12,7 @@ using steqr::Entry;
 using steqr::Table;
 
 // Compile-time orders the build provides, smallest first.
-constexpr int kOrders[] = {4, 8, 16, 32, 64, 128};
+constexpr int kOrders[] = {4, 8, 16, 32, 64, 128, 256};
 
 int padded_order(int n) {
     for (int N : kOrders)
@@ -31,6 +31,9 @@ int padded_order(int n) {
 // or without its consumers); P = 64 selects one problem per wavefront at
 // orders 33..64.
 int default_lanes(int dtype, int N, int jobz, int band) {
+    // order 256: one problem per producer wavefront with eigenvectors; two
+    // per wavefront (32 lanes each) without
+    if (N == 256) return band == 3 ? 64 : 32;
     // order 128, producer lanes per problem: float with eigenvectors runs
     // whole rows of Q per lane (5 problems per producer at 8 lanes each);
     // double with eigenvectors measured 1.4% faster at 32 than at 16
@@ -69,6 +72,7 @@ const Entry* search(const Table& t, int dtype, int N, int P, int jobz, int band)
 }
 
 const Entry* find_entry(int dtype, int N, int P, int jobz, int band, int pg) {
+    if (N == 256) return search(pg ? steqr::table_huge_pg() : steqr::table_huge(), dtype, N, P, jobz, band);
     if (N == 128) return search(pg ? steqr::table_big_pg() : steqr::table_big(), dtype, N, P, jobz, band);
     if (band == 3) return search(pg ? steqr::table_pc_pg() : steqr::table_pc(), dtype, N, P, jobz, band);
     if (N == 64) {
@@ -169,11 +173,13 @@ int plan_launch(int n, int batch, int jobz, int dtype, const steqr_params* prm, 
     const Entry* ent = find_entry(dtype, N, P, jobz, band, pg);
     if (!ent) return -10;
     int per_block;
+    int gpp = 1;  // workgroups per problem (producer-consumer, rows split)
     if (band == 3) {
         // consumer wavefronts (one row of Q per lane) and one producer
         // wavefront per workgroup
         waves = ent->pc_waves;
         per_block = ent->pc_np;
+        gpp = ent->pc_gpp;
         p.R = 1;
     } else {
         // keep a workgroup's LDS within 64 KiB
@@ -193,7 +199,7 @@ int plan_launch(int n, int batch, int jobz, int dtype, const steqr_params* prm, 
     p.N = N;
     p.P = P;
     p.band = band;
-    p.grid = batch > 0 ? (int)(((long)batch + per_block - 1) / per_block) : 0;
+    p.grid = batch > 0 ? (int)(((long)batch + per_block - 1) / per_block * gpp) : 0;
     *out = p;
     return 0;
 }

@@ -59,10 +59,11 @@ __device__ __forceinline__ int chunk_sumi(int v) {
 template <typename T, int N>
 __global__ void __launch_bounds__(256) steqr_bisect_kernel(KernelArgs args) {
     // L lanes per problem, E = N / L positions and eigenvalue indices per
-    // lane (k, k + L, ...): one index per lane up to order 64, two at 128
+    // lane (k, k + L, ...): one index per lane up to order 64, two at 128,
+    // four at 256
     constexpr int L = N < 64 ? N : 64;
     constexpr int E = N / L;
-    static_assert(N >= 2 && N <= 128 && (64 % L) == 0 && E * L == N, "lanes per position");
+    static_assert(N >= 2 && N <= 256 && (64 % L) == 0 && E * L == N, "lanes per position");
     using F = Fp<T>;
     using S = SmemB<T, N>;
     constexpr int CH = 64 / L;

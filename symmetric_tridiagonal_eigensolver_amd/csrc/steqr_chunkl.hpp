@@ -42,20 +42,36 @@ struct SmemL {
 // OR / max over the P lanes of a chunk (every lane of the chunk must be
 // active, which holds because a chunk's lanes share control flow). The OR
 // takes DPP lane moves, whose partners never leave the chunk.
+// With 64 lanes per problem the result is the same in every lane of the
+// wavefront: read it into a scalar register, so that the masks and the
+// per-problem state derived from them live in scalar registers.
 template <int P>
 __device__ __forceinline__ unsigned chunk_or(unsigned v) {
-    return chunk_or_dpp<P>(v);
+    v = chunk_or_dpp<P>(v);
+    if constexpr (P == 64) v = (unsigned)__builtin_amdgcn_readfirstlane((int)v);
+    return v;
 }
 // OR over the P lanes of a chunk for 32-, 64- and 128-bit masks (DPP lane
 // moves on each 32-bit word)
 template <int P, typename M>
 __device__ __forceinline__ M chunk_or_mask(M v) {
-    M out = 0;
-    static_for<(int)(sizeof(M) / 4)>([&](auto WW) {
-        constexpr int w = decltype(WW)::value;
-        out |= (M)chunk_or<P>((unsigned)(v >> (32 * w))) << (32 * w);
-    });
-    return out;
+    if constexpr (sizeof(M) <= 16) {
+        M out = 0;
+        static_for<(int)(sizeof(M) / 4)>([&](auto WW) {
+            constexpr int w = decltype(WW)::value;
+            out |= (M)chunk_or<P>((unsigned)(v >> (32 * w))) << (32 * w);
+        });
+        return out;
+    } else {
+        M out;
+        static_for<4>([&](auto WW) {
+            constexpr int w = decltype(WW)::value;
+            const uint64_t lo = chunk_or<P>((unsigned)v.w[w]);
+            const uint64_t hi = chunk_or<P>((unsigned)(v.w[w] >> 32));
+            out.w[w] = lo | (hi << 32);
+        });
+        return out;
+    }
 }
 
 // Deflation test [algo, deflation] of every position of a chunk's band copy
@@ -104,6 +120,16 @@ template <int P, typename T>
 __device__ __forceinline__ T chunk_max(T v) {
 #pragma unroll
     for (int o = 1; o < P; o <<= 1) v = Fp<T>::max(v, __shfl_xor(v, o, 64));
+    if constexpr (P == 64) {
+        if constexpr (sizeof(T) == 4) {
+            v = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
+        } else {
+            const long long b = __double_as_longlong(v);
+            const int lo = __builtin_amdgcn_readfirstlane((int)b);
+            const int hi = __builtin_amdgcn_readfirstlane((int)(b >> 32));
+            v = __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+        }
+    }
     return v;
 }
 

@@ -195,9 +195,59 @@ __device__ __forceinline__ unsigned chunk_or_dpp(unsigned v) {
 
 typedef unsigned __int128 u128;
 
+// 256-bit position mask (orders 129..256): four 64-bit words, word i
+// holding positions 64i .. 64i+63. The operators are the ones the solver's
+// mask arithmetic uses; shifts take run-time counts (word index and bit
+// offset selected per lane).
+struct u256 {
+    uint64_t w[4];
+    __device__ constexpr u256() : w{0, 0, 0, 0} {}
+    __device__ constexpr u256(uint64_t v) : w{v, 0, 0, 0} {}
+    __device__ constexpr u256(uint64_t a, uint64_t b, uint64_t c, uint64_t d) : w{a, b, c, d} {}
+    __device__ u256 operator|(const u256& o) const {
+        return u256(w[0] | o.w[0], w[1] | o.w[1], w[2] | o.w[2], w[3] | o.w[3]);
+    }
+    __device__ u256 operator&(const u256& o) const {
+        return u256(w[0] & o.w[0], w[1] & o.w[1], w[2] & o.w[2], w[3] & o.w[3]);
+    }
+    __device__ u256 operator~() const { return u256(~w[0], ~w[1], ~w[2], ~w[3]); }
+    __device__ u256& operator|=(const u256& o) { return *this = *this | o; }
+    __device__ u256& operator&=(const u256& o) { return *this = *this & o; }
+    __device__ bool operator==(const u256& o) const {
+        return ((w[0] ^ o.w[0]) | (w[1] ^ o.w[1]) | (w[2] ^ o.w[2]) | (w[3] ^ o.w[3])) == 0;
+    }
+    __device__ bool operator!=(const u256& o) const { return !(*this == o); }
+    __device__ explicit operator bool() const { return (w[0] | w[1] | w[2] | w[3]) != 0; }
+    __device__ explicit operator unsigned() const { return (unsigned)w[0]; }
+    // word j of the value (0 outside 0..3)
+    __device__ uint64_t word(int j) const {
+        return j == 0 ? w[0] : (j == 1 ? w[1] : (j == 2 ? w[2] : (j == 3 ? w[3] : 0ull)));
+    }
+    __device__ u256 operator<<(int k) const {
+        const int ws = k >> 6, bs = k & 63;
+        u256 r;
+        for (int i = 0; i < 4; ++i) {
+            const uint64_t hi = word(i - ws), lo = word(i - ws - 1);
+            r.w[i] = (hi << bs) | ((lo >> 1) >> (63 - bs));
+        }
+        return r;
+    }
+    __device__ u256 operator>>(int k) const {
+        const int ws = k >> 6, bs = k & 63;
+        u256 r;
+        for (int i = 0; i < 4; ++i) {
+            const uint64_t lo = word(i + ws), hi = word(i + ws + 1);
+            r.w[i] = (lo >> bs) | ((hi << 1) << (63 - bs));
+        }
+        return r;
+    }
+};
+
 template <int N>
 using PosMask = typename std::conditional<
-    (N > 64), u128, typename std::conditional<(N > 32), uint64_t, uint32_t>::type>::type;
+    (N > 128), u256,
+    typename std::conditional<(N > 64), u128,
+                              typename std::conditional<(N > 32), uint64_t, uint32_t>::type>::type>::type;
 
 // bits [0, k), 0 <= k <= width
 template <typename M>
@@ -206,8 +256,15 @@ __device__ __forceinline__ M bits_below(int k) {
         return (M)((1ull << k) - 1ull);
     } else if constexpr (sizeof(M) == 8) {
         return k >= 64 ? ~(M)0 : (((M)1 << k) - (M)1);
-    } else {
+    } else if constexpr (sizeof(M) == 16) {
         return k >= 128 ? ~(M)0 : (((M)1 << k) - (M)1);
+    } else {
+        u256 r;
+        for (int i = 0; i < 4; ++i) {
+            const int b = k - 64 * i;  // bits of word i below k
+            r.w[i] = b >= 64 ? ~0ull : (b <= 0 ? 0ull : ((1ull << b) - 1ull));
+        }
+        return r;
     }
 }
 
@@ -224,9 +281,14 @@ __device__ __forceinline__ int msb(M x) {
         return 31 - __clz((int)x);
     } else if constexpr (sizeof(M) == 8) {
         return 63 - __clzll((long long)x);
-    } else {
+    } else if constexpr (sizeof(M) == 16) {
         const uint64_t hi = (uint64_t)(x >> 64), lo = (uint64_t)x;
         return hi ? 127 - __clzll((long long)hi) : 63 - __clzll((long long)lo);
+    } else {
+        return x.w[3] ? 255 - __clzll((long long)x.w[3])
+                      : (x.w[2] ? 191 - __clzll((long long)x.w[2])
+                                : (x.w[1] ? 127 - __clzll((long long)x.w[1])
+                                          : 63 - __clzll((long long)x.w[0])));
     }
 }
 template <typename M>
@@ -235,9 +297,14 @@ __device__ __forceinline__ int lsb(M x) {
         return __ffs((int)x) - 1;
     } else if constexpr (sizeof(M) == 8) {
         return __ffsll((long long)x) - 1;
-    } else {
+    } else if constexpr (sizeof(M) == 16) {
         const uint64_t hi = (uint64_t)(x >> 64), lo = (uint64_t)x;
         return lo ? __ffsll((long long)lo) - 1 : 63 + __ffsll((long long)hi);
+    } else {
+        return x.w[0] ? __ffsll((long long)x.w[0]) - 1
+                      : (x.w[1] ? 63 + __ffsll((long long)x.w[1])
+                                : (x.w[2] ? 127 + __ffsll((long long)x.w[2])
+                                          : 191 + __ffsll((long long)x.w[3])));
     }
 }
 
@@ -245,7 +312,31 @@ template <typename M>
 __device__ __forceinline__ int popc(M x) {
     if constexpr (sizeof(M) == 4) return __popc((unsigned)x);
     else if constexpr (sizeof(M) == 8) return __popcll((unsigned long long)x);
-    else return __popcll((unsigned long long)x) + __popcll((unsigned long long)(x >> 64));
+    else if constexpr (sizeof(M) == 16)
+        return __popcll((unsigned long long)x) + __popcll((unsigned long long)(x >> 64));
+    else
+        return __popcll(x.w[0]) + __popcll(x.w[1]) + __popcll(x.w[2]) + __popcll(x.w[3]);
+}
+
+// bit p set (0 <= p < width)
+template <typename M>
+__device__ __forceinline__ M bit_at(int p) {
+    if constexpr (sizeof(M) <= 16) {
+        return (M)1 << p;
+    } else {
+        u256 r;
+        for (int i = 0; i < 4; ++i) r.w[i] = (p >> 6) == i ? (1ull << (p & 63)) : 0ull;
+        return r;
+    }
+}
+// whether bit p is set
+template <typename M>
+__device__ __forceinline__ bool bit_test(const M& x, int p) {
+    if constexpr (sizeof(M) <= 16) {
+        return ((x >> p) & 1) != 0;
+    } else {
+        return ((x.word(p >> 6) >> (p & 63)) & 1ull) != 0;
+    }
 }
 
 // ---------------------------------------------------------------- arithmetic

@@ -39,20 +39,24 @@
 
 namespace steqr {
 
-// W consumer wavefronts. RS lanes hold one row of Q (RS = 2 at order 128
-// by default: two half rows), so a consumer holds RPW = 64/RS rows: CQ =
-// RPW/N problems when N <= RPW, else WPP = N/RPW consumers per problem;
-// NP = W * CQ / WPP problems per workgroup.
-template <int N>
-constexpr int pc_default_rs() { return N > 64 ? 2 : 1; }
+// W consumer wavefronts. RS lanes hold one row of Q (at order 128 by
+// default two half rows; at order 256 halves in float, quarters in double,
+// 128 registers per lane either way), so a consumer holds RPW = 64/RS
+// rows: CQ = RPW/N problems when N <= RPW, else WPP = N/RPW consumers per
+// problem. When one problem needs more consumers than a workgroup holds
+// (double at order 256: 16), GPP = WPP/W workgroups share it, each with its
+// own producer (the producers compute the same rotations) and a slice of
+// the rows. NP = W * CQ / WPP problems per workgroup (1 when shared).
+template <typename T, int N>
+constexpr int pc_default_rs() { return N <= 64 ? 1 : (N == 128 ? 2 : (sizeof(T) == 4 ? 2 : 4)); }
 
-template <typename T, int N, int W, int P, int RS = pc_default_rs<N>()>
+template <typename T, int N, int W, int P, int RS = pc_default_rs<T, N>()>
 struct SmemPC {
-    static constexpr bool HALF = RS == 2;                 // two lanes per row of Q
     static constexpr int RPW = 64 / RS;                   // rows per consumer
     static constexpr int CQ = N <= RPW ? RPW / N : 1;     // problems per consumer
     static constexpr int WPP = N <= RPW ? 1 : N / RPW;    // consumers per problem
-    static constexpr int NP = W * CQ / WPP;               // problems per workgroup
+    static constexpr int GPP = (W > 0 && WPP > W) ? WPP / W : 1;  // workgroups per problem
+    static constexpr int NP = GPP > 1 ? 1 : W * CQ / WPP; // problems per workgroup
     static constexpr int CH = 64 / P;                     // producer chunks (>= NP)
     static constexpr int SLOT = 2 * N + 1;                // d[N], e[N], pad
     static constexpr size_t band_bytes = ((CH * SLOT * sizeof(T) + 15) / 16) * 16;
@@ -80,8 +84,8 @@ struct SmemPV {
 
 enum { PC_CTRL_PASS = 1, PC_CTRL_END = 2 };
 
-// Consumer wavefront: hold rows of Q (lane = row, or at order 128 half a
-// row: columns c0 .. c0+QW-1 with the other half in lane ^ 32) and apply the
+// Consumer wavefront: hold rows of Q (lane = row; with RS lanes per row,
+// lane row + RPW*k holds columns kQW .. kQW+QW-1 of the row) and apply the
 // producer's logged rotations pass by pass; at the end store the rows with
 // the sort's column permutation.
 template <typename T, int N, int W, int P, int RS>
@@ -90,16 +94,17 @@ __device__ __forceinline__ void consume(const KernelArgs& args, int lane, int wa
                                         const int* fin) {
     using S = SmemPC<T, N, W, P, RS>;
     using F = Fp<T>;
-    constexpr bool HALF = S::HALF;
     constexpr int NP = S::NP;
-    constexpr int QW = HALF ? N / 2 : N;  // columns held per lane
+    constexpr int QW = N / RS;  // columns held per lane
     T* __restrict__ gq = static_cast<T*>(args.q);
     const int n = args.n;
     constexpr int RPW = S::RPW;
-    const int pi = (N <= RPW) ? wave * S::CQ + lane / N : wave / S::WPP;
-    const int hf = HALF ? (lane >> 5) : 0;
-    const int row = (N <= RPW) ? lane % N : (wave % S::WPP) * RPW + lane % RPW;
-    const int c0 = hf * QW;
+    constexpr int WL = S::WPP / S::GPP;  // this workgroup's consumers of a problem
+    const int pi = (N <= RPW) ? wave * S::CQ + lane / N : wave / WL;
+    const int part = RS > 1 ? lane / RPW : 0;  // which QW columns of the row
+    const int slice = S::GPP > 1 ? (int)(blockIdx.x % S::GPP) : 0;
+    const int row = (N <= RPW) ? lane % N : ((wave % WL) + slice * WL) * RPW + lane % RPW;
+    const int c0 = part * QW;
     const long prob = first + pi;
     const bool live = prob < (long)args.batch;
     // the identity, or with back-transformation [algo, eigenvector
@@ -111,15 +116,18 @@ __device__ __forceinline__ void consume(const KernelArgs& args, int lane, int wa
         load_basis_cols<T, QW>(gq + pc * n * n, n, row, c0, live, args.back_transform != 0, vec,
                                q);
     }
-    // the rotation straddling the halves (columns QW-1 and QW): the pair of
-    // lanes swaps its boundary values; `lead` is the lane whose value is the
-    // rotation's first operand
-    auto straddle = [&](bool lead, T c, T sn) __attribute__((always_inline)) {
-        const T mine = hf == 0 ? q[QW - 1] : q[0];
-        const T other = __shfl_xor(mine, 32, 64);
+    // The rotation straddling parts j and j+1 of a row (columns (j+1)QW - 1
+    // and (j+1)QW): the two lanes swap their boundary values (every lane of
+    // the wavefront takes part in the shuffle); `lead_upper` says whether
+    // part j+1 holds the rotation's first operand.
+    auto straddle = [&](int j, bool lead_upper, T c, T sn) __attribute__((always_inline)) {
+        const bool lower = part == j, upper = part == j + 1;
+        const T mine = upper ? q[0] : q[QW - 1];
+        const T other = __shfl(mine, (upper ? lane - RPW : lane + RPW) & 63, 64);
+        const bool lead = lead_upper ? upper : lower;
         const T upd = lead ? F::fma(c, mine, sn * other) : F::fma(c, mine, -(sn * other));
-        if (hf == 0) q[QW - 1] = upd;
-        else q[0] = upd;
+        if (lower) q[QW - 1] = upd;
+        if (upper) q[0] = upd;
     };
     // The producer mirrors a problem (positions p <-> N-1-p, Q's columns
     // included) while a block that converges at its top is reduced.
@@ -132,13 +140,29 @@ __device__ __forceinline__ void consume(const KernelArgs& args, int lane, int wa
         __syncthreads();
         const int* h = hdr + slot * S::HDR;
         if (h[0] == PC_CTRL_END) break;
-        orient ^= h[1 + 3 * pi];
+        if constexpr (RS == 1) {
+            orient ^= h[1 + 3 * pi];
+        } else if (h[1 + 3 * pi]) {
+            // with a row split over RS lanes the mirror is applied to the
+            // registers (column j of part k <-> column QW-1-j of part
+            // RS-1-k, pairwise through lane shuffles; a problem's blocks
+            // open and close a few times), so that the passes below need
+            // only the one orientation
+            const int src = (lane % RPW) + RPW * (RS - 1 - part);
+            static_for<QW / 2>([&](auto J) {
+                constexpr int j = decltype(J)::value;
+                const T a = __shfl(q[QW - 1 - j], src, 64);
+                const T b = __shfl(q[j], src, 64);
+                q[j] = a;
+                q[QW - 1 - j] = b;
+            });
+        }
         const int s = h[2 + 3 * pi];
         const int steps = h[3 + 3 * pi];
         const T* lg = rot + (size_t)(slot * (NP + 1) + pi) * (N - 1) * 2;
         if (steps > 0) {
             const int me = s + steps;
-            if constexpr (!HALF) {
+            if constexpr (RS == 1) {
                 if (orient == 0) {
                     static_for_while<N - 1>([&](auto I) {
                         constexpr int p = decltype(I)::value;
@@ -153,48 +177,28 @@ __device__ __forceinline__ void consume(const KernelArgs& args, int lane, int wa
                     });
                 }
             } else {
-                // positions 0..QW-2 fall in the first half of the columns
-                // (second half when mirrored), QW-1 straddles, the rest fall
-                // in the other half: run the three parts in position order,
-                // each half under one lane mask
-                const int lead = orient;  // the half that holds positions 0..QW-2
-                if (hf == lead) {
-                    if (orient == 0) {
+                // Positions kQW .. kQW+QW-2 fall inside part k of the columns,
+                // kQW+QW-1 straddles parts k and k+1: the parts run in
+                // position order, each under one lane mask (the problem's s
+                // and me are uniform over the wavefront; the registers are
+                // never mirrored here, see above).
+                static_for<RS>([&](auto LQ) {
+                    constexpr int lq = decltype(LQ)::value;
+                    constexpr int pos0 = lq * QW;
+                    const int sl = s - pos0, el = me - pos0;
+                    if ((el > 0) & (sl < QW - 1) & (part == lq)) {
+                        const T* lgl = lg + 2 * pos0;
                         static_for_while<QW - 1>([&](auto I) {
                             constexpr int p = decltype(I)::value;
-                            if (p >= s) F::rot(q[p], q[p + 1], lg[2 * p], lg[2 * p + 1]);
-                            return p + 1 < me;
-                        });
-                    } else {
-                        static_for_while<QW - 1>([&](auto I) {
-                            constexpr int p = decltype(I)::value;
-                            if (p >= s)
-                                F::rot(q[QW - 1 - p], q[QW - 2 - p], lg[2 * p], lg[2 * p + 1]);
-                            return p + 1 < me;
+                            if (p >= sl) F::rot(q[p], q[p + 1], lgl[2 * p], lgl[2 * p + 1]);
+                            return p + 1 < el;
                         });
                     }
-                }
-                if ((s <= QW - 1) & (QW - 1 < me))
-                    straddle(hf == lead, lg[2 * (QW - 1)], lg[2 * (QW - 1) + 1]);
-                if ((hf != lead) & (me > QW)) {
-                    const int s2 = s > QW ? s - QW : 0;
-                    const int me2 = me - QW;
-                    const T* lg2 = lg + 2 * QW;
-                    if (orient == 0) {
-                        static_for_while<QW - 1>([&](auto I) {
-                            constexpr int p = decltype(I)::value;
-                            if (p >= s2) F::rot(q[p], q[p + 1], lg2[2 * p], lg2[2 * p + 1]);
-                            return p + 1 < me2;
-                        });
-                    } else {
-                        static_for_while<QW - 1>([&](auto I) {
-                            constexpr int p = decltype(I)::value;
-                            if (p >= s2)
-                                F::rot(q[QW - 1 - p], q[QW - 2 - p], lg2[2 * p], lg2[2 * p + 1]);
-                            return p + 1 < me2;
-                        });
+                    if constexpr (lq + 1 < RS) {
+                        constexpr int ps = pos0 + QW - 1;
+                        if ((s <= ps) & (ps < me)) straddle(lq, false, lg[2 * ps], lg[2 * ps + 1]);
                     }
-                }
+                });
             }
         }
         slot ^= 1;
@@ -224,7 +228,7 @@ constexpr int pc_min_waves() {
 }
 
 template <typename T, int N, int W, int P, bool PG, bool WANTQ = true,
-          int RS = pc_default_rs<N>()>
+          int RS = pc_default_rs<T, N>()>
 __global__ void __launch_bounds__((WANTQ ? (W + 1) * 64 : 256), (pc_min_waves<T, N, W>()))
     steqr_pc_kernel(KernelArgs args) {
     using S = SmemPC<T, N, W, P, RS>;
@@ -234,8 +238,10 @@ __global__ void __launch_bounds__((WANTQ ? (W + 1) * 64 : 256), (pc_min_waves<T,
     constexpr int NP = WANTQ ? S::NP : CH;
     // At order 32 (two problems per consumer) this split measured slower
     // than the LDS-band chunked kernel, so orders 64 and 128 are built.
-    static_assert(N == 64 || N == 128, "the producer-consumer kernel is for orders 64 and 128");
-    static_assert(!WANTQ || (W % WPP) == 0, "whole problems per workgroup");
+    static_assert(N == 64 || N == 128 || N == 256,
+                  "the producer-consumer kernel is for orders 64, 128 and 256");
+    static_assert(!WANTQ || (W % WPP) == 0 || (WPP % W) == 0,
+                  "whole problems per workgroup, or whole workgroups per problem");
     static_assert(P >= 2 && (64 % P) == 0 && (N % P) == 0 && 64 / P >= NP, "P lanes per chunk");
     constexpr int K = N / P;  // positions per producer lane
     using M = PosMask<N>;
@@ -261,9 +267,14 @@ __global__ void __launch_bounds__((WANTQ ? (W + 1) * 64 : 256), (pc_min_waves<T,
     T* __restrict__ glam = static_cast<T*>(args.lam);
     T* __restrict__ gq = static_cast<T*>(args.q);
     const int n = args.n;
-    // the first problem of the workgroup (with Q) or of this wavefront
-    const long first = WANTQ ? (long)blockIdx.x * NP
+    // the first problem of the workgroup (with Q; GPP workgroups share one
+    // problem when it needs more consumers than a workgroup holds) or of
+    // this wavefront
+    const long first = WANTQ ? (long)(blockIdx.x / S::GPP) * NP
                              : ((long)blockIdx.x * (blockDim.x >> 6) + wave) * CH;
+    // of the workgroups sharing a problem, the first stores its eigenvalues
+    // and status (the others computed the same ones)
+    const bool lead_wg = !WANTQ || (blockIdx.x % S::GPP) == 0;
 
     if constexpr (WANTQ) {
         if (wave < W) {
@@ -306,7 +317,7 @@ __global__ void __launch_bounds__((WANTQ ? (W + 1) * 64 : 256), (pc_min_waves<T,
         static_for<K>([&](auto KK) {
             constexpr int k = decltype(KK)::value;
             const int p = r + k * P;
-            part |= (se[p] == T(0)) ? ((M)1 << p) : (M)0;
+            part |= (se[p] == T(0)) ? bit_at<M>(p) : (M)0;
         });
         zeromask = chunk_or_mask<P>(part);
     }
@@ -352,7 +363,7 @@ __global__ void __launch_bounds__((WANTQ ? (W + 1) * 64 : 256), (pc_min_waves<T,
             constexpr int k = decltype(KK)::value;
             const int p = r + k * P;
             T ev = se[p], dv = sd[p];
-            ev = ((zeroed >> p) & 1) ? T(0) : ev;
+            ev = bit_test(zeroed, p) ? T(0) : ev;
             if (mode != 0) {
                 dv = ((p >= bt) & (p <= bb)) ? dv * un : dv;
                 ev = (fail & (p >= bt) & (p < bb)) ? ev * un : ev;
@@ -413,7 +424,7 @@ __global__ void __launch_bounds__((WANTQ ? (W + 1) * 64 : 256), (pc_min_waves<T,
             bt = mir ? N - 1 - hi : lo;
             bb = mir ? N - 1 - lo : hi;
             m = bb;
-            zeroed = bt > 0 ? ((M)1 << (bt - 1)) : (M)0;
+            zeroed = bt > 0 ? bit_at<M>(bt - 1) : (M)0;
             state = ST_ITER;
         }
     };
@@ -434,7 +445,7 @@ __global__ void __launch_bounds__((WANTQ ? (W + 1) * 64 : 256), (pc_min_waves<T,
         const int t = msb((M)(clr | (M)1));
         const M above = nb & bit_range<M>(bt, t - 1);
         const int s2 = above ? msb(above) + 1 : bt;
-        const M znew = (nb & bit_range<M>(t + 1, m - 1)) | (above ? ((M)1 << (above ? s2 - 1 : 0)) : (M)0);
+        const M znew = (nb & bit_range<M>(t + 1, m - 1)) | (above ? bit_at<M>(above ? s2 - 1 : 0) : (M)0);
         zeroed |= conv ? nb : (go ? znew : (M)0);
         const bool jac = go & (t == s2);
         const bool fail = go & !jac & (jtot >= nmaxit);
@@ -453,13 +464,13 @@ __global__ void __launch_bounds__((WANTQ ? (W + 1) * 64 : 256), (pc_min_waves<T,
                     static_for<K>([&](auto KK) {
                         constexpr int k = decltype(KK)::value;
                         const int p = r + k * P;
-                        part |= ((p < n - 1) & (se[p] != T(0))) ? ((M)1 << p) : (M)0;
+                        part |= ((p < n - 1) & (se[p] != T(0))) ? bit_at<M>(p) : (M)0;
                     });
                     info = popc(chunk_or_mask<P>(part));
                     info = info > 0 ? info : 1;
                     // the status is final: store it now rather than keep
                     // it in a register through the remaining passes
-                    if (live & (args.info != nullptr) & (r == 0)) args.info[prob] = info;
+                    if (live & lead_wg & (args.info != nullptr) & (r == 0)) args.info[prob] = info;
                 }
                 state = fail ? ST_DONE : ST_OPEN;
             }
@@ -480,7 +491,7 @@ __global__ void __launch_bounds__((WANTQ ? (W + 1) * 64 : 256), (pc_min_waves<T,
             sym2x2(dm1, em1, dm, rt1, rt2, cs, sj);
             x = jac ? (PG ? cs * em1 : cs) : x;
             y = jac ? -sj : y;
-            zeroed |= jac ? ((M)1 << jpos) : (M)0;
+            zeroed |= jac ? bit_at<M>(jpos) : (M)0;
         }
         const unsigned steps = sweep ? (unsigned)(m - s) : (jac ? 1u : 0u);
         // hand the pass to the consumers: mirror parity, first position,
@@ -631,7 +642,7 @@ __global__ void __launch_bounds__((WANTQ ? (W + 1) * 64 : 256), (pc_min_waves<T,
         myrank[kk] = sort_it ? rk : j;
         srank[j] = myrank[kk];
     });
-    if (live) {
+    if (live & lead_wg) {
         // addressed from the wavefront's first problem (scalar) and the
         // chunk index, so no 64-bit problem index stays live through the loop
         T* const glw = glam + first * n;

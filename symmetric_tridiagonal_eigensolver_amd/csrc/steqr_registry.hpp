@@ -33,6 +33,7 @@ struct Entry {
     LaunchFn fn;
     int pc_np = 0;         // band 3: problems per workgroup
     int pc_waves = 0;      // band 3: wavefronts per workgroup (consumers + producer)
+    int pc_gpp = 1;        // band 3: workgroups sharing one problem (rows split)
 };
 
 template <typename T, int N, int P, bool WANTQ, bool PG, bool DENSE = false>
@@ -78,7 +79,7 @@ hipError_t launch_chunkl(const KernelArgs& args, int grid, int block, hipStream_
 // Producer-consumer with eigenvectors: W consumer wavefronts (RS lanes per
 // row of Q) and one producer per workgroup; the grid and block are given
 // by the caller.
-template <typename T, int N, int W, int P, bool PG, int RS = pc_default_rs<N>()>
+template <typename T, int N, int W, int P, bool PG, int RS = pc_default_rs<T, N>()>
 hipError_t launch_pc(const KernelArgs& args, int grid, int block, hipStream_t stream) {
     constexpr size_t lds = SmemPC<T, N, W, P, RS>::bytes;
     hipLaunchKernelGGL((steqr_pc_kernel<T, N, W, P, PG, true, RS>), dim3(grid), dim3(block), lds,
@@ -101,13 +102,15 @@ hipError_t launch_pcv(const KernelArgs& args, int grid, int block, hipStream_t s
 
 #define STEQR_PC_ENTRY(DT, T, N, W, P) \
     { DT, N, P, 1, 3, (int)SmemPC<T, N, W, P>::bytes, \
-      &launch_pc<T, N, W, P, STEQR_INST_PG != 0>, SmemPC<T, N, W, P>::NP, (W) + 1 }
+      &launch_pc<T, N, W, P, STEQR_INST_PG != 0>, SmemPC<T, N, W, P>::NP, (W) + 1, \
+      SmemPC<T, N, W, P>::GPP }
 
 // The same with RS lanes per row of Q chosen explicitly (order 128 with
 // whole rows per lane: RS = 1).
 #define STEQR_PCR_ENTRY(DT, T, N, W, P, RS) \
     { DT, N, P, 1, 3, (int)SmemPC<T, N, W, P, RS>::bytes, \
-      &launch_pc<T, N, W, P, STEQR_INST_PG != 0, RS>, SmemPC<T, N, W, P, RS>::NP, (W) + 1 }
+      &launch_pc<T, N, W, P, STEQR_INST_PG != 0, RS>, SmemPC<T, N, W, P, RS>::NP, (W) + 1, \
+      SmemPC<T, N, W, P, RS>::GPP }
 
 #define STEQR_ENTRY(DT, T, N, P, Q) \
     { DT, N, P, Q, 1, (int)Smem<T, N, P, (Q) != 0>::bytes_per_wave, \
@@ -149,6 +152,8 @@ Table table_lds_f64_pg();
 Table table_pc_pg();
 Table table_big();
 Table table_big_pg();
+Table table_huge();
+Table table_huge_pg();
 Table table_syev_f32();
 Table table_syev_f64();
 Table table_bisect();

@@ -105,3 +105,60 @@ def test_big_values_shapes(dt, lanes):
         g = run_gpu(d, e, False, lanes=lanes)
         o = oracle.steqr(d, e, False, threads=8)
         assert check(d, e, g, o, False) == []
+
+
+# ---------------------------------------------------------------- orders 129..256
+# Producer and consumer wavefronts at compiled order 256: one problem per
+# producer, rows of Q split over two (float) or four (double) lanes, double
+# with two workgroups sharing each problem's rows; values only with two
+# problems per producer wavefront.
+
+@pytest.mark.parametrize("jobz", [True, False], ids=["V", "N"])
+@pytest.mark.parametrize("dt", [np.float32, np.float64], ids=["f32", "f64"])
+@pytest.mark.parametrize("n", [129, 130, 191, 200, 255, 256])
+def test_huge_orders(n, dt, jobz):
+    print("huge case", n, dt.__name__, jobz, flush=True)
+    d, e = W.random_batch(n, 61, dt, salt=600 + n)
+    g = run_gpu(d, e, jobz)
+    o = oracle.steqr(d, e, jobz, threads=8)
+    assert check(d, e, g, o, jobz) == []
+
+
+@pytest.mark.parametrize("kind", range(5), ids=W.EDGE_NAMES)
+@pytest.mark.parametrize("dt", [np.float32, np.float64], ids=["f32", "f64"])
+def test_huge_edge_items(kind, dt):
+    n = 256
+    print("huge edge", W.EDGE_NAMES[kind], dt.__name__, flush=True)
+    d, e = W.edge_batch(kind, n, 30, dt)
+    for jobz in (True, False):
+        g = run_gpu(d, e, jobz)
+        o = oracle.steqr(d, e, jobz, threads=8)
+        assert check(d, e, g, o, jobz) == [], (W.EDGE_NAMES[kind], jobz)
+        if kind == W.EDGE_NAN:
+            assert np.all(g[2] > 0)
+
+
+@pytest.mark.parametrize("dt", [np.float32, np.float64], ids=["f32", "f64"])
+def test_huge_schemes_shift_basis_and_lanes(dt):
+    n = 240
+    d, e = W.random_batch(n, 40, dt, salt=610)
+    for scheme, shift in ((1, 0), (0, 1)):
+        print("huge scheme/shift", dt.__name__, scheme, shift, flush=True)
+        for jobz in (True, False):
+            g = run_gpu(d, e, jobz, scheme=scheme, shift=shift)
+            o = oracle.steqr(d, e, jobz, threads=8, scheme=scheme, shift=shift)
+            assert check(d, e, g, o, jobz) == [], (scheme, shift, jobz)
+    Z = W.random_basis(n, 40, dt, salt=611)
+    g = run_gpu(d, e, True, Z=Z)
+    o = oracle.steqr(d, e, True, threads=8, Z=Z)
+    assert check_basis(d, e, Z, g, o) == []
+    # values only with four problems per producer wavefront (16 lanes each)
+    g = run_gpu(d, e, False, lanes=16)
+    o = oracle.steqr(d, e, False, threads=8)
+    assert check(d, e, g, o, False) == []
+    # unsorted output and a sweep budget of zero
+    g = run_gpu(d, e, True, sort=False)
+    o = oracle.steqr(d, e, True, sort=False, threads=8)
+    assert check(d, e, (np.sort(g[0], 1), None, g[2]), (np.sort(o[0], 1), None, o[2]), False) == []
+    g = run_gpu(d, e, True, max_sweeps_per_n=-1)
+    assert np.all(g[2] > 0)

@@ -59,6 +59,11 @@ def test_back_transform_pins(oracle_mod, scheme, shift):
     assert P.pin_back_transform(oracle_mod, quick=False, scheme=scheme, shift=shift) == []
 
 
+@pytest.mark.parametrize("scheme,shift", [(0, 0), (1, 1)])
+def test_large_order_pins(oracle_mod, scheme, shift):
+    assert P.pin_large_orders(oracle_mod, scheme=scheme, shift=shift) == []
+
+
 @pytest.mark.parametrize("scheme,shift", [(0, 0), (0, 1), (1, 0), (1, 1)])
 @pytest.mark.parametrize("pin", [P.pin_direction, P.pin_block2], ids=["direction", "block2"])
 def test_direction_and_2x2_pins(oracle_mod, pin, scheme, shift):

@@ -64,6 +64,8 @@ WORKLOADS: Dict[str, Workload] = {
     # beyond the sub-group width: the work-group path's orders (65..128)
     "w_f32_n128": Workload(6, "w_f32_n128", "f32", 128, 8192, ("V", "N"), 16),
     "w_f64_n128": Workload(7, "w_f64_n128", "f64", 128, 8192, ("V", "N"), 16),
+    "w_f32_n256": Workload(8, "w_f32_n256", "f32", 256, 1024, ("V", "N"), 32),
+    "w_f64_n256": Workload(10, "w_f64_n256", "f64", 256, 1024, ("V", "N"), 32),
 }
 
 HEADLINE = "c2_f32_n16"
