@@ -82,13 +82,16 @@ typedef struct steqr_params {
     /* Where a chunked kernel keeps the band d, e during the solve:
      * 0 = tuned default, 1 = replicated in every lane's registers,
      * 2 = shared in LDS (frees registers for more rows of Q per lane),
-     * 3 = (orders 33..128 with eigenvectors) shared in LDS by one producer
-     *     wavefront per workgroup that runs the chase for several problems
-     *     and logs its rotations, applied to Q by consumer wavefronts (one
-     *     per problem up to order 64; four per problem, two lanes per row,
-     *     at orders 65..128); lanes_per_problem then counts producer lanes.
+     * 3 = (orders 33..256 with eigenvectors) shared in LDS by one producer
+     *     wavefront per workgroup that runs the chase for one or several
+     *     problems and logs its rotations, applied to Q by consumer
+     *     wavefronts (one per problem up to order 64; at 65..128 two lanes
+     *     per row, or whole rows in float; at 129..256 eight consumers per
+     *     problem, two lanes per row in float, four in double with two
+     *     workgroups sharing a problem); lanes_per_problem then counts
+     *     producer lanes.
      * Orders above 32 always use LDS (1 means the default there); orders
-     * 65..128 without eigenvectors run the producer's algorithm alone in
+     * 65..256 without eigenvectors run the producer's algorithm alone in
      * every wavefront (band storage 2). */
     int band_storage;
     /* Form of the implicit step (BatchLAS steqr algorithm page, "the two CTA
@@ -125,7 +128,8 @@ typedef struct steqr_params {
      * a band holding a NaN (all eigenvalues NaN). max_sweeps_per_n and
      * no_sort do not apply; update_scheme, shift, band_storage,
      * back_transform must be 0 and lanes_per_problem 0 or the lanes the
-     * kernel uses (the padded order, 64 at order 128; -10 otherwise). */
+     * kernel uses (the padded order, 64 at orders 128 and 256; -10
+     * otherwise). */
     int method;
 } steqr_params;
 
