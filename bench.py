@@ -31,6 +31,8 @@ import workloads as W  # noqa: E402
 
 PEAK_TFLOPS = {"f32": 157.3, "f64": 78.6}  # MI355X published vector peaks
 HBM_PEAK_GBS = 8000.0
+# non-packed vector rate: 256 CUs x 4 SIMDs x 16 lanes x 2 (FMA) x 2.4 GHz
+PEAK_NONPACKED_TFLOPS = 78.6
 
 
 def flops_per_matrix(stats: np.ndarray, n: int, jobz: bool) -> np.ndarray:
@@ -72,6 +74,22 @@ def kernel_source_hash(family: str = "chunk") -> str:
     for f in KERNEL_SOURCES[family]:
         h.update(open(os.path.join(cs, f), "rb").read())
     return h.hexdigest()[:16]
+
+
+def kernel_family(plan: dict, jobz: bool, method: int = 0) -> str:
+    """Kernel family a launch plan runs: bisection; producer and consumer
+    wavefronts (band 3), or their producer alone (values only from order 64
+    at fewer than 64 lanes per problem); one problem per wavefront (64
+    lanes at order 64); the chunked kernel with the band in LDS or in
+    registers."""
+    if method:
+        return "bisect"
+    if plan["band_storage"] == 3 or (not jobz and plan["padded_n"] >= 64
+                                     and plan["lanes_per_problem"] < 64):
+        return "pc"
+    if plan["lanes_per_problem"] == 64:
+        return "wave"
+    return "chunkl" if plan["band_storage"] == 2 else "chunk"
 
 
 def counters_from_profiles(wname: str, jobz: bool, family: str):
@@ -341,9 +359,7 @@ def main() -> int:
     dtype = w.dtype
     peak = PEAK_TFLOPS[dtype]
     roof = None
-    family = ("bisect" if method else "pc" if plan["band_storage"] == 3 else
-              ("wave" if plan["lanes_per_problem"] == 64 else
-               ("chunkl" if plan["band_storage"] == 2 else "chunk")))
+    family = kernel_family(plan, jobz, method)
     if flops is not None:
         ach = flops / sec / 1e12
         ctr = (None if (args.replicate or scheme or bt or method)
@@ -353,6 +369,11 @@ def main() -> int:
                              plan["lanes_per_problem"], "V" if jobz else "N"),
                 "bound": "alu", "achieved": ach, "peak": peak, "unit": "TFLOP/s",
                 "frac": ach / peak,
+                # the published FP32 peak counts packed FP32 FMAs, which this
+                # build does not emit (-packed-fp32-ops); the non-packed rate
+                # is half of it (the FP64 peak is non-packed already)
+                "peak_nonpacked": PEAK_NONPACKED_TFLOPS,
+                "frac_nonpacked": ach / PEAK_NONPACKED_TFLOPS,
                 "traffic": None if ctr is None else ctr.get("hbm_bytes_per_launch"),
                 "algorithmic_flops_per_launch": flops,
                 "algorithmic_flops_per_matrix": flops / nb}
@@ -360,6 +381,7 @@ def main() -> int:
             # executed VALU FLOPs (64 lanes x FP counter) at this run's time
             ex = ctr["executed_flops_per_launch"] / sec / 1e12
             roof["executed"] = {"tflops": ex, "frac": ex / peak,
+                                "frac_nonpacked": ex / PEAK_NONPACKED_TFLOPS,
                                 "flops_per_launch": ctr["executed_flops_per_launch"],
                                 "source": "rocprofv3 SQ_INSTS_VALU_FLOPS_FP%s" % dtype[1:]}
         if ctr is not None and ctr.get("valu_insts_replicated"):

@@ -74,18 +74,13 @@ def parse_resource_usage(text: str) -> dict:
 # Producer-consumer shapes whose register budget is fixed by the workgroup
 # (12 or 11 wavefronts per CU, three per SIMD: 168 registers per lane) and
 # which keep a few bytes per lane in scratch memory (measured by this
-# report): a value held across the pass loop (double, order 64: 12 bytes;
-# float, order 128: 12 bytes), never touched by the chase or the rotation
-# of Q, and in the float order-64 shapes a 20-byte private segment that no
-# instruction accesses (as in the double order-256 shape, 36 bytes). Any
-# other kernel with scratch fails the build.
+# report): a value held across the pass loop (double, order 64, and float,
+# order 128: 12 bytes), never touched by the chase or the rotation of Q;
+# and the double order-256 shape, whose 36-byte private segment no
+# instruction accesses. Any other kernel with scratch fails the build.
 SCRATCH_ALLOWED = {
     "_ZN5steqr15steqr_pc_kernelIdLi64ELi11ELi4ELb0ELb1ELi1EEEvNS_10KernelArgsE": 12,
     "_ZN5steqr15steqr_pc_kernelIdLi64ELi11ELi4ELb1ELb1ELi1EEEvNS_10KernelArgsE": 12,
-    "_ZN5steqr15steqr_pc_kernelIfLi64ELi3ELi16ELb0ELb1ELi1EEEvNS_10KernelArgsE": 20,
-    "_ZN5steqr15steqr_pc_kernelIfLi64ELi3ELi16ELb1ELb1ELi1EEEvNS_10KernelArgsE": 20,
-    "_ZN5steqr15steqr_pc_kernelIfLi64ELi7ELi8ELb0ELb1ELi1EEEvNS_10KernelArgsE": 20,
-    "_ZN5steqr15steqr_pc_kernelIfLi64ELi7ELi8ELb1ELb1ELi1EEEvNS_10KernelArgsE": 20,
     "_ZN5steqr15steqr_pc_kernelIfLi128ELi10ELi8ELb0ELb1ELi1EEEvNS_10KernelArgsE": 12,
     "_ZN5steqr15steqr_pc_kernelIfLi128ELi10ELi8ELb1ELb1ELi1EEEvNS_10KernelArgsE": 12,
     "_ZN5steqr15steqr_pc_kernelIdLi256ELi8ELi64ELb0ELb1ELi4EEEvNS_10KernelArgsE": 36,

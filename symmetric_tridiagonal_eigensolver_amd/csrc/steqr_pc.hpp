@@ -68,7 +68,15 @@ struct SmemPC {
     static constexpr size_t hdr_bytes = ((2 * HDR * sizeof(int) + 15) / 16) * 16;
     static constexpr size_t rank_bytes = ((CH * N * sizeof(int) + 15) / 16) * 16;
     static constexpr size_t fin_bytes = ((NP * sizeof(int) + 15) / 16) * 16;
-    static constexpr size_t bytes = band_bytes + rot_bytes + hdr_bytes + rank_bytes + fin_bytes;
+    // store staging: each consumer writes GROUP of its rows at a time, with
+    // the sort's column permutation, into a GROUP x N tile and copies the
+    // tile to HBM as contiguous 16-byte pieces (about 4 KiB per consumer)
+    static constexpr int ROWS = N <= RPW ? N : RPW;  // rows a consumer holds
+    static constexpr int GROUP_ = (int)(4096 / (N * sizeof(T)));
+    static constexpr int GROUP = GROUP_ < 2 ? 2 : (GROUP_ > ROWS ? ROWS : GROUP_);
+    static constexpr size_t stage_bytes = (size_t)W * GROUP * N * sizeof(T);
+    static constexpr size_t bytes =
+        band_bytes + rot_bytes + hdr_bytes + rank_bytes + fin_bytes + stage_bytes;
 };
 
 // Values-only form (WANTQ false): the producer's algorithm alone, every
@@ -207,14 +215,74 @@ __device__ __forceinline__ void consume(const KernelArgs& args, int lane, int wa
     // every block is closed, hence un-mirrored, by now (orient ^ fin is
     // 0); a remaining reversal would be folded into the column index
     const bool rev = (orient ^ fin[pi]) != 0;
-    if (live & (row < n)) {
-        const int* rk = ranks + pi * N;
-        T* qrow = gq + prob * (long)n * n + (long)row * n;
-        static_for<QW>([&](auto J) {
-            constexpr int j = decltype(J)::value;
-            const int jg = c0 + j;
-            const int jj = rev ? N - 1 - jg : jg;
-            if (jj < n) qrow[rk[jj]] = q[j];
+    // Store through the wavefront's staging tile, GROUP rows at a time: the
+    // lanes of those rows write their values unpermuted (contiguous), then
+    // the whole wavefront writes the rows (contiguous in HBM) in 16-byte
+    // pieces, gathering column c of the sorted order from column inv[c]
+    // (the producer's inverse permutation; reversed when a mirror is left).
+    // Writing permuted columns straight to HBM touched each line several
+    // times (1.6x the algorithmic bytes at order 64).
+    static_assert(S::CQ == 1, "one problem per consumer wavefront");
+    constexpr int G = S::GROUP;
+    constexpr int V = 16 / (int)sizeof(T);
+    T* const stg = reinterpret_cast<T*>(
+        reinterpret_cast<unsigned char*>(const_cast<int*>(fin)) + S::fin_bytes) +
+        (size_t)wave * G * N;
+    const int rl = lane % RPW;    // the lane's row among the wavefront's rows
+    const int row0 = row - rl;    // the wavefront's first row (uniform)
+    if (live) {
+        const int* inv = ranks + pi * N;
+        T* const qb = gq + prob * (long)n * n;
+        static_for<S::ROWS / G>([&](auto GG) {
+            constexpr int g = decltype(GG)::value;
+            const int rg0 = row0 + g * G;  // first row of the group (uniform)
+            if (rg0 < n) {
+                const int gl = rl - g * G;
+                if ((gl >= 0) & (gl < G)) {
+                    static_for<QW>([&](auto J) {
+                        constexpr int j = decltype(J)::value;
+                        stg[gl * N + c0 + j] = q[j];
+                    });
+                }
+                __builtin_amdgcn_wave_barrier();
+                const int rows = n - rg0 < G ? n - rg0 : G;
+                const int total = rows * n;
+                T* const dst = qb + (long)rg0 * n;
+                auto src = [&](int idx) __attribute__((always_inline)) {
+                    const int r = idx / n, c = idx - r * n;
+                    const int jj = inv[c];
+                    return stg[r * N + (rev ? N - 1 - jj : jj)];
+                };
+                if (((reinterpret_cast<uintptr_t>(dst) & 15) == 0) & ((n % V) == 0)) {
+                    // V consecutive elements stay within one row
+                    static_for<(G * N + 64 * V - 1) / (64 * V)>([&](auto K) {
+                        constexpr int k = decltype(K)::value;
+                        const int idx = (k * 64 + lane) * V;
+                        if (idx < total) {
+                            const int r = idx / n, c = idx - r * n;
+                            const T* const sr = stg + r * N;
+                            T v[V];
+                            static_for<V>([&](auto U) {
+                                constexpr int u = decltype(U)::value;
+                                const int jj = inv[c + u];
+                                v[u] = sr[rev ? N - 1 - jj : jj];
+                            });
+                            if constexpr (sizeof(T) == 4) {
+                                *reinterpret_cast<float4*>(dst + idx) = make_float4(v[0], v[1], v[2], v[3]);
+                            } else {
+                                *reinterpret_cast<double2*>(dst + idx) = make_double2(v[0], v[1]);
+                            }
+                        }
+                    });
+                } else {
+                    static_for<(G * N + 63) / 64>([&](auto K) {
+                        constexpr int k = decltype(K)::value;
+                        const int idx = k * 64 + lane;
+                        if (idx < total) dst[idx] = src(idx);
+                    });
+                }
+                __builtin_amdgcn_wave_barrier();
+            }
         });
     }
 }
@@ -640,7 +708,9 @@ __global__ void __launch_bounds__((WANTQ ? (W + 1) * 64 : 256), (pc_min_waves<T,
         }
         myd[kk] = dj;
         myrank[kk] = sort_it ? rk : j;
-        srank[j] = myrank[kk];
+        // the consumers gather column c of the sorted order from column
+        // srank[c] (the inverse permutation; ranks of j < n cover 0..n-1)
+        if (j < n) srank[myrank[kk]] = j;
     });
     if (live & lead_wg) {
         // addressed from the wavefront's first problem (scalar) and the
