@@ -68,11 +68,35 @@ KERNEL_SOURCES = {
 }
 
 
+def strip_comments(src: str) -> str:
+    """C++ source without its comments and blank space (so that a record
+    taken on some code stays valid when only the comments change)."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        if src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        elif src[i] == '"':
+            j = i + 1
+            while j < n and src[j] != '"':
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        else:
+            out.append(src[i])
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_hash(family: str = "chunk") -> str:
+    """Hash of the code (comments stripped) of a kernel family's sources."""
     h = hashlib.sha256()
     cs = os.path.join(ROOT, "symmetric_tridiagonal_eigensolver_amd", "csrc")
     for f in KERNEL_SOURCES[family]:
-        h.update(open(os.path.join(cs, f), "rb").read())
+        h.update(strip_comments(open(os.path.join(cs, f)).read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -5,8 +5,8 @@
  * The operation (BatchLAS steqr algorithm page, problem statement at the top
  * of the page): for each matrix b of a batch, the symmetric tridiagonal
  *     T_b = tridiag(e_1..e_{n-1}; d_1..d_n; e_1..e_{n-1})
- * stored only by its diagonal d and off-diagonal e (band storage, same
- * page), compute the eigenvalues Lambda and, on request, an orthogonal Q
+ * held as the vector d of its n diagonal entries and the vector e of
+ * its n-1 couplings (band storage, same page), compute the eigenvalues Lambda and, on request, an orthogonal Q
  * with T_b = Q Lambda Q^T. The method is the implicit shifted QR/QL
  * iteration of that page: relative deflation, block scaling, a shift from
  * the end 2x2 block, a Givens bulge chase, analytic 2x2 blocks and a final
@@ -64,8 +64,8 @@ enum { STEQR_METHOD_QR = 0, STEQR_METHOD_BISECT = 1 };    /* method */
 
 /* Options of steqr_batched_ex. Zero-initialised fields mean "default". */
 typedef struct steqr_params {
-    /* Sweep budget: max_sweeps_per_n * n implicit sweeps per matrix, the
-     * pages' "30 sweeps per eigenvalue" (BatchLAS "STEQR: the CTA
+    /* Sweep budget: max_sweeps_per_n * n implicit sweeps per matrix; the
+     * pages time with thirty per eigenvalue (BatchLAS "STEQR: the CTA
      * tridiagonal solver" page, setup paragraph). 0 = 30; negative values
      * mean a budget of zero sweeps (every matrix that needs one fails). */
     int max_sweeps_per_n;

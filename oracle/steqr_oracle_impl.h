@@ -7,9 +7,9 @@
  * smoke check and the benchmark's CPU-baseline leg may load it.
  *
  * It is a plain, slow, step-by-step implicit shifted QR/QL solver written
- * from the BatchLAS steqr algorithm page ("steqr, steqr_wg and steqr_cta
- * solve batches of symmetric tridiagonal eigenproblems by implicit shifted
- * QR/QL with deflation"). Each function names the passage it follows.
+ * from the BatchLAS steqr algorithm page (its opening summary: batched
+ * symmetric tridiagonal eigenvalue problems by the implicit shifted QR or
+ * QL iteration with deflation). Each function names the passage it follows.
  * Compile with -ffp-contract=off and without fast-math: every operation is
  * one IEEE operation in precision REAL, in the order written.
  *
@@ -21,9 +21,9 @@
  *   R_SQRT, R_FABS, R_HYPOT, R_COPYSIGN   libm functions for REAL
  */
 
-/* Constants of the scaling step (algorithm page, scaling paragraph: scale
- * a block by ssfmax/||T|| when its norm is too large and by ssfmin/||T||
- * when it is too small but nonzero). The page names ssfmax and ssfmin
+/* Constants of the scaling step (algorithm page, scaling paragraph: a block
+ * whose norm exceeds the safe range is multiplied by ssfmax/||T||, one with a
+ * nonzero norm below it by ssfmin/||T||). The page names ssfmax and ssfmin
  * without defining them; we take the LAPACK definitions sqrt(safmax)/3 and
  * sqrt(safmin)/eps^2 with safmax = 1/safmin. */
 static REAL SFX(c_eps)(void) { return R_EPS; }
@@ -87,7 +87,7 @@ REAL SFX(oracle_shift_closed)(REAL d1, REAL d2, REAL e1)
 }
 
 /* Analytic solve of a deflated 2x2 block [[a, b], [b, c]] (algorithm page,
- * "A deflated block of size 2 is solved analytically" paragraph): returns
+ * 2x2 block paragraph: such a block is diagonalised in closed form): returns
  * its eigenvalues rt1 (replacing a) and rt2 (replacing c) and a rotation
  * (cs, sn) such that J^T B J = diag(rt1, rt2) with J = [[cs, sn], [-sn, cs]].
  * The rotation is the symmetric 2x2 Schur decomposition of Golub and Van
@@ -137,8 +137,9 @@ static void SFX(rot_cols)(REAL *Q, int n, int k, REAL c, REAL s)
 }
 
 /* One implicit shifted QR sweep on the unreduced block [s, m] with shift mu
- * (algorithm page: "QR uses the physical ordering", the Givens/adjacent
- * similarity paragraphs and the bulge paragraph). The first rotation comes
+ * (algorithm page: QR/QL paragraph, where the QR sweep runs in storage order;
+ * the Givens/adjacent similarity paragraphs and the bulge paragraph). The
+ * first rotation comes
  * from (d_s - mu, e_s); each later one from (e_{i-1}, bulge) and annihilates
  * the bulge, storing r in e_{i-1}. Each rotation is applied as the
  * congruence G^T B G of the 2x2 block at (i, i+1):
@@ -179,8 +180,8 @@ long SFX(oracle_sweep)(REAL *d, REAL *e, REAL *Q, int n, int s, int m, REAL mu)
 }
 
 /* One implicit QR sweep on [s, m] in the Parlett-Gray (PG) form of the
- * algorithm page ("the two CTA update schemes"): the scalars (g, p, c, s)
- * are carried along the sweep instead of writing each local similarity.
+ * algorithm page (update-scheme paragraph): four running scalars (g, p, c, s)
+ * pass from step to step in place of the written-out 2x2 congruence.
  * Step i (QR form, as the page writes it):
  *   f_i = s_{i-1} e_i,  (c_i, s_i, r_i) = lartg(g_{i-1}, f_i),
  *   g*_i = d_i - p_{i-1},  r*_i = (d_{i+1} - g*_i) s_i + 2 c_i c_{i-1} e_i,
@@ -218,8 +219,8 @@ long SFX(oracle_sweep_pg)(REAL *d, REAL *e, REAL *Q, int n, int s, int m, REAL m
 }
 
 /* Reverse the block [l, hi] in place: d~_k = d_{l+hi-k}, e~_k = e_{l+hi-1-k}
- * and reverse Q's columns l..hi (algorithm page: "QL runs the same formulas
- * on reversed local indices"). Applying it twice restores the block. */
+ * and reverse Q's columns l..hi (algorithm page, QR/QL paragraph: the QL
+ * sweep is the QR sweep with the local indices reversed). Applying it twice restores the block. */
 static void SFX(reverse_block)(REAL *d, REAL *e, REAL *Q, int n, int l, int hi)
 {
     for (int i = l, j = hi; i < j; ++i, --j) {
@@ -244,8 +245,9 @@ static void SFX(reverse_block)(REAL *d, REAL *e, REAL *Q, int n, int l, int hi)
 }
 
 /* The QR procedure on one split block [l, hi] whose bottom end converges
- * first (algorithm page: "re-tests deflation and locates ... the last (QR)
- * new zero", the 2x2 paragraph, the shift and sweep paragraphs). Loop:
+ * first (algorithm page: deflation paragraph, where each step repeats the
+ * test and finds the last new zero from the converging end; the 2x2, shift
+ * and sweep paragraphs). Loop:
  *  (i)   scan from the bottom for the largest s in (l, m] with e_{s-1}
  *        negligible, zero that e_{s-1}; no such s gives s = l;
  *  (ii)  s == m: d_m has converged, m <- m - 1;

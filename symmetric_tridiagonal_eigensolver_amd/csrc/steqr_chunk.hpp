@@ -12,10 +12,11 @@
 //    (R = ceil(N/P)); each rotation is a lane-parallel update of two columns
 //    of those rows [algo, eigenvector accumulation].
 //  * Static positions. N is a compile-time order (n <= N, padded with a
-//    zero problem tail, [cta, "padding rows are zeroed"]); every loop over
+//    zero problem tail, as on the CTA page's set-up); every loop over
 //    positions is fully unrolled, so d[p], e[p], q[i][p] are registers.
-//  * Direction unification [cta, "QL versus QR ... QR runs as QL on the
-//    mirrored block"]: a block that must converge at its top is mirrored
+//  * Direction unification [cta, micro-structure list, QL versus QR: one
+//    direction runs as the other on the reversed block]: a block that must
+//    converge at its top is mirrored
 //    (the whole order-N problem, Q's columns included, by a static register
 //    reversal) so that every chunk always chases top to bottom and always
 //    converges at the bottom of its block.
@@ -29,7 +30,7 @@
 //    A 2x2 block is a one-step chase at its position, seeded with its
 //    closed-form rotation. The step is written in the EXP form (local
 //    similarity) or, with the PG template flag, in the Parlett-Gray form
-//    [algo, the two CTA update schemes].
+//    [algo, update-scheme paragraph].
 //  * Run-time positions (the shift inputs at the converging end, the block
 //    ends, the sort keys) are read from a per-chunk copy of the band in LDS,
 //    kept current after every change of the band (written by the chase's
@@ -37,7 +38,7 @@
 //    arrays are only ever indexed by compile-time positions.
 //
 // The per-chunk sequence of operations is the one of the steqr algorithm
-// page: split blocks at exact zeros with a running left boundary [algo,
+// page: split blocks at exact zeros, the left boundary moving right [algo,
 // steqr_cta paragraph], scale each block [algo, scaling], converge the end
 // of smaller |d| first [cta, micro-structure list], re-test deflation after
 // every step and locate the last new zero from the converging end [algo],
@@ -290,7 +291,7 @@ __global__ void __launch_bounds__(256) steqr_chunk_kernel(KernelArgs args) {
     // being reduced; ST_DONE: nothing left to reduce (a converged last block
     // may still wait for its close, `pending`).
     int state = live ? ST_OPEN : ST_DONE;
-    int l1 = 0;           // running left boundary of the next split block (original coords)
+    int l1 = 0;           // left boundary of the next split block (original coords)
     int bt = 0, bb = 0;   // current block [bt, bb] in current (possibly mirrored) coords
     int m = 0;            // converging (bottom) end of the active part
     int s = 0;            // top of the unreduced part [s, m]
@@ -468,8 +469,8 @@ __global__ void __launch_bounds__(256) steqr_chunk_kernel(KernelArgs args) {
         // carries g in x and the previous sine in y (f = y e_p)
         x = sd[si] - mu;
         y = PG ? T(1) : se[si];
-        // A 2x2 block at (jpos, jpos+1) [algo, "A deflated block of size 2"
-        // paragraph]: its closed-form Schur rotation becomes the running
+        // A 2x2 block at (jpos, jpos+1) [algo, 2x2 block paragraph]: its
+        // closed-form Schur rotation becomes the running
         // pair of a one-step chase at jpos (lartg returns that rotation, for
         // PG from (cs e, -sj e), the same rotation up to sign), so it is
         // applied by the same similarity and Q update as the sweeps. The
@@ -506,7 +507,7 @@ __global__ void __launch_bounds__(256) steqr_chunk_kernel(KernelArgs args) {
             if ((unsigned)(p - s) < steps) {
                 T c, sn, rr;
                 if constexpr (PG) {
-                    // PG step [algo, the two CTA update schemes]: f = s' e_p,
+                    // PG step [algo, update-scheme paragraph]: f = s' e_p,
                     // (c, s, r) = lartg(g, f), r* = (d_{p+1} - g*) s + 2 c c' e_p,
                     // d_p = g* + s r*, g = c r* - c' e_p (c', s' of the previous
                     // step). g* = d_p - s' r*' is folded into d_p by the

@@ -1,7 +1,7 @@
 // Chunked steqr kernel with the band in LDS (gfx950, wave64).
 //
 // Same per-problem algorithm and lockstep pass structure as
-// steqr_chunk.hpp (one problem per chunk of P lanes, Q rows in VGPRs,
+// steqr_chunk.hpp (P lanes serve one problem, Q rows in VGPRs,
 // mirrored blocks so every chunk chases top to bottom), but the band d, e of
 // each chunk lives in LDS instead of being replicated in every lane's
 // VGPRs. That frees 2N VGPRs per lane, which is what lets a lane hold more
@@ -407,7 +407,7 @@ __global__ void __launch_bounds__(256) steqr_chunkl_kernel(KernelArgs args) {
         dcur = sd[si];
         x = dcur - mu;
         y = PG ? T(1) : se[si];
-        // A 2x2 block at (jpos, jpos+1) [algo, "A deflated block of size 2"
+        // A 2x2 block at (jpos, jpos+1) [algo, 2x2 block
         // paragraph]: its closed-form Schur rotation becomes the running
         // pair of a one-step chase at jpos (lartg returns that rotation, for
         // PG from (cs e, -sj e), the same rotation up to sign), so it is
@@ -447,7 +447,7 @@ __global__ void __launch_bounds__(256) steqr_chunkl_kernel(KernelArgs args) {
                 // the chunk writes the same value to the same word.
                 T c, sn, rr;
                 if constexpr (PG) {
-                    // PG step [algo, the two CTA update schemes]; dcur holds
+                    // PG step [algo, update-scheme paragraph]; dcur holds
                     // g* = d_p - s' r*' (folded in by the previous step), and
                     // after the last step d_m - p and g are what the sweep's
                     // end writes back

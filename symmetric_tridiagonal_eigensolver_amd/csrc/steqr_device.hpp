@@ -2,8 +2,8 @@
 //
 // Everything here runs per lane on values the lane holds in registers; no
 // cross-lane operation is involved. Citations name the BatchLAS pages:
-//   [algo]  the steqr algorithm page ("steqr, steqr_wg and steqr_cta solve
-//           batches of symmetric tridiagonal eigenproblems ...");
+//   [algo]  the BatchLAS steqr algorithm page (batched symmetric tridiagonal
+//           eigensolvers by implicit shifted QR/QL);
 //   [cta]   "STEQR: the CTA tridiagonal solver".
 #pragma once
 
@@ -360,7 +360,8 @@ __device__ __forceinline__ bool negligible(T e, T d1, T d2) {
 // of max(|f|,|g|)) so that f^2 + g^2 lies in [1/16, 1] and can neither
 // overflow nor underflow; the norm is a hardware reciprocal square root
 // (refined in double, see rsq_refined) [cta, Givens rotation paragraph]; g = 0 gives
-// (1, 0, f) through a final select [cta, Givens rotation paragraph]. NaN
+// the identity rotation with r = f, by a final select [cta, Givens rotation
+// paragraph]. NaN
 // inputs give NaN outputs. |f| + |g| cannot overflow for the block-scaled
 // values the solver passes (|f|, |g| stay within a small multiple of ssfmax).
 template <typename T>
@@ -456,7 +457,7 @@ __device__ __forceinline__ T sweep_shift(bool closed, T d1, T d2, T e1) {
     return lapack_shift(d1, d2, e1);
 }
 
-// Analytic 2x2 solve [algo, "A deflated block of size 2" paragraph]: for
+// Analytic 2x2 solve [algo, 2x2 block paragraph]: for
 // B = [[a, b], [b, c]] the symmetric Schur rotation J = [[cs, sn], [-sn, cs]]
 // with J^T B J = diag(a - t b, c + t b), tau = (c - a)/(2b),
 // t = sign(tau)/(|tau| + sqrt(1 + tau^2)) (sign(0) = +1), cs = 1/sqrt(1+t^2),

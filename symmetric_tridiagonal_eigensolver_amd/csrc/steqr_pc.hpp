@@ -596,7 +596,7 @@ __global__ void __launch_bounds__((WANTQ ? (W + 1) * 64 : 256), (pc_min_waves<T,
             if ((unsigned)(p - s) < steps) {
                 T c, sn, rr;
                 if constexpr (PG) {
-                    // PG step [algo, the two CTA update schemes], as in
+                    // PG step [algo, update-scheme paragraph], as in
                     // steqr_chunkl.hpp
                     const T f = y * e0;
                     const T b = cp * e0;

@@ -253,7 +253,7 @@ __global__ void __launch_bounds__(256) steqr_wave_kernel(KernelArgs args) {
                     const T ep = ecur;
                     T c, sn, rr;
                     if constexpr (PG) {
-                        // PG step [algo, the two CTA update schemes]; dcur
+                        // PG step [algo, update-scheme paragraph]; dcur
                         // holds g* (see steqr_chunk.hpp)
                         const T f = y * ep;
                         const T b = cp * ep;

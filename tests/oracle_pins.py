@@ -303,9 +303,9 @@ def pin_direction(oracle, libpath: Optional[str] = None, quick: bool = False,
                   scheme: int = 0, shift: int = 0) -> List[str]:
     """The choice of the converging end ("STEQR: the CTA tridiagonal solver",
     micro-structure list, QL versus QR; the steqr algorithm page, QR/QL
-    paragraph): a graded block must converge its small end first. The CTA
-    page reports that the opposite rule needed about twice the steps and
-    lost relative accuracy on graded input. Pinned on graded items with the
+    paragraph): a graded block must converge its small end first. By the CTA
+    page the opposite choice roughly doubled the number of steps and gave
+    worse relative errors for graded matrices. Pinned on graded items with the
     small end at the bottom and, reversed, at the top (a rule that always or
     never reverses fails one of the two):
       * implicit sweeps per eigenvalue, averaged over the batch, at most 1.5

@@ -5,7 +5,7 @@ holds only input construction (random numbers and the edge-item recipes);
 none of the solver's arithmetic lives here, so both the HIP path and the
 CPU oracle can be fed from it without sharing any of the method.
 
-Each matrix is stored as its diagonal ``d`` (n entries) and off-diagonal
+A matrix is given by its diagonal ``d`` (n entries) and off-diagonal
 ``e`` (n-1 entries), packed per matrix: ``d`` has shape (batch, n) and
 ``e`` shape (batch, n-1), as in the BatchLAS steqr algorithm page (the
 problem statement and band storage at the top of the page).
