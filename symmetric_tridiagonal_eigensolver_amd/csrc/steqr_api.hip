@@ -14,7 +14,13 @@ using steqr::Table;
 // Compile-time orders the build provides, smallest first.
 constexpr int kOrders[] = {4, 8, 16, 32, 64, 128, 256};
 
-int padded_order(int n) {
+// The compiled order a problem of order n runs at. Orders 9..12 in double
+// with eigenvectors have their own instantiation (order 12, 3 rows of Q per
+// lane): padded to 16, a block mirrored for its QL direction lands on
+// positions 4..15 while unmirrored ones occupy 0..11, so the lockstep pass
+// spans both ranges (1.44x the instructions of the lockstep ideal).
+int padded_order(int n, int dtype = -1, int jobz = -1) {
+    if (n > 8 && n <= 12 && dtype == STEQR_F64 && jobz == STEQR_V) return 12;
     for (int N : kOrders)
         if (n <= N) return N;
     return -1;
@@ -31,9 +37,10 @@ int padded_order(int n) {
 // or without its consumers); P = 64 selects one problem per wavefront at
 // orders 33..64.
 int default_lanes(int dtype, int N, int jobz, int band) {
-    // order 256: one problem per producer wavefront with eigenvectors; two
-    // per wavefront (32 lanes each) without
-    if (N == 256) return band == 3 ? 64 : 32;
+    // order 256: one problem per producer wavefront (without eigenvectors
+    // 1024 matrices took 6.52 ms in float at 64 lanes, 6.79 at 32, 6.59 at
+    // 16; double 9.48, 9.65, 9.55)
+    if (N == 256) return 64;
     // order 128, producer lanes per problem: float with eigenvectors runs
     // whole rows of Q per lane (5 problems per producer at 8 lanes each);
     // double with eigenvectors measured 1.4% faster at 32 than at 16
@@ -48,7 +55,7 @@ int default_lanes(int dtype, int N, int jobz, int band) {
     if (N == 64 && !jobz) return 8;
     if (N >= 64) return 64;
     if (jobz) {
-        if (N == 4) return 4;
+        if (N == 4 || N == 12) return 4;
         if (N == 8) return dtype == STEQR_F32 ? 2 : 4;
         // double with the band in registers at 4 lanes needs more than
         // 256 registers per lane and is not built: 8 lanes there
@@ -110,7 +117,8 @@ struct Plan {
 // rows of Q: order 32, and order 16 in double precision.
 int default_band(int dtype, int N, int jobz) {
     if (N >= 64) return jobz ? 3 : 2;
-    if (jobz && (N == 32 || (N == 16 && dtype == STEQR_F64))) return 2;
+    // (order 12 in double: 82.8 against 136 us for 32,768 matrices)
+    if (jobz && (N == 32 || ((N == 16 || N == 12) && dtype == STEQR_F64))) return 2;
     return 1;
 }
 
@@ -147,7 +155,8 @@ int plan_launch(int n, int batch, int jobz, int dtype, const steqr_params* prm, 
         *out = p;
         return 0;
     }
-    const int N = padded_order(n < 2 ? 2 : n);
+    const bool bisect = prm && prm->method == STEQR_METHOD_BISECT;
+    const int N = bisect ? padded_order(n < 2 ? 2 : n) : padded_order(n < 2 ? 2 : n, dtype, jobz);
     if (N < 0) return -5;  // order not provided by this build
     if (prm && prm->method == STEQR_METHOD_BISECT) {
         // values-only bisection: one lane per eigenvalue

@@ -12,8 +12,10 @@ static const Entry kEntries[] = {
     STEQR_PC_ENTRY(1, double, 256, 8, 64),
     STEQR_PCV_ENTRY(0, float, 256, 16),
     STEQR_PCV_ENTRY(0, float, 256, 32),
+    STEQR_PCV_ENTRY(0, float, 256, 64),
     STEQR_PCV_ENTRY(1, double, 256, 16),
     STEQR_PCV_ENTRY(1, double, 256, 32),
+    STEQR_PCV_ENTRY(1, double, 256, 64),
 };
 
 Table STEQR_TABLE(table_huge)() { return {kEntries, (int)(sizeof(kEntries) / sizeof(kEntries[0]))}; }

@@ -58,11 +58,11 @@ def test_version(st):
 
 
 @pytest.mark.parametrize("n,jobz,dtype,N,P", [
-    (1, 1, 0, 4, 4), (4, 1, 0, 4, 4), (5, 1, 0, 8, 2), (8, 0, 0, 8, 1), (12, 1, 1, 16, 4),
+    (1, 1, 0, 4, 4), (4, 1, 0, 4, 4), (5, 1, 0, 8, 2), (8, 0, 0, 8, 1), (12, 1, 1, 12, 4), (12, 0, 1, 16, 1),
     (16, 1, 0, 16, 4), (17, 1, 0, 32, 8), (32, 1, 1, 32, 16), (32, 0, 1, 32, 1), (32, 0, 0, 32, 4), (16, 0, 0, 16, 2), (16, 0, 1, 16, 1),
     (33, 1, 1, 64, 4), (64, 1, 1, 64, 4), (64, 1, 0, 64, 16), (64, 0, 0, 64, 8),
     (40, 0, 1, 64, 8), (100, 1, 0, 128, 8), (100, 1, 1, 128, 32), (128, 0, 0, 128, 16),
-    (129, 1, 0, 256, 64), (256, 1, 1, 256, 64), (200, 0, 0, 256, 32), (256, 0, 1, 256, 32)])
+    (129, 1, 0, 256, 64), (256, 1, 1, 256, 64), (200, 0, 0, 256, 64), (256, 0, 1, 256, 64)])
 def test_query_default_plan(st, n, jobz, dtype, N, P):
     q = st.steqr_query(n, 1000, jobz, dtype)
     assert q["padded_n"] == N and q["lanes_per_problem"] == P

@@ -95,6 +95,9 @@ LANE_CASES += [
     (np.float32, 32, True, 16, 2), (np.float32, 32, True, 8, 2),
     (np.float64, 16, True, 8, 2), (np.float64, 16, True, 4, 2), (np.float64, 32, True, 16, 2),
     (np.float32, 12, True, 4, 2), (np.float64, 27, True, 16, 2),
+    # compiled order 12 (double with eigenvectors, orders 9..12)
+    (np.float64, 12, True, 4, 2), (np.float64, 9, True, 4, 2), (np.float64, 12, True, 4, 1),
+    (np.float64, 10, True, 4, 1),
 ]
 # the producer's algorithm alone, several problems per wavefront (orders
 # 33..64 without eigenvectors)
