@@ -16,6 +16,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import statistics
@@ -91,35 +92,51 @@ def strip_comments(src: str) -> str:
     return " ".join("".join(out).split())
 
 
+# statements of the profiling build's phase timers: they expand to nothing
+# in the library (the compiled kernels are those of the source without them)
+PHASE_TIMER_STMT = re.compile(r'(#include "steqr_phase\.hpp"|STEQR_PHASE_[A-Z]+(\([^()]*\))?;) ?')
+
+
 def kernel_source_hash(family: str = "chunk") -> str:
-    """Hash of the code (comments stripped) of a kernel family's sources."""
+    """Hash of the code (comments and phase-timer statements stripped) of a
+    kernel family's sources."""
     h = hashlib.sha256()
     cs = os.path.join(ROOT, "symmetric_tridiagonal_eigensolver_amd", "csrc")
     for f in KERNEL_SOURCES[family]:
-        h.update(strip_comments(open(os.path.join(cs, f)).read()).encode())
+        src = strip_comments(open(os.path.join(cs, f)).read())
+        h.update(PHASE_TIMER_STMT.sub("", src).encode())
     return h.hexdigest()[:16]
 
 
 def kernel_family(plan: dict, jobz: bool, method: int = 0) -> str:
     """Kernel family a launch plan runs: bisection; producer and consumer
-    wavefronts (band 3), or their producer alone (values only from order 64
-    at fewer than 64 lanes per problem); one problem per wavefront (64
-    lanes at order 64); the chunked kernel with the band in LDS or in
-    registers."""
+    wavefronts (band 3), or their producer alone (values only: at order 64
+    with fewer than 64 lanes per problem, and above order 64); one problem
+    per wavefront (64 lanes at order 64); the chunked kernel with the band
+    in LDS or in registers."""
     if method:
         return "bisect"
     if plan["band_storage"] == 3 or (not jobz and plan["padded_n"] >= 64
-                                     and plan["lanes_per_problem"] < 64):
+                                     and (plan["lanes_per_problem"] < 64
+                                          or plan["padded_n"] > 64)):
         return "pc"
     if plan["lanes_per_problem"] == 64:
         return "wave"
     return "chunkl" if plan["band_storage"] == 2 else "chunk"
 
 
-def counters_from_profiles(wname: str, jobz: bool, family: str):
+def kernel_label(plan: dict, jobz: bool, dtype: str, family: str) -> str:
+    """Name of the kernel instantiation a launch plan runs."""
+    return "steqr_%s_kernel<%s, N=%d, P=%d, %s>" % (
+        family, "float" if dtype == "f32" else "double", plan["padded_n"],
+        plan["lanes_per_problem"], "V" if jobz else "N")
+
+
+def counters_from_profiles(wname: str, jobz: bool, family: str, kernel: str):
     """Per-launch counter record (HBM bytes, executed VALU instructions and
     FLOPs, replicated-batch instructions) committed under profiles/, or None
-    when absent or taken on other kernel sources."""
+    when absent, taken on another kernel instantiation or on other kernel
+    sources."""
     p = os.path.join(ROOT, "profiles", "counters_%s_%s.json" % (wname, "V" if jobz else "N"))
     if not os.path.exists(p):
         return None
@@ -127,7 +144,7 @@ def counters_from_profiles(wname: str, jobz: bool, family: str):
         t = json.load(open(p))
     except Exception:
         return None
-    if t.get("kernel_source_hash") != kernel_source_hash(family):
+    if t.get("kernel_source_hash") != kernel_source_hash(family) or t.get("kernel") != kernel:
         return None
     return t
 
@@ -384,13 +401,12 @@ def main() -> int:
     peak = PEAK_TFLOPS[dtype]
     roof = None
     family = kernel_family(plan, jobz, method)
+    kname = kernel_label(plan, jobz, dtype, family)
     if flops is not None:
         ach = flops / sec / 1e12
         ctr = (None if (args.replicate or scheme or bt or method)
-               else counters_from_profiles(w.name, jobz, family))
-        roof = {"kernel": "steqr_%s_kernel<%s, N=%d, P=%d, %s>"
-                          % (family, "float" if dtype == "f32" else "double", plan["padded_n"],
-                             plan["lanes_per_problem"], "V" if jobz else "N"),
+               else counters_from_profiles(w.name, jobz, family, kname))
+        roof = {"kernel": kname,
                 "bound": "alu", "achieved": ach, "peak": peak, "unit": "TFLOP/s",
                 "frac": ach / peak,
                 # the published FP32 peak counts packed FP32 FMAs, which this

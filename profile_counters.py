@@ -92,10 +92,7 @@ def kernel_family(st, wname: str, jobz: bool):
     import bench
     plan = st.steqr_query(w.n, w.batch, int(jobz), 0 if w.dtype == "f32" else 1)
     fam = bench.kernel_family(plan, jobz)
-    name = "steqr_%s_kernel<%s, N=%d, P=%d, %s>" % (
-        fam, "float" if w.dtype == "f32" else "double", plan["padded_n"],
-        plan["lanes_per_problem"], "V" if jobz else "N")
-    return fam, name, w
+    return fam, bench.kernel_label(plan, jobz, w.dtype, fam), w
 
 
 def calibrate(timeout: int) -> dict:

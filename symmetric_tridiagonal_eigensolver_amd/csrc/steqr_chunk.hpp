@@ -51,6 +51,7 @@
 
 #include "steqr_device.hpp"
 #include "syev_reduce.hpp"
+#include "steqr_phase.hpp"
 
 namespace steqr {
 
@@ -175,6 +176,10 @@ __global__ void __launch_bounds__(256) steqr_chunk_kernel(KernelArgs args) {
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
+    // phase slots: 0 load, 5 settle up to the next operation (block open,
+    // deflation scan, masks), 6 settle's closes and shift, 1 settle's 2x2
+    // step setup, 2 chase, 3 epilogue, 4 passes
+    STEQR_PHASE_START;
     const int chunk = lane / P;
     const int r = lane % P;
     const long prob = ((long)blockIdx.x * (blockDim.x >> 6) + wave) * CH + chunk;
@@ -380,6 +385,7 @@ __global__ void __launch_bounds__(256) steqr_chunk_kernel(KernelArgs args) {
     };
 
     T x = T(0), y = T(0);  // running pair of the chase
+    STEQR_PHASE_MARK(0);
     while (true) {
         // ------------------------------------------------------------ settle
         // Opening and closing blocks are rare (once per block); they run
@@ -437,6 +443,7 @@ __global__ void __launch_bounds__(256) steqr_chunk_kernel(KernelArgs args) {
         m = jac ? s2 - 1 : (go ? t + 1 : m);
         s = go ? s2 : s;
         jtot += sweep ? 1 : 0;
+        STEQR_PHASE_MARK(5);
         // a failed block, or a converged block with another one after it
         const bool close_now = fail | (conv & !last);
         if (__any(close_now)) {
@@ -469,6 +476,7 @@ __global__ void __launch_bounds__(256) steqr_chunk_kernel(KernelArgs args) {
         // carries g in x and the previous sine in y (f = y e_p)
         x = sd[si] - mu;
         y = PG ? T(1) : se[si];
+        STEQR_PHASE_MARK(6);
         // A 2x2 block at (jpos, jpos+1) [algo, 2x2 block paragraph]: its
         // closed-form Schur rotation becomes the running
         // pair of a one-step chase at jpos (lartg returns that rotation, for
@@ -493,6 +501,8 @@ __global__ void __launch_bounds__(256) steqr_chunk_kernel(KernelArgs args) {
         // negligible e already in `zeroed`, which the next deflation test
         // keeps and closing the block restores.
         T cp = T(1);
+        STEQR_PHASE_MARK(1);
+        STEQR_PHASE_ADD(4, 1);
         // The chase runs at a raised issue priority and the settle at the
         // default one: with two wavefronts per SIMD the SIMD's arbiter then
         // prefers the chase's dense VALU stream over the other wavefront's
@@ -572,10 +582,12 @@ __global__ void __launch_bounds__(256) steqr_chunk_kernel(KernelArgs args) {
         __builtin_amdgcn_s_setprio(0);
         if constexpr (WANTQ) __builtin_amdgcn_wave_barrier();
         else publish();
+        STEQR_PHASE_MARK(2);
         // a NaN shift turns [s, m] into NaN, a fixed point of every further
         // sweep: spend the rest of the budget at once (same final state)
         jtot = (sweep & (mu != mu)) ? nmaxit : jtot;
     }
+    STEQR_PHASE_MARK(1);
     // closes of converged last blocks, all at once
     if (__any(pending)) {
         if (pending) close_block(false);
@@ -690,6 +702,8 @@ __global__ void __launch_bounds__(256) steqr_chunk_kernel(KernelArgs args) {
         __builtin_amdgcn_wave_barrier();
         copy_block<T, CH * N * N>(gq + first * nn, stage, nprob * nn, lane, qvec);
     }
+    STEQR_PHASE_MARK(3);
+    STEQR_PHASE_STORE(wave, lane);
 }
 
 }  // namespace steqr

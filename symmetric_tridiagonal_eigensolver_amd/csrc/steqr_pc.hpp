@@ -100,6 +100,9 @@ template <typename T, int N, int W, int P, int RS>
 __device__ __forceinline__ void consume(const KernelArgs& args, int lane, int wave, long first,
                                         const T* rot, const int* hdr, const int* ranks,
                                         const int* fin) {
+    // slots: 0 load, 1 waiting for a pass, 2 applying a pass, 3 epilogue,
+    // 5 passes
+    STEQR_PHASE_START;
     using S = SmemPC<T, N, W, P, RS>;
     using F = Fp<T>;
     constexpr int NP = S::NP;
@@ -144,10 +147,13 @@ __device__ __forceinline__ void consume(const KernelArgs& args, int lane, int wa
     // columns (N-1-p, N-2-p), which is the same update.
     int orient = 0;
     int slot = 0;
+    STEQR_PHASE_MARK(0);
     while (true) {
         __syncthreads();
+        STEQR_PHASE_MARK(1);
         const int* h = hdr + slot * S::HDR;
         if (h[0] == PC_CTRL_END) break;
+        STEQR_PHASE_ADD(5, 1);
         if constexpr (RS == 1) {
             orient ^= h[1 + 3 * pi];
         } else if (h[1 + 3 * pi]) {
@@ -210,8 +216,10 @@ __device__ __forceinline__ void consume(const KernelArgs& args, int lane, int wa
             }
         }
         slot ^= 1;
+        STEQR_PHASE_MARK(2);
     }
     __syncthreads();
+    STEQR_PHASE_MARK(1);
     // every block is closed, hence un-mirrored, by now (orient ^ fin is
     // 0); a remaining reversal would be folded into the column index
     const bool rev = (orient ^ fin[pi]) != 0;
@@ -285,6 +293,8 @@ __device__ __forceinline__ void consume(const KernelArgs& args, int lane, int wa
             }
         });
     }
+    STEQR_PHASE_MARK(3);
+    STEQR_PHASE_STORE(wave, lane);
 }
 
 // Wavefronts per SIMD the register allocation must allow: at order 128 in
@@ -319,6 +329,9 @@ __global__ void __launch_bounds__((WANTQ ? (W + 1) * 64 : 256), (pc_min_waves<T,
     extern __shared__ __align__(16) unsigned char smem_raw[];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
+    // producer's phase slots: 0 load, 1 settle, 2 chase, 3 epilogue, 4
+    // waiting for the consumers, 5 passes, 6 sum of the passes' chase bounds
+    STEQR_PHASE_START;
     using SV = SmemPV<T, N, P>;
     unsigned char* const base = WANTQ ? smem_raw : smem_raw + (size_t)wave * SV::bytes_per_wave;
     T* const band = reinterpret_cast<T*>(base);
@@ -499,6 +512,7 @@ __global__ void __launch_bounds__((WANTQ ? (W + 1) * 64 : 256), (pc_min_waves<T,
 
     int slot = 0;
     T x = T(0), y = T(0), dcur = T(0);
+    STEQR_PHASE_MARK(0);
     while (true) {
         // ------------------------------------------------------------ settle
         if (__any(state == ST_OPEN)) open_blocks();
@@ -576,6 +590,8 @@ __global__ void __launch_bounds__((WANTQ ? (W + 1) * 64 : 256), (pc_min_waves<T,
         flip = 0;
 
         // ------------------------------------------------------------ chase
+        STEQR_PHASE_MARK(1);
+        STEQR_PHASE_ADD(5, 1);
         T* const lg = rot + (size_t)(slot * (NP + 1) + (chunk < NP ? chunk : NP)) * (N - 1) * 2;
         T d0 = sd[0], e0 = se[0], d1 = sd[1], e1 = se[1];
         T cp = T(1);
@@ -586,6 +602,7 @@ __global__ void __launch_bounds__((WANTQ ? (W + 1) * 64 : 256), (pc_min_waves<T,
         // wavefront steps through, tested after every second position (one
         // scalar branch per two positions; an extra position steps no chunk)
         const int me_w = wave_max_uniform(steps != 0u ? s + (int)steps : 0);
+        STEQR_PHASE_ADD(6, me_w);
         static_for_while<N - 1>([&](auto I) {
             constexpr int p = decltype(I)::value;
             T d2 = T(0), e2 = T(0);
@@ -643,9 +660,12 @@ __global__ void __launch_bounds__((WANTQ ? (W + 1) * 64 : 256), (pc_min_waves<T,
         if constexpr (!WANTQ) __builtin_amdgcn_s_setprio(0);
         __builtin_amdgcn_wave_barrier();
         jtot = (sweep & (mu != mu)) ? nmaxit : jtot;
+        STEQR_PHASE_MARK(2);
         if constexpr (WANTQ) __syncthreads();  // the log of this pass is complete
+        STEQR_PHASE_MARK(4);
         slot ^= 1;
     }
+    STEQR_PHASE_MARK(1);
     if constexpr (WANTQ) {
         // no pass left: tell the consumers (their last pass was the previous slot)
         if (lane == 0) hdr[slot * S::HDR] = PC_CTRL_END;
@@ -724,6 +744,8 @@ __global__ void __launch_bounds__((WANTQ ? (W + 1) * 64 : 256), (pc_min_waves<T,
         if (args.info != nullptr && r == 0 && !failed) (args.info + first)[chunk] = 0;
     }
     if constexpr (WANTQ) __syncthreads();  // ranks and final parity are visible to the consumers
+    STEQR_PHASE_MARK(3);
+    STEQR_PHASE_STORE(wave, lane);
 }
 
 }  // namespace steqr
