@@ -165,6 +165,8 @@ def cpu_baseline(d: np.ndarray, e: np.ndarray, jobz: bool, wname: str, scheme: i
     oracle.steqr(d[:64], e[:64], jobz)  # load / warm
     times = []
     stats = None
+    # the full batch once (its rotation counts give the algorithmic flops),
+    # twice more when a run takes under 10 s (median of 3)
     for _ in range(3):
         t = time.perf_counter()
         if method == 1:
@@ -172,10 +174,13 @@ def cpu_baseline(d: np.ndarray, e: np.ndarray, jobz: bool, wname: str, scheme: i
         else:
             _, _, _, stats = oracle.steqr(d, e, jobz, threads=cores, scheme=scheme, Z=Z)
         times.append(time.perf_counter() - t)
+        if times[0] >= 10.0:
+            break
     tmed = statistics.median(times)
     nb = d.shape[0]
-    # one-thread figure on a bounded prefix of the batch
-    m1 = min(nb, 2048)
+    # one-thread figure on a prefix of the batch bounded to about 10 s
+    per1 = tmed * cores / nb
+    m1 = int(min(nb, 2048, max(4, 10.0 / max(per1, 1e-9))))
     t = time.perf_counter()
     if method == 1:
         oracle.stebz(d[:m1], e[:m1], threads=1)
@@ -186,8 +191,8 @@ def cpu_baseline(d: np.ndarray, e: np.ndarray, jobz: bool, wname: str, scheme: i
     return {
         "value": nb / tmed, "unit": "matrices/s", "cores": cores, "kind": "oracle",
         "us_per_matrix": tmed / nb * 1e6,
-        "sample": "full %s batch (%d matrices), median of 3 runs on %d threads"
-                  % (wname, nb, cores),
+        "sample": "full %s batch (%d matrices), median of %d run%s on %d threads"
+                  % (wname, nb, len(times), "s" if len(times) > 1 else "", cores),
         "one_thread_us_per_matrix": t1 / m1 * 1e6,
         "one_thread_sample": "first %d matrices, one run on 1 thread" % m1,
     }, stats

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define STEQR_MAX_N 256
+#define STEQR_MAX_N 512
 
 enum { STEQR_N = 0, STEQR_V = 1 };     /* jobz: values only / values+vectors */
 enum { STEQR_F32 = 0, STEQR_F64 = 1 }; /* dtype */
@@ -82,16 +82,18 @@ typedef struct steqr_params {
     /* Where a chunked kernel keeps the band d, e during the solve:
      * 0 = tuned default, 1 = replicated in every lane's registers,
      * 2 = shared in LDS (frees registers for more rows of Q per lane),
-     * 3 = (orders 33..256 with eigenvectors) shared in LDS by one producer
+     * 3 = (orders 33..512 with eigenvectors) shared in LDS by one producer
      *     wavefront per workgroup that runs the chase for one or several
      *     problems and logs its rotations, applied to Q by consumer
      *     wavefronts (one per problem up to order 64; at 65..128 two lanes
      *     per row, or whole rows in float; at 129..256 eight consumers per
      *     problem, two lanes per row in float, four in double with two
-     *     workgroups sharing a problem); lanes_per_problem then counts
-     *     producer lanes.
+     *     workgroups sharing a problem; at 257..512 eight consumers per
+     *     workgroup, eight lanes per row in float, sixteen in double, with
+     *     eight or sixteen workgroups sharing a problem, each running the
+     *     same chase); lanes_per_problem then counts producer lanes.
      * Orders above 32 always use LDS (1 means the default there); orders
-     * 65..256 without eigenvectors run the producer's algorithm alone in
+     * 65..512 without eigenvectors run the producer's algorithm alone in
      * every wavefront (band storage 2). */
     int band_storage;
     /* Form of the implicit step (BatchLAS steqr algorithm page, "the two CTA
@@ -128,7 +130,7 @@ typedef struct steqr_params {
      * a band holding a NaN (all eigenvalues NaN). max_sweeps_per_n and
      * no_sort do not apply; update_scheme, shift, band_storage,
      * back_transform must be 0 and lanes_per_problem 0 or the lanes the
-     * kernel uses (the padded order, 64 at orders 128 and 256; -10
+     * kernel uses (the padded order, 64 at orders 128 to 512; -10
      * otherwise). */
     int method;
 } steqr_params;

@@ -155,7 +155,7 @@ int SFX(oracle_stebz_one)(int n, const REAL *d, const REAL *e, REAL *lam, long l
 int SFX(oracle_stebz_batched)(const REAL *d, const REAL *e, REAL *lam, int *info,
                               long long *counts, int n, long batch)
 {
-    if (n < 0 || n > 256)
+    if (n < 0 || n > 512)
         return -1;
     for (long b = 0; b < batch && n > 0; ++b) {
         int inf = SFX(oracle_stebz_one)(n, d + b * n, e + b * (n - 1), lam + b * n,

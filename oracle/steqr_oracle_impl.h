@@ -424,7 +424,7 @@ int SFX(oracle_solve_one)(int n, REAL *d, REAL *e, REAL *Q, REAL *lam,
         return info;
     }
     /* stable ascending sort: rank_j = #{k : (d_k, k) before (d_j, j)} */
-    int rank_buf[256];
+    int rank_buf[512];
     int *rank = rank_buf;
     REAL *qtmp = 0;
     for (int j = 0; j < n; ++j) {
@@ -458,7 +458,7 @@ int SFX(oracle_steqr_batched)(const REAL *d, const REAL *e, REAL *lam,
                               long batch, int max_sweeps_per_n, int sort, int scheme,
                               int shift, int back_transform)
 {
-    if (n < 0 || n > 256)
+    if (n < 0 || n > 512)
         return -1;
     if (n == 0)
         return 0;

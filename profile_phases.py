@@ -52,6 +52,8 @@ CASES = {
     "w_f32_n128:V": (3, "f32", 128, 8, 3, 10),
     "c2_f32_n16:N": (4, "f32", 16, 2, 1, 0),
     "c4_f64_n32:N": (5, "f64", 32, 1, 1, 0),
+    "w_f32_n256:V": (6, "f32", 256, 64, 3, 8),
+    "w_f64_n256:V": (7, "f64", 256, 64, 3, 8),
 }
 LATENCY = ["double FMA (v_fma_f64)", "double reciprocal square root (v_rsq_f64)",
            "refined double reciprocal square root (solver's rsq_refined)",

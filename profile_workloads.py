@@ -32,12 +32,12 @@ CASES = ["c1_f32_n4:V", "c2_f32_n8:V", "c2_f32_n8:N", "c2_f32_n16:V", "c2_f32_n1
          "c3_f64_n12:V", "c3_f64_n16:V", "c4_f32_n32:V", "c4_f32_n32:N", "c4_f64_n32:V",
          "c4_f64_n32:N", "c5_f64_n64:V", "c5_f64_n64:N", "w_f32_n128:V", "w_f32_n128:N",
          "w_f64_n128:V", "w_f64_n128:N", "w_f32_n256:V", "w_f32_n256:N", "w_f64_n256:V",
-         "w_f64_n256:N"]
+         "w_f64_n256:N", "w_f32_n512:V", "w_f32_n512:N", "w_f64_n512:V", "w_f64_n512:N"]
 HEADLINE = "c2_f32_n16:V"
 
 
 def bench_args(wname: str, j: str):
-    steps = "20" if wname.startswith(("w_", "c5_")) else "200"
+    steps = ("5" if wname.endswith("n512") else "20") if wname.startswith(("w_", "c5_")) else "200"
     return ["--workload", wname, "--jobz", j, "--steps", steps, "--warmup", "5"]
 
 
@@ -100,6 +100,7 @@ def collect(case: str, out: str, timeout: int) -> str:
     wname, j = case.split(":")
     t = time.time()
     line = run_bench(bench_args(wname, j), timeout)
+    print("  %s: bench.py done (%.0fs)" % (case, time.time() - t), flush=True)
     rows, tcmd = run_trace(trace_args(wname, j), timeout)
     fam = line["roofline"]["kernel"].split("<")[0][len("steqr_"):-len("_kernel")]
     rec = {"case": case, "bench": line, "bench_command": "python3 bench.py " +
@@ -133,7 +134,7 @@ def summarise(src: str) -> None:
         "    python3 profile_workloads.py --out OUT " + " ".join(order),
         "    python3 profile_workloads.py --summarise OUT", "",
         "which runs, per case:", "",
-        "    python3 bench.py --workload WL --jobz J --steps S --warmup 5   (S = 20 for c5 and w_*, else 200)",
+        "    python3 bench.py --workload WL --jobz J --steps S --warmup 5   (S = 5 at order 512, 20 for c5 and the other w_*, else 200)",
         "    rocprofv3 --kernel-trace --stats -d OUT -o run --output-format csv -- python3 bench.py --workload WL "
         "--jobz J --steps 20 --warmup 2 --no-cpu --no-named --no-saturation", "",
         "The trace average covers the warm-up, timed and spread-round launches of the short run. "

@@ -18,7 +18,7 @@ STEQR_F32, STEQR_F64 = 0, 1
 STEQR_EXP, STEQR_PG = 0, 1
 STEQR_SHIFT_LAPACK, STEQR_SHIFT_CLOSED = 0, 1
 STEQR_METHOD_QR, STEQR_METHOD_BISECT = 0, 1
-STEQR_MAX_N = 256
+STEQR_MAX_N = 512
 SYEV_MAX_N = 32
 SYEV_MAX_N_F64_V = 16
 

@@ -12,7 +12,7 @@ using steqr::Entry;
 using steqr::Table;
 
 // Compile-time orders the build provides, smallest first.
-constexpr int kOrders[] = {4, 8, 16, 32, 64, 128, 256};
+constexpr int kOrders[] = {4, 8, 16, 32, 64, 128, 256, 512};
 
 // The compiled order a problem of order n runs at. Orders 9..12 in double
 // with eigenvectors have their own instantiation (order 12, 3 rows of Q per
@@ -33,14 +33,14 @@ int padded_order(int n, int dtype = -1, int jobz = -1) {
 // four to eight rows per lane while the wavefront still fits two waves per
 // SIMD. Values only keep one lane per problem in double and at orders up to
 // 8, two at order 16 and four at order 32 in float (measured). At orders
-// 33..128 P counts the producer lanes of the producer-consumer kernel (with
+// 33..512 P counts the producer lanes of the producer-consumer kernel (with
 // or without its consumers); P = 64 selects one problem per wavefront at
 // orders 33..64.
 int default_lanes(int dtype, int N, int jobz, int band) {
-    // order 256: one problem per producer wavefront (without eigenvectors
-    // 1024 matrices took 6.52 ms in float at 64 lanes, 6.79 at 32, 6.59 at
-    // 16; double 9.48, 9.65, 9.55)
-    if (N == 256) return 64;
+    // orders 256 and 512: one problem per producer wavefront (without
+    // eigenvectors 1024 matrices of order 256 took 6.52 ms in float at 64
+    // lanes, 6.79 at 32, 6.59 at 16; double 9.48, 9.65, 9.55)
+    if (N >= 256) return 64;
     // order 128, producer lanes per problem: float with eigenvectors runs
     // whole rows of Q per lane (5 problems per producer at 8 lanes each);
     // double with eigenvectors measured 1.4% faster at 32 than at 16
@@ -79,6 +79,7 @@ const Entry* search(const Table& t, int dtype, int N, int P, int jobz, int band)
 }
 
 const Entry* find_entry(int dtype, int N, int P, int jobz, int band, int pg) {
+    if (N == 512) return search(pg ? steqr::table_n512_pg() : steqr::table_n512(), dtype, N, P, jobz, band);
     if (N == 256) return search(pg ? steqr::table_huge_pg() : steqr::table_huge(), dtype, N, P, jobz, band);
     if (N == 128) return search(pg ? steqr::table_big_pg() : steqr::table_big(), dtype, N, P, jobz, band);
     if (band == 3) return search(pg ? steqr::table_pc_pg() : steqr::table_pc(), dtype, N, P, jobz, band);

@@ -60,10 +60,10 @@ template <typename T, int N>
 __global__ void __launch_bounds__(256) steqr_bisect_kernel(KernelArgs args) {
     // L lanes per problem, E = N / L positions and eigenvalue indices per
     // lane (k, k + L, ...): one index per lane up to order 64, two at 128,
-    // four at 256
+    // four at 256, eight at 512
     constexpr int L = N < 64 ? N : 64;
     constexpr int E = N / L;
-    static_assert(N >= 2 && N <= 256 && (64 % L) == 0 && E * L == N, "lanes per position");
+    static_assert(N >= 2 && N <= 512 && (64 % L) == 0 && E * L == N, "lanes per position");
     using F = Fp<T>;
     using S = SmemB<T, N>;
     constexpr int CH = 64 / L;

@@ -51,7 +51,7 @@ __device__ __forceinline__ unsigned chunk_or(unsigned v) {
     if constexpr (P == 64) v = (unsigned)__builtin_amdgcn_readfirstlane((int)v);
     return v;
 }
-// OR over the P lanes of a chunk for 32-, 64- and 128-bit masks (DPP lane
+// OR over the P lanes of a chunk for masks of 32 to 512 bits (DPP lane
 // moves on each 32-bit word)
 template <int P, typename M>
 __device__ __forceinline__ M chunk_or_mask(M v) {
@@ -64,7 +64,7 @@ __device__ __forceinline__ M chunk_or_mask(M v) {
         return out;
     } else {
         M out;
-        static_for<4>([&](auto WW) {
+        static_for<M::WORDS>([&](auto WW) {
             constexpr int w = decltype(WW)::value;
             const uint64_t lo = chunk_or<P>((unsigned)v.w[w]);
             const uint64_t hi = chunk_or<P>((unsigned)(v.w[w] >> 32));

@@ -195,59 +195,81 @@ __device__ __forceinline__ unsigned chunk_or_dpp(unsigned v) {
 
 typedef unsigned __int128 u128;
 
-// 256-bit position mask (orders 129..256): four 64-bit words, word i
-// holding positions 64i .. 64i+63. The operators are the ones the solver's
-// mask arithmetic uses; shifts take run-time counts (word index and bit
-// offset selected per lane).
-struct u256 {
-    uint64_t w[4];
-    __device__ constexpr u256() : w{0, 0, 0, 0} {}
-    __device__ constexpr u256(uint64_t v) : w{v, 0, 0, 0} {}
-    __device__ constexpr u256(uint64_t a, uint64_t b, uint64_t c, uint64_t d) : w{a, b, c, d} {}
-    __device__ u256 operator|(const u256& o) const {
-        return u256(w[0] | o.w[0], w[1] | o.w[1], w[2] | o.w[2], w[3] | o.w[3]);
+// Wide position masks (orders 129..512): W 64-bit words, word i holding
+// positions 64i .. 64i+63. The operators are the ones the solver's mask
+// arithmetic uses; shifts take run-time counts (word index and bit offset
+// selected per lane).
+template <int W>
+struct uwide {
+    static constexpr int WORDS = W;
+    uint64_t w[W];
+    __device__ constexpr uwide() : w{} {}
+    __device__ constexpr uwide(uint64_t v) : w{v} {}
+    __device__ uwide operator|(const uwide& o) const {
+        uwide r;
+        for (int i = 0; i < W; ++i) r.w[i] = w[i] | o.w[i];
+        return r;
     }
-    __device__ u256 operator&(const u256& o) const {
-        return u256(w[0] & o.w[0], w[1] & o.w[1], w[2] & o.w[2], w[3] & o.w[3]);
+    __device__ uwide operator&(const uwide& o) const {
+        uwide r;
+        for (int i = 0; i < W; ++i) r.w[i] = w[i] & o.w[i];
+        return r;
     }
-    __device__ u256 operator~() const { return u256(~w[0], ~w[1], ~w[2], ~w[3]); }
-    __device__ u256& operator|=(const u256& o) { return *this = *this | o; }
-    __device__ u256& operator&=(const u256& o) { return *this = *this & o; }
-    __device__ bool operator==(const u256& o) const {
-        return ((w[0] ^ o.w[0]) | (w[1] ^ o.w[1]) | (w[2] ^ o.w[2]) | (w[3] ^ o.w[3])) == 0;
+    __device__ uwide operator~() const {
+        uwide r;
+        for (int i = 0; i < W; ++i) r.w[i] = ~w[i];
+        return r;
     }
-    __device__ bool operator!=(const u256& o) const { return !(*this == o); }
-    __device__ explicit operator bool() const { return (w[0] | w[1] | w[2] | w[3]) != 0; }
+    __device__ uwide& operator|=(const uwide& o) { return *this = *this | o; }
+    __device__ uwide& operator&=(const uwide& o) { return *this = *this & o; }
+    __device__ bool operator==(const uwide& o) const {
+        uint64_t d = 0;
+        for (int i = 0; i < W; ++i) d |= w[i] ^ o.w[i];
+        return d == 0;
+    }
+    __device__ bool operator!=(const uwide& o) const { return !(*this == o); }
+    __device__ explicit operator bool() const {
+        uint64_t d = 0;
+        for (int i = 0; i < W; ++i) d |= w[i];
+        return d != 0;
+    }
     __device__ explicit operator unsigned() const { return (unsigned)w[0]; }
-    // word j of the value (0 outside 0..3)
+    // word j of the value (0 outside 0..W-1)
     __device__ uint64_t word(int j) const {
-        return j == 0 ? w[0] : (j == 1 ? w[1] : (j == 2 ? w[2] : (j == 3 ? w[3] : 0ull)));
+        uint64_t r = 0;
+        for (int i = W - 1; i >= 0; --i) r = j == i ? w[i] : r;
+        return r;
     }
-    __device__ u256 operator<<(int k) const {
+    __device__ uwide operator<<(int k) const {
         const int ws = k >> 6, bs = k & 63;
-        u256 r;
-        for (int i = 0; i < 4; ++i) {
+        uwide r;
+        for (int i = 0; i < W; ++i) {
             const uint64_t hi = word(i - ws), lo = word(i - ws - 1);
             r.w[i] = (hi << bs) | ((lo >> 1) >> (63 - bs));
         }
         return r;
     }
-    __device__ u256 operator>>(int k) const {
+    __device__ uwide operator>>(int k) const {
         const int ws = k >> 6, bs = k & 63;
-        u256 r;
-        for (int i = 0; i < 4; ++i) {
+        uwide r;
+        for (int i = 0; i < W; ++i) {
             const uint64_t lo = word(i + ws), hi = word(i + ws + 1);
             r.w[i] = (lo >> bs) | ((hi << 1) << (63 - bs));
         }
         return r;
     }
 };
+typedef uwide<4> u256;
+typedef uwide<8> u512;
 
 template <int N>
 using PosMask = typename std::conditional<
-    (N > 128), u256,
-    typename std::conditional<(N > 64), u128,
-                              typename std::conditional<(N > 32), uint64_t, uint32_t>::type>::type>::type;
+    (N > 256), u512,
+    typename std::conditional<
+        (N > 128), u256,
+        typename std::conditional<(N > 64), u128,
+                                  typename std::conditional<(N > 32), uint64_t,
+                                                            uint32_t>::type>::type>::type>::type;
 
 // bits [0, k), 0 <= k <= width
 template <typename M>
@@ -259,8 +281,8 @@ __device__ __forceinline__ M bits_below(int k) {
     } else if constexpr (sizeof(M) == 16) {
         return k >= 128 ? ~(M)0 : (((M)1 << k) - (M)1);
     } else {
-        u256 r;
-        for (int i = 0; i < 4; ++i) {
+        M r;
+        for (int i = 0; i < M::WORDS; ++i) {
             const int b = k - 64 * i;  // bits of word i below k
             r.w[i] = b >= 64 ? ~0ull : (b <= 0 ? 0ull : ((1ull << b) - 1ull));
         }
@@ -285,10 +307,11 @@ __device__ __forceinline__ int msb(M x) {
         const uint64_t hi = (uint64_t)(x >> 64), lo = (uint64_t)x;
         return hi ? 127 - __clzll((long long)hi) : 63 - __clzll((long long)lo);
     } else {
-        return x.w[3] ? 255 - __clzll((long long)x.w[3])
-                      : (x.w[2] ? 191 - __clzll((long long)x.w[2])
-                                : (x.w[1] ? 127 - __clzll((long long)x.w[1])
-                                          : 63 - __clzll((long long)x.w[0])));
+        // the highest nonzero word decides
+        int r = 0;
+        for (int i = 0; i < M::WORDS; ++i)
+            r = x.w[i] ? 64 * i + 63 - __clzll((long long)x.w[i]) : r;
+        return r;
     }
 }
 template <typename M>
@@ -301,10 +324,11 @@ __device__ __forceinline__ int lsb(M x) {
         const uint64_t hi = (uint64_t)(x >> 64), lo = (uint64_t)x;
         return lo ? __ffsll((long long)lo) - 1 : 63 + __ffsll((long long)hi);
     } else {
-        return x.w[0] ? __ffsll((long long)x.w[0]) - 1
-                      : (x.w[1] ? 63 + __ffsll((long long)x.w[1])
-                                : (x.w[2] ? 127 + __ffsll((long long)x.w[2])
-                                          : 191 + __ffsll((long long)x.w[3])));
+        // the lowest nonzero word decides
+        int r = 0;
+        for (int i = M::WORDS - 1; i >= 0; --i)
+            r = x.w[i] ? 64 * i + __ffsll((long long)x.w[i]) - 1 : r;
+        return r;
     }
 }
 
@@ -314,8 +338,11 @@ __device__ __forceinline__ int popc(M x) {
     else if constexpr (sizeof(M) == 8) return __popcll((unsigned long long)x);
     else if constexpr (sizeof(M) == 16)
         return __popcll((unsigned long long)x) + __popcll((unsigned long long)(x >> 64));
-    else
-        return __popcll(x.w[0]) + __popcll(x.w[1]) + __popcll(x.w[2]) + __popcll(x.w[3]);
+    else {
+        int r = 0;
+        for (int i = 0; i < M::WORDS; ++i) r += __popcll(x.w[i]);
+        return r;
+    }
 }
 
 // bit p set (0 <= p < width)
@@ -324,8 +351,8 @@ __device__ __forceinline__ M bit_at(int p) {
     if constexpr (sizeof(M) <= 16) {
         return (M)1 << p;
     } else {
-        u256 r;
-        for (int i = 0; i < 4; ++i) r.w[i] = (p >> 6) == i ? (1ull << (p & 63)) : 0ull;
+        M r;
+        for (int i = 0; i < M::WORDS; ++i) r.w[i] = (p >> 6) == i ? (1ull << (p & 63)) : 0ull;
         return r;
     }
 }

@@ -7,11 +7,11 @@ static const Entry kEntries[] = {
     STEQR_BISECT_ENTRY(0, float, 4), STEQR_BISECT_ENTRY(0, float, 8),
     STEQR_BISECT_ENTRY(0, float, 16), STEQR_BISECT_ENTRY(0, float, 32),
     STEQR_BISECT_ENTRY(0, float, 64), STEQR_BISECT_ENTRY(0, float, 128),
-    STEQR_BISECT_ENTRY(0, float, 256),
+    STEQR_BISECT_ENTRY(0, float, 256), STEQR_BISECT_ENTRY(0, float, 512),
     STEQR_BISECT_ENTRY(1, double, 4), STEQR_BISECT_ENTRY(1, double, 8),
     STEQR_BISECT_ENTRY(1, double, 16), STEQR_BISECT_ENTRY(1, double, 32),
     STEQR_BISECT_ENTRY(1, double, 64), STEQR_BISECT_ENTRY(1, double, 128),
-    STEQR_BISECT_ENTRY(1, double, 256),
+    STEQR_BISECT_ENTRY(1, double, 256), STEQR_BISECT_ENTRY(1, double, 512),
 };
 
 Table table_bisect() { return {kEntries, (int)(sizeof(kEntries) / sizeof(kEntries[0]))}; }

@@ -1,5 +1,5 @@
-// Producer-consumer steqr kernel for orders 33..128 with eigenvectors (and
-// values only at 65..128)
+// Producer-consumer steqr kernel for orders 33..512 with eigenvectors (and
+// values only at 65..512)
 // (gfx950, wave64).
 //
 // At these orders a problem's Q fills much of a wavefront's registers (at
@@ -19,12 +19,14 @@
 //  * W consumer wavefronts each hold the Q of 64/N problems (lane = row) and apply
 //    the logged rotations of the previous pass while the producer computes
 //    the next one (two log slots, one workgroup barrier per pass).
-// At order 128 a row of Q is split over two lanes of one wavefront (columns
-// 0..63 and 64..127, lanes l and l^32), so a consumer wavefront holds 32
-// rows and a problem takes four; the unrolled pass applies the rotations in
-// position order, so the lanes of the half a rotation falls in run it while
-// the others are masked, and the one rotation that straddles the halves
-// swaps the two boundary values across the lane pair. Without eigenvectors
+// From order 128 a row of Q is split over RS lanes of one wavefront (at
+// order 128 two: columns 0..63 and 64..127 in lanes l and l^32; at 256 two
+// or four, at 512 eight or sixteen), so a consumer wavefront holds 64/RS
+// rows; the unrolled pass applies the rotations in position order, so the
+// lanes of the part a rotation falls in run it while the others are masked,
+// and a rotation that straddles two parts swaps the two boundary values
+// across the lane pair. When a problem needs more consumers than a
+// workgroup holds, several workgroups share it, each with its own producer. Without eigenvectors
 // (WANTQ false) every wavefront is a producer of its own problems and no
 // log is written.
 // The consumers' column updates are the same as the other kernels' and
@@ -41,14 +43,21 @@ namespace steqr {
 
 // W consumer wavefronts. RS lanes hold one row of Q (at order 128 by
 // default two half rows; at order 256 halves in float, quarters in double,
-// 128 registers per lane either way), so a consumer holds RPW = 64/RS
+// 128 registers per lane either way; at order 512 eighths in float and
+// sixteenths in double, 64 registers per lane, which keeps the kernel
+// within the 168 registers per lane of three wavefronts per SIMD without
+// spilling), so a consumer holds RPW = 64/RS
 // rows: CQ = RPW/N problems when N <= RPW, else WPP = N/RPW consumers per
 // problem. When one problem needs more consumers than a workgroup holds
-// (double at order 256: 16), GPP = WPP/W workgroups share it, each with its
+// (double at order 256: 16; at 512: 64 in float, 128 in double), GPP = WPP/W
+// workgroups share it, each with its
 // own producer (the producers compute the same rotations) and a slice of
 // the rows. NP = W * CQ / WPP problems per workgroup (1 when shared).
 template <typename T, int N>
-constexpr int pc_default_rs() { return N <= 64 ? 1 : (N == 128 ? 2 : (sizeof(T) == 4 ? 2 : 4)); }
+constexpr int pc_default_rs() {
+    return N <= 64 ? 1 : (N == 128 ? 2 : (N == 256 ? (sizeof(T) == 4 ? 2 : 4)
+                                                    : (sizeof(T) == 4 ? 8 : 16)));
+}
 
 template <typename T, int N, int W, int P, int RS = pc_default_rs<T, N>()>
 struct SmemPC {
@@ -316,8 +325,8 @@ __global__ void __launch_bounds__((WANTQ ? (W + 1) * 64 : 256), (pc_min_waves<T,
     constexpr int NP = WANTQ ? S::NP : CH;
     // At order 32 (two problems per consumer) this split measured slower
     // than the LDS-band chunked kernel, so orders 64 and 128 are built.
-    static_assert(N == 64 || N == 128 || N == 256,
-                  "the producer-consumer kernel is for orders 64, 128 and 256");
+    static_assert(N == 64 || N == 128 || N == 256 || N == 512,
+                  "the producer-consumer kernel is for orders 64, 128, 256 and 512");
     static_assert(!WANTQ || (W % WPP) == 0 || (WPP % W) == 0,
                   "whole problems per workgroup, or whole workgroups per problem");
     static_assert(P >= 2 && (64 % P) == 0 && (N % P) == 0 && 64 / P >= NP, "P lanes per chunk");
@@ -732,14 +741,20 @@ __global__ void __launch_bounds__((WANTQ ? (W + 1) * 64 : 256), (pc_min_waves<T,
         // srank[c] (the inverse permutation; ranks of j < n cover 0..n-1)
         if (j < n) srank[myrank[kk]] = j;
     });
+    __builtin_amdgcn_wave_barrier();  // srank is complete
     if (live & lead_wg) {
         // addressed from the wavefront's first problem (scalar) and the
-        // chunk index, so no 64-bit problem index stays live through the loop
+        // chunk index, so no 64-bit problem index stays live through the
+        // loop; lane r writes sorted places r, r+P, ... (consecutive lanes,
+        // consecutive words) from the inverse permutation: a scattered store
+        // at the ranks touched each line several times (2.6x the
+        // algorithmic bytes for 256 float matrices of order 512 without
+        // eigenvectors)
         T* const glw = glam + first * n;
         static_for<K>([&](auto KK) {
             constexpr int kk = decltype(KK)::value;
-            const int j = r + kk * P;
-            if (j < n) glw[chunk * n + myrank[kk]] = myd[kk];
+            const int c = r + kk * P;
+            if (c < n) glw[chunk * n + c] = sd[srank[c]];
         });
         if (args.info != nullptr && r == 0 && !failed) (args.info + first)[chunk] = 0;
     }

@@ -154,6 +154,8 @@ Table table_big();
 Table table_big_pg();
 Table table_huge();
 Table table_huge_pg();
+Table table_n512();
+Table table_n512_pg();
 Table table_syev_f32();
 Table table_syev_f64();
 Table table_bisect();

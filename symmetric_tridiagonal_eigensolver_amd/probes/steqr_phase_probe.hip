@@ -17,6 +17,9 @@ using LaunchFn = steqr::LaunchFn;
 //        3 producer-consumer <float, 128, 10 consumers, 8 lanes, whole rows>
 //        4 chunked <float, 16, 2 lanes, values only>
 //        5 chunked <double, 32, 1 lane, values only>
+//        6 producer-consumer <float, 256, 8 consumers, 64 lanes>
+//        7 producer-consumer <double, 256, 8 consumers, 64 lanes> (two
+//          workgroups per problem)
 LaunchFn kernel_of(int which) {
     switch (which) {
         case 0: return &steqr::launch_chunk<float, 16, 4, true, false>;
@@ -25,6 +28,8 @@ LaunchFn kernel_of(int which) {
         case 3: return &steqr::launch_pc<float, 128, 10, 8, false, 1>;
         case 4: return &steqr::launch_chunk<float, 16, 2, false, false>;
         case 5: return &steqr::launch_chunk<double, 32, 1, false, false>;
+        case 6: return &steqr::launch_pc<float, 256, 8, 64, false>;
+        case 7: return &steqr::launch_pc<double, 256, 8, 64, false>;
         default: return nullptr;
     }
 }
@@ -72,7 +77,7 @@ extern "C" int steqr_phase_launch(int which, const void* d, const void* e, void*
     const LaunchFn fn = kernel_of(which);
     if (fn == nullptr) return -1;
     if (d == nullptr || e == nullptr || lambda == nullptr || phase == nullptr) return -2;
-    if (which <= 3 && Q == nullptr) return -2;  // the kernels with eigenvectors
+    if ((which <= 3 || which >= 6) && Q == nullptr) return -2;  // kernels with eigenvectors
     if (n < 1 || batch < 1 || grid < 1 || block < 64 || (block % 64) != 0) return -3;
     KernelArgs a{};
     a.d = d;

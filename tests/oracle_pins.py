@@ -382,15 +382,15 @@ def pin_block2(oracle, libpath: Optional[str] = None, quick: bool = False,
 
 def pin_large_orders(oracle, libpath: Optional[str] = None, scheme: int = 0,
                      shift: int = 0) -> List[str]:
-    """Orders 129..256 (beyond the largest sub-group-width kernels): random
+    """Orders 129..512 (beyond the largest sub-group-width kernels): random
     items against long-double Sturm bisection with the residual and
     orthogonality bounds, the Kac-Sylvester-Clement integer spectrum and the
-    Toeplitz closed form a + 2b cos(k pi/(n+1)) at order 256."""
+    Toeplitz closed form a + 2b cos(k pi/(n+1)) at orders 256 and 512."""
     out: List[str] = []
     kw = dict(libpath=libpath, scheme=scheme, shift=shift)
     for dt in (np.float32, np.float64):
-        for n in (129, 200, 256):
-            d, e = W.random_batch(n, 4, dt, salt=77)
+        for n in (129, 200, 256, 300, 512):
+            d, e = W.random_batch(n, 4 if n <= 256 else 2, dt, salt=77)
             lam, Q, info, _ = oracle.steqr(d, e, True, **kw)
             tol = V.tol_of(dt, n)
             ref = V.sturm_eigvals(d, e).astype(np.float64)
@@ -398,19 +398,21 @@ def pin_large_orders(oracle, libpath: Optional[str] = None, scheme: int = 0,
             _fail(out, not info.any() and err <= tol, "order %d %s vs Sturm: %g" % (n, dt.__name__, err))
             _fail(out, V.band_residual(d, e, lam, Q).max() <= tol
                   and V.orthogonality(Q).max() <= tol, "order %d %s residual" % (n, dt.__name__))
-        n = 256
-        cd, ce, cref = clement(n)
-        lam, _, info, _ = oracle.steqr(cd.astype(dt), ce.astype(dt), False, **kw)
-        err = np.abs(lam[0].astype(np.float64) - cref).max() / V.tnorm1(cd, ce)[0]
-        _fail(out, info[0] == 0 and err <= V.tol_of(dt, n), "Clement 256 %s: %g" % (dt.__name__, err))
-        a, b = 0.5, -1.25
-        td = np.full((1, n), a)
-        te = np.full((1, n - 1), b)
-        k = np.arange(1, n + 1)
-        tref = np.sort(a + 2 * b * np.cos(k * np.pi / (n + 1)))
-        lam, _, info, _ = oracle.steqr(td.astype(dt), te.astype(dt), False, **kw)
-        err = np.abs(lam[0].astype(np.float64) - tref).max() / V.tnorm1(td, te)[0]
-        _fail(out, info[0] == 0 and err <= V.tol_of(dt, n), "Toeplitz 256 %s: %g" % (dt.__name__, err))
+        for n in (256, 512):
+            cd, ce, cref = clement(n)
+            lam, _, info, _ = oracle.steqr(cd.astype(dt), ce.astype(dt), False, **kw)
+            err = np.abs(lam[0].astype(np.float64) - cref).max() / V.tnorm1(cd, ce)[0]
+            _fail(out, info[0] == 0 and err <= V.tol_of(dt, n),
+                  "Clement %d %s: %g" % (n, dt.__name__, err))
+            a, b = 0.5, -1.25
+            td = np.full((1, n), a)
+            te = np.full((1, n - 1), b)
+            k = np.arange(1, n + 1)
+            tref = np.sort(a + 2 * b * np.cos(k * np.pi / (n + 1)))
+            lam, _, info, _ = oracle.steqr(td.astype(dt), te.astype(dt), False, **kw)
+            err = np.abs(lam[0].astype(np.float64) - tref).max() / V.tnorm1(td, te)[0]
+            _fail(out, info[0] == 0 and err <= V.tol_of(dt, n),
+                  "Toeplitz %d %s: %g" % (n, dt.__name__, err))
     return out
 
 

@@ -62,7 +62,8 @@ def test_version(st):
     (16, 1, 0, 16, 4), (17, 1, 0, 32, 8), (32, 1, 1, 32, 16), (32, 0, 1, 32, 1), (32, 0, 0, 32, 4), (16, 0, 0, 16, 2), (16, 0, 1, 16, 1),
     (33, 1, 1, 64, 4), (64, 1, 1, 64, 4), (64, 1, 0, 64, 16), (64, 0, 0, 64, 8),
     (40, 0, 1, 64, 8), (100, 1, 0, 128, 8), (100, 1, 1, 128, 32), (128, 0, 0, 128, 16),
-    (129, 1, 0, 256, 64), (256, 1, 1, 256, 64), (200, 0, 0, 256, 64), (256, 0, 1, 256, 64)])
+    (129, 1, 0, 256, 64), (256, 1, 1, 256, 64), (200, 0, 0, 256, 64), (256, 0, 1, 256, 64),
+    (257, 1, 0, 512, 64), (512, 1, 1, 512, 64), (300, 0, 0, 512, 64), (512, 0, 1, 512, 64)])
 def test_query_default_plan(st, n, jobz, dtype, N, P):
     q = st.steqr_query(n, 1000, jobz, dtype)
     assert q["padded_n"] == N and q["lanes_per_problem"] == P
@@ -72,11 +73,13 @@ def test_query_default_plan(st, n, jobz, dtype, N, P):
         # consumers per problem: 1 up to order 64; at 128 two (float, whole
         # rows) or four (double, half rows); at 256 eight (float, half rows:
         # one workgroup per problem) or sixteen (double, quarter rows: two
-        # workgroups per problem)
-        if N == 256:
+        # workgroups per problem); at 512 sixty-four (float, eighth rows:
+        # eight workgroups per problem) or 128 (double, sixteenth rows:
+        # sixteen workgroups per problem)
+        if N >= 256:
             assert q["waves_per_block"] == 9
-            want = 1000 * (1 if dtype == 0 else 2)
-            assert q["workgroups"] == want
+            gpp = {(256, 0): 1, (256, 1): 2, (512, 0): 8, (512, 1): 16}[(N, dtype)]
+            assert q["workgroups"] == 1000 * gpp
             return
         cpp = 1 if N <= 64 else (2 if dtype == 0 else 4)
         per_block = (q["waves_per_block"] - 1) // cpp
@@ -152,7 +155,7 @@ def test_query_band_storage(st):
     ((8, 8, 0, 8, 4, 10, 1, 0), -3),
     ((8, 8, 8, 0, 4, 10, 1, 0), -4),
     ((8, 8, 8, 8, -1, 10, 1, 0), -5),
-    ((8, 8, 8, 8, 257, 10, 1, 0), -5),
+    ((8, 8, 8, 8, 513, 10, 1, 0), -5),
     ((8, 8, 8, 8, 4, -1, 1, 0), -6),
     ((8, 8, 8, 8, 4, 10, 2, 0), -7),
     ((8, 8, 8, 8, 4, 10, 1, 5), -8),
@@ -268,7 +271,7 @@ def test_syev_argument_errors(st):
 @pytest.mark.parametrize("n,dtype,N,band", [(1, 0, 4, 1), (3, 1, 4, 1), (16, 0, 16, 1),
                                             (17, 1, 32, 1), (64, 0, 64, 1), (40, 1, 64, 2),
                                             (65, 0, 128, 2), (128, 1, 128, 2), (129, 0, 256, 2),
-                                            (256, 1, 256, 2)])
+                                            (256, 1, 256, 2), (257, 0, 512, 2), (512, 1, 512, 2)])
 def test_bisect_plans(st, n, dtype, N, band):
     q = st.steqr_query(n, 32768, 0, dtype, st.make_params(method=st.STEQR_METHOD_BISECT))
     L = min(N, 64)
@@ -316,6 +319,7 @@ def _case_lists():
     for dt in (np.float32, np.float64):
         for jobz in (True, False):
             out += [(dt, n, jobz, 0, 0, sc) for n in (129, 200, 256) for sc in (0, 1)]
+            out += [(dt, n, jobz, 0, 0, sc) for n in (257, 450, 512) for sc in (0, 1)]
         out += [(dt, 240, False, 16, 0, 0)]
     for dt in (np.float32, np.float64):
         for band in (1, 2):

@@ -1,7 +1,8 @@
-"""GPU parity at orders 65..128 (producer and consumer wavefronts with
-eigenvectors, two lanes per row of Q; producer wavefronts alone for values
-only) against the oracle on the same seeded inputs. Needs an MI355X; run
-with -m gpu."""
+"""GPU parity at orders 65..512 (producer and consumer wavefronts with
+eigenvectors, rows of Q split over lanes and, from order 256 in double and
+512 in float, over workgroups; producer wavefronts alone for values only)
+against the oracle on the same seeded inputs. Needs an MI355X; run with
+-m gpu."""
 import numpy as np
 import pytest
 
@@ -110,8 +111,8 @@ def test_big_values_shapes(dt, lanes):
 # ---------------------------------------------------------------- orders 129..256
 # Producer and consumer wavefronts at compiled order 256: one problem per
 # producer, rows of Q split over two (float) or four (double) lanes, double
-# with two workgroups sharing each problem's rows; values only with two
-# problems per producer wavefront.
+# with two workgroups sharing each problem's rows; values only with one
+# problem per producer wavefront (two or four selectable).
 
 @pytest.mark.parametrize("jobz", [True, False], ids=["V", "N"])
 @pytest.mark.parametrize("dt", [np.float32, np.float64], ids=["f32", "f64"])
@@ -157,6 +158,57 @@ def test_huge_schemes_shift_basis_and_lanes(dt):
     o = oracle.steqr(d, e, False, threads=8)
     assert check(d, e, g, o, False) == []
     # unsorted output and a sweep budget of zero
+    g = run_gpu(d, e, True, sort=False)
+    o = oracle.steqr(d, e, True, sort=False, threads=8)
+    assert check(d, e, (np.sort(g[0], 1), None, g[2]), (np.sort(o[0], 1), None, o[2]), False) == []
+    g = run_gpu(d, e, True, max_sweeps_per_n=-1)
+    assert np.all(g[2] > 0)
+
+
+# ---------------------------------------------------------------- orders 257..512
+# Compiled order 512: one problem per producer; rows of Q split over eight
+# (float) or sixteen (double) lanes, and over eight (float) or sixteen
+# (double) workgroups per problem, each with its own producer.
+
+@pytest.mark.parametrize("jobz", [True, False], ids=["V", "N"])
+@pytest.mark.parametrize("dt", [np.float32, np.float64], ids=["f32", "f64"])
+@pytest.mark.parametrize("n", [257, 300, 383, 511, 512])
+def test_n512_orders(n, dt, jobz):
+    print("n512 case", n, dt.__name__, jobz, flush=True)
+    d, e = W.random_batch(n, 13, dt, salt=700 + n)
+    g = run_gpu(d, e, jobz)
+    o = oracle.steqr(d, e, jobz, threads=8)
+    assert check(d, e, g, o, jobz) == []
+
+
+@pytest.mark.parametrize("kind", range(5), ids=W.EDGE_NAMES)
+@pytest.mark.parametrize("dt", [np.float32, np.float64], ids=["f32", "f64"])
+def test_n512_edge_items(kind, dt):
+    n = 512
+    print("n512 edge", W.EDGE_NAMES[kind], dt.__name__, flush=True)
+    d, e = W.edge_batch(kind, n, 6, dt)
+    for jobz in (True, False):
+        g = run_gpu(d, e, jobz)
+        o = oracle.steqr(d, e, jobz, threads=8)
+        assert check(d, e, g, o, jobz) == [], (W.EDGE_NAMES[kind], jobz)
+        if kind == W.EDGE_NAN:
+            assert np.all(g[2] > 0)
+
+
+@pytest.mark.parametrize("dt", [np.float32, np.float64], ids=["f32", "f64"])
+def test_n512_schemes_shift_basis_and_lanes(dt):
+    n = 450
+    d, e = W.random_batch(n, 6, dt, salt=710)
+    for scheme, shift in ((1, 0), (0, 1)):
+        print("n512 scheme/shift", dt.__name__, scheme, shift, flush=True)
+        for jobz in (True, False):
+            g = run_gpu(d, e, jobz, scheme=scheme, shift=shift)
+            o = oracle.steqr(d, e, jobz, threads=8, scheme=scheme, shift=shift)
+            assert check(d, e, g, o, jobz) == [], (scheme, shift, jobz)
+    Z = W.random_basis(n, 6, dt, salt=711)
+    g = run_gpu(d, e, True, Z=Z)
+    o = oracle.steqr(d, e, True, threads=8, Z=Z)
+    assert check_basis(d, e, Z, g, o) == []
     g = run_gpu(d, e, True, sort=False)
     o = oracle.steqr(d, e, True, sort=False, threads=8)
     assert check(d, e, (np.sort(g[0], 1), None, g[2]), (np.sort(o[0], 1), None, o[2]), False) == []

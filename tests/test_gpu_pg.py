@@ -26,7 +26,7 @@ def _gpu():
 SMALL = 1000 + 13
 
 
-@pytest.mark.parametrize("wname", list(W.WORKLOADS))
+@pytest.mark.parametrize("wname", W.SMALL_BATCH_WORKLOADS)
 @pytest.mark.parametrize("jobz", [True, False], ids=["V", "N"])
 def test_pg_workload_small_batch(wname, jobz):
     w = W.WORKLOADS[wname]

@@ -26,7 +26,7 @@ SMALL = 1000 + 13
 
 
 @pytest.mark.parametrize("scheme", [0, 1], ids=["exp", "pg"])
-@pytest.mark.parametrize("wname", list(W.WORKLOADS))
+@pytest.mark.parametrize("wname", W.SMALL_BATCH_WORKLOADS)
 @pytest.mark.parametrize("jobz", [True, False], ids=["V", "N"])
 def test_closed_shift_workload_small_batch(wname, jobz, scheme):
     w = W.WORKLOADS[wname]

@@ -200,7 +200,7 @@ def test_workload_items_vs_sturm_and_invariants(oracle_mod, wname):
     Sturm bisection (n <= 32 here), residual, orthogonality, trace and
     Frobenius invariants, for each item that converged."""
     w = W.WORKLOADS[wname]
-    nb = 64 if w.n <= 32 else 16
+    nb = 64 if w.n <= 32 else (16 if w.n <= 256 else 4)
     d, e = W.make_batch(w, nb)
     lam, Q, info, _ = oracle_mod.steqr(d, e, True)
     ok = np.isfinite(d).all(1) & np.isfinite(e).all(1)

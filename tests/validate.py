@@ -1,7 +1,7 @@
 """Validators shared by the oracle pins and the GPU parity tests.
 
 Test infrastructure: plain numpy, independent of both the oracle and the
-HIP path. Tolerances follow the spec acceptance rule: sorted
+HIP path. Acceptance rule for floating point: sorted
 eigenvalues within 16*n*eps*||T||, residual ||TQ - Q Lambda|| / ||T|| and
 orthogonality ||Q^T Q - I|| within 16*n*eps, with eps the machine epsilon
 of the item's precision (2^-23 for float32, 2^-52 for float64) and ||.||
