@@ -54,6 +54,8 @@ CASES = {
     "c4_f64_n32:N": (5, "f64", 32, 1, 1, 0),
     "w_f32_n256:V": (6, "f32", 256, 64, 3, 8),
     "w_f64_n256:V": (7, "f64", 256, 64, 3, 8),
+    "w_f32_n512:V": (8, "f32", 512, 64, 3, 8),
+    "w_f64_n512:V": (9, "f64", 512, 64, 3, 8),
 }
 LATENCY = ["double FMA (v_fma_f64)", "double reciprocal square root (v_rsq_f64)",
            "refined double reciprocal square root (solver's rsq_refined)",

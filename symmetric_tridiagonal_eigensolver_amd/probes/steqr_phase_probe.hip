@@ -20,6 +20,10 @@ using LaunchFn = steqr::LaunchFn;
 //        6 producer-consumer <float, 256, 8 consumers, 64 lanes>
 //        7 producer-consumer <double, 256, 8 consumers, 64 lanes> (two
 //          workgroups per problem)
+//        8 producer-consumer <float, 512, 8 consumers, 64 lanes> (eight
+//          workgroups per problem)
+//        9 producer-consumer <double, 512, 8 consumers, 64 lanes> (sixteen
+//          workgroups per problem)
 LaunchFn kernel_of(int which) {
     switch (which) {
         case 0: return &steqr::launch_chunk<float, 16, 4, true, false>;
@@ -30,6 +34,8 @@ LaunchFn kernel_of(int which) {
         case 5: return &steqr::launch_chunk<double, 32, 1, false, false>;
         case 6: return &steqr::launch_pc<float, 256, 8, 64, false>;
         case 7: return &steqr::launch_pc<double, 256, 8, 64, false>;
+        case 8: return &steqr::launch_pc<float, 512, 8, 64, false>;
+        case 9: return &steqr::launch_pc<double, 512, 8, 64, false>;
         default: return nullptr;
     }
 }
