@@ -54,7 +54,7 @@ def test_bisect_workload_small_batch(wname):
 
 
 @pytest.mark.parametrize("wname", ["c2_f32_n16", "c4_f32_n32", "c4_f64_n32", "c5_f64_n64",
-                                   "w_f32_n128", "w_f64_n128"])
+                                   "w_f32_n128", "w_f64_n128", "w_f32_n256", "w_f64_n512"])
 def test_bisect_full_batch_sampled(wname):
     """The full batch in the benchmark's launch; the oracle on every 64th item."""
     w = W.WORKLOADS[wname]
@@ -68,7 +68,7 @@ def test_bisect_full_batch_sampled(wname):
 
 @pytest.mark.parametrize("dt", [np.float32, np.float64], ids=["f32", "f64"])
 def test_bisect_every_order(dt):
-    for n in list(range(1, 65)) + [65, 70, 96, 127, 128]:
+    for n in list(range(1, 65)) + [65, 70, 96, 127, 128, 129, 200, 256, 257, 300, 511, 512]:
         print("bisect order", dt.__name__, n, flush=True)
         d, e = W.random_batch(n, 67, dt, salt=400 + n)
         g = run_bisect(d, e)
@@ -78,7 +78,7 @@ def test_bisect_every_order(dt):
 
 @pytest.mark.parametrize("kind", range(5), ids=W.EDGE_NAMES)
 @pytest.mark.parametrize("dt", [np.float32, np.float64], ids=["f32", "f64"])
-@pytest.mark.parametrize("n", [1, 2, 3, 16, 32, 64, 100, 128])
+@pytest.mark.parametrize("n", [1, 2, 3, 16, 32, 64, 100, 128, 256, 512])
 def test_bisect_edge_items(kind, dt, n):
     print("bisect edge", W.EDGE_NAMES[kind], dt.__name__, n, flush=True)
     d, e = W.edge_batch(kind, n, 130, dt)
@@ -90,7 +90,7 @@ def test_bisect_edge_items(kind, dt, n):
 
 
 @pytest.mark.parametrize("dt", [np.float32, np.float64], ids=["f32", "f64"])
-@pytest.mark.parametrize("n", [5, 16, 64, 128])
+@pytest.mark.parametrize("n", [5, 16, 64, 128, 256, 512])
 def test_bisect_power_of_two_scaling_is_exact(dt, n):
     d, e = W.random_batch(n, 200, dt, salt=76)
     base = run_bisect(d, e)[0]
