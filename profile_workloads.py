@@ -3,8 +3,9 @@
 Per case (workload:V or workload:N), on an MI355X from the repository root:
   1. bench.py at the default launch (HIP-event mean over the timed region,
      roofline with the counter record's figures, CPU oracle baseline);
-  2. rocprofv3 --kernel-trace --stats of a short bench.py run, from which the
-     solver kernel's dispatch statistics are taken.
+  2. rocprofv3 --kernel-trace --stats of the same bench.py command without
+     its CPU, saturation and named-lanes legs, from which the solver
+     kernel's dispatch statistics are taken.
 Each case's results go to OUT/<workload>_<V|N>.json; `--summarise` turns the
 JSON files of a directory into profiles/steqr_all_workloads_trace.md and the
 headline's profiles/steqr_chunk_f32_n16_V_headline.md:
@@ -42,8 +43,9 @@ def bench_args(wname: str, j: str):
 
 
 def trace_args(wname: str, j: str):
-    return ["--workload", wname, "--jobz", j, "--steps", "20", "--warmup", "2", "--no-cpu",
-            "--no-named", "--no-saturation"]
+    # the bench line's own steps and warm-up, without the legs that launch
+    # other shapes (twice the batch, other lanes) under the same kernel name
+    return bench_args(wname, j) + ["--no-cpu", "--no-named", "--no-saturation"]
 
 
 def run_bench(args, timeout: int) -> dict:
@@ -130,14 +132,14 @@ def summarise(src: str) -> None:
         "# Kernel traces and bench lines of every workload (one MI355X)", "",
         "Per case (workload and jobz), bench.py at the default launch (HIP-event mean over the "
         "timed region, seeded synthetic inputs, recipes in workloads.py) and a rocprofv3 "
-        "kernel-trace run of a short bench.py invocation, both from:", "",
+        "kernel-trace run of the same bench.py command, both from:", "",
         "    python3 profile_workloads.py --out OUT " + " ".join(order),
         "    python3 profile_workloads.py --summarise OUT", "",
         "which runs, per case:", "",
         "    python3 bench.py --workload WL --jobz J --steps S --warmup 5   (S = 5 at order 512, 20 for c5 and the other w_*, else 200)",
         "    rocprofv3 --kernel-trace --stats -d OUT -o run --output-format csv -- python3 bench.py --workload WL "
-        "--jobz J --steps 20 --warmup 2 --no-cpu --no-named --no-saturation", "",
-        "The trace average covers the warm-up, timed and spread-round launches of the short run. "
+        "--jobz J --steps S --warmup 5 --no-cpu --no-named --no-saturation", "",
+        "The trace average covers the warm-up, timed and spread-round launches of that run. "
         "`alg.` is the algorithmic fraction of the dtype's vector peak (157.3 TFLOP/s FP32 with "
         "packed FMA, 78.6 FP64); `exec.` the executed FLOP rate's fraction "
         "(SQ_INSTS_VALU_FLOPS counter); `busy` VALU instructions x 4 cycles over the SIMDs' "
