@@ -64,10 +64,17 @@ LATENCY_ITERS = 256  # x 16 operations
 SLOTS = 9  # per-wavefront slots the profiling build stores
 
 
+def probe_build_command():
+    """hipcc command of the profiling library (the library's own flags)."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("_steqr_build", os.path.join(PKG, "build.py"))
+    B = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(B)
+    return [B.HIPCC, *B.HIP_FLAGS, "-shared", "-o", PROBE_LIB, PROBE_SRC]
+
+
 def build_probe() -> str:
-    from symmetric_tridiagonal_eigensolver_amd import build as B
-    cmd = [B.HIPCC, *B.HIP_FLAGS, "-shared", "-o", PROBE_LIB, PROBE_SRC]
-    r = subprocess.run(cmd, capture_output=True, text=True)
+    r = subprocess.run(probe_build_command(), capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("probe build failed:\n%s" % r.stderr)
     return PROBE_LIB
