@@ -36,16 +36,47 @@ CASES = ["c1_f32_n4:V", "c2_f32_n8:V", "c2_f32_n8:N", "c2_f32_n16:V", "c2_f32_n1
          "w_f64_n256:N", "w_f32_n512:V", "w_f32_n512:N", "w_f64_n512:V", "w_f64_n512:N"]
 HEADLINE = "c2_f32_n16:V"
 
+# The NEXT rows' option sets: case "workload:jobz:mode" with mode bt
+# (back-transformation), syev (fused dense syev on a dense workload) or
+# bisect (values-only bisection); each set has a summary of its own.
+MODES = {"bt": ["--back-transform"], "syev": ["--op", "syev"], "bisect": ["--method", "bisect"]}
+EXTRA_SETS = {
+    "bt": ("steqr_back_transform.md", "Back-transformation (Q holds a basis on entry)",
+           ["c2_f32_n16:V:bt", "c3_f64_n16:V:bt", "c4_f32_n32:V:bt", "c4_f64_n32:V:bt",
+            "c5_f64_n64:V:bt", "w_f64_n128:V:bt"]),
+    "syev": ("syev_chunk_dense_workloads.md",
+             "Fused dense syev (reduction + tridiagonal solve + back-transformation)",
+             ["s_f32_n8:V:syev", "s_f32_n8:N:syev", "s_f32_n16:V:syev", "s_f32_n16:N:syev",
+              "s_f32_n32:V:syev", "s_f32_n32:N:syev", "s_f64_n16:V:syev", "s_f64_n16:N:syev",
+              "s_f64_n32:N:syev"]),
+    "bisect": ("steqr_bisect_values.md", "Values-only bisection (steqr_bisect_kernel)",
+               ["c2_f32_n8:N:bisect", "c2_f32_n16:N:bisect", "c4_f32_n32:N:bisect",
+                "c3_f64_n16:N:bisect", "c4_f64_n32:N:bisect", "c5_f64_n64:N:bisect",
+                "w_f32_n128:N:bisect", "w_f64_n128:N:bisect", "w_f32_n256:N:bisect",
+                "w_f64_n256:N:bisect", "w_f32_n512:N:bisect", "w_f64_n512:N:bisect"]),
+}
 
-def bench_args(wname: str, j: str):
+
+def split_case(case: str):
+    parts = case.split(":")
+    return parts[0], parts[1], (parts[2] if len(parts) > 2 else "")
+
+
+def case_file(case: str) -> str:
+    wname, j, mode = split_case(case)
+    return "%s_%s%s.json" % (wname, j, "_" + mode if mode else "")
+
+
+def bench_args(wname: str, j: str, mode: str = ""):
     steps = ("5" if wname.endswith("n512") else "20") if wname.startswith(("w_", "c5_")) else "200"
-    return ["--workload", wname, "--jobz", j, "--steps", steps, "--warmup", "5"]
+    return (["--workload", wname, "--jobz", j, "--steps", steps, "--warmup", "5"]
+            + MODES.get(mode, []))
 
 
-def trace_args(wname: str, j: str):
+def trace_args(wname: str, j: str, mode: str = ""):
     # the bench line's own steps and warm-up, without the legs that launch
     # other shapes (twice the batch, other lanes) under the same kernel name
-    return bench_args(wname, j) + ["--no-cpu", "--no-named", "--no-saturation"]
+    return bench_args(wname, j, mode) + ["--no-cpu", "--no-named", "--no-saturation"]
 
 
 def run_bench(args, timeout: int) -> dict:
@@ -99,16 +130,16 @@ def solver_row(rows, family: str):
 
 
 def collect(case: str, out: str, timeout: int) -> str:
-    wname, j = case.split(":")
+    wname, j, mode = split_case(case)
     t = time.time()
-    line = run_bench(bench_args(wname, j), timeout)
+    line = run_bench(bench_args(wname, j, mode), timeout)
     print("  %s: bench.py done (%.0fs)" % (case, time.time() - t), flush=True)
-    rows, tcmd = run_trace(trace_args(wname, j), timeout)
+    rows, tcmd = run_trace(trace_args(wname, j, mode), timeout)
     fam = line["roofline"]["kernel"].split("<")[0][len("steqr_"):-len("_kernel")]
     rec = {"case": case, "bench": line, "bench_command": "python3 bench.py " +
-           " ".join(bench_args(wname, j)), "trace": rows, "trace_command": tcmd,
+           " ".join(bench_args(wname, j, mode)), "trace": rows, "trace_command": tcmd,
            "solver": solver_row(rows, fam)}
-    path = os.path.join(out, "%s_%s.json" % (wname, j))
+    path = os.path.join(out, case_file(case))
     with open(path, "w") as f:
         json.dump(rec, f, indent=1)
     print("  %s: %.1f us (trace %.1f us), %.0fs" % (case, line["ms_per_step"] * 1e3,
@@ -128,6 +159,9 @@ def summarise(src: str) -> None:
         if "bench" in r:
             recs[r["case"]] = r
     order = [c for c in CASES if c in recs]
+    if not order and HEADLINE not in recs and not any(
+            c in recs for _, (_, _, cs) in EXTRA_SETS.items() for c in cs):
+        raise SystemExit("no records in %s" % src)
     lines = [
         "# Kernel traces and bench lines of every workload (one MI355X)", "",
         "Per case (workload and jobz), bench.py at the default launch (HIP-event mean over the "
@@ -163,12 +197,53 @@ def summarise(src: str) -> None:
             b["ms_per_step"] * 1e3, b["value"], fmt(rf["frac"], "%.4f"), fmt(ex, "%.4f"),
             fmt(rf.get("valu_busy"), "%.2f"), fmt(rf.get("divergence"), "%.3f"),
             fmt(hb, "%.3f"), fmt(cpu, "%.3f")))
-    out = os.path.join(ROOT, "profiles", "steqr_all_workloads_trace.md")
+    if order:
+        out = os.path.join(ROOT, "profiles", "steqr_all_workloads_trace.md")
+        with open(out, "w") as f:
+            f.write("\n".join(lines) + "\n")
+        print("wrote", out)
+    if HEADLINE in recs:
+        write_headline(recs[HEADLINE])
+    for mode, (fname, title, cases) in EXTRA_SETS.items():
+        have = [c for c in cases if c in recs]
+        if have:
+            write_extra(mode, fname, title, have, recs)
+
+
+def write_extra(mode: str, fname: str, title: str, cases, recs) -> None:
+    """Summary of one option set, with the plain (QR, no basis) time of the
+    same workload from the same directory for comparison where it exists."""
+    lines = ["# %s, one MI355X" % title, "",
+             "Per case, bench.py and a rocprofv3 kernel trace of the same command, from:", "",
+             "    python3 profile_workloads.py --out OUT " + " ".join(cases),
+             "    python3 profile_workloads.py --summarise OUT", "",
+             "which runs, per case:", "",
+             "    python3 bench.py --workload WL --jobz J --steps S --warmup 5 %s" % " ".join(MODES[mode]),
+             "    rocprofv3 --kernel-trace --stats -d OUT -o run --output-format csv -- python3 bench.py "
+             "--workload WL --jobz J --steps S --warmup 5 %s --no-cpu --no-named --no-saturation"
+             % " ".join(MODES[mode]), "",
+             "`alg.`: algorithmic fraction of the dtype's vector peak (157.3 TFLOP/s FP32 with packed "
+             "FMA, 78.6 FP64); `plain`: the default solve of the same workload (QR, no basis) "
+             "from the records summarised in steqr_all_workloads_trace.md.", "",
+             "| case | kernel | trace avg (us) | bench.py (us) | matrices/s | alg. | plain (us) "
+             "| ratio | CPU oracle us/matrix |", "|---|---|---:|---:|---:|---:|---:|---:|---:|"]
+    for c in cases:
+        r = recs[c]
+        b, s = r["bench"], r["solver"]
+        rf = b.get("roofline") or {}
+        wname, j, _ = split_case(c)
+        plain = recs.get("%s:%s" % (wname, j))
+        pt = plain["bench"]["ms_per_step"] * 1e3 if plain else None
+        t = b["ms_per_step"] * 1e3
+        cpu = (b.get("cpu_baseline") or {}).get("us_per_matrix")
+        lines.append("| %s %s | %s | %.2f | %.2f | %.3g | %s | %s | %s | %s |" % (
+            wname, j, s["name"].split("(")[0].replace("void ", ""), s["avg_us"], t, b["value"],
+            fmt(rf.get("frac"), "%.4f"), fmt(pt, "%.2f"), fmt(t / pt if pt else None, "%.3f"),
+            fmt(cpu, "%.3f")))
+    out = os.path.join(ROOT, "profiles", fname)
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("wrote", out)
-    if HEADLINE in recs:
-        write_headline(recs[HEADLINE])
 
 
 def write_headline(r: dict) -> None:
