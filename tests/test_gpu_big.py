@@ -214,3 +214,17 @@ def test_n512_schemes_shift_basis_and_lanes(dt):
     assert check(d, e, (np.sort(g[0], 1), None, g[2]), (np.sort(o[0], 1), None, o[2]), False) == []
     g = run_gpu(d, e, True, max_sweeps_per_n=-1)
     assert np.all(g[2] > 0)
+
+
+@pytest.mark.parametrize("jobz", [True, False], ids=["V", "N"])
+@pytest.mark.parametrize("dt", [np.float32, np.float64], ids=["f32", "f64"])
+def test_orders_65_to_512_sampled(dt, jobz):
+    """Every 17th order from 65 to 512 (each compiled order with a range of
+    padding, ragged row slices of Q and, from 257, problems shared by several
+    workgroups), a few items each."""
+    for n in range(65, 513, 17):
+        print("order sweep", dt.__name__, jobz, n, flush=True)
+        d, e = W.random_batch(n, 5, dt, salt=900 + n)
+        g = run_gpu(d, e, jobz)
+        o = oracle.steqr(d, e, jobz, threads=8)
+        assert check(d, e, g, o, jobz) == [], "n=%d" % n
