@@ -9,7 +9,7 @@ shape the library's default plan gives the workload, checks that its
 results equal the library's bit for bit, and writes a summary per case:
 
     python3 profile_phases.py --build-only          # on the build machine
-    python3 profile_phases.py --out gpurun_out/profiles   # on an MI355X
+    python3 profile_phases.py --out OUT                   # on an MI355X
 
 Slots (cycles of the shader clock read with s_memtime, added up between
 consecutive marks, per wavefront):

@@ -10,8 +10,8 @@ Each case's results go to OUT/<workload>_<V|N>.json; `--summarise` turns the
 JSON files of a directory into profiles/steqr_all_workloads_trace.md and the
 headline's profiles/steqr_chunk_f32_n16_V_headline.md:
 
-    python3 profile_workloads.py --out gpurun_out/wl c2_f32_n16:V c5_f64_n64:V ...
-    python3 profile_workloads.py --summarise gpurun_out/wl
+    python3 profile_workloads.py --out OUT c2_f32_n16:V c5_f64_n64:V ...
+    python3 profile_workloads.py --summarise OUT
 """
 from __future__ import annotations
 
