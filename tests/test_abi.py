@@ -343,3 +343,17 @@ def test_syev_test_cases_have_built_kernels(st):
     for dt, n, lanes, jobz in SY.CASES:
         code = st.STEQR_F32 if dt == np.float32 else st.STEQR_F64
         st.syev_query(n, 777, int(jobz), code, st.make_params(lanes_per_problem=lanes))
+
+
+def test_c_caller_compiles_against_the_header(tmp_path):
+    """include/steqr.h is valid C: the plain C caller of the ABI compiles and
+    links against libsteqr.so (it runs in tests/test_gpu_c_abi.py)."""
+    import shutil
+    import subprocess
+    import __graft_entry__ as g
+    if shutil.which("gcc") is None:
+        pytest.skip("no gcc")
+    out = str(tmp_path / "steqr_c_check")
+    r = subprocess.run(g.c_check_command(out), capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    assert os.path.exists(out)
