@@ -286,8 +286,10 @@ def write_headline(r: dict) -> None:
              + fl["SQ_INSTS_VALU_TRANS_F32"])
     other = fl["SQ_INSTS_VALU"] - arith - fl["SQ_INSTS_VALU_INT32"]
     lines += ["", "Derived:",
-              "* divergence = VALU instructions, random / replicated = %.3f the lockstep ideal;"
-              % (v["SQ_INSTS_VALU"] / vr["SQ_INSTS_VALU"]),
+              "* divergence = VALU instructions, random / replicated = %.3f the lockstep ideal "
+              "(VALU + SALU: %.3f);" % (v["SQ_INSTS_VALU"] / vr["SQ_INSTS_VALU"],
+                                       (v["SQ_INSTS_VALU"] + v["SQ_INSTS_SALU"])
+                                       / (vr["SQ_INSTS_VALU"] + vr["SQ_INSTS_SALU"])),
               "* clock from SQ_BUSY_CYCLES: %.2f GHz;" % clk,
               "* VALU busy = VALU instructions x 4 cycles / (1,024 SIMDs x the dispatch's cycles) "
               "= %.0f%%;" % (100 * rf.get("valu_busy", 0)),
