@@ -125,19 +125,27 @@ def kernel_family(plan: dict, jobz: bool, method: int = 0) -> str:
     return "chunkl" if plan["band_storage"] == 2 else "chunk"
 
 
-def kernel_label(plan: dict, jobz: bool, dtype: str, family: str) -> str:
-    """Name of the kernel instantiation a launch plan runs."""
-    return "steqr_%s_kernel<%s, N=%d, P=%d, %s>" % (
+def kernel_label(plan: dict, jobz: bool, dtype: str, family: str, scheme: int = 0) -> str:
+    """Name of the kernel instantiation a launch plan runs (", PG" for the
+    Parlett-Gray form of the step)."""
+    return "steqr_%s_kernel<%s, N=%d, P=%d, %s%s>" % (
         family, "float" if dtype == "f32" else "double", plan["padded_n"],
-        plan["lanes_per_problem"], "V" if jobz else "N")
+        plan["lanes_per_problem"], "V" if jobz else "N", ", PG" if scheme else "")
 
 
-def counters_from_profiles(wname: str, jobz: bool, family: str, kernel: str):
+def record_suffix(bt: bool, scheme: int, method: int) -> str:
+    """Counter-record name suffix of a launch option set: back-transformation,
+    the PG step or bisection (the default solve has none)."""
+    return "_bt" if bt else ("_pg" if scheme else ("_bisect" if method else ""))
+
+
+def counters_from_profiles(wname: str, jobz: bool, family: str, kernel: str, suffix: str = ""):
     """Per-launch counter record (HBM bytes, executed VALU instructions and
     FLOPs, replicated-batch instructions) committed under profiles/, or None
     when absent, taken on another kernel instantiation or on other kernel
     sources."""
-    p = os.path.join(ROOT, "profiles", "counters_%s_%s.json" % (wname, "V" if jobz else "N"))
+    p = os.path.join(ROOT, "profiles", "counters_%s_%s%s.json" % (wname, "V" if jobz else "N",
+                                                                   suffix))
     if not os.path.exists(p):
         return None
     try:
@@ -406,11 +414,12 @@ def main() -> int:
     peak = PEAK_TFLOPS[dtype]
     roof = None
     family = kernel_family(plan, jobz, method)
-    kname = kernel_label(plan, jobz, dtype, family)
+    kname = kernel_label(plan, jobz, dtype, family, scheme)
     if flops is not None:
         ach = flops / sec / 1e12
-        ctr = (None if (args.replicate or scheme or bt or method)
-               else counters_from_profiles(w.name, jobz, family, kname))
+        ctr = (None if args.replicate
+               else counters_from_profiles(w.name, jobz, family, kname,
+                                           record_suffix(bt, scheme, method)))
         roof = {"kernel": kname,
                 "bound": "alu", "achieved": ach, "peak": peak, "unit": "TFLOP/s",
                 "frac": ach / peak,

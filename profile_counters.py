@@ -86,13 +86,19 @@ def run_pass(counters, bench_args, kernel_key: str, timeout: int):
     return vals, us, len(per), " ".join(cmd[4:]).replace(out, "OUT")
 
 
-def kernel_family(st, wname: str, jobz: bool):
+# launch option sets with records of their own (case "workload:J:mode")
+MODE_ARGS = {"bt": ["--back-transform"], "pg": ["--scheme", "pg"], "bisect": ["--method", "bisect"]}
+
+
+def kernel_family(st, wname: str, jobz: bool, mode: str = ""):
     import workloads as W
     w = W.WORKLOADS[wname]
     import bench
-    plan = st.steqr_query(w.n, w.batch, int(jobz), 0 if w.dtype == "f32" else 1)
-    fam = bench.kernel_family(plan, jobz)
-    return fam, bench.kernel_label(plan, jobz, w.dtype, fam), w
+    scheme, method = int(mode == "pg"), int(mode == "bisect")
+    plan = st.steqr_query(w.n, w.batch, int(jobz), 0 if w.dtype == "f32" else 1,
+                          st.make_params(update_scheme=scheme, method=method))
+    fam = bench.kernel_family(plan, jobz, method)
+    return fam, bench.kernel_label(plan, jobz, w.dtype, fam, scheme), w
 
 
 def calibrate(timeout: int) -> dict:
@@ -109,13 +115,13 @@ def calibrate(timeout: int) -> dict:
             "commands": [c1, c2]}
 
 
-def collect(wname: str, jobz: bool, cal: dict, timeout: int) -> dict:
+def collect(wname: str, jobz: bool, cal: dict, timeout: int, mode: str = "") -> dict:
     import bench
     import symmetric_tridiagonal_eigensolver_amd as st
-    fam, kname, w = kernel_family(st, wname, jobz)
+    fam, kname, w = kernel_family(st, wname, jobz, mode)
     key = "steqr_%s_kernel" % fam
     base = ["--workload", wname, "--jobz", "V" if jobz else "N", "--steps", "3", "--warmup", "1",
-            "--no-cpu", "--no-named", "--no-saturation"]
+            "--no-cpu", "--no-named", "--no-saturation"] + MODE_ARGS.get(mode, [])
     raw, cmds = {}, []
     for tag, ctrs, extra in (("fetch", ["FETCH_SIZE"], []), ("write", ["WRITE_SIZE"], []),
                              ("valu", VALU_GROUP, []), ("valu_replicated", VALU_GROUP, ["--replicate"]),
@@ -132,12 +138,12 @@ def collect(wname: str, jobz: bool, cal: dict, timeout: int) -> dict:
     fl = raw["flops"]
     fc = "SQ_INSTS_VALU_FLOPS_FP%s" % ("32" if w.dtype == "f32" else "64")
     return {
-        "workload": wname, "jobz": "V" if jobz else "N", "kernel": kname,
+        "workload": wname, "jobz": "V" if jobz else "N", "mode": mode, "kernel": kname,
         "kernel_source_hash": bench.kernel_source_hash(fam),
         "fetch_bytes_per_launch": fetch, "write_bytes_per_launch": write,
         "hbm_bytes_per_launch": fetch + write,
         "algorithmic_bytes_per_launch": bench.bytes_per_matrix(w.n, 4 if w.dtype == "f32" else 8,
-                                                               jobz) * w.batch,
+                                                               jobz, mode == "bt") * w.batch,
         "calibration": {k: cal[k] for k in ("fetch_factor", "write_factor", "reference")},
         "valu_insts_per_launch": raw["valu"]["SQ_INSTS_VALU"],
         "salu_insts_per_launch": raw["valu"]["SQ_INSTS_SALU"],
@@ -153,7 +159,8 @@ def collect(wname: str, jobz: bool, cal: dict, timeout: int) -> dict:
 
 def main() -> int:
     ap = argparse.ArgumentParser()
-    ap.add_argument("cases", nargs="+", help="workload:V or workload:N")
+    ap.add_argument("cases", nargs="+",
+                    help="workload:V or workload:N, optionally :bt, :pg or :bisect")
     ap.add_argument("--calibrate", action="store_true",
                     help="measure the copy / fill scale factors (else reuse the headline record's)")
     ap.add_argument("--timeout", type=int, default=120, help="seconds per rocprofv3 pass")
@@ -168,11 +175,14 @@ def main() -> int:
     else:
         ref = json.load(open(os.path.join(ROOT, "profiles", "counters_c2_f32_n16_V.json")))
         cal = dict(ref["calibration"])
+    import bench
     for case in args.cases:
-        wname, j = case.split(":")
-        rec = collect(wname, j == "V", cal, args.timeout)
+        parts = case.split(":")
+        wname, j, mode = parts[0], parts[1], (parts[2] if len(parts) > 2 else "")
+        rec = collect(wname, j == "V", cal, args.timeout, mode)
         os.makedirs(args.out, exist_ok=True)
-        path = os.path.join(args.out, "counters_%s_%s.json" % (wname, j))
+        suffix = bench.record_suffix(mode == "bt", int(mode == "pg"), int(mode == "bisect"))
+        path = os.path.join(args.out, "counters_%s_%s%s.json" % (wname, j, suffix))
         with open(path, "w") as f:
             json.dump(rec, f, indent=1)
         print("wrote %s: VALU %.3g, divergence %.3f, HBM %.4g B (algorithmic %.4g)" % (

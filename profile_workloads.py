@@ -39,7 +39,8 @@ HEADLINE = "c2_f32_n16:V"
 # The NEXT rows' option sets: case "workload:jobz:mode" with mode bt
 # (back-transformation), syev (fused dense syev on a dense workload) or
 # bisect (values-only bisection); each set has a summary of its own.
-MODES = {"bt": ["--back-transform"], "syev": ["--op", "syev"], "bisect": ["--method", "bisect"]}
+MODES = {"bt": ["--back-transform"], "syev": ["--op", "syev"], "bisect": ["--method", "bisect"],
+         "pg": ["--scheme", "pg"]}
 EXTRA_SETS = {
     "bt": ("steqr_back_transform.md", "Back-transformation (Q holds a basis on entry)",
            ["c2_f32_n16:V:bt", "c3_f64_n16:V:bt", "c4_f32_n32:V:bt", "c4_f64_n32:V:bt",
@@ -49,6 +50,8 @@ EXTRA_SETS = {
              ["s_f32_n8:V:syev", "s_f32_n8:N:syev", "s_f32_n16:V:syev", "s_f32_n16:N:syev",
               "s_f32_n32:V:syev", "s_f32_n32:N:syev", "s_f64_n16:V:syev", "s_f64_n16:N:syev",
               "s_f64_n32:N:syev"]),
+    "pg": ("steqr_pg_step.md", "The Parlett-Gray form of the chase step",
+           ["c2_f32_n16:V:pg", "c3_f64_n16:V:pg", "c4_f64_n32:V:pg", "c5_f64_n64:V:pg"]),
     "bisect": ("steqr_bisect_values.md", "Values-only bisection (steqr_bisect_kernel)",
                ["c2_f32_n8:N:bisect", "c2_f32_n16:N:bisect", "c4_f32_n32:N:bisect",
                 "c3_f64_n16:N:bisect", "c4_f64_n32:N:bisect", "c5_f64_n64:N:bisect",
@@ -223,10 +226,14 @@ def write_extra(mode: str, fname: str, title: str, cases, recs) -> None:
              "--workload WL --jobz J --steps S --warmup 5 %s --no-cpu --no-named --no-saturation"
              % " ".join(MODES[mode]), "",
              "`alg.`: algorithmic fraction of the dtype's vector peak (157.3 TFLOP/s FP32 with packed "
-             "FMA, 78.6 FP64); `plain`: the default solve of the same workload (QR, no basis) "
-             "from the records summarised in steqr_all_workloads_trace.md.", "",
-             "| case | kernel | trace avg (us) | bench.py (us) | matrices/s | alg. | plain (us) "
-             "| ratio | CPU oracle us/matrix |", "|---|---|---:|---:|---:|---:|---:|---:|---:|"]
+             "FMA, 78.6 FP64); `exec.`, `busy`, `div.`, `HBM`: executed fraction, VALU busy, "
+             "divergence and measured over algorithmic HBM bytes from the option set's counter "
+             "record (profiles/counters_<workload>_<jobz>_<set>.json, where one was taken); "
+             "`plain`: the default solve of the same workload (EXP step, QR, no basis) from the "
+             "records summarised in steqr_all_workloads_trace.md.", "",
+             "| case | kernel | trace avg (us) | bench.py (us) | matrices/s | alg. | exec. | busy "
+             "| div. | HBM | plain (us) | ratio | CPU oracle us/matrix |",
+             "|---|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|"]
     for c in cases:
         r = recs[c]
         b, s = r["bench"], r["solver"]
@@ -236,10 +243,14 @@ def write_extra(mode: str, fname: str, title: str, cases, recs) -> None:
         pt = plain["bench"]["ms_per_step"] * 1e3 if plain else None
         t = b["ms_per_step"] * 1e3
         cpu = (b.get("cpu_baseline") or {}).get("us_per_matrix")
-        lines.append("| %s %s | %s | %.2f | %.2f | %.3g | %s | %s | %s | %s |" % (
+        ex = (rf.get("executed") or {}).get("frac")
+        hb = (rf["traffic"] / b["hbm"]["algorithmic_bytes_per_launch"]
+              if rf.get("traffic") else None)
+        lines.append("| %s %s | %s | %.2f | %.2f | %.3g | %s | %s | %s | %s | %s | %s | %s | %s |" % (
             wname, j, s["name"].split("(")[0].replace("void ", ""), s["avg_us"], t, b["value"],
-            fmt(rf.get("frac"), "%.4f"), fmt(pt, "%.2f"), fmt(t / pt if pt else None, "%.3f"),
-            fmt(cpu, "%.3f")))
+            fmt(rf.get("frac"), "%.4f"), fmt(ex, "%.4f"), fmt(rf.get("valu_busy"), "%.2f"),
+            fmt(rf.get("divergence"), "%.3f"), fmt(hb, "%.3f"), fmt(pt, "%.2f"),
+            fmt(t / pt if pt else None, "%.3f"), fmt(cpu, "%.3f")))
     out = os.path.join(ROOT, "profiles", fname)
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")

@@ -42,12 +42,17 @@ def test_counter_record_is_current(st, path):
     r = json.load(open(path))
     w = W.WORKLOADS[r["workload"]]
     jobz = r["jobz"] == "V"
-    plan = st.steqr_query(w.n, w.batch, int(jobz), st.STEQR_F32 if w.dtype == "f32" else st.STEQR_F64)
-    fam = bench.kernel_family(plan, jobz)
-    kname = bench.kernel_label(plan, jobz, w.dtype, fam)
+    mode = r.get("mode", "")
+    scheme, method = int(mode == "pg"), int(mode == "bisect")
+    plan = st.steqr_query(w.n, w.batch, int(jobz), st.STEQR_F32 if w.dtype == "f32" else st.STEQR_F64,
+                          st.make_params(update_scheme=scheme, method=method))
+    fam = bench.kernel_family(plan, jobz, method)
+    kname = bench.kernel_label(plan, jobz, w.dtype, fam, scheme)
+    suffix = bench.record_suffix(mode == "bt", scheme, method)
+    assert os.path.basename(path) == "counters_%s_%s%s.json" % (r["workload"], r["jobz"], suffix)
     assert r["kernel"] == kname
     assert r["kernel_source_hash"] == bench.kernel_source_hash(fam)
-    assert bench.counters_from_profiles(r["workload"], jobz, fam, kname) is not None
+    assert bench.counters_from_profiles(r["workload"], jobz, fam, kname, suffix) is not None
     # the HBM bytes are at least the algorithmic bytes (the calibrated
     # counters cannot read less than the data that must move)
     assert r["hbm_bytes_per_launch"] >= 0.95 * r["algorithmic_bytes_per_launch"]
