@@ -353,10 +353,16 @@ def main() -> int:
         lam2 = torch.empty_like(td2)
         Q2 = torch.empty((2 * nb, n, n), dtype=td.dtype, device=dev) if jobz else None
         info2 = torch.empty((2 * nb,), dtype=torch.int32, device=dev)
+        # the same kernel: the default lanes per problem of values-only
+        # launches depend on the batch, so fix the ones of the timed launch
+        prm2 = st.make_params(lanes_per_problem=plan["lanes_per_problem"],
+                              waves_per_block=args.waves,
+                              band_storage=plan["band_storage"] if method == 0 else 0,
+                              update_scheme=scheme, back_transform=bt, method=method)
 
         def step2():
             rc = st.steqr_batched_ex(td2, te2, lam2, Q2, n, 2 * nb, int(jobz),
-                                     st.dtype_code(td.dtype), stream, info2, prm)
+                                     st.dtype_code(td.dtype), stream, info2, prm2)
             if rc != 0:
                 raise st.SteqrError(rc, "steqr_batched_ex")
         step2()

@@ -36,7 +36,7 @@ int padded_order(int n, int dtype = -1, int jobz = -1) {
 // 33..512 P counts the producer lanes of the producer-consumer kernel (with
 // or without its consumers); P = 64 selects one problem per wavefront at
 // orders 33..64.
-int default_lanes(int dtype, int N, int jobz, int band) {
+int default_lanes(int dtype, int N, int jobz, int band, long batch) {
     // orders 256 and 512: one problem per producer wavefront (without
     // eigenvectors 1024 matrices of order 256 took 6.52 ms in float at 64
     // lanes, 6.79 at 32, 6.59 at 16; double 9.48, 9.65, 9.55)
@@ -63,8 +63,21 @@ int default_lanes(int dtype, int N, int jobz, int band) {
         if (band == 2) return dtype == STEQR_F32 ? 8 : 16;  // N == 32
         return 16;  // double, band in registers: not built (-10)
     }
-    // values only in float: the split deflation scan pays at 4 lanes for
-    // order 32 (-3% against 2) and 2 lanes beat 1 at order 16 (-2%)
+    // values only in float: at the batch of 32,768 the split deflation scan
+    // pays at 4 lanes for order 32 (-3% against 2) and 2 lanes beat 1 at
+    // order 16 (-2%). A larger batch fills the SIMDs with fewer lanes per
+    // problem, and then the fewer lanes (less repeated chase work) win:
+    // one lane from 1,024 wavefronts at order 16 and from 2,048 at order 32,
+    // two lanes from 2,048 at order 32 (order 16 at 65,536 / 131,072 /
+    // 262,144 matrices: 1.00 / 0.56 / 0.40 ns per matrix at one lane against
+    // 1.06 / 0.74 / 0.64 at two; order 32: 3.62 us at two lanes against 4.11
+    // at four on 65,536, 2.05 at one against 3.81 at four on 131,072)
+    if (dtype == STEQR_F32 && band == 1 && (N == 16 || N == 32)) {
+        const long fill = (N == 16 ? 1024L : 2048L) * 64;  // wavefronts x 64
+        if (batch >= fill) return 1;
+        if (N == 32 && 2 * batch >= fill) return 2;
+        return N == 32 ? 4 : 2;
+    }
     if (N == 32 && dtype == STEQR_F32) return 4;
     if (N == 16 && dtype == STEQR_F32) return 2;
     return 1;
@@ -179,7 +192,7 @@ int plan_launch(int n, int batch, int jobz, int dtype, const steqr_params* prm, 
         return 0;
     }
     if (band == 0 || (N >= 64 && band == 1)) band = default_band(dtype, N, jobz);
-    if (P == 0) P = default_lanes(dtype, N, jobz, band);
+    if (P == 0) P = default_lanes(dtype, N, jobz, band, (long)batch);
     const Entry* ent = find_entry(dtype, N, P, jobz, band, pg);
     if (!ent) return -10;
     int per_block;

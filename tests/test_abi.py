@@ -57,6 +57,20 @@ def test_version(st):
     assert "gfx950" in st.version()
 
 
+@pytest.mark.parametrize("n,batch,P", [
+    (16, 1000, 2), (16, 32768, 2), (16, 65535, 2), (16, 65536, 1), (16, 262144, 1),
+    (32, 1000, 4), (32, 32768, 4), (32, 65536, 2), (32, 131071, 2), (32, 131072, 1)])
+def test_query_values_only_lanes_follow_batch(st, n, batch, P):
+    """Values only in float at orders 16 and 32: the default lanes per
+    problem drop once the batch fills the SIMDs with fewer (1,024 wavefronts
+    at order 16, 2,048 at order 32); an explicit band in LDS keeps the
+    fixed default, and so does every other dtype and jobz."""
+    q = st.steqr_query(n, batch, 0, 0)
+    assert (q["padded_n"], q["lanes_per_problem"], q["band_storage"]) == (n, P, 1)
+    assert st.steqr_query(n, batch, 0, 1)["lanes_per_problem"] == 1
+    assert st.steqr_query(n, batch, 1, 0)["lanes_per_problem"] == (4 if n == 16 else 8)
+
+
 @pytest.mark.parametrize("n,jobz,dtype,N,P", [
     (1, 1, 0, 4, 4), (4, 1, 0, 4, 4), (5, 1, 0, 8, 2), (8, 0, 0, 8, 1), (12, 1, 1, 12, 4), (12, 0, 1, 16, 1),
     (16, 1, 0, 16, 4), (17, 1, 0, 32, 8), (32, 1, 1, 32, 16), (32, 0, 1, 32, 1), (32, 0, 0, 32, 4), (16, 0, 0, 16, 2), (16, 0, 1, 16, 1),

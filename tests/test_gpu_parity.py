@@ -70,6 +70,34 @@ def test_workload_full_size(wname, jobz):
         assert V.orthogonality(Q[ok]).max() <= tol
 
 
+@pytest.mark.parametrize("wname,batch,P", [("c2_f32_n16", 65536, 1), ("c4_f32_n32", 65536, 2),
+                                           ("c4_f32_n32", 131072, 1)])
+def test_values_only_large_batch_default(wname, batch, P):
+    """Values only at two and four times the configuration's batch, where
+    the default launch takes fewer lanes per problem: a spread sample and
+    the tail against the oracle, properties on every item."""
+    import symmetric_tridiagonal_eigensolver_amd as st
+    w = W.WORKLOADS[wname]
+    _case(w, False, batch)
+    assert st.steqr_query(w.n, batch, 0, 0)["lanes_per_problem"] == P
+    d, e = W.make_batch(w, batch)
+    g = run_gpu(d, e, False)
+    items = np.unique(np.concatenate([np.linspace(0, batch - 1, 512).astype(int),
+                                      np.arange(batch - 64, batch)]))
+    o = oracle.steqr(d[items], e[items], False, threads=8)
+    assert check(d, e, g, o, False, items=items) == []
+    lam, _, info = g
+    finite = np.isfinite(d).all(1) & np.isfinite(e).all(1)
+    assert not info[finite].any()
+    assert np.all(info[~finite] > 0)
+    ok = info == 0
+    tol = V.tol_of(d.dtype, w.n)
+    assert np.all(np.diff(lam[ok], axis=1) >= 0)
+    tn = V.tnorm1(d[ok], e[ok])
+    assert np.all(np.abs(lam[ok].astype(np.float64).sum(1)
+                         - d[ok].astype(np.float64).sum(1)) <= w.n * tol * tn)
+
+
 LANE_CASES = [
     # dtype, n, jobz, lanes
     (np.float32, 4, True, 4), (np.float32, 4, True, 2), (np.float32, 4, True, 1),
