@@ -36,6 +36,14 @@ int padded_order(int n, int dtype = -1, int jobz = -1) {
 // 33..512 P counts the producer lanes of the producer-consumer kernel (with
 // or without its consumers); P = 64 selects one problem per wavefront at
 // orders 33..64.
+// The smallest of the ascending lane counts cand[0..k) whose launch has at
+// least T wavefronts (batch * P / 64), else the largest.
+int fill_lanes(long batch, const int* cand, int k, long T) {
+    for (int i = 0; i < k; ++i)
+        if (batch * cand[i] >= T * 64) return cand[i];
+    return cand[k - 1];
+}
+
 int default_lanes(int dtype, int N, int jobz, int band, long batch) {
     // orders 256 and 512: one problem per producer wavefront (without
     // eigenvectors 1024 matrices of order 256 took 6.52 ms in float at 64
@@ -54,6 +62,47 @@ int default_lanes(int dtype, int N, int jobz, int band, long batch) {
     // problem per wavefront)
     if (N == 64 && !jobz) return 8;
     if (N >= 64) return 64;
+    // Orders 8..32 in their default band storage: the lanes per problem
+    // follow the batch. Fewer lanes repeat less of the serial chase, more
+    // lanes spread a small batch over more SIMDs, so the default is the
+    // fewest lanes whose launch still has T wavefronts (all 1,024 SIMDs
+    // busy, two wavefronts each where the kernel hides latency with a
+    // second one). Each (candidates, T) reproduces the tuned choice at the
+    // configurations' batches (65,536 at order 8, 32,768 above) and was
+    // swept from 512 to 262,144 matrices on one MI355X, e.g. order 16 in
+    // float with eigenvectors: 63.1 us at 16 lanes against 73.0 at 4 on
+    // 8,192 matrices, 71.7 at 8 against 76.6 at 4 on 16,384; without
+    // eigenvectors 1.00 / 0.56 / 0.40 ns per matrix at one lane against
+    // 1.06 / 0.74 / 0.64 at two on 65,536 / 131,072 / 262,144; order 32
+    // without eigenvectors 3.62 us at two lanes against 4.11 at four on
+    // 65,536, 2.05 at one against 3.81 at four on 131,072.
+    if (dtype == STEQR_F32) {
+        if (jobz && band == 1 && N == 16) {
+            static const int c[] = {4, 8, 16};
+            return fill_lanes(batch, c, 3, 2048);
+        }
+        if (jobz && band == 1 && N == 8) {
+            static const int c[] = {2, 4, 8};
+            return fill_lanes(batch, c, 3, 2048);
+        }
+        if (jobz && band == 2 && N == 32) {
+            static const int c[] = {8, 16};
+            return fill_lanes(batch, c, 2, 2048);
+        }
+        if (!jobz && band == 1 && (N == 16 || N == 32)) {
+            static const int c[] = {1, 2, 4};
+            return fill_lanes(batch, c, 3, N == 16 ? 1024 : 2048);
+        }
+    } else {
+        if (jobz && band == 2 && N == 16) {
+            static const int c[] = {4, 8};
+            return fill_lanes(batch, c, 2, 1024);
+        }
+        if (!jobz && band == 1 && N == 32) {
+            static const int c[] = {1, 2};
+            return fill_lanes(batch, c, 2, 512);
+        }
+    }
     if (jobz) {
         if (N == 4 || N == 12) return 4;
         if (N == 8) return dtype == STEQR_F32 ? 2 : 4;
@@ -63,21 +112,8 @@ int default_lanes(int dtype, int N, int jobz, int band, long batch) {
         if (band == 2) return dtype == STEQR_F32 ? 8 : 16;  // N == 32
         return 16;  // double, band in registers: not built (-10)
     }
-    // values only in float: at the batch of 32,768 the split deflation scan
-    // pays at 4 lanes for order 32 (-3% against 2) and 2 lanes beat 1 at
-    // order 16 (-2%). A larger batch fills the SIMDs with fewer lanes per
-    // problem, and then the fewer lanes (less repeated chase work) win:
-    // one lane from 1,024 wavefronts at order 16 and from 2,048 at order 32,
-    // two lanes from 2,048 at order 32 (order 16 at 65,536 / 131,072 /
-    // 262,144 matrices: 1.00 / 0.56 / 0.40 ns per matrix at one lane against
-    // 1.06 / 0.74 / 0.64 at two; order 32: 3.62 us at two lanes against 4.11
-    // at four on 65,536, 2.05 at one against 3.81 at four on 131,072)
-    if (dtype == STEQR_F32 && band == 1 && (N == 16 || N == 32)) {
-        const long fill = (N == 16 ? 1024L : 2048L) * 64;  // wavefronts x 64
-        if (batch >= fill) return 1;
-        if (N == 32 && 2 * batch >= fill) return 2;
-        return N == 32 ? 4 : 2;
-    }
+    // values only in float with the band in LDS (asked for explicitly): the
+    // register kernel's choice at the batch of 32,768
     if (N == 32 && dtype == STEQR_F32) return 4;
     if (N == 16 && dtype == STEQR_F32) return 2;
     return 1;

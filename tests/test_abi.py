@@ -57,29 +57,48 @@ def test_version(st):
     assert "gfx950" in st.version()
 
 
-@pytest.mark.parametrize("n,batch,P", [
-    (16, 1000, 2), (16, 32768, 2), (16, 65535, 2), (16, 65536, 1), (16, 262144, 1),
-    (32, 1000, 4), (32, 32768, 4), (32, 65536, 2), (32, 131071, 2), (32, 131072, 1)])
-def test_query_values_only_lanes_follow_batch(st, n, batch, P):
-    """Values only in float at orders 16 and 32: the default lanes per
-    problem drop once the batch fills the SIMDs with fewer (1,024 wavefronts
-    at order 16, 2,048 at order 32); an explicit band in LDS keeps the
-    fixed default, and so does every other dtype and jobz."""
-    q = st.steqr_query(n, batch, 0, 0)
-    assert (q["padded_n"], q["lanes_per_problem"], q["band_storage"]) == (n, P, 1)
-    assert st.steqr_query(n, batch, 0, 1)["lanes_per_problem"] == 1
-    assert st.steqr_query(n, batch, 1, 0)["lanes_per_problem"] == (4 if n == 16 else 8)
+@pytest.mark.parametrize("dtype,jobz,n,cases", [
+    (0, 1, 16, [(512, 16), (8192, 16), (16384, 8), (32767, 8), (32768, 4), (262144, 4)]),
+    (0, 1, 8, [(1000, 8), (16384, 8), (32768, 4), (65535, 4), (65536, 2)]),
+    (0, 1, 32, [(1000, 16), (16383, 16), (16384, 8), (32768, 8)]),
+    (1, 1, 16, [(1000, 8), (16383, 8), (16384, 4), (32768, 4)]),
+    (0, 0, 16, [(1000, 4), (16384, 4), (32768, 2), (65535, 2), (65536, 1), (262144, 1)]),
+    (0, 0, 32, [(1000, 4), (32768, 4), (65536, 2), (131071, 2), (131072, 1)]),
+    (1, 0, 32, [(1000, 2), (16384, 2), (32767, 2), (32768, 1)]),
+    # outside the batch rule: fixed lanes at any batch
+    (0, 1, 4, [(512, 4), (262144, 4)]), (1, 1, 12, [(512, 4), (262144, 4)]),
+    (1, 1, 32, [(512, 16), (262144, 16)]), (0, 0, 8, [(512, 1), (262144, 1)]),
+    (1, 0, 16, [(512, 1), (262144, 1)])])
+def test_query_lanes_follow_batch(st, dtype, jobz, n, cases):
+    """Orders 8..32 in their default band storage: the default lanes per
+    problem are the fewest whose launch still has the case's wavefront
+    count (2,048 in float with eigenvectors, 1,024 in double with them and
+    in float values only at order 16, 2,048 at order 32, 512 in double
+    values only at order 32), else the most of the case's candidates; an
+    explicit band storage keeps the fixed choice."""
+    for batch, P in cases:
+        q = st.steqr_query(n, batch, jobz, dtype)
+        assert q["lanes_per_problem"] == P, (batch, q)
+    if dtype == 0 and n in (16, 32) and not jobz:
+        q = st.steqr_query(n, 262144, 0, 0, st.make_params(band_storage=1))
+        assert q["lanes_per_problem"] == 1
+    if dtype == 0 and n == 16 and jobz:
+        q = st.steqr_query(n, 512, 1, 0, st.make_params(band_storage=2))
+        assert (q["lanes_per_problem"], q["band_storage"]) == (4, 2)
 
 
 @pytest.mark.parametrize("n,jobz,dtype,N,P", [
-    (1, 1, 0, 4, 4), (4, 1, 0, 4, 4), (5, 1, 0, 8, 2), (8, 0, 0, 8, 1), (12, 1, 1, 12, 4), (12, 0, 1, 16, 1),
+    (1, 1, 0, 4, 4), (4, 1, 0, 4, 4), (5, 1, 0, 8, 4), (8, 0, 0, 8, 1), (12, 1, 1, 12, 4), (12, 0, 1, 16, 1),
     (16, 1, 0, 16, 4), (17, 1, 0, 32, 8), (32, 1, 1, 32, 16), (32, 0, 1, 32, 1), (32, 0, 0, 32, 4), (16, 0, 0, 16, 2), (16, 0, 1, 16, 1),
     (33, 1, 1, 64, 4), (64, 1, 1, 64, 4), (64, 1, 0, 64, 16), (64, 0, 0, 64, 8),
     (40, 0, 1, 64, 8), (100, 1, 0, 128, 8), (100, 1, 1, 128, 32), (128, 0, 0, 128, 16),
     (129, 1, 0, 256, 64), (256, 1, 1, 256, 64), (200, 0, 0, 256, 64), (256, 0, 1, 256, 64),
     (257, 1, 0, 512, 64), (512, 1, 1, 512, 64), (300, 0, 0, 512, 64), (512, 0, 1, 512, 64)])
 def test_query_default_plan(st, n, jobz, dtype, N, P):
-    q = st.steqr_query(n, 1000, jobz, dtype)
+    """Default launches at the configurations' batch of 32,768 (orders
+    8..32 pick their lanes by batch: test_query_lanes_follow_batch)."""
+    B = 32768
+    q = st.steqr_query(n, B, jobz, dtype)
     assert q["padded_n"] == N and q["lanes_per_problem"] == P
     if q["band_storage"] == 3:
         # producer and consumer wavefronts: one problem per consumer
@@ -93,14 +112,14 @@ def test_query_default_plan(st, n, jobz, dtype, N, P):
         if N >= 256:
             assert q["waves_per_block"] == 9
             gpp = {(256, 0): 1, (256, 1): 2, (512, 0): 8, (512, 1): 16}[(N, dtype)]
-            assert q["workgroups"] == 1000 * gpp
+            assert q["workgroups"] == B * gpp
             return
         cpp = 1 if N <= 64 else (2 if dtype == 0 else 4)
         per_block = (q["waves_per_block"] - 1) // cpp
     else:
         assert q["rows_per_lane"] == ((N + P - 1) // P if jobz else 0)
         per_block = q["waves_per_block"] * (64 // P)
-    assert q["workgroups"] == -(-1000 // per_block)
+    assert q["workgroups"] == -(-B // per_block)
 
 
 def test_query_producer_consumer_plans(st):
