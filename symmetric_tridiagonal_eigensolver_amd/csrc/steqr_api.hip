@@ -74,8 +74,8 @@ int default_lanes(int dtype, int N, int jobz, int band, long batch) {
     // 8,192 matrices, 71.7 at 8 against 76.6 at 4 on 16,384; without
     // eigenvectors 1.00 / 0.56 / 0.40 ns per matrix at one lane against
     // 1.06 / 0.74 / 0.64 at two on 65,536 / 131,072 / 262,144; order 32
-    // without eigenvectors 3.62 us at two lanes against 4.11 at four on
-    // 65,536, 2.05 at one against 3.81 at four on 131,072.
+    // without eigenvectors 3.62 ns per matrix at two lanes against 4.11 at
+    // four on 65,536, 2.05 at one against 3.81 at four on 131,072.
     if (dtype == STEQR_F32) {
         if (jobz && band == 1 && N == 16) {
             static const int c[] = {4, 8, 16};
