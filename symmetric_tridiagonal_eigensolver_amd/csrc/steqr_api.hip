@@ -54,9 +54,22 @@ int default_lanes(int dtype, int N, int jobz, int band, long batch) {
     // double with eigenvectors measured 1.4% faster at 32 than at 16
     if (N == 128) {
         if (band == 3) return dtype == STEQR_F32 ? 8 : 32;
+        // values only in float: 8 lanes once they still give 2,048
+        // wavefronts (16,384 matrices: 1.96 ms against 2.53 at 16 lanes)
+        if (dtype == STEQR_F32 && !jobz) {
+            static const int c[] = {8, 16};
+            return fill_lanes(batch, c, 2, 2048);
+        }
         return 16;
     }
-    if (band == 3) return dtype == STEQR_F32 ? 16 : 4;  // producer lanes per problem
+    // producer lanes per problem at order 64 with eigenvectors; in double
+    // 4 lanes (11 problems per workgroup) while that still gives 256
+    // workgroups, else 16 (3 per workgroup, more CUs busy: 1,024 matrices
+    // 0.79 ms against 0.84 at 4 lanes, 256 matrices 0.75 against 0.82)
+    if (band == 3) {
+        if (dtype == STEQR_F32) return 16;
+        return batch >= 256L * 11 ? 4 : 16;
+    }
     // order 64 without eigenvectors: the producer's algorithm, 8 problems
     // per wavefront (measured 2.9x (float) and 4x (double) faster than one
     // problem per wavefront)

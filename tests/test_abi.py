@@ -68,7 +68,13 @@ def test_version(st):
     # outside the batch rule: fixed lanes at any batch
     (0, 1, 4, [(512, 4), (262144, 4)]), (1, 1, 12, [(512, 4), (262144, 4)]),
     (1, 1, 32, [(512, 16), (262144, 16)]), (0, 0, 8, [(512, 1), (262144, 1)]),
-    (1, 0, 16, [(512, 1), (262144, 1)])])
+    (1, 0, 16, [(512, 1), (262144, 1)]),
+    # order 128 values only in float; order 64 in double with eigenvectors
+    # (producer lanes: 11 problems per workgroup at 4, 3 at 16)
+    (0, 0, 128, [(256, 16), (8192, 16), (16383, 16), (16384, 8)]),
+    (1, 0, 128, [(256, 16), (65536, 16)]),
+    (1, 1, 64, [(256, 16), (2815, 16), (2816, 4), (16384, 4)]),
+    (0, 1, 64, [(256, 16), (16384, 16)])])
 def test_query_lanes_follow_batch(st, dtype, jobz, n, cases):
     """Orders 8..32 in their default band storage: the default lanes per
     problem are the fewest whose launch still has the case's wavefront
@@ -91,7 +97,8 @@ def test_query_lanes_follow_batch(st, dtype, jobz, n, cases):
     (1, 1, 0, 4, 4), (4, 1, 0, 4, 4), (5, 1, 0, 8, 4), (8, 0, 0, 8, 1), (12, 1, 1, 12, 4), (12, 0, 1, 16, 1),
     (16, 1, 0, 16, 4), (17, 1, 0, 32, 8), (32, 1, 1, 32, 16), (32, 0, 1, 32, 1), (32, 0, 0, 32, 4), (16, 0, 0, 16, 2), (16, 0, 1, 16, 1),
     (33, 1, 1, 64, 4), (64, 1, 1, 64, 4), (64, 1, 0, 64, 16), (64, 0, 0, 64, 8),
-    (40, 0, 1, 64, 8), (100, 1, 0, 128, 8), (100, 1, 1, 128, 32), (128, 0, 0, 128, 16),
+    (40, 0, 1, 64, 8), (100, 1, 0, 128, 8), (100, 1, 1, 128, 32), (128, 0, 0, 128, 8),
+    (128, 0, 1, 128, 16),
     (129, 1, 0, 256, 64), (256, 1, 1, 256, 64), (200, 0, 0, 256, 64), (256, 0, 1, 256, 64),
     (257, 1, 0, 512, 64), (512, 1, 1, 512, 64), (300, 0, 0, 512, 64), (512, 0, 1, 512, 64)])
 def test_query_default_plan(st, n, jobz, dtype, N, P):
@@ -127,9 +134,9 @@ def test_query_producer_consumer_plans(st):
     wavefronts; band storage 2 still selects one problem per wavefront, and
     band 3 is rejected where no such kernel exists."""
     for dtype, w in ((0, 3), (1, 11)):
-        q = st.steqr_query(50, 700, 1, dtype)
+        q = st.steqr_query(50, 7000, 1, dtype)
         assert q["band_storage"] == 3 and q["waves_per_block"] == w + 1
-        assert q["workgroups"] == -(-700 // w)
+        assert q["workgroups"] == -(-7000 // w)
         if dtype == 0:
             q2 = st.steqr_query(50, 700, 1, dtype, st.make_params(band_storage=2))
             assert q2["band_storage"] == 2 and q2["lanes_per_problem"] == 64

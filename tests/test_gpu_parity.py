@@ -71,7 +71,7 @@ def test_workload_full_size(wname, jobz):
 
 
 @pytest.mark.parametrize("wname,batch,P", [("c2_f32_n16", 65536, 1), ("c4_f32_n32", 65536, 2),
-                                           ("c4_f32_n32", 131072, 1)])
+                                           ("c4_f32_n32", 131072, 1), ("w_f32_n128", 16384, 8)])
 def test_values_only_large_batch_default(wname, batch, P):
     """Values only at two and four times the configuration's batch, where
     the default launch takes fewer lanes per problem: a spread sample and
