@@ -2,9 +2,10 @@
 (1..512, most of them at most 32), precision, jobz, update scheme, shift,
 back-transformation, sorting, lanes per problem and band storage (any
 combination the library accepts for that order), batch size, and a mix of
-ordinary and edge items (splits, graded, zero, scaled, NaN) in one batch.
-Each case is checked item by item as the other parity tests are. Needs an
-MI355X; run with -m gpu."""
+ordinary and edge items (splits, graded, zero, scaled, NaN) in one batch;
+likewise the values-only bisection and the fused dense solver. Each case is
+checked item by item as the other parity tests are. Needs an MI355X; run
+with -m gpu."""
 import numpy as np
 import pytest
 
@@ -100,3 +101,78 @@ def test_random_configuration(seed):
         assert check_basis(d, e, Z, g, o) == []
     else:
         assert check(d, e, g, o, jobz) == []
+
+
+def _mixed_items(g, n, nb, dt, seed):
+    d, e = W.random_batch(n, nb, dt, salt=seed, cfg=9)
+    for b in range(nb):
+        if g.random() < 0.2:
+            kind = int(g.integers(0, 5))
+            de, ee = W.edge_batch(kind, n, 1, dt, salt=2000 * seed + b)
+            d[b], e[b] = de[0], ee[0]
+    return d, e
+
+
+@pytest.mark.parametrize("seed", range(64))
+def test_random_bisection(seed):
+    """Values-only bisection at random orders 1..512 and batches with mixed
+    edge items, against the oracle's bisection."""
+    import torch
+    import symmetric_tridiagonal_eigensolver_amd as st
+    g = np.random.default_rng(0xB15E + seed)
+    dt = np.float32 if g.random() < 0.5 else np.float64
+    u = g.random()
+    n = int(g.integers(1, 65)) if u < 0.7 else int(g.integers(65, 513))
+    nb = int(g.integers(1, 258)) if n <= 64 else int(g.integers(1, 17))
+    print("fuzz bisection seed=%d %s n=%d batch=%d" % (seed, dt.__name__, n, nb), flush=True)
+    d, e = _mixed_items(g, n, nb, dt, seed)
+    dev = torch.device("cuda:0")
+    lam, _, info = st.solve(torch.from_numpy(d).to(dev), torch.from_numpy(e).to(dev), False,
+                            info=True, method=1)
+    torch.cuda.synchronize()
+    gpu = (lam.cpu().numpy(), None, info.cpu().numpy())
+    lo, io = oracle.stebz(d, e, threads=8)
+    assert check(d, e, gpu, (lo, None, io), False) == []
+
+
+@pytest.mark.parametrize("seed", range(64))
+def test_random_syev(seed):
+    """The fused dense solver at random orders 1..32, batches, shifts,
+    sorting and lanes, with zero, diagonal, tridiagonal and scaled items
+    among random symmetric ones, against the oracle's syev."""
+    import symmetric_tridiagonal_eigensolver_amd as st
+    from parity import check_dense, run_gpu_syev
+    g = np.random.default_rng(0x5E7 + seed)
+    dt = np.float32 if g.random() < 0.5 else np.float64
+    n = int(g.integers(1, 33))
+    jobz = bool(g.random() < 0.7) and (dt == np.float32 or n <= st.SYEV_MAX_N_F64_V)
+    shift = int(g.random() < 0.3)
+    sort = bool(g.random() < 0.8)
+    nb = int(g.integers(1, 301))
+    code = 0 if dt == np.float32 else 1
+    options = [0]
+    for lanes in (1, 2, 4, 8, 16, 32, 64):
+        try:
+            st.syev_query(n, nb, int(jobz), code, st.make_params(lanes_per_problem=lanes,
+                                                                shift=shift))
+        except st.SteqrError:
+            continue
+        options.append(lanes)
+    lanes = options[int(g.integers(0, len(options)))]
+    print("fuzz syev seed=%d %s n=%d jobz=%s shift=%d sort=%s batch=%d lanes=%d"
+          % (seed, dt.__name__, n, jobz, shift, sort, nb, lanes), flush=True)
+    A = W.random_symmetric(n, nb, np.float64, salt=seed, cfg=10)
+    for b in range(nb):
+        r = g.random()
+        if r < 0.04:
+            A[b] = 0.0
+        elif r < 0.08:
+            A[b] = np.diag(np.diag(A[b]))
+        elif r < 0.12:
+            A[b] = np.triu(np.tril(A[b], 1), -1)
+        elif r < 0.16:
+            A[b] *= 10.0 ** (int(g.integers(-12, 13)))
+    A = np.ascontiguousarray(A.astype(dt))
+    gpu = run_gpu_syev(A, jobz, sort=sort, lanes=lanes, shift=shift)
+    o = oracle.syev(A, jobz, threads=8, shift=shift, sort=sort)
+    assert check_dense(A, gpu, o, jobz, sort=sort) == []
