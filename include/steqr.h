@@ -72,8 +72,12 @@ typedef struct steqr_params {
     /* 0 = sort eigenpairs ascending (default), 1 = keep converged order. */
     int no_sort;
     /* Lanes per problem P (problems per 64-lane wavefront = 64 / P). 0 =
-     * tuned default; otherwise a power of two the build provides for this
-     * (dtype, n, jobz); steqr_query() lists it. */
+     * tuned default, which depends on the order, dtype, jobz and band
+     * storage and, at orders 8..32 (and 64, 128 in some cases), on the
+     * batch: the fewest lanes whose launch still fills the SIMDs; otherwise
+     * a power of two the build provides for this (dtype, n, jobz).
+     * steqr_query() reports the choice for a given batch. Results do not
+     * depend on P beyond rounding order. */
     int lanes_per_problem;
     /* Wavefronts per workgroup (1, 2 or 4); 0 = default (4, fewer when a
      * small batch would otherwise leave fewer than 256 workgroups). Launch
