@@ -76,8 +76,8 @@ typedef struct steqr_params {
      * storage and, at orders 8..32 (and 64, 128 in some cases), on the
      * batch: the fewest lanes whose launch still fills the SIMDs; otherwise
      * a power of two the build provides for this (dtype, n, jobz).
-     * steqr_query() reports the choice for a given batch. Results do not
-     * depend on P beyond rounding order. */
+     * steqr_query() reports the choice for a given batch. Every P and band
+     * storage gives the same results bit for bit. */
     int lanes_per_problem;
     /* Wavefronts per workgroup (1, 2 or 4); 0 = default (4, fewer when a
      * small batch would otherwise leave fewer than 256 workgroups). Launch

@@ -3,9 +3,10 @@
 //
 // With one problem per wavefront every decision of the solve is uniform
 // across the wavefront, so the design differs from the chunked kernel:
-//  * the band d, e lives in LDS (broadcast reads, one writer lane); the
-//    chase reads the next position's entries one step ahead, so the LDS
-//    latency overlaps the current rotation;
+//  * the band d, e lives in LDS (broadcast reads; every lane writes the
+//    same words, so no lane mask); the chase reads the next position's
+//    entries one step ahead, so the LDS latency overlaps the current
+//    rotation;
 //  * block bounds, the active part [s, m], the sweep counter and the status
 //    are scalar (SGPR) values and every branch is a scalar branch;
 //  * the deflation test runs on all lanes at once (lane i tests e_i) and one
@@ -66,7 +67,6 @@ __global__ void __launch_bounds__(256) steqr_wave_kernel(KernelArgs args) {
     T* const sd = reinterpret_cast<T*>(ws);
     T* const se = sd + N;
     int* const srank = reinterpret_cast<int*>(se + N);
-    const bool writer = (lane == 0);
 
     // ---------------------------------------------------------------- load
     {
@@ -228,18 +228,38 @@ __global__ void __launch_bounds__(256) steqr_wave_kernel(KernelArgs args) {
         }
         if (state == ST_DONE) break;
 
-        if (sweep) {
-            // chase over [s, m]. Carried: dcur = current d_p (updated by the
-            // previous step), ecur = original e_p, cp = previous cosine (the
-            // update e_p <- c_{p-1} e_p is applied here), (x, y) = running
-            // pair. d_{p+1}, e_{p+1} are read one step ahead: no step writes
-            // them before step p.
-            // running pair (d_s - mu, e_s) for the first rotation (PG: g
-            // in x, the previous sine in y)
+        if (sweep | jac) {
+            // chase over [s, me - 1]. Carried: dcur = current d_p (updated by
+            // the previous step), ecur = original e_p, cp = previous cosine
+            // (the update e_p <- c_{p-1} e_p is applied here), (x, y) =
+            // running pair. d_{p+1}, e_{p+1} are read one step ahead: no step
+            // writes them before step p.
             T dcur = sd[s], ecur = se[s];
-            T x = dcur - mu, y = PG ? T(1) : ecur, cp = T(1);
+            T x, y;
+            int me = m;
+            if (jac) {
+                // A 2x2 block at (jpos, jpos+1) [algo, 2x2 block paragraph],
+                // as in the chunked kernels: its closed-form Schur rotation
+                // seeds a one-step chase at jpos (lartg returns that rotation;
+                // for PG from (cs e, -sj e)), so the similarity and the Q
+                // update are those of the sweeps, and every kernel family
+                // computes the same bits. The leftover e_jpos (rounding size)
+                // joins `zeroed`; s == jpos here.
+                T rt1, rt2, cs, sj;
+                sym2x2(dcur, ecur, sd[jpos + 1], rt1, rt2, cs, sj);
+                x = PG ? cs * ecur : cs;
+                y = -sj;
+                me = jpos + 1;
+                zeroed |= (M)1 << jpos;
+            } else {
+                // running pair (d_s - mu, e_s) for the first rotation (PG: g
+                // in x, the previous sine in y)
+                x = dcur - mu;
+                y = PG ? T(1) : ecur;
+            }
+            T cp = T(1);
             T dnext = sd[s + 1], enext = se[s + 1];
-            // positions s .. m-1; the walk stops after m-1 (uniform branch)
+            // positions s .. me-1; the walk stops after me-1 (uniform branch)
             static_for_while<N - 1>([&](auto I) {
                 constexpr int p = decltype(I)::value;
                 if (p >= s) {
@@ -283,30 +303,12 @@ __global__ void __launch_bounds__(256) steqr_wave_kernel(KernelArgs args) {
                         F::rot(q[p], q[p + 1], c, sn);
                     }
                 }
-                return p + 1 < m;
+                return p + 1 < me;
             });
-            sd[m] = dcur;
-            se[m - 1] = x;
+            sd[me] = dcur;
+            se[me - 1] = x;
             __builtin_amdgcn_wave_barrier();
-            if (uniform_int(mu != mu)) jtot = nmaxit;
-        }
-        if (jac) {
-            static_for<N - 1>([&](auto I) {
-                constexpr int p = decltype(I)::value;
-                if (p == jpos) {
-                    T rt1, rt2, cs, sj;
-                    sym2x2(sd[p], se[p], sd[p + 1], rt1, rt2, cs, sj);
-                    if (writer) {
-                        sd[p] = rt1;
-                        sd[p + 1] = rt2;
-                        se[p] = T(0);
-                    }
-                    if constexpr (WANTQ) {
-                        F::rot(q[p], q[p + 1], cs, -sj);
-                    }
-                }
-            });
-            __builtin_amdgcn_wave_barrier();
+            if (sweep && uniform_int(mu != mu)) jtot = nmaxit;
         }
     }
 
