@@ -287,7 +287,7 @@ def main() -> int:
                           band_storage=args.band, update_scheme=scheme, method=method)
     lanes0 = st.steqr_query(w.n, w.batch, int(jobz), 0 if w.dtype == "f32" else 1,
                             prm0)["lanes_per_problem"]
-    d, e = W.make_batch(w, replicate=(64 // lanes0) if args.replicate else 1)
+    d, e = W.make_batch(w, replicate=max(1, 64 // lanes0) if args.replicate else 1)
     dev = torch.device("cuda:0")
     td = torch.from_numpy(d).to(dev)
     te = torch.from_numpy(e).to(dev)

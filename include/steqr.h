@@ -133,9 +133,13 @@ typedef struct steqr_params {
      * that ran out of halvings (0 for any finite input in practice), n for
      * a band holding a NaN (all eigenvalues NaN). max_sweeps_per_n and
      * no_sort do not apply; update_scheme, shift, band_storage,
-     * back_transform must be 0 and lanes_per_problem 0 or the lanes the
-     * kernel uses (the padded order, 64 at orders 128 to 512; -10
-     * otherwise). */
+     * back_transform must be 0 (-10 otherwise). lanes_per_problem: 0
+     * (default) or the lanes the kernel uses: the padded order up to 64;
+     * from order 128 64, 128 or 256 (the problem's indices spread over one,
+     * two or four wavefronts of a workgroup, at most the padded order; the
+     * default takes the fewest whose launch has 2,048 wavefronts, and
+     * waves_per_block then does not apply); -10 otherwise. Every choice
+     * gives the same results bit for bit. */
     int method;
 } steqr_params;
 

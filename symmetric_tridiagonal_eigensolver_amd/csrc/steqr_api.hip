@@ -132,6 +132,23 @@ int default_lanes(int dtype, int N, int jobz, int band, long batch) {
     return 1;
 }
 
+// Lanes per problem of the values-only bisection: min(N, 64) up to order
+// 64; from order 128 the fewest of 1, 2 or 4 wavefronts per problem (at most
+// N / 64) whose launch has 2,048 wavefronts. The indices' bisections are
+// independent, so every choice gives the same bits. Measured: order 512,
+// 256 matrices, 1 / 2 / 4 wavefronts: float 2.16 / 1.41 / 1.04 ms, double
+// 7.51 / 4.64 / 2.92 ms; 1,024 matrices: float 2.21 / 1.73 / 1.71, double
+// 7.58 / 7.08 / 7.12; order 256, 1,024 matrices: float 0.64 / 0.55 / 0.53,
+// double 2.27 / 2.01 / 2.04; 4,096 matrices: float 1.60 / 1.68 / 1.69,
+// double 6.57 / 7.44 / 6.91; order 128, 8,192 matrices: float 0.82 / 0.88.
+int bisect_default_lanes(int dtype, int N, long batch) {
+    (void)dtype;
+    if (N < 128) return N < 64 ? N : 64;
+    int G = 1;
+    while (G < 4 && 64 * G < N && batch * G < 2048) G *= 2;
+    return 64 * G;
+}
+
 const Entry* search(const Table& t, int dtype, int N, int P, int jobz, int band) {
     for (int i = 0; i < t.count; ++i) {
         const Entry& x = t.entries[i];
@@ -206,7 +223,10 @@ int plan_launch(int n, int batch, int jobz, int dtype, const steqr_params* prm, 
             waves = prm->waves_per_block;
         }
         P = prm->lanes_per_problem;
-        if (P < 0 || P > 64 || (P != 0 && (64 % P) != 0)) return -10;
+        // a power of two up to 64; bisection also takes several wavefronts
+        // per problem (up to the padded order, checked below)
+        const int pmax = prm->method == STEQR_METHOD_BISECT ? 512 : 64;
+        if (P < 0 || P > pmax || (P != 0 && (P & (P - 1)) != 0)) return -10;
         if (prm->no_sort != 0 && prm->no_sort != 1) return -10;
         if (prm->back_transform != 0 && prm->back_transform != 1) return -10;
         if (prm->back_transform == 1 && jobz != STEQR_V) return -10;
@@ -222,20 +242,28 @@ int plan_launch(int n, int batch, int jobz, int dtype, const steqr_params* prm, 
     const int N = bisect ? padded_order(n < 2 ? 2 : n) : padded_order(n < 2 ? 2 : n, dtype, jobz);
     if (N < 0) return -5;  // order not provided by this build
     if (prm && prm->method == STEQR_METHOD_BISECT) {
-        // values-only bisection: one lane per eigenvalue
-        const int L = N < 64 ? N : 64;  // lanes per problem
+        // values-only bisection: one lane per eigenvalue index, min(N, 64)
+        // lanes of a wavefront per problem; from order 128 also 64 G lanes,
+        // G wavefronts of one workgroup per problem
+        const int L = N < 64 ? N : 64;
         if (jobz != STEQR_N || prm->update_scheme != 0 || prm->shift != 0 ||
-            prm->band_storage != 0 || prm->back_transform != 0 || (P != 0 && P != L))
+            prm->band_storage != 0 || prm->back_transform != 0)
             return -10;
-        const Entry* ent = search(steqr::table_bisect(), dtype, N, L, STEQR_N,
+        const int Pb = P != 0 ? P : bisect_default_lanes(dtype, N, (long)batch);
+        if (Pb < L || Pb > (N < 128 ? L : N)) return -10;
+        const Entry* ent = search(steqr::table_bisect(), dtype, N, Pb, STEQR_N,
                                   (2 * N * (dtype == STEQR_F32 ? 4 : 8) / 4 <= 128) ? 1 : 2);
         if (!ent) return -10;
+        const int G = Pb / L;  // wavefronts per problem
         p.entry = ent;
         p.N = N;
-        p.P = L;
+        p.P = Pb;
         p.R = 0;
         p.band = ent->band;
-        const int per_block = waves * (64 / L);
+        // several wavefronts per problem: one problem per workgroup (the
+        // workgroup size is then G wavefronts, whatever waves_per_block says)
+        p.waves = G > 1 ? G : waves;
+        const int per_block = G > 1 ? 1 : waves * (64 / L);
         p.grid = batch > 0 ? (int)(((long)batch + per_block - 1) / per_block) : 0;
         *out = p;
         return 0;
@@ -370,7 +398,10 @@ int syev_plan(int n, int batch, int jobz, int dtype, const steqr_params* prm, Pl
             waves = prm->waves_per_block;
         }
         P = prm->lanes_per_problem;
-        if (P < 0 || P > 64 || (P != 0 && (64 % P) != 0)) return -10;
+        // a power of two up to 64; bisection also takes several wavefronts
+        // per problem (up to the padded order, checked below)
+        const int pmax = prm->method == STEQR_METHOD_BISECT ? 512 : 64;
+        if (P < 0 || P > pmax || (P != 0 && (P & (P - 1)) != 0)) return -10;
     }
     Plan p{};
     p.waves = waves;

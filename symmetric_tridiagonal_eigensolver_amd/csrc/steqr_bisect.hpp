@@ -4,11 +4,14 @@
 // exits on the tolerance, the halving budget or a stalled midpoint).
 //
 // Design (MI355X-first). One problem per chunk of N lanes (N = the padded
-// order; at order 128 one problem per wavefront with two indices, k and
-// k + 64, per lane), one eigenvalue index per lane: lane k of a chunk bisects the k-th
-// smallest eigenvalue with Sturm counts of its own, so the 64 lanes of a
-// wavefront run 64 independent bisections in lockstep with no exchange at
-// all after the set-up. Every bisection takes about the same number of
+// order; from order 128 one problem per wavefront with N / 64 indices per
+// lane, k, k + 64, ..., or spread over G wavefronts of one workgroup with
+// N / (64 G) indices each), one eigenvalue index per lane: lane k of a chunk
+// bisects the k-th smallest eigenvalue with Sturm counts of its own, so the
+// 64 lanes of a wavefront run 64 independent bisections in lockstep with no
+// exchange at all after the set-up. With G wavefronts per problem every
+// wavefront repeats the (cheap) set-up over the whole band and bisects its
+// own share of the indices; the status sums the shares through LDS. Every bisection takes about the same number of
 // halvings (the interval starts as the Gershgorin interval and ends at a
 // few ulps of ||T||), so lockstep costs little; a lane that has converged
 // is masked off until every lane of the wavefront has.
@@ -33,7 +36,9 @@ namespace steqr {
 template <typename T, int N>
 struct SmemB {
     static constexpr int CH = N < 64 ? 64 / N : 1;
-    static constexpr size_t bytes_per_wave = (size_t)CH * 2 * N * sizeof(T);
+    // the chunks' scaled bands, then one int (the wavefront's failed
+    // indices, for G wavefronts per problem)
+    static constexpr size_t bytes_per_wave = (size_t)CH * 2 * N * sizeof(T) + 16;
 };
 
 // Butterfly over the N lanes of a chunk.
@@ -56,14 +61,17 @@ __device__ __forceinline__ int chunk_sumi(int v) {
     return v;
 }
 
-template <typename T, int N>
-__global__ void __launch_bounds__(256) steqr_bisect_kernel(KernelArgs args) {
-    // L lanes per problem, E = N / L positions and eigenvalue indices per
-    // lane (k, k + L, ...): one index per lane up to order 64, two at 128,
-    // four at 256, eight at 512
+template <typename T, int N, int G = 1>
+__global__ void __launch_bounds__(G > 1 ? 64 * G : 256) steqr_bisect_kernel(KernelArgs args) {
+    // L lanes per wavefront and problem, E = N / L positions per lane for
+    // the set-up (k, k + L, ...): one up to order 64, two at 128, four at
+    // 256, eight at 512; the G wavefronts of a problem bisect EB = E / G
+    // indices per lane each (wavefront g: k0 + (g EB + j) L, j < EB)
     constexpr int L = N < 64 ? N : 64;
     constexpr int E = N / L;
+    constexpr int EB = E / G;
     static_assert(N >= 2 && N <= 512 && (64 % L) == 0 && E * L == N, "lanes per position");
+    static_assert(G >= 1 && EB * G == E && (G == 1 || L == 64), "wavefronts per problem");
     using F = Fp<T>;
     using S = SmemB<T, N>;
     constexpr int CH = 64 / L;
@@ -81,7 +89,8 @@ __global__ void __launch_bounds__(256) steqr_bisect_kernel(KernelArgs args) {
     const int wave = threadIdx.x >> 6;
     const int chunk = lane / L;
     const int k0 = lane % L;  // first position / eigenvalue index of this lane
-    const long prob = ((long)blockIdx.x * (blockDim.x >> 6) + wave) * CH + chunk;
+    const int grp = wave % G;  // this wavefront's share of the indices
+    const long prob = ((long)blockIdx.x * ((blockDim.x >> 6) / G) + wave / G) * CH + chunk;
     const bool live = prob < (long)args.batch;
     const long pb = live ? prob : (long)args.batch - 1;
     T* const sdd = reinterpret_cast<T*>(smem_raw + (size_t)wave * S::bytes_per_wave) + chunk * 2 * N;
@@ -152,16 +161,16 @@ __global__ void __launch_bounds__(256) steqr_bisect_kernel(KernelArgs args) {
         });
     }
 
-    // Sturm counts of the scaled band below x[0..E) in one traversal
-    auto count = [&](const T (&x)[E], int (&c)[E]) __attribute__((always_inline)) {
-        T q[E];
-        static_for<E>([&](auto J) { c[decltype(J)::value] = 0; });
+    // Sturm counts of the scaled band below x[0..EB) in one traversal
+    auto count = [&](const T (&x)[EB], int (&c)[EB]) __attribute__((always_inline)) {
+        T q[EB];
+        static_for<EB>([&](auto J) { c[decltype(J)::value] = 0; });
         static_for_while<N>([&](auto I) {
             constexpr int i = decltype(I)::value;
             const T di = REGS ? bd[i] : sdd[i];
             T ei = T(0);
             if constexpr (i > 0) ei = REGS ? be2[i - 1] : se2[i - 1];
-            static_for<E>([&](auto J) {
+            static_for<EB>([&](auto J) {
                 constexpr int j = decltype(J)::value;
                 if constexpr (i == 0) {
                     q[j] = di - x[j];
@@ -176,23 +185,29 @@ __global__ void __launch_bounds__(256) steqr_bisect_kernel(KernelArgs args) {
     };
 
     // ------------------------------------------------------------ bisection
-    T lo[E], hi[E];
-    bool done[E];
-    int fail = 0, it[E];
+    // index k0 + (grp EB + j) L of the lane's share
+    bool mine[EB];
+    static_for<EB>([&](auto J) {
+        constexpr int j = decltype(J)::value;
+        mine[j] = live & (k0 + (grp * EB + j) * L < n);
+    });
+    T lo[EB], hi[EB];
+    bool done[EB];
+    int fail = 0, it[EB];
     bool any_open = false;
-    static_for<E>([&](auto J) {
+    static_for<EB>([&](auto J) {
         constexpr int j = decltype(J)::value;
         lo[j] = gl0 - widen;
         hi[j] = gu0 + widen;
-        done[j] = !hasd[j] | bad | zero;
+        done[j] = !mine[j] | bad | zero;
         it[j] = 0;
         any_open |= !done[j];
     });
     while (__builtin_amdgcn_ballot_w64(any_open)) {
         if (any_open) {
-            T mid[E];
-            bool step[E];
-            static_for<E>([&](auto J) {
+            T mid[EB];
+            bool step[EB];
+            static_for<EB>([&](auto J) {
                 constexpr int j = decltype(J)::value;
                 step[j] = false;
                 mid[j] = (lo[j] + hi[j]) * T(0.5);
@@ -212,13 +227,13 @@ __global__ void __launch_bounds__(256) steqr_bisect_kernel(KernelArgs args) {
                 }
             });
             bool any_step = false;
-            static_for<E>([&](auto J) { any_step |= step[decltype(J)::value]; });
+            static_for<EB>([&](auto J) { any_step |= step[decltype(J)::value]; });
             if (any_step) {
-                int c[E];
+                int c[EB];
                 count(mid, c);
-                static_for<E>([&](auto J) {
+                static_for<EB>([&](auto J) {
                     constexpr int j = decltype(J)::value;
-                    const int k = k0 + j * L;
+                    const int k = k0 + (grp * EB + j) * L;
                     if (step[j]) {
                         if (c[j] <= k)
                             lo[j] = mid[j];
@@ -229,21 +244,34 @@ __global__ void __launch_bounds__(256) steqr_bisect_kernel(KernelArgs args) {
                 });
             }
             any_open = false;
-            static_for<E>([&](auto J) { any_open |= !done[decltype(J)::value]; });
+            static_for<EB>([&](auto J) { any_open |= !done[decltype(J)::value]; });
         }
     }
 
     // ------------------------------------------------------------ store
     const T us = F::ldexp(T(1), ex);
-    static_for<E>([&](auto J) {
+    static_for<EB>([&](auto J) {
         constexpr int j = decltype(J)::value;
         T lam = ((lo[j] + hi[j]) * T(0.5)) * us;
         lam = zero ? T(0) : lam;
         lam = bad ? F::qnan() : lam;
-        if (hasd[j]) glam[prob * n + k0 + j * L] = lam;
+        if (mine[j]) glam[prob * n + k0 + (grp * EB + j) * L] = lam;
     });
-    const int nfail = chunk_sumi<L>(fail);
-    if (live & (k0 == 0) & (args.info != nullptr)) args.info[prob] = bad ? n : nfail;
+    int nfail = chunk_sumi<L>(fail);
+    if constexpr (G > 1) {
+        // the G wavefronts of the problem (consecutive in the workgroup)
+        // add their counts through LDS; every wavefront reaches the barrier
+        int* const fl = reinterpret_cast<int*>(smem_raw + (size_t)(wave + 1) * S::bytes_per_wave) - 4;
+        if (lane == 0) fl[0] = nfail;
+        __syncthreads();
+        nfail = 0;
+        static_for<G>([&](auto GG) {
+            constexpr int gg = decltype(GG)::value;
+            nfail += reinterpret_cast<const int*>(
+                smem_raw + (size_t)(wave - grp + gg + 1) * S::bytes_per_wave)[-4];
+        });
+    }
+    if (live & (grp == 0) & (k0 == 0) & (args.info != nullptr)) args.info[prob] = bad ? n : nfail;
 }
 
 }  // namespace steqr

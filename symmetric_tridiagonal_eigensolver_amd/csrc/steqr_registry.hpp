@@ -116,18 +116,24 @@ hipError_t launch_pcv(const KernelArgs& args, int grid, int block, hipStream_t s
     { DT, N, P, Q, 1, (int)Smem<T, N, P, (Q) != 0>::bytes_per_wave, \
       &launch_chunk<T, N, P, (Q) != 0, STEQR_INST_PG != 0> }
 
-// Values-only bisection: one lane per eigenvalue index (two at order 128),
-// min(N, 64) lanes per problem.
-template <typename T, int N>
+// Values-only bisection: one lane per eigenvalue index (N / 64 per lane
+// from order 128), min(N, 64) lanes per problem; from order 128 also G
+// wavefronts of one workgroup per problem (64 G lanes, N / (64 G) indices
+// per lane; the workgroup holds whole problems).
+template <typename T, int N, int G = 1>
 hipError_t launch_bisect(const KernelArgs& args, int grid, int block, hipStream_t stream) {
     const size_t lds = (size_t)(block / 64) * SmemB<T, N>::bytes_per_wave;
-    hipLaunchKernelGGL((steqr_bisect_kernel<T, N>), dim3(grid), dim3(block), lds, stream, args);
+    hipLaunchKernelGGL((steqr_bisect_kernel<T, N, G>), dim3(grid), dim3(block), lds, stream, args);
     return hipGetLastError();
 }
 
 #define STEQR_BISECT_ENTRY(DT, T, N) \
     { DT, N, (N) < 64 ? (N) : 64, 0, (2 * N * (int)sizeof(T) / 4 <= 128) ? 1 : 2, \
       (int)SmemB<T, N>::bytes_per_wave, &launch_bisect<T, N> }
+
+#define STEQR_BISECT_G_ENTRY(DT, T, N, G) \
+    { DT, N, 64 * (G), 0, (2 * N * (int)sizeof(T) / 4 <= 128) ? 1 : 2, \
+      (int)SmemB<T, N>::bytes_per_wave, &launch_bisect<T, N, G> }
 
 struct Table {
     const Entry* entries;

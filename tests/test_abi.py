@@ -320,6 +320,33 @@ def test_bisect_plans(st, n, dtype, N, band):
     assert q["workgroups"] == -(-32768 // (q["waves_per_block"] * 64 // L))
 
 
+@pytest.mark.parametrize("n,dtype,batch,P,waves,wgs", [
+    (512, 0, 256, 256, 4, 256), (512, 1, 1024, 128, 2, 1024), (512, 0, 2048, 64, 4, 512),
+    (300, 1, 2047, 128, 2, 2047), (256, 0, 1024, 128, 2, 1024), (256, 1, 4096, 64, 4, 1024),
+    (200, 0, 100, 256, 4, 100), (128, 0, 8192, 64, 4, 2048), (128, 1, 1000, 128, 2, 1000),
+    (100, 0, 10, 128, 2, 10), (64, 0, 10, 64, 4, 3)])
+def test_bisect_wavefronts_per_problem(st, n, dtype, batch, P, waves, wgs):
+    """From order 128 the bisection spreads a problem's eigenvalue indices
+    over 1, 2 or 4 wavefronts of one workgroup (64, 128 or 256 lanes per
+    problem): the fewest whose launch has 2,048 wavefronts."""
+    q = st.steqr_query(n, batch, 0, dtype, st.make_params(method=st.STEQR_METHOD_BISECT))
+    assert (q["lanes_per_problem"], q["waves_per_block"], q["workgroups"]) == (P, waves, wgs)
+
+
+def test_bisect_lanes_choices(st):
+    def q(n, lanes):
+        return st.steqr_query(n, 100, 0, 0, st.make_params(method=1, lanes_per_problem=lanes))
+    for n, lanes, waves in ((512, 64, 4), (512, 128, 2), (512, 256, 4), (256, 256, 4),
+                            (128, 128, 2), (64, 64, 4), (16, 16, 4)):
+        r = q(n, lanes)
+        assert (r["lanes_per_problem"], r["waves_per_block"]) == (lanes, waves)
+    # more lanes than the padded order, eight wavefronts, fewer than a
+    # wavefront from order 64, or more than one below order 128: rejected
+    for n, lanes in ((128, 256), (512, 512), (512, 32), (64, 128), (100, 32), (16, 64)):
+        with pytest.raises(st.SteqrError):
+            q(n, lanes)
+
+
 def test_bisect_argument_errors(st):
     L = st.lib()
     bad = [st.make_params(method=2), st.make_params(method=-1),

@@ -113,3 +113,27 @@ def test_bisect_agrees_with_qr_and_closed_forms(dt):
         cl = run_bisect(np.zeros((1, n), dtype=dt), ce)[0][0]
         ref = np.arange(-(n - 1), n, 2, dtype=np.float64)
         assert np.abs(cl - ref).max() <= V.tol_of(dt, n) * (2 * ce.max())
+
+
+@pytest.mark.parametrize("dt,n,lanes", [
+    (np.float32, 512, 128), (np.float32, 512, 256), (np.float64, 512, 128),
+    (np.float64, 512, 256), (np.float64, 300, 128), (np.float32, 257, 256),
+    (np.float32, 256, 128), (np.float64, 256, 256), (np.float32, 200, 256),
+    (np.float64, 129, 128), (np.float32, 128, 128), (np.float64, 100, 128),
+    (np.float32, 65, 128)])
+def test_bisect_several_wavefronts_per_problem(dt, n, lanes):
+    """A problem's indices spread over 2 or 4 wavefronts of a workgroup:
+    the oracle's eigenvalues and status on a ragged batch with every edge
+    kind, and the same bits as one wavefront per problem."""
+    print("bisect wavefronts case", dt.__name__, n, lanes, flush=True)
+    nb = 37
+    d, e = W.random_batch(n, nb, dt, salt=31)
+    for b in range(4, nb, 7):
+        de, ee = W.edge_batch((b // 7) % 5, n, 1, dt, salt=b)
+        d[b], e[b] = de[0], ee[0]
+    g = run_bisect(d, e, lanes_per_problem=lanes)
+    o = oracle_bisect(d, e)
+    assert check(d, e, g, o, False) == []
+    g1 = run_bisect(d, e, lanes_per_problem=64)
+    assert np.array_equal(g[0].view(np.uint8), g1[0].view(np.uint8))
+    assert np.array_equal(g[2], g1[2])
