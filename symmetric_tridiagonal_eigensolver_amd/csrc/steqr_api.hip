@@ -368,7 +368,31 @@ namespace {
 // the replicated band within the register file at two wavefronts per SIMD;
 // without Q there is room for twice the rows at orders 16 (double) and 32
 // (float).
-int syev_default_lanes(int dtype, int N, int jobz) {
+int syev_default_lanes(int dtype, int N, int jobz, long batch) {
+    // Below the configurations' batches more lanes per problem spread the
+    // batch over more SIMDs: the fewest of the candidates whose launch has
+    // T wavefronts (each rule keeps the tuned choice at the configuration's
+    // batch). Measured: float order 8 with vectors, 32,768 matrices 32.0 us
+    // at 4 lanes against 34.9 at 2; float order 16 with vectors, 16,384
+    // matrices 85.0 at 8 against 95.8 at 4; float order 32 values only,
+    // 4,096 matrices 201.7 at 16 against 208.4 at 8; double order 16 values
+    // only, 4,096 matrices 90.5 at 8 against 96.0 at 4.
+    if (dtype == STEQR_F32 && jobz && N == 8) {
+        static const int c[] = {2, 4};
+        return fill_lanes(batch, c, 2, 2048);
+    }
+    if (dtype == STEQR_F32 && jobz && N == 16) {
+        static const int c[] = {4, 8};
+        return fill_lanes(batch, c, 2, 2048);
+    }
+    if (dtype == STEQR_F32 && !jobz && N == 32) {
+        static const int c[] = {8, 16};
+        return fill_lanes(batch, c, 2, 2048);
+    }
+    if (dtype == STEQR_F64 && !jobz && N == 16) {
+        static const int c[] = {4, 8};
+        return fill_lanes(batch, c, 2, 1024);
+    }
     if (N == 4) return 4;
     if (N == 8) return dtype == STEQR_F32 ? 2 : 4;
     // double with vectors at 4 lanes (271 against 351 us at 8) needs more
@@ -410,7 +434,7 @@ int syev_plan(int n, int batch, int jobz, int dtype, const steqr_params* prm, Pl
         return 0;
     }
     const int N = padded_order(n < 2 ? 2 : n);
-    if (P == 0) P = syev_default_lanes(dtype, N, jobz);
+    if (P == 0) P = syev_default_lanes(dtype, N, jobz, (long)batch);
     const Table t = dtype == STEQR_F32 ? steqr::table_syev_f32() : steqr::table_syev_f64();
     const Entry* ent = search(t, dtype, N, P, jobz, 1);
     if (!ent) return -10;

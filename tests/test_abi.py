@@ -272,7 +272,7 @@ def test_uninstantiated_lanes_rejected_by_query(st):
 # ---------------------------------------------------------------- dense syev
 
 @pytest.mark.parametrize("n,jobz,dtype,N,P,R", [
-    (1, 1, 0, 4, 4, 1), (4, 1, 0, 4, 4, 1), (5, 1, 0, 8, 2, 4), (16, 1, 0, 16, 4, 4),
+    (1, 1, 0, 4, 4, 1), (4, 1, 0, 4, 4, 1), (5, 1, 0, 8, 4, 2), (16, 1, 0, 16, 4, 4),
     (16, 0, 0, 16, 4, 4), (12, 1, 1, 16, 8, 2), (17, 1, 0, 32, 16, 2), (32, 0, 1, 32, 32, 1),
     (8, 0, 1, 8, 4, 2), (32, 0, 0, 32, 8, 4), (16, 0, 1, 16, 4, 4), (16, 1, 1, 16, 8, 2)])
 def test_syev_default_plans(st, n, jobz, dtype, N, P, R):
@@ -280,6 +280,20 @@ def test_syev_default_plans(st, n, jobz, dtype, N, P, R):
     assert (q["padded_n"], q["lanes_per_problem"], q["rows_per_lane"]) == (N, P, R)
     per_block = q["waves_per_block"] * 64 // P
     assert q["workgroups"] == -(-32768 // per_block)
+
+
+@pytest.mark.parametrize("n,jobz,dtype,cases", [
+    (8, 1, 0, [(1024, 4), (32767, 4), (32768, 4), (65536, 2)]),
+    (16, 1, 0, [(1024, 8), (16384, 8), (32768, 4), (65536, 4)]),
+    (32, 0, 0, [(1024, 16), (16383, 16), (16384, 8)]),
+    (16, 0, 1, [(1024, 8), (16383, 8), (16384, 4), (32768, 4)]),
+    (16, 0, 0, [(1024, 4), (65536, 4)]), (8, 0, 0, [(1024, 2), (65536, 2)])])
+def test_syev_lanes_follow_batch(st, n, jobz, dtype, cases):
+    """The fused dense solver's default lanes per problem: more lanes for
+    batches that would leave SIMDs idle (the tuned choice at the
+    configurations' batches)."""
+    for batch, P in cases:
+        assert st.syev_query(n, batch, jobz, dtype)["lanes_per_problem"] == P, batch
 
 
 def test_syev_argument_errors(st):
