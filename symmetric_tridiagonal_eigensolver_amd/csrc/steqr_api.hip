@@ -53,7 +53,11 @@ int default_lanes(int dtype, int N, int jobz, int band, long batch) {
     // whole rows of Q per lane (5 problems per producer at 8 lanes each);
     // double with eigenvectors measured 1.4% faster at 32 than at 16
     if (N == 128) {
-        if (band == 3) return dtype == STEQR_F32 ? 8 : 32;
+        // float with eigenvectors: whole rows (5 problems per workgroup,
+        // one workgroup per CU) unless the batch leaves most CUs idle, then
+        // half rows at 32 producer lanes (2 per workgroup): 512 matrices
+        // 1.89 against 2.02 ms, 1,024 matrices 3.76 against 2.05
+        if (band == 3) return dtype == STEQR_F32 ? (batch <= 512 ? 32 : 8) : 32;
         // values only in float: 8 lanes once they still give 2,048
         // wavefronts (16,384 matrices: 1.96 ms against 2.53 at 16 lanes)
         if (dtype == STEQR_F32 && !jobz) {
@@ -70,9 +74,16 @@ int default_lanes(int dtype, int N, int jobz, int band, long batch) {
         if (dtype == STEQR_F32) return 16;
         return batch >= 256L * 11 ? 4 : 16;
     }
-    // order 64 without eigenvectors: the producer's algorithm, 8 problems
-    // per wavefront (measured 2.9x (float) and 4x (double) faster than one
-    // problem per wavefront)
+    // order 64 without eigenvectors: the producer's algorithm, 4 to 16
+    // problems per wavefront (measured 2.9x (float) and 4x (double) faster
+    // than one problem per wavefront), the fewest lanes whose launch has
+    // 2,048 wavefronts: 8 at 16,384 matrices; 65,536 matrices 1.18 ms at 4
+    // lanes against 1.42 at 8 (float), 2.89 against 3.15 (double); 4,096
+    // matrices 0.48 at 16 against 0.51 at 8 (float), 0.69 against 0.74
+    if (N == 64 && !jobz && band == 2) {
+        static const int c[] = {4, 8, 16};
+        return fill_lanes(batch, c, 3, 2048);
+    }
     if (N == 64 && !jobz) return 8;
     if (N >= 64) return 64;
     // Orders 8..32 in their default band storage: the lanes per problem

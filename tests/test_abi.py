@@ -74,7 +74,12 @@ def test_version(st):
     (0, 0, 128, [(256, 16), (8192, 16), (16383, 16), (16384, 8)]),
     (1, 0, 128, [(256, 16), (65536, 16)]),
     (1, 1, 64, [(256, 16), (2815, 16), (2816, 4), (16384, 4)]),
-    (0, 1, 64, [(256, 16), (16384, 16)])])
+    (0, 1, 64, [(256, 16), (16384, 16)]),
+    # order 64 without eigenvectors (producer lanes 4, 8, 16); order 128 in
+    # float with eigenvectors (whole rows at 8, half rows at 32)
+    (0, 0, 64, [(1024, 16), (16383, 16), (16384, 8), (32767, 8), (32768, 4)]),
+    (1, 0, 64, [(4096, 16), (16384, 8), (65536, 4)]),
+    (0, 1, 128, [(64, 32), (512, 32), (513, 8), (8192, 8)])])
 def test_query_lanes_follow_batch(st, dtype, jobz, n, cases):
     """Orders 8..32 in their default band storage: the default lanes per
     problem are the fewest whose launch still has the case's wavefront
@@ -96,8 +101,8 @@ def test_query_lanes_follow_batch(st, dtype, jobz, n, cases):
 @pytest.mark.parametrize("n,jobz,dtype,N,P", [
     (1, 1, 0, 4, 4), (4, 1, 0, 4, 4), (5, 1, 0, 8, 4), (8, 0, 0, 8, 1), (12, 1, 1, 12, 4), (12, 0, 1, 16, 1),
     (16, 1, 0, 16, 4), (17, 1, 0, 32, 8), (32, 1, 1, 32, 16), (32, 0, 1, 32, 1), (32, 0, 0, 32, 4), (16, 0, 0, 16, 2), (16, 0, 1, 16, 1),
-    (33, 1, 1, 64, 4), (64, 1, 1, 64, 4), (64, 1, 0, 64, 16), (64, 0, 0, 64, 8),
-    (40, 0, 1, 64, 8), (100, 1, 0, 128, 8), (100, 1, 1, 128, 32), (128, 0, 0, 128, 8),
+    (33, 1, 1, 64, 4), (64, 1, 1, 64, 4), (64, 1, 0, 64, 16), (64, 0, 0, 64, 4),
+    (40, 0, 1, 64, 4), (100, 1, 0, 128, 8), (100, 1, 1, 128, 32), (128, 0, 0, 128, 8),
     (128, 0, 1, 128, 16),
     (129, 1, 0, 256, 64), (256, 1, 1, 256, 64), (200, 0, 0, 256, 64), (256, 0, 1, 256, 64),
     (257, 1, 0, 512, 64), (512, 1, 1, 512, 64), (300, 0, 0, 512, 64), (512, 0, 1, 512, 64)])
