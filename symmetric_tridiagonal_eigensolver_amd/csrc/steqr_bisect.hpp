@@ -11,10 +11,11 @@
 // 64 lanes of a wavefront run 64 independent bisections in lockstep with no
 // exchange at all after the set-up. With G wavefronts per problem every
 // wavefront repeats the (cheap) set-up over the whole band and bisects its
-// own share of the indices; the status sums the shares through LDS. Every bisection takes about the same number of
-// halvings (the interval starts as the Gershgorin interval and ends at a
-// few ulps of ||T||), so lockstep costs little; a lane that has converged
-// is masked off until every lane of the wavefront has.
+// own share of the indices; the status sums the shares through LDS. Every
+// bisection takes about the same number of halvings (the interval starts
+// as the Gershgorin interval and ends at a few ulps of ||T||), so lockstep
+// costs little; a lane that has converged is masked off until every lane
+// of the wavefront has.
 //
 // Set-up per chunk (lane k handles position k): the Gershgorin norm
 // max |e_{k-1}| + |d_k| + |e_k| by a butterfly (NaN-propagating), the exact
