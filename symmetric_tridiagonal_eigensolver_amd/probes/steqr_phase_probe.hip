@@ -102,6 +102,23 @@ extern "C" int steqr_phase_launch(int which, const void* d, const void* e, void*
     return err == hipSuccess ? 0 : (int)err;
 }
 
+// Hardware seeds of the double reciprocal (kind 0) and reciprocal square
+// root (kind 1), one value per thread, for their accuracy against exact
+// results computed on the host.
+__global__ void __launch_bounds__(256) seed_kernel(int kind, const double* x, double* y, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) y[i] = kind == 0 ? __builtin_amdgcn_rcp(x[i]) : __builtin_amdgcn_rsq(x[i]);
+}
+
+extern "C" int steqr_seed_launch(int kind, const double* x, double* y, int n,
+                                 hipStream_t stream) {
+    if (kind < 0 || kind > 1 || x == nullptr || y == nullptr || n < 1) return -1;
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(seed_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, kind, x, y, n);
+    const hipError_t err = hipGetLastError();
+    return err == hipSuccess ? 0 : (int)err;
+}
+
 extern "C" int steqr_latency_launch(int kind, int iters, double* out,
                                     unsigned long long* cycles, hipStream_t stream) {
     if (kind < 0 || kind > 4 || iters < 1 || out == nullptr || cycles == nullptr) return -1;
