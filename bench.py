@@ -221,6 +221,9 @@ def main() -> int:
     ap.add_argument("--workload", default=None,
                     choices=list(W.WORKLOADS) + list(W.DENSE_WORKLOADS))
     ap.add_argument("--jobz", default="V", choices=["V", "N"])
+    ap.add_argument("--batch", type=int, default=0,
+                    help="matrices per launch (0 = the workload's own batch; another batch "
+                         "runs the default launch for that batch, without counter records)")
     ap.add_argument("--lanes", type=int, default=0, help="lanes per problem (0 = default)")
     ap.add_argument("--waves", type=int, default=0, help="waves per workgroup (0 = default)")
     ap.add_argument("--band", type=int, default=0,
@@ -289,9 +292,13 @@ def main() -> int:
     scheme = 1 if args.scheme == "pg" else 0
     prm0 = st.make_params(lanes_per_problem=args.lanes, waves_per_block=args.waves,
                           band_storage=args.band, update_scheme=scheme, method=method)
-    lanes0 = st.steqr_query(w.n, w.batch, int(jobz), 0 if w.dtype == "f32" else 1,
+    if args.batch < 0:
+        print("bench.py: --batch must be positive", file=sys.stderr)
+        return 2
+    nb0 = args.batch or w.batch
+    lanes0 = st.steqr_query(w.n, nb0, int(jobz), 0 if w.dtype == "f32" else 1,
                             prm0)["lanes_per_problem"]
-    d, e = W.make_batch(w, replicate=max(1, 64 // lanes0) if args.replicate else 1)
+    d, e = W.make_batch(w, nb0, replicate=max(1, 64 // lanes0) if args.replicate else 1)
     dev = torch.device("cuda:0")
     td = torch.from_numpy(d).to(dev)
     te = torch.from_numpy(e).to(dev)
@@ -427,7 +434,8 @@ def main() -> int:
     kname = kernel_label(plan, jobz, dtype, family, scheme)
     if flops is not None:
         ach = flops / sec / 1e12
-        ctr = (None if args.replicate
+        # the counter records are per launch of the workload's own batch
+        ctr = (None if args.replicate or nb != w.batch
                else counters_from_profiles(w.name, jobz, family, kname,
                                            record_suffix(bt, scheme, method)))
         roof = {"kernel": kname,
@@ -515,8 +523,12 @@ def run_syev(args, torch, st) -> int:
               file=sys.stderr)
         return 2
     dtype, n, nb = W.DENSE_WORKLOADS[name]
+    if args.batch < 0:
+        print("bench.py: --batch must be positive", file=sys.stderr)
+        return 2
+    nb = args.batch or nb
     jobz = args.jobz == "V"
-    A = W.make_dense(name)
+    A = W.make_dense(name, nb)
     dev = torch.device("cuda:0")
     tA = torch.from_numpy(A).to(dev)
     lam = torch.empty((nb, n), dtype=tA.dtype, device=dev)
