@@ -167,8 +167,12 @@ __global__ void __launch_bounds__(G > 1 ? 64 * G : 256) steqr_bisect_kernel(Kern
     const T widen = T(2) * T(n) * ulp * tns + T(2) * pivmin;
     const T atol = ulp * tns;
     // floor(log2(r)) = e - 1 for r = f 2^e, f in [0.5, 1): exact
-    const int itmax =
+    // (at most 1,024 for a finite band, whose norm is scaled to [0.5, 1);
+    // an infinite entry makes the ratio infinite or NaN, and the bound keeps
+    // the loop finite whatever the exponent instruction returns for those)
+    const int itraw =
         __builtin_amdgcn_frexp_exp(((double)tns + (double)pivmin) / (double)pivmin) + 1;
+    const int itmax = itraw < 1 ? 1 : (itraw > 1100 ? 1100 : itraw);
 
     T bd[REGS ? N : 1], be2[REGS ? N : 1];
     if constexpr (REGS) {

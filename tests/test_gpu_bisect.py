@@ -137,3 +137,20 @@ def test_bisect_several_wavefronts_per_problem(dt, n, lanes):
     g1 = run_bisect(d, e, lanes_per_problem=64)
     assert np.array_equal(g[0].view(np.uint8), g1[0].view(np.uint8))
     assert np.array_equal(g[2], g1[2])
+
+
+@pytest.mark.parametrize("dt", [np.float32, np.float64], ids=["f32", "f64"])
+@pytest.mark.parametrize("n", [2, 4, 16, 64, 128, 256, 512])
+def test_bisect_infinite_entries(n, dt):
+    """Items with +-inf in d or e: the same status and NaN positions as the
+    oracle's bisection."""
+    print("bisect infinite entries", n, dt.__name__, flush=True)
+    nb = 40 if n <= 64 else 12
+    d, e = W.random_batch(n, nb, dt, salt=52)
+    g = np.random.default_rng(n + 7)
+    for b in range(0, nb, 3):
+        if n > 1 and g.random() < 0.5:
+            e[b, int(g.integers(0, n - 1))] = np.inf if g.random() < 0.5 else -np.inf
+        else:
+            d[b, int(g.integers(0, n))] = np.inf if g.random() < 0.5 else -np.inf
+    assert check(d, e, run_bisect(d, e), oracle_bisect(d, e), False) == []

@@ -372,3 +372,24 @@ def test_graded_keeps_relative_accuracy(dt, n, top):
     ref = np.sort(V.sturm_eigvals(d[:64], e[:64]).astype(np.float64), axis=1)
     rel = np.abs(np.sort(g[0][:64].astype(np.float64), axis=1) - ref) / np.abs(ref)
     assert rel.max() <= (2.0 ** -6 if dt == np.float32 else 2.0 ** -30)
+
+
+@pytest.mark.parametrize("dt", [np.float32, np.float64], ids=["f32", "f64"])
+@pytest.mark.parametrize("n", [2, 4, 16, 32, 64, 128, 256])
+@pytest.mark.parametrize("jobz", [True, False], ids=["V", "N"])
+def test_infinite_entries(n, dt, jobz):
+    """Items with +-inf in d or e among ordinary ones: the same status,
+    NaN positions and values as the oracle (the block scaling turns an
+    infinite norm into NaN entries, as on the CPU)."""
+    print("infinite entries", n, dt.__name__, jobz, flush=True)
+    nb = 40 if n <= 64 else 12
+    d, e = W.random_batch(n, nb, dt, salt=51)
+    g = np.random.default_rng(n)
+    for b in range(0, nb, 3):
+        if n > 1 and g.random() < 0.5:
+            e[b, int(g.integers(0, n - 1))] = np.inf if g.random() < 0.5 else -np.inf
+        else:
+            d[b, int(g.integers(0, n))] = np.inf if g.random() < 0.5 else -np.inf
+    gpu = run_gpu(d, e, jobz)
+    o = oracle.steqr(d, e, jobz, threads=8)
+    assert check(d, e, gpu, o, jobz) == []
