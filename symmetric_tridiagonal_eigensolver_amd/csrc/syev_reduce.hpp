@@ -94,14 +94,20 @@ __device__ __forceinline__ void householder_chunk(T (&a)[RA][N], T (&q)[RQ][N], 
                     constexpr int j = k + 1 + decltype(J)::value;
                     x[j] = sx[j];
                 });
-                // reflector of (alpha, x_{k+2..}): scaled 2-norm, NaN-propagating
+                // reflector of (alpha, x_{k+2..}): scaled 2-norm, NaN-propagating;
+                // H = I exactly when the tail x_{k+2..} is zero (tested on the
+                // unscaled entries: a tail far below |alpha|, or an infinite
+                // alpha, scales to squares that vanish but still takes the
+                // reflector, here as in the larfg convention)
                 const T alpha = x[k + 1];
                 T sc = F::abs(alpha);
                 bool hasnan = alpha != alpha;
+                bool tailnz = false;
                 static_for<N - k - 2>([&](auto J) {
                     constexpr int j = k + 2 + decltype(J)::value;
                     sc = F::max(sc, F::abs(x[j]));
                     hasnan = hasnan | (x[j] != x[j]);
+                    tailnz = tailnz | (x[j] != T(0));
                 });
                 sc = hasnan ? F::qnan() : sc;
                 const T inv = (sc == T(0)) ? T(0) : F::rcp(sc);
@@ -112,7 +118,7 @@ __device__ __forceinline__ void householder_chunk(T (&a)[RA][N], T (&q)[RQ][N], 
                     ss = F::fma(y, y, ss);
                 });
                 T tau = T(0), beta = alpha, scal = T(0);
-                if (!(ss == T(0))) {
+                if (tailnz) {
                     const T ya = alpha * inv;
                     const T nrm = sc * F::sqrt_fast(F::fma(ya, ya, ss));
                     beta = -F::copysign(nrm, alpha);

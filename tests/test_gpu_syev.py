@@ -130,3 +130,25 @@ def test_syev_double_vectors_limit():
     import symmetric_tridiagonal_eigensolver_amd as st
     assert st.lib().syev_batched(8, 8, 8, 17, 10, st.STEQR_V, st.STEQR_F64, None) == -4
     assert st.syev_query(32, 10, st.STEQR_N, st.STEQR_F64)["lanes_per_problem"] == 32
+
+
+@pytest.mark.parametrize("dt", [np.float32, np.float64], ids=["f32", "f64"])
+@pytest.mark.parametrize("n", [2, 5, 16, 32])
+@pytest.mark.parametrize("jobz", [True, False], ids=["V", "N"])
+def test_syev_infinite_entries(dt, n, jobz):
+    """Items with +-inf in the lower triangle among ordinary ones: status
+    and NaN positions as the oracle's."""
+    print("syev infinite", dt.__name__, n, jobz, flush=True)
+    if jobz and not _vectors_ok(dt, n):
+        pytest.skip("double with eigenvectors is built up to order 16")
+    A = W.random_symmetric(n, 40, dt, salt=67)
+    g = np.random.default_rng(n + 3)
+    for b in range(0, 40, 4):
+        i = int(g.integers(0, n))
+        j = int(g.integers(0, i + 1))
+        v = np.inf if g.random() < 0.5 else -np.inf
+        A[b, i, j] = v
+        A[b, j, i] = v
+    gpu = run_gpu_syev(A, jobz)
+    o = oracle.syev(A, jobz)
+    assert check_dense(A, gpu, o, jobz) == []
