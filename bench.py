@@ -585,8 +585,9 @@ def run_syev(args, torch, st) -> int:
         flops = float(flops_per_matrix(stats, n, jobz).sum()) + nb * dense_flops_per_matrix(n, jobz)
         ach = flops / sec / 1e12
         peak = PEAK_TFLOPS[dtype]
-        roof = {"kernel": "steqr_chunk_kernel<%s, N=%d, P=%d, %s, dense>"
-                          % ("float" if dtype == "f32" else "double", plan["padded_n"],
+        roof = {"kernel": "steqr_%s_kernel<%s, N=%d, P=%d, %s, dense>"
+                          % ("chunkl" if plan["band_storage"] == 2 else "chunk",
+                             "float" if dtype == "f32" else "double", plan["padded_n"],
                              plan["lanes_per_problem"], "V" if jobz else "N"),
                 "bound": "alu", "achieved": ach, "peak": peak, "unit": "TFLOP/s",
                 "frac": ach / peak, "traffic": None,
@@ -614,6 +615,7 @@ def run_syev(args, torch, st) -> int:
                    "rows_per_lane": plan["rows_per_lane"], "padded_n": plan["padded_n"],
                    "waves_per_block": plan["waves_per_block"],
                    "workgroups": plan["workgroups"],
+                   "band_storage": {1: "registers", 2: "LDS"}[plan["band_storage"]],
                    "inputs": "dense symmetric, lower triangle iid N(0,1), seed 1234"},
         "roofline": roof,
         "hbm": {"algorithmic_bytes_per_launch": bpm * nb,

@@ -197,14 +197,17 @@ int steqr_query(int n, int batch, int jobz, int dtype, const steqr_params *param
  *      eigenvectors)                             -5 batch < 0
  *   -6 jobz invalid       -7 dtype invalid
  *   -10 (_ex) params: update_scheme other than STEQR_EXP, back_transform
- *       set, band_storage other than 0/1, or a lanes_per_problem /
- *       waves_per_block the build does not provide (syev_query lists them)
+ *       set, band_storage other than 0/1/2, or a lanes_per_problem /
+ *       band_storage / waves_per_block the build does not provide
+ *       (syev_query lists them)
  * A positive value is a hipError_t from the launch; n == 0 or batch == 0
  * returns 0 without touching the GPU. */
 #define SYEV_MAX_N 32
-/* Double precision with eigenvectors: rows of A and Q and the band of an
- * order-32 problem do not fit 256 registers per lane. */
-#define SYEV_MAX_N_F64_V 16
+/* Double precision with eigenvectors: the same limit. At order 32 the rows
+ * of A and Q and the replicated band do not fit 256 registers per lane
+ * together, so that order runs with the band in LDS (band_storage 2, the
+ * default there). */
+#define SYEV_MAX_N_F64_V 32
 
 int syev_batched(const void *A, void *lambda, void *Q, int n, int batch, int jobz, int dtype,
                  hipStream_t stream);
@@ -215,7 +218,7 @@ int syev_batched_ex(const void *A, void *lambda, void *Q, int n, int batch, int 
 /* The launch syev_batched_ex would make (outputs as for steqr_query). */
 int syev_query(int n, int batch, int jobz, int dtype, const steqr_params *params,
                int *padded_n, int *lanes_per_problem, int *rows_per_lane,
-               int *waves_per_block, int *workgroups);
+               int *waves_per_block, int *workgroups, int *band_storage);
 
 /* Library version string, e.g. "steqr-mi355x 0.1.0 gfx950". */
 const char *steqr_version(void);

@@ -20,7 +20,7 @@ STEQR_SHIFT_LAPACK, STEQR_SHIFT_CLOSED = 0, 1
 STEQR_METHOD_QR, STEQR_METHOD_BISECT = 0, 1
 STEQR_MAX_N = 512
 SYEV_MAX_N = 32
-SYEV_MAX_N_F64_V = 16
+SYEV_MAX_N_F64_V = 32
 
 
 class steqr_params(ct.Structure):
@@ -63,7 +63,7 @@ _lib.syev_batched_ex.restype = _i
 _lib.syev_batched_ex.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp,
                                  ct.POINTER(steqr_params)]
 _lib.syev_query.restype = _i
-_lib.syev_query.argtypes = [_i, _i, _i, _i, ct.POINTER(steqr_params)] + [ct.POINTER(_i)] * 5
+_lib.syev_query.argtypes = [_i, _i, _i, _i, ct.POINTER(steqr_params)] + [ct.POINTER(_i)] * 6
 
 EXPORTS = ("steqr_batched", "steqr_batched_ex", "steqr_query", "steqr_version",
            "syev_batched", "syev_batched_ex", "syev_query")
@@ -195,13 +195,14 @@ def syev_batched_ex(A, lam, Q, n: int, batch: int, jobz: int, dtype: int, stream
 
 def syev_query(n: int, batch: int, jobz: int, dtype: int,
                params: Optional[steqr_params] = None) -> dict:
-    outs = [ct.c_int(0) for _ in range(5)]
+    outs = [ct.c_int(0) for _ in range(6)]
     rc = _lib.syev_query(int(n), int(batch), int(jobz), int(dtype),
                          ct.byref(params) if params is not None else None,
                          *[ct.byref(o) for o in outs])
     if rc != 0:
         raise SteqrError(rc, "syev_query")
-    keys = ("padded_n", "lanes_per_problem", "rows_per_lane", "waves_per_block", "workgroups")
+    keys = ("padded_n", "lanes_per_problem", "rows_per_lane", "waves_per_block", "workgroups",
+            "band_storage")
     return dict(zip(keys, (o.value for o in outs)))
 
 

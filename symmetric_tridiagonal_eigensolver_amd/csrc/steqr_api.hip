@@ -409,7 +409,7 @@ int syev_default_lanes(int dtype, int N, int jobz, long batch) {
     // double with vectors at 4 lanes (271 against 351 us at 8) needs more
     // than 256 registers per lane and is not built
     if (N == 16) return (dtype == STEQR_F64 && jobz) ? 8 : 4;
-    if (dtype == STEQR_F64) return 32;  // values only (no order-32 double with vectors)
+    if (dtype == STEQR_F64) return 32;  // with vectors: the band in LDS
     return jobz ? 16 : 8;
 }
 
@@ -419,13 +419,14 @@ int syev_plan(int n, int batch, int jobz, int dtype, const steqr_params* prm, Pl
     if (batch < 0) return -5;
     if (jobz != STEQR_N && jobz != STEQR_V) return -6;
     if (dtype != STEQR_F32 && dtype != STEQR_F64) return -7;
-    int waves = 4, P = 0;
+    int waves = 4, P = 0, band = 0;
     if (prm) {
         if (prm->update_scheme != STEQR_EXP) return -10;
         if (prm->shift != STEQR_SHIFT_LAPACK && prm->shift != STEQR_SHIFT_CLOSED) return -10;
         if (prm->back_transform != 0) return -10;
         if (prm->method != STEQR_METHOD_QR) return -10;
-        if (prm->band_storage != 0 && prm->band_storage != 1) return -10;
+        if (prm->band_storage < 0 || prm->band_storage > 2) return -10;
+        band = prm->band_storage;
         if (prm->no_sort != 0 && prm->no_sort != 1) return -10;
         if (prm->waves_per_block != 0) {
             if (prm->waves_per_block != 1 && prm->waves_per_block != 2 && prm->waves_per_block != 4)
@@ -447,7 +448,9 @@ int syev_plan(int n, int batch, int jobz, int dtype, const steqr_params* prm, Pl
     const int N = padded_order(n < 2 ? 2 : n);
     if (P == 0) P = syev_default_lanes(dtype, N, jobz, (long)batch);
     const Table t = dtype == STEQR_F32 ? steqr::table_syev_f32() : steqr::table_syev_f64();
-    const Entry* ent = search(t, dtype, N, P, jobz, 1);
+    // the band in registers where that variant is built, else in LDS
+    const Entry* ent = band != 2 ? search(t, dtype, N, P, jobz, 1) : nullptr;
+    if (!ent && band != 1) ent = search(t, dtype, N, P, jobz, 2);
     if (!ent) return -10;
     while (waves > 1 && (long)waves * ent->lds_per_wave > 65536) waves /= 2;
     p.waves = waves;
@@ -455,7 +458,7 @@ int syev_plan(int n, int batch, int jobz, int dtype, const steqr_params* prm, Pl
     p.N = N;
     p.P = P;
     p.R = N / P;
-    p.band = 1;
+    p.band = ent->band;
     const int per_block = waves * (64 / P);
     p.grid = batch > 0 ? (int)(((long)batch + per_block - 1) / per_block) : 0;
     *out = p;
@@ -466,7 +469,7 @@ int syev_plan(int n, int batch, int jobz, int dtype, const steqr_params* prm, Pl
 
 extern "C" int syev_query(int n, int batch, int jobz, int dtype, const steqr_params* params,
                           int* padded_n, int* lanes_per_problem, int* rows_per_lane,
-                          int* waves_per_block, int* workgroups) {
+                          int* waves_per_block, int* workgroups, int* band_storage) {
     Plan p;
     const int rc = syev_plan(n, batch, jobz, dtype, params, &p);
     if (rc != 0) return rc;
@@ -475,6 +478,7 @@ extern "C" int syev_query(int n, int batch, int jobz, int dtype, const steqr_par
     if (rows_per_lane) *rows_per_lane = p.R;
     if (waves_per_block) *waves_per_block = p.waves;
     if (workgroups) *workgroups = p.grid;
+    if (band_storage) *band_storage = p.band;
     return 0;
 }
 

@@ -232,7 +232,7 @@ __global__ void __launch_bounds__(256) steqr_chunk_kernel(KernelArgs args) {
                 q[i][j] = (WANTQ & (row == j)) ? T(1) : T(0);
             });
         });
-        householder_chunk<T, N, P, RA, WANTQ, RQ>(a, q, d, e, sd, se, n, r);
+        householder_chunk<T, N, P, RA, WANTQ, RQ>(a, q, d, e, sd, se, nullptr, n, r);
     } else {
         static_for<N>([&](auto I) {
             constexpr int p = decltype(I)::value;

@@ -133,9 +133,16 @@ __device__ __forceinline__ T chunk_max(T v) {
     return v;
 }
 
-template <typename T, int N, int P, bool WANTQ, bool PG>
+// DENSE: the fused dense eigensolver, as in the chunked kernel with the band
+// in registers: the wavefront's dense matrices are staged in LDS, each lane
+// reduces its N/P consecutive rows of A with the identity rows of Q it
+// holds, and the reduction leaves T's bands in the chunk's band slots, where
+// the solve below starts from them.
+template <typename T, int N, int P, bool WANTQ, bool PG, bool DENSE = false>
 __global__ void __launch_bounds__(256) steqr_chunkl_kernel(KernelArgs args) {
     static_assert(P >= 2 && P <= N && (N % P) == 0 && (64 % P) == 0, "2 <= P <= N, P | N");
+    static_assert(!DENSE || (64 / P) * N * N <= 64 * (N + 1),
+                  "dense: the wavefront's matrices fit the staging area");
     static_assert(N <= 32, "position masks are 32 bits");
     constexpr int CH = 64 / P;
     constexpr int K = N / P;                       // positions per lane
@@ -170,19 +177,72 @@ __global__ void __launch_bounds__(256) steqr_chunkl_kernel(KernelArgs args) {
     T* const stage = reinterpret_cast<T*>(ws + S::band_bytes + S::rank_bytes);
 
     // ---------------------------------------------------------------- load
-    static_for<K>([&](auto KK) {
-        constexpr int k = decltype(KK)::value;
-        const int p = r + k * P;
-        const int pc = p < n ? p : n - 1;
-        const T v = gd[pb * n + pc];
-        sd[p] = (live & (p < n)) ? v : T(0);
-        T w = T(0);
-        if (n > 1) {
-            const int ec = p < n - 1 ? p : n - 2;
-            w = ge[pb * (n - 1) + ec];
-        }
-        se[p] = (live & (p < n - 1)) ? w : T(0);
-    });
+    // lane r of a chunk holds rows r, r+P, r+2P, ... of Q, so that the
+    // chunk's lanes hold P consecutive rows in each row slice i
+    T q[RQ][N];
+    if constexpr (DENSE) {
+        // one coalesced copy of the wavefront's matrices into the staging
+        // area, each lane's rows of A (strict upper triangle mirrored from
+        // the lower one) and identity rows of Q, then the reduction
+        constexpr int RA = N / P;
+        const T* __restrict__ ga = static_cast<const T*>(args.a);
+        const int nn = n * n;
+        const long first = ((long)blockIdx.x * (blockDim.x >> 6) + wave) * CH;
+        const int nprob = (long)args.batch - first < CH ? (int)((long)args.batch - first) : CH;
+        const bool avec = ((nn & 3) == 0) & ((reinterpret_cast<uintptr_t>(ga) & 15) == 0);
+        copy_block<T, CH * N * N>(stage, ga + first * nn, nprob * nn, lane, avec);
+        __builtin_amdgcn_wave_barrier();
+        const T* const st = stage + chunk * nn;
+        T a[RA][N];
+        static_for<RA>([&](auto II) {
+            constexpr int i = decltype(II)::value;
+            const int row = r * RA + i;
+            const bool in = live & (row < n);
+            static_for<N>([&](auto J) {
+                constexpr int j = decltype(J)::value;
+                const bool use = in & (j < n);
+                const int idx = use ? ((j <= row) ? row * n + j : j * n + row) : 0;
+                const T v = st[idx];
+                a[i][j] = use ? v : T(0);
+            });
+        });
+        static_for<RQ>([&](auto II) {
+            constexpr int i = decltype(II)::value;
+            const int row = i * P + r;
+            static_for<N>([&](auto J) {
+                constexpr int j = decltype(J)::value;
+                q[i][j] = (WANTQ & (row == j)) ? T(1) : T(0);
+            });
+        });
+        // w goes through the chunk's e slot, e through its share of the
+        // staging area (whose matrices are in registers now)
+        T* const ez = stage + chunk * S::SLOT;
+        T d0[N], e0[N];  // not used: the band stays in LDS
+        householder_chunk<T, N, P, RA, WANTQ, RQ, true>(a, q, d0, e0, sd, se, ez, n, r);
+        // the band in its slots, zero beyond the order as the tridiagonal
+        // load leaves it
+        static_for<K>([&](auto KK) {
+            constexpr int k = decltype(KK)::value;
+            const int p = r + k * P;
+            const T dv = sd[p];
+            sd[p] = (p < n) ? dv : T(0);
+            se[p] = ez[p];
+        });
+    } else {
+        static_for<K>([&](auto KK) {
+            constexpr int k = decltype(KK)::value;
+            const int p = r + k * P;
+            const int pc = p < n ? p : n - 1;
+            const T v = gd[pb * n + pc];
+            sd[p] = (live & (p < n)) ? v : T(0);
+            T w = T(0);
+            if (n > 1) {
+                const int ec = p < n - 1 ? p : n - 2;
+                w = ge[pb * (n - 1) + ec];
+            }
+            se[p] = (live & (p < n - 1)) ? w : T(0);
+        });
+    }
     __builtin_amdgcn_wave_barrier();
     M zeromask;
     {
@@ -194,10 +254,9 @@ __global__ void __launch_bounds__(256) steqr_chunkl_kernel(KernelArgs args) {
         });
         zeromask = chunk_or<P>(part);
     }
-    // lane r of a chunk holds rows r, r+P, r+2P, ... of Q, so that the
-    // chunk's lanes hold P consecutive rows in each row slice i
-    T q[RQ][N];
-    if (WANTQ && args.back_transform) {
+    if constexpr (DENSE) {
+        // Q holds the reduction's H_0 ... H_{n-2}
+    } else if (WANTQ && args.back_transform) {
         // back-transformation [algo, eigenvector accumulation]: the rows of
         // the caller's basis instead of the identity
         const bool vec = (n == N) & ((reinterpret_cast<uintptr_t>(gq) & 15) == 0);

@@ -50,6 +50,12 @@ hipError_t launch_chunk(const KernelArgs& args, int grid, int block, hipStream_t
     { DT, N, P, Q, 1, (int)Smem<T, N, P, (Q) != 0, true>::bytes_per_wave, \
       &launch_chunk<T, N, P, (Q) != 0, false, true> }
 
+// The fused dense solver with the band in LDS (where the replicated band
+// would not fit the register file next to the rows of A and Q).
+#define STEQR_SYEV_LENTRY(DT, T, N, P, Q) \
+    { DT, N, P, Q, 2, (int)SmemL<T, N, P>::bytes_per_wave, \
+      &launch_chunkl<T, N, P, (Q) != 0, false, true> }
+
 // One problem per wavefront (P = 64).
 template <typename T, int N, bool WANTQ, bool PG>
 hipError_t launch_wave(const KernelArgs& args, int grid, int block, hipStream_t stream) {
@@ -64,11 +70,11 @@ hipError_t launch_wave(const KernelArgs& args, int grid, int block, hipStream_t 
       &launch_wave<T, N, (Q) != 0, STEQR_INST_PG != 0> }
 
 // Chunked, band in LDS.
-template <typename T, int N, int P, bool WANTQ, bool PG>
+template <typename T, int N, int P, bool WANTQ, bool PG, bool DENSE = false>
 hipError_t launch_chunkl(const KernelArgs& args, int grid, int block, hipStream_t stream) {
     const size_t lds = (size_t)(block / 64) * SmemL<T, N, P>::bytes_per_wave;
-    hipLaunchKernelGGL((steqr_chunkl_kernel<T, N, P, WANTQ, PG>), dim3(grid), dim3(block), lds,
-                       stream, args);
+    hipLaunchKernelGGL((steqr_chunkl_kernel<T, N, P, WANTQ, PG, DENSE>), dim3(grid), dim3(block),
+                       lds, stream, args);
     return hipGetLastError();
 }
 

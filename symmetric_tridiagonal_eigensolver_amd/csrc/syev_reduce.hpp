@@ -66,13 +66,19 @@ __device__ __forceinline__ T chunk_sum(T v) {
 }
 
 // Reduce the chunk's matrix (a: the lane's RA rows, row = r*RA + i) to
-// tridiagonal form: d[0..N), e[0..N) receive T's bands (zero beyond n), and
-// with WANTQ q (the same rows of Q, the identity on entry) receives
-// H_0 H_1 ... H_{n-2}. sx and sw are two chunk-private LDS vectors of N
-// elements. a is destroyed.
-template <typename T, int N, int P, int RA, bool WANTQ, int RQ>
+// tridiagonal form. With WANTQ the lane's rows of Q (the identity rows on
+// entry, in any assignment of rows to lanes) receive H_0 H_1 ... H_{n-2}.
+// sx and sw are two chunk-private LDS vectors of N elements. d[0..N) and
+// e[0..N) receive T's bands (zero beyond n); with BAND_LDS they stay in LDS
+// instead, so that they take no registers while the rows of A and Q do: sx
+// then holds the diagonal on return (positions n.. unspecified; step k
+// publishes row k from position k on, so sx[k] is never written again) and
+// se, a third such vector, the subdiagonal (zero from position n-1 on),
+// stored by the chunk's first lane; d and e are not touched. a is
+// destroyed.
+template <typename T, int N, int P, int RA, bool WANTQ, int RQ, bool BAND_LDS = false>
 __device__ __forceinline__ void householder_chunk(T (&a)[RA][N], T (&q)[RQ][N], T (&d)[N],
-                                                  T (&e)[N], T* sx, T* sw, int n, int r) {
+                                                  T (&e)[N], T* sx, T* sw, T* se, int n, int r) {
     using F = Fp<T>;
     static_assert(RA * P == N, "the chunk's lanes hold exactly N rows");
     static_for<N>([&](auto K) {
@@ -85,8 +91,11 @@ __device__ __forceinline__ void householder_chunk(T (&a)[RA][N], T (&q)[RQ][N], 
             });
         }
         __builtin_amdgcn_wave_barrier();
-        d[k] = (k < n) ? sx[k] : T(0);
-        e[k] = T(0);
+        if constexpr (!BAND_LDS) {
+            d[k] = (k < n) ? sx[k] : T(0);
+            e[k] = T(0);
+        }
+        T ek = T(0);
         if constexpr (k + 1 < N) {
             if (k + 1 < n) {  // uniform: n is the same for every problem
                 T x[N];
@@ -125,70 +134,173 @@ __device__ __forceinline__ void householder_chunk(T (&a)[RA][N], T (&q)[RQ][N], 
                     tau = (beta - alpha) * F::rcp(beta);
                     scal = F::rcp(alpha - beta);
                 }
-                e[k] = beta;
+                ek = beta;
+                if constexpr (!BAND_LDS) e[k] = beta;
                 if (tau != T(0)) {
-                    T v[N];
-                    v[k + 1] = T(1);
-                    static_for<N - k - 2>([&](auto J) {
-                        constexpr int j = k + 2 + decltype(J)::value;
-                        v[j] = x[j] * scal;
-                    });
-                    // p = tau A v on the lane's rows (rows <= k are done: 0)
-                    T p[RA], vr[RA];
-                    T part = T(0);
-                    static_for<RA>([&](auto II) {
-                        constexpr int i = decltype(II)::value;
-                        const int row = r * RA + i;
-                        T s = a[i][k + 1];
+                    // short of registers: double at order 32 with vectors
+                    constexpr bool LIGHT = sizeof(T) == 8 && N >= 32 && WANTQ;
+                    constexpr int WT = 8;
+                    if constexpr (!LIGHT) {
+                        T v[N];
+                        v[k + 1] = T(1);
                         static_for<N - k - 2>([&](auto J) {
                             constexpr int j = k + 2 + decltype(J)::value;
-                            s = F::fma(a[i][j], v[j], s);
+                            v[j] = x[j] * scal;
                         });
-                        p[i] = (row > k) ? tau * s : T(0);
-                        const T xr = sx[row];
-                        vr[i] = (row == k + 1) ? T(1) : ((row > k + 1) ? xr * scal : T(0));
-                        part = F::fma(p[i], vr[i], part);
-                    });
-                    const T pv = chunk_sum<P>(part);
-                    const T half = tau * pv * T(0.5);
-                    T w[RA];
-                    static_for<RA>([&](auto II) {
-                        constexpr int i = decltype(II)::value;
-                        w[i] = F::fma(-half, vr[i], p[i]);
-                        sw[r * RA + i] = w[i];
-                    });
-                    __builtin_amdgcn_wave_barrier();
-                    T wv[N];
-                    static_for<N - k - 1>([&](auto J) {
-                        constexpr int j = k + 1 + decltype(J)::value;
-                        wv[j] = sw[j];
-                    });
-                    // A <- A - v w^T - w v^T on the trailing columns
-                    static_for<RA>([&](auto II) {
-                        constexpr int i = decltype(II)::value;
-                        static_for<N - k - 1>([&](auto J) {
-                            constexpr int j = k + 1 + decltype(J)::value;
-                            a[i][j] = F::fma(-w[i], v[j], F::fma(-vr[i], wv[j], a[i][j]));
-                        });
-                    });
-                    // Q <- Q H_k, row by row
-                    if constexpr (WANTQ) {
-                        static_for<RQ>([&](auto II) {
+                        // p = tau A v on the lane's rows (rows <= k are done: 0)
+                        T p[RA], vr[RA];
+                        T part = T(0);
+                        static_for<RA>([&](auto II) {
                             constexpr int i = decltype(II)::value;
-                            T t = q[i][k + 1];
+                            const int row = r * RA + i;
+                            T s = a[i][k + 1];
                             static_for<N - k - 2>([&](auto J) {
                                 constexpr int j = k + 2 + decltype(J)::value;
-                                t = F::fma(q[i][j], v[j], t);
+                                s = F::fma(a[i][j], v[j], s);
                             });
-                            t = tau * t;
+                            p[i] = (row > k) ? tau * s : T(0);
+                            const T xr = sx[row];
+                            vr[i] = (row == k + 1) ? T(1) : ((row > k + 1) ? xr * scal : T(0));
+                            part = F::fma(p[i], vr[i], part);
+                        });
+                        const T pv = chunk_sum<P>(part);
+                        const T half = tau * pv * T(0.5);
+                        T w[RA];
+                        static_for<RA>([&](auto II) {
+                            constexpr int i = decltype(II)::value;
+                            w[i] = F::fma(-half, vr[i], p[i]);
+                            sw[r * RA + i] = w[i];
+                        });
+                        __builtin_amdgcn_wave_barrier();
+                        T wv[N];
+                        static_for<N - k - 1>([&](auto J) {
+                            constexpr int j = k + 1 + decltype(J)::value;
+                            wv[j] = sw[j];
+                        });
+                        // A <- A - v w^T - w v^T on the trailing columns
+                        static_for<RA>([&](auto II) {
+                            constexpr int i = decltype(II)::value;
                             static_for<N - k - 1>([&](auto J) {
                                 constexpr int j = k + 1 + decltype(J)::value;
-                                q[i][j] = F::fma(-t, v[j], q[i][j]);
+                                a[i][j] = F::fma(-w[i], v[j], F::fma(-vr[i], wv[j], a[i][j]));
                             });
+                        });
+                        // Q <- Q H_k, row by row
+                        if constexpr (WANTQ) {
+                            static_for<RQ>([&](auto II) {
+                                constexpr int i = decltype(II)::value;
+                                T t = q[i][k + 1];
+                                static_for<N - k - 2>([&](auto J) {
+                                    constexpr int j = k + 2 + decltype(J)::value;
+                                    t = F::fma(q[i][j], v[j], t);
+                                });
+                                t = tau * t;
+                                static_for<N - k - 1>([&](auto J) {
+                                    constexpr int j = k + 1 + decltype(J)::value;
+                                    q[i][j] = F::fma(-t, v[j], q[i][j]);
+                                });
+                            });
+                        }
+                    } else {
+                        // The same arithmetic with v_j = x_j scal formed
+                        // again from sx (row k stays published until the
+                        // step ends) WT columns at a time, so that neither v
+                        // nor w occupies N registers next to the rows of A
+                        // and Q: the dot products a_i.v and q_i.v in one pass,
+                        // the rank-2 update of A and Q <- Q H_k in a second.
+                        constexpr int NT = (N - k - 1 + WT - 1) / WT;
+                        T sa[RA], tq[RQ];
+                        static_for<RA>([&](auto II) {
+                            sa[decltype(II)::value] = a[decltype(II)::value][k + 1];
+                        });
+                        static_for<RQ>([&](auto II) {
+                            tq[decltype(II)::value] = q[decltype(II)::value][k + 1];
+                        });
+                        static_for<NT>([&](auto TT) {
+                            constexpr int j0 = k + 1 + decltype(TT)::value * WT;
+                            constexpr int nj = (N - j0 < WT) ? N - j0 : WT;
+                            T vt[WT];
+                            static_for<nj>([&](auto J) {
+                                constexpr int j = j0 + decltype(J)::value;
+                                if constexpr (j > k + 1) vt[decltype(J)::value] = sx[j] * scal;
+                            });
+                            static_for<RA>([&](auto II) {
+                                constexpr int i = decltype(II)::value;
+                                static_for<nj>([&](auto J) {
+                                    constexpr int j = j0 + decltype(J)::value;
+                                    if constexpr (j > k + 1)
+                                        sa[i] = F::fma(a[i][j], vt[decltype(J)::value], sa[i]);
+                                });
+                            });
+                            if constexpr (WANTQ) {
+                                static_for<RQ>([&](auto II) {
+                                    constexpr int i = decltype(II)::value;
+                                    static_for<nj>([&](auto J) {
+                                        constexpr int j = j0 + decltype(J)::value;
+                                        if constexpr (j > k + 1)
+                                            tq[i] = F::fma(q[i][j], vt[decltype(J)::value], tq[i]);
+                                    });
+                                });
+                            }
+                            __builtin_amdgcn_wave_barrier();
+                        });
+                        T p[RA], vr[RA];
+                        T part = T(0);
+                        static_for<RA>([&](auto II) {
+                            constexpr int i = decltype(II)::value;
+                            const int row = r * RA + i;
+                            p[i] = (row > k) ? tau * sa[i] : T(0);
+                            const T xr = sx[row];
+                            vr[i] = (row == k + 1) ? T(1) : ((row > k + 1) ? xr * scal : T(0));
+                            part = F::fma(p[i], vr[i], part);
+                        });
+                        const T pv = chunk_sum<P>(part);
+                        const T half = tau * pv * T(0.5);
+                        T w[RA];
+                        static_for<RA>([&](auto II) {
+                            constexpr int i = decltype(II)::value;
+                            w[i] = F::fma(-half, vr[i], p[i]);
+                            sw[r * RA + i] = w[i];
+                        });
+                        T t[RQ];
+                        static_for<RQ>([&](auto II) {
+                            t[decltype(II)::value] = tau * tq[decltype(II)::value];
+                        });
+                        __builtin_amdgcn_wave_barrier();
+                        static_for<NT>([&](auto TT) {
+                            constexpr int j0 = k + 1 + decltype(TT)::value * WT;
+                            constexpr int nj = (N - j0 < WT) ? N - j0 : WT;
+                            T vt[WT], wv[WT];
+                            static_for<nj>([&](auto J) {
+                                constexpr int j = j0 + decltype(J)::value;
+                                vt[decltype(J)::value] = (j == k + 1) ? T(1) : sx[j] * scal;
+                                wv[decltype(J)::value] = sw[j];
+                            });
+                            static_for<RA>([&](auto II) {
+                                constexpr int i = decltype(II)::value;
+                                static_for<nj>([&](auto J) {
+                                    constexpr int jj = decltype(J)::value;
+                                    a[i][j0 + jj] = F::fma(-w[i], vt[jj],
+                                                           F::fma(-vr[i], wv[jj], a[i][j0 + jj]));
+                                });
+                            });
+                            if constexpr (WANTQ) {
+                                static_for<RQ>([&](auto II) {
+                                    constexpr int i = decltype(II)::value;
+                                    static_for<nj>([&](auto J) {
+                                        constexpr int jj = decltype(J)::value;
+                                        q[i][j0 + jj] = F::fma(-t[i], vt[jj], q[i][j0 + jj]);
+                                    });
+                                });
+                            }
+                            __builtin_amdgcn_wave_barrier();
                         });
                     }
                 }
             }
+        }
+        if constexpr (BAND_LDS) {
+            if (r == 0) se[k] = ek;
         }
         // the next step's publish overwrites sx: keep this step's reads first
         __builtin_amdgcn_wave_barrier();

@@ -279,10 +279,13 @@ def test_uninstantiated_lanes_rejected_by_query(st):
 @pytest.mark.parametrize("n,jobz,dtype,N,P,R", [
     (1, 1, 0, 4, 4, 1), (4, 1, 0, 4, 4, 1), (5, 1, 0, 8, 4, 2), (16, 1, 0, 16, 4, 4),
     (16, 0, 0, 16, 4, 4), (12, 1, 1, 16, 8, 2), (17, 1, 0, 32, 16, 2), (32, 0, 1, 32, 32, 1),
-    (8, 0, 1, 8, 4, 2), (32, 0, 0, 32, 8, 4), (16, 0, 1, 16, 4, 4), (16, 1, 1, 16, 8, 2)])
+    (8, 0, 1, 8, 4, 2), (32, 0, 0, 32, 8, 4), (16, 0, 1, 16, 4, 4), (16, 1, 1, 16, 8, 2),
+    (32, 1, 1, 32, 32, 1), (20, 1, 1, 32, 32, 1)])
 def test_syev_default_plans(st, n, jobz, dtype, N, P, R):
     q = st.syev_query(n, 32768, jobz, dtype)
     assert (q["padded_n"], q["lanes_per_problem"], q["rows_per_lane"]) == (N, P, R)
+    # the band in registers except for double with vectors at order 32
+    assert q["band_storage"] == (2 if (dtype, jobz, N) == (1, 1, 32) else 1)
     per_block = q["waves_per_block"] * 64 // P
     assert q["workgroups"] == -(-32768 // per_block)
 
@@ -305,7 +308,7 @@ def test_syev_argument_errors(st):
     L = st.lib()
     # validation happens before any launch (the pointers are not device memory)
     assert L.syev_batched(8, 8, 8, 33, 10, 1, 0, None) == -4
-    assert L.syev_batched(8, 8, 8, 17, 10, 1, 1, None) == -4   # double with vectors: n <= 16
+    assert L.syev_batched(8, 8, 8, 33, 10, 1, 1, None) == -4   # double with vectors: n <= 32
     assert L.syev_batched(8, 8, 8, -1, 10, 1, 0, None) == -4
     assert L.syev_batched(8, 8, 8, 16, -1, 1, 0, None) == -5
     assert L.syev_batched(8, 8, 8, 16, 10, 2, 0, None) == -6
@@ -321,6 +324,12 @@ def test_syev_argument_errors(st):
                 st.make_params(band_storage=2), st.make_params(lanes_per_problem=64),
                 st.make_params(waves_per_block=3), st.make_params(shift=2)):
         assert L.syev_batched_ex(8, 8, 8, 16, 10, 1, 0, None, None, ctypes.byref(prm)) == -10
+    # band storage: 1 or 2 where that variant is built
+    p1, p2, p3 = (st.make_params(band_storage=b) for b in (1, 2, 3))
+    assert L.syev_batched_ex(8, 8, 8, 32, 10, 1, 1, None, None, ctypes.byref(p1)) == -10
+    assert L.syev_batched_ex(8, 8, 8, 32, 10, 1, 1, None, None, ctypes.byref(p3)) == -10
+    assert st.syev_query(32, 10, 1, 1, p2)["band_storage"] == 2
+    assert st.syev_query(16, 10, 1, 0, p1)["band_storage"] == 1
     # the closed-form shift is accepted
     assert st.syev_query(16, 10, 1, 0, st.make_params(shift=st.STEQR_SHIFT_CLOSED))["padded_n"] == 16
 

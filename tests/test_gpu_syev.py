@@ -22,7 +22,8 @@ def _gpu():
 
 
 def _vectors_ok(dt, n: int) -> bool:
-    """Double precision with eigenvectors is built up to order 16."""
+    """Double precision with eigenvectors is built up to SYEV_MAX_N_F64_V
+    (order 32, the last with the band in LDS)."""
     import symmetric_tridiagonal_eigensolver_amd as st
     return dt != np.float64 or n <= st.SYEV_MAX_N_F64_V
 
@@ -35,7 +36,8 @@ CASES = [
     (np.float32, 4, 4, False), (np.float32, 8, 2, False), (np.float32, 16, 4, False),
     (np.float32, 11, 4, False), (np.float32, 32, 16, False),
     (np.float64, 4, 4, True), (np.float64, 8, 4, True), (np.float64, 16, 8, True),
-    (np.float64, 12, 8, True),
+    (np.float64, 12, 8, True), (np.float64, 32, 32, True), (np.float64, 27, 32, True),
+    (np.float64, 17, 32, True),
     (np.float64, 4, 4, False), (np.float64, 8, 4, False), (np.float64, 16, 8, False),
     (np.float64, 32, 32, False), (np.float64, 21, 32, False),
     (np.float32, 8, 1, False), (np.float32, 16, 2, False), (np.float32, 14, 2, False),
@@ -125,11 +127,15 @@ def test_syev_workload_batches(dt, n, shift):
 
 
 def test_syev_double_vectors_limit():
-    """Double precision with eigenvectors above order 16 is rejected (-4)
-    before any launch; values only run up to order 32."""
+    """Double precision with eigenvectors above order 32 is rejected (-4)
+    before any launch; at order 32 it runs with the band in LDS, values only
+    with the band in registers."""
     import symmetric_tridiagonal_eigensolver_amd as st
-    assert st.lib().syev_batched(8, 8, 8, 17, 10, st.STEQR_V, st.STEQR_F64, None) == -4
-    assert st.syev_query(32, 10, st.STEQR_N, st.STEQR_F64)["lanes_per_problem"] == 32
+    assert st.lib().syev_batched(8, 8, 8, 33, 10, st.STEQR_V, st.STEQR_F64, None) == -4
+    q = st.syev_query(32, 10, st.STEQR_N, st.STEQR_F64)
+    assert (q["lanes_per_problem"], q["band_storage"]) == (32, 1)
+    q = st.syev_query(17, 10, st.STEQR_V, st.STEQR_F64)
+    assert (q["lanes_per_problem"], q["band_storage"]) == (32, 2)
 
 
 @pytest.mark.parametrize("dt", [np.float32, np.float64], ids=["f32", "f64"])
