@@ -49,7 +49,7 @@ EXTRA_SETS = {
              "Fused dense syev (reduction + tridiagonal solve + back-transformation)",
              ["s_f32_n8:V:syev", "s_f32_n8:N:syev", "s_f32_n16:V:syev", "s_f32_n16:N:syev",
               "s_f32_n32:V:syev", "s_f32_n32:N:syev", "s_f64_n16:V:syev", "s_f64_n16:N:syev",
-              "s_f64_n32:N:syev"]),
+              "s_f64_n32:V:syev", "s_f64_n32:N:syev"]),
     "pg": ("steqr_pg_step.md", "The Parlett-Gray form of the chase step",
            ["c2_f32_n16:V:pg", "c3_f64_n16:V:pg", "c4_f64_n32:V:pg", "c5_f64_n64:V:pg"]),
     "bisect": ("steqr_bisect_values.md", "Values-only bisection (steqr_bisect_kernel)",
