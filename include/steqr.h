@@ -205,8 +205,8 @@ int steqr_query(int n, int batch, int jobz, int dtype, const steqr_params *param
 #define SYEV_MAX_N 32
 /* Double precision with eigenvectors: the same limit. At order 32 the rows
  * of A and Q and the replicated band do not fit 256 registers per lane
- * together, so that order runs with the band in LDS (band_storage 2, the
- * default there). */
+ * together, so double at order 32 runs with the band in LDS by default
+ * (band_storage 2; values only also with 1). */
 #define SYEV_MAX_N_F64_V 32
 
 int syev_batched(const void *A, void *lambda, void *Q, int n, int batch, int jobz, int dtype,

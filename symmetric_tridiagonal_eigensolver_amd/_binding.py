@@ -208,7 +208,7 @@ def syev_query(n: int, batch: int, jobz: int, dtype: int,
 
 def syev(A, jobz: bool = True, *, info: bool = False, sort: bool = True,
          max_sweeps_per_n: int = 0, lanes_per_problem: int = 0, waves_per_block: int = 0,
-         shift: int = 0, stream=None):
+         shift: int = 0, band_storage: int = 0, stream=None):
     """Eigen-decomposition of a batch of dense symmetric matrices A (batch, n, n)
     held in a device tensor (lower triangle read). Returns (lam, Q or None[, info])
     as device tensors; the work is enqueued on `stream` and not synchronised."""
@@ -221,7 +221,8 @@ def syev(A, jobz: bool = True, *, info: bool = False, sort: bool = True,
     lam = torch.empty((batch, n), dtype=A.dtype, device=A.device)
     Q = torch.empty_like(A) if jobz else None
     inf = torch.empty((batch,), dtype=torch.int32, device=A.device) if info else None
-    prm = make_params(max_sweeps_per_n, sort, lanes_per_problem, waves_per_block, 0, 0, shift)
+    prm = make_params(max_sweeps_per_n, sort, lanes_per_problem, waves_per_block, band_storage, 0,
+                      shift)
     rc = syev_batched_ex(A, lam, Q, n, batch, STEQR_V if jobz else STEQR_N, dtype_code(A.dtype),
                          stream, inf, prm)
     if rc != 0:

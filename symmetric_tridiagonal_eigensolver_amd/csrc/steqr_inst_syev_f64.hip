@@ -10,7 +10,7 @@ static const Entry kEntries[] = {
     // registers need more than 256 registers per lane (rows of A and Q plus
     // the replicated band): order 32 with eigenvectors keeps the band in LDS
     E(4, 4, 1), E(8, 4, 1), E(16, 8, 1), EL(32, 32, 1),
-    E(4, 4, 0), E(8, 4, 0), E(8, 2, 0), E(16, 8, 0), E(16, 4, 0), E(32, 32, 0),
+    E(4, 4, 0), E(8, 4, 0), E(8, 2, 0), E(16, 8, 0), E(16, 4, 0), E(32, 32, 0), EL(32, 32, 0),
 };
 #undef EL
 #undef E

@@ -137,12 +137,13 @@ def sym_from_lower(A) -> np.ndarray:
 
 
 def run_gpu_syev(A: np.ndarray, jobz: bool, *, sort: bool = True, max_sweeps_per_n: int = 0,
-                 lanes: int = 0, waves: int = 0, shift: int = 0):
+                 lanes: int = 0, waves: int = 0, shift: int = 0, band: int = 0):
     import torch
     import symmetric_tridiagonal_eigensolver_amd as st
     tA = torch.from_numpy(np.ascontiguousarray(A)).to(torch.device("cuda:0"))
     lam, Q, info = st.syev(tA, jobz, info=True, sort=sort, max_sweeps_per_n=max_sweeps_per_n,
-                           lanes_per_problem=lanes, waves_per_block=waves, shift=shift)
+                           lanes_per_problem=lanes, waves_per_block=waves, shift=shift,
+                           band_storage=band)
     torch.cuda.synchronize()
     return (lam.cpu().numpy(), None if Q is None else Q.cpu().numpy(), info.cpu().numpy())
 

@@ -284,8 +284,8 @@ def test_uninstantiated_lanes_rejected_by_query(st):
 def test_syev_default_plans(st, n, jobz, dtype, N, P, R):
     q = st.syev_query(n, 32768, jobz, dtype)
     assert (q["padded_n"], q["lanes_per_problem"], q["rows_per_lane"]) == (N, P, R)
-    # the band in registers except for double with vectors at order 32
-    assert q["band_storage"] == (2 if (dtype, jobz, N) == (1, 1, 32) else 1)
+    # the band in registers except for double at order 32
+    assert q["band_storage"] == (2 if (dtype, N) == (1, 32) else 1)
     per_block = q["waves_per_block"] * 64 // P
     assert q["workgroups"] == -(-32768 // per_block)
 
@@ -330,6 +330,7 @@ def test_syev_argument_errors(st):
     assert L.syev_batched_ex(8, 8, 8, 32, 10, 1, 1, None, None, ctypes.byref(p3)) == -10
     assert st.syev_query(32, 10, 1, 1, p2)["band_storage"] == 2
     assert st.syev_query(16, 10, 1, 0, p1)["band_storage"] == 1
+    assert st.syev_query(32, 10, 0, 1, p1)["band_storage"] == 1
     # the closed-form shift is accepted
     assert st.syev_query(16, 10, 1, 0, st.make_params(shift=st.STEQR_SHIFT_CLOSED))["padded_n"] == 16
 

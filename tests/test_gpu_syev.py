@@ -126,14 +126,26 @@ def test_syev_workload_batches(dt, n, shift):
     assert check_dense(A, g, o, jobz) == []
 
 
+@pytest.mark.parametrize("n", [32, 21])
+@pytest.mark.parametrize("band", [1, 2])
+def test_syev_double_order32_band_storage(n, band):
+    """Double at order 32 values only: the band in registers and in LDS (the
+    default) both agree with the oracle."""
+    print("syev f64 values only, band", band, "n", n, flush=True)
+    A = W.random_symmetric(n, 999, np.float64, salt=67)
+    g = run_gpu_syev(A, False, band=band)
+    o = oracle.syev(A, False, threads=8)
+    assert check_dense(A, g, o, False) == []
+
+
 def test_syev_double_vectors_limit():
     """Double precision with eigenvectors above order 32 is rejected (-4)
-    before any launch; at order 32 it runs with the band in LDS, values only
-    with the band in registers."""
+    before any launch; at order 32 double runs with the band in LDS by
+    default."""
     import symmetric_tridiagonal_eigensolver_amd as st
     assert st.lib().syev_batched(8, 8, 8, 33, 10, st.STEQR_V, st.STEQR_F64, None) == -4
     q = st.syev_query(32, 10, st.STEQR_N, st.STEQR_F64)
-    assert (q["lanes_per_problem"], q["band_storage"]) == (32, 1)
+    assert (q["lanes_per_problem"], q["band_storage"]) == (32, 2)
     q = st.syev_query(17, 10, st.STEQR_V, st.STEQR_F64)
     assert (q["lanes_per_problem"], q["band_storage"]) == (32, 2)
 
